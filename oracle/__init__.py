@@ -1,0 +1,93 @@
+"""fp64 CPU oracle for the Gated DeltaNet forward -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The GPU library never loads it and it
+shares no code with the GPU library.
+
+The arithmetic lives in ``gdn_oracle.c`` (plain C, fp64, token-by-token; the
+definition and its source passage are in that file's header).  This module
+only compiles it with gcc and marshals numpy arrays through ctypes.
+
+Parity pins: ``tests/test_oracle_pins.py`` and ``tests/golden/``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gdn_oracle.c")
+_LIB = os.path.join(_HERE, "libgdn_oracle.so")
+_lib = None
+
+DEFAULT_EPS = 1e-6
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP).  Returns the library path."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99",
+               "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
+        dp = ctypes.POINTER(ctypes.c_double)
+        lib.gdn_oracle_fwd.restype = ctypes.c_int
+        lib.gdn_oracle_fwd.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp,
+                                       ctypes.c_long, ctypes.c_long, ctypes.c_long,
+                                       ctypes.c_long, ctypes.c_long,
+                                       ctypes.c_int, ctypes.c_double, ctypes.c_double,
+                                       ctypes.c_int]
+        _lib = lib
+    return _lib
+
+
+def _f64(a):
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def gdn_fwd(q, k, v, alpha, beta, state_in=None, *, qk_l2norm=True, scale=1.0,
+            eps=DEFAULT_EPS, nthreads=0, want_state=True):
+    """Token-by-token fp64 gated delta rule.
+
+    Shapes: q, k [B,H,T,dk]; v [B,H,T,dv]; alpha, beta [B,H,T];
+    state_in [B,H,dk,dv] or None (zero state).  Inputs of any float dtype are
+    converted to fp64 exactly (bf16/fp16/fp32 all embed in fp64).
+    Returns (out [B,H,T,dv] fp64, state_out [B,H,dk,dv] fp64 or None).
+    """
+    q, k, v, alpha, beta = (_f64(x) for x in (q, k, v, alpha, beta))
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    assert k.shape == (B, H, T, dk) and v.shape == (B, H, T, dv)
+    assert alpha.shape == (B, H, T) and beta.shape == (B, H, T)
+    s_in = None
+    if state_in is not None:
+        s_in = _f64(state_in)
+        assert s_in.shape == (B, H, dk, dv)
+    out = np.empty((B, H, T, dv), dtype=np.float64)
+    s_out = np.empty((B, H, dk, dv), dtype=np.float64) if want_state else None
+    rc = _load().gdn_oracle_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                _ptr(s_in), _ptr(out), _ptr(s_out),
+                                B, H, T, dk, dv, 1 if qk_l2norm else 0,
+                                float(scale), float(eps), int(nthreads))
+    if rc != 0:
+        raise RuntimeError("gdn_oracle_fwd failed with code %d" % rc)
+    return out, s_out

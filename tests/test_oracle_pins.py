@@ -1,0 +1,264 @@
+"""Pins of the fp64 oracle against facts fixed by the mathematics of the
+gated delta rule (SANA-Streaming section 2.1; Gated DeltaNet [35]), not by the
+oracle itself: hand-worked golden examples, closed forms of special cases, an
+explicitly unrolled product of d_k x d_k matrices, per-step identities,
+contraction and split invariance.  Each test targets a plausible mistake
+(dropped term, wrong sign, wrong index, transposed operand, missing
+normalisation).
+"""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def unit(x):
+    return x / np.linalg.norm(x, axis=-1, keepdims=True)
+
+
+def rand_case(rng, B=1, H=1, T=20, dk=6, dv=5, state=True):
+    q = rng.standard_normal((B, H, T, dk))
+    k = rng.standard_normal((B, H, T, dk))
+    v = rng.standard_normal((B, H, T, dv))
+    a = np.exp(-np.log1p(np.exp(rng.standard_normal((B, H, T)))))
+    b = 1.0 / (1.0 + np.exp(-rng.standard_normal((B, H, T))))
+    s = rng.standard_normal((B, H, dk, dv)) * 0.5 if state else None
+    return q, k, v, a, b, s
+
+
+# ----------------------------------------------------------------- golden
+
+
+@pytest.mark.parametrize("name", ["worked_example_1.json", "worked_example_2.json"])
+def test_golden_worked_examples(oracle_mod, name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        g = json.load(f)
+    F = lambda a: np.array([[float(Fraction(x)) for x in row] for row in a])
+    q, k, v = F(g["q"]), F(g["k"]), F(g["v"])
+    a = np.array([float(Fraction(x)) for x in g["alpha"]])
+    b = np.array([float(Fraction(x)) for x in g["beta"]])
+    s = None if g["state_in"] is None else F(g["state_in"])[None, None]
+    out, st = oracle_mod.gdn_fwd(q[None, None], k[None, None], v[None, None], a[None, None],
+                                 b[None, None], s, eps=0.0)
+    np.testing.assert_allclose(out[0, 0], F(g["out"]), rtol=0, atol=1e-14)
+    np.testing.assert_allclose(st[0, 0], F(g["state_out"]), rtol=0, atol=1e-14)
+
+
+# ------------------------------------------------------------ closed forms
+
+
+def test_beta_zero_pure_decay(oracle_mod):
+    """beta = 0: no write and no erase, so M_t = gamma_t M_0, o_t = gamma_t M_0^T q_t."""
+    rng = np.random.default_rng(1)
+    q, k, v, a, _, s = rand_case(rng, T=30)
+    b = np.zeros_like(a)
+    out, st = oracle_mod.gdn_fwd(q, k, v, a, b, s, eps=0.0)
+    gam = np.cumprod(a[0, 0])
+    qh = unit(q[0, 0])
+    ref = gam[:, None] * (qh @ s[0, 0])
+    np.testing.assert_allclose(out[0, 0], ref, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(st[0, 0], gam[-1] * s[0, 0], rtol=1e-12, atol=1e-13)
+    # alpha = 1 as well: the state is unchanged
+    out1, st1 = oracle_mod.gdn_fwd(q, k, v, np.ones_like(a), b, s, eps=0.0)
+    np.testing.assert_allclose(st1[0, 0], s[0, 0], rtol=0, atol=1e-14)
+
+
+def test_small_beta_is_causal_linear_attention(oracle_mod):
+    """alpha = 1, M0 = 0, beta = eps*b: o_t / eps -> sum_{s<=t} b_s (k_s . q_t) v_s."""
+    rng = np.random.default_rng(2)
+    q, k, v, _, bb, _ = rand_case(rng, T=25, dk=8, dv=4, state=False)
+    a = np.ones_like(bb)
+    eps = 1e-7
+    out, _ = oracle_mod.gdn_fwd(q, k, v, a, eps * bb, None, eps=0.0)
+    qh, kh = unit(q[0, 0]), unit(k[0, 0])
+    scores = np.tril(qh @ kh.T) * bb[0, 0][None, :]
+    ref = scores @ v[0, 0]
+    np.testing.assert_allclose(out[0, 0] / eps, ref, rtol=0, atol=1e-5 * np.abs(ref).max())
+
+
+def test_orthonormal_keys_gated_linear_attention(oracle_mod):
+    """Orthonormal keys decouple the delta correction: for M0 = 0,
+    o_t = sum_{s<=t} exp(g_t - g_s) beta_s (k_s . q_t) v_s exactly."""
+    rng = np.random.default_rng(3)
+    T, dk, dv = 12, 16, 7
+    Qm, _ = np.linalg.qr(rng.standard_normal((dk, dk)))
+    k = Qm[:T][None, None] * rng.uniform(0.5, 2.0, size=(1, 1, T, 1))   # normalised inside
+    q = rng.standard_normal((1, 1, T, dk))
+    v = rng.standard_normal((1, 1, T, dv))
+    a = rng.uniform(0.3, 1.0, size=(1, 1, T))
+    b = rng.uniform(0.0, 1.0, size=(1, 1, T))
+    out, _ = oracle_mod.gdn_fwd(q, k, v, a, b, None, eps=0.0)
+    g = np.cumsum(np.log(a[0, 0]))
+    G = np.tril(np.exp(g[:, None] - g[None, :]))
+    ref = (G * (unit(q[0, 0]) @ Qm[:T].T) * b[0, 0][None, :]) @ v[0, 0]
+    np.testing.assert_allclose(out[0, 0], ref, rtol=1e-12, atol=1e-13)
+
+
+def test_orthonormal_keys_exact_retrieval(oracle_mod):
+    """beta = alpha = 1, orthonormal keys: querying with an earlier key
+    returns exactly the value written with it."""
+    rng = np.random.default_rng(4)
+    T, dk, dv = 10, 10, 3
+    Qm, _ = np.linalg.qr(rng.standard_normal((dk, dk)))
+    k = Qm[:T][None, None]
+    pick = np.array([rng.integers(0, t + 1) for t in range(T)])
+    q = Qm[pick][None, None]
+    v = rng.standard_normal((1, 1, T, dv))
+    one = np.ones((1, 1, T))
+    out, _ = oracle_mod.gdn_fwd(q, k, v, one, one, None, eps=0.0)
+    np.testing.assert_allclose(out[0, 0], v[0, 0][pick], rtol=0, atol=1e-12)
+
+
+def test_identical_keys_projector(oracle_mod):
+    """k_t = k for all t, alpha = beta = 1: M_t = (I - k k^T) M0 + k v_t^T, so
+    o_t = (q.k) v_t + q^T (I - k k^T) M0 (worst-case collinear keys)."""
+    rng = np.random.default_rng(5)
+    T, dk, dv = 15, 6, 4
+    kk = unit(rng.standard_normal(dk))
+    k = np.tile(kk, (1, 1, T, 1)) * 3.0
+    q = rng.standard_normal((1, 1, T, dk))
+    v = rng.standard_normal((1, 1, T, dv))
+    s = rng.standard_normal((1, 1, dk, dv))
+    one = np.ones((1, 1, T))
+    out, st = oracle_mod.gdn_fwd(q, k, v, one, one, s, eps=0.0)
+    Pm = np.eye(dk) - np.outer(kk, kk)
+    qh = unit(q[0, 0])
+    ref = (qh @ kk)[:, None] * v[0, 0] + qh @ Pm @ s[0, 0]
+    np.testing.assert_allclose(out[0, 0], ref, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(st[0, 0], Pm @ s[0, 0] + np.outer(kk, v[0, 0, -1]), atol=1e-12)
+
+
+def test_dk_one_is_ema(oracle_mod):
+    """dk = 1: k^ = sign(k); m_t = alpha_t (1 - beta_t) m_{t-1} + beta_t sign(k_t) v_t."""
+    rng = np.random.default_rng(6)
+    T, dv = 40, 3
+    q, k, v, a, b, s = rand_case(rng, T=T, dk=1, dv=dv)
+    out, st = oracle_mod.gdn_fwd(q, k, v, a, b, s, eps=0.0)
+    m = s[0, 0, 0].copy()
+    for t in range(T):
+        sk = np.sign(k[0, 0, t, 0])
+        # the erase term uses k^2 = 1 and the write term k^ v
+        m = a[0, 0, t] * (1 - b[0, 0, t]) * m + b[0, 0, t] * sk * v[0, 0, t]
+        np.testing.assert_allclose(out[0, 0, t], np.sign(q[0, 0, t, 0]) * m, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(st[0, 0, 0], m, rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------------- independent forms
+
+
+def test_unrolled_matrix_product(oracle_mod):
+    """M_T = P_T..P_1 M0 + sum_t P_T..P_{t+1} beta_t k_t v_t^T with
+    P_t = alpha_t (I - beta_t k_t k_t^T) as dense dk x dk matrices, and every
+    o_t = M_t^T q_t; S form S_t = alpha S (I - beta k k^T) + beta v k^T too."""
+    rng = np.random.default_rng(7)
+    T, dk, dv = 24, 7, 5
+    q, k, v, a, b, s = rand_case(rng, T=T, dk=dk, dv=dv)
+    out, st = oracle_mod.gdn_fwd(q, k, v, a, b, s, eps=0.0)
+    qh, kh = unit(q[0, 0]), unit(k[0, 0])
+    Ps = [a[0, 0, t] * (np.eye(dk) - b[0, 0, t] * np.outer(kh[t], kh[t])) for t in range(T)]
+    for t in range(T):
+        # product P_t ... P_0 applied to M0, plus the writes
+        prod = np.eye(dk)
+        for j in range(t + 1):
+            prod = Ps[j] @ prod
+        Mt = prod @ s[0, 0]
+        for u in range(t + 1):
+            tail = np.eye(dk)
+            for j in range(u + 1, t + 1):
+                tail = Ps[j] @ tail
+            Mt = Mt + tail @ (b[0, 0, u] * np.outer(kh[u], v[0, 0, u]))
+        np.testing.assert_allclose(out[0, 0, t], Mt.T @ qh[t], rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(st[0, 0], Mt, rtol=1e-11, atol=1e-12)
+    # S form, written directly from the recurrence
+    S = s[0, 0].T.copy()
+    for t in range(T):
+        S = a[0, 0, t] * S @ (np.eye(dk) - b[0, 0, t] * np.outer(kh[t], kh[t])) \
+            + b[0, 0, t] * np.outer(v[0, 0, t], kh[t])
+        np.testing.assert_allclose(out[0, 0, t], S @ qh[t], rtol=1e-11, atol=1e-12)
+
+
+def test_per_step_identity_and_contraction(oracle_mod):
+    """For unit k: S_t k_t = alpha_t (1 - beta_t) S_{t-1} k_t + beta_t v_t
+    (beta = 1 stores v_t exactly along k_t), and ||S_t|| <= alpha_t ||S_{t-1}|| + beta_t ||v_t||."""
+    rng = np.random.default_rng(8)
+    T, dk, dv = 30, 8, 6
+    q, k, v, a, b, s = rand_case(rng, T=T, dk=dk, dv=dv)
+    b[0, 0, ::5] = 1.0
+    M = s.copy()
+    for t in range(T):
+        sl = slice(t, t + 1)
+        _, M1 = oracle_mod.gdn_fwd(q[:, :, sl], k[:, :, sl], v[:, :, sl], a[:, :, sl], b[:, :, sl], M, eps=0.0)
+        kh = unit(k[0, 0, t])
+        lhs = M1[0, 0].T @ kh
+        rhs = a[0, 0, t] * (1 - b[0, 0, t]) * (M[0, 0].T @ kh) + b[0, 0, t] * v[0, 0, t]
+        np.testing.assert_allclose(lhs, rhs, rtol=1e-12, atol=1e-12)
+        n0, n1 = np.linalg.norm(M[0, 0], 2), np.linalg.norm(M1[0, 0], 2)
+        assert n1 <= a[0, 0, t] * n0 + b[0, 0, t] * np.linalg.norm(v[0, 0, t]) + 1e-12
+        M = M1
+
+
+def test_split_invariance(oracle_mod):
+    """Running [0, t1) then [t1, T) with the state carried equals one run."""
+    rng = np.random.default_rng(9)
+    q, k, v, a, b, s = rand_case(rng, B=2, H=3, T=50, dk=8, dv=12)
+    out, st = oracle_mod.gdn_fwd(q, k, v, a, b, s, eps=0.0)
+    for t1 in (1, 17, 49):
+        o1, s1 = oracle_mod.gdn_fwd(q[:, :, :t1], k[:, :, :t1], v[:, :, :t1], a[:, :, :t1], b[:, :, :t1], s, eps=0.0)
+        o2, s2 = oracle_mod.gdn_fwd(q[:, :, t1:], k[:, :, t1:], v[:, :, t1:], a[:, :, t1:], b[:, :, t1:], s1, eps=0.0)
+        np.testing.assert_allclose(np.concatenate([o1, o2], 2), out, rtol=1e-13, atol=1e-13)
+        np.testing.assert_allclose(s2, st, rtol=1e-13, atol=1e-13)
+
+
+def test_heads_are_independent_and_ordered(oracle_mod):
+    """Each (b, h) runs alone; catches mixed-up head strides."""
+    rng = np.random.default_rng(10)
+    q, k, v, a, b, s = rand_case(rng, B=2, H=3, T=9, dk=4, dv=20)
+    out, st = oracle_mod.gdn_fwd(q, k, v, a, b, s, eps=0.0)
+    for bi in range(2):
+        for hi in range(3):
+            sl = (slice(bi, bi + 1), slice(hi, hi + 1))
+            o1, s1 = oracle_mod.gdn_fwd(q[sl], k[sl], v[sl], a[sl], b[sl], s[sl], eps=0.0)
+            np.testing.assert_array_equal(o1[0, 0], out[bi, hi])
+            np.testing.assert_array_equal(s1[0, 0], st[bi, hi])
+
+
+def test_normalisation_scale_and_eps(oracle_mod):
+    """qk_l2norm = 0 uses q, k as given; scale multiplies q^; eps enters the
+    norm as sqrt(|x|^2 + eps)."""
+    rng = np.random.default_rng(11)
+    q, k, v, a, b, s = rand_case(rng, T=6, dk=3, dv=2)
+    qn, kn = unit(q), unit(k)
+    o_pre, s_pre = oracle_mod.gdn_fwd(qn, kn, v, a, b, s, qk_l2norm=False, scale=1.0, eps=0.0)
+    o_in, s_in = oracle_mod.gdn_fwd(q, k, v, a, b, s, qk_l2norm=True, eps=0.0)
+    np.testing.assert_allclose(o_in, o_pre, rtol=1e-12, atol=1e-13)
+    o_sc, _ = oracle_mod.gdn_fwd(q, k, v, a, b, s, eps=0.0, scale=0.125)
+    np.testing.assert_allclose(o_sc, 0.125 * o_in, rtol=1e-12, atol=1e-14)
+    # a tiny key: eps dominates, k^ ~ k / sqrt(eps)
+    k2 = k.copy()
+    k2[0, 0, 0] = 1e-5 * unit(k[0, 0, 0])
+    _, st = oracle_mod.gdn_fwd(q[:, :, :1], k2[:, :, :1], v[:, :, :1], a[:, :, :1], b[:, :, :1], None, eps=1e-6)
+    kh = k2[0, 0, 0] / np.sqrt(1e-10 + 1e-6)
+    np.testing.assert_allclose(st[0, 0], b[0, 0, 0] * np.outer(kh, v[0, 0, 0]), rtol=1e-12)
+
+
+def test_empty_sequence_copies_state(oracle_mod):
+    rng = np.random.default_rng(12)
+    q, k, v, a, b, s = rand_case(rng, T=0, dk=4, dv=4)
+    out, st = oracle_mod.gdn_fwd(q, k, v, a, b, s, eps=0.0)
+    assert out.shape == (1, 1, 0, 4)
+    np.testing.assert_array_equal(st, s)
+    _, z = oracle_mod.gdn_fwd(q, k, v, a, b, None, eps=0.0)
+    np.testing.assert_array_equal(z, np.zeros_like(s))
+
+
+def test_nan_propagates(oracle_mod):
+    rng = np.random.default_rng(13)
+    q, k, v, a, b, s = rand_case(rng, T=5, dk=4, dv=4)
+    v[0, 0, 2, 1] = np.nan
+    out, st = oracle_mod.gdn_fwd(q, k, v, a, b, s, eps=0.0)
+    assert np.isnan(out[0, 0, 2, 1]) and np.isnan(st[0, 0, :, 1]).any()
+    assert np.isfinite(out[0, 0, :2]).all()
