@@ -1,0 +1,244 @@
+"""Benchmark of the Gated DeltaNet forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+
+A step is one call of the whole forward path (gdn_fwd_step through the C ABI:
+norms, decay scan, Gram products, triangular solve, state contractions,
+outputs and the carried fp32 state) over one batch of synthetic input that is
+already resident in device memory.  Inputs rotate over enough distinct sets
+that the working set exceeds the 256 MB last-level cache, so every step reads
+its q/k/v from HBM.  Prints ONE JSON line (rank 0).
+
+The default workload is one streaming chunk of 3 latent frames (B=1, H=16,
+d_k=d_v=64, T=2640 tokens, chunk 64, bf16 inputs, fp32 state in and out,
+fp32 output).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import platform
+import re
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 matrix cores, published
+LLC_BYTES = 256 << 20           # Infinity Cache
+KERNEL_SOURCES = ("linear_attention_recurrence_deltanet_amd/csrc/gdn_fwd.hip",
+                  "linear_attention_recurrence_deltanet_amd/csrc/gdn_common.h")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(wl, out_bytes=4, state_in=True) -> int:
+    """Bytes one call must move at minimum: q, k, v, alpha, beta read once,
+    o written once, fp32 state read (if given) and written once."""
+    s_in = 2 if wl.dtype == "bf16" else 4
+    tokheads = wl.B * wl.H * wl.T
+    b = tokheads * (2 * wl.dk * s_in + wl.dv * s_in + 2 * s_in + wl.dv * out_bytes)
+    st = wl.B * wl.H * wl.dk * wl.dv * 4
+    return b + st + (st if state_in else 0)
+
+
+def algorithmic_flops(wl) -> int:
+    """6 d_k d_v per token and head: y = M^T k, the rank-1 update, o = M^T q."""
+    return 6 * wl.B * wl.H * wl.T * wl.dk * wl.dv
+
+
+def read_traffic(kernel_hash: str, workload: str):
+    """HBM traffic per launch from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"gdn_fwd_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m_hash = re.search(r"kernel_source_hash:\s*([0-9a-f]+)", txt)
+    m_val = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not m_hash or not m_val or m_hash.group(1) != kernel_hash:
+        return None
+    return float(m_val.group(1))
+
+
+def cpu_baseline(wl, budget_s: float):
+    """The fp64 oracle, as it stands, timed on the host cores on distinct
+    input sets of the same workload until about `budget_s` seconds pass."""
+    import oracle
+    from linear_attention_recurrence_deltanet_amd.inputs import make_call, to_numpy64
+    oracle.build(force=False)
+    nthreads = os.cpu_count() or 1
+    sets = [make_call(wl, i) for i in range(2)]
+    npsets = []
+    for d in sets:
+        npsets.append([to_numpy64(d[n]) for n in ("q", "k", "v", "alpha", "beta")] +
+                      [None if d["state_in"] is None else to_numpy64(d["state_in"])])
+    calls = 0
+    t0 = time.perf_counter()
+    while True:
+        q, k, v, a, b, s = npsets[calls % len(npsets)]
+        oracle.gdn_fwd(q, k, v, a, b, s, nthreads=nthreads)
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    tokens = calls * wl.B * wl.T
+    cpu_model = platform.processor() or ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": tokens / el, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"{calls} full calls of the same workload (B={wl.B} H={wl.H} T={wl.T} "
+                      f"dk={wl.dk} dv={wl.dv}) in {el:.1f} s, fp64 token-by-token, "
+                      f"OpenMP over (b, h, 16-column block), CPU: {cpu_model}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="stream_chunk_h16_d64")
+    ap.add_argument("--chunk", type=int, default=0, help="0: gdn_fwd_step; else gdn_fwd_chunked")
+    ap.add_argument("--out-dtype", default="f32", choices=["f32", "bf16"])
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also launch a plain 256 MiB device copy (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs on exactly one GPU; a multi-GPU figure is not "
+              "part of it (heads and value columns shard with no communication).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from linear_attention_recurrence_deltanet_amd import gdn
+    from linear_attention_recurrence_deltanet_amd.inputs import WORKLOADS, make_call
+
+    wl = WORKLOADS[args.workload]
+    if args.chunk:
+        wl = wl.replace(chunk=args.chunk)
+    lib = gdn.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    out_dt = torch.float32 if args.out_dtype == "f32" else torch.bfloat16
+    out_bytes = 4 if args.out_dtype == "f32" else 2
+    state_given = True
+    alg_bytes = algorithmic_bytes(wl, out_bytes, state_given)
+
+    # distinct resident input sets so the rotation exceeds 2x the LLC
+    per_set = wl.B * wl.H * wl.T * (2 * wl.dk + wl.dv + 2) * (2 if wl.dtype == "bf16" else 4)
+    nsets = max(2, min(64, (2 * LLC_BYTES) // max(per_set, 1) + 1))
+    sets = []
+    for i in range(nsets):
+        d = make_call(wl, i)
+        g = {k: (None if v is None else v.to(dev).contiguous()) for k, v in d.items()}
+        sets.append(g)
+    st_shape = (wl.B, wl.H, wl.dk, wl.dv)
+    state0 = sets[0]["state_in"] if sets[0]["state_in"] is not None else torch.zeros(st_shape, device=dev)
+    state = state0.clone()
+    outs = [torch.empty(wl.B, wl.H, wl.T, wl.dv, dtype=out_dt, device=dev) for _ in range(2)]
+    stream = torch.cuda.current_stream()
+    opts = gdn.make_opts(sets[0]["q"].dtype, out_dt, True, 1.0, 1e-6, stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    calls = []
+    for i, g in enumerate(sets):
+        a = (P(g["q"]), P(g["k"]), P(g["v"]), P(g["alpha"]), P(g["beta"]), P(state),
+             P(outs[i % 2]), P(state), wl.B, wl.H, wl.T, wl.dk, wl.dv)
+        calls.append(a)
+    if args.chunk:
+        fn = lambda a: lib.gdn_fwd_chunked(*a, wl.chunk, ctypes.byref(opts))
+    else:
+        fn = lambda a: lib.gdn_fwd_step(*a, ctypes.byref(opts))
+
+    for i in range(args.warmup):
+        st = fn(calls[i % nsets])
+        if st != 0:
+            raise RuntimeError(lib.gdn_last_error().decode())
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(K):
+        ev[i][0].record(stream)
+        fn(calls[i % nsets])
+        ev[i][1].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    per = [a.elapsed_time(b) for a, b in ev]
+    kern_ms = statistics.mean(per)
+    p50 = statistics.median(per)
+    p99 = sorted(per)[min(len(per) - 1, int(0.99 * len(per)))]
+    ms_per_step = max(total_ms, wall * 1e3) / K
+    tokens_per_step = wl.B * wl.T
+
+    if args.copy_calibration:
+        x = torch.empty(64 << 20, dtype=torch.float32, device=dev)
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+
+    khash = kernel_source_hash()
+    achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
+    res = {
+        "metric": "GDN fwd tokens/sec (bf16, 1 GPU) + % of HBM/MFMA roofline vs oracle",
+        "value": tokens_per_step / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "T": wl.T, "dk": wl.dk,
+                   "dv": wl.dv, "chunk": wl.chunk, "entry": "gdn_fwd_chunked" if args.chunk
+                   else "gdn_fwd_step", "out_dtype": args.out_dtype, "state": "fp32 carried",
+                   "input_sets": nsets},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": read_traffic(khash, wl.name)},
+        "kernel": {"avg_ms": kern_ms, "p50_ms": p50, "p99_ms": p99,
+                   "algorithmic_bytes": alg_bytes, "algorithmic_flops": algorithmic_flops(wl),
+                   "mfma_frac_of_bf16_peak": algorithmic_flops(wl) / (kern_ms * 1e-3) / 1e12
+                   / MFMA_BF16_PEAK_TFLOPS,
+                   "source_hash": khash},
+    }
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

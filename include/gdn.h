@@ -1,0 +1,127 @@
+/*
+ * gdn.h -- C ABI of libgdn, the Gated DeltaNet (gated delta rule) forward
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (SANA-Streaming, paperpeel page, section 2.1 "Frame-wise Gated
+ * DeltaNet for Global Accumulated Memory": each linear-attention head keeps a
+ * fixed-size recurrent state, corrected by the delta rule of Gated DeltaNet
+ * [35], and carries it across streaming chunks so memory does not grow with
+ * video length; appendix G.3 names the decay gate alpha and the write gate
+ * beta; section 2.3 "Efficient GDN Kernel" keeps that state on chip while the
+ * q/k/v activations stream from HBM).  The update equation did not survive on
+ * the page; this library implements the token-wise gated delta rule:
+ *
+ *   for each batch b and head h, with unit-normalised q_t, k_t:
+ *     S_t = alpha_t * S_{t-1} * (I - beta_t * k_t k_t^T) + beta_t * v_t k_t^T
+ *     o_t = S_t q_t
+ *
+ * Layouts (all row-major, contiguous, device memory owned by the caller):
+ *   q, k      [B][H][T][dk]     GDN_BF16 or GDN_F32 (opts->in_dtype)
+ *   v         [B][H][T][dv]     same dtype
+ *   alpha     [B][H][T]         same dtype; decay, expected in (0, 1]
+ *   beta      [B][H][T]         same dtype; write strength, expected in [0, 1]
+ *   state_in  [B][H][dk][dv]    fp32, or NULL for a zero initial state
+ *   out       [B][H][T][dv]     opts->out_dtype (default fp32)
+ *   state_out [B][H][dk][dv]    fp32, or NULL (final state not written)
+ * The state is stored transposed relative to S: state[b][h][i][j] = S[j][i],
+ * the weight from key dimension i to value dimension j.
+ *
+ * Conventions:
+ *  - Asynchronous: calls enqueue work on opts->stream (NULL = the null stream)
+ *    and return; results are valid after the caller synchronises that stream.
+ *  - Ownership: the library allocates no device memory.  Paths that split a
+ *    sequence across workgroups need a caller-owned workspace of
+ *    gdn_workspace_bytes() bytes (opts->workspace); without one the
+ *    single-pass path runs instead (same results to rounding).
+ *  - Aliasing: only state_in and state_out may alias (in-place state update).
+ *    Other buffers must not overlap.
+ *  - Errors: argument errors return synchronously before any HIP call
+ *    (GDN_ERR_ARG / GDN_ERR_UNSUPPORTED); a failed launch returns GDN_ERR_HIP.
+ *    gdn_last_error() gives a per-thread message.  No exception crosses the
+ *    ABI.  NaN/Inf in the inputs propagate and are not trapped.
+ *  - T == 0: state_out receives state_in (or zeros); out is untouched.
+ *  - Thread safety: no mutable global state besides the per-thread error text.
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_VERSION 1
+
+typedef enum {
+    GDN_OK = 0,
+    GDN_ERR_ARG = -1,          /* NULL pointer, negative size, misalignment   */
+    GDN_ERR_UNSUPPORTED = -2,  /* head size or chunk outside the built set    */
+    GDN_ERR_HIP = -3           /* a HIP call or kernel launch failed          */
+} gdn_status;
+
+typedef enum { GDN_BF16 = 0, GDN_F32 = 1 } gdn_dtype;
+
+typedef struct gdn_opts {
+    int    in_dtype;         /* gdn_dtype of q, k, v, alpha, beta; default GDN_BF16 */
+    int    out_dtype;        /* gdn_dtype of out; default GDN_F32                  */
+    int    qk_l2norm;        /* 1 (default): q_t, k_t divided by sqrt(|x|^2 + eps)
+                                inside the kernel; 0: used as given              */
+    float  scale;            /* multiplies q_t after normalisation; default 1     */
+    float  eps;              /* default 1e-6                                      */
+    void*  stream;           /* hipStream_t; NULL = null stream                   */
+    void*  workspace;        /* device scratch for the split-sequence path        */
+    size_t workspace_bytes;  /* size of workspace                                 */
+} gdn_opts;
+
+/* Fill *opts with the defaults listed above. */
+void gdn_default_opts(gdn_opts* opts);
+
+/*
+ * gdn_fwd_chunked: the chunked forward over a whole sequence of T tokens per
+ * head, starting from state_in and producing every o_t and the final state.
+ * `chunk` is the kernel's token tile (32, 64 or 128); results do not depend
+ * on it beyond rounding.  dk in {32, 64, 128}; dv in {32, 64, 128}.
+ * opts may be NULL (defaults).  Pointers must be 16-byte aligned.
+ */
+int gdn_fwd_chunked(const void* q, const void* k, const void* v,
+                    const void* alpha, const void* beta,
+                    const float* state_in, void* out, float* state_out,
+                    int B, int H, int T, int dk, int dv, int chunk,
+                    const gdn_opts* opts);
+
+/*
+ * gdn_fwd_step: one streaming chunk (the tokens of a few latent frames) with
+ * the state carried from the previous call: state_out of call i is meant to
+ * be state_in of call i+1 (the two may be the same buffer).  Same arguments
+ * as gdn_fwd_chunked without `chunk`; the library picks the launch that
+ * minimises the latency of one call.
+ */
+int gdn_fwd_step(const void* q, const void* k, const void* v,
+                 const void* alpha, const void* beta,
+                 const float* state_in, void* out, float* state_out,
+                 int B, int H, int T, int dk, int dv,
+                 const gdn_opts* opts);
+
+/*
+ * Workspace size (bytes) that lets gdn_fwd_chunked (chunk > 0) or
+ * gdn_fwd_step (chunk == 0) use the split-sequence path for this shape;
+ * 0 when that path would not be used.  Returns 0 for invalid shapes.
+ */
+size_t gdn_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk,
+                           const gdn_opts* opts);
+
+/* Static description of a status code. */
+const char* gdn_strerror(int status);
+
+/* Detail of the last error on the calling thread ("" if none). */
+const char* gdn_last_error(void);
+
+/* GDN_VERSION of the built library. */
+int gdn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H_ */

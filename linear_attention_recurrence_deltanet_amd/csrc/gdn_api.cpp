@@ -1,0 +1,146 @@
+// gdn_api.cpp -- C ABI of libgdn: argument validation, launch planning and
+// dispatch to the HIP kernels.  Declarations and conventions: include/gdn.h.
+#include "gdn.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "gdn_kernels.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, const char* detail = nullptr) {
+    if (detail)
+        snprintf(g_last_error, sizeof(g_last_error), fmt, detail);
+    else
+        snprintf(g_last_error, sizeof(g_last_error), "%s", fmt);
+    return status;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool head_ok(int d) { return d == 32 || d == 64 || d == 128; }
+
+struct Resolved {
+    gdn_opts o;
+};
+
+void defaults(gdn_opts* o) {
+    o->in_dtype = GDN_BF16;
+    o->out_dtype = GDN_F32;
+    o->qk_l2norm = 1;
+    o->scale = 1.0f;
+    o->eps = 1e-6f;
+    o->stream = nullptr;
+    o->workspace = nullptr;
+    o->workspace_bytes = 0;
+}
+
+int validate(const void* q, const void* k, const void* v, const void* alpha, const void* beta,
+             const float* state_in, const void* out, const float* state_out,
+             int B, int H, int T, int dk, int dv, int chunk, const gdn_opts& o) {
+    if (B <= 0 || H <= 0) return fail(GDN_ERR_ARG, "B and H must be positive");
+    if (T < 0) return fail(GDN_ERR_ARG, "T must be non-negative");
+    if ((long long)B * H * 8 > 0x7fffffffLL) return fail(GDN_ERR_ARG, "B*H too large");
+    if ((long long)T * (dk > dv ? dk : dv) * 4 > 0x7fffffffLL * 4LL)
+        return fail(GDN_ERR_ARG, "T too large");
+    if (!head_ok(dk)) return fail(GDN_ERR_UNSUPPORTED, "dk must be 32, 64 or 128");
+    if (!head_ok(dv)) return fail(GDN_ERR_UNSUPPORTED, "dv must be 32, 64 or 128");
+    if (chunk != 32 && chunk != 64 && chunk != 128)
+        return fail(GDN_ERR_UNSUPPORTED, "chunk must be 32, 64 or 128");
+    if (o.in_dtype != GDN_BF16 && o.in_dtype != GDN_F32) return fail(GDN_ERR_ARG, "bad in_dtype");
+    if (o.out_dtype != GDN_BF16 && o.out_dtype != GDN_F32) return fail(GDN_ERR_ARG, "bad out_dtype");
+    if (T > 0) {
+        if (!q || !k || !v || !alpha || !beta || !out)
+            return fail(GDN_ERR_ARG, "q, k, v, alpha, beta and out must be non-null when T > 0");
+        if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+            return fail(GDN_ERR_ARG, "q, k, v and out must be 16-byte aligned");
+        const size_t esz = o.in_dtype == GDN_F32 ? 4 : 2;
+        if ((reinterpret_cast<uintptr_t>(alpha) % esz) || (reinterpret_cast<uintptr_t>(beta) % esz))
+            return fail(GDN_ERR_ARG, "alpha and beta must be aligned to their element size");
+    }
+    if (state_in && !aligned16(state_in)) return fail(GDN_ERR_ARG, "state_in must be 16-byte aligned");
+    if (state_out && !aligned16(state_out)) return fail(GDN_ERR_ARG, "state_out must be 16-byte aligned");
+    return GDN_OK;
+}
+
+// Value-column tile: the widest tile that still gives every compute unit a
+// workgroup; below that the narrowest tile (most workgroups).
+int choose_bv(int in_f32, int B, int H, int dk, int dv, int chunk) {
+    const int maxbv = gdn::seq_max_bv(in_f32, dk, chunk);
+    const long long bh = (long long)B * H;
+    const int cand[3] = {64, 32, 16};
+    for (int c : cand) {
+        if (c > maxbv || dv % c) continue;
+        if (bh * (dv / c) >= 256) return c;
+    }
+    return maxbv < 16 ? maxbv : 16;
+}
+
+int run(const void* q, const void* k, const void* v, const void* alpha, const void* beta,
+        const float* state_in, void* out, float* state_out,
+        int B, int H, int T, int dk, int dv, int chunk, const gdn_opts* opts) {
+    g_last_error[0] = '\0';
+    gdn_opts o;
+    if (opts) o = *opts; else defaults(&o);
+    int st = validate(q, k, v, alpha, beta, state_in, out, state_out, B, H, T, dk, dv, chunk, o);
+    if (st != GDN_OK) return st;
+    gdn::FwdArgs a;
+    a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta;
+    a.state_in = state_in; a.out = out; a.state_out = state_out;
+    a.B = B; a.H = H; a.T = T; a.dk = dk; a.dv = dv;
+    a.scale = o.scale; a.eps = o.eps; a.qk_l2norm = o.qk_l2norm ? 1 : 0;
+    a.out_bf16 = o.out_dtype == GDN_BF16; a.in_f32 = o.in_dtype == GDN_F32;
+    if (T == 0 && !state_out) return GDN_OK;
+    if (gdn::seq_max_bv(a.in_f32, dk, chunk) == 0)
+        return fail(GDN_ERR_UNSUPPORTED, "this chunk does not fit on chip for fp32 inputs at this dk");
+    const int bv = choose_bv(a.in_f32, B, H, dk, dv, chunk);
+    hipError_t e = gdn::launch_fwd_seq(a, chunk, bv, reinterpret_cast<hipStream_t>(o.stream));
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+void gdn_default_opts(gdn_opts* opts) {
+    if (opts) defaults(opts);
+}
+
+int gdn_fwd_chunked(const void* q, const void* k, const void* v, const void* alpha, const void* beta,
+                    const float* state_in, void* out, float* state_out,
+                    int B, int H, int T, int dk, int dv, int chunk, const gdn_opts* opts) {
+    return run(q, k, v, alpha, beta, state_in, out, state_out, B, H, T, dk, dv, chunk, opts);
+}
+
+int gdn_fwd_step(const void* q, const void* k, const void* v, const void* alpha, const void* beta,
+                 const float* state_in, void* out, float* state_out,
+                 int B, int H, int T, int dk, int dv, const gdn_opts* opts) {
+    return run(q, k, v, alpha, beta, state_in, out, state_out, B, H, T, dk, dv, 64, opts);
+}
+
+size_t gdn_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, const gdn_opts* opts) {
+    (void)B; (void)H; (void)T; (void)dk; (void)dv; (void)chunk; (void)opts;
+    return 0;
+}
+
+const char* gdn_strerror(int status) {
+    switch (status) {
+    case GDN_OK: return "ok";
+    case GDN_ERR_ARG: return "invalid argument";
+    case GDN_ERR_UNSUPPORTED: return "unsupported shape or option";
+    case GDN_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+    }
+}
+
+const char* gdn_last_error(void) { return g_last_error; }
+
+int gdn_version(void) { return GDN_VERSION; }
+
+}  // extern "C"

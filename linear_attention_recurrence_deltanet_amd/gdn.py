@@ -1,0 +1,164 @@
+"""ctypes binding of libgdn (C ABI in include/gdn.h).
+
+Argument marshalling only: every step of the forward runs in the HIP kernels
+of libgdn.so.  PyTorch supplies device memory and the current stream.  There
+is no CPU fallback: if libgdn.so is missing or not built, calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn.so")
+
+GDN_OK, GDN_ERR_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_HIP = 0, -1, -2, -3
+GDN_BF16, GDN_F32 = 0, 1
+
+# every exported entry point of include/gdn.h
+EXPORTS = ("gdn_default_opts", "gdn_fwd_chunked", "gdn_fwd_step", "gdn_workspace_bytes",
+           "gdn_strerror", "gdn_last_error", "gdn_version")
+
+
+class GdnOpts(ctypes.Structure):
+    _fields_ = [("in_dtype", ctypes.c_int),
+                ("out_dtype", ctypes.c_int),
+                ("qk_l2norm", ctypes.c_int),
+                ("scale", ctypes.c_float),
+                ("eps", ctypes.c_float),
+                ("stream", ctypes.c_void_p),
+                ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"libgdn status {status}: {detail}")
+        self.status = status
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load libgdn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"libgdn.so not found at {path}: run "
+                           "`python -m linear_attention_recurrence_deltanet_amd.build` first")
+    lib = ctypes.CDLL(path)
+    vp, i = ctypes.c_void_p, ctypes.c_int
+    fwd_args = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i]
+    lib.gdn_fwd_chunked.argtypes = fwd_args + [i, ctypes.POINTER(GdnOpts)]
+    lib.gdn_fwd_chunked.restype = i
+    lib.gdn_fwd_step.argtypes = fwd_args + [ctypes.POINTER(GdnOpts)]
+    lib.gdn_fwd_step.restype = i
+    lib.gdn_workspace_bytes.argtypes = [i, i, i, i, i, i, ctypes.POINTER(GdnOpts)]
+    lib.gdn_workspace_bytes.restype = ctypes.c_size_t
+    lib.gdn_default_opts.argtypes = [ctypes.POINTER(GdnOpts)]
+    lib.gdn_default_opts.restype = None
+    lib.gdn_strerror.argtypes = [i]
+    lib.gdn_strerror.restype = ctypes.c_char_p
+    lib.gdn_last_error.argtypes = []
+    lib.gdn_last_error.restype = ctypes.c_char_p
+    lib.gdn_version.argtypes = []
+    lib.gdn_version.restype = i
+    _lib = lib
+    return lib
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.bfloat16:
+        return GDN_BF16
+    if dt == torch.float32:
+        return GDN_F32
+    raise TypeError(f"unsupported dtype {dt}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def make_opts(in_dtype=torch.bfloat16, out_dtype=torch.float32, qk_l2norm=True, scale=1.0,
+              eps=1e-6, stream=None, workspace: Optional[torch.Tensor] = None) -> GdnOpts:
+    o = GdnOpts()
+    load().gdn_default_opts(ctypes.byref(o))
+    o.in_dtype = _dtype_code(in_dtype)
+    o.out_dtype = _dtype_code(out_dtype)
+    o.qk_l2norm = 1 if qk_l2norm else 0
+    o.scale = float(scale)
+    o.eps = float(eps)
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    o.stream = ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+    if workspace is not None:
+        o.workspace = ctypes.c_void_p(workspace.data_ptr())
+        o.workspace_bytes = workspace.numel() * workspace.element_size()
+    return o
+
+
+def workspace_bytes(B, H, T, dk, dv, chunk=0, opts: Optional[GdnOpts] = None) -> int:
+    return int(load().gdn_workspace_bytes(B, H, T, dk, dv, chunk,
+                                          ctypes.byref(opts) if opts is not None else None))
+
+
+def _check(status: int):
+    if status != GDN_OK:
+        raise GdnError(status, load().gdn_last_error().decode())
+
+
+def _prep(q, k, v, alpha, beta, state_in, out, state_out, out_dtype):
+    for name, t in (("q", q), ("k", k), ("v", v), ("alpha", alpha), ("beta", beta)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.dtype != q.dtype:
+            raise ValueError(f"{name} dtype {t.dtype} differs from q dtype {q.dtype}")
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or v.shape[:3] != (B, H, T):
+        raise ValueError("shape mismatch between q, k, v")
+    if alpha.shape != (B, H, T) or beta.shape != (B, H, T):
+        raise ValueError("alpha and beta must be [B, H, T]")
+    if state_in is not None and (state_in.dtype != torch.float32 or not state_in.is_contiguous()
+                                 or state_in.shape != (B, H, dk, dv)):
+        raise ValueError("state_in must be contiguous fp32 [B, H, dk, dv]")
+    if out is None:
+        out = torch.empty(B, H, T, dv, dtype=out_dtype, device=q.device)
+    if state_out is None:
+        state_out = torch.empty(B, H, dk, dv, dtype=torch.float32, device=q.device)
+    return B, H, T, dk, dv, out, state_out
+
+
+def fwd_chunked(q, k, v, alpha, beta, state_in=None, chunk: int = 64, *, out=None, state_out=None,
+                out_dtype=torch.float32, qk_l2norm=True, scale=1.0, eps=1e-6, stream=None,
+                workspace: Optional[torch.Tensor] = None, want_state: bool = True):
+    """gdn_fwd_chunked.  Returns (out, state_out)."""
+    B, H, T, dk, dv, out, state_out = _prep(q, k, v, alpha, beta, state_in, out,
+                                            state_out if want_state else None, out_dtype)
+    if not want_state:
+        state_out = None
+    opts = make_opts(q.dtype, out.dtype, qk_l2norm, scale, eps, stream, workspace)
+    _check(load().gdn_fwd_chunked(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                  _ptr(state_in), _ptr(out), _ptr(state_out),
+                                  B, H, T, dk, dv, int(chunk), ctypes.byref(opts)))
+    return out, state_out
+
+
+def fwd_step(q, k, v, alpha, beta, state_in=None, *, out=None, state_out=None,
+             out_dtype=torch.float32, qk_l2norm=True, scale=1.0, eps=1e-6, stream=None,
+             workspace: Optional[torch.Tensor] = None):
+    """gdn_fwd_step: one streaming chunk.  state_out may be state_in (in place)."""
+    B, H, T, dk, dv, out, state_out = _prep(q, k, v, alpha, beta, state_in, out, state_out,
+                                            out_dtype)
+    opts = make_opts(q.dtype, out.dtype, qk_l2norm, scale, eps, stream, workspace)
+    _check(load().gdn_fwd_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                               _ptr(state_in), _ptr(out), _ptr(state_out),
+                               B, H, T, dk, dv, ctypes.byref(opts)))
+    return out, state_out

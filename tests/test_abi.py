@@ -1,0 +1,115 @@
+"""C-ABI contract of libgdn that can be checked without a GPU: the library
+loads, exports every entry point declared in include/gdn.h, and rejects bad
+arguments synchronously (before any HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from linear_attention_recurrence_deltanet_amd import gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "gdn.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(gdn.LIB_PATH):
+        from linear_attention_recurrence_deltanet_amd import build
+        build.build(verbose=False)
+    return gdn.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert set(names) == set(gdn.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_strings(lib):
+    assert lib.gdn_version() == 1
+    assert lib.gdn_strerror(0) == b"ok"
+    assert lib.gdn_strerror(-1) == b"invalid argument"
+    assert lib.gdn_strerror(-2) == b"unsupported shape or option"
+    assert lib.gdn_strerror(-3) == b"HIP error"
+
+
+def test_default_opts(lib):
+    o = gdn.GdnOpts()
+    lib.gdn_default_opts(ctypes.byref(o))
+    assert (o.in_dtype, o.out_dtype, o.qk_l2norm) == (gdn.GDN_BF16, gdn.GDN_F32, 1)
+    assert o.scale == 1.0 and abs(o.eps - 1e-6) < 1e-12
+    assert o.stream is None and o.workspace is None and o.workspace_bytes == 0
+
+
+def _call(lib, q=16, k=16, v=16, a=16, b=16, sin=None, out=16, sout=None,
+          B=1, H=1, T=8, dk=64, dv=64, chunk=64, opts=None):
+    P = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.gdn_fwd_chunked(P(q), P(k), P(v), P(a), P(b), P(sin), P(out), P(sout),
+                               B, H, T, dk, dv, chunk, opts)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), gdn.GDN_ERR_ARG),
+    (dict(out=None), gdn.GDN_ERR_ARG),
+    (dict(B=0), gdn.GDN_ERR_ARG),
+    (dict(H=-1), gdn.GDN_ERR_ARG),
+    (dict(T=-1), gdn.GDN_ERR_ARG),
+    (dict(dk=48), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(dv=256), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(chunk=16), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(chunk=100), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(q=24), gdn.GDN_ERR_ARG),          # misaligned
+    (dict(sin=8), gdn.GDN_ERR_ARG),         # misaligned state
+    (dict(a=17), gdn.GDN_ERR_ARG),          # alpha not element aligned
+])
+def test_argument_errors_are_synchronous(lib, kw, status):
+    # every pointer here is a fake address: validation must reject before any use
+    assert _call(lib, **kw) == status
+    assert len(lib.gdn_last_error()) > 0
+
+
+def test_bad_dtype_in_opts(lib):
+    o = gdn.GdnOpts()
+    lib.gdn_default_opts(ctypes.byref(o))
+    o.in_dtype = 7
+    assert _call(lib, opts=ctypes.byref(o)) == gdn.GDN_ERR_ARG
+    o.in_dtype = gdn.GDN_F32
+    o.out_dtype = 9
+    assert _call(lib, opts=ctypes.byref(o)) == gdn.GDN_ERR_ARG
+
+
+def test_fp32_chunk_that_does_not_fit_is_rejected(lib):
+    o = gdn.GdnOpts()
+    lib.gdn_default_opts(ctypes.byref(o))
+    o.in_dtype = gdn.GDN_F32
+    assert _call(lib, dk=128, chunk=128, opts=ctypes.byref(o)) == gdn.GDN_ERR_UNSUPPORTED
+
+
+def test_step_validates_too(lib):
+    P = ctypes.c_void_p
+    assert lib.gdn_fwd_step(None, P(16), P(16), P(16), P(16), None, P(16), None,
+                            1, 1, 4, 64, 64, None) == gdn.GDN_ERR_ARG
+
+
+def test_workspace_query_is_host_only(lib):
+    assert lib.gdn_workspace_bytes(1, 16, 2640, 64, 64, 64, None) >= 0
+    assert lib.gdn_workspace_bytes(0, 16, 2640, 64, 64, 64, None) == 0
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    import importlib
+    mod = importlib.reload(gdn)
+    try:
+        mod._lib = None
+        with pytest.raises(RuntimeError, match="libgdn.so not found"):
+            mod.load(str(tmp_path / "missing.so"))
+    finally:
+        importlib.reload(gdn)
