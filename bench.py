@@ -159,7 +159,10 @@ def main():
     state = state0.clone()
     outs = [torch.empty(wl.B, wl.H, wl.T, wl.dv, dtype=out_dt, device=dev) for _ in range(2)]
     stream = torch.cuda.current_stream()
-    opts = gdn.make_opts(sets[0]["q"].dtype, out_dt, True, 1.0, 1e-6, stream)
+    ws_bytes = gdn.workspace_bytes(wl.B, wl.H, wl.T, wl.dk, wl.dv, args.chunk,
+                                   gdn.make_opts(sets[0]["q"].dtype, out_dt))
+    workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    opts = gdn.make_opts(sets[0]["q"].dtype, out_dt, True, 1.0, 1e-6, stream, workspace)
     P = lambda t: ctypes.c_void_p(t.data_ptr())
     calls = []
     for i, g in enumerate(sets):
@@ -225,7 +228,7 @@ def main():
         "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "T": wl.T, "dk": wl.dk,
                    "dv": wl.dv, "chunk": wl.chunk, "entry": "gdn_fwd_chunked" if args.chunk
                    else "gdn_fwd_step", "out_dtype": args.out_dtype, "state": "fp32 carried",
-                   "input_sets": nsets},
+                   "input_sets": nsets, "workspace_bytes": ws_bytes},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": read_traffic(khash, wl.name)},

@@ -11,6 +11,8 @@
 
 namespace {
 
+constexpr int STEP_CHUNK = 64;   // token tile of gdn_fwd_step
+
 thread_local char g_last_error[512] = "";
 
 int fail(int status, const char* fmt, const char* detail = nullptr) {
@@ -24,10 +26,6 @@ int fail(int status, const char* fmt, const char* detail = nullptr) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 bool head_ok(int d) { return d == 32 || d == 64 || d == 128; }
-
-struct Resolved {
-    gdn_opts o;
-};
 
 void defaults(gdn_opts* o) {
     o->in_dtype = GDN_BF16;
@@ -68,10 +66,20 @@ int validate(const void* q, const void* k, const void* v, const void* alpha, con
     return GDN_OK;
 }
 
-// Value-column tile: the widest tile that still gives every compute unit a
+// Launch plan of one call.
+struct Plan {
+    bool single;     // single-pass kernel (128-token chunks, or walker does not fit)
+    int bv;          // value-column tile (single) ...
+    int waves;       // ... or waves per workgroup of the walker (tile = 16 * waves)
+    int nseg;        // sequence segments (walker)
+    int seg_chunks;  // chunks per segment
+    size_t ws_bytes; // workspace needed for nseg > 1
+};
+
+// Single-pass kernel: the widest tile that still gives every compute unit a
 // workgroup; below that the narrowest tile (most workgroups).
-int choose_bv(int in_f32, int B, int H, int dk, int dv, int chunk) {
-    const int maxbv = gdn::seq_max_bv(in_f32, dk, chunk);
+int single_bv(int in_f32, int B, int H, int dk, int dv, int chunk) {
+    const int maxbv = gdn::single_max_bv(in_f32, dk, chunk);
     const long long bh = (long long)B * H;
     const int cand[3] = {64, 32, 16};
     for (int c : cand) {
@@ -79,6 +87,40 @@ int choose_bv(int in_f32, int B, int H, int dk, int dv, int chunk) {
         if (bh * (dv / c) >= 256) return c;
     }
     return maxbv < 16 ? maxbv : 16;
+}
+
+// Walker plan.  Without segments a sequence is one chain of chunks per
+// workgroup; with few heads that leaves most of the 256 compute units idle,
+// so the sequence is cut into segments until about one workgroup per compute
+// unit is busy (each segment keeps at least two chunks).
+Plan make_plan(int in_f32, int B, int H, int T, int dk, int dv, int chunk) {
+    Plan pl{};
+    int w = chunk == 128 ? 0 : gdn::walk_max_waves(in_f32, dk, chunk);
+    while (w > 0 && (16 * w > dk || 16 * w > dv)) w >>= 1;
+    if (w < 2) w = 0;
+    if (w == 0) {
+        pl.single = true;
+        pl.bv = single_bv(in_f32, B, H, dk, dv, chunk);
+        pl.nseg = 1;
+        return pl;
+    }
+    pl.waves = w;
+    const int nchunks = (T + chunk - 1) / chunk;
+    const long long base = (long long)B * H * (w ? dv / (16 * w) : 1);
+    int nseg = 1;
+    if (nchunks >= 4 && base < 256) {
+        const long long want = (256 + base - 1) / base;
+        int L = (int)((nchunks + want - 1) / want);
+        if (L < 2) L = 2;
+        nseg = (nchunks + L - 1) / L;
+    }
+    pl.nseg = nseg < 1 ? 1 : nseg;
+    pl.seg_chunks = (nchunks + pl.nseg - 1) / pl.nseg;
+    if (pl.seg_chunks < 1) pl.seg_chunks = 1;
+    pl.nseg = nchunks > 0 ? (nchunks + pl.seg_chunks - 1) / pl.seg_chunks : 1;
+    if (pl.nseg > 1)
+        pl.ws_bytes = ((size_t)B * H * (pl.nseg - 1) * dk * (dk + dv) + (size_t)B * H * dk * dv) * 4;
+    return pl;
 }
 
 int run(const void* q, const void* k, const void* v, const void* alpha, const void* beta,
@@ -89,19 +131,45 @@ int run(const void* q, const void* k, const void* v, const void* alpha, const vo
     if (opts) o = *opts; else defaults(&o);
     int st = validate(q, k, v, alpha, beta, state_in, out, state_out, B, H, T, dk, dv, chunk, o);
     if (st != GDN_OK) return st;
-    gdn::FwdArgs a;
+    gdn::WalkArgs a;
     a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta;
     a.state_in = state_in; a.out = out; a.state_out = state_out;
     a.B = B; a.H = H; a.T = T; a.dk = dk; a.dv = dv;
     a.scale = o.scale; a.eps = o.eps; a.qk_l2norm = o.qk_l2norm ? 1 : 0;
     a.out_bf16 = o.out_dtype == GDN_BF16; a.in_f32 = o.in_dtype == GDN_F32;
     if (T == 0 && !state_out) return GDN_OK;
-    if (gdn::seq_max_bv(a.in_f32, dk, chunk) == 0)
-        return fail(GDN_ERR_UNSUPPORTED, "this chunk does not fit on chip for fp32 inputs at this dk");
-    const int bv = choose_bv(a.in_f32, B, H, dk, dv, chunk);
-    hipError_t e = gdn::launch_fwd_seq(a, chunk, bv, reinterpret_cast<hipStream_t>(o.stream));
+    Plan pl = make_plan(a.in_f32, B, H, T, dk, dv, chunk);
+    hipStream_t stream = reinterpret_cast<hipStream_t>(o.stream);
+    hipError_t e;
+    if (pl.single) {
+        if (pl.bv == 0)
+            return fail(GDN_ERR_UNSUPPORTED, "this chunk does not fit on chip for fp32 inputs at this dk");
+        e = gdn::launch_fwd_single(a, chunk, pl.bv, stream);
+    } else {
+        if (pl.nseg > 1 && (!o.workspace || o.workspace_bytes < pl.ws_bytes)) {
+            pl.nseg = 1;                       // no workspace: unsplit walk
+            pl.seg_chunks = (T + chunk - 1) / chunk;
+        }
+        if (pl.seg_chunks < 1) pl.seg_chunks = 1;
+        a.nseg = pl.nseg;
+        a.seg_chunks = pl.seg_chunks;
+        a.summ = pl.nseg > 1 ? reinterpret_cast<float*>(o.workspace) : nullptr;
+        a.snap = pl.nseg > 1 ? a.summ + (size_t)B * H * (pl.nseg - 1) * dk * (dk + dv) : nullptr;
+        if (pl.nseg > 1 && (reinterpret_cast<uintptr_t>(o.workspace) & 15u))
+            return fail(GDN_ERR_ARG, "workspace must be 16-byte aligned");
+        e = gdn::launch_walk(a, chunk, pl.waves, stream);
+    }
     if (e != hipSuccess) return fail(GDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return GDN_OK;
+}
+
+size_t workspace_for(int B, int H, int T, int dk, int dv, int chunk, const gdn_opts* opts) {
+    gdn_opts o;
+    if (opts) o = *opts; else defaults(&o);
+    if (B <= 0 || H <= 0 || T < 0 || !head_ok(dk) || !head_ok(dv)) return 0;
+    if (chunk != 32 && chunk != 64 && chunk != 128) return 0;
+    Plan pl = make_plan(o.in_dtype == GDN_F32, B, H, T, dk, dv, chunk);
+    return pl.ws_bytes;
 }
 
 }  // namespace
@@ -121,12 +189,11 @@ int gdn_fwd_chunked(const void* q, const void* k, const void* v, const void* alp
 int gdn_fwd_step(const void* q, const void* k, const void* v, const void* alpha, const void* beta,
                  const float* state_in, void* out, float* state_out,
                  int B, int H, int T, int dk, int dv, const gdn_opts* opts) {
-    return run(q, k, v, alpha, beta, state_in, out, state_out, B, H, T, dk, dv, 64, opts);
+    return run(q, k, v, alpha, beta, state_in, out, state_out, B, H, T, dk, dv, STEP_CHUNK, opts);
 }
 
 size_t gdn_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, const gdn_opts* opts) {
-    (void)B; (void)H; (void)T; (void)dk; (void)dv; (void)chunk; (void)opts;
-    return 0;
+    return workspace_for(B, H, T, dk, dv, chunk > 0 ? chunk : STEP_CHUNK, opts);
 }
 
 const char* gdn_strerror(int status) {

@@ -9,13 +9,10 @@ namespace gdn {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
 typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4v __attribute__((ext_vector_type(4)));
-
-// bf16 is carried as its raw 16 bits.
-struct bf16_t { uint16_t bits; };
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
     return __uint_as_float(((uint32_t)b) << 16);
@@ -34,23 +31,30 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 // 16x16 fp32 tile whose lane l holds rows 4*(l/16)+i (i<4) of column l%16.
 // Operand fragments: lane l supplies row (A) or column (B) l%16 and KPER
 // consecutive k values starting at (l/16)*KPER within a KSTEP-wide k block.
-// The k order inside a block is the same for A and B, so any hardware
-// permutation of k inside the instruction cancels in the dot product.
+// Both operands of a product are read with the same k order, so the
+// hardware's k order inside one instruction cancels in the dot product.
 // ---------------------------------------------------------------------------
 
 // fp16 operands (11-bit significand), fp32 accumulate: v_mfma_f32_16x16x32_f16
 struct OpF16 {
     typedef _Float16 elem;
     typedef u16x8 frag;
-    static constexpr int KSTEP = 32, KPER = 8;
+    typedef u16x4 frag16;   // K = 16 variant (v_mfma_f32_16x16x16_f16)
+    static constexpr int KSTEP = 32, KPER = 8, KPER16 = 4;
     __device__ static __forceinline__ f32x4 mma(const frag& a, const frag& b, f32x4 c) {
         return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
                                                       __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
     }
+    __device__ static __forceinline__ f32x4 mma16(const frag16& a, const frag16& b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                                     __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+    }
     __device__ static __forceinline__ elem from_f32(float x) { return (_Float16)x; }
-    __device__ static __forceinline__ float to_f32(elem x) { return (float)x; }
     __device__ static __forceinline__ frag load(const elem* p) {
         return *reinterpret_cast<const frag*>(p);
+    }
+    __device__ static __forceinline__ frag16 load16(const elem* p) {
+        return *reinterpret_cast<const frag16*>(p);
     }
 };
 
@@ -72,12 +76,12 @@ struct OpBF16 {
 struct OpF32 {
     typedef float elem;
     typedef float frag;
-    static constexpr int KSTEP = 4, KPER = 1;
+    typedef float frag16;
+    static constexpr int KSTEP = 4, KPER = 1, KPER16 = 1;
     __device__ static __forceinline__ f32x4 mma(const frag& a, const frag& b, f32x4 c) {
         return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
     }
     __device__ static __forceinline__ elem from_f32(float x) { return x; }
-    __device__ static __forceinline__ float to_f32(elem x) { return x; }
     __device__ static __forceinline__ frag load(const elem* p) { return *p; }
 };
 
@@ -90,5 +94,22 @@ __device__ __forceinline__ typename Op::frag frag_at(const typename Op::elem* ba
 }
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// 16x16 tile += A[16 x 16] * B[16 x 16] with A row-major (k contiguous) and B
+// stored column-major ([n][k], k contiguous), both in LDS.
+template <class Op>
+__device__ __forceinline__ f32x4 mm_k16(const typename Op::elem* a, int lda,
+                                        const typename Op::elem* b, int ldb, f32x4 acc, int lane) {
+    if constexpr (Op::KSTEP == 4) {
+#pragma unroll
+        for (int kb = 0; kb < 16; kb += 4)
+            acc = Op::mma(a[(lane & 15) * lda + kb + (lane >> 4)], b[(lane & 15) * ldb + kb + (lane >> 4)], acc);
+        return acc;
+    } else {
+        auto fa = Op::load16(a + (lane & 15) * lda + (lane >> 4) * Op::KPER16);
+        auto fb = Op::load16(b + (lane & 15) * ldb + (lane >> 4) * Op::KPER16);
+        return Op::mma16(fa, fb, acc);
+    }
+}
 
 }  // namespace gdn

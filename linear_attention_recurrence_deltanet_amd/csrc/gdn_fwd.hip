@@ -1,33 +1,46 @@
-// gdn_fwd.hip -- chunked Gated DeltaNet forward on gfx950 (MI355X).
+// gdn_fwd.hip -- chunked Gated DeltaNet forward on gfx950 (MI355X): the
+// segmented chunk walker used for 32- and 64-token chunks.
 //
-// The recurrence (token-wise gated delta rule; SANA-Streaming, paperpeel page,
-// section 2.1, Gated DeltaNet [35]; state carried across streaming chunks),
-// with the state stored transposed, M = S^T [dk][dv]:
-//     u_t = beta_t (v_t - alpha_t M^T k_t),   M <- alpha_t M + k_t u_t^T,
-//     o_t = M^T q_t                      (q_t, k_t unit-normalised)
+// Recurrence (token-wise gated delta rule; SANA-Streaming, paperpeel page,
+// section 2.1 with Gated DeltaNet [35]; the state is carried across streaming
+// chunks, section 2.1 and appendix G.6).  With the state stored transposed,
+// M = S^T of shape [dk][dv]:
+//     u_t = beta_t (v_t - alpha_t M^T k_t),  M <- alpha_t M + k_t u_t^T,
+//     o_t = M^T q_t                     (q_t, k_t unit-normalised)
 //
-// is evaluated a chunk of C tokens at a time (UT / WY form).  With
-// g_r = sum_{s<=r} log alpha_s inside the chunk, gam = exp(g),
-// G_rs = exp(g_r - g_s) (r >= s only, so every exponent is <= 0):
+// Chunk form (C tokens, incoming state M0, g_r = sum_{s<=r} log alpha_s,
+// gam = exp(g), G_rs = exp(g_r - g_s) for r >= s only, so exponents are <= 0):
 //     A  = diag(beta) strict_tril(K^ K^T .* G)
-//     T  = (I + A)^-1 diag(beta),    T2 = T diag(gam)
-//     W  = T2 K^ ,   Ut = T V,        U = Ut - W M0
+//     T  = (I + A)^-1 diag(beta),   T2 = T diag(gam)
+//     W  = T2 K^,  Ut = T V,  U = Ut - W M0
 //     O  = diag(gam) Q^ M0 + tril(Q^ K^T .* G) U
 //     M  = gam_C M0 + K^T diag(exp(g_C - g)) U
-// A partial last chunk behaves exactly as if padded with alpha = 1,
-// beta = 0, q = k = v = 0.
+// A partial chunk behaves as if padded with alpha = 1, beta = 0, q = k = v = 0.
 //
-// One workgroup (4 waves) owns one (batch, head, value-column tile of BV)
-// and walks the chunks in order; the fp32 state tile lives in registers for
-// the whole sequence (section 2.3 "Efficient GDN Kernel": the state stays on
-// chip while q/k/v stream from HBM).  Matrix products run on the matrix
-// cores: the Gram products on the raw bf16 inputs (exact operands), every
-// product with a computed operand in fp16 (11-bit significand) with fp32
-// accumulation; fp32 inputs use fp32 matrix-core products throughout.
+// Work decomposition (section 2.3 "Efficient GDN Kernel" keeps the state on
+// chip while q/k/v stream from HBM; here re-planned for 64-wide waves):
+//  * a workgroup walks the chunks of one sequence segment for one tile of
+//    16*NW value columns; wave w owns 16 of those columns, so the
+//    state-dependent chain (U, O, the state update) runs inside one wave with
+//    the fp32 state in its registers and no workgroup barrier;
+//  * the state-independent part of a chunk (norms, decay scan, Gram products,
+//    triangular solve, W and Ut) is shared by the waves through LDS; the next
+//    chunk's inputs are prefetched into registers meanwhile;
+//  * for few heads the sequence is cut into segments.  Because the map from a
+//    segment's incoming state to its outgoing state is affine,
+//    M_out = A_s M_in + B_s, a summary pass computes (A_s, B_s) for every
+//    segment but the last by running the same walk on identity columns (v = 0,
+//    M0 = I) and on the value columns (M0 = 0); the main pass then folds the
+//    predecessors' maps into its incoming state and walks its segment.
+// Matrix products: Gram products on the raw bf16 inputs with bf16 MFMA (exact
+// operands); products with a computed operand in fp16 (11-bit significand)
+// with fp32 accumulation; fp32 inputs use fp32 MFMA throughout.
 #include "gdn_common.h"
 #include "gdn_kernels.h"
 
 namespace gdn {
+
+namespace {
 
 template <class In> struct InTraits;
 template <> struct InTraits<uint16_t> {
@@ -39,50 +52,60 @@ template <> struct InTraits<float> {
     __device__ static __forceinline__ float to_f32(float x) { return x; }
 };
 
-__device__ __forceinline__ float warp_xor_sum(float v, int width) {
+__device__ __forceinline__ float group_sum(float v, int width) {
     for (int o = width >> 1; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
     return v;
 }
 
-template <int A_, int B_> struct cmax { static constexpr int v = A_ > B_ ? A_ : B_; };
-constexpr int align16(int x) { return (x + 15) & ~15; }
+constexpr int al16(int x) { return (x + 15) & ~15; }
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
-// Compile-time LDS plan of one workgroup.
-template <class In, class Op, int DK, int C, int BV>
-struct Plan {
+// Compile-time LDS plan.
+template <class In, class Op, int DK, int C, int NW>
+struct WPlan {
     typedef typename Op::elem E;
-    static constexpr int NB = C / 16;
-    static constexpr int PIN = 16 / (int)sizeof(In);
-    static constexpr int PE = 16 / (int)sizeof(E);
-    static constexpr int LDQ = DK + PIN;   // qraw / kraw rows
-    static constexpr int LDA = C + 4;      // fp32 A / X
-    static constexpr int LDT = C + PE;     // T, T2, P, Kt, Vt, Ut, U2t rows
-    static constexpr int LDW = DK + PE;    // W, Mt rows
-    // region X: phase-disjoint union
-    static constexpr int X_IN = 2 * C * LDQ * (int)sizeof(In);
-    static constexpr int X_A = C * LDA * 4;
-    static constexpr int X_T = 2 * C * LDT * (int)sizeof(E);
-    static constexpr int X_W = C * LDW * (int)sizeof(E);
-    static constexpr int X_U = 2 * BV * LDT * (int)sizeof(E);
-    static constexpr int SZ_X = align16(cmax<cmax<X_IN, X_A>::v, cmax<cmax<X_T, X_W>::v, X_U>::v>::v);
-    static constexpr int SZ_KT = align16(DK * LDT * (int)sizeof(E));
-    static constexpr int SZ_VT = align16(BV * LDT * (int)sizeof(E));
-    static constexpr int SZ_P = align16(C * LDT * (int)sizeof(E));
-    static constexpr int SZ_MT = align16(BV * LDW * (int)sizeof(E));
-    static constexpr int SZ_VEC = 6 * C * 4;
-    static constexpr int OFF_X = 0;
-    static constexpr int OFF_KT = OFF_X + SZ_X;
-    static constexpr int OFF_VT = OFF_KT + SZ_KT;
-    static constexpr int OFF_P = OFF_VT + SZ_VT;
-    static constexpr int OFF_MT = OFF_P + SZ_P;
-    static constexpr int OFF_VEC = OFF_MT + SZ_MT;
-    static constexpr int TOTAL = OFF_VEC + SZ_VEC;
+    static constexpr int BV = 16 * NW, NB = C / 16, NT = 64 * NW;
+    static constexpr int SI = (int)sizeof(In), SE = (int)sizeof(E);
+    static constexpr int LDQ = DK + 16 / SI;   // raw q / k rows
+    static constexpr int LDC = C + 16 / SE;    // rows of C elements
+    static constexpr int LDD = DK + 16 / SE;   // rows of DK elements
+    static constexpr int LDX = 16 + 16 / SE;   // rows of 16 elements
+    static constexpr int LDAD = 20;            // fp32 rows of 16 (+4)
+    // region R1: raw q/k (load..Gram) | solve scratch | W (W..chain) | fold A
+    static constexpr int R1_IN = 2 * C * LDQ * SI;
+    static constexpr int O_AOFF = 0;
+    static constexpr int O_TT = al16(O_AOFF + C * LDC * SE);
+    static constexpr int O_AD = al16(O_TT + C * LDC * SE);
+    static constexpr int O_XD = al16(O_AD + NB * 16 * LDAD * 4);
+    static constexpr int R1_SOLVE = al16(O_XD + NB * 16 * LDX * SE);
+    static constexpr int R1_W = C * LDD * SE;
+    static constexpr int R1_FOLD = DK * LDD * SE;
+    static constexpr int SZ_R1 = al16(cmax(cmax(R1_IN, R1_SOLVE), cmax(R1_W, R1_FOLD)));
+    static constexpr int OFF_KT = SZ_R1;                                  // K^T  [DK][LDC]
+    static constexpr int OFF_VT = OFF_KT + al16(DK * LDC * SE);           // V^T  [BV][LDC]
+    static constexpr int OFF_P = OFF_VT + al16(BV * LDC * SE);            // P    [C][LDC]
+    static constexpr int OFF_T = OFF_P + al16(C * LDC * SE);              // T    [C][LDC]
+    static constexpr int OFF_T2 = OFF_T + al16(C * LDC * SE);             // T2   [C][LDC]
+    static constexpr int OFF_VEC = OFF_T2 + al16(C * LDC * SE);           // 6 x C floats
+    static constexpr int OFF_WAVE = OFF_VEC + al16(6 * C * 4);
+    // per wave: M operand [16][LDD], U and eg.*U operands [16][LDC], Y [16][LDX]
+    static constexpr int W_MOP = 0;
+    static constexpr int W_UOP = al16(16 * LDD * SE);
+    static constexpr int W_U2OP = W_UOP + al16(16 * LDC * SE);
+    static constexpr int W_YS = W_U2OP + al16(16 * LDC * SE);
+    static constexpr int W_SIZE = W_YS + al16(16 * LDX * SE);
+    static constexpr int TOTAL = OFF_WAVE + NW * W_SIZE;
 };
 
-template <class In, class Op, int DK, int C, int BV>
-constexpr int lds_bytes() { return Plan<In, Op, DK, C, BV>::TOTAL; }
+template <class In, class Op, int DK, int C, int NW>
+constexpr bool walk_fits() { return WPlan<In, Op, DK, C, NW>::TOTAL <= 160 * 1024; }
 
-// Q^ operand fragment: raw input row scaled by its r_q, converted to Op.
+template <class E>
+__device__ __forceinline__ void st4(E* p, float a, float b, float c, float d) {
+    p[0] = (E)a; p[1] = (E)b; p[2] = (E)c; p[3] = (E)d;
+}
+
+// Q^ operand fragment from the raw input row, scaled by that row's r_q.
 template <class In, class Op>
 __device__ __forceinline__ typename Op::frag qhat_frag(const In* base, int ld, int row0, int kb,
                                                        int lane, float rq) {
@@ -100,45 +123,46 @@ __device__ __forceinline__ typename Op::frag qhat_frag(const In* base, int ld, i
     }
 }
 
-// Store 4 consecutive values of a row as Op elements.
-template <class E>
-__device__ __forceinline__ void st4(E* p, float a, float b, float c, float d) {
-    p[0] = (E)a; p[1] = (E)b; p[2] = (E)c; p[3] = (E)d;
-}
+}  // namespace
 
-template <class In, class Op, int DK, int C, int BV>
-__global__ __launch_bounds__(256)
-void gdn_fwd_seq_kernel(FwdArgs p) {
-    typedef Plan<In, Op, DK, C, BV> L;
+// ---------------------------------------------------------------------------
+// The walker.  SUMMARY = false: main pass (outputs, final state).
+//              SUMMARY = true : segment summaries (A_s, B_s), no outputs.
+// ---------------------------------------------------------------------------
+template <class In, class Op, int DK, int C, int NW, bool SUMMARY>
+__global__ __launch_bounds__(64 * NW)
+void gdn_walk_kernel(WalkArgs p) {
+    typedef WPlan<In, Op, DK, C, NW> L;
     typedef typename Op::elem E;
     typedef typename InTraits<In>::Gram GOp;
-    constexpr int NB = L::NB;
-    constexpr int NCB = BV / 16;                  // column blocks per tile
-    constexpr int NTO = NB * NCB;                 // O / U tiles  [C x BV]
-    constexpr int SO = (NTO + 3) / 4;
-    constexpr int NTM = (DK / 16) * NCB;          // state tiles  [DK x BV]
-    constexpr int SM = (NTM + 3) / 4;
-    constexpr int NTW = (DK / 16) * NB;           // W^T tiles    [DK x C]
-    constexpr int SW = (NTW + 3) / 4;
-    constexpr int NTG = NB * (NB + 1) / 2;        // lower-triangle Gram tiles
-    constexpr int SG = (NTG + 3) / 4;
-    constexpr int EPV = 16 / (int)sizeof(In);     // input elements per 16-byte load
-    constexpr int VPRQ = DK / EPV;                // 16-byte loads per q/k row
-    constexpr int VPRV = BV / EPV;                // 16-byte loads per v tile row
+    constexpr int NT = L::NT, BV = L::BV, NB = L::NB;
+    constexpr int NTG = NB * (NB + 1) / 2;            // lower-triangle 16x16 Gram tiles
+    constexpr int SG = (NTG + NW - 1) / NW;
+    constexpr int NDB = DK / 16;                      // 16-row blocks of the state
+    constexpr int NTW = NDB * NB;                     // W^T tiles
+    constexpr int SW = (NTW + NW - 1) / NW;
+    constexpr int EPV = 16 / (int)sizeof(In);         // input elements per 16-byte load
+    constexpr int VPRQ = DK / EPV;                    // 16-byte loads per q/k row
+    constexpr int VPRV = BV / EPV;                    // 16-byte loads per v row of the tile
+    constexpr int QV = C * VPRQ, QPT = (QV + NT - 1) / NT;
+    constexpr int VV = C * VPRV, VPT = (VV + NT - 1) / NT;
+    constexpr int TPL = C >= 64 ? C / 64 : 1;         // decay tokens per lane of wave 0
+    constexpr bool LOADQ = !SUMMARY;
 
     __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
-    In* qraw = reinterpret_cast<In*>(smem + L::OFF_X);
+    In* qraw = reinterpret_cast<In*>(smem);
     In* kraw = qraw + C * L::LDQ;
-    float* Am = reinterpret_cast<float*>(smem + L::OFF_X);
-    E* Tm = reinterpret_cast<E*>(smem + L::OFF_X);
-    E* T2m = Tm + C * L::LDT;
-    E* Wm = reinterpret_cast<E*>(smem + L::OFF_X);
-    E* Ut = reinterpret_cast<E*>(smem + L::OFF_X);
-    E* U2t = Ut + BV * L::LDT;
+    E* Aoff = reinterpret_cast<E*>(smem + L::O_AOFF);
+    E* Tt = reinterpret_cast<E*>(smem + L::O_TT);
+    float* Adt = reinterpret_cast<float*>(smem + L::O_AD);
+    E* Xd = reinterpret_cast<E*>(smem + L::O_XD);
+    E* Wn = reinterpret_cast<E*>(smem);
+    E* Afold = reinterpret_cast<E*>(smem);
     E* Kt = reinterpret_cast<E*>(smem + L::OFF_KT);
     E* Vt = reinterpret_cast<E*>(smem + L::OFF_VT);
     E* Pm = reinterpret_cast<E*>(smem + L::OFF_P);
-    E* Mt = reinterpret_cast<E*>(smem + L::OFF_MT);
+    E* Tm = reinterpret_cast<E*>(smem + L::OFF_T);
+    E* T2m = reinterpret_cast<E*>(smem + L::OFF_T2);
     float* v_rq = reinterpret_cast<float*>(smem + L::OFF_VEC);
     float* v_rk = v_rq + C;
     float* v_g2 = v_rk + C;
@@ -149,104 +173,217 @@ void gdn_fwd_seq_kernel(FwdArgs p) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int ntile = p.dv / BV;
-    const int tile = blockIdx.x % ntile;
-    const int bh = blockIdx.x / ntile;
-    const int col0 = tile * BV;
+    const int lc = lane & 15;          // column (or row) within a 16-wide block
+    const int lg = lane >> 4;          // lane group 0..3
+    char* wbase = smem + L::OFF_WAVE + wave * L::W_SIZE;
+    E* Mop = reinterpret_cast<E*>(wbase + L::W_MOP);     // [16 cols][DK]
+    E* Uop = reinterpret_cast<E*>(wbase + L::W_UOP);     // [16 cols][C]
+    E* U2op = reinterpret_cast<E*>(wbase + L::W_U2OP);   // [16 cols][C]
+    E* Ys = reinterpret_cast<E*>(wbase + L::W_YS);       // [16][16]
+
     const int T = p.T, dv = p.dv;
+    const int nseg = p.nseg;
+    const int nsum = nseg - 1;
+    // workgroup -> (bh, seg, column tile)
+    int bh, seg, ctile, ncol;
+    if constexpr (SUMMARY) {
+        ncol = (DK + dv) / BV;
+        ctile = blockIdx.x % ncol;
+        const int r = blockIdx.x / ncol;
+        seg = r % nsum;
+        bh = r / nsum;
+    } else {
+        ncol = dv / BV;
+        ctile = blockIdx.x % ncol;
+        const int r = blockIdx.x / ncol;
+        seg = r % nseg;
+        bh = r / nseg;
+    }
+    const bool ident = SUMMARY && ctile < DK / BV;       // identity columns of A_s
+    const int vcol0 = SUMMARY ? (ident ? 0 : (ctile - DK / BV) * BV) : ctile * BV;
+    const int mycol = 16 * wave + lc;                    // this lane's column in the tile
+
+    const int nchunks = (T + C - 1) / C;
+    const int ch0 = seg * p.seg_chunks;
+    const int ch1 = min(nchunks, ch0 + p.seg_chunks);
 
     const In* qg = reinterpret_cast<const In*>(p.q) + (size_t)bh * T * DK;
     const In* kg = reinterpret_cast<const In*>(p.k) + (size_t)bh * T * DK;
     const In* vg = reinterpret_cast<const In*>(p.v) + (size_t)bh * T * dv;
     const In* ag = reinterpret_cast<const In*>(p.alpha) + (size_t)bh * T;
     const In* bg = reinterpret_cast<const In*>(p.beta) + (size_t)bh * T;
+    const size_t sstride = (size_t)DK * (DK + dv);      // one segment summary
+    float* summ_bh = p.summ + (size_t)bh * nsum * sstride;
 
-    // P above the diagonal blocks is structurally zero: clear it once.
-    for (int e = tid; e < C * C; e += 256) {
-        int r = e / C, s = e % C;
-        if ((s >> 4) > (r >> 4)) Pm[r * L::LDT + s] = (E)0.f;
-    }
-
-    // Initial state tile -> registers (fp32) and Mt (operand copy).
-    f32x4 Macc[SM];
-#pragma unroll
-    for (int sl = 0; sl < SM; ++sl) {
-        const int t = wave + 4 * sl;
-        Macc[sl] = zero4();
-        if (t < NTM) {
-            const int i0 = (t / NCB) * 16 + 4 * (lane >> 4);
-            const int c = (t % NCB) * 16 + (lane & 15);
-            if (p.state_in) {
-                const float* sp = p.state_in + (size_t)bh * DK * dv + col0 + c;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) Macc[sl][i] = sp[(size_t)(i0 + i) * dv];
-            }
-            st4(Mt + c * L::LDW + i0, Macc[sl][0], Macc[sl][1], Macc[sl][2], Macc[sl][3]);
+    // Structurally zero parts of the persistent matrices (upper blocks).
+    for (int e = tid; e < C * C; e += NT) {
+        const int r = e / C, s = e % C;
+        if ((s >> 4) > (r >> 4)) {
+            Pm[r * L::LDC + s] = (E)0.f;
+            Tm[r * L::LDC + s] = (E)0.f;
+            T2m[r * L::LDC + s] = (E)0.f;
         }
     }
-    __syncthreads();
 
-    const int nchunks = (T + C - 1) / C;
-    for (int ch = 0; ch < nchunks; ++ch) {
+    // ---------------- incoming state (fp32 registers + fp16 operand) ------
+    f32x4 Macc[NDB];
+#pragma unroll
+    for (int ib = 0; ib < NDB; ++ib) Macc[ib] = zero4();
+    if constexpr (SUMMARY) {
+        if (ident) {
+            const int cidx = vcol0 + ctile * BV + mycol;     // identity column index
+#pragma unroll
+            for (int ib = 0; ib < NDB; ++ib)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) Macc[ib][i] = (16 * ib + 4 * lg + i == cidx) ? 1.f : 0.f;
+        } else if (seg == 0 && p.snap && p.state_in) {
+            // snapshot of the incoming state for the main pass (state_in may alias state_out)
+            const float* sp = p.state_in + (size_t)bh * DK * dv + vcol0 + mycol;
+            float* dp = p.snap + (size_t)bh * DK * dv + vcol0 + mycol;
+            for (int i = lg; i < DK; i += 4) dp[(size_t)i * dv] = sp[(size_t)i * dv];
+        }
+    } else {
+        const float* sinp = nseg > 1 ? (p.state_in ? p.snap : nullptr) : p.state_in;
+        if (sinp) {
+            const float* sp = sinp + (size_t)bh * DK * dv + vcol0 + mycol;
+#pragma unroll
+            for (int ib = 0; ib < NDB; ++ib)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) Macc[ib][i] = sp[(size_t)(16 * ib + 4 * lg + i) * dv];
+        }
+    }
+#pragma unroll
+    for (int ib = 0; ib < NDB; ++ib)
+        st4(Mop + lc * L::LDD + 16 * ib + 4 * lg, Macc[ib][0], Macc[ib][1], Macc[ib][2], Macc[ib][3]);
+
+    if constexpr (!SUMMARY) {
+        // fold the maps of the preceding segments: M <- A_s M + B_s
+        for (int s2 = 0; s2 < seg; ++s2) {
+            const float* Ag = summ_bh + (size_t)s2 * sstride;
+            __syncthreads();                                  // Afold free
+            for (int e = tid * 4; e < DK * DK; e += NT * 4) {
+                const int i = e / DK, j = e % DK;
+                f32x4 a4 = *reinterpret_cast<const f32x4*>(Ag + (size_t)i * (DK + dv) + j);
+                st4(Afold + i * L::LDD + j, a4[0], a4[1], a4[2], a4[3]);
+            }
+            __syncthreads();
+#pragma unroll
+            for (int ib = 0; ib < NDB; ++ib) {
+                f32x4 acc;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    acc[i] = Ag[(size_t)(16 * ib + 4 * lg + i) * (DK + dv) + DK + vcol0 + mycol];
+#pragma unroll
+                for (int kb = 0; kb < DK; kb += Op::KSTEP)
+                    acc = Op::mma(frag_at<Op>(Afold, L::LDD, 16 * ib, kb, lane),
+                                  frag_at<Op>(Mop, L::LDD, 0, kb, lane), acc);
+                Macc[ib] = acc;
+            }
+#pragma unroll
+            for (int ib = 0; ib < NDB; ++ib)
+                st4(Mop + lc * L::LDD + 16 * ib + 4 * lg, Macc[ib][0], Macc[ib][1], Macc[ib][2], Macc[ib][3]);
+        }
+        if (seg > 0) __syncthreads();                         // Afold (region R1) dead
+    }
+
+    // ---------------- register prefetch of one chunk ----------------------
+    uint4 pq[LOADQ ? QPT : 1], pk[QPT], pv[VPT];
+    float pa[TPL], pb[TPL];
+    auto prefetch = [&](int ch) {
+        const int t0 = ch * C;
+        const int n = min(C, T - t0);
+#pragma unroll
+        for (int it = 0; it < QPT; ++it) {
+            const int idx = tid + NT * it;
+            const int r = idx / VPRQ, part = idx % VPRQ;
+            const bool ok = idx < QV && r < n;
+            const size_t off = (size_t)(t0 + r) * DK + part * EPV;
+            pk[it] = ok ? *reinterpret_cast<const uint4*>(kg + off) : make_uint4(0, 0, 0, 0);
+            if constexpr (LOADQ)
+                pq[it] = ok ? *reinterpret_cast<const uint4*>(qg + off) : make_uint4(0, 0, 0, 0);
+        }
+        if (!ident) {
+#pragma unroll
+            for (int it = 0; it < VPT; ++it) {
+                const int idx = tid + NT * it;
+                const int r = idx / VPRV, part = idx % VPRV;
+                const bool ok = idx < VV && r < n;
+                pv[it] = ok ? *reinterpret_cast<const uint4*>(vg + (size_t)(t0 + r) * dv + vcol0 + part * EPV)
+                            : make_uint4(0, 0, 0, 0);
+            }
+        }
+        if (wave == 0) {
+#pragma unroll
+            for (int e = 0; e < TPL; ++e) {
+                const int r = lane * TPL + e;
+                const bool ok = r < n;
+                pa[e] = ok ? InTraits<In>::to_f32(ag[t0 + r]) : 1.f;
+                pb[e] = ok ? InTraits<In>::to_f32(bg[t0 + r]) : 0.f;
+            }
+        }
+    };
+    if (ch0 < ch1) prefetch(ch0);
+
+    for (int ch = ch0; ch < ch1; ++ch) {
         const int t0 = ch * C;
         const int n = min(C, T - t0);
 
-        // ---- phase 1: stage q, k (raw), v^T; per-token norms; decay scan ----
-        for (int it = tid; it < C * VPRQ; it += 256) {
-            const int r = it / VPRQ, part = it % VPRQ;
-            uint4 rq4 = make_uint4(0, 0, 0, 0), rk4 = make_uint4(0, 0, 0, 0);
-            if (r < n) {
-                rq4 = *reinterpret_cast<const uint4*>(qg + (size_t)(t0 + r) * DK + part * EPV);
-                rk4 = *reinterpret_cast<const uint4*>(kg + (size_t)(t0 + r) * DK + part * EPV);
-            }
-            const In* qe = reinterpret_cast<const In*>(&rq4);
-            const In* ke = reinterpret_cast<const In*>(&rk4);
-            float sq = 0.f, sk = 0.f;
+        // ---- P1: staged inputs, norms, K^T, V^T, decay scan; prefetch next ----
 #pragma unroll
-            for (int e = 0; e < EPV; ++e) {
-                float a = InTraits<In>::to_f32(qe[e]), b = InTraits<In>::to_f32(ke[e]);
-                sq += a * a; sk += b * b;
-            }
-            sq = warp_xor_sum(sq, VPRQ);
-            sk = warp_xor_sum(sk, VPRQ);
-            const float rq = p.qk_l2norm ? p.scale / sqrtf(sq + p.eps) : p.scale;
-            const float rk = p.qk_l2norm ? 1.0f / sqrtf(sk + p.eps) : 1.0f;
-            *reinterpret_cast<uint4*>(qraw + r * L::LDQ + part * EPV) = rq4;
-            *reinterpret_cast<uint4*>(kraw + r * L::LDQ + part * EPV) = rk4;
+        for (int it = 0; it < QPT; ++it) {
+            const int idx = tid + NT * it;
+            if (idx < QV) {                           // whole waves in or out
+                const int r = idx / VPRQ, part = idx % VPRQ;
+                const In* ke = reinterpret_cast<const In*>(&pk[it]);
+                float sk = 0.f, sq = 0.f;
 #pragma unroll
-            for (int e = 0; e < EPV; ++e)
-                Kt[(part * EPV + e) * L::LDT + r] = Op::from_f32(InTraits<In>::to_f32(ke[e]) * rk);
-            if (part == 0) { v_rq[r] = rq; v_rk[r] = rk; }
+                for (int e = 0; e < EPV; ++e) { float b = InTraits<In>::to_f32(ke[e]); sk += b * b; }
+                if constexpr (LOADQ) {
+                    const In* qe = reinterpret_cast<const In*>(&pq[it]);
+#pragma unroll
+                    for (int e = 0; e < EPV; ++e) { float a = InTraits<In>::to_f32(qe[e]); sq += a * a; }
+                    sq = group_sum(sq, VPRQ);
+                    *reinterpret_cast<uint4*>(qraw + r * L::LDQ + part * EPV) = pq[it];
+                }
+                sk = group_sum(sk, VPRQ);
+                const float rk = p.qk_l2norm ? 1.0f / sqrtf(sk + p.eps) : 1.0f;
+                *reinterpret_cast<uint4*>(kraw + r * L::LDQ + part * EPV) = pk[it];
+#pragma unroll
+                for (int e = 0; e < EPV; ++e)
+                    Kt[(part * EPV + e) * L::LDC + r] = Op::from_f32(InTraits<In>::to_f32(ke[e]) * rk);
+                if (part == 0) {
+                    v_rk[r] = rk;
+                    if constexpr (LOADQ) v_rq[r] = p.qk_l2norm ? p.scale / sqrtf(sq + p.eps) : p.scale;
+                }
+            }
         }
-        for (int it = tid; it < C * VPRV; it += 256) {
-            const int r = it / VPRV, part = it % VPRV;
-            uint4 rv4 = make_uint4(0, 0, 0, 0);
-            if (r < n)
-                rv4 = *reinterpret_cast<const uint4*>(vg + (size_t)(t0 + r) * dv + col0 + part * EPV);
-            const In* ve = reinterpret_cast<const In*>(&rv4);
+        if (!ident) {
 #pragma unroll
-            for (int e = 0; e < EPV; ++e)
-                Vt[(part * EPV + e) * L::LDT + r] = Op::from_f32(InTraits<In>::to_f32(ve[e]));
+            for (int it = 0; it < VPT; ++it) {
+                const int idx = tid + NT * it;
+                if (idx < VV) {
+                    const int r = idx / VPRV, part = idx % VPRV;
+                    const In* ve = reinterpret_cast<const In*>(&pv[it]);
+#pragma unroll
+                    for (int e = 0; e < EPV; ++e)
+                        Vt[(part * EPV + e) * L::LDC + r] = Op::from_f32(InTraits<In>::to_f32(ve[e]));
+                }
+            }
         }
         if (wave == 0) {
-            constexpr int TPL = C >= 64 ? C / 64 : 1;   // tokens per lane
-            float la[TPL], be[TPL];
+            float la[TPL];
             float run = 0.f;
 #pragma unroll
             for (int e = 0; e < TPL; ++e) {
                 const int r = lane * TPL + e;
-                float a = 1.f, b = 0.f;
-                if (r < n) { a = InTraits<In>::to_f32(ag[t0 + r]); b = InTraits<In>::to_f32(bg[t0 + r]); }
-                // log2(0) = -inf would make g_r - g_s undefined; 2^-200 is 0 in fp32 anyway.
-                float l2 = (r < C) ? fmaxf(log2f(a), -200.f) : 0.f;
-                run += l2;
+                // log2(0) would make g_r - g_s undefined; 2^-200 is 0 in fp32 anyway
+                run += (r < C) ? fmaxf(log2f(pa[e]), -200.f) : 0.f;
                 la[e] = run;
-                be[e] = b;
             }
             float incl = run;
 #pragma unroll
             for (int o = 1; o < 64; o <<= 1) {
-                float y = __shfl_up(incl, o, 64);
+                const float y = __shfl_up(incl, o, 64);
                 if (lane >= o) incl += y;
             }
             const float excl = incl - run;
@@ -259,17 +396,18 @@ void gdn_fwd_seq_kernel(FwdArgs p) {
                     v_g2[r] = g;
                     v_gam[r] = exp2f(g);
                     v_eg[r] = exp2f(gtot - g);
-                    v_beta[r] = be[e];
+                    v_beta[r] = pb[e];
                 }
             }
         }
+        if (ch + 1 < ch1) prefetch(ch + 1);
         __syncthreads();
 
-        // ---- phase 2: Gram products (lower triangle) and O = gam .* (Q^ M0) ----
+        // ---- P2: Gram products (lower tiles); O = gam .* (Q^ M0) -------------
         f32x4 Areg[SG];
 #pragma unroll
         for (int sl = 0; sl < SG; ++sl) {
-            const int t = wave + 4 * sl;
+            const int t = wave + NW * sl;
             Areg[sl] = zero4();
             if (t < NTG) {
                 int I = 0;
@@ -279,283 +417,200 @@ void gdn_fwd_seq_kernel(FwdArgs p) {
 #pragma unroll
                 for (int kb = 0; kb < DK; kb += GOp::KSTEP) {
                     auto a = frag_at<GOp>(kraw, L::LDQ, 16 * J, kb, lane);
-                    auto bk = frag_at<GOp>(kraw, L::LDQ, 16 * I, kb, lane);
-                    auto bq = frag_at<GOp>(qraw, L::LDQ, 16 * I, kb, lane);
-                    kk = GOp::mma(a, bk, kk);
-                    kq = GOp::mma(a, bq, kq);
+                    kk = GOp::mma(a, frag_at<GOp>(kraw, L::LDQ, 16 * I, kb, lane), kk);
+                    if constexpr (!SUMMARY) kq = GOp::mma(a, frag_at<GOp>(qraw, L::LDQ, 16 * I, kb, lane), kq);
                 }
-                // element i: row s = 16J + 4(lane/16) + i, column r = 16I + lane%16
-                const int r = 16 * I + (lane & 15);
-                const int s0 = 16 * J + 4 * (lane >> 4);
-                const float br = v_beta[r], rkr = v_rk[r], rqr = v_rq[r], gr = v_g2[r];
-                float pv[4];
+                // element i: row s = 16J + 4 lg + i, column r = 16I + lc
+                const int r = 16 * I + lc;
+                const int s0 = 16 * J + 4 * lg;
+                const float br = v_beta[r], rkr = v_rk[r], gr = v_g2[r];
+                float pv4[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int s = s0 + i;
                     const float rks = v_rk[s];
                     const float e = (s <= r) ? exp2f(gr - v_g2[s]) : 0.f;
                     Areg[sl][i] = (s < r) ? br * rkr * rks * kk[i] * e : 0.f;
-                    pv[i] = rqr * rks * kq[i] * e;
+                    if constexpr (!SUMMARY) pv4[i] = v_rq[r] * rks * kq[i] * e;
                 }
-                st4(Pm + r * L::LDT + s0, pv[0], pv[1], pv[2], pv[3]);
+                if constexpr (!SUMMARY) st4(Pm + r * L::LDC + s0, pv4[0], pv4[1], pv4[2], pv4[3]);
             }
         }
-        f32x4 Oacc[SO];
+        f32x4 Oacc[NB];
+        if constexpr (!SUMMARY) {
 #pragma unroll
-        for (int sl = 0; sl < SO; ++sl) {
-            const int t = wave + 4 * sl;
-            Oacc[sl] = zero4();
-            if (t < NTO) {
-                const int rb = t / NCB, cb = t % NCB;
-                const float rq = v_rq[16 * rb + (lane & 15)];
+            for (int rb = 0; rb < NB; ++rb) {
+                const float rq = v_rq[16 * rb + lc];
                 f32x4 acc = zero4();
 #pragma unroll
-                for (int kb = 0; kb < DK; kb += Op::KSTEP) {
-                    auto a = qhat_frag<In, Op>(qraw, L::LDQ, 16 * rb, kb, lane, rq);
-                    auto b = frag_at<Op>(Mt, L::LDW, 16 * cb, kb, lane);
-                    acc = Op::mma(a, b, acc);
-                }
+                for (int kb = 0; kb < DK; kb += Op::KSTEP)
+                    acc = Op::mma(qhat_frag<In, Op>(qraw, L::LDQ, 16 * rb, kb, lane, rq),
+                                  frag_at<Op>(Mop, L::LDD, 0, kb, lane), acc);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) Oacc[sl][i] = acc[i] * v_gam[16 * rb + 4 * (lane >> 4) + i];
+                for (int i = 0; i < 4; ++i) Oacc[rb][i] = acc[i] * v_gam[16 * rb + 4 * lg + i];
             }
         }
-        __syncthreads();
+        __syncthreads();                                   // raw q/k dead: R1 -> solve scratch
 #pragma unroll
         for (int sl = 0; sl < SG; ++sl) {
-            const int t = wave + 4 * sl;
+            const int t = wave + NW * sl;
             if (t < NTG) {
                 int I = 0;
                 while ((I + 1) * (I + 2) / 2 <= t) ++I;
                 const int J = t - I * (I + 1) / 2;
-                const int r = 16 * I + (lane & 15);
-                const int s0 = 16 * J + 4 * (lane >> 4);
-                *reinterpret_cast<f32x4*>(Am + r * L::LDA + s0) = Areg[sl];
+                if (I == J) {
+                    // diagonal block, stored transposed: Adt[I][s][r] = A[r][s]
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) Adt[(16 * I + 4 * lg + i) * L::LDAD + lc] = Areg[sl][i];
+                } else {
+                    st4(Aoff + (16 * I + lc) * L::LDC + 16 * J + 4 * lg,
+                        Areg[sl][0], Areg[sl][1], Areg[sl][2], Areg[sl][3]);
+                }
             }
         }
         __syncthreads();
 
-        // ---- phase 3: X = (I + A)^-1, blocked by 16 ----
-        // 3a: diagonal blocks by forward substitution, one lane per column.
-        if (tid < NB * 16) {
-            const int R0 = (tid >> 4) * 16, j = tid & 15;
+        // ---- P3: T = (I + A)^-1 diag(beta) ----------------------------------
+        // diagonal 16x16 blocks: column elimination, one lane per column
+        if (tid < C) {
+            const int b = tid >> 4, j = tid & 15;
             float x[16];
 #pragma unroll
+            for (int r = 0; r < 16; ++r) x[r] = (r == j) ? 1.f : 0.f;
+#pragma unroll
+            for (int s = 0; s < 15; ++s) {
+                const float* col = Adt + (16 * b + s) * L::LDAD;   // A[16b + r][16b + s], r = 0..15
+                const float xs = x[s];
+#pragma unroll
+                for (int r = s + 1; r < 16; ++r) x[r] -= col[r] * xs;
+            }
+            const int c = 16 * b + j;
+            const float bc = v_beta[c], gc = v_gam[c];
+#pragma unroll
             for (int r = 0; r < 16; ++r) {
-                float acc = 0.f;
-                const float* arow = Am + (R0 + r) * L::LDA + R0;
-#pragma unroll
-                for (int s = 0; s < r; ++s) acc += arow[s] * x[s];
-                x[r] = (r < j) ? 0.f : (r == j ? 1.f : -acc);
-            }
-#pragma unroll
-            for (int r = 0; r < 16; ++r) Am[(R0 + r) * L::LDA + R0 + j] = x[r];
-        }
-        __syncthreads();
-        // 3b: block rows below: X_ij = -X_ii sum_{k=j}^{i-1} A_ik X_kj.
-        {
-            const int a = tid >> 4, bc = tid & 15;
-#pragma unroll
-            for (int lev = 1; lev < NB; ++lev) {
-                float R[NB > 1 ? NB - 1 : 1];
-#pragma unroll
-                for (int m = 0; m < lev; ++m) {
-                    float acc = 0.f;
-                    const float* arow = Am + (16 * lev + a) * L::LDA;
-                    for (int kk = m; kk < lev; ++kk) {
-#pragma unroll
-                        for (int c = 0; c < 16; ++c)
-                            acc += arow[16 * kk + c] * Am[(16 * kk + c) * L::LDA + 16 * m + bc];
-                    }
-                    R[m] = acc;
-                }
-                __syncthreads();
-#pragma unroll
-                for (int m = 0; m < lev; ++m) Am[(16 * lev + a) * L::LDA + 16 * m + bc] = R[m];
-                __syncthreads();
-#pragma unroll
-                for (int m = 0; m < lev; ++m) {
-                    float acc = 0.f;
-                    const float* xrow = Am + (16 * lev + a) * L::LDA + 16 * lev;
-#pragma unroll
-                    for (int c = 0; c < 16; ++c)
-                        acc += xrow[c] * Am[(16 * lev + c) * L::LDA + 16 * m + bc];
-                    R[m] = -acc;
-                }
-                __syncthreads();
-#pragma unroll
-                for (int m = 0; m < lev; ++m) Am[(16 * lev + a) * L::LDA + 16 * m + bc] = R[m];
-                __syncthreads();
-            }
-        }
-        // 3c: T = X diag(beta), T2 = T diag(gam), as matrix-core operands.
-        {
-            constexpr int NQ = C * C / 4 / 256 > 0 ? C * C / 4 / 256 : 1;
-            f32x4 xv[NQ];
-#pragma unroll
-            for (int m = 0; m < NQ; ++m) {
-                const int e = (tid + 256 * m) * 4;
-                xv[m] = zero4();
-                if (e < C * C) {
-                    const int r = e / C, s0 = e % C;
-                    f32x4 x = *reinterpret_cast<const f32x4*>(Am + r * L::LDA + s0);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) xv[m][i] = (s0 + i <= r) ? x[i] : 0.f;
-                }
-            }
-            __syncthreads();
-#pragma unroll
-            for (int m = 0; m < NQ; ++m) {
-                const int e = (tid + 256 * m) * 4;
-                if (e < C * C) {
-                    const int r = e / C, s0 = e % C;
-                    float t[4], t2[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        t[i] = xv[m][i] * v_beta[s0 + i];
-                        t2[i] = t[i] * v_gam[s0 + i];
-                    }
-                    st4(Tm + r * L::LDT + s0, t[0], t[1], t[2], t[3]);
-                    st4(T2m + r * L::LDT + s0, t2[0], t2[1], t2[2], t2[3]);
-                }
+                const float t = x[r] * bc;
+                Tm[(16 * b + r) * L::LDC + c] = (E)t;
+                T2m[(16 * b + r) * L::LDC + c] = (E)(t * gc);
+                Tt[c * L::LDC + 16 * b + r] = (E)t;
+                Xd[(16 * b + r) * L::LDX + j] = (E)x[r];
             }
         }
         __syncthreads();
-
-        // ---- phase 4: W^T = K^T T2^T (stored negated), Ut = T V ----
-        f32x4 Wreg[SW];
+        // block rows below: T_ij = -X_ii sum_{k=j}^{i-1} A_ik T_kj
 #pragma unroll
-        for (int sl = 0; sl < SW; ++sl) {
-            const int t = wave + 4 * sl;
-            Wreg[sl] = zero4();
-            if (t < NTW) {
-                const int ib = t / NB, rb = t % NB;
-                f32x4 acc = zero4();
-#pragma unroll
-                for (int kb = 0; kb < C; kb += Op::KSTEP) {
-                    auto a = frag_at<Op>(Kt, L::LDT, 16 * ib, kb, lane);
-                    auto b = frag_at<Op>(T2m, L::LDT, 16 * rb, kb, lane);
-                    acc = Op::mma(a, b, acc);
-                }
-                Wreg[sl] = acc;
-            }
-        }
-        f32x4 Uacc[SO];
-#pragma unroll
-        for (int sl = 0; sl < SO; ++sl) {
-            const int t = wave + 4 * sl;
-            Uacc[sl] = zero4();
-            if (t < NTO) {
-                const int rb = t / NCB, cb = t % NCB;
-                f32x4 acc = zero4();
-#pragma unroll
-                for (int kb = 0; kb < C; kb += Op::KSTEP) {
-                    auto a = frag_at<Op>(Tm, L::LDT, 16 * rb, kb, lane);
-                    auto b = frag_at<Op>(Vt, L::LDT, 16 * cb, kb, lane);
-                    acc = Op::mma(a, b, acc);
-                }
-                Uacc[sl] = acc;
-            }
-        }
-        __syncthreads();
-#pragma unroll
-        for (int sl = 0; sl < SW; ++sl) {
-            const int t = wave + 4 * sl;
-            if (t < NTW) {
-                const int ib = t / NB, rb = t % NB;
-                const int r = 16 * rb + (lane & 15);
-                const int i0 = 16 * ib + 4 * (lane >> 4);
-                st4(Wm + r * L::LDW + i0, -Wreg[sl][0], -Wreg[sl][1], -Wreg[sl][2], -Wreg[sl][3]);
-            }
-        }
-        __syncthreads();
-
-        // ---- phase 5: U = Ut - W M0; O += P U; M = gam_C M0 + K^T (eg .* U) ----
-#pragma unroll
-        for (int sl = 0; sl < SO; ++sl) {
-            const int t = wave + 4 * sl;
-            if (t < NTO) {
-                const int rb = t / NCB, cb = t % NCB;
-#pragma unroll
-                for (int kb = 0; kb < DK; kb += Op::KSTEP) {
-                    auto a = frag_at<Op>(Wm, L::LDW, 16 * rb, kb, lane);
-                    auto b = frag_at<Op>(Mt, L::LDW, 16 * cb, kb, lane);
-                    Uacc[sl] = Op::mma(a, b, Uacc[sl]);
-                }
-            }
-        }
-        __syncthreads();
-#pragma unroll
-        for (int sl = 0; sl < SO; ++sl) {
-            const int t = wave + 4 * sl;
-            if (t < NTO) {
-                const int rb = t / NCB, cb = t % NCB;
-                const int c = 16 * cb + (lane & 15);
-                const int r0 = 16 * rb + 4 * (lane >> 4);
-                st4(Ut + c * L::LDT + r0, Uacc[sl][0], Uacc[sl][1], Uacc[sl][2], Uacc[sl][3]);
-                st4(U2t + c * L::LDT + r0, Uacc[sl][0] * v_eg[r0], Uacc[sl][1] * v_eg[r0 + 1],
-                    Uacc[sl][2] * v_eg[r0 + 2], Uacc[sl][3] * v_eg[r0 + 3]);
-            }
-        }
-        __syncthreads();
-#pragma unroll
-        for (int sl = 0; sl < SO; ++sl) {
-            const int t = wave + 4 * sl;
-            if (t < NTO) {
-                const int rb = t / NCB, cb = t % NCB;
-#pragma unroll
-                for (int kb = 0; kb < C; kb += Op::KSTEP) {
-                    auto a = frag_at<Op>(Pm, L::LDT, 16 * rb, kb, lane);
-                    auto b = frag_at<Op>(Ut, L::LDT, 16 * cb, kb, lane);
-                    Oacc[sl] = Op::mma(a, b, Oacc[sl]);
-                }
-                const int c = col0 + 16 * cb + (lane & 15);
-                const int r0 = 16 * rb + 4 * (lane >> 4);
+        for (int lev = 1; lev < NB; ++lev) {
+            for (int j = wave; j < lev; j += NW) {
+                f32x4 y = zero4();
+                for (int k = j; k < lev; ++k)
+                    y = mm_k16<Op>(Aoff + (16 * lev) * L::LDC + 16 * k, L::LDC,
+                                   Tt + (16 * j) * L::LDC + 16 * k, L::LDC, y, lane);
+                // Y (rows c' = 4 lg + i, column c = lc) -> [c][c'] operand
+                st4(Ys + lc * L::LDX + 4 * lg, y[0], y[1], y[2], y[3]);
+                f32x4 t = mm_k16<Op>(Xd + (16 * lev) * L::LDX, L::LDX, Ys, L::LDX, zero4(), lane);
+                const int c = 16 * j + lc;
+                const float gc = v_gam[c];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int r = r0 + i;
+                    const int r = 16 * lev + 4 * lg + i;
+                    Tm[r * L::LDC + c] = (E)(-t[i]);
+                    T2m[r * L::LDC + c] = (E)(-t[i] * gc);
+                }
+                st4(Tt + c * L::LDC + 16 * lev + 4 * lg, -t[0], -t[1], -t[2], -t[3]);
+            }
+            __syncthreads();
+        }
+
+        // ---- P4: W^T = K^T T2^T (stored negated), Ut = T V -----------------
+#pragma unroll
+        for (int sl = 0; sl < SW; ++sl) {
+            const int t = wave + NW * sl;
+            if (t < NTW) {
+                const int ib = t / NB, rb = t % NB;
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int kb = 0; kb < C; kb += Op::KSTEP)
+                    acc = Op::mma(frag_at<Op>(Kt, L::LDC, 16 * ib, kb, lane),
+                                  frag_at<Op>(T2m, L::LDC, 16 * rb, kb, lane), acc);
+                st4(Wn + (16 * rb + lc) * L::LDD + 16 * ib + 4 * lg, -acc[0], -acc[1], -acc[2], -acc[3]);
+            }
+        }
+        f32x4 Uacc[NB];
+#pragma unroll
+        for (int rb = 0; rb < NB; ++rb) {
+            f32x4 acc = zero4();
+            if (!ident) {
+#pragma unroll
+                for (int kb = 0; kb < C; kb += Op::KSTEP)
+                    acc = Op::mma(frag_at<Op>(Tm, L::LDC, 16 * rb, kb, lane),
+                                  frag_at<Op>(Vt, L::LDC, 16 * wave, kb, lane), acc);
+            }
+            Uacc[rb] = acc;
+        }
+        __syncthreads();                                   // W complete
+
+        // ---- P5 (wave-local): U = Ut - W M0; O += P U; M = gam_C M0 + K^T (eg .* U)
+#pragma unroll
+        for (int rb = 0; rb < NB; ++rb) {
+#pragma unroll
+            for (int kb = 0; kb < DK; kb += Op::KSTEP)
+                Uacc[rb] = Op::mma(frag_at<Op>(Wn, L::LDD, 16 * rb, kb, lane),
+                                   frag_at<Op>(Mop, L::LDD, 0, kb, lane), Uacc[rb]);
+            const int r0 = 16 * rb + 4 * lg;
+            if constexpr (!SUMMARY)
+                st4(Uop + lc * L::LDC + r0, Uacc[rb][0], Uacc[rb][1], Uacc[rb][2], Uacc[rb][3]);
+            st4(U2op + lc * L::LDC + r0, Uacc[rb][0] * v_eg[r0], Uacc[rb][1] * v_eg[r0 + 1],
+                Uacc[rb][2] * v_eg[r0 + 2], Uacc[rb][3] * v_eg[r0 + 3]);
+        }
+        if constexpr (!SUMMARY) {
+#pragma unroll
+            for (int rb = 0; rb < NB; ++rb) {
+#pragma unroll
+                for (int kb = 0; kb < C; kb += Op::KSTEP)
+                    Oacc[rb] = Op::mma(frag_at<Op>(Pm, L::LDC, 16 * rb, kb, lane),
+                                       frag_at<Op>(Uop, L::LDC, 0, kb, lane), Oacc[rb]);
+                const int c = vcol0 + mycol;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 16 * rb + 4 * lg + i;
                     if (r < n) {
                         const size_t o = ((size_t)bh * T + t0 + r) * dv + c;
                         if (p.out_bf16)
-                            reinterpret_cast<uint16_t*>(p.out)[o] = f32_to_bf16(Oacc[sl][i]);
+                            reinterpret_cast<uint16_t*>(p.out)[o] = f32_to_bf16(Oacc[rb][i]);
                         else
-                            reinterpret_cast<float*>(p.out)[o] = Oacc[sl][i];
+                            reinterpret_cast<float*>(p.out)[o] = Oacc[rb][i];
                     }
                 }
             }
         }
         const float gC = v_gam[C - 1];
 #pragma unroll
-        for (int sl = 0; sl < SM; ++sl) {
-            const int t = wave + 4 * sl;
-            if (t < NTM) {
-                const int ib = t / NCB, cb = t % NCB;
-                f32x4 acc = Macc[sl] * gC;
+        for (int ib = 0; ib < NDB; ++ib) {
+            f32x4 acc = Macc[ib] * gC;
 #pragma unroll
-                for (int kb = 0; kb < C; kb += Op::KSTEP) {
-                    auto a = frag_at<Op>(Kt, L::LDT, 16 * ib, kb, lane);
-                    auto b = frag_at<Op>(U2t, L::LDT, 16 * cb, kb, lane);
-                    acc = Op::mma(a, b, acc);
-                }
-                Macc[sl] = acc;
-                const int c = 16 * cb + (lane & 15);
-                const int i0 = 16 * ib + 4 * (lane >> 4);
-                st4(Mt + c * L::LDW + i0, acc[0], acc[1], acc[2], acc[3]);
-            }
+            for (int kb = 0; kb < C; kb += Op::KSTEP)
+                acc = Op::mma(frag_at<Op>(Kt, L::LDC, 16 * ib, kb, lane),
+                              frag_at<Op>(U2op, L::LDC, 0, kb, lane), acc);
+            Macc[ib] = acc;
+            st4(Mop + lc * L::LDD + 16 * ib + 4 * lg, acc[0], acc[1], acc[2], acc[3]);
         }
-        __syncthreads();
+        __syncthreads();                                   // end of chunk: LDS reuse
     }
 
-    if (p.state_out) {
+    // ---------------- results ---------------------------------------------
+    if constexpr (SUMMARY) {
+        const int col = ident ? ctile * BV + mycol : DK + vcol0 + mycol;
+        float* dst = summ_bh + (size_t)seg * sstride + col;
 #pragma unroll
-        for (int sl = 0; sl < SM; ++sl) {
-            const int t = wave + 4 * sl;
-            if (t < NTM) {
-                const int i0 = (t / NCB) * 16 + 4 * (lane >> 4);
-                const int c = (t % NCB) * 16 + (lane & 15);
-                float* sp = p.state_out + (size_t)bh * DK * dv + col0 + c;
+        for (int ib = 0; ib < NDB; ++ib)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sp[(size_t)(i0 + i) * dv] = Macc[sl][i];
-            }
+            for (int i = 0; i < 4; ++i) dst[(size_t)(16 * ib + 4 * lg + i) * (DK + dv)] = Macc[ib][i];
+    } else {
+        if (p.state_out && seg == nseg - 1) {
+            float* sp = p.state_out + (size_t)bh * DK * dv + vcol0 + mycol;
+#pragma unroll
+            for (int ib = 0; ib < NDB; ++ib)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sp[(size_t)(16 * ib + 4 * lg + i) * dv] = Macc[ib][i];
         }
     }
 }
@@ -563,79 +618,82 @@ void gdn_fwd_seq_kernel(FwdArgs p) {
 // ---------------------------------------------------------------------------
 // Launch table
 // ---------------------------------------------------------------------------
-template <class In, class Op, int DK, int C, int BV>
-static hipError_t launch_seq(const FwdArgs& a, int grid, hipStream_t s) {
-    static_assert(lds_bytes<In, Op, DK, C, BV>() <= 160 * 1024, "LDS plan exceeds 160 KiB");
-    hipLaunchKernelGGL((gdn_fwd_seq_kernel<In, Op, DK, C, BV>), dim3(grid), dim3(256), 0, s, a);
+namespace {
+
+template <class In, class Op, int DK, int C, int NW>
+hipError_t launch_walk(const WalkArgs& a, hipStream_t s) {
+    static_assert(walk_fits<In, Op, DK, C, NW>(), "LDS plan exceeds 160 KiB");
+    const int bh = a.B * a.H;
+    if (a.nseg > 1) {
+        const int grid = bh * (a.nseg - 1) * ((DK + a.dv) / (16 * NW));
+        hipLaunchKernelGGL((gdn_walk_kernel<In, Op, DK, C, NW, true>), dim3(grid), dim3(64 * NW), 0, s, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const int grid = bh * a.nseg * (a.dv / (16 * NW));
+    hipLaunchKernelGGL((gdn_walk_kernel<In, Op, DK, C, NW, false>), dim3(grid), dim3(64 * NW), 0, s, a);
     return hipGetLastError();
 }
 
-template <class In, class Op, int DK, int C, int BV>
-constexpr bool fits() { return lds_bytes<In, Op, DK, C, BV>() <= 160 * 1024; }
-
 template <class In, class Op, int DK, int C>
-static hipError_t pick_bv(const FwdArgs& a, int BV, hipStream_t s) {
-    const int bh = a.B * a.H;
-    if constexpr (fits<In, Op, DK, C, 16>())
-        if (BV == 16) return launch_seq<In, Op, DK, C, 16>(a, bh * (a.dv / 16), s);
-    if constexpr (fits<In, Op, DK, C, 32>())
-        if (BV == 32) return launch_seq<In, Op, DK, C, 32>(a, bh * (a.dv / 32), s);
-    if constexpr (fits<In, Op, DK, C, 64>())
-        if (BV == 64) return launch_seq<In, Op, DK, C, 64>(a, bh * (a.dv / 64), s);
+hipError_t pick_nw(const WalkArgs& a, int nw, hipStream_t s) {
+    if constexpr (walk_fits<In, Op, DK, C, 4>())
+        if (nw == 4) return launch_walk<In, Op, DK, C, 4>(a, s);
+    if constexpr (walk_fits<In, Op, DK, C, 2>())
+        if (nw == 2) return launch_walk<In, Op, DK, C, 2>(a, s);
     return hipErrorInvalidValue;
 }
 
 template <class In, class Op, int DK>
-static hipError_t pick_c(const FwdArgs& a, int C, int BV, hipStream_t s) {
+hipError_t pick_c(const WalkArgs& a, int C, int nw, hipStream_t s) {
     switch (C) {
-    case 32: return pick_bv<In, Op, DK, 32>(a, BV, s);
-    case 64: return pick_bv<In, Op, DK, 64>(a, BV, s);
-    case 128: return pick_bv<In, Op, DK, 128>(a, BV, s);
-    default: return hipErrorInvalidValue;
-    }
-}
-
-template <class In, class Op>
-static hipError_t pick_dk(const FwdArgs& a, int C, int BV, hipStream_t s) {
-    switch (a.dk) {
-    case 32: return pick_c<In, Op, 32>(a, C, BV, s);
-    case 64: return pick_c<In, Op, 64>(a, C, BV, s);
-    case 128: return pick_c<In, Op, 128>(a, C, BV, s);
+    case 32: return pick_nw<In, Op, DK, 32>(a, nw, s);
+    case 64: return pick_nw<In, Op, DK, 64>(a, nw, s);
     default: return hipErrorInvalidValue;
     }
 }
 
 template <class In, class Op, int DK, int C>
-static int max_bv_of() {
-    if constexpr (fits<In, Op, DK, C, 64>()) return 64;
-    if constexpr (fits<In, Op, DK, C, 32>()) return 32;
-    if constexpr (fits<In, Op, DK, C, 16>()) return 16;
+int max_nw_of() {
+    if constexpr (walk_fits<In, Op, DK, C, 4>()) return 4;
+    if constexpr (walk_fits<In, Op, DK, C, 2>()) return 2;
     return 0;
 }
 
 template <class In, class Op, int DK>
-static int max_bv_c(int C) {
+int max_nw_c(int C) {
     switch (C) {
-    case 32: return max_bv_of<In, Op, DK, 32>();
-    case 64: return max_bv_of<In, Op, DK, 64>();
-    case 128: return max_bv_of<In, Op, DK, 128>();
+    case 32: return max_nw_of<In, Op, DK, 32>();
+    case 64: return max_nw_of<In, Op, DK, 64>();
     default: return 0;
     }
 }
 
-int seq_max_bv(int in_f32, int dk, int C) {
-    // widest value-column tile whose LDS plan fits one workgroup (0: none)
+}  // namespace
+
+int walk_max_waves(int in_f32, int dk, int C) {
     switch (dk) {
-    case 32: return in_f32 ? max_bv_c<float, OpF32, 32>(C) : max_bv_c<uint16_t, OpF16, 32>(C);
-    case 64: return in_f32 ? max_bv_c<float, OpF32, 64>(C) : max_bv_c<uint16_t, OpF16, 64>(C);
-    case 128: return in_f32 ? max_bv_c<float, OpF32, 128>(C) : max_bv_c<uint16_t, OpF16, 128>(C);
+    case 32: return in_f32 ? max_nw_c<float, OpF32, 32>(C) : max_nw_c<uint16_t, OpF16, 32>(C);
+    case 64: return in_f32 ? max_nw_c<float, OpF32, 64>(C) : max_nw_c<uint16_t, OpF16, 64>(C);
+    case 128: return in_f32 ? 0 : max_nw_c<uint16_t, OpF16, 128>(C);
     default: return 0;
     }
 }
 
-hipError_t launch_fwd_seq(const FwdArgs& a, int C, int BV, hipStream_t s) {
-    if (a.in_f32) return pick_dk<float, OpF32>(a, C, BV, s);
-    return pick_dk<uint16_t, OpF16>(a, C, BV, s);
+hipError_t launch_walk(const WalkArgs& a, int C, int nw, hipStream_t s) {
+    if (a.in_f32) {
+        switch (a.dk) {
+        case 32: return pick_c<float, OpF32, 32>(a, C, nw, s);
+        case 64: return pick_c<float, OpF32, 64>(a, C, nw, s);
+        default: return hipErrorInvalidValue;
+        }
+    }
+    switch (a.dk) {
+    case 32: return pick_c<uint16_t, OpF16, 32>(a, C, nw, s);
+    case 64: return pick_c<uint16_t, OpF16, 64>(a, C, nw, s);
+    case 128: return pick_c<uint16_t, OpF16, 128>(a, C, nw, s);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace gdn

@@ -1,10 +1,11 @@
 // gdn_kernels.h -- internal interface between the C-ABI layer (gdn_api.cpp)
-// and the HIP kernels (gdn_fwd.hip).  Not part of the public ABI.
+// and the HIP kernels.  Not part of the public ABI.
 #pragma once
 #include <hip/hip_runtime.h>
 
 namespace gdn {
 
+// Arguments common to every forward launch.
 struct FwdArgs {
     const void* q;
     const void* k;
@@ -21,10 +22,22 @@ struct FwdArgs {
     int in_f32;              // 1: inputs fp32, 0: bf16
 };
 
-// Single-pass launch: one workgroup per (batch, head, value-column tile).
-hipError_t launch_fwd_seq(const FwdArgs& a, int chunk, int bv, hipStream_t s);
+// Segmented chunk walker (chunk 32 or 64).
+struct WalkArgs : FwdArgs {
+    float* summ;             // [B*H][nseg-1][dk][dk+dv] segment maps (nseg > 1)
+    float* snap;             // [B*H][dk][dv] copy of state_in (nseg > 1)
+    int nseg;                // segments per sequence (1: no split)
+    int seg_chunks;          // chunks per segment
+};
 
-// Largest value-column tile whose LDS plan fits one workgroup.
-int seq_max_bv(int in_f32, int dk, int chunk);
+// Segmented walker: summary pass (if nseg > 1) then main pass.
+hipError_t launch_walk(const WalkArgs& a, int chunk, int waves, hipStream_t s);
+// Waves per workgroup (value tile = 16 * waves) that fit on chip; 0: none.
+int walk_max_waves(int in_f32, int dk, int chunk);
+
+// Single-pass kernel (128-token chunks; fp32 inputs with dk = 128): one
+// workgroup per (batch, head, value-column tile of bv).  0: does not fit.
+hipError_t launch_fwd_single(const FwdArgs& a, int chunk, int bv, hipStream_t s);
+int single_max_bv(int in_f32, int dk, int chunk);
 
 }  // namespace gdn

@@ -107,6 +107,19 @@ def workspace_bytes(B, H, T, dk, dv, chunk=0, opts: Optional[GdnOpts] = None) ->
                                           ctypes.byref(opts) if opts is not None else None))
 
 
+def _workspace(workspace, B, H, T, dk, dv, chunk, in_dtype, device):
+    """None: allocate what the plan needs; False: none (single-segment walk)."""
+    if workspace is False:
+        return None
+    if workspace is not None:
+        return workspace
+    o = GdnOpts()
+    load().gdn_default_opts(ctypes.byref(o))
+    o.in_dtype = _dtype_code(in_dtype)
+    n = int(load().gdn_workspace_bytes(B, H, T, dk, dv, chunk, ctypes.byref(o)))
+    return torch.empty(n, dtype=torch.uint8, device=device) if n > 0 else None
+
+
 def _check(status: int):
     if status != GDN_OK:
         raise GdnError(status, load().gdn_last_error().decode())
@@ -138,12 +151,17 @@ def _prep(q, k, v, alpha, beta, state_in, out, state_out, out_dtype):
 
 def fwd_chunked(q, k, v, alpha, beta, state_in=None, chunk: int = 64, *, out=None, state_out=None,
                 out_dtype=torch.float32, qk_l2norm=True, scale=1.0, eps=1e-6, stream=None,
-                workspace: Optional[torch.Tensor] = None, want_state: bool = True):
-    """gdn_fwd_chunked.  Returns (out, state_out)."""
+                workspace=None, want_state: bool = True):
+    """gdn_fwd_chunked.  Returns (out, state_out).
+
+    workspace: None allocates the scratch the launch plan asks for (sequence
+    split into segments when there are few heads); False passes none, which
+    makes the library walk each sequence unsplit; or a uint8 device tensor."""
     B, H, T, dk, dv, out, state_out = _prep(q, k, v, alpha, beta, state_in, out,
                                             state_out if want_state else None, out_dtype)
     if not want_state:
         state_out = None
+    workspace = _workspace(workspace, B, H, T, dk, dv, chunk, q.dtype, q.device)
     opts = make_opts(q.dtype, out.dtype, qk_l2norm, scale, eps, stream, workspace)
     _check(load().gdn_fwd_chunked(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
                                   _ptr(state_in), _ptr(out), _ptr(state_out),
@@ -153,10 +171,12 @@ def fwd_chunked(q, k, v, alpha, beta, state_in=None, chunk: int = 64, *, out=Non
 
 def fwd_step(q, k, v, alpha, beta, state_in=None, *, out=None, state_out=None,
              out_dtype=torch.float32, qk_l2norm=True, scale=1.0, eps=1e-6, stream=None,
-             workspace: Optional[torch.Tensor] = None):
-    """gdn_fwd_step: one streaming chunk.  state_out may be state_in (in place)."""
+             workspace=None):
+    """gdn_fwd_step: one streaming chunk.  state_out may be state_in (in place).
+    workspace as for fwd_chunked."""
     B, H, T, dk, dv, out, state_out = _prep(q, k, v, alpha, beta, state_in, out, state_out,
                                             out_dtype)
+    workspace = _workspace(workspace, B, H, T, dk, dv, 0, q.dtype, q.device)
     opts = make_opts(q.dtype, out.dtype, qk_l2norm, scale, eps, stream, workspace)
     _check(load().gdn_fwd_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
                                _ptr(state_in), _ptr(out), _ptr(state_out),

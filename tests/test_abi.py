@@ -100,8 +100,16 @@ def test_step_validates_too(lib):
 
 
 def test_workspace_query_is_host_only(lib):
-    assert lib.gdn_workspace_bytes(1, 16, 2640, 64, 64, 64, None) >= 0
+    # few heads: the sequence is split into segments, which needs a workspace
+    n = lib.gdn_workspace_bytes(1, 16, 2640, 64, 64, 64, None)
+    assert n > 0 and n % 4 == 0
+    assert lib.gdn_workspace_bytes(1, 16, 2640, 64, 64, 0, None) == n      # step == chunk 64
+    # many heads fill the chip unsplit: no workspace
+    assert lib.gdn_workspace_bytes(4, 32, 16384, 128, 128, 64, None) == 0
+    assert lib.gdn_workspace_bytes(4, 32, 16384, 128, 128, 128, None) == 0
+    # invalid shapes
     assert lib.gdn_workspace_bytes(0, 16, 2640, 64, 64, 64, None) == 0
+    assert lib.gdn_workspace_bytes(1, 16, 2640, 48, 64, 64, None) == 0
 
 
 def test_binding_fails_loudly_without_library(tmp_path):

@@ -220,3 +220,28 @@ def test_nan_stays_in_its_head(gdn_lib):
     torch.cuda.synchronize()
     assert torch.isfinite(o[0, 0]).all() and torch.isfinite(o[0, 2]).all()
     assert torch.isnan(o[0, 1]).any()
+
+
+@pytest.mark.parametrize("name", ["stream_chunk_h16_d64", "rollout_h16_d128"])
+def test_unsplit_walk_without_workspace(gdn_lib, oracle_mod, name):
+    """Without a workspace every sequence is walked unsplit; both launch plans
+    must match the oracle (and each other to rounding)."""
+    wl = WORKLOADS[name]
+    d = make_call(wl, 0, H=4)
+    g = to_dev(d)
+    announce(f"no-workspace {name}")
+    o1, s1 = gdn_lib.fwd_step(g["q"], g["k"], g["v"], g["alpha"], g["beta"], g["state_in"],
+                              workspace=False)
+    o2, s2 = gdn_lib.fwd_step(g["q"], g["k"], g["v"], g["alpha"], g["beta"], g["state_in"])
+    torch.cuda.synchronize()
+    ro, rs = oracle_rollout(oracle_mod, [d])
+    for o, s, what in ((o1, s1, "unsplit"), (o2, s2, "segmented")):
+        assert_close(o.double().cpu().numpy(), ro[0], False, what + " out")
+        assert_close(s.double().cpu().numpy(), rs, False, what + " state")
+
+
+@pytest.mark.parametrize("dk,chunk", [(64, 64), (128, 64), (128, 32)])
+def test_fp32_inputs_head_sizes(gdn_lib, oracle_mod, dk, chunk):
+    """fp32 inputs beyond the tiny workload (dk = 128 runs the single-pass kernel)."""
+    wl = WORKLOADS["tiny_f32"].replace(dk=dk, dv=dk)
+    _check_rollout(gdn_lib, oracle_mod, wl, 1, H=2, T=300, chunk=chunk, what=f"f32 dk={dk}")
