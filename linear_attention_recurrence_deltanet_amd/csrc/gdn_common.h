@@ -35,6 +35,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 // hardware's k order inside one instruction cancels in the dot product.
 // ---------------------------------------------------------------------------
 
+// "acc-order" fragments.  A 16x16 accumulator tile holds rows 4g+i (g = lane/16,
+// i < 4) in lane g's four registers.  Feeding accumulators of one product as
+// the B operand of the next needs no data movement if the k order of that
+// product follows the accumulator rows: for KSTEP = 32 lane g supplies k =
+// 4g..4g+3 (tile 0) and 16+4g..16+4g+3 (tile 1); for KSTEP = 4, k-step s
+// takes row 4g+s.  The A operand of such a product is then read from LDS in
+// the same k order (a_acc below).
+
 // fp16 operands (11-bit significand), fp32 accumulate: v_mfma_f32_16x16x32_f16
 struct OpF16 {
     typedef _Float16 elem;
@@ -55,6 +63,30 @@ struct OpF16 {
     }
     __device__ static __forceinline__ frag16 load16(const elem* p) {
         return *reinterpret_cast<const frag16*>(p);
+    }
+    // A fragment in acc order: row (lane & 15), k block at kb.
+    __device__ static __forceinline__ frag a_acc(const elem* base, int ld, int row0, int kb, int lane) {
+        const elem* p = base + (row0 + (lane & 15)) * ld + kb + 4 * (lane >> 4);
+        const u16x4 lo = *reinterpret_cast<const u16x4*>(p);
+        const u16x4 hi = *reinterpret_cast<const u16x4*>(p + 16);
+        return frag{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+    // B fragment of k-step ks from accumulator tiles t[2ks], t[2ks+1] (rows = k).
+    __device__ static __forceinline__ frag b_acc(const f32x4* t, int ks) {
+        const f32x4 a = t[2 * ks], b = t[2 * ks + 1];
+        return pack8(a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]);
+    }
+    // eight fp32 -> eight fp16 (round to nearest even), packed in pairs
+    __device__ static __forceinline__ frag pack8(float a0, float a1, float a2, float a3,
+                                                  float a4, float a5, float a6, float a7) {
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        u32x4 w = {pk2(a0, a1), pk2(a2, a3), pk2(a4, a5), pk2(a6, a7)};
+        return __builtin_bit_cast(frag, w);
+    }
+    __device__ static __forceinline__ uint32_t pk2(float a, float b) {
+        typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+        typedef float f2 __attribute__((ext_vector_type(2)));
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{a, b}, h2));
     }
 };
 
@@ -83,6 +115,13 @@ struct OpF32 {
     }
     __device__ static __forceinline__ elem from_f32(float x) { return x; }
     __device__ static __forceinline__ frag load(const elem* p) { return *p; }
+    __device__ static __forceinline__ frag a_acc(const elem* base, int ld, int row0, int kb, int lane) {
+        // k-step kb covers rows 16*(kb/16) + 4g + (kb/4)%4
+        return base[(row0 + (lane & 15)) * ld + (kb & ~15) + 4 * (lane >> 4) + ((kb >> 2) & 3)];
+    }
+    __device__ static __forceinline__ frag b_acc(const f32x4* t, int ks) {
+        return t[ks >> 2][ks & 3];
+    }
 };
 
 // Fragment of a row-major LDS array (row stride `ld` elements): rows
@@ -94,6 +133,120 @@ __device__ __forceinline__ typename Op::frag frag_at(const typename Op::elem* ba
 }
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// ---------------------------------------------------------------------------
+// Raw buffer access: a 128-bit resource (base, byte size) in scalar registers
+// and a 32-bit per-lane byte offset.  Loads past `bytes` return zero and
+// stores past it are dropped by the hardware range check.
+// ---------------------------------------------------------------------------
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;   // 32-bit data format, raw (untyped) access
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+template <class T>
+__device__ __forceinline__ T* uniform(T* p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+    return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
+}
+// Resource of a wave-uniform range (base and size are made scalar).
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, unsigned bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(uniform(base)), (short)0,
+                                             uniform((int)bytes), kRsrcWord3);
+}
+__device__ __forceinline__ uint4 buf_load16(rsrc_t r, unsigned off) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ uint16_t buf_load2(rsrc_t r, unsigned off) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t buf_load4(rsrc_t r, unsigned off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_store4(rsrc_t r, unsigned off, float v) {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_store2(rsrc_t r, unsigned off, uint16_t v) {
+    __builtin_amdgcn_raw_buffer_store_b16(v, r, off, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// Cross-lane helpers on DPP (no LDS traffic).
+// ---------------------------------------------------------------------------
+template <int CTRL, int ROW_MASK = 0xF, bool BOUND_ZERO = false>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                                 ROW_MASK, 0xF, BOUND_ZERO));
+}
+
+// Sum over aligned groups of W consecutive lanes (W = 2..64); every lane of
+// the group gets the total.
+template <int W>
+__device__ __forceinline__ float group_sum(float v) {
+    if constexpr (W >= 2) v += dpp<0xB1>(v);    // quad_perm [1,0,3,2]: lane ^ 1
+    if constexpr (W >= 4) v += dpp<0x4E>(v);    // quad_perm [2,3,0,1]: lane ^ 2
+    if constexpr (W >= 8) v += dpp<0x141>(v);   // row_half_mirror: other quad of the 8
+    if constexpr (W >= 16) v += dpp<0x140>(v);  // row_mirror: other half of the 16
+    if constexpr (W >= 32) v += __shfl_xor(v, 16, 64);
+    if constexpr (W >= 64) v += __shfl_xor(v, 32, 64);
+    return v;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ float wave_prefix_sum(float v) {
+    v += dpp<0x111, 0xF, true>(v);   // row_shr:1
+    v += dpp<0x112, 0xF, true>(v);   // row_shr:2
+    v += dpp<0x114, 0xF, true>(v);   // row_shr:4
+    v += dpp<0x118, 0xF, true>(v);   // row_shr:8
+    v += dpp<0x142, 0xA>(v);         // row_bcast:15 into rows 1 and 3
+    v += dpp<0x143, 0xC>(v);         // row_bcast:31 into rows 2 and 3
+    return v;
+}
+
+// 16x16 block transpose through the matrix core: with B = I the product
+// A * I returns A in accumulator layout, i.e. lane (g, c) receives
+// a[4g+i][c] (i < 4) -- column c of the block, four consecutive rows.  The
+// products are exact (one nonzero term per output).
+template <class Op>
+__device__ __forceinline__ f32x4 transpose16(const typename Op::elem* a, int lda, int lane) {
+    const int lc = lane & 15, lg = lane >> 4;
+    if constexpr (Op::KSTEP == 4) {
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            acc = Op::mma(a[lc * lda + 4 * s + lg], (4 * s + lg == lc) ? 1.f : 0.f, acc);
+        return acc;
+    } else {
+        auto fa = Op::load16(a + lc * lda + 4 * lg);
+        u16x4 one;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) one[j] = (4 * lg + j == lc) ? (uint16_t)0x3C00 : (uint16_t)0;
+        return Op::mma16(fa, one, zero4());
+    }
+}
+
+// 16x16 tile += A[16 x 16] * B, A row-major in LDS (k contiguous), B given
+// as an accumulator tile (rows = k).  For K = 16 the x16 fp16 instruction's
+// operand order already matches the accumulator rows.
+template <class Op>
+__device__ __forceinline__ f32x4 mm_k16_acc(const typename Op::elem* a, int lda, f32x4 b, f32x4 acc,
+                                            int lane) {
+    if constexpr (Op::KSTEP == 4) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            acc = Op::mma(a[(lane & 15) * lda + 4 * (lane >> 4) + s], b[s], acc);
+        return acc;
+    } else {
+        auto fa = Op::load16(a + (lane & 15) * lda + (lane >> 4) * Op::KPER16);
+        u16x4 fb;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) fb[i] = __builtin_bit_cast(uint16_t, (_Float16)b[i]);
+        return Op::mma16(fa, fb, acc);
+    }
+}
 
 // 16x16 tile += A[16 x 16] * B[16 x 16] with A row-major (k contiguous) and B
 // stored column-major ([n][k], k contiguous), both in LDS.

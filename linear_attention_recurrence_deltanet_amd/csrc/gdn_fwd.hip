@@ -52,11 +52,6 @@ template <> struct InTraits<float> {
     __device__ static __forceinline__ float to_f32(float x) { return x; }
 };
 
-__device__ __forceinline__ float group_sum(float v, int width) {
-    for (int o = width >> 1; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
-}
-
 constexpr int al16(int x) { return (x + 15) & ~15; }
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
@@ -65,14 +60,18 @@ template <class In, class Op, int DK, int C, int NW>
 struct WPlan {
     typedef typename Op::elem E;
     static constexpr int BV = 16 * NW, NB = C / 16, NT = 64 * NW;
-    static constexpr int SI = (int)sizeof(In), SE = (int)sizeof(E);
-    static constexpr int LDQ = DK + 16 / SI;   // raw q / k rows
+    static constexpr int SE = (int)sizeof(E);
     static constexpr int LDC = C + 16 / SE;    // rows of C elements
     static constexpr int LDD = DK + 16 / SE;   // rows of DK elements
+    static constexpr int LDV = BV + 16 / SE;   // rows of BV elements
     static constexpr int LDX = 16 + 16 / SE;   // rows of 16 elements
     static constexpr int LDAD = 20;            // fp32 rows of 16 (+4)
-    // region R1: raw q/k (load..Gram) | solve scratch | W (W..chain) | fold A
-    static constexpr int R1_IN = 2 * C * LDQ * SI;
+    // region R1, phase-disjoint: normalised q^, k^ and v rows (load..P2) |
+    // solve scratch (P2..P3) | W (P4..P5) | a folded segment map (before the walk)
+    static constexpr int O_QH = 0;
+    static constexpr int O_KH = al16(O_QH + C * LDD * SE);
+    static constexpr int O_VR = al16(O_KH + C * LDD * SE);
+    static constexpr int R1_IN = al16(O_VR + C * LDV * SE);
     static constexpr int O_AOFF = 0;
     static constexpr int O_TT = al16(O_AOFF + C * LDC * SE);
     static constexpr int O_AD = al16(O_TT + C * LDC * SE);
@@ -82,45 +81,52 @@ struct WPlan {
     static constexpr int R1_FOLD = DK * LDD * SE;
     static constexpr int SZ_R1 = al16(cmax(cmax(R1_IN, R1_SOLVE), cmax(R1_W, R1_FOLD)));
     static constexpr int OFF_KT = SZ_R1;                                  // K^T  [DK][LDC]
-    static constexpr int OFF_VT = OFF_KT + al16(DK * LDC * SE);           // V^T  [BV][LDC]
-    static constexpr int OFF_P = OFF_VT + al16(BV * LDC * SE);            // P    [C][LDC]
+    static constexpr int OFF_P = OFF_KT + al16(DK * LDC * SE);            // P    [C][LDC]
     static constexpr int OFF_T = OFF_P + al16(C * LDC * SE);              // T    [C][LDC]
     static constexpr int OFF_T2 = OFF_T + al16(C * LDC * SE);             // T2   [C][LDC]
-    static constexpr int OFF_VEC = OFF_T2 + al16(C * LDC * SE);           // 6 x C floats
-    static constexpr int OFF_WAVE = OFF_VEC + al16(6 * C * 4);
-    // per wave: M operand [16][LDD], U and eg.*U operands [16][LDC], Y [16][LDX]
-    static constexpr int W_MOP = 0;
-    static constexpr int W_UOP = al16(16 * LDD * SE);
-    static constexpr int W_U2OP = W_UOP + al16(16 * LDC * SE);
-    static constexpr int W_YS = W_U2OP + al16(16 * LDC * SE);
-    static constexpr int W_SIZE = W_YS + al16(16 * LDX * SE);
-    static constexpr int TOTAL = OFF_WAVE + NW * W_SIZE;
+    static constexpr int OFF_VEC = OFF_T2 + al16(C * LDC * SE);           // 4 x C floats
+    static constexpr int TOTAL = OFF_VEC + al16(4 * C * 4);
 };
 
 template <class In, class Op, int DK, int C, int NW>
 constexpr bool walk_fits() { return WPlan<In, Op, DK, C, NW>::TOTAL <= 160 * 1024; }
 
+// Four consecutive elements, one store (p is 8-byte aligned for fp16,
+// 16-byte aligned for fp32 at every call site).
 template <class E>
 __device__ __forceinline__ void st4(E* p, float a, float b, float c, float d) {
-    p[0] = (E)a; p[1] = (E)b; p[2] = (E)c; p[3] = (E)d;
+    if constexpr (sizeof(E) == 2) {
+        *reinterpret_cast<f16x4*>(p) = f16x4{(_Float16)a, (_Float16)b, (_Float16)c, (_Float16)d};
+    } else {
+        *reinterpret_cast<f32x4*>(p) = f32x4{a, b, c, d};
+    }
 }
 
-// Q^ operand fragment from the raw input row, scaled by that row's r_q.
-template <class In, class Op>
-__device__ __forceinline__ typename Op::frag qhat_frag(const In* base, int ld, int row0, int kb,
-                                                       int lane, float rq) {
-    const In* p = base + (row0 + (lane & 15)) * ld + kb + (lane >> 4) * Op::KPER;
-    if constexpr (Op::KPER == 1) {
-        return Op::from_f32(InTraits<In>::to_f32(p[0]) * rq);
-    } else {
-        typename Op::frag f;
+// 16 bytes of input (8 bf16 or 4 fp32) -> scaled Op elements in LDS, one
+// vector store (dst is 16-byte aligned for bf16 -> fp16 and fp32 -> fp32).
+template <class In, class E>
+__device__ __forceinline__ void put16(E* dst, const uint4& raw, float scale) {
+    const In* e = reinterpret_cast<const In*>(&raw);
+    if constexpr (sizeof(In) == 2) {
+        f16x8 h;
 #pragma unroll
-        for (int e = 0; e < Op::KPER; ++e) {
-            _Float16 h = (_Float16)(InTraits<In>::to_f32(p[e]) * rq);
-            f[e] = __builtin_bit_cast(uint16_t, h);
-        }
-        return f;
+        for (int i = 0; i < 8; ++i) h[i] = (_Float16)(InTraits<In>::to_f32(e[i]) * scale);
+        *reinterpret_cast<f16x8*>(dst) = h;
+    } else {
+        f32x4 f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) f[i] = InTraits<In>::to_f32(e[i]) * scale;
+        *reinterpret_cast<f32x4*>(dst) = f;
     }
+}
+
+template <class In>
+__device__ __forceinline__ float sumsq16(const uint4& raw) {
+    const In* e = reinterpret_cast<const In*>(&raw);
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16 / (int)sizeof(In); ++i) { const float x = InTraits<In>::to_f32(e[i]); s += x * x; }
+    return s;
 }
 
 }  // namespace
@@ -134,12 +140,11 @@ __global__ __launch_bounds__(64 * NW)
 void gdn_walk_kernel(WalkArgs p) {
     typedef WPlan<In, Op, DK, C, NW> L;
     typedef typename Op::elem E;
-    typedef typename InTraits<In>::Gram GOp;
     constexpr int NT = L::NT, BV = L::BV, NB = L::NB;
     constexpr int NTG = NB * (NB + 1) / 2;            // lower-triangle 16x16 Gram tiles
     constexpr int SG = (NTG + NW - 1) / NW;
     constexpr int NDB = DK / 16;                      // 16-row blocks of the state
-    constexpr int NTW = NDB * NB;                     // W^T tiles
+    constexpr int NTW = NDB * NB;                     // W^T tiles; also K^T blocks
     constexpr int SW = (NTW + NW - 1) / NW;
     constexpr int EPV = 16 / (int)sizeof(In);         // input elements per 16-byte load
     constexpr int VPRQ = DK / EPV;                    // 16-byte loads per q/k row
@@ -148,10 +153,13 @@ void gdn_walk_kernel(WalkArgs p) {
     constexpr int VV = C * VPRV, VPT = (VV + NT - 1) / NT;
     constexpr int TPL = C >= 64 ? C / 64 : 1;         // decay tokens per lane of wave 0
     constexpr bool LOADQ = !SUMMARY;
+    constexpr int KS_D = DK / Op::KSTEP;              // k-steps over DK
+    constexpr int KS_C = C / Op::KSTEP;               // k-steps over C
 
     __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
-    In* qraw = reinterpret_cast<In*>(smem);
-    In* kraw = qraw + C * L::LDQ;
+    E* Qh = reinterpret_cast<E*>(smem + L::O_QH);      // [C][LDD]  q^ rows
+    E* Kh = reinterpret_cast<E*>(smem + L::O_KH);      // [C][LDD]  k^ rows
+    E* Vr = reinterpret_cast<E*>(smem + L::O_VR);      // [C][LDV]  v rows of the tile
     E* Aoff = reinterpret_cast<E*>(smem + L::O_AOFF);
     E* Tt = reinterpret_cast<E*>(smem + L::O_TT);
     float* Adt = reinterpret_cast<float*>(smem + L::O_AD);
@@ -159,27 +167,19 @@ void gdn_walk_kernel(WalkArgs p) {
     E* Wn = reinterpret_cast<E*>(smem);
     E* Afold = reinterpret_cast<E*>(smem);
     E* Kt = reinterpret_cast<E*>(smem + L::OFF_KT);
-    E* Vt = reinterpret_cast<E*>(smem + L::OFF_VT);
     E* Pm = reinterpret_cast<E*>(smem + L::OFF_P);
     E* Tm = reinterpret_cast<E*>(smem + L::OFF_T);
     E* T2m = reinterpret_cast<E*>(smem + L::OFF_T2);
-    float* v_rq = reinterpret_cast<float*>(smem + L::OFF_VEC);
-    float* v_rk = v_rq + C;
-    float* v_g2 = v_rk + C;
+    float* v_g2 = reinterpret_cast<float*>(smem + L::OFF_VEC);
     float* v_gam = v_g2 + C;
     float* v_eg = v_gam + C;
     float* v_beta = v_eg + C;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
     const int lc = lane & 15;          // column (or row) within a 16-wide block
     const int lg = lane >> 4;          // lane group 0..3
-    char* wbase = smem + L::OFF_WAVE + wave * L::W_SIZE;
-    E* Mop = reinterpret_cast<E*>(wbase + L::W_MOP);     // [16 cols][DK]
-    E* Uop = reinterpret_cast<E*>(wbase + L::W_UOP);     // [16 cols][C]
-    E* U2op = reinterpret_cast<E*>(wbase + L::W_U2OP);   // [16 cols][C]
-    E* Ys = reinterpret_cast<E*>(wbase + L::W_YS);       // [16][16]
 
     const int T = p.T, dv = p.dv;
     const int nseg = p.nseg;
@@ -199,6 +199,9 @@ void gdn_walk_kernel(WalkArgs p) {
         seg = r % nseg;
         bh = r / nseg;
     }
+    bh = uniform(bh);
+    seg = uniform(seg);
+    ctile = uniform(ctile);
     const bool ident = SUMMARY && ctile < DK / BV;       // identity columns of A_s
     const int vcol0 = SUMMARY ? (ident ? 0 : (ctile - DK / BV) * BV) : ctile * BV;
     const int mycol = 16 * wave + lc;                    // this lane's column in the tile
@@ -207,13 +210,24 @@ void gdn_walk_kernel(WalkArgs p) {
     const int ch0 = seg * p.seg_chunks;
     const int ch1 = min(nchunks, ch0 + p.seg_chunks);
 
+    // per-head bases; offsets inside a head fit in 32 bits
     const In* qg = reinterpret_cast<const In*>(p.q) + (size_t)bh * T * DK;
     const In* kg = reinterpret_cast<const In*>(p.k) + (size_t)bh * T * DK;
-    const In* vg = reinterpret_cast<const In*>(p.v) + (size_t)bh * T * dv;
+    const In* vg = reinterpret_cast<const In*>(p.v) + (size_t)bh * T * dv + vcol0;
     const In* ag = reinterpret_cast<const In*>(p.alpha) + (size_t)bh * T;
     const In* bg = reinterpret_cast<const In*>(p.beta) + (size_t)bh * T;
-    const size_t sstride = (size_t)DK * (DK + dv);      // one segment summary
+    const int sstride = DK * (DK + dv);                  // one segment summary
     float* summ_bh = p.summ + (size_t)bh * nsum * sstride;
+    constexpr unsigned SI = sizeof(In);
+    // buffer resources of this head: rows past T read as zero, stores past T drop
+    const rsrc_t rq_ = make_rsrc(qg, (unsigned)T * DK * SI);
+    const rsrc_t rk_ = make_rsrc(kg, (unsigned)T * DK * SI);
+    const rsrc_t rv_ = make_rsrc(reinterpret_cast<const In*>(p.v) + (size_t)bh * T * dv, (unsigned)T * dv * SI);
+    const rsrc_t ra_ = make_rsrc(ag, (unsigned)T * SI);
+    const rsrc_t rb_ = make_rsrc(bg, (unsigned)T * SI);
+    const unsigned osz = p.out_bf16 ? 2u : 4u;
+    const rsrc_t ro_ = make_rsrc(SUMMARY ? nullptr : (const char*)p.out + (size_t)bh * T * dv * osz,
+                                 SUMMARY ? 0u : (unsigned)T * dv * osz);
 
     // Structurally zero parts of the persistent matrices (upper blocks).
     for (int e = tid; e < C * C; e += NT) {
@@ -225,13 +239,14 @@ void gdn_walk_kernel(WalkArgs p) {
         }
     }
 
-    // ---------------- incoming state (fp32 registers + fp16 operand) ------
+    // ---------------- incoming state: fp32 accumulator tiles --------------
+    // Macc[ib] lane (lg, lc): rows 16 ib + 4 lg + i, column mycol
     f32x4 Macc[NDB];
 #pragma unroll
     for (int ib = 0; ib < NDB; ++ib) Macc[ib] = zero4();
     if constexpr (SUMMARY) {
         if (ident) {
-            const int cidx = vcol0 + ctile * BV + mycol;     // identity column index
+            const int cidx = ctile * BV + mycol;             // identity column index
 #pragma unroll
             for (int ib = 0; ib < NDB; ++ib)
 #pragma unroll
@@ -240,120 +255,107 @@ void gdn_walk_kernel(WalkArgs p) {
             // snapshot of the incoming state for the main pass (state_in may alias state_out)
             const float* sp = p.state_in + (size_t)bh * DK * dv + vcol0 + mycol;
             float* dp = p.snap + (size_t)bh * DK * dv + vcol0 + mycol;
-            for (int i = lg; i < DK; i += 4) dp[(size_t)i * dv] = sp[(size_t)i * dv];
+            for (int i = lg; i < DK; i += 4) dp[i * dv] = sp[i * dv];
         }
     } else {
         const float* sinp = nseg > 1 ? (p.state_in ? p.snap : nullptr) : p.state_in;
         if (sinp) {
-            const float* sp = sinp + (size_t)bh * DK * dv + vcol0 + mycol;
+            const float* sp = sinp + (size_t)bh * DK * dv + vcol0;
 #pragma unroll
             for (int ib = 0; ib < NDB; ++ib)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) Macc[ib][i] = sp[(size_t)(16 * ib + 4 * lg + i) * dv];
+                for (int i = 0; i < 4; ++i) Macc[ib][i] = sp[(unsigned)((16 * ib + 4 * lg + i) * dv + mycol)];
         }
-    }
-#pragma unroll
-    for (int ib = 0; ib < NDB; ++ib)
-        st4(Mop + lc * L::LDD + 16 * ib + 4 * lg, Macc[ib][0], Macc[ib][1], Macc[ib][2], Macc[ib][3]);
-
-    if constexpr (!SUMMARY) {
         // fold the maps of the preceding segments: M <- A_s M + B_s
         for (int s2 = 0; s2 < seg; ++s2) {
             const float* Ag = summ_bh + (size_t)s2 * sstride;
             __syncthreads();                                  // Afold free
             for (int e = tid * 4; e < DK * DK; e += NT * 4) {
                 const int i = e / DK, j = e % DK;
-                f32x4 a4 = *reinterpret_cast<const f32x4*>(Ag + (size_t)i * (DK + dv) + j);
+                f32x4 a4 = *reinterpret_cast<const f32x4*>(Ag + i * (DK + dv) + j);
                 st4(Afold + i * L::LDD + j, a4[0], a4[1], a4[2], a4[3]);
             }
             __syncthreads();
+            typename Op::frag mB[KS_D];
+#pragma unroll
+            for (int ks = 0; ks < KS_D; ++ks) mB[ks] = Op::b_acc(Macc, ks);
 #pragma unroll
             for (int ib = 0; ib < NDB; ++ib) {
                 f32x4 acc;
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    acc[i] = Ag[(size_t)(16 * ib + 4 * lg + i) * (DK + dv) + DK + vcol0 + mycol];
+                    acc[i] = Ag[(unsigned)((16 * ib + 4 * lg + i) * (DK + dv) + DK + vcol0 + mycol)];
 #pragma unroll
-                for (int kb = 0; kb < DK; kb += Op::KSTEP)
-                    acc = Op::mma(frag_at<Op>(Afold, L::LDD, 16 * ib, kb, lane),
-                                  frag_at<Op>(Mop, L::LDD, 0, kb, lane), acc);
+                for (int ks = 0; ks < KS_D; ++ks)
+                    acc = Op::mma(Op::a_acc(Afold, L::LDD, 16 * ib, ks * Op::KSTEP, lane), mB[ks], acc);
                 Macc[ib] = acc;
             }
-#pragma unroll
-            for (int ib = 0; ib < NDB; ++ib)
-                st4(Mop + lc * L::LDD + 16 * ib + 4 * lg, Macc[ib][0], Macc[ib][1], Macc[ib][2], Macc[ib][3]);
         }
         if (seg > 0) __syncthreads();                         // Afold (region R1) dead
     }
 
     // ---------------- register prefetch of one chunk ----------------------
+    // Buffer loads: rows past T come back as zero, so nothing is clamped and
+    // nothing waits on the loads until the next chunk consumes them.
     uint4 pq[LOADQ ? QPT : 1], pk[QPT], pv[VPT];
-    float pa[TPL], pb[TPL];
+    In pa[TPL], pb[TPL];
     auto prefetch = [&](int ch) {
         const int t0 = ch * C;
-        const int n = min(C, T - t0);
 #pragma unroll
         for (int it = 0; it < QPT; ++it) {
             const int idx = tid + NT * it;
             const int r = idx / VPRQ, part = idx % VPRQ;
-            const bool ok = idx < QV && r < n;
-            const size_t off = (size_t)(t0 + r) * DK + part * EPV;
-            pk[it] = ok ? *reinterpret_cast<const uint4*>(kg + off) : make_uint4(0, 0, 0, 0);
-            if constexpr (LOADQ)
-                pq[it] = ok ? *reinterpret_cast<const uint4*>(qg + off) : make_uint4(0, 0, 0, 0);
+            const unsigned off = (unsigned)((t0 + r) * DK + part * EPV) * SI;
+            pk[it] = buf_load16(rk_, off);
+            if constexpr (LOADQ) pq[it] = buf_load16(rq_, off);
         }
         if (!ident) {
 #pragma unroll
             for (int it = 0; it < VPT; ++it) {
                 const int idx = tid + NT * it;
                 const int r = idx / VPRV, part = idx % VPRV;
-                const bool ok = idx < VV && r < n;
-                pv[it] = ok ? *reinterpret_cast<const uint4*>(vg + (size_t)(t0 + r) * dv + vcol0 + part * EPV)
-                            : make_uint4(0, 0, 0, 0);
+                pv[it] = buf_load16(rv_, (unsigned)((t0 + r) * dv + vcol0 + part * EPV) * SI);
             }
         }
         if (wave == 0) {
 #pragma unroll
             for (int e = 0; e < TPL; ++e) {
-                const int r = lane * TPL + e;
-                const bool ok = r < n;
-                pa[e] = ok ? InTraits<In>::to_f32(ag[t0 + r]) : 1.f;
-                pb[e] = ok ? InTraits<In>::to_f32(bg[t0 + r]) : 0.f;
+                const unsigned off = (unsigned)(t0 + lane * TPL + e) * SI;
+                if constexpr (sizeof(In) == 2) {
+                    pa[e] = buf_load2(ra_, off);
+                    pb[e] = buf_load2(rb_, off);
+                } else {
+                    pa[e] = __builtin_bit_cast(float, buf_load4(ra_, off));
+                    pb[e] = __builtin_bit_cast(float, buf_load4(rb_, off));
+                }
             }
         }
     };
     if (ch0 < ch1) prefetch(ch0);
 
+    typename Op::frag mB[KS_D];                               // state as B operand
+#pragma unroll
+    for (int ks = 0; ks < KS_D; ++ks) mB[ks] = Op::b_acc(Macc, ks);
+
     for (int ch = ch0; ch < ch1; ++ch) {
         const int t0 = ch * C;
         const int n = min(C, T - t0);
 
-        // ---- P1: staged inputs, norms, K^T, V^T, decay scan; prefetch next ----
+        // ---- P1: q^, k^ (normalised) and v rows into LDS; decay scan --------
 #pragma unroll
         for (int it = 0; it < QPT; ++it) {
             const int idx = tid + NT * it;
             if (idx < QV) {                           // whole waves in or out
                 const int r = idx / VPRQ, part = idx % VPRQ;
-                const In* ke = reinterpret_cast<const In*>(&pk[it]);
-                float sk = 0.f, sq = 0.f;
-#pragma unroll
-                for (int e = 0; e < EPV; ++e) { float b = InTraits<In>::to_f32(ke[e]); sk += b * b; }
+                const uint4 kv = pk[it];                  // zero past the end
+                const float sk = group_sum<VPRQ>(sumsq16<In>(kv));
+                const float rk = p.qk_l2norm ? __builtin_amdgcn_rsqf(sk + p.eps) : 1.0f;
+                put16<In>(Kh + r * L::LDD + part * EPV, kv, rk);
                 if constexpr (LOADQ) {
-                    const In* qe = reinterpret_cast<const In*>(&pq[it]);
-#pragma unroll
-                    for (int e = 0; e < EPV; ++e) { float a = InTraits<In>::to_f32(qe[e]); sq += a * a; }
-                    sq = group_sum(sq, VPRQ);
-                    *reinterpret_cast<uint4*>(qraw + r * L::LDQ + part * EPV) = pq[it];
-                }
-                sk = group_sum(sk, VPRQ);
-                const float rk = p.qk_l2norm ? 1.0f / sqrtf(sk + p.eps) : 1.0f;
-                *reinterpret_cast<uint4*>(kraw + r * L::LDQ + part * EPV) = pk[it];
-#pragma unroll
-                for (int e = 0; e < EPV; ++e)
-                    Kt[(part * EPV + e) * L::LDC + r] = Op::from_f32(InTraits<In>::to_f32(ke[e]) * rk);
-                if (part == 0) {
-                    v_rk[r] = rk;
-                    if constexpr (LOADQ) v_rq[r] = p.qk_l2norm ? p.scale / sqrtf(sq + p.eps) : p.scale;
+                    const uint4 qv = pq[it];
+                    const float sq = group_sum<VPRQ>(sumsq16<In>(qv));
+                    const float rq = p.qk_l2norm ? p.scale * __builtin_amdgcn_rsqf(sq + p.eps) : p.scale;
+                    put16<In>(Qh + r * L::LDD + part * EPV, qv, rq);
                 }
             }
         }
@@ -363,31 +365,26 @@ void gdn_walk_kernel(WalkArgs p) {
                 const int idx = tid + NT * it;
                 if (idx < VV) {
                     const int r = idx / VPRV, part = idx % VPRV;
-                    const In* ve = reinterpret_cast<const In*>(&pv[it]);
-#pragma unroll
-                    for (int e = 0; e < EPV; ++e)
-                        Vt[(part * EPV + e) * L::LDC + r] = Op::from_f32(InTraits<In>::to_f32(ve[e]));
+                    put16<In>(Vr + r * L::LDV + part * EPV, pv[it], 1.0f);
                 }
             }
         }
         if (wave == 0) {
-            float la[TPL];
+            float la[TPL], bb[TPL];
             float run = 0.f;
 #pragma unroll
             for (int e = 0; e < TPL; ++e) {
                 const int r = lane * TPL + e;
+                const bool ok = r < n;
+                const float a = ok ? InTraits<In>::to_f32(pa[e]) : 1.f;
+                bb[e] = ok ? InTraits<In>::to_f32(pb[e]) : 0.f;
                 // log2(0) would make g_r - g_s undefined; 2^-200 is 0 in fp32 anyway
-                run += (r < C) ? fmaxf(log2f(pa[e]), -200.f) : 0.f;
+                run += (r < C) ? fmaxf(log2f(a), -200.f) : 0.f;
                 la[e] = run;
             }
-            float incl = run;
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const float y = __shfl_up(incl, o, 64);
-                if (lane >= o) incl += y;
-            }
+            const float incl = wave_prefix_sum(run);
             const float excl = incl - run;
-            const float gtot = __shfl(incl, 63, 64);
+            const float gtot = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, incl), 63));
 #pragma unroll
             for (int e = 0; e < TPL; ++e) {
                 const int r = lane * TPL + e;
@@ -396,14 +393,15 @@ void gdn_walk_kernel(WalkArgs p) {
                     v_g2[r] = g;
                     v_gam[r] = exp2f(g);
                     v_eg[r] = exp2f(gtot - g);
-                    v_beta[r] = pb[e];
+                    v_beta[r] = bb[e];
                 }
             }
         }
         if (ch + 1 < ch1) prefetch(ch + 1);
         __syncthreads();
 
-        // ---- P2: Gram products (lower tiles); O = gam .* (Q^ M0) -------------
+        // ---- P2: Gram products (lower tiles); K^T and V through the matrix
+        //      core; O = gam .* (Q^ M0) -------------------------------------
         f32x4 Areg[SG];
 #pragma unroll
         for (int sl = 0; sl < SG; ++sl) {
@@ -413,44 +411,72 @@ void gdn_walk_kernel(WalkArgs p) {
                 int I = 0;
                 while ((I + 1) * (I + 2) / 2 <= t) ++I;
                 const int J = t - I * (I + 1) / 2;        // J <= I
+                typename Op::frag fa[KS_D], fk[KS_D], fq[LOADQ ? KS_D : 1];
+#pragma unroll
+                for (int ks = 0; ks < KS_D; ++ks) {
+                    fa[ks] = frag_at<Op>(Kh, L::LDD, 16 * J, ks * Op::KSTEP, lane);
+                    fk[ks] = frag_at<Op>(Kh, L::LDD, 16 * I, ks * Op::KSTEP, lane);
+                    if constexpr (LOADQ) fq[ks] = frag_at<Op>(Qh, L::LDD, 16 * I, ks * Op::KSTEP, lane);
+                }
                 f32x4 kk = zero4(), kq = zero4();
 #pragma unroll
-                for (int kb = 0; kb < DK; kb += GOp::KSTEP) {
-                    auto a = frag_at<GOp>(kraw, L::LDQ, 16 * J, kb, lane);
-                    kk = GOp::mma(a, frag_at<GOp>(kraw, L::LDQ, 16 * I, kb, lane), kk);
-                    if constexpr (!SUMMARY) kq = GOp::mma(a, frag_at<GOp>(qraw, L::LDQ, 16 * I, kb, lane), kq);
+                for (int ks = 0; ks < KS_D; ++ks) {
+                    kk = Op::mma(fa[ks], fk[ks], kk);
+                    if constexpr (LOADQ) kq = Op::mma(fa[ks], fq[ks], kq);
                 }
                 // element i: row s = 16J + 4 lg + i, column r = 16I + lc
                 const int r = 16 * I + lc;
                 const int s0 = 16 * J + 4 * lg;
-                const float br = v_beta[r], rkr = v_rk[r], gr = v_g2[r];
+                const float br = v_beta[r], gr = v_g2[r];
+                const f32x4 gs = *reinterpret_cast<const f32x4*>(v_g2 + s0);
                 float pv4[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int s = s0 + i;
-                    const float rks = v_rk[s];
-                    const float e = (s <= r) ? exp2f(gr - v_g2[s]) : 0.f;
-                    Areg[sl][i] = (s < r) ? br * rkr * rks * kk[i] * e : 0.f;
-                    if constexpr (!SUMMARY) pv4[i] = v_rq[r] * rks * kq[i] * e;
+                    // G_rs = 2^(g_r - g_s) <= 1 for s <= r (clamped: rounding can make it > 0)
+                    const float e = __builtin_amdgcn_exp2f(fminf(gr - gs[i], 0.f));
+                    Areg[sl][i] = (s < r) ? br * kk[i] * e : 0.f;
+                    if constexpr (!SUMMARY) pv4[i] = (s <= r) ? kq[i] * e : 0.f;
                 }
                 if constexpr (!SUMMARY) st4(Pm + r * L::LDC + s0, pv4[0], pv4[1], pv4[2], pv4[3]);
             }
         }
-        f32x4 Oacc[NB];
-        if constexpr (!SUMMARY) {
+        // K^T blocks: Kt[16 ib + c][16 sb + 4 lg + i] = k^[16 sb + 4 lg + i][16 ib + c]
 #pragma unroll
-            for (int rb = 0; rb < NB; ++rb) {
-                const float rq = v_rq[16 * rb + lc];
-                f32x4 acc = zero4();
-#pragma unroll
-                for (int kb = 0; kb < DK; kb += Op::KSTEP)
-                    acc = Op::mma(qhat_frag<In, Op>(qraw, L::LDQ, 16 * rb, kb, lane, rq),
-                                  frag_at<Op>(Mop, L::LDD, 0, kb, lane), acc);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) Oacc[rb][i] = acc[i] * v_gam[16 * rb + 4 * lg + i];
+        for (int sl = 0; sl < SW; ++sl) {
+            const int t = wave + NW * sl;
+            if (t < NTW) {
+                const int ib = t / NB, sb = t % NB;
+                const f32x4 x = transpose16<Op>(Kh + (16 * sb) * L::LDD + 16 * ib, L::LDD, lane);
+                st4(Kt + (16 * ib + lc) * L::LDC + 16 * sb + 4 * lg, x[0], x[1], x[2], x[3]);
             }
         }
-        __syncthreads();                                   // raw q/k dead: R1 -> solve scratch
+        // v rows of this wave's 16 columns in accumulator layout (rows = tokens)
+        f32x4 Vacc[NB];
+#pragma unroll
+        for (int rb = 0; rb < NB; ++rb)
+            Vacc[rb] = ident ? zero4() : transpose16<Op>(Vr + (16 * rb) * L::LDV + 16 * wave, L::LDV, lane);
+        f32x4 Oacc[NB];
+        if constexpr (!SUMMARY) {
+            typename Op::frag fq[2][KS_D];
+#pragma unroll
+            for (int ks = 0; ks < KS_D; ++ks) fq[0][ks] = Op::a_acc(Qh, L::LDD, 0, ks * Op::KSTEP, lane);
+#pragma unroll
+            for (int rb = 0; rb < NB; ++rb) {
+                if (rb + 1 < NB) {
+#pragma unroll
+                    for (int ks = 0; ks < KS_D; ++ks)
+                        fq[(rb + 1) & 1][ks] = Op::a_acc(Qh, L::LDD, 16 * (rb + 1), ks * Op::KSTEP, lane);
+                }
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int ks = 0; ks < KS_D; ++ks) acc = Op::mma(fq[rb & 1][ks], mB[ks], acc);
+                const f32x4 gm = *reinterpret_cast<const f32x4*>(v_gam + 16 * rb + 4 * lg);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) Oacc[rb][i] = acc[i] * gm[i];
+            }
+        }
+        __syncthreads();                                   // q^/k^/v rows dead: R1 -> solve scratch
 #pragma unroll
         for (int sl = 0; sl < SG; ++sl) {
             const int t = wave + NW * sl;
@@ -479,10 +505,14 @@ void gdn_walk_kernel(WalkArgs p) {
             for (int r = 0; r < 16; ++r) x[r] = (r == j) ? 1.f : 0.f;
 #pragma unroll
             for (int s = 0; s < 15; ++s) {
-                const float* col = Adt + (16 * b + s) * L::LDAD;   // A[16b + r][16b + s], r = 0..15
+                // column s of the block: A[16b + r][16b + s], r = 0..15
+                const f32x4* col = reinterpret_cast<const f32x4*>(Adt + (16 * b + s) * L::LDAD);
+                const f32x4 c0 = col[0], c1 = col[1], c2 = col[2], c3 = col[3];
+                const float cv[16] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3],
+                                      c2[0], c2[1], c2[2], c2[3], c3[0], c3[1], c3[2], c3[3]};
                 const float xs = x[s];
 #pragma unroll
-                for (int r = s + 1; r < 16; ++r) x[r] -= col[r] * xs;
+                for (int r = s + 1; r < 16; ++r) x[r] -= cv[r] * xs;
             }
             const int c = 16 * b + j;
             const float bc = v_beta[c], gc = v_gam[c];
@@ -491,9 +521,11 @@ void gdn_walk_kernel(WalkArgs p) {
                 const float t = x[r] * bc;
                 Tm[(16 * b + r) * L::LDC + c] = (E)t;
                 T2m[(16 * b + r) * L::LDC + c] = (E)(t * gc);
-                Tt[c * L::LDC + 16 * b + r] = (E)t;
                 Xd[(16 * b + r) * L::LDX + j] = (E)x[r];
             }
+#pragma unroll
+            for (int r = 0; r < 16; r += 4)
+                st4(Tt + c * L::LDC + 16 * b + r, x[r] * bc, x[r + 1] * bc, x[r + 2] * bc, x[r + 3] * bc);
         }
         __syncthreads();
         // block rows below: T_ij = -X_ii sum_{k=j}^{i-1} A_ik T_kj
@@ -504,9 +536,8 @@ void gdn_walk_kernel(WalkArgs p) {
                 for (int k = j; k < lev; ++k)
                     y = mm_k16<Op>(Aoff + (16 * lev) * L::LDC + 16 * k, L::LDC,
                                    Tt + (16 * j) * L::LDC + 16 * k, L::LDC, y, lane);
-                // Y (rows c' = 4 lg + i, column c = lc) -> [c][c'] operand
-                st4(Ys + lc * L::LDX + 4 * lg, y[0], y[1], y[2], y[3]);
-                f32x4 t = mm_k16<Op>(Xd + (16 * lev) * L::LDX, L::LDX, Ys, L::LDX, zero4(), lane);
+                // Y (rows = k of the next product) feeds X_ii * Y from registers
+                const f32x4 t = mm_k16_acc<Op>(Xd + (16 * lev) * L::LDX, L::LDX, y, zero4(), lane);
                 const int c = 16 * j + lc;
                 const float gc = v_gam[c];
 #pragma unroll
@@ -521,96 +552,134 @@ void gdn_walk_kernel(WalkArgs p) {
         }
 
         // ---- P4: W^T = K^T T2^T (stored negated), Ut = T V -----------------
-#pragma unroll
-        for (int sl = 0; sl < SW; ++sl) {
-            const int t = wave + NW * sl;
-            if (t < NTW) {
+        {
+            typename Op::frag fk[2][KS_C], ft[2][KS_C];
+            auto loadw = [&](int buf, int t) {
                 const int ib = t / NB, rb = t % NB;
-                f32x4 acc = zero4();
 #pragma unroll
-                for (int kb = 0; kb < C; kb += Op::KSTEP)
-                    acc = Op::mma(frag_at<Op>(Kt, L::LDC, 16 * ib, kb, lane),
-                                  frag_at<Op>(T2m, L::LDC, 16 * rb, kb, lane), acc);
-                st4(Wn + (16 * rb + lc) * L::LDD + 16 * ib + 4 * lg, -acc[0], -acc[1], -acc[2], -acc[3]);
-            }
-        }
-        f32x4 Uacc[NB];
+                for (int ks = 0; ks < KS_C; ++ks) {
+                    fk[buf][ks] = frag_at<Op>(Kt, L::LDC, 16 * ib, ks * Op::KSTEP, lane);
+                    ft[buf][ks] = frag_at<Op>(T2m, L::LDC, 16 * rb, ks * Op::KSTEP, lane);
+                }
+            };
+            if (wave < NTW) loadw(0, wave);
 #pragma unroll
-        for (int rb = 0; rb < NB; ++rb) {
-            f32x4 acc = zero4();
-            if (!ident) {
+            for (int sl = 0; sl < SW; ++sl) {
+                const int t = wave + NW * sl;
+                if (t < NTW) {
+                    if (t + NW < NTW) loadw((sl + 1) & 1, t + NW);
+                    const int ib = t / NB, rb = t % NB;
+                    f32x4 acc = zero4();
 #pragma unroll
-                for (int kb = 0; kb < C; kb += Op::KSTEP)
-                    acc = Op::mma(frag_at<Op>(Tm, L::LDC, 16 * rb, kb, lane),
-                                  frag_at<Op>(Vt, L::LDC, 16 * wave, kb, lane), acc);
-            }
-            Uacc[rb] = acc;
-        }
-        __syncthreads();                                   // W complete
-
-        // ---- P5 (wave-local): U = Ut - W M0; O += P U; M = gam_C M0 + K^T (eg .* U)
-#pragma unroll
-        for (int rb = 0; rb < NB; ++rb) {
-#pragma unroll
-            for (int kb = 0; kb < DK; kb += Op::KSTEP)
-                Uacc[rb] = Op::mma(frag_at<Op>(Wn, L::LDD, 16 * rb, kb, lane),
-                                   frag_at<Op>(Mop, L::LDD, 0, kb, lane), Uacc[rb]);
-            const int r0 = 16 * rb + 4 * lg;
-            if constexpr (!SUMMARY)
-                st4(Uop + lc * L::LDC + r0, Uacc[rb][0], Uacc[rb][1], Uacc[rb][2], Uacc[rb][3]);
-            st4(U2op + lc * L::LDC + r0, Uacc[rb][0] * v_eg[r0], Uacc[rb][1] * v_eg[r0 + 1],
-                Uacc[rb][2] * v_eg[r0 + 2], Uacc[rb][3] * v_eg[r0 + 3]);
-        }
-        if constexpr (!SUMMARY) {
-#pragma unroll
-            for (int rb = 0; rb < NB; ++rb) {
-#pragma unroll
-                for (int kb = 0; kb < C; kb += Op::KSTEP)
-                    Oacc[rb] = Op::mma(frag_at<Op>(Pm, L::LDC, 16 * rb, kb, lane),
-                                       frag_at<Op>(Uop, L::LDC, 0, kb, lane), Oacc[rb]);
-                const int c = vcol0 + mycol;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = 16 * rb + 4 * lg + i;
-                    if (r < n) {
-                        const size_t o = ((size_t)bh * T + t0 + r) * dv + c;
-                        if (p.out_bf16)
-                            reinterpret_cast<uint16_t*>(p.out)[o] = f32_to_bf16(Oacc[rb][i]);
-                        else
-                            reinterpret_cast<float*>(p.out)[o] = Oacc[rb][i];
-                    }
+                    for (int ks = 0; ks < KS_C; ++ks) acc = Op::mma(fk[sl & 1][ks], ft[sl & 1][ks], acc);
+                    st4(Wn + (16 * rb + lc) * L::LDD + 16 * ib + 4 * lg, -acc[0], -acc[1], -acc[2], -acc[3]);
                 }
             }
         }
-        const float gC = v_gam[C - 1];
+        f32x4 Uacc[NB];
+        if (!ident) {
+            typename Op::frag vB[KS_C];
 #pragma unroll
-        for (int ib = 0; ib < NDB; ++ib) {
-            f32x4 acc = Macc[ib] * gC;
+            for (int ks = 0; ks < KS_C; ++ks) vB[ks] = Op::b_acc(Vacc, ks);
 #pragma unroll
-            for (int kb = 0; kb < C; kb += Op::KSTEP)
-                acc = Op::mma(frag_at<Op>(Kt, L::LDC, 16 * ib, kb, lane),
-                              frag_at<Op>(U2op, L::LDC, 0, kb, lane), acc);
-            Macc[ib] = acc;
-            st4(Mop + lc * L::LDD + 16 * ib + 4 * lg, acc[0], acc[1], acc[2], acc[3]);
+            for (int rb = 0; rb < NB; ++rb) {
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int ks = 0; ks < KS_C; ++ks)
+                    acc = Op::mma(Op::a_acc(Tm, L::LDC, 16 * rb, ks * Op::KSTEP, lane), vB[ks], acc);
+                Uacc[rb] = acc;
+            }
+        } else {
+#pragma unroll
+            for (int rb = 0; rb < NB; ++rb) Uacc[rb] = zero4();
         }
+        __syncthreads();                                   // W complete
+
+        // ---- P5 (wave-local, registers): U = Ut - W M0; O += P U;
+        //      M = gam_C M0 + K^T (eg .* U)
+        {
+            typename Op::frag fw[2][KS_D];
+#pragma unroll
+            for (int ks = 0; ks < KS_D; ++ks) fw[0][ks] = Op::a_acc(Wn, L::LDD, 0, ks * Op::KSTEP, lane);
+#pragma unroll
+            for (int rb = 0; rb < NB; ++rb) {
+                if (rb + 1 < NB) {
+#pragma unroll
+                    for (int ks = 0; ks < KS_D; ++ks)
+                        fw[(rb + 1) & 1][ks] = Op::a_acc(Wn, L::LDD, 16 * (rb + 1), ks * Op::KSTEP, lane);
+                }
+#pragma unroll
+                for (int ks = 0; ks < KS_D; ++ks) Uacc[rb] = Op::mma(fw[rb & 1][ks], mB[ks], Uacc[rb]);
+            }
+        }
+        typename Op::frag uB[KS_C];
+        if constexpr (!SUMMARY) {
+#pragma unroll
+            for (int ks = 0; ks < KS_C; ++ks) uB[ks] = Op::b_acc(Uacc, ks);
+            typename Op::frag fp[NB][KS_C];
+#pragma unroll
+            for (int rb = 0; rb < NB; ++rb)
+#pragma unroll
+                for (int ks = 0; ks < KS_C; ++ks) fp[rb][ks] = Op::a_acc(Pm, L::LDC, 16 * rb, ks * Op::KSTEP, lane);
+#pragma unroll
+            for (int rb = 0; rb < NB; ++rb) {
+#pragma unroll
+                for (int ks = 0; ks < KS_C; ++ks) Oacc[rb] = Op::mma(fp[rb][ks], uB[ks], Oacc[rb]);
+                // rows past T fall outside the buffer and are dropped
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const unsigned o = (unsigned)((t0 + 16 * rb + 4 * lg + i) * dv + vcol0 + mycol);
+                    if (p.out_bf16) buf_store2(ro_, o * 2u, f32_to_bf16(Oacc[rb][i]));
+                    else buf_store4(ro_, o * 4u, Oacc[rb][i]);
+                }
+            }
+        }
+#pragma unroll
+        for (int rb = 0; rb < NB; ++rb) {
+            const f32x4 eg = *reinterpret_cast<const f32x4*>(v_eg + 16 * rb + 4 * lg);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Uacc[rb][i] *= eg[i];
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS_C; ++ks) uB[ks] = Op::b_acc(Uacc, ks);
+        const float gC = v_gam[C - 1];
+        {
+            typename Op::frag fk[2][KS_C];
+#pragma unroll
+            for (int ks = 0; ks < KS_C; ++ks) fk[0][ks] = Op::a_acc(Kt, L::LDC, 0, ks * Op::KSTEP, lane);
+#pragma unroll
+            for (int ib = 0; ib < NDB; ++ib) {
+                if (ib + 1 < NDB) {
+#pragma unroll
+                    for (int ks = 0; ks < KS_C; ++ks)
+                        fk[(ib + 1) & 1][ks] = Op::a_acc(Kt, L::LDC, 16 * (ib + 1), ks * Op::KSTEP, lane);
+                }
+                f32x4 acc = Macc[ib] * gC;
+#pragma unroll
+                for (int ks = 0; ks < KS_C; ++ks) acc = Op::mma(fk[ib & 1][ks], uB[ks], acc);
+                Macc[ib] = acc;
+            }
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS_D; ++ks) mB[ks] = Op::b_acc(Macc, ks);
         __syncthreads();                                   // end of chunk: LDS reuse
     }
 
     // ---------------- results ---------------------------------------------
     if constexpr (SUMMARY) {
         const int col = ident ? ctile * BV + mycol : DK + vcol0 + mycol;
-        float* dst = summ_bh + (size_t)seg * sstride + col;
+        float* dst = summ_bh + (size_t)seg * sstride;
 #pragma unroll
         for (int ib = 0; ib < NDB; ++ib)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dst[(size_t)(16 * ib + 4 * lg + i) * (DK + dv)] = Macc[ib][i];
+            for (int i = 0; i < 4; ++i) dst[(unsigned)((16 * ib + 4 * lg + i) * (DK + dv) + col)] = Macc[ib][i];
     } else {
         if (p.state_out && seg == nseg - 1) {
-            float* sp = p.state_out + (size_t)bh * DK * dv + vcol0 + mycol;
+            float* sp = p.state_out + (size_t)bh * DK * dv + vcol0;
 #pragma unroll
             for (int ib = 0; ib < NDB; ++ib)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sp[(size_t)(16 * ib + 4 * lg + i) * dv] = Macc[ib][i];
+                for (int i = 0; i < 4; ++i) sp[(unsigned)((16 * ib + 4 * lg + i) * dv + mycol)] = Macc[ib][i];
         }
     }
 }
