@@ -118,8 +118,12 @@ Plan make_plan(int in_f32, int B, int H, int T, int dk, int dv, int chunk) {
     pl.seg_chunks = (nchunks + pl.nseg - 1) / pl.nseg;
     if (pl.seg_chunks < 1) pl.seg_chunks = 1;
     pl.nseg = nchunks > 0 ? (nchunks + pl.seg_chunks - 1) / pl.seg_chunks : 1;
-    if (pl.nseg > 1)
-        pl.ws_bytes = ((size_t)B * H * (pl.nseg - 1) * dk * (dk + dv) + (size_t)B * H * dk * dv) * 4;
+    if (pl.nseg > 1) {
+        const size_t bh = (size_t)B * H, ns = (size_t)(pl.nseg - 1);
+        pl.ws_bytes = bh * ns * dk * dk * (in_f32 ? 4 : 2)     // A_s
+                    + bh * ns * dk * dv * 4                      // B_s
+                    + bh * dk * dv * 4;                          // snapshot of state_in
+    }
     return pl;
 }
 
@@ -153,8 +157,14 @@ int run(const void* q, const void* k, const void* v, const void* alpha, const vo
         if (pl.seg_chunks < 1) pl.seg_chunks = 1;
         a.nseg = pl.nseg;
         a.seg_chunks = pl.seg_chunks;
-        a.summ = pl.nseg > 1 ? reinterpret_cast<float*>(o.workspace) : nullptr;
-        a.snap = pl.nseg > 1 ? a.summ + (size_t)B * H * (pl.nseg - 1) * dk * (dk + dv) : nullptr;
+        a.summA = nullptr; a.summB = nullptr; a.snap = nullptr;
+        if (pl.nseg > 1) {
+            const size_t bh = (size_t)B * H, ns = (size_t)(pl.nseg - 1);
+            char* w = reinterpret_cast<char*>(o.workspace);
+            a.summA = w;
+            a.summB = reinterpret_cast<float*>(w + bh * ns * dk * dk * (a.in_f32 ? 4 : 2));
+            a.snap = a.summB + bh * ns * dk * dv;
+        }
         if (pl.nseg > 1 && (reinterpret_cast<uintptr_t>(o.workspace) & 15u))
             return fail(GDN_ERR_ARG, "workspace must be 16-byte aligned");
         e = gdn::launch_walk(a, chunk, pl.waves, stream);

@@ -66,21 +66,21 @@ struct WPlan {
     static constexpr int LDV = BV + 16 / SE;   // rows of BV elements
     static constexpr int LDX = 16 + 16 / SE;   // rows of 16 elements
     static constexpr int LDAD = 20;            // fp32 rows of 16 (+4)
-    // region R1, phase-disjoint: normalised q^, k^ and v rows (load..P2) |
-    // solve scratch (P2..P3) | W (P4..P5) | a folded segment map (before the walk)
+    // region R1, phase-disjoint: normalised q^, k^ and v rows (load..P3a) |
+    // W (P4..P5) | a folded segment map (before the walk)
     static constexpr int O_QH = 0;
     static constexpr int O_KH = al16(O_QH + C * LDD * SE);
     static constexpr int O_VR = al16(O_KH + C * LDD * SE);
     static constexpr int R1_IN = al16(O_VR + C * LDV * SE);
-    static constexpr int O_AOFF = 0;
-    static constexpr int O_TT = al16(O_AOFF + C * LDC * SE);
-    static constexpr int O_AD = al16(O_TT + C * LDC * SE);
-    static constexpr int O_XD = al16(O_AD + NB * 16 * LDAD * 4);
-    static constexpr int R1_SOLVE = al16(O_XD + NB * 16 * LDX * SE);
     static constexpr int R1_W = C * LDD * SE;
     static constexpr int R1_FOLD = DK * LDD * SE;
-    static constexpr int SZ_R1 = al16(cmax(cmax(R1_IN, R1_SOLVE), cmax(R1_W, R1_FOLD)));
-    static constexpr int OFF_KT = SZ_R1;                                  // K^T  [DK][LDC]
+    static constexpr int SZ_R1 = al16(cmax(R1_IN, cmax(R1_W, R1_FOLD)));
+    // triangular-solve scratch (written by the Gram pass, read by the solve)
+    static constexpr int O_AOFF = SZ_R1;                                  // A off-diag blocks
+    static constexpr int O_TT = al16(O_AOFF + C * LDC * SE);              // T column-major
+    static constexpr int O_AD = al16(O_TT + C * LDC * SE);                // A diag blocks^T fp32
+    static constexpr int O_XD = al16(O_AD + NB * 16 * LDAD * 4);          // diag inverses
+    static constexpr int OFF_KT = al16(O_XD + NB * 16 * LDX * SE);        // K^T  [DK][LDC]
     static constexpr int OFF_P = OFF_KT + al16(DK * LDC * SE);            // P    [C][LDC]
     static constexpr int OFF_T = OFF_P + al16(C * LDC * SE);              // T    [C][LDC]
     static constexpr int OFF_T2 = OFF_T + al16(C * LDC * SE);             // T2   [C][LDC]
@@ -216,8 +216,8 @@ void gdn_walk_kernel(WalkArgs p) {
     const In* vg = reinterpret_cast<const In*>(p.v) + (size_t)bh * T * dv + vcol0;
     const In* ag = reinterpret_cast<const In*>(p.alpha) + (size_t)bh * T;
     const In* bg = reinterpret_cast<const In*>(p.beta) + (size_t)bh * T;
-    const int sstride = DK * (DK + dv);                  // one segment summary
-    float* summ_bh = p.summ + (size_t)bh * nsum * sstride;
+    E* summA_bh = reinterpret_cast<E*>(p.summA) + (size_t)bh * nsum * DK * DK;
+    float* summB_bh = p.summB + (size_t)bh * nsum * DK * dv;
     constexpr unsigned SI = sizeof(In);
     // buffer resources of this head: rows past T read as zero, stores past T drop
     const rsrc_t rq_ = make_rsrc(qg, (unsigned)T * DK * SI);
@@ -266,25 +266,46 @@ void gdn_walk_kernel(WalkArgs p) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) Macc[ib][i] = sp[(unsigned)((16 * ib + 4 * lg + i) * dv + mycol)];
         }
-        // fold the maps of the preceding segments: M <- A_s M + B_s
-        for (int s2 = 0; s2 < seg; ++s2) {
-            const float* Ag = summ_bh + (size_t)s2 * sstride;
-            __syncthreads();                                  // Afold free
-            for (int e = tid * 4; e < DK * DK; e += NT * 4) {
-                const int i = e / DK, j = e % DK;
-                f32x4 a4 = *reinterpret_cast<const f32x4*>(Ag + i * (DK + dv) + j);
-                st4(Afold + i * L::LDD + j, a4[0], a4[1], a4[2], a4[3]);
+        // fold the maps of the preceding segments: M <- A_s M + B_s.  The next
+        // map is loaded into registers while the current one is applied.
+        constexpr int AV = DK * DK * (int)sizeof(E) / 16;      // 16-byte pieces of A_s
+        constexpr int APT = (AV + NT - 1) / NT;
+        uint4 apf[APT];
+        f32x4 bpf[NDB];
+        auto fold_load = [&](int s2) {
+            const uint4* Ag = reinterpret_cast<const uint4*>(summA_bh + (size_t)s2 * DK * DK);
+#pragma unroll
+            for (int it = 0; it < APT; ++it) {
+                const int idx = tid + NT * it;
+                if (idx < AV) apf[it] = Ag[idx];
             }
+            const float* Bg = summB_bh + (size_t)s2 * DK * dv + vcol0 + mycol;
+#pragma unroll
+            for (int ib = 0; ib < NDB; ++ib)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) bpf[ib][i] = Bg[(unsigned)((16 * ib + 4 * lg + i) * dv)];
+        };
+        if (seg > 0) fold_load(0);
+        for (int s2 = 0; s2 < seg; ++s2) {
+            __syncthreads();                                  // Afold free
+            constexpr int EPR = DK * (int)sizeof(E) / 16;     // pieces per row of A_s
+#pragma unroll
+            for (int it = 0; it < APT; ++it) {
+                const int idx = tid + NT * it;
+                if (idx < AV)
+                    *reinterpret_cast<uint4*>(Afold + (idx / EPR) * L::LDD + (idx % EPR) * (16 / (int)sizeof(E))) = apf[it];
+            }
+            f32x4 bcur[NDB];
+#pragma unroll
+            for (int ib = 0; ib < NDB; ++ib) bcur[ib] = bpf[ib];
             __syncthreads();
+            if (s2 + 1 < seg) fold_load(s2 + 1);
             typename Op::frag mB[KS_D];
 #pragma unroll
             for (int ks = 0; ks < KS_D; ++ks) mB[ks] = Op::b_acc(Macc, ks);
 #pragma unroll
             for (int ib = 0; ib < NDB; ++ib) {
-                f32x4 acc;
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    acc[i] = Ag[(unsigned)((16 * ib + 4 * lg + i) * (DK + dv) + DK + vcol0 + mycol)];
+                f32x4 acc = bcur[ib];
 #pragma unroll
                 for (int ks = 0; ks < KS_D; ++ks)
                     acc = Op::mma(Op::a_acc(Afold, L::LDD, 16 * ib, ks * Op::KSTEP, lane), mB[ks], acc);
@@ -397,16 +418,12 @@ void gdn_walk_kernel(WalkArgs p) {
                 }
             }
         }
-        if (ch + 1 < ch1) prefetch(ch + 1);
         __syncthreads();
 
-        // ---- P2: Gram products (lower tiles); K^T and V through the matrix
-        //      core; O = gam .* (Q^ M0) -------------------------------------
-        f32x4 Areg[SG];
+        // ---- P2: Gram products (lower tiles) -> A (solve scratch), P -------
 #pragma unroll
         for (int sl = 0; sl < SG; ++sl) {
             const int t = wave + NW * sl;
-            Areg[sl] = zero4();
             if (t < NTG) {
                 int I = 0;
                 while ((I + 1) * (I + 2) / 2 <= t) ++I;
@@ -429,76 +446,32 @@ void gdn_walk_kernel(WalkArgs p) {
                 const int s0 = 16 * J + 4 * lg;
                 const float br = v_beta[r], gr = v_g2[r];
                 const f32x4 gs = *reinterpret_cast<const f32x4*>(v_g2 + s0);
-                float pv4[4];
+                float av[4], pv4[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int s = s0 + i;
                     // G_rs = 2^(g_r - g_s) <= 1 for s <= r (clamped: rounding can make it > 0)
                     const float e = __builtin_amdgcn_exp2f(fminf(gr - gs[i], 0.f));
-                    Areg[sl][i] = (s < r) ? br * kk[i] * e : 0.f;
+                    av[i] = (s < r) ? br * kk[i] * e : 0.f;
                     if constexpr (!SUMMARY) pv4[i] = (s <= r) ? kq[i] * e : 0.f;
                 }
                 if constexpr (!SUMMARY) st4(Pm + r * L::LDC + s0, pv4[0], pv4[1], pv4[2], pv4[3]);
-            }
-        }
-        // K^T blocks: Kt[16 ib + c][16 sb + 4 lg + i] = k^[16 sb + 4 lg + i][16 ib + c]
-#pragma unroll
-        for (int sl = 0; sl < SW; ++sl) {
-            const int t = wave + NW * sl;
-            if (t < NTW) {
-                const int ib = t / NB, sb = t % NB;
-                const f32x4 x = transpose16<Op>(Kh + (16 * sb) * L::LDD + 16 * ib, L::LDD, lane);
-                st4(Kt + (16 * ib + lc) * L::LDC + 16 * sb + 4 * lg, x[0], x[1], x[2], x[3]);
-            }
-        }
-        // v rows of this wave's 16 columns in accumulator layout (rows = tokens)
-        f32x4 Vacc[NB];
-#pragma unroll
-        for (int rb = 0; rb < NB; ++rb)
-            Vacc[rb] = ident ? zero4() : transpose16<Op>(Vr + (16 * rb) * L::LDV + 16 * wave, L::LDV, lane);
-        f32x4 Oacc[NB];
-        if constexpr (!SUMMARY) {
-            typename Op::frag fq[2][KS_D];
-#pragma unroll
-            for (int ks = 0; ks < KS_D; ++ks) fq[0][ks] = Op::a_acc(Qh, L::LDD, 0, ks * Op::KSTEP, lane);
-#pragma unroll
-            for (int rb = 0; rb < NB; ++rb) {
-                if (rb + 1 < NB) {
-#pragma unroll
-                    for (int ks = 0; ks < KS_D; ++ks)
-                        fq[(rb + 1) & 1][ks] = Op::a_acc(Qh, L::LDD, 16 * (rb + 1), ks * Op::KSTEP, lane);
-                }
-                f32x4 acc = zero4();
-#pragma unroll
-                for (int ks = 0; ks < KS_D; ++ks) acc = Op::mma(fq[rb & 1][ks], mB[ks], acc);
-                const f32x4 gm = *reinterpret_cast<const f32x4*>(v_gam + 16 * rb + 4 * lg);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) Oacc[rb][i] = acc[i] * gm[i];
-            }
-        }
-        __syncthreads();                                   // q^/k^/v rows dead: R1 -> solve scratch
-#pragma unroll
-        for (int sl = 0; sl < SG; ++sl) {
-            const int t = wave + NW * sl;
-            if (t < NTG) {
-                int I = 0;
-                while ((I + 1) * (I + 2) / 2 <= t) ++I;
-                const int J = t - I * (I + 1) / 2;
                 if (I == J) {
                     // diagonal block, stored transposed: Adt[I][s][r] = A[r][s]
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) Adt[(16 * I + 4 * lg + i) * L::LDAD + lc] = Areg[sl][i];
+                    for (int i = 0; i < 4; ++i) Adt[(16 * I + 4 * lg + i) * L::LDAD + lc] = av[i];
                 } else {
-                    st4(Aoff + (16 * I + lc) * L::LDC + 16 * J + 4 * lg,
-                        Areg[sl][0], Areg[sl][1], Areg[sl][2], Areg[sl][3]);
+                    st4(Aoff + r * L::LDC + s0, av[0], av[1], av[2], av[3]);
                 }
             }
         }
         __syncthreads();
 
-        // ---- P3: T = (I + A)^-1 diag(beta) ----------------------------------
-        // diagonal 16x16 blocks: column elimination, one lane per column
+        // ---- P3a: wave 0 inverts the diagonal 16x16 blocks (T = X diag(beta))
+        //      while every wave builds its V operand and O = gam .* (Q^ M0) and
+        //      the waves share the K^T transposes --------------------------------
         if (tid < C) {
+            // column elimination, one lane per column of a diagonal block
             const int b = tid >> 4, j = tid & 15;
             float x[16];
 #pragma unroll
@@ -527,7 +500,45 @@ void gdn_walk_kernel(WalkArgs p) {
             for (int r = 0; r < 16; r += 4)
                 st4(Tt + c * L::LDC + 16 * b + r, x[r] * bc, x[r + 1] * bc, x[r + 2] * bc, x[r + 3] * bc);
         }
-        __syncthreads();
+        // K^T blocks: Kt[16 ib + c][16 sb + 4 lg + i] = k^[16 sb + 4 lg + i][16 ib + c]
+        // (shared by the waves that are not solving; wave 0 solves when C >= 64)
+        {
+            constexpr int NH = (C >= 64 && NW > 1) ? NW - 1 : NW;        // helper waves
+            const int hw = (C >= 64 && NW > 1) ? wave - 1 : wave;
+            if (hw >= 0) {
+                for (int t = hw; t < NTW; t += NH) {
+                    const int ib = t / NB, sb = t % NB;
+                    const f32x4 x = transpose16<Op>(Kh + (16 * sb) * L::LDD + 16 * ib, L::LDD, lane);
+                    st4(Kt + (16 * ib + lc) * L::LDC + 16 * sb + 4 * lg, x[0], x[1], x[2], x[3]);
+                }
+            }
+        }
+        // v rows of this wave's 16 columns in accumulator layout (rows = tokens)
+        f32x4 Vacc[NB];
+#pragma unroll
+        for (int rb = 0; rb < NB; ++rb)
+            Vacc[rb] = ident ? zero4() : transpose16<Op>(Vr + (16 * rb) * L::LDV + 16 * wave, L::LDV, lane);
+        f32x4 Oacc[NB];
+        if constexpr (!SUMMARY) {
+            typename Op::frag fq[2][KS_D];
+#pragma unroll
+            for (int ks = 0; ks < KS_D; ++ks) fq[0][ks] = Op::a_acc(Qh, L::LDD, 0, ks * Op::KSTEP, lane);
+#pragma unroll
+            for (int rb = 0; rb < NB; ++rb) {
+                if (rb + 1 < NB) {
+#pragma unroll
+                    for (int ks = 0; ks < KS_D; ++ks)
+                        fq[(rb + 1) & 1][ks] = Op::a_acc(Qh, L::LDD, 16 * (rb + 1), ks * Op::KSTEP, lane);
+                }
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int ks = 0; ks < KS_D; ++ks) acc = Op::mma(fq[rb & 1][ks], mB[ks], acc);
+                const f32x4 gm = *reinterpret_cast<const f32x4*>(v_gam + 16 * rb + 4 * lg);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) Oacc[rb][i] = acc[i] * gm[i];
+            }
+        }
+        __syncthreads();                                   // q^/k^/v rows dead (R1 free)
         // block rows below: T_ij = -X_ii sum_{k=j}^{i-1} A_ik T_kj
 #pragma unroll
         for (int lev = 1; lev < NB; ++lev) {
@@ -596,7 +607,8 @@ void gdn_walk_kernel(WalkArgs p) {
         __syncthreads();                                   // W complete
 
         // ---- P5 (wave-local, registers): U = Ut - W M0; O += P U;
-        //      M = gam_C M0 + K^T (eg .* U)
+        //      M = gam_C M0 + K^T (eg .* U).  The next chunk's loads go out first.
+        if (ch + 1 < ch1) prefetch(ch + 1);
         {
             typename Op::frag fw[2][KS_D];
 #pragma unroll
@@ -626,11 +638,14 @@ void gdn_walk_kernel(WalkArgs p) {
 #pragma unroll
                 for (int ks = 0; ks < KS_C; ++ks) Oacc[rb] = Op::mma(fp[rb][ks], uB[ks], Oacc[rb]);
                 // rows past T fall outside the buffer and are dropped
+                const unsigned o0 = (unsigned)((t0 + 16 * rb + 4 * lg) * dv + vcol0 + mycol);
+                if (p.out_bf16) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const unsigned o = (unsigned)((t0 + 16 * rb + 4 * lg + i) * dv + vcol0 + mycol);
-                    if (p.out_bf16) buf_store2(ro_, o * 2u, f32_to_bf16(Oacc[rb][i]));
-                    else buf_store4(ro_, o * 4u, Oacc[rb][i]);
+                    for (int i = 0; i < 4; ++i)
+                        buf_store2(ro_, (o0 + i * dv) * 2u, __builtin_bit_cast(uint16_t, (__bf16)Oacc[rb][i]));
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) buf_store4(ro_, (o0 + i * dv) * 4u, Oacc[rb][i]);
                 }
             }
         }
@@ -667,12 +682,20 @@ void gdn_walk_kernel(WalkArgs p) {
 
     // ---------------- results ---------------------------------------------
     if constexpr (SUMMARY) {
-        const int col = ident ? ctile * BV + mycol : DK + vcol0 + mycol;
-        float* dst = summ_bh + (size_t)seg * sstride;
+        if (ident) {
+            // A_s in operand precision, row-major [DK][DK]
+            E* dst = summA_bh + (size_t)seg * DK * DK + ctile * BV + mycol;
 #pragma unroll
-        for (int ib = 0; ib < NDB; ++ib)
+            for (int ib = 0; ib < NDB; ++ib)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dst[(unsigned)((16 * ib + 4 * lg + i) * (DK + dv) + col)] = Macc[ib][i];
+                for (int i = 0; i < 4; ++i) dst[(unsigned)((16 * ib + 4 * lg + i) * DK)] = (E)Macc[ib][i];
+        } else {
+            float* dst = summB_bh + (size_t)seg * DK * dv + vcol0 + mycol;
+#pragma unroll
+            for (int ib = 0; ib < NDB; ++ib)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dst[(unsigned)((16 * ib + 4 * lg + i) * dv)] = Macc[ib][i];
+        }
     } else {
         if (p.state_out && seg == nseg - 1) {
             float* sp = p.state_out + (size_t)bh * DK * dv + vcol0;

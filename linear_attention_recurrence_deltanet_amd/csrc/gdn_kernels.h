@@ -24,8 +24,10 @@ struct FwdArgs {
 
 // Segmented chunk walker (chunk 32 or 64).
 struct WalkArgs : FwdArgs {
-    float* summ;             // [B*H][nseg-1][dk][dk+dv] segment maps (nseg > 1)
-    float* snap;             // [B*H][dk][dv] copy of state_in (nseg > 1)
+    void* summA;             // [B*H][nseg-1][dk][dk] segment transitions A_s, operand
+                             //   precision (fp16; fp32 for fp32 inputs)   (nseg > 1)
+    float* summB;            // [B*H][nseg-1][dk][dv] segment offsets B_s  (nseg > 1)
+    float* snap;             // [B*H][dk][dv] copy of state_in            (nseg > 1)
     int nseg;                // segments per sequence (1: no split)
     int seg_chunks;          // chunks per segment
 };
