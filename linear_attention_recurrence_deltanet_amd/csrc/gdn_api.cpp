@@ -69,8 +69,9 @@ int validate(const void* q, const void* k, const void* v, const void* alpha, con
 // Launch plan of one call.
 struct Plan {
     bool single;     // single-pass kernel (128-token chunks, or walker does not fit)
+    bool pipe;       // pipelined walker (bf16 inputs)
     int bv;          // value-column tile (single) ...
-    int waves;       // ... or waves per workgroup of the walker (tile = 16 * waves)
+    int waves;       // ... or waves per workgroup of the segmented walker (tile = 16 * waves)
     int nseg;        // sequence segments (walker)
     int seg_chunks;  // chunks per segment
     size_t ws_bytes; // workspace needed for nseg > 1
@@ -93,7 +94,44 @@ int single_bv(int in_f32, int B, int H, int dk, int dv, int chunk) {
 // workgroup; with few heads that leaves most of the 256 compute units idle,
 // so the sequence is cut into segments until about one workgroup per compute
 // unit is busy (each segment keeps at least two chunks).
+size_t seg_workspace(int in_f32, int B, int H, int dk, int dv, int nseg) {
+    if (nseg <= 1) return 0;
+    const size_t bh = (size_t)B * H, ns = (size_t)(nseg - 1);
+    return bh * ns * dk * dk * (in_f32 ? 4 : 2)     // A_s
+         + bh * ns * dk * dv * 4                      // B_s
+         + bh * dk * dv * 4;                          // snapshot of state_in
+}
+
+// Pipelined walker: pick the segment count with the shortest estimated
+// critical path, counted in chunk steps: a walk of L chunks takes about L + 1
+// steps, a launch of more workgroups than compute units runs in rounds, and
+// each preceding segment adds a fold of its map to the main pass.
+Plan pipe_plan(int B, int H, int T, int dk, int dv, int chunk) {
+    Plan pl{};
+    pl.pipe = true;
+    const int nchunks = (T + chunk - 1) / chunk;
+    const long long bh = (long long)B * H;
+    const long long base = bh * (dv / 64);                                   // main workgroups / segment
+    const long long sb = bh * ((dk + dv) / (64 * gdn::pipe_summary_tiles(dk, dv)));  // summary
+    const double fold = dk == 64 ? 0.3 : 0.6;
+    auto rounds = [](long long wgs) { return (double)((wgs + 255) / 256); };
+    int best_n = 1;
+    double best = rounds(base) * (nchunks + 1);
+    for (int n = 2; n <= 64 && 2 * n <= nchunks; ++n) {
+        const int L = (nchunks + n - 1) / n;
+        const int ns = (nchunks + L - 1) / L;
+        if (ns < 2 || ns != n) continue;
+        const double cost = rounds(sb * (ns - 1)) * (L + 1) + rounds(base * ns) * (L + 1) + fold * (ns - 1);
+        if (cost < best - 1e-9) { best = cost; best_n = ns; }
+    }
+    pl.nseg = best_n;
+    pl.seg_chunks = best_n > 1 ? (nchunks + best_n - 1) / best_n : (nchunks > 0 ? nchunks : 1);
+    pl.ws_bytes = seg_workspace(0, B, H, dk, dv, pl.nseg);
+    return pl;
+}
+
 Plan make_plan(int in_f32, int B, int H, int T, int dk, int dv, int chunk) {
+    if (gdn::pipe_supported(in_f32, dk, dv, chunk)) return pipe_plan(B, H, T, dk, dv, chunk);
     Plan pl{};
     int w = chunk == 128 ? 0 : gdn::walk_max_waves(in_f32, dk, chunk);
     while (w > 0 && (16 * w > dk || 16 * w > dv)) w >>= 1;
@@ -118,12 +156,7 @@ Plan make_plan(int in_f32, int B, int H, int T, int dk, int dv, int chunk) {
     pl.seg_chunks = (nchunks + pl.nseg - 1) / pl.nseg;
     if (pl.seg_chunks < 1) pl.seg_chunks = 1;
     pl.nseg = nchunks > 0 ? (nchunks + pl.seg_chunks - 1) / pl.seg_chunks : 1;
-    if (pl.nseg > 1) {
-        const size_t bh = (size_t)B * H, ns = (size_t)(pl.nseg - 1);
-        pl.ws_bytes = bh * ns * dk * dk * (in_f32 ? 4 : 2)     // A_s
-                    + bh * ns * dk * dv * 4                      // B_s
-                    + bh * dk * dv * 4;                          // snapshot of state_in
-    }
+    pl.ws_bytes = seg_workspace(in_f32, B, H, dk, dv, pl.nseg);
     return pl;
 }
 
@@ -167,7 +200,7 @@ int run(const void* q, const void* k, const void* v, const void* alpha, const vo
         }
         if (pl.nseg > 1 && (reinterpret_cast<uintptr_t>(o.workspace) & 15u))
             return fail(GDN_ERR_ARG, "workspace must be 16-byte aligned");
-        e = gdn::launch_walk(a, chunk, pl.waves, stream);
+        e = pl.pipe ? gdn::launch_pipe(a, chunk, stream) : gdn::launch_walk(a, chunk, pl.waves, stream);
     }
     if (e != hipSuccess) return fail(GDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return GDN_OK;

@@ -37,6 +37,14 @@ hipError_t launch_walk(const WalkArgs& a, int chunk, int waves, hipStream_t s);
 // Waves per workgroup (value tile = 16 * waves) that fit on chip; 0: none.
 int walk_max_waves(int in_f32, int dk, int chunk);
 
+// Pipelined walker (bf16 inputs, dk 64 or 128, dv a multiple of 64, chunk 32
+// or 64): eight waves per workgroup, value tile of 64 columns in the main
+// pass; the summary pass covers 64 * pipe_summary_tiles(dk, dv) columns of
+// [identity | value] per workgroup.
+bool pipe_supported(int in_f32, int dk, int dv, int chunk);
+int pipe_summary_tiles(int dk, int dv);
+hipError_t launch_pipe(const WalkArgs& a, int chunk, hipStream_t s);
+
 // Single-pass kernel (128-token chunks; fp32 inputs with dk = 128): one
 // workgroup per (batch, head, value-column tile of bv).  0: does not fit.
 hipError_t launch_fwd_single(const FwdArgs& a, int chunk, int bv, hipStream_t s);

@@ -1,0 +1,693 @@
+// gdn_pipe.hip -- pipelined chunk walker for bf16 inputs on gfx950 (MI355X).
+//
+// Same recurrence and chunk form as the segmented walker (SANA-Streaming,
+// paperpeel page, section 2.1 with Gated DeltaNet [35]; state carried across
+// streaming chunks, section 2.1 and appendix G.6).  With M = S^T [dk][dv],
+// g_r = sum_{s<=r} log alpha_s, gam = exp(g), G_rs = exp(g_r - g_s) (r >= s):
+//     A  = diag(beta) strict_tril(K^ K^T .* G),  T = (I + A)^-1 diag(beta)
+//     U  = T V - T diag(gam) (K^ M0)
+//     O  = diag(gam) (Q^ M0) + tril(Q^ K^T .* G) U
+//     M  = gam_C M0 + K^T diag(exp(g_C - g)) U
+//
+// Why a second walker.  With one wave per SIMD the segmented walker spends
+// most of a chunk waiting: every phase is a short dependent chain.  Here a
+// workgroup has eight waves, two per SIMD, with fixed roles:
+//  * four "state" waves own 16 value columns each (CT tiles of 16 per wave)
+//    and keep those columns of M in fp32 registers for the whole walk;
+//  * four "key" waves prepare the state-independent products of the NEXT
+//    chunk: norms, decay scan, Gram products, the triangular solve.
+// The schedule is skewed so that nothing but a few decay vectors needs two
+// LDS copies: the state waves finish chunk c (U, O, state update) while the
+// key waves normalise chunk c+1; then the state waves already form
+// K^ M and Q^ M of chunk c+1 (the only products that need the new state
+// and the raw rows) while the key waves run the Gram products of chunk c+1;
+// the triangular solve of c+1 follows, and T V is formed by the state waves
+// from T at the start of the next step.  The two roles share each SIMD, so
+// the matrix cores, the vector ALUs and LDS are kept busy by different waves.
+//
+// One step (chunk c done, chunk c+1 prepared), phases separated by barriers:
+//   1  state: U = T V + (-T diag gam)(K^ M), O, M update  | key: normalise c+1
+//   2  state: K^ M, Q^ M of c+1                           | key: Gram of c+1
+//   3  state: V tiles of c+1 in operand form              | key: diagonal
+//                                                           inverses, K^T
+//   4.. off-diagonal blocks of T, one block row per phase (all waves)
+// Operand precision as in the segmented walker: fp16 operands (11-bit
+// significand), fp32 accumulation; the state and the solve stay in fp32.
+#include "gdn_common.h"
+#include "gdn_kernels.h"
+
+namespace gdn {
+
+namespace {
+
+constexpr int pal16(int x) { return (x + 15) & ~15; }
+
+// Compile-time LDS plan (bytes).
+template <int DK, int C, int CT, bool SUMMARY>
+struct PPlan {
+    static constexpr int NCW = 4, NPW = 4, NW = NCW + NPW, NT = 64 * NW, NPT = 64 * NPW;
+    static constexpr int BV = 16 * NCW * CT;
+    static constexpr int NB = C / 16, NDB = DK / 16;
+    static constexpr int LDD = DK + 8;        // fp16 rows of DK (+16 bytes)
+    static constexpr int LDC = C + 8;         // fp16 rows of C
+    static constexpr int LDV = BV + 8;        // fp16 rows of BV
+    static constexpr int LDX = 24;            // fp16 rows of 16
+    static constexpr int LDAD = 20;           // fp32 rows of 16 (+4)
+    static constexpr int ADB = 16 * LDAD + 16;  // fp32 stride of one diagonal block
+    static constexpr int O_QH = 0;                                          // q^   [C][LDD]
+    static constexpr int O_KH = O_QH + (SUMMARY ? 0 : pal16(C * LDD * 2));  // k^   [C][LDD]
+    static constexpr int O_KT = O_KH + pal16(C * LDD * 2);                  // k^T  [DK][LDC]
+    static constexpr int O_PM = O_KT + pal16(DK * LDC * 2);                 // P    [C][LDC]
+    static constexpr int O_T2 = O_PM + (SUMMARY ? 0 : pal16(C * LDC * 2));  // -T diag(gam)
+    static constexpr int O_TM = O_T2 + pal16(C * LDC * 2);                  // T    [C][LDC]
+    static constexpr int O_TT = O_TM + pal16(C * LDC * 2);                  // T^T  [C][LDC]
+    static constexpr int O_AOFF = O_TT + pal16(C * LDC * 2);                // A off-diagonal
+    static constexpr int O_AD = O_AOFF + pal16(C * LDC * 2);                // A diag^T fp32
+    static constexpr int O_XD = O_AD + pal16(NB * ADB * 4);                 // diag inverses
+    static constexpr int O_VR = O_XD + pal16(C * LDX * 2);                  // v rows [C][LDV]
+    static constexpr int O_VEC = O_VR + pal16(C * LDV * 2);                 // 2 x 4 x C fp32
+    static constexpr int TOTAL = O_VEC + 2 * 4 * C * 4;
+};
+
+template <int DK, int C, int CT, bool SUMMARY>
+constexpr bool pipe_fits() { return PPlan<DK, C, CT, SUMMARY>::TOTAL <= 160 * 1024; }
+
+// Four fp16 values, one 8-byte store (p 8-byte aligned at every call site).
+__device__ __forceinline__ void st4h(_Float16* p, float a, float b, float c, float d) {
+    *reinterpret_cast<f16x4*>(p) = f16x4{(_Float16)a, (_Float16)b, (_Float16)c, (_Float16)d};
+}
+
+// 8 bf16 -> 8 scaled fp16, one 16-byte store.
+__device__ __forceinline__ void put8(_Float16* dst, const uint4& raw, float scale) {
+    const uint16_t* e = reinterpret_cast<const uint16_t*>(&raw);
+    f16x8 h;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) h[i] = (_Float16)(bf16_to_f32(e[i]) * scale);
+    *reinterpret_cast<f16x8*>(dst) = h;
+}
+
+__device__ __forceinline__ float sumsq8(const uint4& raw) {
+    const uint16_t* e = reinterpret_cast<const uint16_t*>(&raw);
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) { const float x = bf16_to_f32(e[i]); s += x * x; }
+    return s;
+}
+
+}  // namespace
+
+// SUMMARY = false: main pass (outputs, final state).
+// SUMMARY = true : segment maps (A_s on identity columns, B_s on value
+//                  columns with a zero incoming state), no outputs.
+template <int DK, int C, int CT, bool SUMMARY>
+__global__ __launch_bounds__(512) void gdn_pipe_kernel(WalkArgs p) {
+    typedef PPlan<DK, C, CT, SUMMARY> L;
+    typedef OpF16 Op;
+    typedef _Float16 E;
+    typedef Op::frag F;
+    constexpr int NB = L::NB, NDB = L::NDB, BV = L::BV, NCW = L::NCW, NPT = L::NPT, NW = L::NW;
+    constexpr int NTG = NB * (NB + 1) / 2;           // lower-triangle Gram tiles
+    constexpr int NTW = NDB * NB;                    // 16x16 blocks of K^T
+    constexpr int VPRQ = DK / 8;                     // 16-byte pieces per q/k row
+    constexpr int VPRV = BV / 8;                     // 16-byte pieces per v row of the tile
+    constexpr int QV = C * VPRQ, QPT = QV / NPT;
+    constexpr int VV = C * VPRV, VPT = VV / NPT;
+    static_assert(QV % NPT == 0 && VV % NPT == 0, "whole key waves per row set");
+    constexpr int TPL = C >= 64 ? C / 64 : 1;        // decay tokens per lane of the scan wave
+    constexpr int KS_D = DK / 32, KS_C = C / 32;     // k-steps over DK and over C
+
+    __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
+    E* Qh = reinterpret_cast<E*>(smem + L::O_QH);
+    E* Kh = reinterpret_cast<E*>(smem + L::O_KH);
+    E* Kt = reinterpret_cast<E*>(smem + L::O_KT);
+    E* Pm = reinterpret_cast<E*>(smem + L::O_PM);
+    E* T2n = reinterpret_cast<E*>(smem + L::O_T2);
+    E* Tm = reinterpret_cast<E*>(smem + L::O_TM);
+    E* Tt = reinterpret_cast<E*>(smem + L::O_TT);
+    E* Aoff = reinterpret_cast<E*>(smem + L::O_AOFF);
+    float* Adt = reinterpret_cast<float*>(smem + L::O_AD);
+    E* Xd = reinterpret_cast<E*>(smem + L::O_XD);
+    E* Vr = reinterpret_cast<E*>(smem + L::O_VR);
+    float* vecs = reinterpret_cast<float*>(smem + L::O_VEC);   // [2][g2 | gam | eg | beta][C]
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lc = lane & 15, lg = lane >> 4;
+    const bool is_state = wave < NCW;                 // wave-uniform role
+    const int kw = wave - NCW;                        // key-wave index
+    const int ktid = tid - 64 * NCW;                  // thread index among key waves
+
+    const int T = p.T, dv = p.dv;
+    const int nseg = p.nseg, nsum = nseg - 1;
+    int bh, seg, ctile;
+    if constexpr (SUMMARY) {
+        const int ncol = (DK + dv) / BV;
+        ctile = blockIdx.x % ncol;
+        const int r = blockIdx.x / ncol;
+        seg = r % nsum;
+        bh = r / nsum;
+    } else {
+        const int ncol = dv / BV;
+        ctile = blockIdx.x % ncol;
+        const int r = blockIdx.x / ncol;
+        seg = r % nseg;
+        bh = r / nseg;
+    }
+    bh = uniform(bh);
+    seg = uniform(seg);
+    ctile = uniform(ctile);
+    // tile-local columns [vlo, BV) are value columns; global v column = vbase + local
+    int vlo, vbase;
+    if constexpr (SUMMARY) {
+        const int gc0 = ctile * BV;
+        vlo = min(BV, max(0, DK - gc0));
+        vbase = gc0 - DK;
+    } else {
+        vlo = 0;
+        vbase = ctile * BV;
+    }
+    vlo = uniform(vlo);
+
+    const int nchunks = (T + C - 1) / C;
+    const int ch0 = seg * p.seg_chunks;
+    const int ch1 = min(nchunks, ch0 + p.seg_chunks);
+    const int nch = max(0, ch1 - ch0);
+
+    const uint16_t* qg = reinterpret_cast<const uint16_t*>(p.q) + (size_t)bh * T * DK;
+    const uint16_t* kg = reinterpret_cast<const uint16_t*>(p.k) + (size_t)bh * T * DK;
+    const uint16_t* vgp = reinterpret_cast<const uint16_t*>(p.v) + (size_t)bh * T * dv;
+    const uint16_t* ag = reinterpret_cast<const uint16_t*>(p.alpha) + (size_t)bh * T;
+    const uint16_t* bg = reinterpret_cast<const uint16_t*>(p.beta) + (size_t)bh * T;
+    E* summA_bh = reinterpret_cast<E*>(p.summA) + (size_t)bh * nsum * DK * DK;
+    float* summB_bh = p.summB + (size_t)bh * nsum * DK * dv;
+    const rsrc_t rq_ = make_rsrc(qg, (unsigned)T * DK * 2u);
+    const rsrc_t rk_ = make_rsrc(kg, (unsigned)T * DK * 2u);
+    const rsrc_t rv_ = make_rsrc(vgp, (unsigned)T * dv * 2u);
+    const rsrc_t ra_ = make_rsrc(ag, (unsigned)T * 2u);
+    const rsrc_t rb_ = make_rsrc(bg, (unsigned)T * 2u);
+    const unsigned osz = p.out_bf16 ? 2u : 4u;
+    const rsrc_t ro_ = make_rsrc(SUMMARY ? nullptr : (const char*)p.out + (size_t)bh * T * dv * osz,
+                                 SUMMARY ? 0u : (unsigned)T * dv * osz);
+
+    // Structurally zero upper blocks of the lower-triangular operands.
+    for (int e = tid; e < C * C; e += L::NT) {
+        const int r = e / C, s = e % C;
+        if ((s >> 4) > (r >> 4)) {
+            if constexpr (!SUMMARY) Pm[r * L::LDC + s] = (E)0.f;
+            Tm[r * L::LDC + s] = (E)0.f;
+            T2n[r * L::LDC + s] = (E)0.f;
+        }
+    }
+
+    // ---------------- state-wave registers ---------------------------------
+    // Macc[ct][ib] lane (lg, lc): state rows 16 ib + 4 lg + i of column col0(ct) + lc
+    f32x4 Macc[CT][NDB];
+    F mB[CT][KS_D];                                   // state as B operand (fp16)
+    f32x4 QM[SUMMARY ? 1 : CT][NB];                   // Q^ M of the next chunk
+    f32x4 KM[CT][NB];                                 // K^ M of the next chunk
+    F vB[CT][KS_C];                                   // V of the next chunk as B operand
+    auto col0 = [&](int ct) { return 16 * (ct * NCW + wave); };
+    auto ident = [&](int ct) { return SUMMARY && col0(ct) < vlo; };
+
+    // ---------------- key-wave prefetch registers ---------------------------
+    uint4 pq[SUMMARY ? 1 : QPT], pk[QPT], pv[VPT];
+    uint16_t pa[TPL], pb[TPL];
+    auto prefetch = [&](int ch) {
+        const int t0 = ch * C;
+#pragma unroll
+        for (int it = 0; it < QPT; ++it) {
+            const int idx = ktid + NPT * it;
+            const int r = idx / VPRQ, part = idx % VPRQ;
+            const unsigned off = (unsigned)((t0 + r) * DK + part * 8) * 2u;
+            pk[it] = buf_load16(rk_, off);
+            if constexpr (!SUMMARY) pq[it] = buf_load16(rq_, off);
+        }
+#pragma unroll
+        for (int it = 0; it < VPT; ++it) {
+            const int idx = ktid + NPT * it;
+            const int r = idx / VPRV, part = idx % VPRV;
+            // identity columns of a summary tile have no v (left as zero)
+            pv[it] = (part * 8 >= vlo) ? buf_load16(rv_, (unsigned)((t0 + r) * dv + vbase + part * 8) * 2u)
+                                       : make_uint4(0u, 0u, 0u, 0u);
+        }
+        if (kw == 0) {
+#pragma unroll
+            for (int e = 0; e < TPL; ++e) {
+                const unsigned off = (unsigned)(t0 + lane * TPL + e) * 2u;
+                pa[e] = buf_load2(ra_, off);
+                pb[e] = buf_load2(rb_, off);
+            }
+        }
+    };
+    if (!is_state && nch > 0) prefetch(ch0);
+
+    // The two roles run separate loops with the same barrier sequence, so the
+    // compiler allocates registers per role (the branch is wave-uniform).
+    if (is_state) {
+        // ---- incoming state of the walk (before the first step)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+            const int gcol = ctile * BV + col0(ct) + lc;      // summary: [ident | value]
+            const int vcol = vbase + col0(ct) + lc;
+#pragma unroll
+            for (int ib = 0; ib < NDB; ++ib) Macc[ct][ib] = zero4();
+            if constexpr (SUMMARY) {
+                if (ident(ct)) {
+#pragma unroll
+                    for (int ib = 0; ib < NDB; ++ib)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            Macc[ct][ib][i] = (16 * ib + 4 * lg + i == gcol) ? 1.f : 0.f;
+                } else if (seg == 0 && p.snap && p.state_in) {
+                    // snapshot of the incoming state (state_in may alias state_out)
+                    const float* sp = p.state_in + (size_t)bh * DK * dv + vcol;
+                    float* dp = p.snap + (size_t)bh * DK * dv + vcol;
+                    for (int i = lg; i < DK; i += 4) dp[i * dv] = sp[i * dv];
+                }
+            } else {
+                const float* sinp = nseg > 1 ? (p.state_in ? p.snap : nullptr) : p.state_in;
+                if (sinp) {
+                    const float* sp = sinp + (size_t)bh * DK * dv + vcol;
+#pragma unroll
+                    for (int ib = 0; ib < NDB; ++ib)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            Macc[ct][ib][i] = sp[(unsigned)((16 * ib + 4 * lg + i) * dv)];
+                }
+            }
+        }
+        if constexpr (!SUMMARY) {
+            // fold the preceding segments' maps: M <- A_s M + B_s, operands
+            // straight from global memory (the maps are small and shared)
+            for (int s2 = 0; s2 < seg; ++s2) {
+                const E* Ag = summA_bh + (size_t)s2 * DK * DK;
+                const float* Bg = summB_bh + (size_t)s2 * DK * dv + vbase;
+                F mF[CT][KS_D];
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                    for (int ks = 0; ks < KS_D; ++ks) mF[ct][ks] = Op::b_acc(Macc[ct], ks);
+#pragma unroll
+                for (int ib = 0; ib < NDB; ++ib) {
+                    F fa[KS_D];
+#pragma unroll
+                    for (int ks = 0; ks < KS_D; ++ks) fa[ks] = Op::a_acc(Ag, DK, 16 * ib, 32 * ks, lane);
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct) {
+                        f32x4 acc;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            acc[i] = Bg[(unsigned)((16 * ib + 4 * lg + i) * dv + col0(ct) + lc)];
+#pragma unroll
+                        for (int ks = 0; ks < KS_D; ++ks) acc = Op::mma(fa[ks], mF[ct][ks], acc);
+                        Macc[ct][ib] = acc;
+                    }
+                    __builtin_amdgcn_sched_barrier(0);   // bound the operand hoisting
+                }
+            }
+        }
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+            for (int ks = 0; ks < KS_D; ++ks) mB[ct][ks] = Op::b_acc(Macc[ct], ks);
+        for (int s = 0; s <= nch; ++s) {
+            const int pc = ch0 + s;
+            const int vb = s & 1;
+            // ---- phase 1: finish chunk pc - 1
+            if (s > 0) {
+                // finish chunk pc - 1 with the products prepared last step
+                const int t0 = (pc - 1) * C;
+                const float* vg = vecs + (vb ^ 1) * 4 * C;
+                const float* v_gam = vg + C;
+                const float* v_eg = vg + 2 * C;
+                const float gC = v_gam[C - 1];
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+                    const bool idt = ident(ct);
+                    F kmB[KS_C];
+#pragma unroll
+                    for (int ks = 0; ks < KS_C; ++ks) kmB[ks] = Op::b_acc(KM[ct], ks);
+                    f32x4 U[NB];
+#pragma unroll
+                    for (int rb = 0; rb < NB; ++rb) {
+                        f32x4 acc = zero4();
+                        // T and P are lower triangular: k-steps past row block rb are zero
+#pragma unroll
+                        for (int ks = 0; ks <= rb / 2; ++ks) {
+                            if (!idt) acc = Op::mma(Op::a_acc(Tm, L::LDC, 16 * rb, 32 * ks, lane), vB[ct][ks], acc);
+                            acc = Op::mma(Op::a_acc(T2n, L::LDC, 16 * rb, 32 * ks, lane), kmB[ks], acc);
+                        }
+                        U[rb] = acc;
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    if constexpr (!SUMMARY) {
+                        F uB[KS_C];
+#pragma unroll
+                        for (int ks = 0; ks < KS_C; ++ks) uB[ks] = Op::b_acc(U, ks);
+                        const unsigned ocol = (unsigned)(vbase + col0(ct) + lc);
+#pragma unroll
+                        for (int rb = 0; rb < NB; ++rb) {
+                            const f32x4 gm = *reinterpret_cast<const f32x4*>(v_gam + 16 * rb + 4 * lg);
+                            f32x4 o;
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) o[i] = QM[ct][rb][i] * gm[i];
+#pragma unroll
+                            for (int ks = 0; ks <= rb / 2; ++ks)
+                                o = Op::mma(Op::a_acc(Pm, L::LDC, 16 * rb, 32 * ks, lane), uB[ks], o);
+                            // rows past T fall outside the buffer and are dropped
+                            const unsigned o0 = (unsigned)(t0 + 16 * rb + 4 * lg) * (unsigned)dv + ocol;
+                            if (p.out_bf16) {
+#pragma unroll
+                                for (int i = 0; i < 4; ++i)
+                                    buf_store2(ro_, (o0 + i * dv) * 2u, __builtin_bit_cast(uint16_t, (__bf16)o[i]));
+                            } else {
+#pragma unroll
+                                for (int i = 0; i < 4; ++i) buf_store4(ro_, (o0 + i * dv) * 4u, o[i]);
+                            }
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+#pragma unroll
+                    for (int rb = 0; rb < NB; ++rb) {
+                        const f32x4 eg = *reinterpret_cast<const f32x4*>(v_eg + 16 * rb + 4 * lg);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) U[rb][i] *= eg[i];
+                    }
+                    F euB[KS_C];
+#pragma unroll
+                    for (int ks = 0; ks < KS_C; ++ks) euB[ks] = Op::b_acc(U, ks);
+#pragma unroll
+                    for (int ib = 0; ib < NDB; ++ib) {
+                        f32x4 acc = Macc[ct][ib] * gC;
+#pragma unroll
+                        for (int ks = 0; ks < KS_C; ++ks)
+                            acc = Op::mma(Op::a_acc(Kt, L::LDC, 16 * ib, 32 * ks, lane), euB[ks], acc);
+                        Macc[ct][ib] = acc;
+                        if (ib % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+                    }
+#pragma unroll
+                    for (int ks = 0; ks < KS_D; ++ks) mB[ct][ks] = Op::b_acc(Macc[ct], ks);
+                }
+            }
+            if (s == nch) break;
+            __syncthreads();
+            // ---- phase 2: K^ M, Q^ M of chunk pc
+            // K^ M and Q^ M of chunk pc with the state after chunk pc - 1
+#pragma unroll
+            for (int rb = 0; rb < NB; ++rb) {
+                F fk[KS_D], fq[SUMMARY ? 1 : KS_D];
+#pragma unroll
+                for (int ks = 0; ks < KS_D; ++ks) {
+                    fk[ks] = Op::a_acc(Kh, L::LDD, 16 * rb, 32 * ks, lane);
+                    if constexpr (!SUMMARY) fq[ks] = Op::a_acc(Qh, L::LDD, 16 * rb, 32 * ks, lane);
+                }
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+                    f32x4 km = zero4();
+#pragma unroll
+                    for (int ks = 0; ks < KS_D; ++ks) km = Op::mma(fk[ks], mB[ct][ks], km);
+                    KM[ct][rb] = km;
+                    if constexpr (!SUMMARY) {
+                        f32x4 qm = zero4();
+#pragma unroll
+                        for (int ks = 0; ks < KS_D; ++ks) qm = Op::mma(fq[ks], mB[ct][ks], qm);
+                        QM[ct][rb] = qm;
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            __syncthreads();
+            // ---- phase 3: V tiles of chunk pc as B operands
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+                if (!ident(ct)) {
+                    f32x4 Vacc[NB];
+#pragma unroll
+                    for (int rb = 0; rb < NB; ++rb)
+                        Vacc[rb] = transpose16<Op>(Vr + (16 * rb) * L::LDV + col0(ct), L::LDV, lane);
+#pragma unroll
+                    for (int ks = 0; ks < KS_C; ++ks) vB[ct][ks] = Op::b_acc(Vacc, ks);
+                }
+            }
+            __syncthreads();
+            for (int lev = 1; lev < NB; ++lev) __syncthreads();
+        }
+    } else {
+        for (int s = 0; s <= nch; ++s) {
+            const int pc = ch0 + s;
+            const int vb = s & 1;
+            // ---- phase 1: normalise chunk pc, decay scan, prefetch pc + 1
+            if (s == nch) break;
+            // key waves: q^, k^ (normalised) and v rows of chunk pc; decay scan
+            const int n = min(C, T - pc * C);
+#pragma unroll
+            for (int it = 0; it < QPT; ++it) {
+                const int idx = ktid + NPT * it;
+                const int r = idx / VPRQ, part = idx % VPRQ;
+                const float sk = group_sum<VPRQ>(sumsq8(pk[it]));
+                const float rk = p.qk_l2norm ? __builtin_amdgcn_rsqf(sk + p.eps) : 1.0f;
+                put8(Kh + r * L::LDD + part * 8, pk[it], rk);
+                if constexpr (!SUMMARY) {
+                    const float sq = group_sum<VPRQ>(sumsq8(pq[it]));
+                    const float rq = p.qk_l2norm ? p.scale * __builtin_amdgcn_rsqf(sq + p.eps) : p.scale;
+                    put8(Qh + r * L::LDD + part * 8, pq[it], rq);
+                }
+            }
+#pragma unroll
+            for (int it = 0; it < VPT; ++it) {
+                const int idx = ktid + NPT * it;
+                const int r = idx / VPRV, part = idx % VPRV;
+                put8(Vr + r * L::LDV + part * 8, pv[it], 1.0f);
+            }
+            if (kw == 0) {
+                float* vg = vecs + vb * 4 * C;
+                float la[TPL], bb[TPL];
+                float run = 0.f;
+#pragma unroll
+                for (int e = 0; e < TPL; ++e) {
+                    const int r = lane * TPL + e;
+                    const bool ok = r < n;
+                    const float a = ok ? bf16_to_f32(pa[e]) : 1.f;
+                    bb[e] = ok ? bf16_to_f32(pb[e]) : 0.f;
+                    // log2(0) would make g_r - g_s undefined; 2^-200 is 0 in fp32 anyway
+                    run += (r < C) ? fmaxf(log2f(a), -200.f) : 0.f;
+                    la[e] = run;
+                }
+                const float incl = wave_prefix_sum(run);
+                const float excl = incl - run;
+                const float gtot = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, incl), 63));
+#pragma unroll
+                for (int e = 0; e < TPL; ++e) {
+                    const int r = lane * TPL + e;
+                    if (r < C) {
+                        const float g = excl + la[e];
+                        vg[r] = g;
+                        vg[C + r] = exp2f(g);
+                        vg[2 * C + r] = exp2f(gtot - g);
+                        vg[3 * C + r] = bb[e];
+                    }
+                }
+            }
+            if (pc + 1 < ch1) prefetch(pc + 1);
+            __syncthreads();
+            const float* vcur = vecs + vb * 4 * C;
+            const float* v_g2 = vcur;
+            const float* v_gam = vcur + C;
+            const float* v_beta = vcur + 3 * C;
+            // ---- phase 2: Gram tiles of chunk pc
+            // Gram tiles (I, J <= I): A (solve scratch) and P
+            for (int t = kw; t < NTG; t += L::NPW) {
+                int I = 0;
+                while ((I + 1) * (I + 2) / 2 <= t) ++I;
+                const int J = t - I * (I + 1) / 2;
+                F fa[KS_D], fk[KS_D], fq[SUMMARY ? 1 : KS_D];
+#pragma unroll
+                for (int ks = 0; ks < KS_D; ++ks) {
+                    fa[ks] = frag_at<Op>(Kh, L::LDD, 16 * J, ks * 32, lane);
+                    fk[ks] = frag_at<Op>(Kh, L::LDD, 16 * I, ks * 32, lane);
+                    if constexpr (!SUMMARY) fq[ks] = frag_at<Op>(Qh, L::LDD, 16 * I, ks * 32, lane);
+                }
+                f32x4 kk = zero4(), kq = zero4();
+#pragma unroll
+                for (int ks = 0; ks < KS_D; ++ks) {
+                    kk = Op::mma(fa[ks], fk[ks], kk);
+                    if constexpr (!SUMMARY) kq = Op::mma(fa[ks], fq[ks], kq);
+                }
+                // element i: row s = 16J + 4 lg + i, column r = 16I + lc
+                const int r = 16 * I + lc;
+                const int s0 = 16 * J + 4 * lg;
+                const float br = v_beta[r], gr = v_g2[r];
+                const f32x4 gs = *reinterpret_cast<const f32x4*>(v_g2 + s0);
+                float av[4], pv4[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int s_ = s0 + i;
+                    // G_rs = 2^(g_r - g_s) <= 1 for s <= r (clamped: rounding can make it > 0)
+                    const float e = __builtin_amdgcn_exp2f(fminf(gr - gs[i], 0.f));
+                    av[i] = (s_ < r) ? br * kk[i] * e : 0.f;
+                    pv4[i] = (s_ <= r) ? kq[i] * e : 0.f;
+                }
+                if constexpr (!SUMMARY) st4h(Pm + r * L::LDC + s0, pv4[0], pv4[1], pv4[2], pv4[3]);
+                if (I == J) {
+                    // diagonal block, stored transposed: Adt[I][s][r] = A[r][s]
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) Adt[I * L::ADB + (4 * lg + i) * L::LDAD + lc] = av[i];
+                } else {
+                    st4h(Aoff + r * L::LDC + s0, av[0], av[1], av[2], av[3]);
+                }
+            }
+            __syncthreads();
+            // ---- phase 3: diagonal inverses (key wave 0), K^T (the others)
+            if (kw == 0) {
+                // diagonal 16x16 blocks by column elimination, one lane per column:
+                // X = (I + A_bb)^-1; T_bb = X diag(beta)
+                if (lane < C) {
+                    const int b = lane >> 4, j = lane & 15;
+                    float x[16];
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) x[r] = (r == j) ? 1.f : 0.f;
+#pragma unroll
+                    for (int s_ = 0; s_ < 15; ++s_) {
+                        const f32x4* col = reinterpret_cast<const f32x4*>(Adt + b * L::ADB + s_ * L::LDAD);
+                        const f32x4 c0 = col[0], c1 = col[1], c2 = col[2], c3 = col[3];
+                        const float cv[16] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3],
+                                              c2[0], c2[1], c2[2], c2[3], c3[0], c3[1], c3[2], c3[3]};
+                        const float xs = x[s_];
+#pragma unroll
+                        for (int r = s_ + 1; r < 16; ++r) x[r] -= cv[r] * xs;
+                    }
+                    const int c = 16 * b + j;
+                    const float bc = v_beta[c], gc = v_gam[c];
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const float t = x[r] * bc;
+                        Tm[(16 * b + r) * L::LDC + c] = (E)t;
+                        T2n[(16 * b + r) * L::LDC + c] = (E)(-t * gc);
+                        Xd[(16 * b + r) * L::LDX + j] = (E)x[r];
+                    }
+#pragma unroll
+                    for (int r = 0; r < 16; r += 4)
+                        st4h(Tt + c * L::LDC + 16 * b + r, x[r] * bc, x[r + 1] * bc, x[r + 2] * bc, x[r + 3] * bc);
+                }
+            } else {
+                // K^T blocks: Kt[16 ib + c][16 sb + 4 lg + i] = k^[16 sb + 4 lg + i][16 ib + c]
+                for (int t = kw - 1; t < NTW; t += L::NPW - 1) {
+                    const int ib = t / NB, sb = t % NB;
+                    const f32x4 x = transpose16<Op>(Kh + (16 * sb) * L::LDD + 16 * ib, L::LDD, lane);
+                    st4h(Kt + (16 * ib + lc) * L::LDC + 16 * sb + 4 * lg, x[0], x[1], x[2], x[3]);
+                }
+            }
+            __syncthreads();
+            // ---- phases 4..: off-diagonal blocks of T, one block row per phase
+            // T_ij = -X_ii sum_{k=j}^{i-1} A_ik T_kj
+            for (int lev = 1; lev < NB; ++lev) {
+                for (int j = kw; j < lev; j += L::NPW) {
+                    f32x4 y = zero4();
+                    for (int k = j; k < lev; ++k)
+                        y = mm_k16<Op>(Aoff + (16 * lev) * L::LDC + 16 * k, L::LDC,
+                                       Tt + (16 * j) * L::LDC + 16 * k, L::LDC, y, lane);
+                    const f32x4 t = mm_k16_acc<Op>(Xd + (16 * lev) * L::LDX, L::LDX, y, zero4(), lane);
+                    const int c = 16 * j + lc;
+                    const float gc = v_gam[c];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int r = 16 * lev + 4 * lg + i;
+                        Tm[r * L::LDC + c] = (E)(-t[i]);
+                        T2n[r * L::LDC + c] = (E)(t[i] * gc);
+                    }
+                    st4h(Tt + c * L::LDC + 16 * lev + 4 * lg, -t[0], -t[1], -t[2], -t[3]);
+                }
+                __syncthreads();
+            }
+        }
+    }
+
+    // ---------------- results (state waves) --------------------------------
+    if (is_state) {
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+            if constexpr (SUMMARY) {
+                if (ident(ct)) {
+                    // A_s in operand precision, row-major [DK][DK]
+                    E* dst = summA_bh + (size_t)seg * DK * DK + ctile * BV + col0(ct) + lc;
+#pragma unroll
+                    for (int ib = 0; ib < NDB; ++ib)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) dst[(unsigned)((16 * ib + 4 * lg + i) * DK)] = (E)Macc[ct][ib][i];
+                } else {
+                    float* dst = summB_bh + (size_t)seg * DK * dv + vbase + col0(ct) + lc;
+#pragma unroll
+                    for (int ib = 0; ib < NDB; ++ib)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) dst[(unsigned)((16 * ib + 4 * lg + i) * dv)] = Macc[ct][ib][i];
+                }
+            } else {
+                if (p.state_out && seg == nseg - 1) {
+                    float* sp = p.state_out + (size_t)bh * DK * dv + vbase + col0(ct) + lc;
+#pragma unroll
+                    for (int ib = 0; ib < NDB; ++ib)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) sp[(unsigned)((16 * ib + 4 * lg + i) * dv)] = Macc[ct][ib][i];
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Launch table
+// ---------------------------------------------------------------------------
+namespace {
+
+template <int DK, int C, int CTS>
+hipError_t launch_pipe_t(const WalkArgs& a, hipStream_t s) {
+    static_assert(pipe_fits<DK, C, 1, false>() && pipe_fits<DK, C, CTS, true>(), "LDS plan exceeds 160 KiB");
+    const int bh = a.B * a.H;
+    if (a.nseg > 1) {
+        const int grid = bh * (a.nseg - 1) * ((DK + a.dv) / (64 * CTS));
+        hipLaunchKernelGGL((gdn_pipe_kernel<DK, C, CTS, true>), dim3(grid), dim3(512), 0, s, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const int grid = bh * a.nseg * (a.dv / 64);
+    hipLaunchKernelGGL((gdn_pipe_kernel<DK, C, 1, false>), dim3(grid), dim3(512), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int DK, int C>
+hipError_t pipe_cts(const WalkArgs& a, int cts, hipStream_t s) {
+    if constexpr (DK == 64)
+        if (cts == 2) return launch_pipe_t<DK, C, 2>(a, s);
+    return launch_pipe_t<DK, C, 1>(a, s);
+}
+
+template <int DK>
+hipError_t pipe_c(const WalkArgs& a, int C, int cts, hipStream_t s) {
+    switch (C) {
+    case 32: return pipe_cts<DK, 32>(a, cts, s);
+    case 64: return pipe_cts<DK, 64>(a, cts, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+bool pipe_supported(int in_f32, int dk, int dv, int chunk) {
+    return !in_f32 && (dk == 64 || dk == 128) && dv % 64 == 0 && (chunk == 32 || chunk == 64);
+}
+
+int pipe_summary_tiles(int dk, int dv) {
+    return (dk == 64 && (dk + dv) % 128 == 0) ? 2 : 1;
+}
+
+hipError_t launch_pipe(const WalkArgs& a, int chunk, hipStream_t s) {
+    const int cts = pipe_summary_tiles(a.dk, a.dv);
+    switch (a.dk) {
+    case 64: return pipe_c<64>(a, chunk, cts, s);
+    case 128: return pipe_c<128>(a, chunk, 1, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace gdn
