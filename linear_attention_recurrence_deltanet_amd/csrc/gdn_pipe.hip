@@ -28,9 +28,10 @@
 // One step (chunk c done, chunk c+1 prepared), phases separated by barriers:
 //   1  state: U = T V + (-T diag gam)(K^ M), O, M update  | key: normalise c+1
 //   2  state: K^ M, Q^ M of c+1                           | key: Gram of c+1
-//   3  state: V tiles of c+1 in operand form              | key: diagonal
-//                                                           inverses, K^T
-//   4.. off-diagonal blocks of T, one block row per phase (all waves)
+//   3  state: V tiles of c+1 as operands, K^T blocks      | key: diagonal
+//                                                           blocks of T
+//   4  (state idle)                                       | key: off-diagonal
+//                                                           block columns of T
 // Operand precision as in the segmented walker: fp16 operands (11-bit
 // significand), fp32 accumulation; the state and the solve stay in fp32.
 #include "gdn_common.h"
@@ -84,6 +85,16 @@ __device__ __forceinline__ void put8(_Float16* dst, const uint4& raw, float scal
 #pragma unroll
     for (int i = 0; i < 8; ++i) h[i] = (_Float16)(bf16_to_f32(e[i]) * scale);
     *reinterpret_cast<f16x8*>(dst) = h;
+}
+
+// Broadcast lane `src` of each group of four lanes (src constant after unrolling).
+__device__ __forceinline__ float quad_bcast(float v, int src) {
+    switch (src) {
+    case 0: return dpp<0x00>(v);
+    case 1: return dpp<0x55>(v);
+    case 2: return dpp<0xAA>(v);
+    default: return dpp<0xFF>(v);
+    }
 }
 
 __device__ __forceinline__ float sumsq8(const uint4& raw) {
@@ -430,8 +441,17 @@ __global__ __launch_bounds__(512) void gdn_pipe_kernel(WalkArgs p) {
                     for (int ks = 0; ks < KS_C; ++ks) vB[ct][ks] = Op::b_acc(Vacc, ks);
                 }
             }
+            // K^T blocks: Kt[16 ib + c][16 sb + 4 lg + i] = k^[16 sb + 4 lg + i][16 ib + c]
+#pragma unroll
+            for (int u = 0; u < NTW / NCW; ++u) {
+                const int t = wave + NCW * u;
+                const int ib = t / NB, sb = t % NB;
+                const f32x4 x = transpose16<Op>(Kh + (16 * sb) * L::LDD + 16 * ib, L::LDD, lane);
+                st4h(Kt + (16 * ib + lc) * L::LDC + 16 * sb + 4 * lg, x[0], x[1], x[2], x[3]);
+            }
             __syncthreads();
-            for (int lev = 1; lev < NB; ++lev) __syncthreads();
+            // ---- phase 4: (off-diagonal blocks of T on the key waves)
+            __syncthreads();
         }
     } else {
         for (int s = 0; s <= nch; ++s) {
@@ -538,68 +558,67 @@ __global__ __launch_bounds__(512) void gdn_pipe_kernel(WalkArgs p) {
                 }
             }
             __syncthreads();
-            // ---- phase 3: diagonal inverses (key wave 0), K^T (the others)
-            if (kw == 0) {
-                // diagonal 16x16 blocks by column elimination, one lane per column:
-                // X = (I + A_bb)^-1; T_bb = X diag(beta)
-                if (lane < C) {
-                    const int b = lane >> 4, j = lane & 15;
-                    float x[16];
+            // ---- phase 3: diagonal blocks, one per key wave.  X = (I + A_bb)^-1 by
+            // elimination down the columns: lane 4 j + q holds rows 4q..4q+3 of
+            // column j; the pivot row is broadcast inside the group of four.
+            if (kw < NB) {
+                const int b = kw;
+                const int j = lane >> 2, q = lane & 3;
+                f32x4 acol[15];                       // acol[s][i] = A[4q + i][s] (zero for 4q + i <= s)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) x[r] = (r == j) ? 1.f : 0.f;
+                for (int s_ = 0; s_ < 15; ++s_)
+                    acol[s_] = *reinterpret_cast<const f32x4*>(Adt + b * L::ADB + s_ * L::LDAD + 4 * q);
+                float x[4];
 #pragma unroll
-                    for (int s_ = 0; s_ < 15; ++s_) {
-                        const f32x4* col = reinterpret_cast<const f32x4*>(Adt + b * L::ADB + s_ * L::LDAD);
-                        const f32x4 c0 = col[0], c1 = col[1], c2 = col[2], c3 = col[3];
-                        const float cv[16] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3],
-                                              c2[0], c2[1], c2[2], c2[3], c3[0], c3[1], c3[2], c3[3]};
-                        const float xs = x[s_];
+                for (int i = 0; i < 4; ++i) x[i] = (4 * q + i == j) ? 1.f : 0.f;
 #pragma unroll
-                        for (int r = s_ + 1; r < 16; ++r) x[r] -= cv[r] * xs;
-                    }
-                    const int c = 16 * b + j;
-                    const float bc = v_beta[c], gc = v_gam[c];
+                for (int s_ = 0; s_ < 15; ++s_) {
+                    const float xs = quad_bcast(x[s_ & 3], s_ >> 2);   // X[s][j], final
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const float t = x[r] * bc;
-                        Tm[(16 * b + r) * L::LDC + c] = (E)t;
-                        T2n[(16 * b + r) * L::LDC + c] = (E)(-t * gc);
-                        Xd[(16 * b + r) * L::LDX + j] = (E)x[r];
-                    }
-#pragma unroll
-                    for (int r = 0; r < 16; r += 4)
-                        st4h(Tt + c * L::LDC + 16 * b + r, x[r] * bc, x[r + 1] * bc, x[r + 2] * bc, x[r + 3] * bc);
+                    for (int i = 0; i < 4; ++i) x[i] -= acol[s_][i] * xs;
                 }
-            } else {
-                // K^T blocks: Kt[16 ib + c][16 sb + 4 lg + i] = k^[16 sb + 4 lg + i][16 ib + c]
-                for (int t = kw - 1; t < NTW; t += L::NPW - 1) {
-                    const int ib = t / NB, sb = t % NB;
-                    const f32x4 x = transpose16<Op>(Kh + (16 * sb) * L::LDD + 16 * ib, L::LDD, lane);
-                    st4h(Kt + (16 * ib + lc) * L::LDC + 16 * sb + 4 * lg, x[0], x[1], x[2], x[3]);
+                const int c = 16 * b + j;
+                const float bc = v_beta[c], gc = v_gam[c];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 16 * b + 4 * q + i;
+                    const float t = x[i] * bc;
+                    Tm[r * L::LDC + c] = (E)t;
+                    T2n[r * L::LDC + c] = (E)(-t * gc);
+                    Xd[r * L::LDX + j] = (E)x[i];
+                }
+                st4h(Tt + c * L::LDC + 16 * b + 4 * q, x[0] * bc, x[1] * bc, x[2] * bc, x[3] * bc);
+            }
+            __syncthreads();
+            // ---- phase 4: off-diagonal blocks, block column j on key wave j:
+            // T_ij = -X_ii sum_{k=j}^{i-1} A_ik T_kj, the T_kj of the column kept
+            // in registers, so the column needs no barrier
+            if (kw < NB - 1) {
+                const int j = kw;
+                const int c = 16 * j + lc;
+                const float gc = v_gam[c];
+                f32x4 Tc[NB];
+#pragma unroll
+                for (int i = 1; i < NB; ++i) {
+                    if (i > j) {
+                        f32x4 y = mm_k16<Op>(Aoff + (16 * i) * L::LDC + 16 * j, L::LDC,
+                                             Tt + (16 * j) * L::LDC + 16 * j, L::LDC, zero4(), lane);
+#pragma unroll
+                        for (int k = 1; k < i; ++k)
+                            if (k > j) y = mm_k16_acc<Op>(Aoff + (16 * i) * L::LDC + 16 * k, L::LDC, Tc[k], y, lane);
+                        const f32x4 t = mm_k16_acc<Op>(Xd + (16 * i) * L::LDX, L::LDX, y, zero4(), lane);
+#pragma unroll
+                        for (int ii = 0; ii < 4; ++ii) {
+                            Tc[i][ii] = -t[ii];
+                            const int r = 16 * i + 4 * lg + ii;
+                            Tm[r * L::LDC + c] = (E)(-t[ii]);
+                            T2n[r * L::LDC + c] = (E)(t[ii] * gc);
+                        }
+                        st4h(Tt + c * L::LDC + 16 * i + 4 * lg, -t[0], -t[1], -t[2], -t[3]);
+                    }
                 }
             }
             __syncthreads();
-            // ---- phases 4..: off-diagonal blocks of T, one block row per phase
-            // T_ij = -X_ii sum_{k=j}^{i-1} A_ik T_kj
-            for (int lev = 1; lev < NB; ++lev) {
-                for (int j = kw; j < lev; j += L::NPW) {
-                    f32x4 y = zero4();
-                    for (int k = j; k < lev; ++k)
-                        y = mm_k16<Op>(Aoff + (16 * lev) * L::LDC + 16 * k, L::LDC,
-                                       Tt + (16 * j) * L::LDC + 16 * k, L::LDC, y, lane);
-                    const f32x4 t = mm_k16_acc<Op>(Xd + (16 * lev) * L::LDX, L::LDX, y, zero4(), lane);
-                    const int c = 16 * j + lc;
-                    const float gc = v_gam[c];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int r = 16 * lev + 4 * lg + i;
-                        Tm[r * L::LDC + c] = (E)(-t[i]);
-                        T2n[r * L::LDC + c] = (E)(t[i] * gc);
-                    }
-                    st4h(Tt + c * L::LDC + 16 * lev + 4 * lg, -t[0], -t[1], -t[2], -t[3]);
-                }
-                __syncthreads();
-            }
         }
     }
 
