@@ -49,10 +49,13 @@ struct PPlan {
     static constexpr int NCW = 4, NPW = 4, NW = NCW + NPW, NT = 64 * NW, NPT = 64 * NPW;
     static constexpr int BV = 16 * NCW * CT;
     static constexpr int NB = C / 16, NDB = DK / 16;
-    static constexpr int LDD = DK + 8;        // fp16 rows of DK (+16 bytes)
-    static constexpr int LDC = C + 8;         // fp16 rows of C
-    static constexpr int LDV = BV + 8;        // fp16 rows of BV
-    static constexpr int LDX = 24;            // fp16 rows of 16
+    // fp16 row strides of 2 (mod 32) 32-bit words: the 8-byte operand reads
+    // of 16 rows then fall into distinct LDS banks (measured on gfx950; the
+    // strides of 16-byte-aligned rows conflict two-way or worse)
+    static constexpr int LDD = DK + 4;        // rows of DK
+    static constexpr int LDC = C + 4;         // rows of C
+    static constexpr int LDV = BV + 4;        // rows of BV
+    static constexpr int LDX = 20;            // rows of 16
     static constexpr int LDAD = 20;           // fp32 rows of 16 (+4)
     static constexpr int ADB = 16 * LDAD + 16;  // fp32 stride of one diagonal block
     static constexpr int O_QH = 0;                                          // q^   [C][LDD]
@@ -78,13 +81,17 @@ __device__ __forceinline__ void st4h(_Float16* p, float a, float b, float c, flo
     *reinterpret_cast<f16x4*>(p) = f16x4{(_Float16)a, (_Float16)b, (_Float16)c, (_Float16)d};
 }
 
-// 8 bf16 -> 8 scaled fp16, one 16-byte store.
+// 8 bf16 -> 8 scaled fp16, two 8-byte stores (rows are 8-byte aligned).
 __device__ __forceinline__ void put8(_Float16* dst, const uint4& raw, float scale) {
     const uint16_t* e = reinterpret_cast<const uint16_t*>(&raw);
-    f16x8 h;
+    f16x4 lo, hi;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) h[i] = (_Float16)(bf16_to_f32(e[i]) * scale);
-    *reinterpret_cast<f16x8*>(dst) = h;
+    for (int i = 0; i < 4; ++i) {
+        lo[i] = (_Float16)(bf16_to_f32(e[i]) * scale);
+        hi[i] = (_Float16)(bf16_to_f32(e[4 + i]) * scale);
+    }
+    reinterpret_cast<f16x4*>(dst)[0] = lo;
+    reinterpret_cast<f16x4*>(dst)[1] = hi;
 }
 
 // Broadcast lane `src` of each group of four lanes (src constant after unrolling).
@@ -524,9 +531,10 @@ __global__ __launch_bounds__(512) void gdn_pipe_kernel(WalkArgs p) {
                 F fa[KS_D], fk[KS_D], fq[SUMMARY ? 1 : KS_D];
 #pragma unroll
                 for (int ks = 0; ks < KS_D; ++ks) {
-                    fa[ks] = frag_at<Op>(Kh, L::LDD, 16 * J, ks * 32, lane);
-                    fk[ks] = frag_at<Op>(Kh, L::LDD, 16 * I, ks * 32, lane);
-                    if constexpr (!SUMMARY) fq[ks] = frag_at<Op>(Qh, L::LDD, 16 * I, ks * 32, lane);
+                    // both operands in the same (accumulator) k order
+                    fa[ks] = Op::a_acc(Kh, L::LDD, 16 * J, ks * 32, lane);
+                    fk[ks] = Op::a_acc(Kh, L::LDD, 16 * I, ks * 32, lane);
+                    if constexpr (!SUMMARY) fq[ks] = Op::a_acc(Qh, L::LDD, 16 * I, ks * 32, lane);
                 }
                 f32x4 kk = zero4(), kq = zero4();
 #pragma unroll
