@@ -27,10 +27,10 @@
 //
 // One step (chunk c done, chunk c+1 prepared), phases separated by barriers:
 //   1  state: U = T V + (-T diag gam)(K^ M), O, M update  | key: normalise c+1
-//   2  state: K^ M, Q^ M of c+1                           | key: Gram of c+1
+//   2  state: K^ M, Q^ M of c+1                           | key: K^ K^T of c+1
 //   3  state: V tiles of c+1 as operands, K^T blocks      | key: diagonal
 //                                                           blocks of T
-//   4  (state idle)                                       | key: off-diagonal
+//   4  state: P = tril(Q^ K^T .* G) of c+1               | key: off-diagonal
 //                                                           block columns of T
 // Operand precision as in the segmented walker: fp16 operands (11-bit
 // significand), fp32 accumulation; the state and the solve stay in fp32.
@@ -104,12 +104,25 @@ __device__ __forceinline__ float quad_bcast(float v, int src) {
     }
 }
 
+// Sum of squares of 8 bf16 (bf16 products are exact in fp32).
 __device__ __forceinline__ float sumsq8(const uint4& raw) {
-    const uint16_t* e = reinterpret_cast<const uint16_t*>(&raw);
-    float s = 0.f;
+    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+    float s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, raw.x), __builtin_bit_cast(bf2, raw.x), 0.f, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, raw.y), __builtin_bit_cast(bf2, raw.y), s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, raw.z), __builtin_bit_cast(bf2, raw.z), s, false);
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, raw.w), __builtin_bit_cast(bf2, raw.w), s, false);
+}
+
+// 16x16 transpose of raw bf16 through the matrix core (A * I, exact): lane
+// (g, c) receives a[4g+i][c], i < 4.
+__device__ __forceinline__ f32x4 transpose16_bf16(const uint16_t* a, int lda, int lane) {
+    typedef short s4 __attribute__((ext_vector_type(4)));
+    const int lc = lane & 15, lg = lane >> 4;
+    const s4 fa = *reinterpret_cast<const s4*>(a + lc * lda + 4 * lg);
+    s4 one;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) { const float x = bf16_to_f32(e[i]); s += x * x; }
-    return s;
+    for (int j = 0; j < 4; ++j) one[j] = (4 * lg + j == lc) ? (short)0x3F80 : (short)0;
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(fa, one, zero4(), 0, 0, 0);
 }
 
 }  // namespace
@@ -145,7 +158,7 @@ __global__ __launch_bounds__(512) void gdn_pipe_kernel(WalkArgs p) {
     E* Aoff = reinterpret_cast<E*>(smem + L::O_AOFF);
     float* Adt = reinterpret_cast<float*>(smem + L::O_AD);
     E* Xd = reinterpret_cast<E*>(smem + L::O_XD);
-    E* Vr = reinterpret_cast<E*>(smem + L::O_VR);
+    uint16_t* Vr = reinterpret_cast<uint16_t*>(smem + L::O_VR);   // raw bf16 v rows
     float* vecs = reinterpret_cast<float*>(smem + L::O_VEC);   // [2][g2 | gam | eg | beta][C]
 
     const int tid = threadIdx.x;
@@ -443,7 +456,7 @@ __global__ __launch_bounds__(512) void gdn_pipe_kernel(WalkArgs p) {
                     f32x4 Vacc[NB];
 #pragma unroll
                     for (int rb = 0; rb < NB; ++rb)
-                        Vacc[rb] = transpose16<Op>(Vr + (16 * rb) * L::LDV + col0(ct), L::LDV, lane);
+                        Vacc[rb] = transpose16_bf16(Vr + (16 * rb) * L::LDV + col0(ct), L::LDV, lane);
 #pragma unroll
                     for (int ks = 0; ks < KS_C; ++ks) vB[ct][ks] = Op::b_acc(Vacc, ks);
                 }
@@ -457,7 +470,37 @@ __global__ __launch_bounds__(512) void gdn_pipe_kernel(WalkArgs p) {
                 st4h(Kt + (16 * ib + lc) * L::LDC + 16 * sb + 4 * lg, x[0], x[1], x[2], x[3]);
             }
             __syncthreads();
-            // ---- phase 4: (off-diagonal blocks of T on the key waves)
+            // ---- phase 4: P = tril(Q^ K^T .* G) of chunk pc, needed from the
+            // next step on (the key waves solve for T meanwhile)
+            if constexpr (!SUMMARY) {
+                const float* v_g2 = vecs + vb * 4 * C;
+#pragma unroll
+                for (int u = 0; u < (NTG + NCW - 1) / NCW; ++u) {
+                    const int t = wave + NCW * u;
+                    if (t < NTG) {
+                        int I = 0;
+                        while ((I + 1) * (I + 2) / 2 <= t) ++I;
+                        const int J = t - I * (I + 1) / 2;
+                        f32x4 kq = zero4();
+#pragma unroll
+                        for (int ks = 0; ks < KS_D; ++ks)
+                            kq = Op::mma(Op::a_acc(Kh, L::LDD, 16 * J, ks * 32, lane),
+                                         Op::a_acc(Qh, L::LDD, 16 * I, ks * 32, lane), kq);
+                        // element i: row s = 16J + 4 lg + i (key), column r = 16I + lc (query)
+                        const int r = 16 * I + lc;
+                        const int s0 = 16 * J + 4 * lg;
+                        const float gr = v_g2[r];
+                        const f32x4 gs = *reinterpret_cast<const f32x4*>(v_g2 + s0);
+                        float pv4[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const float e = __builtin_amdgcn_exp2f(fminf(gr - gs[i], 0.f));
+                            pv4[i] = (s0 + i <= r) ? kq[i] * e : 0.f;
+                        }
+                        st4h(Pm + r * L::LDC + s0, pv4[0], pv4[1], pv4[2], pv4[3]);
+                    }
+                }
+            }
             __syncthreads();
         }
     } else {
@@ -485,7 +528,9 @@ __global__ __launch_bounds__(512) void gdn_pipe_kernel(WalkArgs p) {
             for (int it = 0; it < VPT; ++it) {
                 const int idx = ktid + NPT * it;
                 const int r = idx / VPRV, part = idx % VPRV;
-                put8(Vr + r * L::LDV + part * 8, pv[it], 1.0f);
+                uint2* dst = reinterpret_cast<uint2*>(Vr + r * L::LDV + part * 8);
+                dst[0] = make_uint2(pv[it].x, pv[it].y);
+                dst[1] = make_uint2(pv[it].z, pv[it].w);
             }
             if (kw == 0) {
                 float* vg = vecs + vb * 4 * C;
@@ -523,40 +568,34 @@ __global__ __launch_bounds__(512) void gdn_pipe_kernel(WalkArgs p) {
             const float* v_gam = vcur + C;
             const float* v_beta = vcur + 3 * C;
             // ---- phase 2: Gram tiles of chunk pc
-            // Gram tiles (I, J <= I): A (solve scratch) and P
+            // Gram tiles (I, J <= I) of K^ K^T -> A (solve scratch)
             for (int t = kw; t < NTG; t += L::NPW) {
                 int I = 0;
                 while ((I + 1) * (I + 2) / 2 <= t) ++I;
                 const int J = t - I * (I + 1) / 2;
-                F fa[KS_D], fk[KS_D], fq[SUMMARY ? 1 : KS_D];
+                F fa[KS_D], fk[KS_D];
 #pragma unroll
                 for (int ks = 0; ks < KS_D; ++ks) {
                     // both operands in the same (accumulator) k order
                     fa[ks] = Op::a_acc(Kh, L::LDD, 16 * J, ks * 32, lane);
                     fk[ks] = Op::a_acc(Kh, L::LDD, 16 * I, ks * 32, lane);
-                    if constexpr (!SUMMARY) fq[ks] = Op::a_acc(Qh, L::LDD, 16 * I, ks * 32, lane);
                 }
-                f32x4 kk = zero4(), kq = zero4();
+                f32x4 kk = zero4();
 #pragma unroll
-                for (int ks = 0; ks < KS_D; ++ks) {
-                    kk = Op::mma(fa[ks], fk[ks], kk);
-                    if constexpr (!SUMMARY) kq = Op::mma(fa[ks], fq[ks], kq);
-                }
+                for (int ks = 0; ks < KS_D; ++ks) kk = Op::mma(fa[ks], fk[ks], kk);
                 // element i: row s = 16J + 4 lg + i, column r = 16I + lc
                 const int r = 16 * I + lc;
                 const int s0 = 16 * J + 4 * lg;
                 const float br = v_beta[r], gr = v_g2[r];
                 const f32x4 gs = *reinterpret_cast<const f32x4*>(v_g2 + s0);
-                float av[4], pv4[4];
+                float av[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int s_ = s0 + i;
                     // G_rs = 2^(g_r - g_s) <= 1 for s <= r (clamped: rounding can make it > 0)
                     const float e = __builtin_amdgcn_exp2f(fminf(gr - gs[i], 0.f));
                     av[i] = (s_ < r) ? br * kk[i] * e : 0.f;
-                    pv4[i] = (s_ <= r) ? kq[i] * e : 0.f;
                 }
-                if constexpr (!SUMMARY) st4h(Pm + r * L::LDC + s0, pv4[0], pv4[1], pv4[2], pv4[3]);
                 if (I == J) {
                     // diagonal block, stored transposed: Adt[I][s][r] = A[r][s]
 #pragma unroll
