@@ -32,8 +32,11 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 matrix cores, published
 LLC_BYTES = 256 << 20           # Infinity Cache
-KERNEL_SOURCES = ("linear_attention_recurrence_deltanet_amd/csrc/gdn_fwd.hip",
-                  "linear_attention_recurrence_deltanet_amd/csrc/gdn_common.h")
+KERNEL_SOURCES = ("linear_attention_recurrence_deltanet_amd/csrc/gdn_pipe.hip",
+                  "linear_attention_recurrence_deltanet_amd/csrc/gdn_fwd.hip",
+                  "linear_attention_recurrence_deltanet_amd/csrc/gdn_fwd_single.hip",
+                  "linear_attention_recurrence_deltanet_amd/csrc/gdn_common.h",
+                  "linear_attention_recurrence_deltanet_amd/csrc/gdn_api.cpp")
 
 
 def kernel_source_hash() -> str:

@@ -171,17 +171,26 @@ __global__ __launch_bounds__(512) void gdn_pipe_kernel(WalkArgs p) {
 
     const int T = p.T, dv = p.dv;
     const int nseg = p.nseg, nsum = nseg - 1;
+    // Workgroups are dealt to the 8 XCDs round-robin.  Remap so that
+    // consecutive logical indices -- the column tiles and segments of one
+    // head -- share an XCD and its L2: they read the same q/k rows and the
+    // same segment maps at about the same time.
+    int wg = blockIdx.x;
+    {
+        const int w8 = (int)gridDim.x / 8 * 8;
+        if (wg < w8) wg = (wg % 8) * (w8 / 8) + wg / 8;
+    }
     int bh, seg, ctile;
     if constexpr (SUMMARY) {
         const int ncol = (DK + dv) / BV;
-        ctile = blockIdx.x % ncol;
-        const int r = blockIdx.x / ncol;
+        ctile = wg % ncol;
+        const int r = wg / ncol;
         seg = r % nsum;
         bh = r / nsum;
     } else {
         const int ncol = dv / BV;
-        ctile = blockIdx.x % ncol;
-        const int r = blockIdx.x / ncol;
+        ctile = wg % ncol;
+        const int r = wg / ncol;
         seg = r % nseg;
         bh = r / nseg;
     }
