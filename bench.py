@@ -65,7 +65,7 @@ def algorithmic_flops(wl) -> int:
 def read_traffic(kernel_hash: str, workload: str):
     """HBM traffic per launch from the committed rocprofv3 counter summary,
     if it was taken on the current kernel source."""
-    path = os.path.join(ROOT, "profiles", f"gdn_fwd_{workload}_traffic.md")
+    path = os.path.join(ROOT, "profiles", f"gdn_pipe_{workload}_traffic.md")
     if not os.path.exists(path):
         return None
     txt = open(path).read()
