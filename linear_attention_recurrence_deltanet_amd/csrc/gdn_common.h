@@ -160,6 +160,11 @@ __device__ __forceinline__ uint4 buf_load16(rsrc_t r, unsigned off) {
     const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
     return make_uint4(v[0], v[1], v[2], v[3]);
 }
+__device__ __forceinline__ uint2 buf_load8(rsrc_t r, unsigned off) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    return make_uint2(v[0], v[1]);
+}
 __device__ __forceinline__ uint16_t buf_load2(rsrc_t r, unsigned off) {
     return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
 }

@@ -70,7 +70,11 @@ struct PPlan {
     static constexpr int O_XD = O_AD + pal16(NB * ADB * 4);                 // diag inverses
     static constexpr int O_VR = O_XD + pal16(C * LDX * 2);                  // v rows [C][LDV]
     static constexpr int O_VEC = O_VR + pal16(C * LDV * 2);                 // 2 x 4 x C fp32
-    static constexpr int TOTAL = O_VEC + 2 * 4 * C * 4;
+    // summary epilogue: the tile's identity columns of A_s, staged row-major
+    // [DK][DK + 4] over the (then dead) start of the plan
+    static constexpr int LDAS = DK + 4;
+    static constexpr int SZ_AS = SUMMARY ? DK * LDAS * 2 : 0;
+    static constexpr int TOTAL = (O_VEC + 2 * 4 * C * 4) > SZ_AS ? (O_VEC + 2 * 4 * C * 4) : SZ_AS;
 };
 
 template <int DK, int C, int CT, bool SUMMARY>
@@ -130,7 +134,9 @@ __device__ __forceinline__ f32x4 transpose16_bf16(const uint16_t* a, int lda, in
 // SUMMARY = false: main pass (outputs, final state).
 // SUMMARY = true : segment maps (A_s on identity columns, B_s on value
 //                  columns with a zero incoming state), no outputs.
-template <int DK, int C, int CT, bool SUMMARY>
+// FOLD: the main pass of a segmented call (folds the preceding maps); the
+//       unsegmented instantiation carries no fold code at all.
+template <int DK, int C, int CT, bool SUMMARY, bool FOLD>
 __global__ __launch_bounds__(512) void gdn_pipe_kernel(WalkArgs p) {
     typedef PPlan<DK, C, CT, SUMMARY> L;
     typedef OpF16 Op;
@@ -317,33 +323,72 @@ __global__ __launch_bounds__(512) void gdn_pipe_kernel(WalkArgs p) {
                 }
             }
         }
-        if constexpr (!SUMMARY) {
+        if constexpr (FOLD) {
             // fold the preceding segments' maps: M <- A_s M + B_s, operands
-            // straight from global memory (the maps are small and shared)
-            for (int s2 = 0; s2 < seg; ++s2) {
-                const E* Ag = summA_bh + (size_t)s2 * DK * DK;
-                const float* Bg = summB_bh + (size_t)s2 * DK * dv + vbase;
-                F mF[CT][KS_D];
+            // straight from global memory (the maps are small, shared and
+            // L2-resident).  Work unit = 4 row blocks of one map; the next
+            // unit's operands load while the current one is applied.
+            constexpr int GI = NDB >= 8 ? 2 : 4, UPM = NDB / GI;   // units per map: 1 or 4
+            F fa[2][GI][KS_D];
+            f32x4 fb[2][CT][GI];
+            F mF[CT][KS_D];
+            const int nu = seg * UPM;
+            // buffer loads (not flat): the waits can then count only the
+            // previous unit's loads
+            const rsrc_t rA = make_rsrc(summA_bh, (unsigned)(nsum * DK * DK * 2));
+            const rsrc_t rB = make_rsrc(summB_bh, (unsigned)(nsum * DK * dv * 4));
+            auto fload = [&](int buf, int u) {
+                const int s2 = u / UPM, ib0 = (u % UPM) * GI;
 #pragma unroll
-                for (int ct = 0; ct < CT; ++ct)
+                for (int i = 0; i < GI; ++i) {
 #pragma unroll
-                    for (int ks = 0; ks < KS_D; ++ks) mF[ct][ks] = Op::b_acc(Macc[ct], ks);
-#pragma unroll
-                for (int ib = 0; ib < NDB; ++ib) {
-                    F fa[KS_D];
-#pragma unroll
-                    for (int ks = 0; ks < KS_D; ++ks) fa[ks] = Op::a_acc(Ag, DK, 16 * ib, 32 * ks, lane);
+                    for (int ks = 0; ks < KS_D; ++ks) {
+                        const unsigned off = (unsigned)(s2 * DK * DK * 2 + (((ib0 + i) * KS_D + ks) * 64 + lane) * 16);
+                        fa[buf][i][ks] = __builtin_bit_cast(F, buf_load16(rA, off));
+                    }
 #pragma unroll
                     for (int ct = 0; ct < CT; ++ct) {
-                        f32x4 acc;
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            acc[i] = Bg[(unsigned)((16 * ib + 4 * lg + i) * dv + col0(ct) + lc)];
-#pragma unroll
-                        for (int ks = 0; ks < KS_D; ++ks) acc = Op::mma(fa[ks], mF[ct][ks], acc);
-                        Macc[ct][ib] = acc;
+                        const int c16 = (vbase + col0(ct)) / 16;
+                        const unsigned off = (unsigned)(s2 * DK * dv * 4 + ((c16 * NDB + ib0 + i) * 64 + lane) * 16);
+                        fb[buf][ct][i] = __builtin_bit_cast(f32x4, buf_load16(rB, off));
                     }
-                    __builtin_amdgcn_sched_barrier(0);   // bound the operand hoisting
+                }
+            };
+            // gi: which 4 row blocks (static in each call site)
+            auto fapply = [&](int buf, int gi) {
+                if (gi == 0) {
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                        for (int ks = 0; ks < KS_D; ++ks) mF[ct][ks] = Op::b_acc(Macc[ct], ks);
+                }
+#pragma unroll
+                for (int i = 0; i < GI; ++i)
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct) {
+                        f32x4 acc = fb[buf][ct][i];
+#pragma unroll
+                        for (int ks = 0; ks < KS_D; ++ks) acc = Op::mma(fa[buf][i][ks], mF[ct][ks], acc);
+                        Macc[ct][GI * gi + i] = acc;
+                    }
+            };
+            if (nu > 0) fload(0, 0);
+            if constexpr (UPM == 1) {
+                // one unit per map: two maps per iteration keep the buffers static
+                for (int u = 0; u < nu; u += 2) {
+                    if (u + 1 < nu) fload(1, u + 1);
+                    fapply(0, 0);
+                    if (u + 2 < nu) fload(0, u + 2);
+                    if (u + 1 < nu) fapply(1, 0);
+                }
+            } else {
+                for (int s2 = 0; s2 < seg; ++s2) {
+#pragma unroll
+                    for (int g = 0; g < UPM; ++g) {
+                        const int u = s2 * UPM + g;
+                        if (u + 1 < nu) fload((g + 1) & 1, u + 1);
+                        fapply(g & 1, g);
+                    }
                 }
             }
         }
@@ -678,26 +723,49 @@ __global__ __launch_bounds__(512) void gdn_pipe_kernel(WalkArgs p) {
         }
     }
 
-    // ---------------- results (state waves) --------------------------------
-    if (is_state) {
+    // ---------------- results ----------------------------------------------
+    if constexpr (SUMMARY) {
+        // Segment maps in the order the main pass consumes them: A_s as MFMA
+        // A-operand fragments [ib][ks][lane] x 16 bytes (fp16), B_s in
+        // accumulator order [column block of 16][ib][lane] x f32x4.  Each
+        // fold operand is then one coalesced 16-byte load per lane.
+        __syncthreads();                                  // both role loops done: LDS free
+        E* As = reinterpret_cast<E*>(smem);
+        if (is_state) {
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-            if constexpr (SUMMARY) {
+            for (int ct = 0; ct < CT; ++ct) {
                 if (ident(ct)) {
-                    // A_s in operand precision, row-major [DK][DK]
-                    E* dst = summA_bh + (size_t)seg * DK * DK + ctile * BV + col0(ct) + lc;
+                    const int c = ctile * BV + col0(ct) + lc;     // identity column = k index
 #pragma unroll
                     for (int ib = 0; ib < NDB; ++ib)
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) dst[(unsigned)((16 * ib + 4 * lg + i) * DK)] = (E)Macc[ct][ib][i];
+                        for (int i = 0; i < 4; ++i) As[(16 * ib + 4 * lg + i) * L::LDAS + c] = (E)Macc[ct][ib][i];
                 } else {
-                    float* dst = summB_bh + (size_t)seg * DK * dv + vbase + col0(ct) + lc;
+                    const int c16 = (vbase + col0(ct)) / 16;
+                    f32x4* dst = reinterpret_cast<f32x4*>(summB_bh + (size_t)seg * DK * dv) + c16 * NDB * 64 + lane;
 #pragma unroll
-                    for (int ib = 0; ib < NDB; ++ib)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) dst[(unsigned)((16 * ib + 4 * lg + i) * dv)] = Macc[ct][ib][i];
+                    for (int ib = 0; ib < NDB; ++ib) dst[ib * 64] = Macc[ct][ib];
                 }
-            } else {
+            }
+        }
+        __syncthreads();
+        const int k0 = ctile * BV;                        // first identity column of the tile
+        if (k0 < DK) {
+            const int ks0 = k0 / 32, nks = (min(DK, k0 + BV) - k0) / 32;
+            uint4* dstA = reinterpret_cast<uint4*>(summA_bh + (size_t)seg * DK * DK);
+            for (int f = wave; f < NDB * nks; f += NW) {
+                const int ib = f / nks, ks = ks0 + f % nks;
+                const F fr = Op::a_acc(As, L::LDAS, 16 * ib, 32 * ks, lane);
+                dstA[(ib * KS_D + ks) * 64 + lane] = __builtin_bit_cast(uint4, fr);
+            }
+        }
+    } else {
+        // Kept in this shape on purpose: folding the role test into the store
+        // condition changed the compiler's block layout and cost 16% on long
+        // unsegmented walks (measured on MI355X, same box, A/B).
+        if (is_state) {
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
                 if (p.state_out && seg == nseg - 1) {
                     float* sp = p.state_out + (size_t)bh * DK * dv + vbase + col0(ct) + lc;
 #pragma unroll
@@ -721,12 +789,15 @@ hipError_t launch_pipe_t(const WalkArgs& a, hipStream_t s) {
     const int bh = a.B * a.H;
     if (a.nseg > 1) {
         const int grid = bh * (a.nseg - 1) * ((DK + a.dv) / (64 * CTS));
-        hipLaunchKernelGGL((gdn_pipe_kernel<DK, C, CTS, true>), dim3(grid), dim3(512), 0, s, a);
+        hipLaunchKernelGGL((gdn_pipe_kernel<DK, C, CTS, true, false>), dim3(grid), dim3(512), 0, s, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     const int grid = bh * a.nseg * (a.dv / 64);
-    hipLaunchKernelGGL((gdn_pipe_kernel<DK, C, 1, false>), dim3(grid), dim3(512), 0, s, a);
+    if (a.nseg > 1)
+        hipLaunchKernelGGL((gdn_pipe_kernel<DK, C, 1, false, true>), dim3(grid), dim3(512), 0, s, a);
+    else
+        hipLaunchKernelGGL((gdn_pipe_kernel<DK, C, 1, false, false>), dim3(grid), dim3(512), 0, s, a);
     return hipGetLastError();
 }
 
