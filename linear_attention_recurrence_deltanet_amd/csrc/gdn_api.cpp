@@ -113,7 +113,7 @@ Plan pipe_plan(int B, int H, int T, int dk, int dv, int chunk) {
     const long long bh = (long long)B * H;
     const long long base = bh * (dv / 64);                                   // main workgroups / segment
     const long long sb = bh * ((dk + dv) / (64 * gdn::pipe_summary_tiles(dk, dv)));  // summary
-    const double fold = dk == 64 ? 0.3 : 0.6;
+    const double fold = dk == 64 ? 0.15 : 0.35;           // measured cost of one folded map
     auto rounds = [](long long wgs) { return (double)((wgs + 255) / 256); };
     int best_n = 1;
     double best = rounds(base) * (nchunks + 1);

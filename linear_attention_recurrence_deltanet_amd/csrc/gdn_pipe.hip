@@ -803,8 +803,7 @@ hipError_t launch_pipe_t(const WalkArgs& a, hipStream_t s) {
 
 template <int DK, int C>
 hipError_t pipe_cts(const WalkArgs& a, int cts, hipStream_t s) {
-    if constexpr (DK == 64)
-        if (cts == 2) return launch_pipe_t<DK, C, 2>(a, s);
+    if (cts == 2) return launch_pipe_t<DK, C, 2>(a, s);
     return launch_pipe_t<DK, C, 1>(a, s);
 }
 
@@ -824,14 +823,14 @@ bool pipe_supported(int in_f32, int dk, int dv, int chunk) {
 }
 
 int pipe_summary_tiles(int dk, int dv) {
-    return (dk == 64 && (dk + dv) % 128 == 0) ? 2 : 1;
+    return (dk + dv) % 128 == 0 ? 2 : 1;
 }
 
 hipError_t launch_pipe(const WalkArgs& a, int chunk, hipStream_t s) {
     const int cts = pipe_summary_tiles(a.dk, a.dv);
     switch (a.dk) {
     case 64: return pipe_c<64>(a, chunk, cts, s);
-    case 128: return pipe_c<128>(a, chunk, 1, s);
+    case 128: return pipe_c<128>(a, chunk, cts, s);
     default: return hipErrorInvalidValue;
     }
 }
