@@ -286,6 +286,20 @@ __global__ __launch_bounds__(512) void gdn_pipe_kernel(WalkArgs p) {
             }
         }
     };
+    if constexpr (SUMMARY) {
+        // Snapshot of the incoming state for the main pass (state_in may alias
+        // state_out): segment 0's workgroups copy their value columns, rows of
+        // 16-byte pieces spread over all 512 threads.
+        if (seg == 0 && p.snap && p.state_in && vlo < BV) {
+            const int pr = (BV - vlo) / 4;                       // 16-byte pieces per row
+            const size_t base = (size_t)bh * DK * dv + vbase + vlo;
+            for (int e = tid; e < DK * pr; e += L::NT) {
+                const int r = e / pr, c4 = e % pr;
+                *reinterpret_cast<float4*>(p.snap + base + (size_t)r * dv + 4 * c4) =
+                    *reinterpret_cast<const float4*>(p.state_in + base + (size_t)r * dv + 4 * c4);
+            }
+        }
+    }
     if (!is_state && nch > 0) prefetch(ch0);
 
     // The two roles run separate loops with the same barrier sequence, so the
@@ -305,11 +319,6 @@ __global__ __launch_bounds__(512) void gdn_pipe_kernel(WalkArgs p) {
 #pragma unroll
                         for (int i = 0; i < 4; ++i)
                             Macc[ct][ib][i] = (16 * ib + 4 * lg + i == gcol) ? 1.f : 0.f;
-                } else if (seg == 0 && p.snap && p.state_in) {
-                    // snapshot of the incoming state (state_in may alias state_out)
-                    const float* sp = p.state_in + (size_t)bh * DK * dv + vcol;
-                    float* dp = p.snap + (size_t)bh * DK * dv + vcol;
-                    for (int i = lg; i < DK; i += 4) dp[i * dv] = sp[i * dv];
                 }
             } else {
                 const float* sinp = nseg > 1 ? (p.state_in ? p.snap : nullptr) : p.state_in;
@@ -329,8 +338,12 @@ __global__ __launch_bounds__(512) void gdn_pipe_kernel(WalkArgs p) {
             // L2-resident).  Work unit = 4 row blocks of one map; the next
             // unit's operands load while the current one is applied.
             constexpr int GI = NDB >= 8 ? 2 : 4, UPM = NDB / GI;   // units per map: 1 or 4
-            F fa[2][GI][KS_D];
-            f32x4 fb[2][CT][GI];
+            // prefetch depth in units; the loop is unrolled by UF = max(PD, UPM)
+            // (one divides the other) so buffer and row-block indices are static
+            constexpr int PD = UPM == 1 ? 3 : 2;
+            constexpr int UF = PD > UPM ? PD : UPM;
+            F fa[PD][GI][KS_D];
+            f32x4 fb[PD][CT][GI];
             F mF[CT][KS_D];
             const int nu = seg * UPM;
             // buffer loads (not flat): the waits can then count only the
@@ -372,23 +385,14 @@ __global__ __launch_bounds__(512) void gdn_pipe_kernel(WalkArgs p) {
                         Macc[ct][GI * gi + i] = acc;
                     }
             };
-            if (nu > 0) fload(0, 0);
-            if constexpr (UPM == 1) {
-                // one unit per map: two maps per iteration keep the buffers static
-                for (int u = 0; u < nu; u += 2) {
-                    if (u + 1 < nu) fload(1, u + 1);
-                    fapply(0, 0);
-                    if (u + 2 < nu) fload(0, u + 2);
-                    if (u + 1 < nu) fapply(1, 0);
-                }
-            } else {
-                for (int s2 = 0; s2 < seg; ++s2) {
 #pragma unroll
-                    for (int g = 0; g < UPM; ++g) {
-                        const int u = s2 * UPM + g;
-                        if (u + 1 < nu) fload((g + 1) & 1, u + 1);
-                        fapply(g & 1, g);
-                    }
+            for (int j = 0; j < PD - 1; ++j)
+                if (j < nu) fload(j, j);
+            for (int u = 0; u < nu; u += UF) {
+#pragma unroll
+                for (int j = 0; j < UF; ++j) {
+                    if (u + j + PD - 1 < nu) fload((j + PD - 1) % PD, u + j + PD - 1);
+                    if (u + j < nu) fapply(j % PD, j % UPM);
                 }
             }
         }
