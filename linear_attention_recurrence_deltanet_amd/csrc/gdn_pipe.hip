@@ -74,7 +74,11 @@ struct PPlan {
     // [DK][DK + 4] over the (then dead) start of the plan
     static constexpr int LDAS = DK + 4;
     static constexpr int SZ_AS = SUMMARY ? DK * LDAS * 2 : 0;
-    static constexpr int TOTAL = (O_VEC + 2 * 4 * C * 4) > SZ_AS ? (O_VEC + 2 * 4 * C * 4) : SZ_AS;
+    // main pass of a segmented call: two segment maps staged for the fold
+    static constexpr int SZ_FOLD = SUMMARY ? 0 : 2 * DK * DK * 2;
+    static constexpr int SZ_STEP = O_VEC + 2 * 4 * C * 4;
+    static constexpr int TOTAL = SZ_STEP > SZ_AS ? (SZ_STEP > SZ_FOLD ? SZ_STEP : SZ_FOLD)
+                                                 : (SZ_AS > SZ_FOLD ? SZ_AS : SZ_FOLD);
 };
 
 template <int DK, int C, int CT, bool SUMMARY>
@@ -106,6 +110,18 @@ __device__ __forceinline__ float quad_bcast(float v, int src) {
     case 2: return dpp<0xAA>(v);
     default: return dpp<0xFF>(v);
     }
+}
+
+// Fragment (row block rb, k-step ks) of a lower-triangular C x C operand in
+// accumulator k order.  A k-step spans the column blocks 2ks and 2ks+1; when
+// 2ks+1 > rb the second is above the diagonal: zero in registers, not read.
+template <int LD>
+__device__ __forceinline__ OpF16::frag a_lower(const _Float16* base, int rb, int ks, int lane) {
+    if (2 * ks + 1 > rb) {
+        const u16x4 lo = *reinterpret_cast<const u16x4*>(base + (16 * rb + (lane & 15)) * LD + 32 * ks + 4 * (lane >> 4));
+        return OpF16::frag{lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
+    }
+    return OpF16::a_acc(base, LD, 16 * rb, 32 * ks, lane);
 }
 
 // Sum of squares of 8 bf16 (bf16 products are exact in fp32).
@@ -236,15 +252,6 @@ __global__ __launch_bounds__(512) void gdn_pipe_kernel(WalkArgs p) {
     const rsrc_t ro_ = make_rsrc(SUMMARY ? nullptr : (const char*)p.out + (size_t)bh * T * dv * osz,
                                  SUMMARY ? 0u : (unsigned)T * dv * osz);
 
-    // Structurally zero upper blocks of the lower-triangular operands.
-    for (int e = tid; e < C * C; e += L::NT) {
-        const int r = e / C, s = e % C;
-        if ((s >> 4) > (r >> 4)) {
-            if constexpr (!SUMMARY) Pm[r * L::LDC + s] = (E)0.f;
-            Tm[r * L::LDC + s] = (E)0.f;
-            T2n[r * L::LDC + s] = (E)0.f;
-        }
-    }
 
     // ---------------- state-wave registers ---------------------------------
     // Macc[ct][ib] lane (lg, lc): state rows 16 ib + 4 lg + i of column col0(ct) + lc
@@ -300,12 +307,8 @@ __global__ __launch_bounds__(512) void gdn_pipe_kernel(WalkArgs p) {
             }
         }
     }
-    if (!is_state && nch > 0) prefetch(ch0);
-
-    // The two roles run separate loops with the same barrier sequence, so the
-    // compiler allocates registers per role (the branch is wave-uniform).
-    if (is_state) {
-        // ---- incoming state of the walk (before the first step)
+    // ---- incoming state of the walk (state waves)
+    auto init_state = [&]() {
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
             const int gcol = ctile * BV + col0(ct) + lc;      // summary: [ident | value]
@@ -332,70 +335,96 @@ __global__ __launch_bounds__(512) void gdn_pipe_kernel(WalkArgs p) {
                 }
             }
         }
-        if constexpr (FOLD) {
-            // fold the preceding segments' maps: M <- A_s M + B_s, operands
-            // straight from global memory (the maps are small, shared and
-            // L2-resident).  Work unit = 4 row blocks of one map; the next
-            // unit's operands load while the current one is applied.
-            constexpr int GI = NDB >= 8 ? 2 : 4, UPM = NDB / GI;   // units per map: 1 or 4
-            // prefetch depth in units; the loop is unrolled by UF = max(PD, UPM)
-            // (one divides the other) so buffer and row-block indices are static
-            constexpr int PD = UPM == 1 ? 3 : 2;
-            constexpr int UF = PD > UPM ? PD : UPM;
-            F fa[PD][GI][KS_D];
-            f32x4 fb[PD][CT][GI];
+    };
+    if constexpr (FOLD) {
+        if (is_state) init_state();           // before the fold, which needs every wave
+    }
+    if constexpr (FOLD) {
+        // Fold the preceding segments' maps into the incoming state,
+        // M <- A_s M + B_s.  A_s (d_k x d_k, fp16, MFMA fragment order) is the
+        // same for every state wave, so it is staged once per workgroup: the
+        // key waves copy map s+1 into LDS (and load map s+2 into registers)
+        // while the state waves apply map s; one barrier per map.
+        E* Ast = reinterpret_cast<E*>(smem);                 // [2][DK*DK] fragment order
+        constexpr int APK = DK * DK * 2 / 16 / NPT;          // 16-byte pieces per key thread
+        const rsrc_t rA = make_rsrc(summA_bh, (unsigned)(nsum * DK * DK * 2));
+        const rsrc_t rB = make_rsrc(summB_bh, (unsigned)(nsum * DK * dv * 4));
+        uint4 ka[2][APK];                                    // key waves: maps in flight
+        f32x4 fb[2][CT][NDB];                                // state waves: B_s of own columns
+        auto kload = [&](int buf, int s2) {
+#pragma unroll
+            for (int j = 0; j < APK; ++j)
+                ka[buf][j] = buf_load16(rA, (unsigned)(s2 * DK * DK * 2 + (ktid + NPT * j) * 16));
+        };
+        auto kstore = [&](int buf, int lbuf) {
+            uint4* dst = reinterpret_cast<uint4*>(Ast + lbuf * DK * DK);
+#pragma unroll
+            for (int j = 0; j < APK; ++j) dst[ktid + NPT * j] = ka[buf][j];
+        };
+        auto bload = [&](int buf, int s2) {
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+                const int c16 = (vbase + col0(ct)) / 16;
+#pragma unroll
+                for (int ib = 0; ib < NDB; ++ib)
+                    fb[buf][ct][ib] = __builtin_bit_cast(f32x4, buf_load16(rB,
+                        (unsigned)(s2 * DK * dv * 4 + ((c16 * NDB + ib) * 64 + lane) * 16)));
+            }
+        };
+        auto apply = [&](int buf, int lbuf) {
             F mF[CT][KS_D];
-            const int nu = seg * UPM;
-            // buffer loads (not flat): the waits can then count only the
-            // previous unit's loads
-            const rsrc_t rA = make_rsrc(summA_bh, (unsigned)(nsum * DK * DK * 2));
-            const rsrc_t rB = make_rsrc(summB_bh, (unsigned)(nsum * DK * dv * 4));
-            auto fload = [&](int buf, int u) {
-                const int s2 = u / UPM, ib0 = (u % UPM) * GI;
 #pragma unroll
-                for (int i = 0; i < GI; ++i) {
+            for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-                    for (int ks = 0; ks < KS_D; ++ks) {
-                        const unsigned off = (unsigned)(s2 * DK * DK * 2 + (((ib0 + i) * KS_D + ks) * 64 + lane) * 16);
-                        fa[buf][i][ks] = __builtin_bit_cast(F, buf_load16(rA, off));
-                    }
+                for (int ks = 0; ks < KS_D; ++ks) mF[ct][ks] = Op::b_acc(Macc[ct], ks);
+            const uint4* As = reinterpret_cast<const uint4*>(Ast + lbuf * DK * DK);
 #pragma unroll
-                    for (int ct = 0; ct < CT; ++ct) {
-                        const int c16 = (vbase + col0(ct)) / 16;
-                        const unsigned off = (unsigned)(s2 * DK * dv * 4 + ((c16 * NDB + ib0 + i) * 64 + lane) * 16);
-                        fb[buf][ct][i] = __builtin_bit_cast(f32x4, buf_load16(rB, off));
-                    }
-                }
-            };
-            // gi: which 4 row blocks (static in each call site)
-            auto fapply = [&](int buf, int gi) {
-                if (gi == 0) {
+            for (int ib = 0; ib < NDB; ++ib) {
+                F fa[KS_D];
 #pragma unroll
-                    for (int ct = 0; ct < CT; ++ct)
+                for (int ks = 0; ks < KS_D; ++ks) fa[ks] = __builtin_bit_cast(F, As[(ib * KS_D + ks) * 64 + lane]);
 #pragma unroll
-                        for (int ks = 0; ks < KS_D; ++ks) mF[ct][ks] = Op::b_acc(Macc[ct], ks);
-                }
+                for (int ct = 0; ct < CT; ++ct) {
+                    f32x4 acc = fb[buf][ct][ib];
 #pragma unroll
-                for (int i = 0; i < GI; ++i)
-#pragma unroll
-                    for (int ct = 0; ct < CT; ++ct) {
-                        f32x4 acc = fb[buf][ct][i];
-#pragma unroll
-                        for (int ks = 0; ks < KS_D; ++ks) acc = Op::mma(fa[buf][i][ks], mF[ct][ks], acc);
-                        Macc[ct][GI * gi + i] = acc;
-                    }
-            };
-#pragma unroll
-            for (int j = 0; j < PD - 1; ++j)
-                if (j < nu) fload(j, j);
-            for (int u = 0; u < nu; u += UF) {
-#pragma unroll
-                for (int j = 0; j < UF; ++j) {
-                    if (u + j + PD - 1 < nu) fload((j + PD - 1) % PD, u + j + PD - 1);
-                    if (u + j < nu) fapply(j % PD, j % UPM);
+                    for (int ks = 0; ks < KS_D; ++ks) acc = Op::mma(fa[ks], mF[ct][ks], acc);
+                    Macc[ct][ib] = acc;
                 }
             }
+        };
+        // one step of the fold: map s2 applied from LDS copy s2 & 1
+        auto fstep = [&](int s2, int par) {
+            if (is_state) {
+                if (s2 + 1 < seg) bload(par ^ 1, s2 + 1);
+                apply(par, par);
+            } else {
+                if (s2 + 1 < seg) kstore(par ^ 1, par ^ 1);
+                if (s2 + 2 < seg) kload(par, s2 + 2);
+            }
+            __syncthreads();
+        };
+        if (seg > 0) {
+            if (is_state) {
+                bload(0, 0);
+            } else {
+                kload(0, 0);
+                kstore(0, 0);
+                if (seg > 1) kload(1, 1);
+            }
+            __syncthreads();
+            for (int s2 = 0; s2 < seg; s2 += 2) {
+                fstep(s2, 0);
+                if (s2 + 1 < seg) fstep(s2 + 1, 1);
+            }
         }
+    }
+
+    if (!is_state && nch > 0) prefetch(ch0);
+
+    // The two roles run separate loops with the same barrier sequence, so the
+    // compiler allocates registers per role (the branch is wave-uniform).
+    if (is_state) {
+        if constexpr (!FOLD) init_state();
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
@@ -424,8 +453,8 @@ __global__ __launch_bounds__(512) void gdn_pipe_kernel(WalkArgs p) {
                         // T and P are lower triangular: k-steps past row block rb are zero
 #pragma unroll
                         for (int ks = 0; ks <= rb / 2; ++ks) {
-                            if (!idt) acc = Op::mma(Op::a_acc(Tm, L::LDC, 16 * rb, 32 * ks, lane), vB[ct][ks], acc);
-                            acc = Op::mma(Op::a_acc(T2n, L::LDC, 16 * rb, 32 * ks, lane), kmB[ks], acc);
+                            if (!idt) acc = Op::mma(a_lower<L::LDC>(Tm, rb, ks, lane), vB[ct][ks], acc);
+                            acc = Op::mma(a_lower<L::LDC>(T2n, rb, ks, lane), kmB[ks], acc);
                         }
                         U[rb] = acc;
                     }
@@ -443,7 +472,7 @@ __global__ __launch_bounds__(512) void gdn_pipe_kernel(WalkArgs p) {
                             for (int i = 0; i < 4; ++i) o[i] = QM[ct][rb][i] * gm[i];
 #pragma unroll
                             for (int ks = 0; ks <= rb / 2; ++ks)
-                                o = Op::mma(Op::a_acc(Pm, L::LDC, 16 * rb, 32 * ks, lane), uB[ks], o);
+                                o = Op::mma(a_lower<L::LDC>(Pm, rb, ks, lane), uB[ks], o);
                             // rows past T fall outside the buffer and are dropped
                             const unsigned o0 = (unsigned)(t0 + 16 * rb + 4 * lg) * (unsigned)dv + ocol;
                             if (p.out_bf16) {
