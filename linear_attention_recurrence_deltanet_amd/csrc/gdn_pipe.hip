@@ -124,6 +124,33 @@ __device__ __forceinline__ OpF16::frag a_lower(const _Float16* base, int rb, int
     return OpF16::a_acc(base, LD, 16 * rb, 32 * ks, lane);
 }
 
+// Tile t of P = tril(Q^ K^T .* G) (lower-triangle enumeration: t -> (I, J <= I)).
+template <class L>
+__device__ __forceinline__ void p_tile(const _Float16* Kh, const _Float16* Qh, _Float16* Pm,
+                                       const float* v_g2, int t, int lane) {
+    constexpr int KS_D = L::NDB * 16 / 32;
+    int I = 0;
+    while ((I + 1) * (I + 2) / 2 <= t) ++I;
+    const int J = t - I * (I + 1) / 2;
+    f32x4 kq = zero4();
+#pragma unroll
+    for (int ks = 0; ks < KS_D; ++ks)
+        kq = OpF16::mma(OpF16::a_acc(Kh, L::LDD, 16 * J, ks * 32, lane),
+                        OpF16::a_acc(Qh, L::LDD, 16 * I, ks * 32, lane), kq);
+    // element i: row s = 16J + 4 lg + i (key), column r = 16I + lc (query)
+    const int r = 16 * I + (lane & 15);
+    const int s0 = 16 * J + 4 * (lane >> 4);
+    const float gr = v_g2[r];
+    const f32x4 gs = *reinterpret_cast<const f32x4*>(v_g2 + s0);
+    float pv4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float e = __builtin_amdgcn_exp2f(fminf(gr - gs[i], 0.f));
+        pv4[i] = (s0 + i <= r) ? kq[i] * e : 0.f;
+    }
+    st4h(Pm + r * L::LDC + s0, pv4[0], pv4[1], pv4[2], pv4[3]);
+}
+
 // Sum of squares of 8 bf16 (bf16 products are exact in fp32).
 __device__ __forceinline__ float sumsq8(const uint4& raw) {
     typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
@@ -160,6 +187,10 @@ __global__ __launch_bounds__(512) void gdn_pipe_kernel(WalkArgs p) {
     typedef Op::frag F;
     constexpr int NB = L::NB, NDB = L::NDB, BV = L::BV, NCW = L::NCW, NPT = L::NPT, NW = L::NW;
     constexpr int NTG = NB * (NB + 1) / 2;           // lower-triangle Gram tiles
+    // P tiles: NTS on the state waves (a multiple of their count), the rest
+    // (at most two) on the last key waves
+    constexpr int NTS = NTG >= 2 * L::NCW ? L::NCW * (NTG / L::NCW) : NTG;
+    static_assert(NTG - NTS <= 2 && (NTS % L::NCW == 0 || NTS == NTG), "P tile split");
     constexpr int NTW = NDB * NB;                    // 16x16 blocks of K^T
     constexpr int VPRQ = DK / 8;                     // 16-byte pieces per q/k row
     constexpr int VPRV = BV / 8;                     // 16-byte pieces per v row of the tile
@@ -167,6 +198,7 @@ __global__ __launch_bounds__(512) void gdn_pipe_kernel(WalkArgs p) {
     constexpr int VV = C * VPRV, VPT = VV / NPT;
     static_assert(QV % NPT == 0 && VV % NPT == 0, "whole key waves per row set");
     constexpr int TPL = C >= 64 ? C / 64 : 1;        // decay tokens per lane of the scan wave
+    constexpr int SCANW = L::NPW - 1;                // key wave of the decay scan (no block column)
     constexpr int KS_D = DK / 32, KS_C = C / 32;     // k-steps over DK and over C
 
     __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
@@ -284,7 +316,7 @@ __global__ __launch_bounds__(512) void gdn_pipe_kernel(WalkArgs p) {
             pv[it] = (part * 8 >= vlo) ? buf_load16(rv_, (unsigned)((t0 + r) * dv + vbase + part * 8) * 2u)
                                        : make_uint4(0u, 0u, 0u, 0u);
         }
-        if (kw == 0) {
+        if (kw == SCANW) {
 #pragma unroll
             for (int e = 0; e < TPL; ++e) {
                 const unsigned off = (unsigned)(t0 + lane * TPL + e) * 2u;
@@ -558,35 +590,13 @@ __global__ __launch_bounds__(512) void gdn_pipe_kernel(WalkArgs p) {
             }
             __syncthreads();
             // ---- phase 4: P = tril(Q^ K^T .* G) of chunk pc, needed from the
-            // next step on (the key waves solve for T meanwhile)
+            // next step on (the key waves solve for T meanwhile; the two key
+            // waves with the shortest block columns take the last tiles)
             if constexpr (!SUMMARY) {
                 const float* v_g2 = vecs + vb * 4 * C;
 #pragma unroll
-                for (int u = 0; u < (NTG + NCW - 1) / NCW; ++u) {
-                    const int t = wave + NCW * u;
-                    if (t < NTG) {
-                        int I = 0;
-                        while ((I + 1) * (I + 2) / 2 <= t) ++I;
-                        const int J = t - I * (I + 1) / 2;
-                        f32x4 kq = zero4();
-#pragma unroll
-                        for (int ks = 0; ks < KS_D; ++ks)
-                            kq = Op::mma(Op::a_acc(Kh, L::LDD, 16 * J, ks * 32, lane),
-                                         Op::a_acc(Qh, L::LDD, 16 * I, ks * 32, lane), kq);
-                        // element i: row s = 16J + 4 lg + i (key), column r = 16I + lc (query)
-                        const int r = 16 * I + lc;
-                        const int s0 = 16 * J + 4 * lg;
-                        const float gr = v_g2[r];
-                        const f32x4 gs = *reinterpret_cast<const f32x4*>(v_g2 + s0);
-                        float pv4[4];
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const float e = __builtin_amdgcn_exp2f(fminf(gr - gs[i], 0.f));
-                            pv4[i] = (s0 + i <= r) ? kq[i] * e : 0.f;
-                        }
-                        st4h(Pm + r * L::LDC + s0, pv4[0], pv4[1], pv4[2], pv4[3]);
-                    }
-                }
+                for (int u = 0; u < (NTS + NCW - 1) / NCW; ++u)
+                    if (wave + NCW * u < NTS) p_tile<L>(Kh, Qh, Pm, v_g2, wave + NCW * u, lane);
             }
             __syncthreads();
         }
@@ -619,7 +629,7 @@ __global__ __launch_bounds__(512) void gdn_pipe_kernel(WalkArgs p) {
                 dst[0] = make_uint2(pv[it].x, pv[it].y);
                 dst[1] = make_uint2(pv[it].z, pv[it].w);
             }
-            if (kw == 0) {
+            if (kw == SCANW) {
                 float* vg = vecs + vb * 4 * C;
                 float la[TPL], bb[TPL];
                 float run = 0.f;
@@ -751,6 +761,9 @@ __global__ __launch_bounds__(512) void gdn_pipe_kernel(WalkArgs p) {
                         st4h(Tt + c * L::LDC + 16 * i + 4 * lg, -t[0], -t[1], -t[2], -t[3]);
                     }
                 }
+            }
+            if constexpr (!SUMMARY && NTG > NTS) {
+                if (kw >= L::NPW - (NTG - NTS)) p_tile<L>(Kh, Qh, Pm, v_g2, NTS + (L::NPW - 1 - kw), lane);
             }
             __syncthreads();
         }
