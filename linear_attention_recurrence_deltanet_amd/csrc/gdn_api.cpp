@@ -44,7 +44,7 @@ int validate(const void* q, const void* k, const void* v, const void* alpha, con
     if (B <= 0 || H <= 0) return fail(GDN_ERR_ARG, "B and H must be positive");
     if (T < 0) return fail(GDN_ERR_ARG, "T must be non-negative");
     if ((long long)B * H * 8 > 0x7fffffffLL) return fail(GDN_ERR_ARG, "B*H too large");
-    if ((long long)T * (dk > dv ? dk : dv) * 4 > 0x7fffffffLL * 4LL)
+    if ((long long)T * (dk > dv ? dk : dv) * 4 > 0x7fffffffLL)   // byte ranges of one head below 2 GiB
         return fail(GDN_ERR_ARG, "T too large");
     if (!head_ok(dk)) return fail(GDN_ERR_UNSUPPORTED, "dk must be 32, 64 or 128");
     if (!head_ok(dv)) return fail(GDN_ERR_UNSUPPORTED, "dv must be 32, 64 or 128");
@@ -103,30 +103,41 @@ size_t seg_workspace(int in_f32, int B, int H, int dk, int dv, int nseg) {
 }
 
 // Pipelined walker: pick the segment count with the shortest estimated
-// critical path, counted in chunk steps: a walk of L chunks takes about L + 1
-// steps, a launch of more workgroups than compute units runs in rounds, and
-// each preceding segment adds a fold of its map to the main pass.
+// critical path, in units of one chunk step of the unsegmented walk.
+// Unsegmented, a walk of L chunks takes about L + 1 steps.  Segmented, every
+// segment is walked once on [identity | value] columns (heavier steps), then
+// the correction pass pays a launch and its first memory round trips, one
+// folded map per preceding segment and the rewrite of the segment's outputs.
+// A launch of more workgroups than compute units runs in rounds.  Constants
+// measured on MI355X.
 Plan pipe_plan(int B, int H, int T, int dk, int dv, int chunk) {
     Plan pl{};
     pl.pipe = true;
     const int nchunks = (T + chunk - 1) / chunk;
     const long long bh = (long long)B * H;
-    const long long base = bh * (dv / 64);                                   // main workgroups / segment
-    const long long sb = bh * ((dk + dv) / (64 * gdn::pipe_summary_tiles(dk, dv)));  // summary
-    const double fold = dk == 64 ? 0.15 : 0.35;           // measured cost of one folded map
+    const long long base = bh * (dv / 64);                                  // workgroups, unsegmented
+    const int cts = gdn::pipe_seg_tiles(dk, dv);
+    const long long sb = bh * ((dk + dv) / (64 * cts));                     // per segment
+    const double step_us = (dk == 64 ? 2.7 : 4.0) * (chunk == 64 ? 1.0 : 0.6);
+    const double wstep = dk == 64 ? 1.45 : 1.33;         // segment-walk step / unsegmented step
+    const double fix = 9.0 / step_us;                     // correction pass: launch, first loads
+    const double fold = 0.15;                             // one folded map
+    const double corr = 0.3 * chunk / 64;                 // outputs of one chunk rewritten
     auto rounds = [](long long wgs) { return (double)((wgs + 255) / 256); };
-    int best_n = 1;
-    double best = rounds(base) * (nchunks + 1);
+    int best_n = 0;
+    double best = 0;
     for (int n = 2; n <= 64 && 2 * n <= nchunks; ++n) {
         const int L = (nchunks + n - 1) / n;
         const int ns = (nchunks + L - 1) / L;
         if (ns < 2 || ns != n) continue;
-        const double cost = rounds(sb * (ns - 1)) * (L + 1) + rounds(base * ns) * (L + 1) + fold * (ns - 1);
-        if (cost < best - 1e-9) { best = cost; best_n = ns; }
+        const double cost = rounds(sb * ns) * (L + 1) * wstep + fix + fold * (ns - 1) + corr * L;
+        if (best_n == 0 || cost < best) { best = cost; best_n = ns; }
     }
+    // segments only for a clear gain over the unsegmented walk
+    if (best_n == 0 || best > 0.9 * rounds(base) * (nchunks + 1)) best_n = 1;
     pl.nseg = best_n;
     pl.seg_chunks = best_n > 1 ? (nchunks + best_n - 1) / best_n : (nchunks > 0 ? nchunks : 1);
-    pl.ws_bytes = seg_workspace(0, B, H, dk, dv, pl.nseg);
+    pl.ws_bytes = gdn::pipe_workspace(B, H, dk, dv, chunk, pl.nseg, pl.seg_chunks);
     return pl;
 }
 
@@ -190,13 +201,20 @@ int run(const void* q, const void* k, const void* v, const void* alpha, const vo
         if (pl.seg_chunks < 1) pl.seg_chunks = 1;
         a.nseg = pl.nseg;
         a.seg_chunks = pl.seg_chunks;
-        a.summA = nullptr; a.summB = nullptr; a.snap = nullptr;
+        a.summA = nullptr; a.summB = nullptr; a.snap = nullptr; a.phi = nullptr; a.ostage = nullptr;
         if (pl.nseg > 1) {
-            const size_t bh = (size_t)B * H, ns = (size_t)(pl.nseg - 1);
+            const size_t bh = (size_t)B * H;
+            // maps of segments 0 .. nseg-2 (segmented walker) or of all nseg (pipelined)
+            const size_t ns = (size_t)(pl.pipe ? pl.nseg : pl.nseg - 1);
             char* w = reinterpret_cast<char*>(o.workspace);
             a.summA = w;
             a.summB = reinterpret_cast<float*>(w + bh * ns * dk * dk * (a.in_f32 ? 4 : 2));
             a.snap = a.summB + bh * ns * dk * dv;
+            if (pl.pipe) {
+                char* ph = reinterpret_cast<char*>(a.snap + bh * dk * dv);
+                a.phi = ph;
+                a.ostage = ph + bh * pl.nseg * (size_t)pl.seg_chunks * chunk * dk * 2;
+            }
         }
         if (pl.nseg > 1 && (reinterpret_cast<uintptr_t>(o.workspace) & 15u))
             return fail(GDN_ERR_ARG, "workspace must be 16-byte aligned");

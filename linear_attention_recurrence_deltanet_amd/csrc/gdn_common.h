@@ -177,6 +177,20 @@ __device__ __forceinline__ void buf_store4(rsrc_t r, unsigned off, float v) {
 __device__ __forceinline__ void buf_store2(rsrc_t r, unsigned off, uint16_t v) {
     __builtin_amdgcn_raw_buffer_store_b16(v, r, off, 0, 0);
 }
+// soff: a wave-uniform byte offset added in the scalar operand (not part of
+// the range check: only for stores known to be in range)
+__device__ __forceinline__ void buf_store8(rsrc_t r, unsigned off, uint2 v, unsigned soff = 0) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{v.x, v.y}, r, off, (int)soff, 0);
+}
+__device__ __forceinline__ void buf_store16(rsrc_t r, unsigned off, uint4 v) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4{v.x, v.y, v.z, v.w}, r, off, 0, 0);
+}
+// Offset past every range a resource here covers (ranges stay below 2 GiB):
+// a load from it returns zeros and a store to it is dropped, with no memory
+// traffic.  Used to keep loads and stores unconditional.
+constexpr unsigned kOffNone = 0x80000000u;
 
 // ---------------------------------------------------------------------------
 // Cross-lane helpers on DPP (no LDS traffic).

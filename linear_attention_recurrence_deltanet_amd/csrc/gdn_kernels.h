@@ -22,12 +22,19 @@ struct FwdArgs {
     int in_f32;              // 1: inputs fp32, 0: bf16
 };
 
-// Segmented chunk walker (chunk 32 or 64).
+// Segmented chunk walkers (chunk 32 or 64).  With nseg > 1 the workspace
+// holds the segment maps M_out = A_s M_in + B_s:
+//   segmented walker (fp32 inputs): segments 0 .. nseg-2, A_s row-major
+//     (operand precision: fp16, fp32 for fp32 inputs), B_s row-major;
+//   pipelined walker: all nseg segments, A_s fp16 in MFMA fragment order,
+//     B_s fp32 in accumulator order, plus Phi (the outputs' linear part) and
+//     the outputs from a zero incoming state (fp16), both in fragment order.
 struct WalkArgs : FwdArgs {
-    void* summA;             // [B*H][nseg-1][dk][dk] segment transitions A_s, operand
-                             //   precision (fp16; fp32 for fp32 inputs)   (nseg > 1)
-    float* summB;            // [B*H][nseg-1][dk][dv] segment offsets B_s  (nseg > 1)
-    float* snap;             // [B*H][dk][dv] copy of state_in            (nseg > 1)
+    void* summA;             // [B*H][nseg(-1)][dk][dk] segment transitions A_s
+    float* summB;            // [B*H][nseg(-1)][dk][dv] segment offsets B_s
+    float* snap;             // [B*H][dk][dv] copy of state_in
+    void* phi;               // pipelined: [B*H][nseg][seg_chunks*chunk][dk] fp16, fragment order
+    void* ostage;            // pipelined: [B*H][nseg][seg_chunks*chunk][dv] fp16 partial outputs
     int nseg;                // segments per sequence (1: no split)
     int seg_chunks;          // chunks per segment
 };
@@ -38,11 +45,13 @@ hipError_t launch_walk(const WalkArgs& a, int chunk, int waves, hipStream_t s);
 int walk_max_waves(int in_f32, int dk, int chunk);
 
 // Pipelined walker (bf16 inputs, dk 64 or 128, dv a multiple of 64, chunk 32
-// or 64): eight waves per workgroup, value tile of 64 columns in the main
-// pass; the summary pass covers 64 * pipe_summary_tiles(dk, dv) columns of
-// [identity | value] per workgroup.
+// or 64): eight waves per workgroup, value tile of 64 columns without
+// segments; with segments one walk per segment covers 64 * pipe_seg_tiles(dk,
+// dv) columns of [identity | value] per workgroup, and a correction pass
+// completes outputs and state.
 bool pipe_supported(int in_f32, int dk, int dv, int chunk);
-int pipe_summary_tiles(int dk, int dv);
+int pipe_seg_tiles(int dk, int dv);
+size_t pipe_workspace(int B, int H, int dk, int dv, int chunk, int nseg, int seg_chunks);
 hipError_t launch_pipe(const WalkArgs& a, int chunk, hipStream_t s);
 
 // Single-pass kernel (128-token chunks; fp32 inputs with dk = 128): one

@@ -44,7 +44,7 @@ namespace {
 constexpr int pal16(int x) { return (x + 15) & ~15; }
 
 // Compile-time LDS plan (bytes).
-template <int DK, int C, int CT, bool SUMMARY>
+template <int DK, int C, int CT, bool SEG>
 struct PPlan {
     static constexpr int NCW = 4, NPW = 4, NW = NCW + NPW, NT = 64 * NW, NPT = 64 * NPW;
     static constexpr int BV = 16 * NCW * CT;
@@ -58,31 +58,28 @@ struct PPlan {
     static constexpr int LDX = 20;            // rows of 16
     static constexpr int LDAD = 20;           // fp32 rows of 16 (+4)
     static constexpr int ADB = 16 * LDAD + 16;  // fp32 stride of one diagonal block
-    static constexpr int O_QH = 0;                                          // q^   [C][LDD]
-    static constexpr int O_KH = O_QH + (SUMMARY ? 0 : pal16(C * LDD * 2));  // k^   [C][LDD]
-    static constexpr int O_KT = O_KH + pal16(C * LDD * 2);                  // k^T  [DK][LDC]
-    static constexpr int O_PM = O_KT + pal16(DK * LDC * 2);                 // P    [C][LDC]
-    static constexpr int O_T2 = O_PM + (SUMMARY ? 0 : pal16(C * LDC * 2));  // -T diag(gam)
-    static constexpr int O_TM = O_T2 + pal16(C * LDC * 2);                  // T    [C][LDC]
-    static constexpr int O_TT = O_TM + pal16(C * LDC * 2);                  // T^T  [C][LDC]
-    static constexpr int O_AOFF = O_TT + pal16(C * LDC * 2);                // A off-diagonal
-    static constexpr int O_AD = O_AOFF + pal16(C * LDC * 2);                // A diag^T fp32
-    static constexpr int O_XD = O_AD + pal16(NB * ADB * 4);                 // diag inverses
-    static constexpr int O_VR = O_XD + pal16(C * LDX * 2);                  // v rows [C][LDV]
-    static constexpr int O_VEC = O_VR + pal16(C * LDV * 2);                 // 2 x 4 x C fp32
-    // summary epilogue: the tile's identity columns of A_s, staged row-major
-    // [DK][DK + 4] over the (then dead) start of the plan
+    static constexpr int O_QH = 0;                                  // q^   [C][LDD]
+    static constexpr int O_KH = O_QH + pal16(C * LDD * 2);          // k^   [C][LDD]
+    static constexpr int O_KT = O_KH + pal16(C * LDD * 2);          // k^T  [DK][LDC]
+    static constexpr int O_PM = O_KT + pal16(DK * LDC * 2);         // P    [C][LDC]
+    static constexpr int O_T2 = O_PM + pal16(C * LDC * 2);          // -T diag(gam)
+    static constexpr int O_TM = O_T2 + pal16(C * LDC * 2);          // T    [C][LDC]
+    static constexpr int O_TT = O_TM + pal16(C * LDC * 2);          // T^T  [C][LDC]
+    static constexpr int O_AOFF = O_TT + pal16(C * LDC * 2);        // A off-diagonal
+    static constexpr int O_AD = O_AOFF + pal16(C * LDC * 2);        // A diag^T fp32
+    static constexpr int O_XD = O_AD + pal16(NB * ADB * 4);         // diag inverses
+    static constexpr int O_VR = O_XD + pal16(C * LDX * 2);          // v rows [C][LDV]
+    static constexpr int O_VEC = O_VR + pal16(C * LDV * 2);         // 2 x 4 x C fp32
+    // segment walk epilogue: the tile's identity columns of the segment map,
+    // staged row-major [DK][DK + 4] over the (then dead) start of the plan
     static constexpr int LDAS = DK + 4;
-    static constexpr int SZ_AS = SUMMARY ? DK * LDAS * 2 : 0;
-    // main pass of a segmented call: two segment maps staged for the fold
-    static constexpr int SZ_FOLD = SUMMARY ? 0 : 2 * DK * DK * 2;
+    static constexpr int SZ_AS = SEG ? DK * LDAS * 2 : 0;
     static constexpr int SZ_STEP = O_VEC + 2 * 4 * C * 4;
-    static constexpr int TOTAL = SZ_STEP > SZ_AS ? (SZ_STEP > SZ_FOLD ? SZ_STEP : SZ_FOLD)
-                                                 : (SZ_AS > SZ_FOLD ? SZ_AS : SZ_FOLD);
+    static constexpr int TOTAL = SZ_STEP > SZ_AS ? SZ_STEP : SZ_AS;
 };
 
-template <int DK, int C, int CT, bool SUMMARY>
-constexpr bool pipe_fits() { return PPlan<DK, C, CT, SUMMARY>::TOTAL <= 160 * 1024; }
+template <int DK, int C, int CT, bool SEG>
+constexpr bool pipe_fits() { return PPlan<DK, C, CT, SEG>::TOTAL <= 160 * 1024; }
 
 // Four fp16 values, one 8-byte store (p 8-byte aligned at every call site).
 __device__ __forceinline__ void st4h(_Float16* p, float a, float b, float c, float d) {
@@ -174,14 +171,19 @@ __device__ __forceinline__ f32x4 transpose16_bf16(const uint16_t* a, int lda, in
 
 }  // namespace
 
-// SUMMARY = false: main pass (outputs, final state).
-// SUMMARY = true : segment maps (A_s on identity columns, B_s on value
-//                  columns with a zero incoming state), no outputs.
-// FOLD: the main pass of a segmented call (folds the preceding maps); the
-//       unsegmented instantiation carries no fold code at all.
-template <int DK, int C, int CT, bool SUMMARY, bool FOLD>
+// SEG = false: one walk per (head, value tile) over the whole sequence,
+//              from state_in; outputs and the final state.
+// SEG = true : one walk per (head, segment, tile of [identity | value]
+//              columns).  The walk is affine in the segment's incoming state
+//              M_in, so it is run once on identity columns (the linear part)
+//              and once on value columns from a zero state (the offset):
+//                outputs  O = O_val + Phi M_in,   state  M_out = A_s M_in + B_s.
+//              Value columns write O_val, identity columns write Phi (their
+//              outputs, transposed) and both write the map (A_s, B_s); the
+//              correction pass then folds the maps and adds Phi M_in.
+template <int DK, int C, int CT, bool SEG>
 __global__ __launch_bounds__(512) void gdn_pipe_kernel(WalkArgs p) {
-    typedef PPlan<DK, C, CT, SUMMARY> L;
+    typedef PPlan<DK, C, CT, SEG> L;
     typedef OpF16 Op;
     typedef _Float16 E;
     typedef Op::frag F;
@@ -224,25 +226,19 @@ __global__ __launch_bounds__(512) void gdn_pipe_kernel(WalkArgs p) {
     const int ktid = tid - 64 * NCW;                  // thread index among key waves
 
     const int T = p.T, dv = p.dv;
-    const int nseg = p.nseg, nsum = nseg - 1;
+    const int nseg = p.nseg;
     // Workgroups are dealt to the 8 XCDs round-robin.  Remap so that
     // consecutive logical indices -- the column tiles and segments of one
-    // head -- share an XCD and its L2: they read the same q/k rows and the
-    // same segment maps at about the same time.
+    // head -- share an XCD and its L2: they read the same q/k rows at about
+    // the same time.
     int wg = blockIdx.x;
     {
         const int w8 = (int)gridDim.x / 8 * 8;
         if (wg < w8) wg = (wg % 8) * (w8 / 8) + wg / 8;
     }
     int bh, seg, ctile;
-    if constexpr (SUMMARY) {
-        const int ncol = (DK + dv) / BV;
-        ctile = wg % ncol;
-        const int r = wg / ncol;
-        seg = r % nsum;
-        bh = r / nsum;
-    } else {
-        const int ncol = dv / BV;
+    {
+        const int ncol = SEG ? (DK + dv) / BV : dv / BV;
         ctile = wg % ncol;
         const int r = wg / ncol;
         seg = r % nseg;
@@ -253,7 +249,7 @@ __global__ __launch_bounds__(512) void gdn_pipe_kernel(WalkArgs p) {
     ctile = uniform(ctile);
     // tile-local columns [vlo, BV) are value columns; global v column = vbase + local
     int vlo, vbase;
-    if constexpr (SUMMARY) {
+    if constexpr (SEG) {
         const int gc0 = ctile * BV;
         vlo = min(BV, max(0, DK - gc0));
         vbase = gc0 - DK;
@@ -273,30 +269,40 @@ __global__ __launch_bounds__(512) void gdn_pipe_kernel(WalkArgs p) {
     const uint16_t* vgp = reinterpret_cast<const uint16_t*>(p.v) + (size_t)bh * T * dv;
     const uint16_t* ag = reinterpret_cast<const uint16_t*>(p.alpha) + (size_t)bh * T;
     const uint16_t* bg = reinterpret_cast<const uint16_t*>(p.beta) + (size_t)bh * T;
-    E* summA_bh = reinterpret_cast<E*>(p.summA) + (size_t)bh * nsum * DK * DK;
-    float* summB_bh = p.summB + (size_t)bh * nsum * DK * dv;
     const rsrc_t rq_ = make_rsrc(qg, (unsigned)T * DK * 2u);
     const rsrc_t rk_ = make_rsrc(kg, (unsigned)T * DK * 2u);
     const rsrc_t rv_ = make_rsrc(vgp, (unsigned)T * dv * 2u);
     const rsrc_t ra_ = make_rsrc(ag, (unsigned)T * 2u);
     const rsrc_t rb_ = make_rsrc(bg, (unsigned)T * 2u);
+    // outputs of the unsegmented walk; a segment walk stages fp16 partial
+    // outputs that the correction pass completes
     const unsigned osz = p.out_bf16 ? 2u : 4u;
-    const rsrc_t ro_ = make_rsrc(SUMMARY ? nullptr : (const char*)p.out + (size_t)bh * T * dv * osz,
-                                 SUMMARY ? 0u : (unsigned)T * dv * osz);
-
+    const rsrc_t ro_ = make_rsrc(SEG ? nullptr : (const char*)p.out + (size_t)bh * T * dv * osz,
+                                 SEG ? 0u : (unsigned)T * dv * osz);
+    // Phi of this segment: [chunk][row block][k-step of 32 columns of d_k][lane] x 8 fp16,
+    // an MFMA operand fragment in accumulator k order (16-column blocks 2 ks, 2 ks + 1);
+    // partial outputs: [chunk][row block][16 value columns][lane] x 4 fp16
+    const rsrc_t rphi_ = make_rsrc(SEG ? reinterpret_cast<E*>(p.phi) + ((size_t)bh * nseg + seg) * (size_t)p.seg_chunks * C * DK
+                                       : nullptr,
+                                   SEG ? (unsigned)(p.seg_chunks * C * DK * 2) : 0u);
+    const rsrc_t rosg_ = make_rsrc(SEG ? reinterpret_cast<E*>(p.ostage) + ((size_t)bh * nseg + seg) * (size_t)p.seg_chunks * C * dv
+                                       : nullptr,
+                                   SEG ? (unsigned)(p.seg_chunks * C * dv * 2) : 0u);
 
     // ---------------- state-wave registers ---------------------------------
     // Macc[ct][ib] lane (lg, lc): state rows 16 ib + 4 lg + i of column col0(ct) + lc
     f32x4 Macc[CT][NDB];
     F mB[CT][KS_D];                                   // state as B operand (fp16)
-    f32x4 QM[SUMMARY ? 1 : CT][NB];                   // Q^ M of the next chunk
-    f32x4 KM[CT][NB];                                 // K^ M of the next chunk
+    // (Q^ M)^T = M^T Q^^T of the next chunk: lane (lg, lc) holds row 16 rb + lc,
+    // columns col0 + 4 lg + i
+    f32x4 QM[CT][NB];
+    F KMf[CT][KS_C];                                  // K^ M of the next chunk as B operand (fp16)
     F vB[CT][KS_C];                                   // V of the next chunk as B operand
     auto col0 = [&](int ct) { return 16 * (ct * NCW + wave); };
-    auto ident = [&](int ct) { return SUMMARY && col0(ct) < vlo; };
+    auto ident = [&](int ct) { return SEG && col0(ct) < vlo; };
 
     // ---------------- key-wave prefetch registers ---------------------------
-    uint4 pq[SUMMARY ? 1 : QPT], pk[QPT], pv[VPT];
+    uint4 pq[QPT], pk[QPT], pv[VPT];
     uint16_t pa[TPL], pb[TPL];
     auto prefetch = [&](int ch) {
         const int t0 = ch * C;
@@ -306,13 +312,13 @@ __global__ __launch_bounds__(512) void gdn_pipe_kernel(WalkArgs p) {
             const int r = idx / VPRQ, part = idx % VPRQ;
             const unsigned off = (unsigned)((t0 + r) * DK + part * 8) * 2u;
             pk[it] = buf_load16(rk_, off);
-            if constexpr (!SUMMARY) pq[it] = buf_load16(rq_, off);
+            pq[it] = buf_load16(rq_, off);
         }
 #pragma unroll
         for (int it = 0; it < VPT; ++it) {
             const int idx = ktid + NPT * it;
             const int r = idx / VPRV, part = idx % VPRV;
-            // identity columns of a summary tile have no v (left as zero)
+            // identity columns of a segment tile have no v (left as zero)
             pv[it] = (part * 8 >= vlo) ? buf_load16(rv_, (unsigned)((t0 + r) * dv + vbase + part * 8) * 2u)
                                        : make_uint4(0u, 0u, 0u, 0u);
         }
@@ -325,10 +331,10 @@ __global__ __launch_bounds__(512) void gdn_pipe_kernel(WalkArgs p) {
             }
         }
     };
-    if constexpr (SUMMARY) {
-        // Snapshot of the incoming state for the main pass (state_in may alias
-        // state_out): segment 0's workgroups copy their value columns, rows of
-        // 16-byte pieces spread over all 512 threads.
+    if constexpr (SEG) {
+        // Copy of the incoming state for the correction pass (state_in may
+        // alias state_out): segment 0's workgroups copy their value columns,
+        // rows of 16-byte pieces spread over all 512 threads.
         if (seg == 0 && p.snap && p.state_in && vlo < BV) {
             const int pr = (BV - vlo) / 4;                       // 16-byte pieces per row
             const size_t base = (size_t)bh * DK * dv + vbase + vlo;
@@ -339,15 +345,16 @@ __global__ __launch_bounds__(512) void gdn_pipe_kernel(WalkArgs p) {
             }
         }
     }
-    // ---- incoming state of the walk (state waves)
+    // ---- incoming state of the walk (state waves): identity on identity
+    // columns and zero on value columns of a segment walk, else state_in
     auto init_state = [&]() {
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
-            const int gcol = ctile * BV + col0(ct) + lc;      // summary: [ident | value]
+            const int gcol = ctile * BV + col0(ct) + lc;      // segment tile: [ident | value]
             const int vcol = vbase + col0(ct) + lc;
 #pragma unroll
             for (int ib = 0; ib < NDB; ++ib) Macc[ct][ib] = zero4();
-            if constexpr (SUMMARY) {
+            if constexpr (SEG) {
                 if (ident(ct)) {
 #pragma unroll
                     for (int ib = 0; ib < NDB; ++ib)
@@ -356,9 +363,8 @@ __global__ __launch_bounds__(512) void gdn_pipe_kernel(WalkArgs p) {
                             Macc[ct][ib][i] = (16 * ib + 4 * lg + i == gcol) ? 1.f : 0.f;
                 }
             } else {
-                const float* sinp = nseg > 1 ? (p.state_in ? p.snap : nullptr) : p.state_in;
-                if (sinp) {
-                    const float* sp = sinp + (size_t)bh * DK * dv + vcol;
+                if (p.state_in) {
+                    const float* sp = p.state_in + (size_t)bh * DK * dv + vcol;
 #pragma unroll
                     for (int ib = 0; ib < NDB; ++ib)
 #pragma unroll
@@ -368,95 +374,13 @@ __global__ __launch_bounds__(512) void gdn_pipe_kernel(WalkArgs p) {
             }
         }
     };
-    if constexpr (FOLD) {
-        if (is_state) init_state();           // before the fold, which needs every wave
-    }
-    if constexpr (FOLD) {
-        // Fold the preceding segments' maps into the incoming state,
-        // M <- A_s M + B_s.  A_s (d_k x d_k, fp16, MFMA fragment order) is the
-        // same for every state wave, so it is staged once per workgroup: the
-        // key waves copy map s+1 into LDS (and load map s+2 into registers)
-        // while the state waves apply map s; one barrier per map.
-        E* Ast = reinterpret_cast<E*>(smem);                 // [2][DK*DK] fragment order
-        constexpr int APK = DK * DK * 2 / 16 / NPT;          // 16-byte pieces per key thread
-        const rsrc_t rA = make_rsrc(summA_bh, (unsigned)(nsum * DK * DK * 2));
-        const rsrc_t rB = make_rsrc(summB_bh, (unsigned)(nsum * DK * dv * 4));
-        uint4 ka[2][APK];                                    // key waves: maps in flight
-        f32x4 fb[2][CT][NDB];                                // state waves: B_s of own columns
-        auto kload = [&](int buf, int s2) {
-#pragma unroll
-            for (int j = 0; j < APK; ++j)
-                ka[buf][j] = buf_load16(rA, (unsigned)(s2 * DK * DK * 2 + (ktid + NPT * j) * 16));
-        };
-        auto kstore = [&](int buf, int lbuf) {
-            uint4* dst = reinterpret_cast<uint4*>(Ast + lbuf * DK * DK);
-#pragma unroll
-            for (int j = 0; j < APK; ++j) dst[ktid + NPT * j] = ka[buf][j];
-        };
-        auto bload = [&](int buf, int s2) {
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct) {
-                const int c16 = (vbase + col0(ct)) / 16;
-#pragma unroll
-                for (int ib = 0; ib < NDB; ++ib)
-                    fb[buf][ct][ib] = __builtin_bit_cast(f32x4, buf_load16(rB,
-                        (unsigned)(s2 * DK * dv * 4 + ((c16 * NDB + ib) * 64 + lane) * 16)));
-            }
-        };
-        auto apply = [&](int buf, int lbuf) {
-            F mF[CT][KS_D];
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-                for (int ks = 0; ks < KS_D; ++ks) mF[ct][ks] = Op::b_acc(Macc[ct], ks);
-            const uint4* As = reinterpret_cast<const uint4*>(Ast + lbuf * DK * DK);
-#pragma unroll
-            for (int ib = 0; ib < NDB; ++ib) {
-                F fa[KS_D];
-#pragma unroll
-                for (int ks = 0; ks < KS_D; ++ks) fa[ks] = __builtin_bit_cast(F, As[(ib * KS_D + ks) * 64 + lane]);
-#pragma unroll
-                for (int ct = 0; ct < CT; ++ct) {
-                    f32x4 acc = fb[buf][ct][ib];
-#pragma unroll
-                    for (int ks = 0; ks < KS_D; ++ks) acc = Op::mma(fa[ks], mF[ct][ks], acc);
-                    Macc[ct][ib] = acc;
-                }
-            }
-        };
-        // one step of the fold: map s2 applied from LDS copy s2 & 1
-        auto fstep = [&](int s2, int par) {
-            if (is_state) {
-                if (s2 + 1 < seg) bload(par ^ 1, s2 + 1);
-                apply(par, par);
-            } else {
-                if (s2 + 1 < seg) kstore(par ^ 1, par ^ 1);
-                if (s2 + 2 < seg) kload(par, s2 + 2);
-            }
-            __syncthreads();
-        };
-        if (seg > 0) {
-            if (is_state) {
-                bload(0, 0);
-            } else {
-                kload(0, 0);
-                kstore(0, 0);
-                if (seg > 1) kload(1, 1);
-            }
-            __syncthreads();
-            for (int s2 = 0; s2 < seg; s2 += 2) {
-                fstep(s2, 0);
-                if (s2 + 1 < seg) fstep(s2 + 1, 1);
-            }
-        }
-    }
 
     if (!is_state && nch > 0) prefetch(ch0);
 
     // The two roles run separate loops with the same barrier sequence, so the
     // compiler allocates registers per role (the branch is wave-uniform).
     if (is_state) {
-        if constexpr (!FOLD) init_state();
+        init_state();
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
@@ -475,9 +399,7 @@ __global__ __launch_bounds__(512) void gdn_pipe_kernel(WalkArgs p) {
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct) {
                     const bool idt = ident(ct);
-                    F kmB[KS_C];
-#pragma unroll
-                    for (int ks = 0; ks < KS_C; ++ks) kmB[ks] = Op::b_acc(KM[ct], ks);
+                    const F* kmB = KMf[ct];
                     f32x4 U[NB];
 #pragma unroll
                     for (int rb = 0; rb < NB; ++rb) {
@@ -491,29 +413,51 @@ __global__ __launch_bounds__(512) void gdn_pipe_kernel(WalkArgs p) {
                         U[rb] = acc;
                     }
                     __builtin_amdgcn_sched_barrier(0);
-                    if constexpr (!SUMMARY) {
+                    {
                         F uB[KS_C];
 #pragma unroll
                         for (int ks = 0; ks < KS_C; ++ks) uB[ks] = Op::b_acc(U, ks);
-                        const unsigned ocol = (unsigned)(vbase + col0(ct) + lc);
+                        // O^T = M^T Q^^T diag(gam) + U^T P^T, tiles of 16 columns x 16 rows;
+                        // lane (lg, lc) holds row 16 rb + lc, columns col0 + 4 lg + i
+                        const int cb = (ctile * BV + col0(ct)) / 16;      // 16-column block of the tile
+                        const int lch = pc - 1 - ch0;                     // chunk within the segment
 #pragma unroll
                         for (int rb = 0; rb < NB; ++rb) {
-                            const f32x4 gm = *reinterpret_cast<const f32x4*>(v_gam + 16 * rb + 4 * lg);
+                            const float gr = v_gam[16 * rb + lc];
                             f32x4 o;
 #pragma unroll
-                            for (int i = 0; i < 4; ++i) o[i] = QM[ct][rb][i] * gm[i];
+                            for (int i = 0; i < 4; ++i) o[i] = QM[ct][rb][i] * gr;
 #pragma unroll
                             for (int ks = 0; ks <= rb / 2; ++ks)
-                                o = Op::mma(a_lower<L::LDC>(Pm, rb, ks, lane), uB[ks], o);
-                            // rows past T fall outside the buffer and are dropped
-                            const unsigned o0 = (unsigned)(t0 + 16 * rb + 4 * lg) * (unsigned)dv + ocol;
-                            if (p.out_bf16) {
-#pragma unroll
-                                for (int i = 0; i < 4; ++i)
-                                    buf_store2(ro_, (o0 + i * dv) * 2u, __builtin_bit_cast(uint16_t, (__bf16)o[i]));
+                                o = Op::mma(uB[ks], a_lower<L::LDC>(Pm, rb, ks, lane), o);
+                            if constexpr (SEG) {
+                                const uint2 w = make_uint2(Op::pk2(o[0], o[1]), Op::pk2(o[2], o[3]));
+                                // in range by construction: the wave-uniform part of the
+                                // offset goes in the scalar operand
+                                if (idt) {
+                                    // identity columns: Phi, an operand fragment as stored
+                                    buf_store8(rphi_, (unsigned)lane * 16u, w,
+                                               uniform((lch * C * DK + (rb * KS_D + cb / 2) * 512 + (cb & 1) * 4) * 2));
+                                } else {
+                                    // value columns: partial output (zero incoming state)
+                                    const int vb16 = cb - DK / 16;
+                                    buf_store8(rosg_, (unsigned)lane * 8u, w,
+                                               uniform((lch * C * dv + (rb * (dv / 16) + vb16) * 256) * 2));
+                                }
                             } else {
-#pragma unroll
-                                for (int i = 0; i < 4; ++i) buf_store4(ro_, (o0 + i * dv) * 4u, o[i]);
+                                // rows past T fall outside the buffer and are dropped
+                                const unsigned e0 = (unsigned)(t0 + 16 * rb + lc) * (unsigned)dv +
+                                                    (unsigned)(vbase + col0(ct) + 4 * lg);
+                                if (p.out_bf16) {
+                                    const uint2 w = make_uint2(
+                                        (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)o[0]) |
+                                            ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)o[1]) << 16),
+                                        (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)o[2]) |
+                                            ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)o[3]) << 16));
+                                    buf_store8(ro_, e0 * 2u, w);
+                                } else {
+                                    buf_store16(ro_, e0 * 4u, __builtin_bit_cast(uint4, o));
+                                }
                             }
                         }
                         __builtin_amdgcn_sched_barrier(0);
@@ -544,26 +488,30 @@ __global__ __launch_bounds__(512) void gdn_pipe_kernel(WalkArgs p) {
             __syncthreads();
             // ---- phase 2: K^ M, Q^ M of chunk pc
             // K^ M and Q^ M of chunk pc with the state after chunk pc - 1
+            f32x4 KMlo[CT];
 #pragma unroll
             for (int rb = 0; rb < NB; ++rb) {
-                F fk[KS_D], fq[SUMMARY ? 1 : KS_D];
+                F fk[KS_D], fq[KS_D];
 #pragma unroll
                 for (int ks = 0; ks < KS_D; ++ks) {
                     fk[ks] = Op::a_acc(Kh, L::LDD, 16 * rb, 32 * ks, lane);
-                    if constexpr (!SUMMARY) fq[ks] = Op::a_acc(Qh, L::LDD, 16 * rb, 32 * ks, lane);
+                    fq[ks] = Op::a_acc(Qh, L::LDD, 16 * rb, 32 * ks, lane);
                 }
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct) {
                     f32x4 km = zero4();
 #pragma unroll
                     for (int ks = 0; ks < KS_D; ++ks) km = Op::mma(fk[ks], mB[ct][ks], km);
-                    KM[ct][rb] = km;
-                    if constexpr (!SUMMARY) {
-                        f32x4 qm = zero4();
+                    // kept as the B operand of phase 1 (row blocks 2j, 2j+1 -> k-step j)
+                    if (rb % 2 == 0)
+                        KMlo[ct] = km;
+                    else
+                        KMf[ct][rb / 2] = Op::pack8(KMlo[ct][0], KMlo[ct][1], KMlo[ct][2], KMlo[ct][3],
+                                                    km[0], km[1], km[2], km[3]);
+                    f32x4 qm = zero4();
 #pragma unroll
-                        for (int ks = 0; ks < KS_D; ++ks) qm = Op::mma(fq[ks], mB[ct][ks], qm);
-                        QM[ct][rb] = qm;
-                    }
+                    for (int ks = 0; ks < KS_D; ++ks) qm = Op::mma(mB[ct][ks], fq[ks], qm);
+                    QM[ct][rb] = qm;
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -592,7 +540,7 @@ __global__ __launch_bounds__(512) void gdn_pipe_kernel(WalkArgs p) {
             // ---- phase 4: P = tril(Q^ K^T .* G) of chunk pc, needed from the
             // next step on (the key waves solve for T meanwhile; the two key
             // waves with the shortest block columns take the last tiles)
-            if constexpr (!SUMMARY) {
+            {
                 const float* v_g2 = vecs + vb * 4 * C;
 #pragma unroll
                 for (int u = 0; u < (NTS + NCW - 1) / NCW; ++u)
@@ -615,7 +563,7 @@ __global__ __launch_bounds__(512) void gdn_pipe_kernel(WalkArgs p) {
                 const float sk = group_sum<VPRQ>(sumsq8(pk[it]));
                 const float rk = p.qk_l2norm ? __builtin_amdgcn_rsqf(sk + p.eps) : 1.0f;
                 put8(Kh + r * L::LDD + part * 8, pk[it], rk);
-                if constexpr (!SUMMARY) {
+                {
                     const float sq = group_sum<VPRQ>(sumsq8(pq[it]));
                     const float rq = p.qk_l2norm ? p.scale * __builtin_amdgcn_rsqf(sq + p.eps) : p.scale;
                     put8(Qh + r * L::LDD + part * 8, pq[it], rq);
@@ -762,7 +710,7 @@ __global__ __launch_bounds__(512) void gdn_pipe_kernel(WalkArgs p) {
                     }
                 }
             }
-            if constexpr (!SUMMARY && NTG > NTS) {
+            if constexpr (NTG > NTS) {
                 if (kw >= L::NPW - (NTG - NTS)) p_tile<L>(Kh, Qh, Pm, v_g2, NTS + (L::NPW - 1 - kw), lane);
             }
             __syncthreads();
@@ -770,11 +718,13 @@ __global__ __launch_bounds__(512) void gdn_pipe_kernel(WalkArgs p) {
     }
 
     // ---------------- results ----------------------------------------------
-    if constexpr (SUMMARY) {
-        // Segment maps in the order the main pass consumes them: A_s as MFMA
-        // A-operand fragments [ib][ks][lane] x 16 bytes (fp16), B_s in
+    if constexpr (SEG) {
+        // Segment maps in the order the correction pass consumes them: A_s as
+        // MFMA A-operand fragments [ib][ks][lane] x 16 bytes (fp16), B_s in
         // accumulator order [column block of 16][ib][lane] x f32x4.  Each
         // fold operand is then one coalesced 16-byte load per lane.
+        E* summA_bh = reinterpret_cast<E*>(p.summA) + (size_t)bh * nseg * DK * DK;
+        float* summB_bh = p.summB + (size_t)bh * nseg * DK * dv;
         __syncthreads();                                  // both role loops done: LDS free
         E* As = reinterpret_cast<E*>(smem);
         if (is_state) {
@@ -824,6 +774,203 @@ __global__ __launch_bounds__(512) void gdn_pipe_kernel(WalkArgs p) {
     }
 }
 
+// Correction pass of a segmented call.  One workgroup of four waves per
+// (head, segment, 64 value columns); wave w owns columns 16 w .. 16 w + 15 of
+// the tile and keeps them of the state in fp32 accumulators.  The state
+// entering the segment is folded from the copy of state_in through the maps
+// of the preceding segments, M <- A_s M + B_s, then the segment's outputs get
+// Phi M added (fp32; written as bf16 from the staging buffer when out is
+// bf16).  The last segment also applies its own map for state_out.
+template <int DK, int C>
+__global__ __launch_bounds__(256) void gdn_pipe_fix_kernel(WalkArgs p) {
+    typedef OpF16 Op;
+    typedef Op::frag F;
+    constexpr int NDB = DK / 16, KS_D = DK / 32, NB = C / 16;
+    constexpr int APT = DK * DK * 2 / 16 / 256;        // 16-byte pieces of A_s per thread
+    constexpr int D = DK == 64 ? 3 : 2;                // maps in flight
+    __shared__ uint4 Ast[2][DK * DK * 2 / 16];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lc = lane & 15, lg = lane >> 4;
+    const int T = p.T, dv = p.dv, nseg = p.nseg;
+    int wg = blockIdx.x;
+    {
+        // the segments of one head read the same maps: keep them on one XCD
+        const int w8 = (int)gridDim.x / 8 * 8;
+        if (wg < w8) wg = (wg % 8) * (w8 / 8) + wg / 8;
+    }
+    const int ntile = dv / 64;
+    const int vt = uniform(wg % ntile);
+    const int seg = uniform((wg / ntile) % nseg);
+    const int bh = uniform(wg / ntile / nseg);
+    const bool last = seg == nseg - 1 && p.state_out != nullptr;
+    const bool has_in = p.state_in != nullptr;
+
+    const int col = vt * 64 + 16 * wave + lc;           // value column of this lane
+    const int c16 = vt * 4 + wave;                      // its 16-column block
+    const int nchunks = (T + C - 1) / C;
+    const int ch0 = seg * p.seg_chunks;
+    const int ch1 = min(nchunks, ch0 + p.seg_chunks);
+    const rsrc_t rA = make_rsrc(reinterpret_cast<const _Float16*>(p.summA) + (size_t)bh * nseg * DK * DK,
+                                (unsigned)(nseg * DK * DK * 2));
+    const rsrc_t rB = make_rsrc(p.summB + (size_t)bh * nseg * DK * dv, (unsigned)(nseg * DK * dv * 4));
+    const rsrc_t rP = make_rsrc(reinterpret_cast<const _Float16*>(p.phi) +
+                                    ((size_t)bh * nseg + seg) * (size_t)p.seg_chunks * C * DK,
+                                (unsigned)(p.seg_chunks * C * DK * 2));
+    const rsrc_t rO = make_rsrc(reinterpret_cast<const _Float16*>(p.ostage) +
+                                    ((size_t)bh * nseg + seg) * (size_t)p.seg_chunks * C * dv,
+                                (unsigned)(p.seg_chunks * C * dv * 2));
+    const rsrc_t rW = make_rsrc((const char*)p.out + (size_t)bh * T * dv * (p.out_bf16 ? 2 : 4),
+                                (unsigned)T * dv * (p.out_bf16 ? 2u : 4u));
+
+    // ---- state entering segment 0 (rows 16 ib + 4 lg + i, column col)
+    f32x4 Macc[NDB];
+#pragma unroll
+    for (int ib = 0; ib < NDB; ++ib) Macc[ib] = zero4();
+    if (has_in) {
+        const float* sp = p.snap + (size_t)bh * DK * dv + col;
+#pragma unroll
+        for (int ib = 0; ib < NDB; ++ib)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Macc[ib][i] = sp[(16 * ib + 4 * lg + i) * dv];
+    }
+
+    // Loads and stores below are unconditional (kOffNone where there is
+    // nothing to move) so that the compiler counts the loads in flight
+    // exactly and never drains them early.
+    //
+    // ---- correction operands, PB chunks in flight; the first PB are issued
+    // before the fold, which they do not depend on.  The product is formed
+    // transposed, O^T = M^T Phi^T: lane (lg, lc) then holds row lc and four
+    // consecutive columns, one 16-byte access.
+    const int col4 = vt * 64 + 16 * wave + 4 * lg;       // first of this lane's four columns
+    constexpr int PB = DK == 64 ? 3 : 2;
+    uint4 ph[PB][NB][KS_D];
+    uint2 ov[PB][NB];
+    auto cload = [&](uint4 (&h)[NB][KS_D], uint2 (&o)[NB], int c) {
+        const bool ok = c < ch1;
+#pragma unroll
+        for (int r = 0; r < NB; ++r) {
+#pragma unroll
+            for (int ks = 0; ks < KS_D; ++ks)
+                h[r][ks] = buf_load16(rP, ok ? (unsigned)((((c - ch0) * NB + r) * KS_D + ks) * 64 + lane) * 16u
+                                             : kOffNone);
+            o[r] = buf_load8(rO, ok ? (unsigned)((((c - ch0) * NB + r) * (dv / 16) + c16) * 64 + lane) * 8u
+                                    : kOffNone);
+        }
+    };
+#pragma unroll
+    for (int b = 0; b < PB; ++b) cload(ph[b], ov[b], ch0 + b);
+
+    // ---- fold: maps 0 .. seg-1, D in flight; the last segment also applies
+    // its own map (state_out), loaded from the start
+    const int nfold = seg;
+    uint4 ra[D][APT], ral[APT];
+    f32x4 rb[D][NDB], rbl[NDB];
+    auto issue = [&](uint4 (&a)[APT], f32x4 (&b)[NDB], int i, bool ok) {
+#pragma unroll
+        for (int j = 0; j < APT; ++j)
+            a[j] = buf_load16(rA, ok ? (unsigned)(i * DK * DK * 2 + (tid + 256 * j) * 16) : kOffNone);
+#pragma unroll
+        for (int ib = 0; ib < NDB; ++ib)
+            b[ib] = __builtin_bit_cast(f32x4, buf_load16(rB,
+                        ok ? (unsigned)(i * DK * dv * 4 + ((c16 * NDB + ib) * 64 + lane) * 16) : kOffNone));
+    };
+    // M <- A M + B with A from an LDS copy; the fragments of A are read in
+    // batches of at most 16 so that the MFMAs do not wait on each read
+    auto apply = [&](const uint4* sl, const f32x4 (&b)[NDB]) {
+        F mF[KS_D];
+#pragma unroll
+        for (int ks = 0; ks < KS_D; ++ks) mF[ks] = Op::b_acc(Macc, ks);
+        constexpr int G = NDB * KS_D <= 16 ? NDB : 16 / KS_D;
+#pragma unroll
+        for (int ib0 = 0; ib0 < NDB; ib0 += G) {
+            F fa[G][KS_D];
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+#pragma unroll
+                for (int ks = 0; ks < KS_D; ++ks)
+                    fa[g][ks] = __builtin_bit_cast(F, sl[((ib0 + g) * KS_D + ks) * 64 + lane]);
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                f32x4 acc = b[ib0 + g];
+#pragma unroll
+                for (int ks = 0; ks < KS_D; ++ks) acc = Op::mma(fa[g][ks], mF[ks], acc);
+                Macc[ib0 + g] = acc;
+            }
+        }
+    };
+    issue(ral, rbl, seg, last);
+#pragma unroll
+    for (int d = 0; d < D; ++d) issue(ra[d], rb[d], d, d < nfold);
+    for (int i0 = 0; i0 < nfold; i0 += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const int i = i0 + d;
+            uint4* slot = Ast[i & 1];
+#pragma unroll
+            for (int j = 0; j < APT; ++j) slot[tid + 256 * j] = ra[d][j];
+            __syncthreads();
+            if (i < nfold) apply(slot, rb[d]);
+            issue(ra[d], rb[d], i + D, i + D < nfold);
+        }
+    }
+    f32x4 Min[NDB];                                     // state entering this segment
+#pragma unroll
+    for (int ib = 0; ib < NDB; ++ib) Min[ib] = Macc[ib];
+    if (last) {
+        uint4* slot = Ast[nfold & 1];
+#pragma unroll
+        for (int j = 0; j < APT; ++j) slot[tid + 256 * j] = ral[j];
+        __syncthreads();
+        apply(slot, rbl);
+    }
+
+    // ---- outputs of the segment: O += Phi M_in
+    F mI[KS_D];
+#pragma unroll
+    for (int ks = 0; ks < KS_D; ++ks) mI[ks] = Op::b_acc(Min, ks);
+    auto cfix = [&](const uint4 (&h)[NB][KS_D], const uint2 (&o)[NB], int c) {
+        const bool ok = c < ch1;
+#pragma unroll
+        for (int r = 0; r < NB; ++r) {
+            typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+            const h4 ot = __builtin_bit_cast(h4, o[r]);
+            f32x4 acc = {(float)ot[0], (float)ot[1], (float)ot[2], (float)ot[3]};
+#pragma unroll
+            for (int ks = 0; ks < KS_D; ++ks) acc = Op::mma(mI[ks], __builtin_bit_cast(F, h[r][ks]), acc);
+            // rows past T fall outside the buffer and are dropped
+            const unsigned e0 = (unsigned)((c * C + 16 * r + lc) * dv + col4);
+            if (p.out_bf16) {
+                const uint2 w = make_uint2(
+                    (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[0]) |
+                        ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[1]) << 16),
+                    (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[2]) |
+                        ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[3]) << 16));
+                buf_store8(rW, ok ? e0 * 2u : kOffNone, w);
+            } else {
+                buf_store16(rW, ok ? e0 * 4u : kOffNone, __builtin_bit_cast(uint4, acc));
+            }
+        }
+    };
+    for (int c = ch0; c < ch1; c += PB) {
+#pragma unroll
+        for (int b = 0; b < PB; ++b) {
+            cfix(ph[b], ov[b], c + b);
+            cload(ph[b], ov[b], c + b + PB);
+        }
+    }
+    if (last) {
+        float* sp = p.state_out + (size_t)bh * DK * dv + col;
+#pragma unroll
+        for (int ib = 0; ib < NDB; ++ib)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sp[(16 * ib + 4 * lg + i) * dv] = Macc[ib][i];
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Launch table
 // ---------------------------------------------------------------------------
@@ -834,16 +981,14 @@ hipError_t launch_pipe_t(const WalkArgs& a, hipStream_t s) {
     static_assert(pipe_fits<DK, C, 1, false>() && pipe_fits<DK, C, CTS, true>(), "LDS plan exceeds 160 KiB");
     const int bh = a.B * a.H;
     if (a.nseg > 1) {
-        const int grid = bh * (a.nseg - 1) * ((DK + a.dv) / (64 * CTS));
-        hipLaunchKernelGGL((gdn_pipe_kernel<DK, C, CTS, true, false>), dim3(grid), dim3(512), 0, s, a);
+        const int grid = bh * a.nseg * ((DK + a.dv) / (64 * CTS));
+        hipLaunchKernelGGL((gdn_pipe_kernel<DK, C, CTS, true>), dim3(grid), dim3(512), 0, s, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((gdn_pipe_fix_kernel<DK, C>), dim3(bh * a.nseg * (a.dv / 64)), dim3(256), 0, s, a);
+        return hipGetLastError();
     }
-    const int grid = bh * a.nseg * (a.dv / 64);
-    if (a.nseg > 1)
-        hipLaunchKernelGGL((gdn_pipe_kernel<DK, C, 1, false, true>), dim3(grid), dim3(512), 0, s, a);
-    else
-        hipLaunchKernelGGL((gdn_pipe_kernel<DK, C, 1, false, false>), dim3(grid), dim3(512), 0, s, a);
+    hipLaunchKernelGGL((gdn_pipe_kernel<DK, C, 1, false>), dim3(bh * (a.dv / 64)), dim3(512), 0, s, a);
     return hipGetLastError();
 }
 
@@ -868,12 +1013,22 @@ bool pipe_supported(int in_f32, int dk, int dv, int chunk) {
     return !in_f32 && (dk == 64 || dk == 128) && dv % 64 == 0 && (chunk == 32 || chunk == 64);
 }
 
-int pipe_summary_tiles(int dk, int dv) {
+int pipe_seg_tiles(int dk, int dv) {
     return (dk + dv) % 128 == 0 ? 2 : 1;
 }
 
+size_t pipe_workspace(int B, int H, int dk, int dv, int chunk, int nseg, int seg_chunks) {
+    if (nseg <= 1) return 0;
+    const size_t bh = (size_t)B * H, ns = (size_t)nseg, rows = (size_t)seg_chunks * chunk;
+    return bh * ns * dk * dk * 2          // A_s (fp16)
+         + bh * ns * dk * dv * 4          // B_s
+         + bh * dk * dv * 4               // copy of state_in
+         + bh * ns * rows * dk * 2        // Phi (fp16)
+         + bh * ns * rows * dv * 2;       // partial outputs (fp16)
+}
+
 hipError_t launch_pipe(const WalkArgs& a, int chunk, hipStream_t s) {
-    const int cts = pipe_summary_tiles(a.dk, a.dv);
+    const int cts = pipe_seg_tiles(a.dk, a.dv);
     switch (a.dk) {
     case 64: return pipe_c<64>(a, chunk, cts, s);
     case 128: return pipe_c<128>(a, chunk, cts, s);

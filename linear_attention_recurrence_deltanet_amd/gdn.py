@@ -107,7 +107,7 @@ def workspace_bytes(B, H, T, dk, dv, chunk=0, opts: Optional[GdnOpts] = None) ->
                                           ctypes.byref(opts) if opts is not None else None))
 
 
-def _workspace(workspace, B, H, T, dk, dv, chunk, in_dtype, device):
+def _workspace(workspace, B, H, T, dk, dv, chunk, in_dtype, out_dtype, device):
     """None: allocate what the plan needs; False: none (single-segment walk)."""
     if workspace is False:
         return None
@@ -116,6 +116,7 @@ def _workspace(workspace, B, H, T, dk, dv, chunk, in_dtype, device):
     o = GdnOpts()
     load().gdn_default_opts(ctypes.byref(o))
     o.in_dtype = _dtype_code(in_dtype)
+    o.out_dtype = _dtype_code(out_dtype)
     n = int(load().gdn_workspace_bytes(B, H, T, dk, dv, chunk, ctypes.byref(o)))
     return torch.empty(n, dtype=torch.uint8, device=device) if n > 0 else None
 
@@ -161,7 +162,7 @@ def fwd_chunked(q, k, v, alpha, beta, state_in=None, chunk: int = 64, *, out=Non
                                             state_out if want_state else None, out_dtype)
     if not want_state:
         state_out = None
-    workspace = _workspace(workspace, B, H, T, dk, dv, chunk, q.dtype, q.device)
+    workspace = _workspace(workspace, B, H, T, dk, dv, chunk, q.dtype, out.dtype, q.device)
     opts = make_opts(q.dtype, out.dtype, qk_l2norm, scale, eps, stream, workspace)
     _check(load().gdn_fwd_chunked(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
                                   _ptr(state_in), _ptr(out), _ptr(state_out),
@@ -176,7 +177,7 @@ def fwd_step(q, k, v, alpha, beta, state_in=None, *, out=None, state_out=None,
     workspace as for fwd_chunked."""
     B, H, T, dk, dv, out, state_out = _prep(q, k, v, alpha, beta, state_in, out, state_out,
                                             out_dtype)
-    workspace = _workspace(workspace, B, H, T, dk, dv, 0, q.dtype, q.device)
+    workspace = _workspace(workspace, B, H, T, dk, dv, 0, q.dtype, out.dtype, q.device)
     opts = make_opts(q.dtype, out.dtype, qk_l2norm, scale, eps, stream, workspace)
     _check(load().gdn_fwd_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
                                _ptr(state_in), _ptr(out), _ptr(state_out),
