@@ -44,9 +44,9 @@ namespace {
 constexpr int pal16(int x) { return (x + 15) & ~15; }
 
 // Compile-time LDS plan (bytes).
-template <int DK, int C, int CT, bool SEG>
+template <int DK, int C, int CT, bool SEG, int NCW_ = 4>
 struct PPlan {
-    static constexpr int NCW = 4, NPW = 4, NW = NCW + NPW, NT = 64 * NW, NPT = 64 * NPW;
+    static constexpr int NCW = NCW_, NPW = 4, NW = NCW + NPW, NT = 64 * NW, NPT = 64 * NPW;
     static constexpr int BV = 16 * NCW * CT;
     static constexpr int NB = C / 16, NDB = DK / 16;
     // fp16 row strides of 2 (mod 32) 32-bit words: the 8-byte operand reads
@@ -78,8 +78,8 @@ struct PPlan {
     static constexpr int TOTAL = SZ_STEP > SZ_AS ? SZ_STEP : SZ_AS;
 };
 
-template <int DK, int C, int CT, bool SEG>
-constexpr bool pipe_fits() { return PPlan<DK, C, CT, SEG>::TOTAL <= 160 * 1024; }
+template <int DK, int C, int CT, bool SEG, int NCW = 4>
+constexpr bool pipe_fits() { return PPlan<DK, C, CT, SEG, NCW>::TOTAL <= 160 * 1024; }
 
 // Four fp16 values, one 8-byte store (p 8-byte aligned at every call site).
 __device__ __forceinline__ void st4h(_Float16* p, float a, float b, float c, float d) {
@@ -181,18 +181,21 @@ __device__ __forceinline__ f32x4 transpose16_bf16(const uint16_t* a, int lda, in
 //              Value columns write O_val, identity columns write Phi (their
 //              outputs, transposed) and both write the map (A_s, B_s); the
 //              correction pass then folds the maps and adds Phi M_in.
-template <int DK, int C, int CT, bool SEG>
-__global__ __launch_bounds__(512) void gdn_pipe_kernel(WalkArgs p) {
-    typedef PPlan<DK, C, CT, SEG> L;
+// NCW: state waves (4, or 8 with one column tile each: three waves per SIMD
+//      instead of two when one state wave would otherwise carry two tiles).
+template <int DK, int C, int CT, bool SEG, int NCW = 4>
+__global__ __launch_bounds__(64 * (NCW + 4)) void gdn_pipe_kernel(WalkArgs p) {
+    typedef PPlan<DK, C, CT, SEG, NCW> L;
     typedef OpF16 Op;
     typedef _Float16 E;
     typedef Op::frag F;
-    constexpr int NB = L::NB, NDB = L::NDB, BV = L::BV, NCW = L::NCW, NPT = L::NPT, NW = L::NW;
+    constexpr int NB = L::NB, NDB = L::NDB, BV = L::BV, NPT = L::NPT, NW = L::NW;
     constexpr int NTG = NB * (NB + 1) / 2;           // lower-triangle Gram tiles
     // P tiles: NTS on the state waves (a multiple of their count), the rest
     // (at most two) on the last key waves
     constexpr int NTS = NTG >= 2 * L::NCW ? L::NCW * (NTG / L::NCW) : NTG;
     static_assert(NTG - NTS <= 2 && (NTS % L::NCW == 0 || NTS == NTG), "P tile split");
+    static_assert((NDB * NB) % NCW == 0, "K^T blocks per state wave");
     constexpr int NTW = NDB * NB;                    // 16x16 blocks of K^T
     constexpr int VPRQ = DK / 8;                     // 16-byte pieces per q/k row
     constexpr int VPRV = BV / 8;                     // 16-byte pieces per v row of the tile
@@ -978,11 +981,15 @@ namespace {
 
 template <int DK, int C, int CTS>
 hipError_t launch_pipe_t(const WalkArgs& a, hipStream_t s) {
-    static_assert(pipe_fits<DK, C, 1, false>() && pipe_fits<DK, C, CTS, true>(), "LDS plan exceeds 160 KiB");
+    // a segment tile of 128 columns: eight state waves of one tile at d_k = 64
+    // (three waves per SIMD fit its registers), four of two tiles at 128
+    constexpr int SNCW = (CTS == 2 && DK == 64) ? 8 : 4;
+    constexpr int SCT = CTS * 4 / SNCW;
+    static_assert(pipe_fits<DK, C, 1, false>() && pipe_fits<DK, C, SCT, true, SNCW>(), "LDS plan exceeds 160 KiB");
     const int bh = a.B * a.H;
     if (a.nseg > 1) {
         const int grid = bh * a.nseg * ((DK + a.dv) / (64 * CTS));
-        hipLaunchKernelGGL((gdn_pipe_kernel<DK, C, CTS, true>), dim3(grid), dim3(512), 0, s, a);
+        hipLaunchKernelGGL((gdn_pipe_kernel<DK, C, SCT, true, SNCW>), dim3(grid), dim3(64 * (SNCW + 4)), 0, s, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL((gdn_pipe_fix_kernel<DK, C>), dim3(bh * a.nseg * (a.dv / 64)), dim3(256), 0, s, a);
