@@ -981,9 +981,10 @@ namespace {
 
 template <int DK, int C, int CTS>
 hipError_t launch_pipe_t(const WalkArgs& a, hipStream_t s) {
-    // a segment tile of 128 columns: eight state waves of one tile at d_k = 64
-    // (three waves per SIMD fit its registers), four of two tiles at 128
-    constexpr int SNCW = (CTS == 2 && DK == 64) ? 8 : 4;
+    // a segment tile of 128 columns: eight state waves of one tile each
+    // (three waves per SIMD; measured faster than four state waves of two
+    // tiles, which spill at d_k = 128)
+    constexpr int SNCW = CTS == 2 ? 8 : 4;
     constexpr int SCT = CTS * 4 / SNCW;
     static_assert(pipe_fits<DK, C, 1, false>() && pipe_fits<DK, C, SCT, true, SNCW>(), "LDS plan exceeds 160 KiB");
     const int bh = a.B * a.H;
