@@ -44,9 +44,9 @@ namespace {
 constexpr int pal16(int x) { return (x + 15) & ~15; }
 
 // Compile-time LDS plan (bytes).
-template <int DK, int C, int CT, bool SEG, int NCW_ = 4>
+template <int DK, int C, int CT, bool SEG, int NCW_ = 4, int NPW_ = 4>
 struct PPlan {
-    static constexpr int NCW = NCW_, NPW = 4, NW = NCW + NPW, NT = 64 * NW, NPT = 64 * NPW;
+    static constexpr int NCW = NCW_, NPW = NPW_, NW = NCW + NPW, NT = 64 * NW, NPT = 64 * NPW;
     static constexpr int BV = 16 * NCW * CT;
     static constexpr int NB = C / 16, NDB = DK / 16;
     // fp16 row strides of 2 (mod 32) 32-bit words: the 8-byte operand reads
@@ -78,8 +78,8 @@ struct PPlan {
     static constexpr int TOTAL = SZ_STEP > SZ_AS ? SZ_STEP : SZ_AS;
 };
 
-template <int DK, int C, int CT, bool SEG, int NCW = 4>
-constexpr bool pipe_fits() { return PPlan<DK, C, CT, SEG, NCW>::TOTAL <= 160 * 1024; }
+template <int DK, int C, int CT, bool SEG, int NCW = 4, int NPW = 4>
+constexpr bool pipe_fits() { return PPlan<DK, C, CT, SEG, NCW, NPW>::TOTAL <= 160 * 1024; }
 
 // Four fp16 values, one 8-byte store (p 8-byte aligned at every call site).
 __device__ __forceinline__ void st4h(_Float16* p, float a, float b, float c, float d) {
@@ -183,9 +183,10 @@ __device__ __forceinline__ f32x4 transpose16_bf16(const uint16_t* a, int lda, in
 //              correction pass then folds the maps and adds Phi M_in.
 // NCW: state waves (4, or 8 with one column tile each: three waves per SIMD
 //      instead of two when one state wave would otherwise carry two tiles).
-template <int DK, int C, int CT, bool SEG, int NCW = 4>
-__global__ __launch_bounds__(64 * (NCW + 4)) void gdn_pipe_kernel(WalkArgs p) {
-    typedef PPlan<DK, C, CT, SEG, NCW> L;
+// NPW: key waves (4 or 8).
+template <int DK, int C, int CT, bool SEG, int NCW = 4, int NPW = 4>
+__global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) {
+    typedef PPlan<DK, C, CT, SEG, NCW, NPW> L;
     typedef OpF16 Op;
     typedef _Float16 E;
     typedef Op::frag F;
@@ -986,7 +987,8 @@ hipError_t launch_pipe_t(const WalkArgs& a, hipStream_t s) {
     // tiles, which spill at d_k = 128)
     constexpr int SNCW = CTS == 2 ? 8 : 4;
     constexpr int SCT = CTS * 4 / SNCW;
-    static_assert(pipe_fits<DK, C, 1, false>() && pipe_fits<DK, C, SCT, true, SNCW>(), "LDS plan exceeds 160 KiB");
+    constexpr int UNPW = C == 64 ? 8 : 4;                // key waves of the unsegmented walk
+    static_assert(pipe_fits<DK, C, 1, false, 4, UNPW>() && pipe_fits<DK, C, SCT, true, SNCW>(), "LDS plan exceeds 160 KiB");
     const int bh = a.B * a.H;
     if (a.nseg > 1) {
         const int grid = bh * a.nseg * ((DK + a.dv) / (64 * CTS));
@@ -996,7 +998,7 @@ hipError_t launch_pipe_t(const WalkArgs& a, hipStream_t s) {
         hipLaunchKernelGGL((gdn_pipe_fix_kernel<DK, C>), dim3(bh * a.nseg * (a.dv / 64)), dim3(256), 0, s, a);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL((gdn_pipe_kernel<DK, C, 1, false>), dim3(bh * (a.dv / 64)), dim3(512), 0, s, a);
+    hipLaunchKernelGGL((gdn_pipe_kernel<DK, C, 1, false, 4, UNPW>), dim3(bh * (a.dv / 64)), dim3(64 * (4 + UNPW)), 0, s, a);
     return hipGetLastError();
 }
 
