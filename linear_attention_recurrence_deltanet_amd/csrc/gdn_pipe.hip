@@ -793,6 +793,7 @@ __global__ __launch_bounds__(256) void gdn_pipe_fix_kernel(WalkArgs p) {
     constexpr int APT = DK * DK * 2 / 16 / 256;        // 16-byte pieces of A_s per thread
     constexpr int D = DK == 64 ? 3 : 2;                // maps in flight
     __shared__ uint4 Ast[2][DK * DK * 2 / 16];
+    __shared__ uint4 Phs[DK == 64 ? 3 : 2][C * DK * 2 / 16];    // Phi of the chunks in flight
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -846,24 +847,25 @@ __global__ __launch_bounds__(256) void gdn_pipe_fix_kernel(WalkArgs p) {
     // exactly and never drains them early.
     //
     // ---- correction operands, PB chunks in flight; the first PB are issued
-    // before the fold, which they do not depend on.  The product is formed
-    // transposed, O^T = M^T Phi^T: lane (lg, lc) then holds row lc and four
-    // consecutive columns, one 16-byte access.
+    // before the fold, which they do not depend on.  Phi (the same for every
+    // wave) is loaded once per workgroup, 16 bytes per thread and piece, and
+    // shared through LDS.  The product is formed transposed,
+    // O^T = M^T Phi^T: lane (lg, lc) then holds row lc and four consecutive
+    // columns, one 16-byte access.
     const int col4 = vt * 64 + 16 * wave + 4 * lg;       // first of this lane's four columns
     constexpr int PB = DK == 64 ? 3 : 2;
-    uint4 ph[PB][NB][KS_D];
+    constexpr int PPT = C * DK * 2 / 16 / 256;           // 16-byte pieces of a chunk's Phi per thread
+    uint4 ph[PB][PPT];
     uint2 ov[PB][NB];
-    auto cload = [&](uint4 (&h)[NB][KS_D], uint2 (&o)[NB], int c) {
+    auto cload = [&](uint4 (&h)[PPT], uint2 (&o)[NB], int c) {
         const bool ok = c < ch1;
 #pragma unroll
-        for (int r = 0; r < NB; ++r) {
+        for (int j = 0; j < PPT; ++j)
+            h[j] = buf_load16(rP, ok ? (unsigned)((c - ch0) * C * DK * 2 + (tid + 256 * j) * 16) : kOffNone);
 #pragma unroll
-            for (int ks = 0; ks < KS_D; ++ks)
-                h[r][ks] = buf_load16(rP, ok ? (unsigned)((((c - ch0) * NB + r) * KS_D + ks) * 64 + lane) * 16u
-                                             : kOffNone);
+        for (int r = 0; r < NB; ++r)
             o[r] = buf_load8(rO, ok ? (unsigned)((((c - ch0) * NB + r) * (dv / 16) + c16) * 64 + lane) * 8u
                                     : kOffNone);
-        }
     };
 #pragma unroll
     for (int b = 0; b < PB; ++b) cload(ph[b], ov[b], ch0 + b);
@@ -936,15 +938,20 @@ __global__ __launch_bounds__(256) void gdn_pipe_fix_kernel(WalkArgs p) {
     F mI[KS_D];
 #pragma unroll
     for (int ks = 0; ks < KS_D; ++ks) mI[ks] = Op::b_acc(Min, ks);
-    auto cfix = [&](const uint4 (&h)[NB][KS_D], const uint2 (&o)[NB], int c) {
+    auto cfix = [&](const uint4 (&h)[PPT], const uint2 (&o)[NB], int c, int slot) {
         const bool ok = c < ch1;
+        uint4* sl = Phs[slot];
+#pragma unroll
+        for (int j = 0; j < PPT; ++j) sl[tid + 256 * j] = h[j];
+        __syncthreads();                 // slot reused PB chunks later, after another barrier
 #pragma unroll
         for (int r = 0; r < NB; ++r) {
             typedef _Float16 h4 __attribute__((ext_vector_type(4)));
             const h4 ot = __builtin_bit_cast(h4, o[r]);
             f32x4 acc = {(float)ot[0], (float)ot[1], (float)ot[2], (float)ot[3]};
 #pragma unroll
-            for (int ks = 0; ks < KS_D; ++ks) acc = Op::mma(mI[ks], __builtin_bit_cast(F, h[r][ks]), acc);
+            for (int ks = 0; ks < KS_D; ++ks)
+                acc = Op::mma(mI[ks], __builtin_bit_cast(F, sl[(r * KS_D + ks) * 64 + lane]), acc);
             // rows past T fall outside the buffer and are dropped
             const unsigned e0 = (unsigned)((c * C + 16 * r + lc) * dv + col4);
             if (p.out_bf16) {
@@ -962,7 +969,7 @@ __global__ __launch_bounds__(256) void gdn_pipe_fix_kernel(WalkArgs p) {
     for (int c = ch0; c < ch1; c += PB) {
 #pragma unroll
         for (int b = 0; b < PB; ++b) {
-            cfix(ph[b], ov[b], c + b);
+            cfix(ph[b], ov[b], c + b, b);
             cload(ph[b], ov[b], c + b + PB);
         }
     }
