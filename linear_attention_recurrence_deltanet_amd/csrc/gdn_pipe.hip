@@ -148,6 +148,49 @@ __device__ __forceinline__ void p_tile(const _Float16* Kh, const _Float16* Qh, _
     st4h(Pm + r * L::LDC + s0, pv4[0], pv4[1], pv4[2], pv4[3]);
 }
 
+// Tile t of A = diag(beta) strict_tril(K^ K^T .* G) (t -> (I, J <= I)): the
+// diagonal blocks fp32 and transposed into Adt, the others fp16 into Aoff.
+template <class L>
+__device__ __forceinline__ void g_tile(const _Float16* Kh, float* Adt, _Float16* Aoff,
+                                       const float* v_beta, const float* v_g2, int t, int lane) {
+    constexpr int KS_D = L::NDB * 16 / 32;
+    typedef OpF16::frag F;
+    const int lc = lane & 15, lg = lane >> 4;
+    int I = 0;
+    while ((I + 1) * (I + 2) / 2 <= t) ++I;
+    const int J = t - I * (I + 1) / 2;
+    F fa[KS_D], fk[KS_D];
+#pragma unroll
+    for (int ks = 0; ks < KS_D; ++ks) {
+        // both operands in the same (accumulator) k order
+        fa[ks] = OpF16::a_acc(Kh, L::LDD, 16 * J, ks * 32, lane);
+        fk[ks] = OpF16::a_acc(Kh, L::LDD, 16 * I, ks * 32, lane);
+    }
+    f32x4 kk = zero4();
+#pragma unroll
+    for (int ks = 0; ks < KS_D; ++ks) kk = OpF16::mma(fa[ks], fk[ks], kk);
+    // element i: row s = 16J + 4 lg + i, column r = 16I + lc
+    const int r = 16 * I + lc;
+    const int s0 = 16 * J + 4 * lg;
+    const float br = v_beta[r], gr = v_g2[r];
+    const f32x4 gs = *reinterpret_cast<const f32x4*>(v_g2 + s0);
+    float av[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int s_ = s0 + i;
+        // G_rs = 2^(g_r - g_s) <= 1 for s <= r (clamped: rounding can make it > 0)
+        const float e = __builtin_amdgcn_exp2f(fminf(gr - gs[i], 0.f));
+        av[i] = (s_ < r) ? br * kk[i] * e : 0.f;
+    }
+    if (I == J) {
+        // diagonal block, stored transposed: Adt[I][s][r] = A[r][s]
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Adt[I * L::ADB + (4 * lg + i) * L::LDAD + lc] = av[i];
+    } else {
+        st4h(Aoff + r * L::LDC + s0, av[0], av[1], av[2], av[3]);
+    }
+}
+
 // Sum of squares of 8 bf16 (bf16 products are exact in fp32).
 __device__ __forceinline__ float sumsq8(const uint4& raw) {
     typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
@@ -197,6 +240,10 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
     constexpr int NTS = NTG >= 2 * L::NCW ? L::NCW * (NTG / L::NCW) : NTG;
     static_assert(NTG - NTS <= 2 && (NTS % L::NCW == 0 || NTS == NTG), "P tile split");
     static_assert((NDB * NB) % NCW == 0, "K^T blocks per state wave");
+    // Gram tiles on state waves: with eight state waves at d_k = 64 their
+    // K^ M, Q^ M leave room in phase 2, and the key waves then take two
+    // tiles each instead of three
+    constexpr int NGS = (NCW == 8 && DK == 64) ? NTG % L::NPW : 0;
     constexpr int NTW = NDB * NB;                    // 16x16 blocks of K^T
     constexpr int VPRQ = DK / 8;                     // 16-byte pieces per q/k row
     constexpr int VPRV = BV / 8;                     // 16-byte pieces per v row of the tile
@@ -519,6 +566,12 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
+            if constexpr (NGS > 0) {
+                if (wave < NGS) {
+                    const float* vcur = vecs + vb * 4 * C;
+                    g_tile<L>(Kh, Adt, Aoff, vcur + 3 * C, vcur, wave, lane);
+                }
+            }
             __syncthreads();
             // ---- phase 3: V tiles of chunk pc as B operands
 #pragma unroll
@@ -617,42 +670,9 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
             const float* v_gam = vcur + C;
             const float* v_beta = vcur + 3 * C;
             // ---- phase 2: Gram tiles of chunk pc
-            // Gram tiles (I, J <= I) of K^ K^T -> A (solve scratch)
-            for (int t = kw; t < NTG; t += L::NPW) {
-                int I = 0;
-                while ((I + 1) * (I + 2) / 2 <= t) ++I;
-                const int J = t - I * (I + 1) / 2;
-                F fa[KS_D], fk[KS_D];
-#pragma unroll
-                for (int ks = 0; ks < KS_D; ++ks) {
-                    // both operands in the same (accumulator) k order
-                    fa[ks] = Op::a_acc(Kh, L::LDD, 16 * J, ks * 32, lane);
-                    fk[ks] = Op::a_acc(Kh, L::LDD, 16 * I, ks * 32, lane);
-                }
-                f32x4 kk = zero4();
-#pragma unroll
-                for (int ks = 0; ks < KS_D; ++ks) kk = Op::mma(fa[ks], fk[ks], kk);
-                // element i: row s = 16J + 4 lg + i, column r = 16I + lc
-                const int r = 16 * I + lc;
-                const int s0 = 16 * J + 4 * lg;
-                const float br = v_beta[r], gr = v_g2[r];
-                const f32x4 gs = *reinterpret_cast<const f32x4*>(v_g2 + s0);
-                float av[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int s_ = s0 + i;
-                    // G_rs = 2^(g_r - g_s) <= 1 for s <= r (clamped: rounding can make it > 0)
-                    const float e = __builtin_amdgcn_exp2f(fminf(gr - gs[i], 0.f));
-                    av[i] = (s_ < r) ? br * kk[i] * e : 0.f;
-                }
-                if (I == J) {
-                    // diagonal block, stored transposed: Adt[I][s][r] = A[r][s]
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) Adt[I * L::ADB + (4 * lg + i) * L::LDAD + lc] = av[i];
-                } else {
-                    st4h(Aoff + r * L::LDC + s0, av[0], av[1], av[2], av[3]);
-                }
-            }
+            // Gram tiles (I, J <= I) of K^ K^T -> A (solve scratch); the first
+            // NGS tiles are on state waves
+            for (int t = NGS + kw; t < NTG; t += L::NPW) g_tile<L>(Kh, Adt, Aoff, v_beta, v_g2, t, lane);
             __syncthreads();
             // ---- phase 3: diagonal blocks, one per key wave.  X = (I + A_bb)^-1 by
             // elimination down the columns: lane 4 j + q holds rows 4q..4q+3 of
