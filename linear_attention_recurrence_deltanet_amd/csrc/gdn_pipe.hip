@@ -34,6 +34,8 @@
 //                                                           block columns of T
 // Operand precision as in the segmented walker: fp16 operands (11-bit
 // significand), fp32 accumulation; the state and the solve stay in fp32.
+#include <type_traits>
+
 #include "gdn_common.h"
 #include "gdn_kernels.h"
 
@@ -244,6 +246,10 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
     // K^ M, Q^ M leave room in phase 2, and the key waves then take two
     // tiles each instead of three
     constexpr int NGS = (NCW == 8 && DK == 64) ? NTG % L::NPW : 0;
+    // Block columns of the solve with their operands read ahead into
+    // registers (measured faster), except where the registers are at the cap
+    // of three waves per SIMD at d_k = 128 (the extra registers spill there).
+    constexpr bool COL_AHEAD = !(NCW == 8 && DK == 128);
     constexpr int NTW = NDB * NB;                    // 16x16 blocks of K^T
     constexpr int VPRQ = DK / 8;                     // 16-byte pieces per q/k row
     constexpr int VPRV = BV / 8;                     // 16-byte pieces per v row of the tile
@@ -709,28 +715,84 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
             // ---- phase 4: off-diagonal blocks, block column j on key wave j:
             // T_ij = -X_ii sum_{k=j}^{i-1} A_ik T_kj, the T_kj of the column kept
             // in registers, so the column needs no barrier
-            if (kw < NB - 1) {
-                const int j = kw;
-                const int c = 16 * j + lc;
-                const float gc = v_gam[c];
-                f32x4 Tc[NB];
-#pragma unroll
-                for (int i = 1; i < NB; ++i) {
-                    if (i > j) {
-                        f32x4 y = mm_k16<Op>(Aoff + (16 * i) * L::LDC + 16 * j, L::LDC,
-                                             Tt + (16 * j) * L::LDC + 16 * j, L::LDC, zero4(), lane);
-#pragma unroll
-                        for (int k = 1; k < i; ++k)
-                            if (k > j) y = mm_k16_acc<Op>(Aoff + (16 * i) * L::LDC + 16 * k, L::LDC, Tc[k], y, lane);
-                        const f32x4 t = mm_k16_acc<Op>(Xd + (16 * i) * L::LDX, L::LDX, y, zero4(), lane);
-#pragma unroll
+            if constexpr (COL_AHEAD) {
+                // The column's operands (A_ik, X_ii, T_jj) are read before its
+                // first store, so the stores do not hold back the reads.
+                auto column = [&](auto jc) {
+                    constexpr int j = decltype(jc)::value;
+                    const int c = 16 * j + lc;
+                    const float gc = v_gam[c];
+                    auto frag16 = [&](const E* base, int ld) {
+                        return Op::load16(base + lc * ld + lg * Op::KPER16);
+                    };
+                    Op::frag16 fA[NB][NB], fX[NB];
+                    const Op::frag16 fT = frag16(Tt + (16 * j) * L::LDC + 16 * j, L::LDC);
+    #pragma unroll
+                    for (int i = j + 1; i < NB; ++i) {
+    #pragma unroll
+                        for (int k = j; k < i; ++k) fA[i][k] = frag16(Aoff + (16 * i) * L::LDC + 16 * k, L::LDC);
+                        fX[i] = frag16(Xd + (16 * i) * L::LDX, L::LDX);
+                    }
+                    auto asB = [](const f32x4& v) {
+                        u16x4 fb;
+    #pragma unroll
+                        for (int e = 0; e < 4; ++e) fb[e] = __builtin_bit_cast(uint16_t, (E)v[e]);
+                        return fb;
+                    };
+                    Op::frag16 fTc[NB];
+    #pragma unroll
+                    for (int i = j + 1; i < NB; ++i) {
+                        f32x4 y = Op::mma16(fA[i][j], fT, zero4());
+    #pragma unroll
+                        for (int k = j + 1; k < i; ++k) y = Op::mma16(fA[i][k], fTc[k], y);
+                        const f32x4 t = Op::mma16(fX[i], asB(y), zero4());
+                        f32x4 tn;
+    #pragma unroll
+                        for (int ii = 0; ii < 4; ++ii) tn[ii] = -t[ii];
+                        fTc[i] = asB(tn);
+    #pragma unroll
                         for (int ii = 0; ii < 4; ++ii) {
-                            Tc[i][ii] = -t[ii];
                             const int r = 16 * i + 4 * lg + ii;
-                            Tm[r * L::LDC + c] = (E)(-t[ii]);
+                            Tm[r * L::LDC + c] = (E)tn[ii];
                             T2n[r * L::LDC + c] = (E)(t[ii] * gc);
                         }
-                        st4h(Tt + c * L::LDC + 16 * i + 4 * lg, -t[0], -t[1], -t[2], -t[3]);
+                        st4h(Tt + c * L::LDC + 16 * i + 4 * lg, tn[0], tn[1], tn[2], tn[3]);
+                    }
+                };
+                if constexpr (NB > 1) {
+                    if (kw == 0) column(std::integral_constant<int, 0>{});
+                }
+                if constexpr (NB > 2) {
+                    if (kw == 1) column(std::integral_constant<int, 1>{});
+                }
+                if constexpr (NB > 3) {
+                    if (kw == 2) column(std::integral_constant<int, 2>{});
+                }
+                static_assert(NB <= 4, "block columns");
+            } else {
+                if (kw < NB - 1) {
+                    const int j = kw;
+                    const int c = 16 * j + lc;
+                    const float gc = v_gam[c];
+                    f32x4 Tc[NB];
+    #pragma unroll
+                    for (int i = 1; i < NB; ++i) {
+                        if (i > j) {
+                            f32x4 y = mm_k16<Op>(Aoff + (16 * i) * L::LDC + 16 * j, L::LDC,
+                                                 Tt + (16 * j) * L::LDC + 16 * j, L::LDC, zero4(), lane);
+    #pragma unroll
+                            for (int k = 1; k < i; ++k)
+                                if (k > j) y = mm_k16_acc<Op>(Aoff + (16 * i) * L::LDC + 16 * k, L::LDC, Tc[k], y, lane);
+                            const f32x4 t = mm_k16_acc<Op>(Xd + (16 * i) * L::LDX, L::LDX, y, zero4(), lane);
+    #pragma unroll
+                            for (int ii = 0; ii < 4; ++ii) {
+                                Tc[i][ii] = -t[ii];
+                                const int r = 16 * i + 4 * lg + ii;
+                                Tm[r * L::LDC + c] = (E)(-t[ii]);
+                                T2n[r * L::LDC + c] = (E)(t[ii] * gc);
+                            }
+                            st4h(Tt + c * L::LDC + 16 * i + 4 * lg, -t[0], -t[1], -t[2], -t[3]);
+                        }
                     }
                 }
             }
