@@ -860,26 +860,37 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
     }
 }
 
-// Correction pass of a segmented call.  One workgroup of four waves per
-// (head, segment, 64 value columns); wave w owns columns 16 w .. 16 w + 15 of
-// the tile and keeps them of the state in fp32 accumulators.  The state
-// entering the segment is folded from the copy of state_in through the maps
-// of the preceding segments, M <- A_s M + B_s, then the segment's outputs get
-// Phi M added (fp32; written as bf16 from the staging buffer when out is
-// bf16).  The last segment also applies its own map for state_out.
+// Correction pass of a segmented call.  One workgroup of 16 waves per
+// (head, segment, 64 value columns).  Wave (cg, rg) = (wave % 4, wave / 4)
+// owns value columns 16 cg .. 16 cg + 15 of the tile and, of the state, the
+// RB 16-row blocks of row group rg, in fp32 accumulators.  The state entering
+// the segment is folded from the copy of state_in through the maps of the
+// preceding segments, M <- A_s M + B_s: per map every wave forms its rows
+// from A_s (staged once in LDS) and the whole of M, which the waves exchange
+// as fp16 operand fragments through LDS -- one barrier and a few MFMAs per
+// map.  The segment's outputs then get Phi M added, row block rg of each
+// chunk on row group rg (fp32 out, or bf16); the last segment also applies
+// its own map for state_out.
 template <int DK, int C>
-__global__ __launch_bounds__(256) void gdn_pipe_fix_kernel(WalkArgs p) {
+__global__ __launch_bounds__(1024) void gdn_pipe_fix_kernel(WalkArgs p) {
     typedef OpF16 Op;
     typedef Op::frag F;
     constexpr int NDB = DK / 16, KS_D = DK / 32, NB = C / 16;
-    constexpr int APT = DK * DK * 2 / 16 / 256;        // 16-byte pieces of A_s per thread
-    constexpr int D = DK == 64 ? 3 : 2;                // maps in flight
-    __shared__ uint4 Ast[2][DK * DK * 2 / 16];
-    __shared__ uint4 Phs[DK == 64 ? 3 : 2][C * DK * 2 / 16];    // Phi of the chunks in flight
+    constexpr int RG = 4, RB = NDB / RG;                // row groups; state row blocks per wave
+    constexpr int CPG = RG / NB;                        // chunks per correction group
+    constexpr int APC = DK * DK * 2 / 16;               // 16-byte pieces of one A_s
+    constexpr int APT = (APC + 1023) / 1024;            // ... per thread
+    constexpr int PPG = RG * 16 * DK * 2 / 16;          // 16-byte pieces of Phi per correction group
+    constexpr int D = DK == 64 ? 4 : 3;                 // maps in flight
+    static_assert(NDB % RG == 0 && RG % NB == 0 && PPG <= 1024 && APC % 512 == 0, "fix layout");
+    __shared__ uint4 Ast[2][APC];
+    __shared__ uint4 Mf[2][KS_D][4][64];                // M as fp16 B fragments [k-step][column group][lane]
+    __shared__ uint4 Phs[2][PPG];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int cg = wave & 3, rg = wave >> 2;
     const int lc = lane & 15, lg = lane >> 4;
     const int T = p.T, dv = p.dv, nseg = p.nseg;
     int wg = blockIdx.x;
@@ -895,8 +906,8 @@ __global__ __launch_bounds__(256) void gdn_pipe_fix_kernel(WalkArgs p) {
     const bool last = seg == nseg - 1 && p.state_out != nullptr;
     const bool has_in = p.state_in != nullptr;
 
-    const int col = vt * 64 + 16 * wave + lc;           // value column of this lane
-    const int c16 = vt * 4 + wave;                      // its 16-column block
+    const int col = vt * 64 + 16 * cg + lc;             // value column of this lane
+    const int c16 = vt * 4 + cg;                        // its 16-column block
     const int nchunks = (T + C - 1) / C;
     const int ch0 = seg * p.seg_chunks;
     const int ch1 = min(nchunks, ch0 + p.seg_chunks);
@@ -912,82 +923,85 @@ __global__ __launch_bounds__(256) void gdn_pipe_fix_kernel(WalkArgs p) {
     const rsrc_t rW = make_rsrc((const char*)p.out + (size_t)bh * T * dv * (p.out_bf16 ? 2 : 4),
                                 (unsigned)T * dv * (p.out_bf16 ? 2u : 4u));
 
-    // ---- state entering segment 0 (rows 16 ib + 4 lg + i, column col)
-    f32x4 Macc[NDB];
-#pragma unroll
-    for (int ib = 0; ib < NDB; ++ib) Macc[ib] = zero4();
-    if (has_in) {
-        const float* sp = p.snap + (size_t)bh * DK * dv + col;
-#pragma unroll
-        for (int ib = 0; ib < NDB; ++ib)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) Macc[ib][i] = sp[(16 * ib + 4 * lg + i) * dv];
-    }
-
     // Loads and stores below are unconditional (kOffNone where there is
     // nothing to move) so that the compiler counts the loads in flight
     // exactly and never drains them early.
-    //
-    // ---- correction operands, PB chunks in flight; the first PB are issued
-    // before the fold, which they do not depend on.  Phi (the same for every
-    // wave) is loaded once per workgroup, 16 bytes per thread and piece, and
-    // shared through LDS.  The product is formed transposed,
-    // O^T = M^T Phi^T: lane (lg, lc) then holds row lc and four consecutive
-    // columns, one 16-byte access.
-    const int col4 = vt * 64 + 16 * wave + 4 * lg;       // first of this lane's four columns
-    constexpr int PB = DK == 64 ? 3 : 2;
-    constexpr int PPT = C * DK * 2 / 16 / 256;           // 16-byte pieces of a chunk's Phi per thread
-    uint4 ph[PB][PPT];
-    uint2 ov[PB][NB];
-    auto cload = [&](uint4 (&h)[PPT], uint2 (&o)[NB], int c) {
-        const bool ok = c < ch1;
-#pragma unroll
-        for (int j = 0; j < PPT; ++j)
-            h[j] = buf_load16(rP, ok ? (unsigned)((c - ch0) * C * DK * 2 + (tid + 256 * j) * 16) : kOffNone);
-#pragma unroll
-        for (int r = 0; r < NB; ++r)
-            o[r] = buf_load8(rO, ok ? (unsigned)((((c - ch0) * NB + r) * (dv / 16) + c16) * 64 + lane) * 8u
-                                    : kOffNone);
-    };
-#pragma unroll
-    for (int b = 0; b < PB; ++b) cload(ph[b], ov[b], ch0 + b);
 
-    // ---- fold: maps 0 .. seg-1, D in flight; the last segment also applies
-    // its own map (state_out), loaded from the start
+    // ---- state entering segment 0: rows 16 (rg RB + r) + 4 lg + i, column col
+    f32x4 Macc[RB];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) Macc[r] = zero4();
+    if (has_in) {
+        const float* sp = p.snap + (size_t)bh * DK * dv + col;
+#pragma unroll
+        for (int r = 0; r < RB; ++r)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Macc[r][i] = sp[(16 * (rg * RB + r) + 4 * lg + i) * dv];
+    }
+
+    // ---- correction operands of a group of CPG chunks (RG row blocks): one
+    // 16-byte piece of Phi per thread, staged in LDS; the wave's own row block
+    // of the partial outputs (fp16, 4 columns per lane)
+    auto cload = [&](uint4& h, uint2& o, int g) {
+        const int c0 = ch0 + g * CPG;
+        const int c = c0 + rg / NB, rb = rg % NB;
+        h = buf_load16(rP, (c0 < ch1 && tid < PPG) ? (unsigned)((c0 - ch0) * C * DK * 2 + tid * 16) : kOffNone);
+        o = buf_load8(rO, c < ch1 ? (unsigned)((((c - ch0) * NB + rb) * (dv / 16) + c16) * 64 + lane) * 8u
+                                  : kOffNone);
+    };
+    uint4 ph[2];
+    uint2 ov[2];
+    cload(ph[0], ov[0], 0);
+    cload(ph[1], ov[1], 1);
+
+    // ---- fold: maps 0 .. seg-1, D in flight; the last segment's own map
+    // (state_out) is loaded from the start
     const int nfold = seg;
     uint4 ra[D][APT], ral[APT];
-    f32x4 rb[D][NDB], rbl[NDB];
-    auto issue = [&](uint4 (&a)[APT], f32x4 (&b)[NDB], int i, bool ok) {
+    f32x4 rb[D][RB], rbl[RB];
+    auto issue = [&](uint4 (&a)[APT], f32x4 (&b)[RB], int i, bool ok) {
 #pragma unroll
         for (int j = 0; j < APT; ++j)
-            a[j] = buf_load16(rA, ok ? (unsigned)(i * DK * DK * 2 + (tid + 256 * j) * 16) : kOffNone);
+            a[j] = buf_load16(rA, (ok && tid + 1024 * j < APC) ? (unsigned)(i * APC * 16 + (tid + 1024 * j) * 16)
+                                                               : kOffNone);
 #pragma unroll
-        for (int ib = 0; ib < NDB; ++ib)
-            b[ib] = __builtin_bit_cast(f32x4, buf_load16(rB,
-                        ok ? (unsigned)(i * DK * dv * 4 + ((c16 * NDB + ib) * 64 + lane) * 16) : kOffNone));
+        for (int r = 0; r < RB; ++r)
+            b[r] = __builtin_bit_cast(f32x4, buf_load16(rB,
+                        ok ? (unsigned)(i * DK * dv * 4 + ((c16 * NDB + rg * RB + r) * 64 + lane) * 16) : kOffNone));
     };
-    // M <- A M + B with A from an LDS copy; the fragments of A are read in
-    // batches of at most 16 so that the MFMAs do not wait on each read
-    auto apply = [&](const uint4* sl, const f32x4 (&b)[NDB]) {
-        F mF[KS_D];
+    // A_s into LDS copy buf (APC pieces over the first APC threads' slots)
+    auto put_a = [&](const uint4 (&a)[APT], int buf) {
 #pragma unroll
-        for (int ks = 0; ks < KS_D; ++ks) mF[ks] = Op::b_acc(Macc, ks);
-        constexpr int G = NDB * KS_D <= 16 ? NDB : 16 / KS_D;
+        for (int j = 0; j < APT; ++j)
+            if (tid + 1024 * j < APC) Ast[buf][tid + 1024 * j] = a[j];
+    };
+    // this wave's rows of M as halves of fp16 B fragments (rows 32 ks + 16 h + ...)
+    auto put_m = [&](int buf) {
 #pragma unroll
-        for (int ib0 = 0; ib0 < NDB; ib0 += G) {
-            F fa[G][KS_D];
+        for (int r = 0; r < RB; ++r) {
+            const int ib = rg * RB + r;
+            reinterpret_cast<uint2*>(&Mf[buf][ib / 2][cg][lane])[ib & 1] =
+                make_uint2(Op::pk2(Macc[r][0], Macc[r][1]), Op::pk2(Macc[r][2], Macc[r][3]));
+        }
+    };
+    auto get_m = [&](F (&mF)[KS_D], int buf) {
 #pragma unroll
-            for (int g = 0; g < G; ++g)
+        for (int ks = 0; ks < KS_D; ++ks) mF[ks] = __builtin_bit_cast(F, Mf[buf][ks][cg][lane]);
+    };
+    // this wave's rows of A M + B
+    auto apply = [&](const F (&mF)[KS_D], int buf, const f32x4 (&b)[RB]) {
+        F fa[RB][KS_D];
 #pragma unroll
-                for (int ks = 0; ks < KS_D; ++ks)
-                    fa[g][ks] = __builtin_bit_cast(F, sl[((ib0 + g) * KS_D + ks) * 64 + lane]);
+        for (int r = 0; r < RB; ++r)
 #pragma unroll
-            for (int g = 0; g < G; ++g) {
-                f32x4 acc = b[ib0 + g];
+            for (int ks = 0; ks < KS_D; ++ks)
+                fa[r][ks] = __builtin_bit_cast(F, Ast[buf][((rg * RB + r) * KS_D + ks) * 64 + lane]);
 #pragma unroll
-                for (int ks = 0; ks < KS_D; ++ks) acc = Op::mma(fa[g][ks], mF[ks], acc);
-                Macc[ib0 + g] = acc;
-            }
+        for (int r = 0; r < RB; ++r) {
+            f32x4 acc = b[r];
+#pragma unroll
+            for (int ks = 0; ks < KS_D; ++ks) acc = Op::mma(fa[r][ks], mF[ks], acc);
+            Macc[r] = acc;
         }
     };
     issue(ral, rbl, seg, last);
@@ -997,70 +1011,67 @@ __global__ __launch_bounds__(256) void gdn_pipe_fix_kernel(WalkArgs p) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             const int i = i0 + d;
-            uint4* slot = Ast[i & 1];
-#pragma unroll
-            for (int j = 0; j < APT; ++j) slot[tid + 256 * j] = ra[d][j];
+            // copies i & 1 were last read two steps ago, before the previous barrier
+            put_a(ra[d], i & 1);
+            put_m(i & 1);
             __syncthreads();
-            if (i < nfold) apply(slot, rb[d]);
+            if (i < nfold) {
+                F mF[KS_D];
+                get_m(mF, i & 1);
+                apply(mF, i & 1, rb[d]);
+            }
             issue(ra[d], rb[d], i + D, i + D < nfold);
         }
     }
-    f32x4 Min[NDB];                                     // state entering this segment
-#pragma unroll
-    for (int ib = 0; ib < NDB; ++ib) Min[ib] = Macc[ib];
-    if (last) {
-        uint4* slot = Ast[nfold & 1];
-#pragma unroll
-        for (int j = 0; j < APT; ++j) slot[tid + 256 * j] = ral[j];
-        __syncthreads();
-        apply(slot, rbl);
-    }
-
-    // ---- outputs of the segment: O += Phi M_in
+    // M_in of this segment as B fragments for every wave; the last segment's
+    // own map alongside
+    put_m(nfold & 1);
+    if (last) put_a(ral, nfold & 1);
+    __syncthreads();
     F mI[KS_D];
-#pragma unroll
-    for (int ks = 0; ks < KS_D; ++ks) mI[ks] = Op::b_acc(Min, ks);
-    auto cfix = [&](const uint4 (&h)[PPT], const uint2 (&o)[NB], int c, int slot) {
-        const bool ok = c < ch1;
-        uint4* sl = Phs[slot];
-#pragma unroll
-        for (int j = 0; j < PPT; ++j) sl[tid + 256 * j] = h[j];
-        __syncthreads();                 // slot reused PB chunks later, after another barrier
-#pragma unroll
-        for (int r = 0; r < NB; ++r) {
-            typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-            const h4 ot = __builtin_bit_cast(h4, o[r]);
-            f32x4 acc = {(float)ot[0], (float)ot[1], (float)ot[2], (float)ot[3]};
-#pragma unroll
-            for (int ks = 0; ks < KS_D; ++ks)
-                acc = Op::mma(mI[ks], __builtin_bit_cast(F, sl[(r * KS_D + ks) * 64 + lane]), acc);
-            // rows past T fall outside the buffer and are dropped
-            const unsigned e0 = (unsigned)((c * C + 16 * r + lc) * dv + col4);
-            if (p.out_bf16) {
-                const uint2 w = make_uint2(
-                    (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[0]) |
-                        ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[1]) << 16),
-                    (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[2]) |
-                        ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[3]) << 16));
-                buf_store8(rW, ok ? e0 * 2u : kOffNone, w);
-            } else {
-                buf_store16(rW, ok ? e0 * 4u : kOffNone, __builtin_bit_cast(uint4, acc));
-            }
-        }
-    };
-    for (int c = ch0; c < ch1; c += PB) {
-#pragma unroll
-        for (int b = 0; b < PB; ++b) {
-            cfix(ph[b], ov[b], c + b, b);
-            cload(ph[b], ov[b], c + b + PB);
-        }
-    }
+    get_m(mI, nfold & 1);
     if (last) {
+        apply(mI, nfold & 1, rbl);
         float* sp = p.state_out + (size_t)bh * DK * dv + col;
 #pragma unroll
-        for (int ib = 0; ib < NDB; ++ib)
+        for (int r = 0; r < RB; ++r)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sp[(16 * ib + 4 * lg + i) * dv] = Macc[ib][i];
+            for (int i = 0; i < 4; ++i) sp[(16 * (rg * RB + r) + 4 * lg + i) * dv] = Macc[r][i];
+    }
+
+    // ---- outputs of the segment: O += Phi M_in, formed transposed
+    // (O^T = M^T Phi^T): lane (lg, lc) holds row lc of the wave's row block
+    // and four consecutive columns, one 16-byte access
+    const int col4 = vt * 64 + 16 * cg + 4 * lg;
+    auto cfix = [&](const uint4& h, const uint2& o, int g, int buf) {
+        const int c = ch0 + g * CPG + rg / NB, rb = rg % NB;
+        if (tid < PPG) Phs[buf][tid] = h;
+        __syncthreads();                  // copy buf reused two groups later, after another barrier
+        typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+        const h4 ot = __builtin_bit_cast(h4, o);
+        f32x4 acc = {(float)ot[0], (float)ot[1], (float)ot[2], (float)ot[3]};
+#pragma unroll
+        for (int ks = 0; ks < KS_D; ++ks)
+            acc = Op::mma(mI[ks], __builtin_bit_cast(F, Phs[buf][(rg * KS_D + ks) * 64 + lane]), acc);
+        // rows past T fall outside the buffer and are dropped
+        const unsigned e0 = (unsigned)((c * C + 16 * rb + lc) * dv + col4);
+        if (p.out_bf16) {
+            const uint2 w = make_uint2(
+                (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[0]) |
+                    ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[1]) << 16),
+                (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[2]) |
+                    ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[3]) << 16));
+            buf_store8(rW, c < ch1 ? e0 * 2u : kOffNone, w);
+        } else {
+            buf_store16(rW, c < ch1 ? e0 * 4u : kOffNone, __builtin_bit_cast(uint4, acc));
+        }
+    };
+    const int ngroups = (ch1 - ch0 + CPG - 1) / CPG;
+    for (int g = 0; g < ngroups; g += 2) {
+        cfix(ph[0], ov[0], g, 0);
+        cload(ph[0], ov[0], g + 2);
+        cfix(ph[1], ov[1], g + 1, 1);
+        cload(ph[1], ov[1], g + 3);
     }
 }
 
@@ -1084,7 +1095,7 @@ hipError_t launch_pipe_t(const WalkArgs& a, hipStream_t s) {
         hipLaunchKernelGGL((gdn_pipe_kernel<DK, C, SCT, true, SNCW>), dim3(grid), dim3(64 * (SNCW + 4)), 0, s, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((gdn_pipe_fix_kernel<DK, C>), dim3(bh * a.nseg * (a.dv / 64)), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((gdn_pipe_fix_kernel<DK, C>), dim3(bh * a.nseg * (a.dv / 64)), dim3(1024), 0, s, a);
         return hipGetLastError();
     }
     hipLaunchKernelGGL((gdn_pipe_kernel<DK, C, 1, false, 4, UNPW>), dim3(bh * (a.dv / 64)), dim3(64 * (4 + UNPW)), 0, s, a);
