@@ -72,6 +72,14 @@ typedef struct gdn_opts {
     void*  stream;           /* hipStream_t; NULL = null stream                   */
     void*  workspace;        /* device scratch for the split-sequence path        */
     size_t workspace_bytes;  /* size of workspace                                 */
+    /* Fused gates (SANA-Streaming, appendix G.3 names a decay gate, a write
+     * gate and an output gate; their formulas are not on the page, so the
+     * maps are those the benchmark inputs are drawn with): */
+    int    gate_logits;      /* 0 (default): alpha, beta are the gate values;
+                                1: they are logits a, b and the kernel forms
+                                alpha = exp(-softplus(a)), beta = sigmoid(b)   */
+    const void* out_gate;    /* NULL (default), or [B][H][T][dv] in in_dtype:
+                                out = o_t * g_t elementwise                     */
 } gdn_opts;
 
 /* Fill *opts with the defaults listed above. */

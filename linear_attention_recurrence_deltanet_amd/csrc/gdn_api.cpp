@@ -36,6 +36,8 @@ void defaults(gdn_opts* o) {
     o->stream = nullptr;
     o->workspace = nullptr;
     o->workspace_bytes = 0;
+    o->gate_logits = 0;
+    o->out_gate = nullptr;
 }
 
 int validate(const void* q, const void* k, const void* v, const void* alpha, const void* beta,
@@ -57,6 +59,8 @@ int validate(const void* q, const void* k, const void* v, const void* alpha, con
             return fail(GDN_ERR_ARG, "q, k, v, alpha, beta and out must be non-null when T > 0");
         if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
             return fail(GDN_ERR_ARG, "q, k, v and out must be 16-byte aligned");
+        if (o.out_gate && !aligned16(o.out_gate))
+            return fail(GDN_ERR_ARG, "out_gate must be 16-byte aligned");
         const size_t esz = o.in_dtype == GDN_F32 ? 4 : 2;
         if ((reinterpret_cast<uintptr_t>(alpha) % esz) || (reinterpret_cast<uintptr_t>(beta) % esz))
             return fail(GDN_ERR_ARG, "alpha and beta must be aligned to their element size");
@@ -185,6 +189,8 @@ int run(const void* q, const void* k, const void* v, const void* alpha, const vo
     a.B = B; a.H = H; a.T = T; a.dk = dk; a.dv = dv;
     a.scale = o.scale; a.eps = o.eps; a.qk_l2norm = o.qk_l2norm ? 1 : 0;
     a.out_bf16 = o.out_dtype == GDN_BF16; a.in_f32 = o.in_dtype == GDN_F32;
+    a.gate_logits = o.gate_logits ? 1 : 0;
+    a.out_gate = o.out_gate;
     if (T == 0 && !state_out) return GDN_OK;
     Plan pl = make_plan(a.in_f32, B, H, T, dk, dv, chunk);
     hipStream_t stream = reinterpret_cast<hipStream_t>(o.stream);

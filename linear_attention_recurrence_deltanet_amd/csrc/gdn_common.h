@@ -193,6 +193,36 @@ __device__ __forceinline__ void buf_store16(rsrc_t r, unsigned off, uint4 v) {
 constexpr unsigned kOffNone = 0x80000000u;
 
 // ---------------------------------------------------------------------------
+// Gate maps.  The decay and write gates arrive as values (alpha in (0, 1],
+// beta) or as logits a, b with alpha = exp(-softplus(a)), beta = sigmoid(b).
+// The scan needs log2 alpha; from a logit it is formed directly,
+// -softplus(a) / ln 2 = -(max(a, 0) + log(1 + exp(-|a|))) / ln 2, which
+// stays exact where alpha rounds to 1 in fp32.  log2(0) is clamped at -200
+// (2^-200 is 0 in fp32, so the state resets as alpha = 0 asks).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float gate_log2_alpha(float x, bool logits) {
+    constexpr float kLog2e = 1.4426950408889634f;
+    if (!logits) return fmaxf(log2f(x), -200.f);
+    const float t = exp2f(-fabsf(x) * kLog2e);                 // exp(-|a|) in (0, 1]
+    return -(fmaxf(x, 0.f) * kLog2e + log2f(1.f + t));
+}
+__device__ __forceinline__ float gate_beta(float x, bool logits) {
+    constexpr float kLog2e = 1.4426950408889634f;
+    return logits ? 1.f / (1.f + exp2f(-x * kLog2e)) : x;
+}
+
+// Output gate (elementwise on out, input dtype): element e of a head's slice,
+// and four consecutive bf16 values (8 bytes) as fp32.
+__device__ __forceinline__ float gate_at(rsrc_t r, unsigned e, bool f32) {
+    return f32 ? __builtin_bit_cast(float, buf_load4(r, e * 4u)) : bf16_to_f32(buf_load2(r, e * 2u));
+}
+__device__ __forceinline__ f32x4 gate4_bf16(rsrc_t r, unsigned e) {
+    const uint2 w = buf_load8(r, e * 2u);
+    return f32x4{__builtin_bit_cast(float, w.x << 16), __builtin_bit_cast(float, w.x & 0xffff0000u),
+                 __builtin_bit_cast(float, w.y << 16), __builtin_bit_cast(float, w.y & 0xffff0000u)};
+}
+
+// ---------------------------------------------------------------------------
 // Cross-lane helpers on DPP (no LDS traffic).
 // ---------------------------------------------------------------------------
 template <int CTRL, int ROW_MASK = 0xF, bool BOUND_ZERO = false>

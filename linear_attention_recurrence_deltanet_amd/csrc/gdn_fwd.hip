@@ -228,6 +228,9 @@ void gdn_walk_kernel(WalkArgs p) {
     const unsigned osz = p.out_bf16 ? 2u : 4u;
     const rsrc_t ro_ = make_rsrc(SUMMARY ? nullptr : (const char*)p.out + (size_t)bh * T * dv * osz,
                                  SUMMARY ? 0u : (unsigned)T * dv * osz);
+    const bool gated = !SUMMARY && p.out_gate != nullptr;
+    const rsrc_t rg_ = make_rsrc(gated ? (const char*)p.out_gate + (size_t)bh * T * dv * SI : nullptr,
+                                 gated ? (unsigned)T * dv * SI : 0u);
 
     // Structurally zero parts of the persistent matrices (upper blocks).
     for (int e = tid; e < C * C; e += NT) {
@@ -397,10 +400,9 @@ void gdn_walk_kernel(WalkArgs p) {
             for (int e = 0; e < TPL; ++e) {
                 const int r = lane * TPL + e;
                 const bool ok = r < n;
-                const float a = ok ? InTraits<In>::to_f32(pa[e]) : 1.f;
-                bb[e] = ok ? InTraits<In>::to_f32(pb[e]) : 0.f;
-                // log2(0) would make g_r - g_s undefined; 2^-200 is 0 in fp32 anyway
-                run += (r < C) ? fmaxf(log2f(a), -200.f) : 0.f;
+                // padding rows: alpha = 1, beta = 0
+                bb[e] = ok ? gate_beta(InTraits<In>::to_f32(pb[e]), p.gate_logits) : 0.f;
+                run += ok ? gate_log2_alpha(InTraits<In>::to_f32(pa[e]), p.gate_logits) : 0.f;
                 la[e] = run;
             }
             const float incl = wave_prefix_sum(run);
@@ -639,6 +641,10 @@ void gdn_walk_kernel(WalkArgs p) {
                 for (int ks = 0; ks < KS_C; ++ks) Oacc[rb] = Op::mma(fp[rb][ks], uB[ks], Oacc[rb]);
                 // rows past T fall outside the buffer and are dropped
                 const unsigned o0 = (unsigned)((t0 + 16 * rb + 4 * lg) * dv + vcol0 + mycol);
+                if (gated) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) Oacc[rb][i] *= gate_at(rg_, o0 + i * dv, SI == 4);
+                }
                 if (p.out_bf16) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i)

@@ -238,10 +238,12 @@ void gdn_fwd_single_kernel(FwdArgs p) {
 #pragma unroll
             for (int e = 0; e < TPL; ++e) {
                 const int r = lane * TPL + e;
-                float a = 1.f, b = 0.f;
-                if (r < n) { a = InTraits<In>::to_f32(ag[t0 + r]); b = InTraits<In>::to_f32(bg[t0 + r]); }
-                // log2(0) = -inf would make g_r - g_s undefined; 2^-200 is 0 in fp32 anyway.
-                float l2 = (r < C) ? fmaxf(log2f(a), -200.f) : 0.f;
+                // padding rows: alpha = 1, beta = 0
+                float l2 = 0.f, b = 0.f;
+                if (r < n) {
+                    l2 = gate_log2_alpha(InTraits<In>::to_f32(ag[t0 + r]), p.gate_logits);
+                    b = gate_beta(InTraits<In>::to_f32(bg[t0 + r]), p.gate_logits);
+                }
                 run += l2;
                 la[e] = run;
                 be[e] = b;
@@ -518,10 +520,13 @@ void gdn_fwd_single_kernel(FwdArgs p) {
                     const int r = r0 + i;
                     if (r < n) {
                         const size_t o = ((size_t)bh * T + t0 + r) * dv + c;
+                        float ov = Oacc[sl][i];
+                        if (p.out_gate)
+                            ov *= InTraits<In>::to_f32(reinterpret_cast<const In*>(p.out_gate)[o]);
                         if (p.out_bf16)
-                            reinterpret_cast<uint16_t*>(p.out)[o] = f32_to_bf16(Oacc[sl][i]);
+                            reinterpret_cast<uint16_t*>(p.out)[o] = f32_to_bf16(ov);
                         else
-                            reinterpret_cast<float*>(p.out)[o] = Oacc[sl][i];
+                            reinterpret_cast<float*>(p.out)[o] = ov;
                     }
                 }
             }

@@ -20,6 +20,8 @@ struct FwdArgs {
     int qk_l2norm;
     int out_bf16;            // 1: out is bf16, 0: fp32
     int in_f32;              // 1: inputs fp32, 0: bf16
+    int gate_logits;         // 1: alpha, beta hold logits (gate_log2_alpha, gate_beta)
+    const void* out_gate;    // null, or [B*H][T][dv] in the input dtype: out *= gate
 };
 
 // Segmented chunk walkers (chunk 32 or 64).  With nseg > 1 the workspace

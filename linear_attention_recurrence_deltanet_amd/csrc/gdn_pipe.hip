@@ -229,7 +229,9 @@ __device__ __forceinline__ f32x4 transpose16_bf16(const uint16_t* a, int lda, in
 // NCW: state waves (4, or 8 with one column tile each: three waves per SIMD
 //      instead of two when one state wave would otherwise carry two tiles).
 // NPW: key waves (4 or 8).
-template <int DK, int C, int CT, bool SEG, int NCW = 4, int NPW = 4>
+// GATES: gate logits and the output gate are honoured (a separate
+//        instantiation, so that calls without them run no gate code).
+template <int DK, int C, int CT, bool SEG, int NCW = 4, int NPW = 4, bool GATES = false>
 __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) {
     typedef PPlan<DK, C, CT, SEG, NCW, NPW> L;
     typedef OpF16 Op;
@@ -336,6 +338,10 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
     const unsigned osz = p.out_bf16 ? 2u : 4u;
     const rsrc_t ro_ = make_rsrc(SEG ? nullptr : (const char*)p.out + (size_t)bh * T * dv * osz,
                                  SEG ? 0u : (unsigned)T * dv * osz);
+    const bool gated = GATES && !SEG && p.out_gate != nullptr;   // a segment walk leaves it to the correction
+    const bool logits = GATES && p.gate_logits;
+    const rsrc_t rg_ = make_rsrc(gated ? (const char*)p.out_gate + (size_t)bh * T * dv * 2 : nullptr,
+                                 gated ? (unsigned)T * dv * 2u : 0u);
     // Phi of this segment: [chunk][row block][k-step of 32 columns of d_k][lane] x 8 fp16,
     // an MFMA operand fragment in accumulator k order (16-column blocks 2 ks, 2 ks + 1);
     // partial outputs: [chunk][row block][16 value columns][lane] x 4 fp16
@@ -505,6 +511,11 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
                                 // rows past T fall outside the buffer and are dropped
                                 const unsigned e0 = (unsigned)(t0 + 16 * rb + lc) * (unsigned)dv +
                                                     (unsigned)(vbase + col0(ct) + 4 * lg);
+                                if (gated) {
+                                    const f32x4 gv = gate4_bf16(rg_, e0);
+#pragma unroll
+                                    for (int i = 0; i < 4; ++i) o[i] *= gv[i];
+                                }
                                 if (p.out_bf16) {
                                     const uint2 w = make_uint2(
                                         (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)o[0]) |
@@ -648,10 +659,9 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
                 for (int e = 0; e < TPL; ++e) {
                     const int r = lane * TPL + e;
                     const bool ok = r < n;
-                    const float a = ok ? bf16_to_f32(pa[e]) : 1.f;
-                    bb[e] = ok ? bf16_to_f32(pb[e]) : 0.f;
-                    // log2(0) would make g_r - g_s undefined; 2^-200 is 0 in fp32 anyway
-                    run += (r < C) ? fmaxf(log2f(a), -200.f) : 0.f;
+                    // padding rows: alpha = 1, beta = 0
+                    bb[e] = ok ? gate_beta(bf16_to_f32(pb[e]), logits) : 0.f;
+                    run += ok ? gate_log2_alpha(bf16_to_f32(pa[e]), logits) : 0.f;
                     la[e] = run;
                 }
                 const float incl = wave_prefix_sum(run);
@@ -922,6 +932,9 @@ __global__ __launch_bounds__(1024) void gdn_pipe_fix_kernel(WalkArgs p) {
                                 (unsigned)(p.seg_chunks * C * dv * 2));
     const rsrc_t rW = make_rsrc((const char*)p.out + (size_t)bh * T * dv * (p.out_bf16 ? 2 : 4),
                                 (unsigned)T * dv * (p.out_bf16 ? 2u : 4u));
+    const bool gated = p.out_gate != nullptr;
+    const rsrc_t rG = make_rsrc(gated ? (const char*)p.out_gate + (size_t)bh * T * dv * 2 : nullptr,
+                                gated ? (unsigned)T * dv * 2u : 0u);
 
     // Loads and stores below are unconditional (kOffNone where there is
     // nothing to move) so that the compiler counts the loads in flight
@@ -1055,6 +1068,11 @@ __global__ __launch_bounds__(1024) void gdn_pipe_fix_kernel(WalkArgs p) {
             acc = Op::mma(mI[ks], __builtin_bit_cast(F, Phs[buf][(rg * KS_D + ks) * 64 + lane]), acc);
         // rows past T fall outside the buffer and are dropped
         const unsigned e0 = (unsigned)((c * C + 16 * rb + lc) * dv + col4);
+        if (gated) {
+            const f32x4 gv = gate4_bf16(rG, e0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] *= gv[i];
+        }
         if (p.out_bf16) {
             const uint2 w = make_uint2(
                 (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[0]) |
@@ -1080,8 +1098,8 @@ __global__ __launch_bounds__(1024) void gdn_pipe_fix_kernel(WalkArgs p) {
 // ---------------------------------------------------------------------------
 namespace {
 
-template <int DK, int C, int CTS>
-hipError_t launch_pipe_t(const WalkArgs& a, hipStream_t s) {
+template <int DK, int C, int CTS, bool GATES>
+hipError_t launch_pipe_g(const WalkArgs& a, hipStream_t s) {
     // a segment tile of 128 columns: eight state waves of one tile each
     // (three waves per SIMD; measured faster than four state waves of two
     // tiles, which spill at d_k = 128)
@@ -1092,14 +1110,20 @@ hipError_t launch_pipe_t(const WalkArgs& a, hipStream_t s) {
     const int bh = a.B * a.H;
     if (a.nseg > 1) {
         const int grid = bh * a.nseg * ((DK + a.dv) / (64 * CTS));
-        hipLaunchKernelGGL((gdn_pipe_kernel<DK, C, SCT, true, SNCW>), dim3(grid), dim3(64 * (SNCW + 4)), 0, s, a);
+        hipLaunchKernelGGL((gdn_pipe_kernel<DK, C, SCT, true, SNCW, 4, GATES>), dim3(grid), dim3(64 * (SNCW + 4)), 0, s, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL((gdn_pipe_fix_kernel<DK, C>), dim3(bh * a.nseg * (a.dv / 64)), dim3(1024), 0, s, a);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL((gdn_pipe_kernel<DK, C, 1, false, 4, UNPW>), dim3(bh * (a.dv / 64)), dim3(64 * (4 + UNPW)), 0, s, a);
+    hipLaunchKernelGGL((gdn_pipe_kernel<DK, C, 1, false, 4, UNPW, GATES>), dim3(bh * (a.dv / 64)), dim3(64 * (4 + UNPW)), 0, s, a);
     return hipGetLastError();
+}
+
+template <int DK, int C, int CTS>
+hipError_t launch_pipe_t(const WalkArgs& a, hipStream_t s) {
+    if (a.gate_logits || a.out_gate) return launch_pipe_g<DK, C, CTS, true>(a, s);
+    return launch_pipe_g<DK, C, CTS, false>(a, s);
 }
 
 template <int DK, int C>

@@ -31,7 +31,9 @@ class GdnOpts(ctypes.Structure):
                 ("eps", ctypes.c_float),
                 ("stream", ctypes.c_void_p),
                 ("workspace", ctypes.c_void_p),
-                ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace_bytes", ctypes.c_size_t),
+                ("gate_logits", ctypes.c_int),
+                ("out_gate", ctypes.c_void_p)]
 
 
 class GdnError(RuntimeError):
@@ -85,7 +87,8 @@ def _ptr(t: Optional[torch.Tensor]):
 
 
 def make_opts(in_dtype=torch.bfloat16, out_dtype=torch.float32, qk_l2norm=True, scale=1.0,
-              eps=1e-6, stream=None, workspace: Optional[torch.Tensor] = None) -> GdnOpts:
+              eps=1e-6, stream=None, workspace: Optional[torch.Tensor] = None,
+              gate_logits: bool = False, out_gate: Optional[torch.Tensor] = None) -> GdnOpts:
     o = GdnOpts()
     load().gdn_default_opts(ctypes.byref(o))
     o.in_dtype = _dtype_code(in_dtype)
@@ -99,6 +102,9 @@ def make_opts(in_dtype=torch.bfloat16, out_dtype=torch.float32, qk_l2norm=True, 
     if workspace is not None:
         o.workspace = ctypes.c_void_p(workspace.data_ptr())
         o.workspace_bytes = workspace.numel() * workspace.element_size()
+    o.gate_logits = 1 if gate_logits else 0
+    if out_gate is not None:
+        o.out_gate = ctypes.c_void_p(out_gate.data_ptr())
     return o
 
 
@@ -150,20 +156,32 @@ def _prep(q, k, v, alpha, beta, state_in, out, state_out, out_dtype):
     return B, H, T, dk, dv, out, state_out
 
 
+def _check_gate(out_gate, q, B, H, T, dv):
+    if out_gate is None:
+        return
+    if (not out_gate.is_cuda or not out_gate.is_contiguous() or out_gate.dtype != q.dtype
+            or tuple(out_gate.shape) != (B, H, T, dv)):
+        raise ValueError("out_gate must be a contiguous device tensor [B, H, T, dv] of q's dtype")
+
+
 def fwd_chunked(q, k, v, alpha, beta, state_in=None, chunk: int = 64, *, out=None, state_out=None,
                 out_dtype=torch.float32, qk_l2norm=True, scale=1.0, eps=1e-6, stream=None,
-                workspace=None, want_state: bool = True):
+                workspace=None, want_state: bool = True, gate_logits: bool = False, out_gate=None):
     """gdn_fwd_chunked.  Returns (out, state_out).
 
     workspace: None allocates the scratch the launch plan asks for (sequence
     split into segments when there are few heads); False passes none, which
-    makes the library walk each sequence unsplit; or a uint8 device tensor."""
+    makes the library walk each sequence unsplit; or a uint8 device tensor.
+    gate_logits: alpha and beta are logits (alpha = exp(-softplus(a)),
+    beta = sigmoid(b) inside the kernel).  out_gate: multiplies out
+    elementwise."""
     B, H, T, dk, dv, out, state_out = _prep(q, k, v, alpha, beta, state_in, out,
                                             state_out if want_state else None, out_dtype)
     if not want_state:
         state_out = None
+    _check_gate(out_gate, q, B, H, T, dv)
     workspace = _workspace(workspace, B, H, T, dk, dv, chunk, q.dtype, out.dtype, q.device)
-    opts = make_opts(q.dtype, out.dtype, qk_l2norm, scale, eps, stream, workspace)
+    opts = make_opts(q.dtype, out.dtype, qk_l2norm, scale, eps, stream, workspace, gate_logits, out_gate)
     _check(load().gdn_fwd_chunked(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
                                   _ptr(state_in), _ptr(out), _ptr(state_out),
                                   B, H, T, dk, dv, int(chunk), ctypes.byref(opts)))
@@ -172,13 +190,14 @@ def fwd_chunked(q, k, v, alpha, beta, state_in=None, chunk: int = 64, *, out=Non
 
 def fwd_step(q, k, v, alpha, beta, state_in=None, *, out=None, state_out=None,
              out_dtype=torch.float32, qk_l2norm=True, scale=1.0, eps=1e-6, stream=None,
-             workspace=None):
+             workspace=None, gate_logits: bool = False, out_gate=None):
     """gdn_fwd_step: one streaming chunk.  state_out may be state_in (in place).
-    workspace as for fwd_chunked."""
+    workspace, gate_logits and out_gate as for fwd_chunked."""
     B, H, T, dk, dv, out, state_out = _prep(q, k, v, alpha, beta, state_in, out, state_out,
                                             out_dtype)
+    _check_gate(out_gate, q, B, H, T, dv)
     workspace = _workspace(workspace, B, H, T, dk, dv, 0, q.dtype, out.dtype, q.device)
-    opts = make_opts(q.dtype, out.dtype, qk_l2norm, scale, eps, stream, workspace)
+    opts = make_opts(q.dtype, out.dtype, qk_l2norm, scale, eps, stream, workspace, gate_logits, out_gate)
     _check(load().gdn_fwd_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
                                _ptr(state_in), _ptr(out), _ptr(state_out),
                                B, H, T, dk, dv, ctypes.byref(opts)))

@@ -77,11 +77,15 @@ def _unit_rows(x: torch.Tensor) -> torch.Tensor:
 
 
 def make_call(wl: Workload, call: int = 0, *, B: Optional[int] = None, H: Optional[int] = None,
-              T: Optional[int] = None):
+              T: Optional[int] = None, gates: bool = False):
     """Draw the inputs of call number `call` (CPU tensors in the workload dtype).
 
     B, H, T may be overridden (smaller tests) while keeping the distribution.
     Returns dict(q, k, v, alpha, beta) plus 'state_in' (fp32, or None).
+    gates: also 'alpha_logit', 'beta_logit' (the normal draws alpha and beta
+    are mapped from, in the workload dtype) and 'out_gate' ([B,H,T,dv],
+    sigmoid of a standard normal draw), drawn after everything else so that
+    the other inputs do not change.
     """
     B = wl.B if B is None else B
     H = wl.H if H is None else H
@@ -100,8 +104,13 @@ def make_call(wl: Workload, call: int = 0, *, B: Optional[int] = None, H: Option
     if call == 0 and wl.state_sigma is not None:
         state = torch.randn(B, H, wl.dk, wl.dv, generator=g, dtype=f32) * wl.state_sigma
     dt = wl.torch_dtype
-    return dict(q=q.to(dt), k=k.to(dt), v=v.to(dt), alpha=alpha.to(dt), beta=beta.to(dt),
-                state_in=state)
+    d = dict(q=q.to(dt), k=k.to(dt), v=v.to(dt), alpha=alpha.to(dt), beta=beta.to(dt),
+             state_in=state)
+    if gates:
+        d["alpha_logit"] = za.to(dt)
+        d["beta_logit"] = zb.to(dt)
+        d["out_gate"] = torch.sigmoid(torch.randn(B, H, T, wl.dv, generator=g, dtype=f32)).to(dt)
+    return d
 
 
 def to_numpy64(t: torch.Tensor):

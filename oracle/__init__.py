@@ -50,6 +50,8 @@ def _load():
                                        ctypes.c_long, ctypes.c_long,
                                        ctypes.c_int, ctypes.c_double, ctypes.c_double,
                                        ctypes.c_int]
+        lib.gdn_oracle_gates.restype = None
+        lib.gdn_oracle_gates.argtypes = [dp, dp, dp, dp, ctypes.c_long]
         _lib = lib
     return _lib
 
@@ -64,16 +66,30 @@ def _ptr(a):
     return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
 
 
+def gates(a, b):
+    """alpha = exp(-softplus(a)), beta = sigmoid(b) in fp64 (gdn_oracle_gates)."""
+    a, b = _f64(a), _f64(b)
+    assert a.shape == b.shape
+    alpha = np.empty_like(a)
+    beta = np.empty_like(b)
+    _load().gdn_oracle_gates(_ptr(a), _ptr(b), _ptr(alpha), _ptr(beta), a.size)
+    return alpha, beta
+
+
 def gdn_fwd(q, k, v, alpha, beta, state_in=None, *, qk_l2norm=True, scale=1.0,
-            eps=DEFAULT_EPS, nthreads=0, want_state=True):
+            eps=DEFAULT_EPS, nthreads=0, want_state=True, gate_logits=False, out_gate=None):
     """Token-by-token fp64 gated delta rule.
 
     Shapes: q, k [B,H,T,dk]; v [B,H,T,dv]; alpha, beta [B,H,T];
     state_in [B,H,dk,dv] or None (zero state).  Inputs of any float dtype are
     converted to fp64 exactly (bf16/fp16/fp32 all embed in fp64).
+    gate_logits: alpha, beta hold logits a, b (see gates()).  out_gate
+    [B,H,T,dv]: the outputs are multiplied by it elementwise.
     Returns (out [B,H,T,dv] fp64, state_out [B,H,dk,dv] fp64 or None).
     """
     q, k, v, alpha, beta = (_f64(x) for x in (q, k, v, alpha, beta))
+    if gate_logits:
+        alpha, beta = gates(alpha, beta)
     B, H, T, dk = q.shape
     dv = v.shape[-1]
     assert k.shape == (B, H, T, dk) and v.shape == (B, H, T, dv)
@@ -90,4 +106,8 @@ def gdn_fwd(q, k, v, alpha, beta, state_in=None, *, qk_l2norm=True, scale=1.0,
                                 float(scale), float(eps), int(nthreads))
     if rc != 0:
         raise RuntimeError("gdn_oracle_fwd failed with code %d" % rc)
+    if out_gate is not None:
+        g = _f64(out_gate)
+        assert g.shape == out.shape
+        out = out * g
     return out, s_out

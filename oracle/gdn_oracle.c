@@ -156,4 +156,23 @@ int gdn_oracle_fwd(const double* q, const double* k, const double* v,
     return err ? -2 : 0;
 }
 
-int gdn_oracle_abi_version(void) { return 1; }
+/*
+ * gdn_oracle_gates: the decay and write gates from their logits, n values.
+ * SANA-Streaming (paperpeel page, appendix G.3 "Gate parameterization") names
+ * a frame-wise decay gate, a token-wise write gate and an output gate but the
+ * formulas did not survive on the page; the maps used are those the benchmark
+ * inputs are drawn with:
+ *     alpha = exp(-softplus(a)),  softplus(a) = log(1 + exp(a))
+ *     beta  = 1 / (1 + exp(-b))
+ * softplus is evaluated as max(a, 0) + log1p(exp(-|a|)), the same number
+ * without overflow of exp for large a.
+ */
+void gdn_oracle_gates(const double* a, const double* b, double* alpha, double* beta, long n) {
+    for (long i = 0; i < n; ++i) {
+        double sp = (a[i] > 0.0 ? a[i] : 0.0) + log1p(exp(-fabs(a[i])));
+        alpha[i] = exp(-sp);
+        beta[i] = 1.0 / (1.0 + exp(-b[i]));
+    }
+}
+
+int gdn_oracle_abi_version(void) { return 2; }

@@ -47,6 +47,7 @@ def test_default_opts(lib):
     assert (o.in_dtype, o.out_dtype, o.qk_l2norm) == (gdn.GDN_BF16, gdn.GDN_F32, 1)
     assert o.scale == 1.0 and abs(o.eps - 1e-6) < 1e-12
     assert o.stream is None and o.workspace is None and o.workspace_bytes == 0
+    assert o.gate_logits == 0 and o.out_gate is None
 
 
 def _call(lib, q=16, k=16, v=16, a=16, b=16, sin=None, out=16, sout=None,

@@ -262,3 +262,55 @@ def test_nan_propagates(oracle_mod):
     out, st = oracle_mod.gdn_fwd(q, k, v, a, b, s, eps=0.0)
     assert np.isnan(out[0, 0, 2, 1]) and np.isnan(st[0, 0, :, 1]).any()
     assert np.isfinite(out[0, 0, :2]).all()
+
+
+# ------------------------------------------------------------ fused gates
+
+
+def test_gate_maps_closed_forms(oracle_mod):
+    """alpha = exp(-softplus(a)) is the logistic function of -a, beta = sigmoid(b):
+    alpha(a) + beta(a) = 1 (exp(-log(1 + e^a)) = 1 / (1 + e^a)), sigmoid(0) = 1/2,
+    and the tails: alpha -> 1 and beta -> e^b for b -> -inf, alpha -> e^-a for a -> +inf.
+    A sign slip (softplus(-a), exp(+b)) or a dropped exp fails these."""
+    x = np.array([-60.0, -30.0, -5.0, -1.0, -0.25, 0.0, 0.25, 1.0, 5.0, 30.0, 60.0])
+    al, be = oracle_mod.gates(x, x)
+    np.testing.assert_allclose(al + be, 1.0, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(al, 1.0 / (1.0 + np.exp(x)), rtol=1e-14, atol=0)
+    assert be[x == 0.0][0] == 0.5 and al[x == 0.0][0] == 0.5
+    np.testing.assert_allclose(be[:2], np.exp(x[:2]), rtol=1e-12)        # beta -> e^b
+    np.testing.assert_allclose(al[-2:], np.exp(-x[-2:]), rtol=1e-12)     # alpha -> e^-a
+    assert al[0] == 1.0 and be[-1] == 1.0
+    # monotone: alpha decreasing, beta increasing
+    assert np.all(np.diff(al) < 0) and np.all(np.diff(be) > 0)
+
+
+def test_gate_logits_equal_gate_values(oracle_mod):
+    """The recurrence from logits equals the recurrence from gate values formed
+    by the logistic closed form alpha = 1 / (1 + e^a), beta = 1 / (1 + e^-b)."""
+    rng = np.random.default_rng(41)
+    q, k, v, _, _, s = rand_case(rng, B=2, H=2, T=40, dk=8, dv=7)
+    za = rng.standard_normal(q.shape[:3]) * 2 - 1
+    zb = rng.standard_normal(q.shape[:3])
+    o1, s1 = oracle_mod.gdn_fwd(q, k, v, za, zb, s, gate_logits=True)
+    o2, s2 = oracle_mod.gdn_fwd(q, k, v, 1.0 / (1.0 + np.exp(za)), 1.0 / (1.0 + np.exp(-zb)), s)
+    np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(s1, s2, rtol=0, atol=1e-12)
+
+
+def test_output_gate_is_elementwise(oracle_mod):
+    """g = 1 leaves the outputs unchanged, g = 0 zeroes them, and a general g
+    scales each output element by itself; the state is not gated."""
+    rng = np.random.default_rng(43)
+    q, k, v, a, b, s = rand_case(rng, T=25, dk=6, dv=5)
+    o0, s0 = oracle_mod.gdn_fwd(q, k, v, a, b, s)
+    o1, s1 = oracle_mod.gdn_fwd(q, k, v, a, b, s, out_gate=np.ones_like(o0))
+    oz, _ = oracle_mod.gdn_fwd(q, k, v, a, b, s, out_gate=np.zeros_like(o0))
+    g = rng.uniform(0.0, 1.0, o0.shape)
+    og, sg = oracle_mod.gdn_fwd(q, k, v, a, b, s, out_gate=g)
+    assert np.array_equal(o1, o0) and np.array_equal(s1, s0)
+    assert np.all(oz == 0.0)
+    # element (t, j) of the gated output, written out from the definition
+    for t in (0, 7, 24):
+        for j in range(o0.shape[-1]):
+            assert og[0, 0, t, j] == o0[0, 0, t, j] * g[0, 0, t, j]
+    assert np.array_equal(sg, s0)
