@@ -47,12 +47,14 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(wl, out_bytes=4, state_in=True) -> int:
+def algorithmic_bytes(wl, out_bytes=4, state_in=True, out_gate=False) -> int:
     """Bytes one call must move at minimum: q, k, v, alpha, beta read once,
-    o written once, fp32 state read (if given) and written once."""
+    o written once, fp32 state read (if given) and written once; with an
+    output gate, the gate read once."""
     s_in = 2 if wl.dtype == "bf16" else 4
     tokheads = wl.B * wl.H * wl.T
-    b = tokheads * (2 * wl.dk * s_in + wl.dv * s_in + 2 * s_in + wl.dv * out_bytes)
+    b = tokheads * (2 * wl.dk * s_in + wl.dv * s_in + 2 * s_in + wl.dv * out_bytes
+                    + (wl.dv * s_in if out_gate else 0))
     st = wl.B * wl.H * wl.dk * wl.dv * 4
     return b + st + (st if state_in else 0)
 
@@ -76,23 +78,26 @@ def read_traffic(kernel_hash: str, workload: str):
     return float(m_val.group(1))
 
 
-def cpu_baseline(wl, budget_s: float):
+def cpu_baseline(wl, budget_s: float, gates: bool = False):
     """The fp64 oracle, as it stands, timed on the host cores on distinct
-    input sets of the same workload until about `budget_s` seconds pass."""
+    input sets of the same workload (same gate mode) until about `budget_s`
+    seconds pass."""
     import oracle
     from linear_attention_recurrence_deltanet_amd.inputs import make_call, to_numpy64
     oracle.build(force=False)
     nthreads = os.cpu_count() or 1
-    sets = [make_call(wl, i) for i in range(2)]
+    sets = [make_call(wl, i, gates=gates) for i in range(2)]
+    names = ("q", "k", "v") + (("alpha_logit", "beta_logit") if gates else ("alpha", "beta"))
     npsets = []
     for d in sets:
-        npsets.append([to_numpy64(d[n]) for n in ("q", "k", "v", "alpha", "beta")] +
-                      [None if d["state_in"] is None else to_numpy64(d["state_in"])])
+        npsets.append([to_numpy64(d[n]) for n in names] +
+                      [None if d["state_in"] is None else to_numpy64(d["state_in"]),
+                       to_numpy64(d["out_gate"]) if gates else None])
     calls = 0
     t0 = time.perf_counter()
     while True:
-        q, k, v, a, b, s = npsets[calls % len(npsets)]
-        oracle.gdn_fwd(q, k, v, a, b, s, nthreads=nthreads)
+        q, k, v, a, b, s, og = npsets[calls % len(npsets)]
+        oracle.gdn_fwd(q, k, v, a, b, s, nthreads=nthreads, gate_logits=gates, out_gate=og)
         calls += 1
         el = time.perf_counter() - t0
         if el >= budget_s:
@@ -123,6 +128,8 @@ def main():
     ap.add_argument("--out-dtype", default="f32", choices=["f32", "bf16"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--gates", action="store_true",
+                    help="alpha, beta as logits mapped in the kernel, and an output gate")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also launch a plain 256 MiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -147,14 +154,15 @@ def main():
     out_dt = torch.float32 if args.out_dtype == "f32" else torch.bfloat16
     out_bytes = 4 if args.out_dtype == "f32" else 2
     state_given = True
-    alg_bytes = algorithmic_bytes(wl, out_bytes, state_given)
+    alg_bytes = algorithmic_bytes(wl, out_bytes, state_given, args.gates)
 
     # distinct resident input sets so the rotation exceeds 2x the LLC
-    per_set = wl.B * wl.H * wl.T * (2 * wl.dk + wl.dv + 2) * (2 if wl.dtype == "bf16" else 4)
+    per_set = (wl.B * wl.H * wl.T * (2 * wl.dk + wl.dv + 2 + (wl.dv if args.gates else 0))
+               * (2 if wl.dtype == "bf16" else 4))
     nsets = max(2, min(64, (2 * LLC_BYTES) // max(per_set, 1) + 1))
     sets = []
     for i in range(nsets):
-        d = make_call(wl, i)
+        d = make_call(wl, i, gates=args.gates)
         g = {k: (None if v is None else v.to(dev).contiguous()) for k, v in d.items()}
         sets.append(g)
     st_shape = (wl.B, wl.H, wl.dk, wl.dv)
@@ -165,17 +173,20 @@ def main():
     ws_bytes = gdn.workspace_bytes(wl.B, wl.H, wl.T, wl.dk, wl.dv, args.chunk,
                                    gdn.make_opts(sets[0]["q"].dtype, out_dt))
     workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
-    opts = gdn.make_opts(sets[0]["q"].dtype, out_dt, True, 1.0, 1e-6, stream, workspace)
     P = lambda t: ctypes.c_void_p(t.data_ptr())
+    a_key, b_key = ("alpha_logit", "beta_logit") if args.gates else ("alpha", "beta")
     calls = []
     for i, g in enumerate(sets):
-        a = (P(g["q"]), P(g["k"]), P(g["v"]), P(g["alpha"]), P(g["beta"]), P(state),
+        # per input set: its output gate, when gated
+        o = gdn.make_opts(g["q"].dtype, out_dt, True, 1.0, 1e-6, stream, workspace,
+                          gate_logits=args.gates, out_gate=g["out_gate"] if args.gates else None)
+        a = (P(g["q"]), P(g["k"]), P(g["v"]), P(g[a_key]), P(g[b_key]), P(state),
              P(outs[i % 2]), P(state), wl.B, wl.H, wl.T, wl.dk, wl.dv)
-        calls.append(a)
+        calls.append((a, ctypes.pointer(o)))
     if args.chunk:
-        fn = lambda a: lib.gdn_fwd_chunked(*a, wl.chunk, ctypes.byref(opts))
+        fn = lambda c: lib.gdn_fwd_chunked(*c[0], wl.chunk, c[1])
     else:
-        fn = lambda a: lib.gdn_fwd_step(*a, ctypes.byref(opts))
+        fn = lambda c: lib.gdn_fwd_step(*c[0], c[1])
 
     for i in range(args.warmup):
         st = fn(calls[i % nsets])
@@ -238,7 +249,8 @@ def main():
         "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "T": wl.T, "dk": wl.dk,
                    "dv": wl.dv, "chunk": wl.chunk, "entry": "gdn_fwd_chunked" if args.chunk
                    else "gdn_fwd_step", "out_dtype": args.out_dtype, "state": "fp32 carried",
-                   "input_sets": nsets, "workspace_bytes": ws_bytes},
+                   "input_sets": nsets, "workspace_bytes": ws_bytes,
+                   "gates": "logits in, output gate" if args.gates else "values in, no output gate"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": read_traffic(khash, wl.name)},
@@ -249,7 +261,7 @@ def main():
                    "source_hash": khash},
     }
     if not args.no_cpu:
-        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, args.gates)
     print(json.dumps(res), flush=True)
 
 

@@ -211,15 +211,9 @@ __device__ __forceinline__ float gate_beta(float x, bool logits) {
     return logits ? 1.f / (1.f + exp2f(-x * kLog2e)) : x;
 }
 
-// Output gate (elementwise on out, input dtype): element e of a head's slice,
-// and four consecutive bf16 values (8 bytes) as fp32.
+// Output gate (elementwise on out, input dtype): element e of a head's slice.
 __device__ __forceinline__ float gate_at(rsrc_t r, unsigned e, bool f32) {
     return f32 ? __builtin_bit_cast(float, buf_load4(r, e * 4u)) : bf16_to_f32(buf_load2(r, e * 2u));
-}
-__device__ __forceinline__ f32x4 gate4_bf16(rsrc_t r, unsigned e) {
-    const uint2 w = buf_load8(r, e * 2u);
-    return f32x4{__builtin_bit_cast(float, w.x << 16), __builtin_bit_cast(float, w.x & 0xffff0000u),
-                 __builtin_bit_cast(float, w.y << 16), __builtin_bit_cast(float, w.y & 0xffff0000u)};
 }
 
 // ---------------------------------------------------------------------------

@@ -361,6 +361,9 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
     f32x4 QM[CT][NB];
     F KMf[CT][KS_C];                                  // K^ M of the next chunk as B operand (fp16)
     F vB[CT][KS_C];                                   // V of the next chunk as B operand
+    // output gate of the next chunk's rows (this lane's row and 4 columns per
+    // row block), loaded a step ahead of its use
+    uint2 GV[GATES && !SEG ? CT : 1][GATES && !SEG ? NB : 1];
     auto col0 = [&](int ct) { return 16 * (ct * NCW + wave); };
     auto ident = [&](int ct) { return SEG && col0(ct) < vlo; };
 
@@ -511,10 +514,14 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
                                 // rows past T fall outside the buffer and are dropped
                                 const unsigned e0 = (unsigned)(t0 + 16 * rb + lc) * (unsigned)dv +
                                                     (unsigned)(vbase + col0(ct) + 4 * lg);
-                                if (gated) {
-                                    const f32x4 gv = gate4_bf16(rg_, e0);
-#pragma unroll
-                                    for (int i = 0; i < 4; ++i) o[i] *= gv[i];
+                                if constexpr (GATES && !SEG) {
+                                    if (gated) {
+                                        const uint2 w = GV[ct][rb];
+                                        o[0] *= __builtin_bit_cast(float, w.x << 16);
+                                        o[1] *= __builtin_bit_cast(float, w.x & 0xffff0000u);
+                                        o[2] *= __builtin_bit_cast(float, w.y << 16);
+                                        o[3] *= __builtin_bit_cast(float, w.y & 0xffff0000u);
+                                    }
                                 }
                                 if (p.out_bf16) {
                                     const uint2 w = make_uint2(
@@ -619,6 +626,17 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
 #pragma unroll
                 for (int u = 0; u < (NTS + NCW - 1) / NCW; ++u)
                     if (wave + NCW * u < NTS) p_tile<L>(Kh, Qh, Pm, v_g2, wave + NCW * u, lane);
+            }
+            if constexpr (GATES && !SEG) {
+                // output gate of chunk pc, used when it is finished next step
+                if (gated) {
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                        for (int rb = 0; rb < NB; ++rb)
+                            GV[ct][rb] = buf_load8(rg_, ((unsigned)(pc * C + 16 * rb + lc) * (unsigned)dv +
+                                                         (unsigned)(vbase + col0(ct) + 4 * lg)) * 2u);
+                }
             }
             __syncthreads();
         }
@@ -935,6 +953,7 @@ __global__ __launch_bounds__(1024) void gdn_pipe_fix_kernel(WalkArgs p) {
     const bool gated = p.out_gate != nullptr;
     const rsrc_t rG = make_rsrc(gated ? (const char*)p.out_gate + (size_t)bh * T * dv * 2 : nullptr,
                                 gated ? (unsigned)T * dv * 2u : 0u);
+    const int col4 = vt * 64 + 16 * cg + 4 * lg;        // first of this lane's four output columns
 
     // Loads and stores below are unconditional (kOffNone where there is
     // nothing to move) so that the compiler counts the loads in flight
@@ -955,17 +974,19 @@ __global__ __launch_bounds__(1024) void gdn_pipe_fix_kernel(WalkArgs p) {
     // ---- correction operands of a group of CPG chunks (RG row blocks): one
     // 16-byte piece of Phi per thread, staged in LDS; the wave's own row block
     // of the partial outputs (fp16, 4 columns per lane)
-    auto cload = [&](uint4& h, uint2& o, int g) {
+    auto cload = [&](uint4& h, uint2& o, uint2& gt, int g) {
         const int c0 = ch0 + g * CPG;
         const int c = c0 + rg / NB, rb = rg % NB;
         h = buf_load16(rP, (c0 < ch1 && tid < PPG) ? (unsigned)((c0 - ch0) * C * DK * 2 + tid * 16) : kOffNone);
         o = buf_load8(rO, c < ch1 ? (unsigned)((((c - ch0) * NB + rb) * (dv / 16) + c16) * 64 + lane) * 8u
                                   : kOffNone);
+        // output gate of the same four elements (the range is empty without one)
+        gt = buf_load8(rG, c < ch1 ? (unsigned)((c * C + 16 * rb + lc) * dv + col4) * 2u : kOffNone);
     };
     uint4 ph[2];
-    uint2 ov[2];
-    cload(ph[0], ov[0], 0);
-    cload(ph[1], ov[1], 1);
+    uint2 ov[2], gv2[2];
+    cload(ph[0], ov[0], gv2[0], 0);
+    cload(ph[1], ov[1], gv2[1], 1);
 
     // ---- fold: maps 0 .. seg-1, D in flight; the last segment's own map
     // (state_out) is loaded from the start
@@ -1055,8 +1076,7 @@ __global__ __launch_bounds__(1024) void gdn_pipe_fix_kernel(WalkArgs p) {
     // ---- outputs of the segment: O += Phi M_in, formed transposed
     // (O^T = M^T Phi^T): lane (lg, lc) holds row lc of the wave's row block
     // and four consecutive columns, one 16-byte access
-    const int col4 = vt * 64 + 16 * cg + 4 * lg;
-    auto cfix = [&](const uint4& h, const uint2& o, int g, int buf) {
+    auto cfix = [&](const uint4& h, const uint2& o, const uint2& gt, int g, int buf) {
         const int c = ch0 + g * CPG + rg / NB, rb = rg % NB;
         if (tid < PPG) Phs[buf][tid] = h;
         __syncthreads();                  // copy buf reused two groups later, after another barrier
@@ -1069,9 +1089,10 @@ __global__ __launch_bounds__(1024) void gdn_pipe_fix_kernel(WalkArgs p) {
         // rows past T fall outside the buffer and are dropped
         const unsigned e0 = (unsigned)((c * C + 16 * rb + lc) * dv + col4);
         if (gated) {
-            const f32x4 gv = gate4_bf16(rG, e0);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] *= gv[i];
+            acc[0] *= __builtin_bit_cast(float, gt.x << 16);
+            acc[1] *= __builtin_bit_cast(float, gt.x & 0xffff0000u);
+            acc[2] *= __builtin_bit_cast(float, gt.y << 16);
+            acc[3] *= __builtin_bit_cast(float, gt.y & 0xffff0000u);
         }
         if (p.out_bf16) {
             const uint2 w = make_uint2(
@@ -1086,10 +1107,10 @@ __global__ __launch_bounds__(1024) void gdn_pipe_fix_kernel(WalkArgs p) {
     };
     const int ngroups = (ch1 - ch0 + CPG - 1) / CPG;
     for (int g = 0; g < ngroups; g += 2) {
-        cfix(ph[0], ov[0], g, 0);
-        cload(ph[0], ov[0], g + 2);
-        cfix(ph[1], ov[1], g + 1, 1);
-        cload(ph[1], ov[1], g + 3);
+        cfix(ph[0], ov[0], gv2[0], g, 0);
+        cload(ph[0], ov[0], gv2[0], g + 2);
+        cfix(ph[1], ov[1], gv2[1], g + 1, 1);
+        cload(ph[1], ov[1], gv2[1], g + 3);
     }
 }
 
