@@ -451,9 +451,23 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
         for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
             for (int ks = 0; ks < KS_D; ++ks) mB[ct][ks] = Op::b_acc(Macc[ct], ks);
+        if constexpr (GATES && !SEG) {
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                for (int rb = 0; rb < NB; ++rb) GV[ct][rb] = make_uint2(0u, 0u);
+        }
         for (int s = 0; s <= nch; ++s) {
             const int pc = ch0 + s;
             const int vb = s & 1;
+            if constexpr (GATES && !SEG) {
+                // the gate loaded last step arrives here on every path, so no
+                // later reuse of its registers waits for the output stores
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                    for (int rb = 0; rb < NB; ++rb) asm volatile("" ::"v"(GV[ct][rb].x), "v"(GV[ct][rb].y));
+            }
             // ---- phase 1: finish chunk pc - 1
             if (s > 0) {
                 // finish chunk pc - 1 with the products prepared last step
@@ -515,13 +529,15 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
                                 const unsigned e0 = (unsigned)(t0 + 16 * rb + lc) * (unsigned)dv +
                                                     (unsigned)(vbase + col0(ct) + 4 * lg);
                                 if constexpr (GATES && !SEG) {
-                                    if (gated) {
-                                        const uint2 w = GV[ct][rb];
-                                        o[0] *= __builtin_bit_cast(float, w.x << 16);
-                                        o[1] *= __builtin_bit_cast(float, w.x & 0xffff0000u);
-                                        o[2] *= __builtin_bit_cast(float, w.y << 16);
-                                        o[3] *= __builtin_bit_cast(float, w.y & 0xffff0000u);
-                                    }
+                                    // consumed on every path (1 without a gate): a use under a
+                                    // branch leaves the load pending on the other path, and the
+                                    // next write of these registers then waits for every
+                                    // outstanding store
+                                    const uint2 w = GV[ct][rb];
+                                    o[0] *= gated ? __builtin_bit_cast(float, w.x << 16) : 1.f;
+                                    o[1] *= gated ? __builtin_bit_cast(float, w.x & 0xffff0000u) : 1.f;
+                                    o[2] *= gated ? __builtin_bit_cast(float, w.y << 16) : 1.f;
+                                    o[3] *= gated ? __builtin_bit_cast(float, w.y & 0xffff0000u) : 1.f;
                                 }
                                 if (p.out_bf16) {
                                     const uint2 w = make_uint2(
@@ -628,15 +644,16 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
                     if (wave + NCW * u < NTS) p_tile<L>(Kh, Qh, Pm, v_g2, wave + NCW * u, lane);
             }
             if constexpr (GATES && !SEG) {
-                // output gate of chunk pc, used when it is finished next step
-                if (gated) {
+                // output gate of chunk pc, used when it is finished next step.
+                // Issued whether or not a gate is given (the resource is empty
+                // then), so that the wait before its use counts exactly and
+                // does not drain the output stores issued in between
 #pragma unroll
-                    for (int ct = 0; ct < CT; ++ct)
+                for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-                        for (int rb = 0; rb < NB; ++rb)
-                            GV[ct][rb] = buf_load8(rg_, ((unsigned)(pc * C + 16 * rb + lc) * (unsigned)dv +
-                                                         (unsigned)(vbase + col0(ct) + 4 * lg)) * 2u);
-                }
+                    for (int rb = 0; rb < NB; ++rb)
+                        GV[ct][rb] = buf_load8(rg_, ((unsigned)(pc * C + 16 * rb + lc) * (unsigned)dv +
+                                                     (unsigned)(vbase + col0(ct) + 4 * lg)) * 2u);
             }
             __syncthreads();
         }
