@@ -78,7 +78,7 @@ def read_traffic(kernel_hash: str, workload: str):
     return float(m_val.group(1))
 
 
-def cpu_baseline(wl, budget_s: float, gates: bool = False):
+def cpu_baseline(wl, budget_s: float, gates: bool = False, bidir: bool = False):
     """The fp64 oracle, as it stands, timed on the host cores on distinct
     input sets of the same workload (same gate mode) until about `budget_s`
     seconds pass."""
@@ -97,7 +97,8 @@ def cpu_baseline(wl, budget_s: float, gates: bool = False):
     t0 = time.perf_counter()
     while True:
         q, k, v, a, b, s, og = npsets[calls % len(npsets)]
-        oracle.gdn_fwd(q, k, v, a, b, s, nthreads=nthreads, gate_logits=gates, out_gate=og)
+        scan = oracle.gdn_bidir if bidir else oracle.gdn_fwd
+        scan(q, k, v, a, b, s, nthreads=nthreads, gate_logits=gates, out_gate=og)
         calls += 1
         el = time.perf_counter() - t0
         if el >= budget_s:
@@ -114,7 +115,8 @@ def cpu_baseline(wl, budget_s: float, gates: bool = False):
         pass
     return {"value": tokens / el, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
             "sample": f"{calls} full calls of the same workload (B={wl.B} H={wl.H} T={wl.T} "
-                      f"dk={wl.dk} dv={wl.dv}) in {el:.1f} s, fp64 token-by-token, "
+                      f"dk={wl.dk} dv={wl.dv}{', gates' if gates else ''}"
+                      f"{', bidirectional' if bidir else ''}) in {el:.1f} s, fp64 token-by-token, "
                       f"OpenMP over (b, h, 16-column block), CPU: {cpu_model}"}
 
 
@@ -130,6 +132,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--gates", action="store_true",
                     help="alpha, beta as logits mapped in the kernel, and an output gate")
+    ap.add_argument("--bidir", action="store_true",
+                    help="gdn_fwd_bidir: forward scan plus backward scan within the call")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also launch a plain 256 MiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -170,8 +174,12 @@ def main():
     state = state0.clone()
     outs = [torch.empty(wl.B, wl.H, wl.T, wl.dv, dtype=out_dt, device=dev) for _ in range(2)]
     stream = torch.cuda.current_stream()
-    ws_bytes = gdn.workspace_bytes(wl.B, wl.H, wl.T, wl.dk, wl.dv, args.chunk,
-                                   gdn.make_opts(sets[0]["q"].dtype, out_dt))
+    ws_opts = gdn.make_opts(sets[0]["q"].dtype, out_dt)
+    if args.bidir:
+        ws_bytes = int(lib.gdn_bidir_workspace_bytes(wl.B, wl.H, wl.T, wl.dk, wl.dv, args.chunk,
+                                                     ctypes.byref(ws_opts)))
+    else:
+        ws_bytes = gdn.workspace_bytes(wl.B, wl.H, wl.T, wl.dk, wl.dv, args.chunk, ws_opts)
     workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     P = lambda t: ctypes.c_void_p(t.data_ptr())
     a_key, b_key = ("alpha_logit", "beta_logit") if args.gates else ("alpha", "beta")
@@ -183,7 +191,9 @@ def main():
         a = (P(g["q"]), P(g["k"]), P(g["v"]), P(g[a_key]), P(g[b_key]), P(state),
              P(outs[i % 2]), P(state), wl.B, wl.H, wl.T, wl.dk, wl.dv)
         calls.append((a, ctypes.pointer(o)))
-    if args.chunk:
+    if args.bidir:
+        fn = lambda c: lib.gdn_fwd_bidir(*c[0], args.chunk, c[1])
+    elif args.chunk:
         fn = lambda c: lib.gdn_fwd_chunked(*c[0], wl.chunk, c[1])
     else:
         fn = lambda c: lib.gdn_fwd_step(*c[0], c[1])
@@ -247,13 +257,14 @@ def main():
         "dtype": wl.dtype,
         "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "T": wl.T, "dk": wl.dk,
-                   "dv": wl.dv, "chunk": wl.chunk, "entry": "gdn_fwd_chunked" if args.chunk
-                   else "gdn_fwd_step", "out_dtype": args.out_dtype, "state": "fp32 carried",
+                   "dv": wl.dv, "chunk": wl.chunk, "entry": "gdn_fwd_bidir" if args.bidir
+                   else "gdn_fwd_chunked" if args.chunk else "gdn_fwd_step", "out_dtype": args.out_dtype, "state": "fp32 carried",
                    "input_sets": nsets, "workspace_bytes": ws_bytes,
-                   "gates": "logits in, output gate" if args.gates else "values in, no output gate"},
+                   "gates": "logits in, output gate" if args.gates else "values in, no output gate",
+                   "scan": "bidirectional" if args.bidir else "forward"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": read_traffic(khash, wl.name)},
+                     "traffic": None if (args.gates or args.bidir) else read_traffic(khash, wl.name)},
         "kernel": {"avg_ms": kern_ms, "p50_ms": p50, "p99_ms": p99,
                    "algorithmic_bytes": alg_bytes, "algorithmic_flops": algorithmic_flops(wl),
                    "mfma_frac_of_bf16_peak": algorithmic_flops(wl) / (kern_ms * 1e-3) / 1e12
@@ -261,7 +272,7 @@ def main():
                    "source_hash": khash},
     }
     if not args.no_cpu:
-        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, args.gates)
+        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, args.gates, args.bidir)
     print(json.dumps(res), flush=True)
 
 

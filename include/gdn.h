@@ -33,6 +33,7 @@
  *    sequence across workgroups need a caller-owned workspace of
  *    gdn_workspace_bytes() bytes (opts->workspace); without one the
  *    single-pass path runs instead (same results to rounding).
+ *    gdn_fwd_bidir needs the workspace of gdn_bidir_workspace_bytes().
  *  - Aliasing: only state_in and state_out may alias (in-place state update).
  *    Other buffers must not overlap.
  *  - Errors: argument errors return synchronously before any HIP call
@@ -51,7 +52,7 @@
 extern "C" {
 #endif
 
-#define GDN_VERSION 1
+#define GDN_VERSION 2
 
 typedef enum {
     GDN_OK = 0,
@@ -110,6 +111,44 @@ int gdn_fwd_step(const void* q, const void* k, const void* v,
                  const float* state_in, void* out, float* state_out,
                  int B, int H, int T, int dk, int dv,
                  const gdn_opts* opts);
+
+/*
+ * gdn_fwd_bidir: bidirectional Gated DeltaNet over one streaming chunk
+ * (SANA-Streaming, section 4.1: the streaming model runs a forward scan from
+ * the previous cache and a backward scan within the chunk; section 2.3
+ * "Efficient GDN Kernel": the forward and reverse histories are combined for
+ * the output).  With S^f the forward recurrence from state_in and S^b the
+ * same recurrence run over the tokens in reverse order from a zero state,
+ * each token keeping its own alpha_t, beta_t:
+ *
+ *   S^b_t = alpha_t * S^b_{t+1} * (I - beta_t * k_t k_t^T) + beta_t * v_t k_t^T,
+ *   S^b_T = 0,     o_t = S^f_t q_t + S^b_t q_t
+ *
+ * (both scans include token t itself).  state_out receives the final forward
+ * state S^f_{T-1}; the backward state is not kept.  Same arguments, layouts
+ * and conventions as gdn_fwd_chunked; chunk 0 picks the gdn_fwd_step tile.
+ * The backward scan writes its outputs, in fp32, to a plane at the start of
+ * the workspace; the forward scan adds them to its own before their one
+ * rounding to out_dtype.  The call therefore needs a workspace (16-byte
+ * aligned) of at least that plane, B*H*T*dv*4 bytes rounded up to 256, and
+ * returns GDN_ERR_ARG without one; gdn_bidir_workspace_bytes() adds the
+ * split-sequence data (without them both scans run unsplit).  out must not
+ * alias any input.  The output gate, if given, multiplies the sum.
+ */
+int gdn_fwd_bidir(const void* q, const void* k, const void* v,
+                  const void* alpha, const void* beta,
+                  const float* state_in, void* out, float* state_out,
+                  int B, int H, int T, int dk, int dv, int chunk,
+                  const gdn_opts* opts);
+
+/*
+ * Workspace size (bytes) for gdn_fwd_bidir with this shape and chunk (0: the
+ * gdn_fwd_step tile): the fp32 plane of B*H*T*dv values rounded up to 256
+ * bytes, then the split-sequence data of gdn_workspace_bytes().  Returns 0
+ * for T == 0 and for invalid shapes.
+ */
+size_t gdn_bidir_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk,
+                                 const gdn_opts* opts);
 
 /*
  * Workspace size (bytes) that lets gdn_fwd_chunked (chunk > 0) or

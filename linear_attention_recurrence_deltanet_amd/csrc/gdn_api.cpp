@@ -175,14 +175,13 @@ Plan make_plan(int in_f32, int B, int H, int T, int dk, int dv, int chunk) {
     return pl;
 }
 
-int run(const void* q, const void* k, const void* v, const void* alpha, const void* beta,
-        const float* state_in, void* out, float* state_out,
-        int B, int H, int T, int dk, int dv, int chunk, const gdn_opts* opts) {
-    g_last_error[0] = '\0';
-    gdn_opts o;
-    if (opts) o = *opts; else defaults(&o);
-    int st = validate(q, k, v, alpha, beta, state_in, out, state_out, B, H, T, dk, dv, chunk, o);
-    if (st != GDN_OK) return st;
+// One scan over the sequence.  reverse: walk the tokens backward; accumulate:
+// add the outputs to out (fp32 out), or add acc_src before rounding (bf16
+// out).  Arguments are validated by the caller.
+int scan(const void* q, const void* k, const void* v, const void* alpha, const void* beta,
+         const float* state_in, void* out, float* state_out,
+         int B, int H, int T, int dk, int dv, int chunk, const gdn_opts& o, int reverse, int accumulate,
+         const float* acc_src = nullptr) {
     gdn::WalkArgs a;
     a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta;
     a.state_in = state_in; a.out = out; a.state_out = state_out;
@@ -191,6 +190,9 @@ int run(const void* q, const void* k, const void* v, const void* alpha, const vo
     a.out_bf16 = o.out_dtype == GDN_BF16; a.in_f32 = o.in_dtype == GDN_F32;
     a.gate_logits = o.gate_logits ? 1 : 0;
     a.out_gate = o.out_gate;
+    a.reverse = reverse;
+    a.accumulate = accumulate;
+    a.acc_src = acc_src;
     if (T == 0 && !state_out) return GDN_OK;
     Plan pl = make_plan(a.in_f32, B, H, T, dk, dv, chunk);
     hipStream_t stream = reinterpret_cast<hipStream_t>(o.stream);
@@ -230,6 +232,57 @@ int run(const void* q, const void* k, const void* v, const void* alpha, const vo
     return GDN_OK;
 }
 
+int run(const void* q, const void* k, const void* v, const void* alpha, const void* beta,
+        const float* state_in, void* out, float* state_out,
+        int B, int H, int T, int dk, int dv, int chunk, const gdn_opts* opts) {
+    g_last_error[0] = '\0';
+    gdn_opts o;
+    if (opts) o = *opts; else defaults(&o);
+    int st = validate(q, k, v, alpha, beta, state_in, out, state_out, B, H, T, dk, dv, chunk, o);
+    if (st != GDN_OK) return st;
+    return scan(q, k, v, alpha, beta, state_in, out, state_out, B, H, T, dk, dv, chunk, o, 0, 0);
+}
+
+// The fp32 plane of a bidirectional call (the backward scan's outputs) at the
+// start of its workspace, 256-byte aligned; the segment data follow it.
+size_t plane_bytes(int B, int H, int T, int dv) {
+    return ((size_t)B * H * T * dv * 4 + 255) & ~(size_t)255;
+}
+size_t bidir_workspace(int B, int H, int T, int dk, int dv, int chunk, const gdn_opts& o);
+
+// Bidirectional: the backward scan (zero state, tokens in reverse, no state
+// kept) writes its fp32 outputs to the plane, then the forward scan from
+// state_in adds the plane to its own outputs before their one rounding and
+// writes state_out.  The output gate is applied in both (it distributes over
+// the sum).  Stream order keeps the two scans apart, so they share the
+// segment data; a workspace of the plane alone runs both scans unsplit.
+int run_bidir(const void* q, const void* k, const void* v, const void* alpha, const void* beta,
+              const float* state_in, void* out, float* state_out,
+              int B, int H, int T, int dk, int dv, int chunk, const gdn_opts* opts) {
+    g_last_error[0] = '\0';
+    gdn_opts o;
+    if (opts) o = *opts; else defaults(&o);
+    int st = validate(q, k, v, alpha, beta, state_in, out, state_out, B, H, T, dk, dv, chunk, o);
+    if (st != GDN_OK) return st;
+    if (T == 0) return scan(q, k, v, alpha, beta, state_in, out, state_out, B, H, T, dk, dv, chunk, o, 0, 0);
+    const size_t pb = plane_bytes(B, H, T, dv);
+    if (!o.workspace || o.workspace_bytes < pb || !aligned16(o.workspace)) {
+        char n[32];
+        snprintf(n, sizeof(n), "%zu", bidir_workspace(B, H, T, dk, dv, chunk, o));
+        return fail(GDN_ERR_ARG, "gdn_fwd_bidir needs a 16-byte aligned workspace of at least the "
+                    "fp32 plane (gdn_bidir_workspace_bytes() = %s bytes with the segment data)", n);
+    }
+    float* plane = reinterpret_cast<float*>(o.workspace);
+    gdn_opts os = o;                               // segment data after the plane
+    os.workspace = reinterpret_cast<char*>(o.workspace) + pb;
+    os.workspace_bytes = o.workspace_bytes - pb;
+    gdn_opts ob = os;
+    ob.out_dtype = GDN_F32;
+    st = scan(q, k, v, alpha, beta, nullptr, plane, nullptr, B, H, T, dk, dv, chunk, ob, 1, 0);
+    if (st != GDN_OK) return st;
+    return scan(q, k, v, alpha, beta, state_in, out, state_out, B, H, T, dk, dv, chunk, os, 0, 1, plane);
+}
+
 size_t workspace_for(int B, int H, int T, int dk, int dv, int chunk, const gdn_opts* opts) {
     gdn_opts o;
     if (opts) o = *opts; else defaults(&o);
@@ -237,6 +290,13 @@ size_t workspace_for(int B, int H, int T, int dk, int dv, int chunk, const gdn_o
     if (chunk != 32 && chunk != 64 && chunk != 128) return 0;
     Plan pl = make_plan(o.in_dtype == GDN_F32, B, H, T, dk, dv, chunk);
     return pl.ws_bytes;
+}
+
+size_t bidir_workspace(int B, int H, int T, int dk, int dv, int chunk, const gdn_opts& o) {
+    if (B <= 0 || H <= 0 || T < 0 || !head_ok(dk) || !head_ok(dv)) return 0;
+    if (chunk != 32 && chunk != 64 && chunk != 128) return 0;
+    const Plan pl = make_plan(o.in_dtype == GDN_F32, B, H, T, dk, dv, chunk);
+    return T == 0 ? 0 : plane_bytes(B, H, T, dv) + pl.ws_bytes;
 }
 
 }  // namespace
@@ -257,6 +317,19 @@ int gdn_fwd_step(const void* q, const void* k, const void* v, const void* alpha,
                  const float* state_in, void* out, float* state_out,
                  int B, int H, int T, int dk, int dv, const gdn_opts* opts) {
     return run(q, k, v, alpha, beta, state_in, out, state_out, B, H, T, dk, dv, STEP_CHUNK, opts);
+}
+
+int gdn_fwd_bidir(const void* q, const void* k, const void* v, const void* alpha, const void* beta,
+                  const float* state_in, void* out, float* state_out,
+                  int B, int H, int T, int dk, int dv, int chunk, const gdn_opts* opts) {
+    return run_bidir(q, k, v, alpha, beta, state_in, out, state_out, B, H, T, dk, dv,
+                     chunk > 0 ? chunk : STEP_CHUNK, opts);
+}
+
+size_t gdn_bidir_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, const gdn_opts* opts) {
+    gdn_opts o;
+    if (opts) o = *opts; else defaults(&o);
+    return bidir_workspace(B, H, T, dk, dv, chunk > 0 ? chunk : STEP_CHUNK, o);
 }
 
 size_t gdn_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, const gdn_opts* opts) {

@@ -187,6 +187,29 @@ __device__ __forceinline__ void buf_store16(rsrc_t r, unsigned off, uint4 v) {
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     __builtin_amdgcn_raw_buffer_store_b128(u32x4{v.x, v.y, v.z, v.w}, r, off, 0, 0);
 }
+// Accumulating outputs (the second scan of a bidirectional call) add fp32
+// values from a separate plane before their one rounding: four of them, as
+// loaded, to a lane's four outputs.
+template <class V4>
+__device__ __forceinline__ void add_f32x4(V4& o, uint4 w) {
+    o[0] += __builtin_bit_cast(float, w.x);
+    o[1] += __builtin_bit_cast(float, w.y);
+    o[2] += __builtin_bit_cast(float, w.z);
+    o[3] += __builtin_bit_cast(float, w.w);
+}
+
+// Walk position -> token row.  A backward scan walks the tokens in reverse:
+// position t < T is token T - 1 - t.  Positions at or past T (the padding of
+// a partial last chunk) stay rows at or past T in both directions, so their
+// offsets lie past the range as usual (loads read zero, stores are dropped)
+// and no offset is ever negative.
+struct TokMap {
+    int T;
+    bool rev;
+    __device__ __forceinline__ int operator()(int t) const { return (rev && t < T) ? T - 1 - t : t; }
+};
+__device__ __forceinline__ TokMap tok_map(int T, int reverse) { return TokMap{T, reverse != 0}; }
+
 // Offset past every range a resource here covers (ranges stay below 2 GiB):
 // a load from it returns zeros and a store to it is dropped, with no memory
 // traffic.  Used to keep loads and stores unconditional.

@@ -229,6 +229,10 @@ void gdn_walk_kernel(WalkArgs p) {
     const rsrc_t ro_ = make_rsrc(SUMMARY ? nullptr : (const char*)p.out + (size_t)bh * T * dv * osz,
                                  SUMMARY ? 0u : (unsigned)T * dv * osz);
     const bool gated = !SUMMARY && p.out_gate != nullptr;
+    const TokMap tm = tok_map(T, p.reverse);             // walk position -> token
+    const bool accum = !SUMMARY && p.accumulate;     // fp32 plane added before the store
+    const rsrc_t rac_ = make_rsrc(accum ? p.acc_src + (size_t)bh * T * dv : nullptr,
+                                  accum ? (unsigned)T * dv * 4u : 0u);
     const rsrc_t rg_ = make_rsrc(gated ? (const char*)p.out_gate + (size_t)bh * T * dv * SI : nullptr,
                                  gated ? (unsigned)T * dv * SI : 0u);
 
@@ -329,7 +333,7 @@ void gdn_walk_kernel(WalkArgs p) {
         for (int it = 0; it < QPT; ++it) {
             const int idx = tid + NT * it;
             const int r = idx / VPRQ, part = idx % VPRQ;
-            const unsigned off = (unsigned)((t0 + r) * DK + part * EPV) * SI;
+            const unsigned off = (unsigned)(tm(t0 + r) * DK + part * EPV) * SI;
             pk[it] = buf_load16(rk_, off);
             if constexpr (LOADQ) pq[it] = buf_load16(rq_, off);
         }
@@ -338,13 +342,13 @@ void gdn_walk_kernel(WalkArgs p) {
             for (int it = 0; it < VPT; ++it) {
                 const int idx = tid + NT * it;
                 const int r = idx / VPRV, part = idx % VPRV;
-                pv[it] = buf_load16(rv_, (unsigned)((t0 + r) * dv + vcol0 + part * EPV) * SI);
+                pv[it] = buf_load16(rv_, (unsigned)(tm(t0 + r) * dv + vcol0 + part * EPV) * SI);
             }
         }
         if (wave == 0) {
 #pragma unroll
             for (int e = 0; e < TPL; ++e) {
-                const unsigned off = (unsigned)(t0 + lane * TPL + e) * SI;
+                const unsigned off = (unsigned)tm(t0 + lane * TPL + e) * SI;
                 if constexpr (sizeof(In) == 2) {
                     pa[e] = buf_load2(ra_, off);
                     pb[e] = buf_load2(rb_, off);
@@ -640,18 +644,27 @@ void gdn_walk_kernel(WalkArgs p) {
 #pragma unroll
                 for (int ks = 0; ks < KS_C; ++ks) Oacc[rb] = Op::mma(fp[rb][ks], uB[ks], Oacc[rb]);
                 // rows past T fall outside the buffer and are dropped
-                const unsigned o0 = (unsigned)((t0 + 16 * rb + 4 * lg) * dv + vcol0 + mycol);
+                unsigned oe[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    oe[i] = (unsigned)(tm(t0 + 16 * rb + 4 * lg + i) * dv + vcol0 + mycol);
                 if (gated) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) Oacc[rb][i] *= gate_at(rg_, o0 + i * dv, SI == 4);
+                    for (int i = 0; i < 4; ++i) Oacc[rb][i] *= gate_at(rg_, oe[i], SI == 4);
+                }
+                if (accum) {
+                    // accumulating: the fp32 plane is added, the sum rounded once
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        Oacc[rb][i] += __builtin_bit_cast(float, buf_load4(rac_, oe[i] * 4u));
                 }
                 if (p.out_bf16) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        buf_store2(ro_, (o0 + i * dv) * 2u, __builtin_bit_cast(uint16_t, (__bf16)Oacc[rb][i]));
+                        buf_store2(ro_, oe[i] * 2u, __builtin_bit_cast(uint16_t, (__bf16)Oacc[rb][i]));
                 } else {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) buf_store4(ro_, (o0 + i * dv) * 4u, Oacc[rb][i]);
+                    for (int i = 0; i < 4; ++i) buf_store4(ro_, oe[i] * 4u, Oacc[rb][i]);
                 }
             }
         }

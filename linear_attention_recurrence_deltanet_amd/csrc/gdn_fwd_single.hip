@@ -157,6 +157,7 @@ void gdn_fwd_single_kernel(FwdArgs p) {
     const int bh = blockIdx.x / ntile;
     const int col0 = tile * BV;
     const int T = p.T, dv = p.dv;
+    const TokMap tm = tok_map(T, p.reverse);   // walk position -> token
 
     const In* qg = reinterpret_cast<const In*>(p.q) + (size_t)bh * T * DK;
     const In* kg = reinterpret_cast<const In*>(p.k) + (size_t)bh * T * DK;
@@ -199,8 +200,8 @@ void gdn_fwd_single_kernel(FwdArgs p) {
             const int r = it / VPRQ, part = it % VPRQ;
             uint4 rq4 = make_uint4(0, 0, 0, 0), rk4 = make_uint4(0, 0, 0, 0);
             if (r < n) {
-                rq4 = *reinterpret_cast<const uint4*>(qg + (size_t)(t0 + r) * DK + part * EPV);
-                rk4 = *reinterpret_cast<const uint4*>(kg + (size_t)(t0 + r) * DK + part * EPV);
+                rq4 = *reinterpret_cast<const uint4*>(qg + (size_t)tm(t0 + r) * DK + part * EPV);
+                rk4 = *reinterpret_cast<const uint4*>(kg + (size_t)tm(t0 + r) * DK + part * EPV);
             }
             const In* qe = reinterpret_cast<const In*>(&rq4);
             const In* ke = reinterpret_cast<const In*>(&rk4);
@@ -225,7 +226,7 @@ void gdn_fwd_single_kernel(FwdArgs p) {
             const int r = it / VPRV, part = it % VPRV;
             uint4 rv4 = make_uint4(0, 0, 0, 0);
             if (r < n)
-                rv4 = *reinterpret_cast<const uint4*>(vg + (size_t)(t0 + r) * dv + col0 + part * EPV);
+                rv4 = *reinterpret_cast<const uint4*>(vg + (size_t)tm(t0 + r) * dv + col0 + part * EPV);
             const In* ve = reinterpret_cast<const In*>(&rv4);
 #pragma unroll
             for (int e = 0; e < EPV; ++e)
@@ -241,8 +242,8 @@ void gdn_fwd_single_kernel(FwdArgs p) {
                 // padding rows: alpha = 1, beta = 0
                 float l2 = 0.f, b = 0.f;
                 if (r < n) {
-                    l2 = gate_log2_alpha(InTraits<In>::to_f32(ag[t0 + r]), p.gate_logits);
-                    b = gate_beta(InTraits<In>::to_f32(bg[t0 + r]), p.gate_logits);
+                    l2 = gate_log2_alpha(InTraits<In>::to_f32(ag[tm(t0 + r)]), p.gate_logits);
+                    b = gate_beta(InTraits<In>::to_f32(bg[tm(t0 + r)]), p.gate_logits);
                 }
                 run += l2;
                 la[e] = run;
@@ -515,19 +516,26 @@ void gdn_fwd_single_kernel(FwdArgs p) {
                 }
                 const int c = col0 + 16 * cb + (lane & 15);
                 const int r0 = 16 * rb + 4 * (lane >> 4);
+                float ov[4];
+                unsigned oe[4];                                   // element within the head
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int r = r0 + i;
-                    if (r < n) {
-                        const size_t o = ((size_t)bh * T + t0 + r) * dv + c;
-                        float ov = Oacc[sl][i];
-                        if (p.out_gate)
-                            ov *= InTraits<In>::to_f32(reinterpret_cast<const In*>(p.out_gate)[o]);
-                        if (p.out_bf16)
-                            reinterpret_cast<uint16_t*>(p.out)[o] = f32_to_bf16(ov);
-                        else
-                            reinterpret_cast<float*>(p.out)[o] = ov;
-                    }
+                    oe[i] = r < n ? (unsigned)(tm(t0 + r) * dv + c) : kOffNone;
+                    ov[i] = Oacc[sl][i];
+                    if (p.out_gate && r < n)
+                        ov[i] *= InTraits<In>::to_f32(reinterpret_cast<const In*>(p.out_gate)[(size_t)bh * T * dv + oe[i]]);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (r0 + i >= n) continue;
+                    const size_t o = (size_t)bh * T * dv + oe[i];
+                    // accumulating: the fp32 plane is added, the sum rounded once
+                    if (p.accumulate) ov[i] += p.acc_src[o];
+                    if (p.out_bf16)
+                        reinterpret_cast<uint16_t*>(p.out)[o] = f32_to_bf16(ov[i]);
+                    else
+                        reinterpret_cast<float*>(p.out)[o] = ov[i];
                 }
             }
         }

@@ -22,6 +22,9 @@ struct FwdArgs {
     int in_f32;              // 1: inputs fp32, 0: bf16
     int gate_logits;         // 1: alpha, beta hold logits (gate_log2_alpha, gate_beta)
     const void* out_gate;    // null, or [B*H][T][dv] in the input dtype: out *= gate
+    int reverse;             // 1: walk the tokens backward (position t is token T-1-t)
+    int accumulate;          // 1: out = (gated) outputs + acc_src, rounded once
+    const float* acc_src;    // accumulate: fp32 [B*H][T][dv] to add
 };
 
 // Segmented chunk walkers (chunk 32 or 64).  With nseg > 1 the workspace

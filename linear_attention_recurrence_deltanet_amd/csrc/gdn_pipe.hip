@@ -229,9 +229,10 @@ __device__ __forceinline__ f32x4 transpose16_bf16(const uint16_t* a, int lda, in
 // NCW: state waves (4, or 8 with one column tile each: three waves per SIMD
 //      instead of two when one state wave would otherwise carry two tiles).
 // NPW: key waves (4 or 8).
-// GATES: gate logits and the output gate are honoured (a separate
-//        instantiation, so that calls without them run no gate code).
-template <int DK, int C, int CT, bool SEG, int NCW = 4, int NPW = 4, bool GATES = false>
+// EXT: gate logits, the output gate, the backward walk and accumulating
+//      outputs are honoured (a separate instantiation, so that calls without
+//      them run none of that code).
+template <int DK, int C, int CT, bool SEG, int NCW = 4, int NPW = 4, bool EXT = false>
 __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) {
     typedef PPlan<DK, C, CT, SEG, NCW, NPW> L;
     typedef OpF16 Op;
@@ -338,8 +339,13 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
     const unsigned osz = p.out_bf16 ? 2u : 4u;
     const rsrc_t ro_ = make_rsrc(SEG ? nullptr : (const char*)p.out + (size_t)bh * T * dv * osz,
                                  SEG ? 0u : (unsigned)T * dv * osz);
-    const bool gated = GATES && !SEG && p.out_gate != nullptr;   // a segment walk leaves it to the correction
-    const bool logits = GATES && p.gate_logits;
+    const bool gated = EXT && !SEG && p.out_gate != nullptr;   // a segment walk leaves it to the correction
+    const bool logits = EXT && p.gate_logits;
+    const bool accum = EXT && !SEG && p.accumulate;
+    // accumulating outputs add fp32 values from a separate plane before the store
+    const rsrc_t rac_ = make_rsrc(accum ? p.acc_src + (size_t)bh * T * dv : nullptr,
+                                  accum ? (unsigned)T * dv * 4u : 0u);
+    const TokMap tm = tok_map(T, EXT && p.reverse);   // walk position -> token
     const rsrc_t rg_ = make_rsrc(gated ? (const char*)p.out_gate + (size_t)bh * T * dv * 2 : nullptr,
                                  gated ? (unsigned)T * dv * 2u : 0u);
     // Phi of this segment: [chunk][row block][k-step of 32 columns of d_k][lane] x 8 fp16,
@@ -363,7 +369,8 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
     F vB[CT][KS_C];                                   // V of the next chunk as B operand
     // output gate of the next chunk's rows (this lane's row and 4 columns per
     // row block), loaded a step ahead of its use
-    uint2 GV[GATES && !SEG ? CT : 1][GATES && !SEG ? NB : 1];
+    uint2 GV[EXT && !SEG ? CT : 1][EXT && !SEG ? NB : 1];
+    uint4 AV[EXT && !SEG ? CT : 1][EXT && !SEG ? NB : 1];     // values to accumulate onto, likewise
     auto col0 = [&](int ct) { return 16 * (ct * NCW + wave); };
     auto ident = [&](int ct) { return SEG && col0(ct) < vlo; };
 
@@ -376,7 +383,7 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
         for (int it = 0; it < QPT; ++it) {
             const int idx = ktid + NPT * it;
             const int r = idx / VPRQ, part = idx % VPRQ;
-            const unsigned off = (unsigned)((t0 + r) * DK + part * 8) * 2u;
+            const unsigned off = (unsigned)(tm(t0 + r) * DK + part * 8) * 2u;
             pk[it] = buf_load16(rk_, off);
             pq[it] = buf_load16(rq_, off);
         }
@@ -385,13 +392,13 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
             const int idx = ktid + NPT * it;
             const int r = idx / VPRV, part = idx % VPRV;
             // identity columns of a segment tile have no v (left as zero)
-            pv[it] = (part * 8 >= vlo) ? buf_load16(rv_, (unsigned)((t0 + r) * dv + vbase + part * 8) * 2u)
+            pv[it] = (part * 8 >= vlo) ? buf_load16(rv_, (unsigned)(tm(t0 + r) * dv + vbase + part * 8) * 2u)
                                        : make_uint4(0u, 0u, 0u, 0u);
         }
         if (kw == SCANW) {
 #pragma unroll
             for (int e = 0; e < TPL; ++e) {
-                const unsigned off = (unsigned)(t0 + lane * TPL + e) * 2u;
+                const unsigned off = (unsigned)tm(t0 + lane * TPL + e) * 2u;
                 pa[e] = buf_load2(ra_, off);
                 pb[e] = buf_load2(rb_, off);
             }
@@ -451,22 +458,27 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
         for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
             for (int ks = 0; ks < KS_D; ++ks) mB[ct][ks] = Op::b_acc(Macc[ct], ks);
-        if constexpr (GATES && !SEG) {
+        if constexpr (EXT && !SEG) {
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-                for (int rb = 0; rb < NB; ++rb) GV[ct][rb] = make_uint2(0u, 0u);
+                for (int rb = 0; rb < NB; ++rb) {
+                    GV[ct][rb] = make_uint2(0u, 0u);
+                    AV[ct][rb] = make_uint4(0u, 0u, 0u, 0u);
+                }
         }
         for (int s = 0; s <= nch; ++s) {
             const int pc = ch0 + s;
             const int vb = s & 1;
-            if constexpr (GATES && !SEG) {
+            if constexpr (EXT && !SEG) {
                 // the gate loaded last step arrives here on every path, so no
                 // later reuse of its registers waits for the output stores
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-                    for (int rb = 0; rb < NB; ++rb) asm volatile("" ::"v"(GV[ct][rb].x), "v"(GV[ct][rb].y));
+                    for (int rb = 0; rb < NB; ++rb)
+                        asm volatile("" ::"v"(GV[ct][rb].x), "v"(GV[ct][rb].y), "v"(AV[ct][rb].x),
+                                     "v"(AV[ct][rb].y), "v"(AV[ct][rb].z), "v"(AV[ct][rb].w));
             }
             // ---- phase 1: finish chunk pc - 1
             if (s > 0) {
@@ -526,9 +538,9 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
                                 }
                             } else {
                                 // rows past T fall outside the buffer and are dropped
-                                const unsigned e0 = (unsigned)(t0 + 16 * rb + lc) * (unsigned)dv +
-                                                    (unsigned)(vbase + col0(ct) + 4 * lg);
-                                if constexpr (GATES && !SEG) {
+                                const unsigned e0 = (unsigned)(tm(t0 + 16 * rb + lc) * dv +
+                                                               vbase + col0(ct) + 4 * lg);
+                                if constexpr (EXT && !SEG) {
                                     // consumed on every path (1 without a gate): a use under a
                                     // branch leaves the load pending on the other path, and the
                                     // next write of these registers then waits for every
@@ -538,6 +550,8 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
                                     o[1] *= gated ? __builtin_bit_cast(float, w.x & 0xffff0000u) : 1.f;
                                     o[2] *= gated ? __builtin_bit_cast(float, w.y << 16) : 1.f;
                                     o[3] *= gated ? __builtin_bit_cast(float, w.y & 0xffff0000u) : 1.f;
+                                    // accumulating: the plane is added (zeros otherwise), one rounding
+                                    add_f32x4(o, AV[ct][rb]);
                                 }
                                 if (p.out_bf16) {
                                     const uint2 w = make_uint2(
@@ -643,17 +657,20 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
                 for (int u = 0; u < (NTS + NCW - 1) / NCW; ++u)
                     if (wave + NCW * u < NTS) p_tile<L>(Kh, Qh, Pm, v_g2, wave + NCW * u, lane);
             }
-            if constexpr (GATES && !SEG) {
-                // output gate of chunk pc, used when it is finished next step.
+            if constexpr (EXT && !SEG) {
+                // output gate and values to accumulate onto of chunk pc, used
+                // when it is finished next step.
                 // Issued whether or not a gate is given (the resource is empty
                 // then), so that the wait before its use counts exactly and
                 // does not drain the output stores issued in between
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-                    for (int rb = 0; rb < NB; ++rb)
-                        GV[ct][rb] = buf_load8(rg_, ((unsigned)(pc * C + 16 * rb + lc) * (unsigned)dv +
-                                                     (unsigned)(vbase + col0(ct) + 4 * lg)) * 2u);
+                    for (int rb = 0; rb < NB; ++rb) {
+                        const unsigned e = (unsigned)(tm(pc * C + 16 * rb + lc) * dv + vbase + col0(ct) + 4 * lg);
+                        GV[ct][rb] = buf_load8(rg_, e * 2u);
+                        AV[ct][rb] = buf_load16(rac_, e * 4u);
+                    }
             }
             __syncthreads();
         }
@@ -971,6 +988,10 @@ __global__ __launch_bounds__(1024) void gdn_pipe_fix_kernel(WalkArgs p) {
     const rsrc_t rG = make_rsrc(gated ? (const char*)p.out_gate + (size_t)bh * T * dv * 2 : nullptr,
                                 gated ? (unsigned)T * dv * 2u : 0u);
     const int col4 = vt * 64 + 16 * cg + 4 * lg;        // first of this lane's four output columns
+    const TokMap tm = tok_map(T, p.reverse);            // walk position -> token
+    // accumulating outputs add an fp32 plane before the store (empty range otherwise)
+    const rsrc_t rAc = make_rsrc(p.accumulate ? p.acc_src + (size_t)bh * T * dv : nullptr,
+                                 p.accumulate ? (unsigned)T * dv * 4u : 0u);
 
     // Loads and stores below are unconditional (kOffNone where there is
     // nothing to move) so that the compiler counts the loads in flight
@@ -991,19 +1012,22 @@ __global__ __launch_bounds__(1024) void gdn_pipe_fix_kernel(WalkArgs p) {
     // ---- correction operands of a group of CPG chunks (RG row blocks): one
     // 16-byte piece of Phi per thread, staged in LDS; the wave's own row block
     // of the partial outputs (fp16, 4 columns per lane)
-    auto cload = [&](uint4& h, uint2& o, uint2& gt, int g) {
+    auto cload = [&](uint4& h, uint2& o, uint2& gt, uint4& av, int g) {
         const int c0 = ch0 + g * CPG;
         const int c = c0 + rg / NB, rb = rg % NB;
         h = buf_load16(rP, (c0 < ch1 && tid < PPG) ? (unsigned)((c0 - ch0) * C * DK * 2 + tid * 16) : kOffNone);
         o = buf_load8(rO, c < ch1 ? (unsigned)((((c - ch0) * NB + rb) * (dv / 16) + c16) * 64 + lane) * 8u
                                   : kOffNone);
         // output gate of the same four elements (the range is empty without one)
-        gt = buf_load8(rG, c < ch1 ? (unsigned)((c * C + 16 * rb + lc) * dv + col4) * 2u : kOffNone);
+        const unsigned e = (unsigned)(tm(c * C + 16 * rb + lc) * dv + col4);
+        gt = buf_load8(rG, c < ch1 ? e * 2u : kOffNone);
+        // values to accumulate onto (the range is empty unless accumulating)
+        av = buf_load16(rAc, c < ch1 ? e * 4u : kOffNone);
     };
-    uint4 ph[2];
+    uint4 ph[2], av2[2];
     uint2 ov[2], gv2[2];
-    cload(ph[0], ov[0], gv2[0], 0);
-    cload(ph[1], ov[1], gv2[1], 1);
+    cload(ph[0], ov[0], gv2[0], av2[0], 0);
+    cload(ph[1], ov[1], gv2[1], av2[1], 1);
 
     // ---- fold: maps 0 .. seg-1, D in flight; the last segment's own map
     // (state_out) is loaded from the start
@@ -1093,7 +1117,7 @@ __global__ __launch_bounds__(1024) void gdn_pipe_fix_kernel(WalkArgs p) {
     // ---- outputs of the segment: O += Phi M_in, formed transposed
     // (O^T = M^T Phi^T): lane (lg, lc) holds row lc of the wave's row block
     // and four consecutive columns, one 16-byte access
-    auto cfix = [&](const uint4& h, const uint2& o, const uint2& gt, int g, int buf) {
+    auto cfix = [&](const uint4& h, const uint2& o, const uint2& gt, const uint4& av, int g, int buf) {
         const int c = ch0 + g * CPG + rg / NB, rb = rg % NB;
         if (tid < PPG) Phs[buf][tid] = h;
         __syncthreads();                  // copy buf reused two groups later, after another barrier
@@ -1104,13 +1128,14 @@ __global__ __launch_bounds__(1024) void gdn_pipe_fix_kernel(WalkArgs p) {
         for (int ks = 0; ks < KS_D; ++ks)
             acc = Op::mma(mI[ks], __builtin_bit_cast(F, Phs[buf][(rg * KS_D + ks) * 64 + lane]), acc);
         // rows past T fall outside the buffer and are dropped
-        const unsigned e0 = (unsigned)((c * C + 16 * rb + lc) * dv + col4);
+        const unsigned e0 = (unsigned)(tm(c * C + 16 * rb + lc) * dv + col4);
         if (gated) {
             acc[0] *= __builtin_bit_cast(float, gt.x << 16);
             acc[1] *= __builtin_bit_cast(float, gt.x & 0xffff0000u);
             acc[2] *= __builtin_bit_cast(float, gt.y << 16);
             acc[3] *= __builtin_bit_cast(float, gt.y & 0xffff0000u);
         }
+        add_f32x4(acc, av);                // accumulating: one rounding of the sum
         if (p.out_bf16) {
             const uint2 w = make_uint2(
                 (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[0]) |
@@ -1124,10 +1149,10 @@ __global__ __launch_bounds__(1024) void gdn_pipe_fix_kernel(WalkArgs p) {
     };
     const int ngroups = (ch1 - ch0 + CPG - 1) / CPG;
     for (int g = 0; g < ngroups; g += 2) {
-        cfix(ph[0], ov[0], gv2[0], g, 0);
-        cload(ph[0], ov[0], gv2[0], g + 2);
-        cfix(ph[1], ov[1], gv2[1], g + 1, 1);
-        cload(ph[1], ov[1], gv2[1], g + 3);
+        cfix(ph[0], ov[0], gv2[0], av2[0], g, 0);
+        cload(ph[0], ov[0], gv2[0], av2[0], g + 2);
+        cfix(ph[1], ov[1], gv2[1], av2[1], g + 1, 1);
+        cload(ph[1], ov[1], gv2[1], av2[1], g + 3);
     }
 }
 
@@ -1136,7 +1161,7 @@ __global__ __launch_bounds__(1024) void gdn_pipe_fix_kernel(WalkArgs p) {
 // ---------------------------------------------------------------------------
 namespace {
 
-template <int DK, int C, int CTS, bool GATES>
+template <int DK, int C, int CTS, bool EXT>
 hipError_t launch_pipe_g(const WalkArgs& a, hipStream_t s) {
     // a segment tile of 128 columns: eight state waves of one tile each
     // (three waves per SIMD; measured faster than four state waves of two
@@ -1148,19 +1173,19 @@ hipError_t launch_pipe_g(const WalkArgs& a, hipStream_t s) {
     const int bh = a.B * a.H;
     if (a.nseg > 1) {
         const int grid = bh * a.nseg * ((DK + a.dv) / (64 * CTS));
-        hipLaunchKernelGGL((gdn_pipe_kernel<DK, C, SCT, true, SNCW, 4, GATES>), dim3(grid), dim3(64 * (SNCW + 4)), 0, s, a);
+        hipLaunchKernelGGL((gdn_pipe_kernel<DK, C, SCT, true, SNCW, 4, EXT>), dim3(grid), dim3(64 * (SNCW + 4)), 0, s, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL((gdn_pipe_fix_kernel<DK, C>), dim3(bh * a.nseg * (a.dv / 64)), dim3(1024), 0, s, a);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL((gdn_pipe_kernel<DK, C, 1, false, 4, UNPW, GATES>), dim3(bh * (a.dv / 64)), dim3(64 * (4 + UNPW)), 0, s, a);
+    hipLaunchKernelGGL((gdn_pipe_kernel<DK, C, 1, false, 4, UNPW, EXT>), dim3(bh * (a.dv / 64)), dim3(64 * (4 + UNPW)), 0, s, a);
     return hipGetLastError();
 }
 
 template <int DK, int C, int CTS>
 hipError_t launch_pipe_t(const WalkArgs& a, hipStream_t s) {
-    if (a.gate_logits || a.out_gate) return launch_pipe_g<DK, C, CTS, true>(a, s);
+    if (a.gate_logits || a.out_gate || a.reverse || a.accumulate) return launch_pipe_g<DK, C, CTS, true>(a, s);
     return launch_pipe_g<DK, C, CTS, false>(a, s);
 }
 

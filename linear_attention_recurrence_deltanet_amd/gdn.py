@@ -19,8 +19,9 @@ GDN_OK, GDN_ERR_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_HIP = 0, -1, -2, -3
 GDN_BF16, GDN_F32 = 0, 1
 
 # every exported entry point of include/gdn.h
-EXPORTS = ("gdn_default_opts", "gdn_fwd_chunked", "gdn_fwd_step", "gdn_workspace_bytes",
-           "gdn_strerror", "gdn_last_error", "gdn_version")
+EXPORTS = ("gdn_default_opts", "gdn_fwd_chunked", "gdn_fwd_step", "gdn_fwd_bidir",
+           "gdn_workspace_bytes", "gdn_bidir_workspace_bytes", "gdn_strerror", "gdn_last_error",
+           "gdn_version")
 
 
 class GdnOpts(ctypes.Structure):
@@ -60,8 +61,12 @@ def load(path: str = LIB_PATH):
     lib.gdn_fwd_chunked.restype = i
     lib.gdn_fwd_step.argtypes = fwd_args + [ctypes.POINTER(GdnOpts)]
     lib.gdn_fwd_step.restype = i
+    lib.gdn_fwd_bidir.argtypes = fwd_args + [i, ctypes.POINTER(GdnOpts)]
+    lib.gdn_fwd_bidir.restype = i
     lib.gdn_workspace_bytes.argtypes = [i, i, i, i, i, i, ctypes.POINTER(GdnOpts)]
     lib.gdn_workspace_bytes.restype = ctypes.c_size_t
+    lib.gdn_bidir_workspace_bytes.argtypes = [i, i, i, i, i, i, ctypes.POINTER(GdnOpts)]
+    lib.gdn_bidir_workspace_bytes.restype = ctypes.c_size_t
     lib.gdn_default_opts.argtypes = [ctypes.POINTER(GdnOpts)]
     lib.gdn_default_opts.restype = None
     lib.gdn_strerror.argtypes = [i]
@@ -113,7 +118,7 @@ def workspace_bytes(B, H, T, dk, dv, chunk=0, opts: Optional[GdnOpts] = None) ->
                                           ctypes.byref(opts) if opts is not None else None))
 
 
-def _workspace(workspace, B, H, T, dk, dv, chunk, in_dtype, out_dtype, device):
+def _workspace(workspace, B, H, T, dk, dv, chunk, in_dtype, out_dtype, device, bidir=False):
     """None: allocate what the plan needs; False: none (single-segment walk)."""
     if workspace is False:
         return None
@@ -123,7 +128,8 @@ def _workspace(workspace, B, H, T, dk, dv, chunk, in_dtype, out_dtype, device):
     load().gdn_default_opts(ctypes.byref(o))
     o.in_dtype = _dtype_code(in_dtype)
     o.out_dtype = _dtype_code(out_dtype)
-    n = int(load().gdn_workspace_bytes(B, H, T, dk, dv, chunk, ctypes.byref(o)))
+    query = load().gdn_bidir_workspace_bytes if bidir else load().gdn_workspace_bytes
+    n = int(query(B, H, T, dk, dv, chunk, ctypes.byref(o)))
     return torch.empty(n, dtype=torch.uint8, device=device) if n > 0 else None
 
 
@@ -201,4 +207,24 @@ def fwd_step(q, k, v, alpha, beta, state_in=None, *, out=None, state_out=None,
     _check(load().gdn_fwd_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
                                _ptr(state_in), _ptr(out), _ptr(state_out),
                                B, H, T, dk, dv, ctypes.byref(opts)))
+    return out, state_out
+
+
+def fwd_bidir(q, k, v, alpha, beta, state_in=None, chunk: int = 0, *, out=None, state_out=None,
+              out_dtype=torch.float32, qk_l2norm=True, scale=1.0, eps=1e-6, stream=None,
+              workspace=None, gate_logits: bool = False, out_gate=None):
+    """gdn_fwd_bidir: forward scan from state_in plus backward scan (zero state,
+    reversed tokens) over one streaming chunk; out is the sum of the two
+    scans' outputs and state_out the forward scan's final state.  chunk 0:
+    the gdn_fwd_step tile.  workspace: None allocates gdn_bidir_workspace_bytes
+    (bf16 outputs need it); other arguments as for fwd_chunked."""
+    B, H, T, dk, dv, out, state_out = _prep(q, k, v, alpha, beta, state_in, out, state_out,
+                                            out_dtype)
+    _check_gate(out_gate, q, B, H, T, dv)
+    workspace = _workspace(workspace, B, H, T, dk, dv, chunk, q.dtype, out.dtype, q.device,
+                           bidir=True)
+    opts = make_opts(q.dtype, out.dtype, qk_l2norm, scale, eps, stream, workspace, gate_logits, out_gate)
+    _check(load().gdn_fwd_bidir(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                _ptr(state_in), _ptr(out), _ptr(state_out),
+                                B, H, T, dk, dv, int(chunk), ctypes.byref(opts)))
     return out, state_out

@@ -50,6 +50,8 @@ def _load():
                                        ctypes.c_long, ctypes.c_long,
                                        ctypes.c_int, ctypes.c_double, ctypes.c_double,
                                        ctypes.c_int]
+        lib.gdn_oracle_scan.restype = ctypes.c_int
+        lib.gdn_oracle_scan.argtypes = lib.gdn_oracle_fwd.argtypes[:-1] + [ctypes.c_int, ctypes.c_int]
         lib.gdn_oracle_gates.restype = None
         lib.gdn_oracle_gates.argtypes = [dp, dp, dp, dp, ctypes.c_long]
         _lib = lib
@@ -77,14 +79,16 @@ def gates(a, b):
 
 
 def gdn_fwd(q, k, v, alpha, beta, state_in=None, *, qk_l2norm=True, scale=1.0,
-            eps=DEFAULT_EPS, nthreads=0, want_state=True, gate_logits=False, out_gate=None):
+            eps=DEFAULT_EPS, nthreads=0, want_state=True, gate_logits=False, out_gate=None,
+            reverse=False):
     """Token-by-token fp64 gated delta rule.
 
     Shapes: q, k [B,H,T,dk]; v [B,H,T,dv]; alpha, beta [B,H,T];
     state_in [B,H,dk,dv] or None (zero state).  Inputs of any float dtype are
     converted to fp64 exactly (bf16/fp16/fp32 all embed in fp64).
     gate_logits: alpha, beta hold logits a, b (see gates()).  out_gate
-    [B,H,T,dv]: the outputs are multiplied by it elementwise.
+    [B,H,T,dv]: the outputs are multiplied by it elementwise.  reverse: the
+    backward scan (tokens visited from T-1 down to 0; gdn_oracle_scan).
     Returns (out [B,H,T,dv] fp64, state_out [B,H,dk,dv] fp64 or None).
     """
     q, k, v, alpha, beta = (_f64(x) for x in (q, k, v, alpha, beta))
@@ -100,10 +104,10 @@ def gdn_fwd(q, k, v, alpha, beta, state_in=None, *, qk_l2norm=True, scale=1.0,
         assert s_in.shape == (B, H, dk, dv)
     out = np.empty((B, H, T, dv), dtype=np.float64)
     s_out = np.empty((B, H, dk, dv), dtype=np.float64) if want_state else None
-    rc = _load().gdn_oracle_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
-                                _ptr(s_in), _ptr(out), _ptr(s_out),
-                                B, H, T, dk, dv, 1 if qk_l2norm else 0,
-                                float(scale), float(eps), int(nthreads))
+    rc = _load().gdn_oracle_scan(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                 _ptr(s_in), _ptr(out), _ptr(s_out),
+                                 B, H, T, dk, dv, 1 if qk_l2norm else 0,
+                                 float(scale), float(eps), 1 if reverse else 0, int(nthreads))
     if rc != 0:
         raise RuntimeError("gdn_oracle_fwd failed with code %d" % rc)
     if out_gate is not None:
@@ -111,3 +115,23 @@ def gdn_fwd(q, k, v, alpha, beta, state_in=None, *, qk_l2norm=True, scale=1.0,
         assert g.shape == out.shape
         out = out * g
     return out, s_out
+
+
+def gdn_bidir(q, k, v, alpha, beta, state_in=None, *, qk_l2norm=True, scale=1.0,
+              eps=DEFAULT_EPS, nthreads=0, gate_logits=False, out_gate=None):
+    """Bidirectional GDN over one streaming chunk (SANA-Streaming section 4.1:
+    forward scan from the previous cache, backward scan within the chunk;
+    section 2.3: the two histories are combined for the output):
+    out = o^f + o^b, with o^f the forward scan from state_in and o^b the
+    backward scan from a zero state; then the output gate.  Returns
+    (out, the forward scan's final state)."""
+    of, sf = gdn_fwd(q, k, v, alpha, beta, state_in, qk_l2norm=qk_l2norm, scale=scale, eps=eps,
+                     nthreads=nthreads, gate_logits=gate_logits)
+    ob, _ = gdn_fwd(q, k, v, alpha, beta, None, qk_l2norm=qk_l2norm, scale=scale, eps=eps,
+                    nthreads=nthreads, want_state=False, gate_logits=gate_logits, reverse=True)
+    out = of + ob
+    if out_gate is not None:
+        g = _f64(out_gate)
+        assert g.shape == out.shape
+        out = out * g
+    return out, sf

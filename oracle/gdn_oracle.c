@@ -28,6 +28,16 @@
  * Columns j of M never mix, so work is split over (b, h, column block)
  * without changing any arithmetic.
  *
+ * Backward scan (bidirectional GDN: SANA-Streaming section 4.1 runs a forward
+ * scan from the previous cache and a backward scan within the chunk; section
+ * 2.3 "Efficient GDN Kernel" combines the forward and reverse histories for
+ * the output): the same recurrence over the tokens in reverse order, from a
+ * zero state, each token with its own alpha_t, beta_t:
+ *       S^b_t = alpha_t S^b_{t+1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ *       o^b_t = S^b_t q_t,   S^b_T = 0.
+ * gdn_oracle_scan with reverse = 1 is that loop (t = T-1 down to 0); the
+ * bidirectional output o^f_t + o^b_t is formed by the Python wrapper.
+ *
  * L2 normalisation (when qk_l2norm != 0): x_hat = x / sqrt(sum x^2 + eps),
  * then q is multiplied by `scale`.
  *
@@ -62,14 +72,15 @@ static void run_item(const double* q, const double* k, const double* v,
                      const double* alpha, const double* beta,
                      const double* m_in, double* out, double* m_out,
                      long T, long dk, long dv, long j0, long j1,
-                     int qk_l2norm, double scale, double eps,
+                     int qk_l2norm, double scale, double eps, int reverse,
                      double* M, double* kh, double* qh) {
     long w = j1 - j0;
     for (long i = 0; i < dk; ++i)
         for (long j = 0; j < w; ++j)
             M[i * w + j] = m_in ? m_in[i * dv + j0 + j] : 0.0;
 
-    for (long t = 0; t < T; ++t) {
+    for (long n = 0; n < T; ++n) {
+        const long t = reverse ? T - 1 - n : n;  /* token visited n-th */
         const double* qt = q + t * dk;
         const double* kt = k + t * dk;
         const double* vt = v + t * dv;
@@ -100,7 +111,9 @@ static void run_item(const double* q, const double* k, const double* v,
 }
 
 /*
- * gdn_oracle_fwd: full forward over B*H independent heads.
+ * gdn_oracle_scan: full scan over B*H independent heads, tokens in order
+ * (reverse = 0, the forward recurrence) or in reverse (reverse = 1, the
+ * backward scan above).
  *   q, k     [B][H][T][dk]   fp64
  *   v        [B][H][T][dv]   fp64
  *   alpha    [B][H][T]       decay in (0, 1]
@@ -111,11 +124,11 @@ static void run_item(const double* q, const double* k, const double* v,
  *   nthreads <= 0 uses the OpenMP default.
  * Returns 0, or -1 on a bad argument.
  */
-int gdn_oracle_fwd(const double* q, const double* k, const double* v,
-                   const double* alpha, const double* beta,
-                   const double* state_in, double* out, double* state_out,
-                   long B, long H, long T, long dk, long dv,
-                   int qk_l2norm, double scale, double eps, int nthreads) {
+int gdn_oracle_scan(const double* q, const double* k, const double* v,
+                    const double* alpha, const double* beta,
+                    const double* state_in, double* out, double* state_out,
+                    long B, long H, long T, long dk, long dv,
+                    int qk_l2norm, double scale, double eps, int reverse, int nthreads) {
     if (B < 0 || H < 0 || T < 0 || dk <= 0 || dv <= 0) return -1;
     if (T > 0 && (!q || !k || !v || !alpha || !beta || !out)) return -1;
     if (state_out && state_in && state_out == state_in) return -1;
@@ -148,12 +161,22 @@ int gdn_oracle_fwd(const double* q, const double* k, const double* v,
                 run_item(q + tk, k + tk, v + tv, alpha + ts, beta + ts,
                          state_in ? state_in + ss : NULL, out + tv,
                          state_out ? state_out + ss : NULL,
-                         T, dk, dv, j0, j1, qk_l2norm, scale, eps, M, kh, qh);
+                         T, dk, dv, j0, j1, qk_l2norm, scale, eps, reverse, M, kh, qh);
             }
         }
         free(M); free(kh); free(qh);
     }
     return err ? -2 : 0;
+}
+
+/* gdn_oracle_fwd: the forward scan (gdn_oracle_scan with reverse = 0). */
+int gdn_oracle_fwd(const double* q, const double* k, const double* v,
+                   const double* alpha, const double* beta,
+                   const double* state_in, double* out, double* state_out,
+                   long B, long H, long T, long dk, long dv,
+                   int qk_l2norm, double scale, double eps, int nthreads) {
+    return gdn_oracle_scan(q, k, v, alpha, beta, state_in, out, state_out, B, H, T, dk, dv,
+                           qk_l2norm, scale, eps, 0, nthreads);
 }
 
 /*
@@ -175,4 +198,4 @@ void gdn_oracle_gates(const double* a, const double* b, double* alpha, double* b
     }
 }
 
-int gdn_oracle_abi_version(void) { return 2; }
+int gdn_oracle_abi_version(void) { return 3; }

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.gdn_version() == 1
+    assert lib.gdn_version() == 2
     assert lib.gdn_strerror(0) == b"ok"
     assert lib.gdn_strerror(-1) == b"invalid argument"
     assert lib.gdn_strerror(-2) == b"unsupported shape or option"

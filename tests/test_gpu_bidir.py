@@ -1,0 +1,131 @@
+"""GPU parity of the bidirectional scan (gdn_fwd_bidir; SANA-Streaming section
+4.1: forward scan from the carried state plus a backward scan within the
+streaming chunk, section 2.3: the two histories combined for the output)
+against the fp64 oracle (oracle.gdn_bidir) on the same bits: every launch
+path (segment walk plus correction, unsegmented walk, fp32 walker, 128-token
+single pass), the state carried across calls, ragged lengths whose padding
+sits at the start of the backward walk, gates, bf16 outputs."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import announce, assert_close, to_dev
+from linear_attention_recurrence_deltanet_amd.inputs import WORKLOADS, make_call, to_numpy64
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(gdn, oracle, wl, calls, *, B=None, H=None, T=None, chunk=0, gates=False,
+         out_dtype=torch.float32, workspace=None, what=""):
+    announce(f"bidir {what} {wl.name} calls={calls} B={B or wl.B} H={H or wl.H} T={T or wl.T} "
+             f"chunk={chunk} gates={gates} out={out_dtype}")
+    g_outs, o_outs = [], []
+    g_state = o_state = None
+    for c in range(calls):
+        d = make_call(wl, c, B=B, H=H, T=T, gates=gates)
+        g = to_dev(d)
+        a_key, b_key = ("alpha_logit", "beta_logit") if gates else ("alpha", "beta")
+        s_in = g["state_in"] if g["state_in"] is not None else g_state
+        kw = dict(out_dtype=out_dtype, gate_logits=gates, out_gate=g["out_gate"] if gates else None)
+        if workspace is not None:
+            kw["workspace"] = workspace
+        o, s = gdn.fwd_bidir(g["q"], g["k"], g["v"], g[a_key], g[b_key], s_in, chunk, **kw)
+        g_outs.append(o.to("cpu", torch.float64).numpy())
+        g_state = s
+        q, k, v, a, b = (to_numpy64(d[n]) for n in ("q", "k", "v", a_key, b_key))
+        os_in = to_numpy64(d["state_in"]) if d["state_in"] is not None else o_state
+        oo, o_state = oracle.gdn_bidir(q, k, v, a, b, os_in, gate_logits=gates,
+                                       out_gate=to_numpy64(d["out_gate"]) if gates else None)
+        o_outs.append(oo)
+    torch.cuda.synchronize()
+    f32 = wl.dtype == "f32"
+    r1 = assert_close(np.concatenate(g_outs, 2), np.concatenate(o_outs, 2), f32, what + " out")
+    r2 = assert_close(g_state.to("cpu", torch.float64).numpy(), o_state, f32, what + " state")
+    print(f"   out maxabs {r1[0]:.2e} rel {r1[1]:.2e} | state maxabs {r2[0]:.2e} rel {r2[1]:.2e}",
+          flush=True)
+
+
+def test_bidir_stream_segmented(gdn_lib, oracle_mod):
+    # 16 heads, 42 chunks: both scans as segment walk plus correction (d = 64)
+    _run(gdn_lib, oracle_mod, WORKLOADS["stream_chunk_h16_d64"], 1, what="stream")
+
+
+def test_bidir_rollout_carried_d128(gdn_lib, oracle_mod):
+    # forward state carried over three calls; the backward scans start at zero
+    _run(gdn_lib, oracle_mod, WORKLOADS["rollout_h16_d128"], 3, H=3, what="rollout")
+
+
+def test_bidir_frame_unsegmented(gdn_lib, oracle_mod):
+    # 48 heads, 14 chunks: one unsegmented walk per head and direction (d = 128)
+    _run(gdn_lib, oracle_mod, WORKLOADS["frame_step_b2_h24_d128"], 2, what="frame")
+
+
+def test_bidir_gates(gdn_lib, oracle_mod):
+    _run(gdn_lib, oracle_mod, WORKLOADS["stream_chunk_h16_d64"], 1, gates=True, what="gates")
+    _run(gdn_lib, oracle_mod, WORKLOADS["frame_step_b2_h24_d128"], 1, B=1, gates=True,
+         what="gates-unsegmented")
+
+
+def test_bidir_unsplit_and_bf16_out(gdn_lib, oracle_mod):
+    wl = WORKLOADS["stream_chunk_h16_d64"]
+    # a workspace of the fp32 plane alone: both scans walk unsplit
+    plane = torch.empty(4 * 700 * 64 * 4, dtype=torch.uint8, device="cuda")
+    _run(gdn_lib, oracle_mod, wl, 1, H=4, T=700, workspace=plane, what="unsplit")
+    _run(gdn_lib, oracle_mod, wl, 1, H=4, T=700, workspace=plane, out_dtype=torch.bfloat16,
+         what="bf16-out-unsplit")
+    # bf16 outputs: the backward part goes through the fp32 plane, one rounding
+    _run(gdn_lib, oracle_mod, wl, 1, H=4, T=700, out_dtype=torch.bfloat16, what="bf16-out")
+    _run(gdn_lib, oracle_mod, WORKLOADS["frame_step_b2_h24_d128"], 1, out_dtype=torch.bfloat16,
+         what="bf16-out-unsegmented")
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_bidir_walker_d32(gdn_lib, oracle_mod, out_dtype):
+    # d_k = d_v = 32 with bf16 inputs runs on the segmented walker
+    wl = WORKLOADS["stream_chunk_h16_d64"].replace(name="stream_d32", dk=32, dv=32)
+    _run(gdn_lib, oracle_mod, wl, 1, H=4, T=1500, out_dtype=out_dtype, what="walker-d32")
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_bidir_needs_its_workspace(gdn_lib, out_dtype):
+    wl = WORKLOADS["stream_chunk_h16_d64"]
+    g = to_dev(make_call(wl, 0, H=2, T=100))
+    with pytest.raises(gdn_lib.GdnError, match="gdn_bidir_workspace_bytes"):
+        gdn_lib.fwd_bidir(g["q"], g["k"], g["v"], g["alpha"], g["beta"], g["state_in"],
+                          out_dtype=out_dtype, workspace=False)
+    small = torch.empty(2 * 100 * 64 * 4 - 16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(gdn_lib.GdnError, match="gdn_bidir_workspace_bytes"):
+        gdn_lib.fwd_bidir(g["q"], g["k"], g["v"], g["alpha"], g["beta"], g["state_in"],
+                          out_dtype=out_dtype, workspace=small)
+
+
+@pytest.mark.parametrize("T", [1, 15, 63, 65, 129, 1000])
+def test_bidir_ragged(gdn_lib, oracle_mod, T):
+    # a partial last chunk is the first chunk of the backward walk
+    _run(gdn_lib, oracle_mod, WORKLOADS["stream_chunk_h16_d64"], 1, H=3, T=T, what=f"T{T}")
+
+
+@pytest.mark.parametrize("chunk", [32, 128])
+def test_bidir_other_chunks(gdn_lib, oracle_mod, chunk):
+    _run(gdn_lib, oracle_mod, WORKLOADS["stream_chunk_h16_d64"], 1, H=4, T=1000, chunk=chunk,
+         what=f"chunk{chunk}")
+    _run(gdn_lib, oracle_mod, WORKLOADS["stream_chunk_h16_d64"], 1, H=4, T=1000, chunk=chunk,
+         out_dtype=torch.bfloat16, what=f"chunk{chunk}-bf16-out")
+
+
+@pytest.mark.parametrize("chunk", [32, 64])
+def test_bidir_fp32(gdn_lib, oracle_mod, chunk):
+    _run(gdn_lib, oracle_mod, WORKLOADS["tiny_f32"], 1, chunk=chunk, what="fp32")
+    _run(gdn_lib, oracle_mod, WORKLOADS["tiny_f32"], 1, T=77, chunk=chunk, what="fp32-ragged")
+
+
+def test_bidir_empty_sequence(gdn_lib):
+    # T = 0: out untouched, state_out = state_in
+    q = torch.zeros(1, 2, 0, 64, dtype=torch.bfloat16, device="cuda")
+    v = torch.zeros(1, 2, 0, 64, dtype=torch.bfloat16, device="cuda")
+    a = torch.zeros(1, 2, 0, dtype=torch.bfloat16, device="cuda")
+    s0 = torch.randn(1, 2, 64, 64, device="cuda")
+    out, st = gdn_lib.fwd_bidir(q, q, v, a, a, s0)
+    torch.cuda.synchronize()
+    assert out.shape == (1, 2, 0, 64)
+    assert torch.equal(st, s0)

@@ -314,3 +314,94 @@ def test_output_gate_is_elementwise(oracle_mod):
         for j in range(o0.shape[-1]):
             assert og[0, 0, t, j] == o0[0, 0, t, j] * g[0, 0, t, j]
     assert np.array_equal(sg, s0)
+
+
+# ---- bidirectional scan (SANA-Streaming section 4.1: forward scan from the
+# cache plus a backward scan within the chunk; section 2.3: both histories
+# are combined for the output)
+
+def _rev(x):
+    return np.ascontiguousarray(np.asarray(x)[:, :, ::-1])
+
+
+def test_bidir_time_reversal_symmetry(oracle_mod):
+    """From a zero state the bidirectional output of the reversed sequence is
+    the reversed output: the backward scan is the forward recurrence run over
+    the tokens in reverse, each token with its own gates."""
+    rng = np.random.default_rng(31)
+    q, k, v, a, b, _ = rand_case(rng, B=2, H=2, T=23, dk=5, dv=4)
+    out, _ = oracle_mod.gdn_bidir(q, k, v, a, b, None)
+    out_r, _ = oracle_mod.gdn_bidir(_rev(q), _rev(k), _rev(v), _rev(a), _rev(b), None)
+    np.testing.assert_allclose(_rev(out_r), out, rtol=1e-12, atol=1e-12)
+    # and the two halves are not symmetric on their own
+    fwd, _ = oracle_mod.gdn_fwd(q, k, v, a, b, None)
+    assert np.abs(fwd - out).max() > 1e-3
+
+
+def test_bidir_orthonormal_keys_both_sides(oracle_mod):
+    """Orthonormal keys decouple the delta correction in both scans: with a
+    zero state, o_t = sum_s w_ts beta_s (k_s . q_t) v_s with
+    w_ts = prod_{r=s+1..t} alpha_r for s <= t (forward) plus
+    prod_{r=t..s-1} alpha_r for s >= t (backward: moving from token s back to
+    t applies the gates of tokens t .. s-1), so the diagonal counts twice."""
+    rng = np.random.default_rng(32)
+    T, dk, dv = 11, 16, 5
+    Qm, _ = np.linalg.qr(rng.standard_normal((dk, dk)))
+    k = Qm[:T][None, None] * rng.uniform(0.5, 2.0, size=(1, 1, T, 1))
+    q = rng.standard_normal((1, 1, T, dk))
+    v = rng.standard_normal((1, 1, T, dv))
+    a = rng.uniform(0.3, 1.0, size=(1, 1, T))
+    b = rng.uniform(0.0, 1.0, size=(1, 1, T))
+    out, _ = oracle_mod.gdn_bidir(q, k, v, a, b, None, eps=0.0)
+    al = a[0, 0]
+    W = np.zeros((T, T))
+    for t in range(T):
+        for s in range(T):
+            if s <= t:
+                W[t, s] += np.prod(al[s + 1:t + 1])
+            if s >= t:
+                W[t, s] += np.prod(al[t:s])
+    ref = (W * (unit(q[0, 0]) @ Qm[:T].T) * b[0, 0][None, :]) @ v[0, 0]
+    np.testing.assert_allclose(out[0, 0], ref, rtol=1e-12, atol=1e-13)
+
+
+def test_bidir_small_beta_is_bidirectional_linear_attention(oracle_mod):
+    """From a zero state and to first order in beta (any keys) the delta
+    correction vanishes and the output is gated bidirectional linear
+    attention with the weights of the orthonormal case (the error is second
+    order in beta)."""
+    rng = np.random.default_rng(33)
+    T, dk, dv = 14, 6, 4
+    q = rng.standard_normal((1, 1, T, dk))
+    k = rng.standard_normal((1, 1, T, dk))
+    v = rng.standard_normal((1, 1, T, dv))
+    a = rng.uniform(0.4, 1.0, size=(1, 1, T))
+    eps_b = 1e-4
+    b = eps_b * rng.uniform(0.5, 1.0, size=(1, 1, T))
+    out, _ = oracle_mod.gdn_bidir(q, k, v, a, b, None, eps=0.0)
+    al = a[0, 0]
+    W = np.zeros((T, T))
+    for t in range(T):
+        for s in range(T):
+            if s <= t:
+                W[t, s] += np.prod(al[s + 1:t + 1])
+            if s >= t:
+                W[t, s] += np.prod(al[t:s])
+    qh, kh = unit(q[0, 0]), unit(k[0, 0])
+    ref = (W * (qh @ kh.T) * b[0, 0][None, :]) @ v[0, 0]
+    err = np.abs(out[0, 0] - ref).max()
+    assert err < 10 * eps_b * np.abs(ref).max(), err
+    assert np.abs(ref).max() > 0.5 * eps_b
+
+
+def test_bidir_beta_zero_is_forward_decay(oracle_mod):
+    """beta = 0: nothing is written, the backward scan (zero state) adds
+    nothing and the output is the decayed incoming state read out."""
+    rng = np.random.default_rng(34)
+    q, k, v, a, _, s0 = rand_case(rng, T=9)
+    z = np.zeros_like(a)
+    out, st = oracle_mod.gdn_bidir(q, k, v, a, z, s0, eps=0.0)
+    g = np.cumprod(a[0, 0])
+    ref = g[:, None] * (unit(q[0, 0]) @ s0[0, 0])
+    np.testing.assert_allclose(out[0, 0], ref, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(st[0, 0], g[-1] * s0[0, 0], rtol=1e-12, atol=1e-13)
