@@ -179,9 +179,11 @@ __device__ __forceinline__ void buf_store2(rsrc_t r, unsigned off, uint16_t v) {
 }
 // soff: a wave-uniform byte offset added in the scalar operand (not part of
 // the range check: only for stores known to be in range)
+// AUX: cache-policy bits of the store (0: default).
+template <int AUX = 0>
 __device__ __forceinline__ void buf_store8(rsrc_t r, unsigned off, uint2 v, unsigned soff = 0) {
     typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-    __builtin_amdgcn_raw_buffer_store_b64(u32x2{v.x, v.y}, r, off, (int)soff, 0);
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{v.x, v.y}, r, off, (int)soff, AUX);
 }
 __device__ __forceinline__ void buf_store16(rsrc_t r, unsigned off, uint4 v) {
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
