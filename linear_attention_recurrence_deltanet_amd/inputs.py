@@ -116,3 +116,57 @@ def make_call(wl: Workload, call: int = 0, *, B: Optional[int] = None, H: Option
 def to_numpy64(t: torch.Tensor):
     """Exact upcast of a CPU tensor (bf16/fp32) to a float64 numpy array."""
     return t.detach().to("cpu", torch.float64).numpy()
+
+
+# ---------------------------------------------------------------------------
+# Softmax attention with a persistent sink and a recent window (the other block
+# type of the hybrid: SANA-Streaming section 2.1, "Softmax blocks for local
+# window and sink refinement"): the current streaming chunk attends, with no
+# mask, to the sink chunk (the stream's first chunk), a window of recent
+# chunks and itself.  q, k, v ~ N(0, 1) in bf16; lengths in tokens.
+
+@dataclasses.dataclass(frozen=True)
+class AttnWorkload:
+    name: str
+    B: int
+    H: int
+    Nq: int             # query tokens (the current chunk)
+    n_sink: int         # tokens of the sink chunk
+    n_win: int          # tokens of the recent window
+    n_cur: int          # tokens of the current chunk (keys and values)
+    d: int              # head dimension
+    seed: int
+
+    def replace(self, **kw) -> "AttnWorkload":
+        return dataclasses.replace(self, **kw)
+
+
+ATTN_WORKLOADS = {
+    # one streaming chunk (3 latent frames, 2640 tokens) attending to a sink
+    # chunk, one recent chunk and itself: 16 heads of 64
+    "attn_chunk_h16_d64": AttnWorkload("attn_chunk_h16_d64", 1, 16, 2640, 2640, 2640, 2640, 64, 2001),
+    # the same with 8 heads of 128
+    "attn_chunk_h8_d128": AttnWorkload("attn_chunk_h8_d128", 1, 8, 2640, 2640, 2640, 2640, 128, 2002),
+}
+
+
+def make_attn_call(wl: AttnWorkload, call: int = 0, *, B: Optional[int] = None, H: Optional[int] = None,
+                   Nq: Optional[int] = None, n_sink: Optional[int] = None, n_win: Optional[int] = None,
+                   n_cur: Optional[int] = None):
+    """q [B,H,Nq,d] and k_x, v_x [B,H,n_x,d] for x in sink, win, cur (bf16 CPU
+    tensors, standard normal draws); sizes may be overridden."""
+    B = wl.B if B is None else B
+    H = wl.H if H is None else H
+    Nq = wl.Nq if Nq is None else Nq
+    ns = wl.n_sink if n_sink is None else n_sink
+    nw = wl.n_win if n_win is None else n_win
+    nc = wl.n_cur if n_cur is None else n_cur
+    g = torch.Generator().manual_seed(wl.seed * 1000 + call)
+    bf = torch.bfloat16
+    r = lambda n: torch.randn(B, H, n, wl.d, generator=g, dtype=torch.float32).to(bf)
+    d = dict(q=r(Nq))
+    for name, n in (("sink", ns), ("win", nw), ("cur", nc)):
+        d["k_" + name] = r(n)
+        d["v_" + name] = r(n)
+    return d
+

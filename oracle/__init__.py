@@ -9,6 +9,9 @@ definition and its source passage are in that file's header).  This module
 only compiles it with gcc and marshals numpy arrays through ctypes.
 
 Parity pins: ``tests/test_oracle_pins.py`` and ``tests/golden/``.
+
+``attn_sink_window`` (from ``attention.py``) is the oracle of the softmax
+attention block with a sink chunk and a recent window.
 """
 from __future__ import annotations
 
@@ -17,6 +20,8 @@ import os
 import subprocess
 
 import numpy as np
+
+from .attention import attn_sink_window  # noqa: F401
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "gdn_oracle.c")

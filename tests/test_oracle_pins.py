@@ -405,3 +405,83 @@ def test_bidir_beta_zero_is_forward_decay(oracle_mod):
     ref = g[:, None] * (unit(q[0, 0]) @ s0[0, 0])
     np.testing.assert_allclose(out[0, 0], ref, rtol=1e-12, atol=1e-13)
     np.testing.assert_allclose(st[0, 0], g[-1] * s0[0, 0], rtol=1e-12, atol=1e-13)
+
+
+# ---- softmax attention with a sink chunk and a recent window (SANA-Streaming
+# section 2.1, "Softmax blocks for local window and sink refinement")
+
+def _attn_case(rng, B=1, H=2, Nq=7, ns=5, nw=3, nc=6, d=8):
+    r = lambda n: rng.standard_normal((B, H, n, d))
+    return r(Nq), r(ns), r(ns), r(nw), r(nw), r(nc), r(nc)
+
+
+def test_attn_zero_query_averages_values(oracle_mod):
+    """q = 0 gives equal scores: every output row is the mean of all values."""
+    rng = np.random.default_rng(41)
+    q, ks, vs, kw, vw, kc, vc = _attn_case(rng)
+    out = oracle_mod.attn_sink_window(np.zeros_like(q), ks, vs, kw, vw, kc, vc)
+    mean = np.concatenate([vs, vw, vc], axis=2).mean(axis=2, keepdims=True)
+    np.testing.assert_allclose(out, np.broadcast_to(mean, out.shape), rtol=1e-13, atol=1e-13)
+
+
+def test_attn_two_keys_closed_form(oracle_mod):
+    """Two keys: the weight of the first is the logistic function of the
+    scaled score difference."""
+    rng = np.random.default_rng(42)
+    d = 4
+    q = rng.standard_normal((1, 1, 3, d))
+    k1, k2 = rng.standard_normal((1, 1, 1, d)), rng.standard_normal((1, 1, 1, d))
+    v1, v2 = rng.standard_normal((1, 1, 1, d)), rng.standard_normal((1, 1, 1, d))
+    e = np.zeros((1, 1, 0, d))
+    out = oracle_mod.attn_sink_window(q, k1, v1, e, e, k2, v2, scale=0.7)
+    w = 1.0 / (1.0 + np.exp(-0.7 * (q[0, 0] @ (k1 - k2)[0, 0, 0])))
+    ref = w[:, None] * v1[0, 0, 0] + (1 - w)[:, None] * v2[0, 0, 0]
+    np.testing.assert_allclose(out[0, 0], ref, rtol=1e-13, atol=1e-14)
+
+
+def test_attn_split_by_log_sum_exp(oracle_mod):
+    """Attention over [A; B] equals the attentions over A and over B mixed by
+    their softmax masses, exp(lse_A) : exp(lse_B) (the identity that lets a
+    kernel walk the context in tiles)."""
+    rng = np.random.default_rng(43)
+    q, ks, vs, kw, vw, kc, vc = _attn_case(rng, d=6)
+    e = np.zeros_like(kw[:, :, :0])
+    s = 1.0 / np.sqrt(6)
+    full = oracle_mod.attn_sink_window(q, ks, vs, kw, vw, kc, vc)
+    oa = oracle_mod.attn_sink_window(q, ks, vs, e, e, e, e)
+    ob = oracle_mod.attn_sink_window(q, e, e, kw, vw, kc, vc)
+    la = np.log(np.exp(s * q @ np.swapaxes(ks, 2, 3)).sum(-1, keepdims=True))
+    kb = np.concatenate([kw, kc], axis=2)
+    lb = np.log(np.exp(s * q @ np.swapaxes(kb, 2, 3)).sum(-1, keepdims=True))
+    wa = 1.0 / (1.0 + np.exp(lb - la))
+    np.testing.assert_allclose(full, wa * oa + (1 - wa) * ob, rtol=1e-12, atol=1e-13)
+
+
+def test_attn_key_permutation_and_segment_placement(oracle_mod):
+    """The output does not depend on the order of the (key, value) pairs nor
+    on which of the three segments holds them."""
+    rng = np.random.default_rng(44)
+    q, ks, vs, kw, vw, kc, vc = _attn_case(rng)
+    out = oracle_mod.attn_sink_window(q, ks, vs, kw, vw, kc, vc)
+    K = np.concatenate([ks, kw, kc], axis=2)
+    V = np.concatenate([vs, vw, vc], axis=2)
+    perm = rng.permutation(K.shape[2])
+    e = K[:, :, :0]
+    out2 = oracle_mod.attn_sink_window(q, e, e, K[:, :, perm[:4]], V[:, :, perm[:4]],
+                                       K[:, :, perm[4:]], V[:, :, perm[4:]])
+    np.testing.assert_allclose(out2, out, rtol=1e-12, atol=1e-13)
+
+
+def test_attn_matches_library_attention(oracle_mod):
+    """Against torch's scaled_dot_product_attention on the CPU in fp64 (an
+    independent implementation), with large scores to exercise the max shift."""
+    import torch
+    rng = np.random.default_rng(45)
+    q, ks, vs, kw, vw, kc, vc = _attn_case(rng, B=2, H=3, Nq=9, ns=4, nw=5, nc=9, d=16)
+    q = q * 4.0
+    out = oracle_mod.attn_sink_window(q, ks, vs, kw, vw, kc, vc)
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x))
+    K = torch.cat([t(ks), t(kw), t(kc)], dim=2)
+    V = torch.cat([t(vs), t(vw), t(vc)], dim=2)
+    ref = torch.nn.functional.scaled_dot_product_attention(t(q), K, V).numpy()
+    np.testing.assert_allclose(out, ref, rtol=1e-10, atol=1e-12)
