@@ -120,6 +120,90 @@ def cpu_baseline(wl, budget_s: float, gates: bool = False, bidir: bool = False):
                       f"OpenMP over (b, h, 16-column block), CPU: {cpu_model}"}
 
 
+def bench_attention(args):
+    """Sink-and-window softmax attention (gdn_attn_sink_window): one step is one
+    call over the workload's chunk; MFMA-bound (4 Nq N d flops per head)."""
+    import torch
+    from linear_attention_recurrence_deltanet_amd import gdn
+    from linear_attention_recurrence_deltanet_amd.inputs import ATTN_WORKLOADS, make_attn_call, to_numpy64
+
+    wl = ATTN_WORKLOADS[args.workload]
+    lib = gdn.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    out_dt = torch.float32 if args.out_dtype == "f32" else torch.bfloat16
+    nk = wl.n_sink + wl.n_win + wl.n_cur
+    per_set = wl.B * wl.H * (wl.Nq + 2 * nk) * wl.d * 2
+    nsets = max(2, min(16, (2 * LLC_BYTES) // max(per_set, 1) + 1))
+    sets = [{k: v.to(dev).contiguous() for k, v in make_attn_call(wl, i).items()} for i in range(nsets)]
+    out = torch.empty(wl.B, wl.H, wl.Nq, wl.d, dtype=out_dt, device=dev)
+    stream = torch.cuda.current_stream()
+    opts = gdn.make_opts(torch.bfloat16, out_dt, stream=stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    calls = [(P(g["q"]), P(g["k_sink"]), P(g["v_sink"]), wl.n_sink, P(g["k_win"]), P(g["v_win"]), wl.n_win,
+              P(g["k_cur"]), P(g["v_cur"]), wl.n_cur, P(out), wl.B, wl.H, wl.Nq, wl.d, 0.0) for g in sets]
+    fn = lambda c: lib.gdn_attn_sink_window(*c, ctypes.byref(opts))
+    for i in range(args.warmup):
+        if fn(calls[i % nsets]) != 0:
+            raise RuntimeError(lib.gdn_last_error().decode())
+    torch.cuda.synchronize()
+    K = args.steps
+    t0e = torch.cuda.Event(enable_timing=True)
+    t1e = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0e.record(stream)
+    for i in range(K):
+        fn(calls[i % nsets])
+    t1e.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = max(t0e.elapsed_time(t1e), wall * 1e3) / K
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for i in range(K):
+        ev[i][0].record(stream)
+        fn(calls[i % nsets])
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    per = [a.elapsed_time(b) for a, b in ev]
+    kern_ms = statistics.mean(per)
+    flops = 4 * wl.B * wl.H * wl.Nq * nk * wl.d
+    achieved = flops / (kern_ms * 1e-3) / 1e12
+    res = {
+        "metric": "sink+window softmax attention query tokens/sec (bf16, 1 GPU) + % of MFMA roofline vs oracle",
+        "value": wl.B * wl.Nq / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "Nq": wl.Nq, "n_sink": wl.n_sink,
+                   "n_win": wl.n_win, "n_cur": wl.n_cur, "d": wl.d, "entry": "gdn_attn_sink_window",
+                   "out_dtype": args.out_dtype, "input_sets": nsets},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None},
+        "kernel": {"avg_ms": kern_ms, "p50_ms": statistics.median(per),
+                   "p99_ms": sorted(per)[min(len(per) - 1, int(0.99 * len(per)))],
+                   "algorithmic_flops": flops, "source_hash": kernel_source_hash()},
+    }
+    if not args.no_cpu:
+        import oracle
+        d = make_attn_call(wl, 0)
+        h = 0
+        t0 = time.perf_counter()
+        while True:
+            sl = lambda x: to_numpy64(x[:, h % wl.H:h % wl.H + 1])
+            oracle.attn_sink_window(sl(d["q"]), sl(d["k_sink"]), sl(d["v_sink"]), sl(d["k_win"]),
+                                    sl(d["v_win"]), sl(d["k_cur"]), sl(d["v_cur"]))
+            h += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds:
+                break
+        res["cpu_baseline"] = {"value": h * wl.Nq / wl.H / el, "unit": "tokens/s",
+                               "cores": os.cpu_count() or 1, "kind": "oracle",
+                               "sample": f"{h} single heads of {wl.name} (Nq={wl.Nq}, {nk} keys, d={wl.d}) "
+                                         f"in {el:.1f} s, fp64 numpy (BLAS threads), scaled to all heads"}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -144,6 +228,10 @@ def main():
               "part of it (heads and value columns shard with no communication).",
               file=sys.stderr)
         sys.exit(2)
+
+    from linear_attention_recurrence_deltanet_amd.inputs import ATTN_WORKLOADS
+    if args.workload in ATTN_WORKLOADS:
+        return bench_attention(args)
 
     import torch
     from linear_attention_recurrence_deltanet_amd import gdn

@@ -158,6 +158,33 @@ size_t gdn_bidir_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk,
 size_t gdn_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk,
                            const gdn_opts* opts);
 
+/*
+ * gdn_attn_sink_window: the softmax attention block of the hybrid model
+ * (SANA-Streaming, section 2.1 "Softmax blocks for local window and sink
+ * refinement": each chunk attends to a constrained context made of itself,
+ * a persistent sink chunk shared across the stream and a short window of
+ * recent chunks; attention sinks after reference [30]).  Per (b, h):
+ *
+ *   K = [k_sink; k_win; k_cur],  V = [v_sink; v_win; v_cur]
+ *   out = softmax(scale * q K^T) V      (softmax over the keys, no mask)
+ *
+ * Layouts (row-major, device memory owned by the caller, bf16 inputs):
+ *   q, out          [B][H][Nq][d]       out in opts->out_dtype (fp32 default)
+ *   k_x, v_x        [B][H][n_x][d]      x = sink, win, cur
+ * d is 64 or 128; scale <= 0 means 1/sqrt(d).  A segment with n_x = 0 may
+ * pass NULL pointers; the three together must hold at least one key (when
+ * B*H*Nq > 0).  Pointers 16-byte aligned; opts->in_dtype must be GDN_BF16.
+ * Precision: q K^T from the bf16 inputs with fp32 accumulation; the softmax
+ * in fp32; P V with fp16 operands (values must lie within the fp16 range,
+ * |v| < 65504) and fp32 accumulation.
+ * Asynchronous on opts->stream like the other entry points; no workspace.
+ */
+int gdn_attn_sink_window(const void* q, const void* k_sink, const void* v_sink, int n_sink,
+                         const void* k_win, const void* v_win, int n_win,
+                         const void* k_cur, const void* v_cur, int n_cur,
+                         void* out, int B, int H, int Nq, int d, float scale,
+                         const gdn_opts* opts);
+
 /* Static description of a status code. */
 const char* gdn_strerror(int status);
 

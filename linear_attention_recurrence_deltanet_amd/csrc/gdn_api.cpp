@@ -3,6 +3,7 @@
 #include "gdn.h"
 
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
 #include <stdio.h>
 #include <string.h>
@@ -324,6 +325,49 @@ int gdn_fwd_bidir(const void* q, const void* k, const void* v, const void* alpha
                   int B, int H, int T, int dk, int dv, int chunk, const gdn_opts* opts) {
     return run_bidir(q, k, v, alpha, beta, state_in, out, state_out, B, H, T, dk, dv,
                      chunk > 0 ? chunk : STEP_CHUNK, opts);
+}
+
+int gdn_attn_sink_window(const void* q, const void* k_sink, const void* v_sink, int n_sink,
+                         const void* k_win, const void* v_win, int n_win,
+                         const void* k_cur, const void* v_cur, int n_cur,
+                         void* out, int B, int H, int Nq, int d, float scale, const gdn_opts* opts) {
+    g_last_error[0] = '\0';
+    gdn_opts o;
+    if (opts) o = *opts; else defaults(&o);
+    if (B < 0 || H < 0 || Nq < 0 || n_sink < 0 || n_win < 0 || n_cur < 0)
+        return fail(GDN_ERR_ARG, "negative size");
+    if (!gdn::attn_supported(d)) return fail(GDN_ERR_UNSUPPORTED, "d must be 64 or 128");
+    if (o.in_dtype != GDN_BF16) return fail(GDN_ERR_UNSUPPORTED, "attention inputs must be bf16");
+    if (o.out_dtype != GDN_BF16 && o.out_dtype != GDN_F32) return fail(GDN_ERR_ARG, "bad out_dtype");
+    if ((long long)B * H * Nq == 0) return GDN_OK;
+    if (n_sink + n_win + n_cur <= 0) return fail(GDN_ERR_ARG, "empty key set");
+    const long long lim = 0x7fffffffLL;
+    if ((long long)Nq * d * 4 > lim || (long long)n_sink * d * 2 > lim || (long long)n_win * d * 2 > lim ||
+        (long long)n_cur * d * 2 > lim)
+        return fail(GDN_ERR_UNSUPPORTED, "per-head size above 2 GiB");
+    if (!q || !out) return fail(GDN_ERR_ARG, "q and out must not be NULL");
+    const void* ks[3] = {k_sink, k_win, k_cur};
+    const void* vs[3] = {v_sink, v_win, v_cur};
+    const int ns[3] = {n_sink, n_win, n_cur};
+    for (int i = 0; i < 3; ++i) {
+        if (ns[i] > 0 && (!ks[i] || !vs[i])) return fail(GDN_ERR_ARG, "keys and values of a non-empty segment must not be NULL");
+        if (ns[i] > 0 && (!aligned16(ks[i]) || !aligned16(vs[i]))) return fail(GDN_ERR_ARG, "keys and values must be 16-byte aligned");
+    }
+    if (!aligned16(q) || !aligned16(out)) return fail(GDN_ERR_ARG, "q and out must be 16-byte aligned");
+    gdn::AttnArgs a;
+    a.q = q;
+    for (int i = 0; i < 3; ++i) {
+        a.k[i] = ks[i];
+        a.v[i] = vs[i];
+        a.n[i] = ns[i];
+    }
+    a.out = out;
+    a.B = B; a.H = H; a.Nq = Nq; a.d = d;
+    a.scale = scale > 0.f ? scale : 1.f / sqrtf((float)d);
+    a.out_bf16 = o.out_dtype == GDN_BF16;
+    hipError_t e = gdn::launch_attn(a, reinterpret_cast<hipStream_t>(o.stream));
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return GDN_OK;
 }
 
 size_t gdn_bidir_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, const gdn_opts* opts) {

@@ -1,0 +1,290 @@
+// gdn_attn.hip -- softmax attention of a streaming chunk over a persistent
+// sink chunk, a window of recent chunks and the chunk itself (SANA-Streaming,
+// paperpeel page, section 2.1 "Softmax blocks for local window and sink
+// refinement": the softmax blocks of the hybrid restrict each chunk's context
+// to itself, a sink chunk shared across the stream and a short recent window),
+// for gfx950.
+//
+//   O = softmax(scale * Q K^T) V,  K = [K_sink; K_win; K_cur], V likewise,
+//   no mask (a chunk is denoised as a whole).
+//
+// One workgroup of four waves per (head, 128 queries); each wave owns 32
+// queries (two blocks of 16).  The keys are walked in tiles of 64 across the
+// three segments, staged in LDS (K row-major, V transposed) and double
+// buffered: the next tile's loads are issued before the current tile's
+// products and written to the other copy after them, one barrier per tile.
+// Per tile and wave the products are formed transposed, so that the softmax
+// statistics and the output rescale belong to lanes (lane (g, c) holds query
+// c of each block):
+//   S^T = K Q^T          keys x queries (K from LDS, Q^T kept in registers),
+//                        bf16 operands as given
+//   online softmax over the keys: running max m and sum l per query, exp2
+//   O^T += V^T P^T       P^T taken as it stands from the S^T accumulators;
+//                        fp16 operands (11-bit significand: P in bf16 alone
+//                        costs ~1e-3 relative on the output), V converted
+//                        exactly while it is transposed into LDS
+// The output is O = (O^T)^T / l: lane (g, c) writes four consecutive columns
+// of query c, one 16-byte store in fp32.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "gdn_common.h"
+#include "gdn_kernels.h"
+
+namespace gdn {
+
+namespace {
+
+constexpr int AQ = 128;   // queries per workgroup (4 waves x 32)
+constexpr int AK = 64;    // keys per tile
+
+template <int D>
+struct APlan {
+    // row strides of 2 (mod 32) 32-bit words beyond 16-byte multiples keep the
+    // 8-byte operand reads of 16 rows in distinct banks
+    static constexpr int LDK = D + 4;             // K rows: D bf16
+    static constexpr int LDV = AK + 4;            // V^T rows: AK bf16
+    static constexpr int KSZ = AK * LDK;          // elements of one K copy
+    static constexpr int VSZ = D * LDV;           // elements of one V^T copy
+    static constexpr int PPR = D / 8;             // 16-byte pieces per key row
+    static constexpr int CPT = AK * PPR / 256;    // pieces per thread per tile (K, and V)
+};
+
+// Operand fragment in accumulator k order (row lane % 16; k = kb + 4 g + i
+// and kb + 16 + 4 g + i for lane group g), from bf16 rows in LDS.
+__device__ __forceinline__ u16x8 frag_rows(const uint16_t* base, int ld, int row0, int kb, int lane) {
+    const uint16_t* p = base + (row0 + (lane & 15)) * ld + kb + 4 * (lane >> 4);
+    const u16x4 lo = *reinterpret_cast<const u16x4*>(p);
+    const u16x4 hi = *reinterpret_cast<const u16x4*>(p + 16);
+    return u16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// Eight fp32 -> fp16 (round to nearest even), packed in pairs.
+__device__ __forceinline__ u16x8 pack8_f16(const f32x4& a, const f32x4& b) {
+    return OpF16::pack8(a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]);
+}
+
+// Eight fp32 -> bf16 (round to nearest even), packed in pairs.
+__device__ __forceinline__ u16x8 pack8_bf16(const f32x4& a, const f32x4& b) {
+    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 w = {__builtin_bit_cast(uint32_t, __builtin_convertvector(f2{a[0], a[1]}, bf2)),
+                     __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{a[2], a[3]}, bf2)),
+                     __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{b[0], b[1]}, bf2)),
+                     __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{b[2], b[3]}, bf2))};
+    return __builtin_bit_cast(u16x8, w);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void gdn_attn_kernel(AttnArgs p) {
+    typedef APlan<D> L;
+    typedef OpBF16 Op;
+    constexpr int KSD = D / 32;                   // k-steps of the head dimension
+    constexpr int NDB = D / 16;                   // 16-row blocks of O^T
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[2][L::KSZ];
+    __shared__ __attribute__((aligned(16))) uint16_t Vt[2][L::VSZ];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lc = lane & 15, lg = lane >> 4;
+    const int Nq = p.Nq;
+    const int nqb = (Nq + AQ - 1) / AQ;
+    int wg = blockIdx.x;
+    {
+        // the query blocks of one head read the same keys: keep them on one XCD
+        const int w8 = (int)gridDim.x / 8 * 8;
+        if (wg < w8) wg = (wg % 8) * (w8 / 8) + wg / 8;
+    }
+    const int qblk = uniform(wg % nqb);
+    const int bh = uniform(wg / nqb);
+    const int q0 = qblk * AQ + 32 * wave;          // this wave's first query
+
+    const rsrc_t rq = make_rsrc(reinterpret_cast<const uint16_t*>(p.q) + (size_t)bh * Nq * D,
+                                (unsigned)Nq * D * 2u);
+    const unsigned osz = p.out_bf16 ? 2u : 4u;
+    const rsrc_t ro = make_rsrc(reinterpret_cast<const char*>(p.out) + (size_t)bh * Nq * D * osz,
+                                (unsigned)Nq * D * osz);
+    // tiles of each segment; tile t of the walk lies in segment seg at key base
+    const int nt0 = (p.n[0] + AK - 1) / AK, nt1 = (p.n[1] + AK - 1) / AK, nt2 = (p.n[2] + AK - 1) / AK;
+    const int ntiles = nt0 + nt1 + nt2;
+    auto locate = [&](int t, int& seg, int& base) {
+        if (t < nt0) { seg = 0; base = t * AK; }
+        else if (t < nt0 + nt1) { seg = 1; base = (t - nt0) * AK; }
+        else { seg = 2; base = (t - nt0 - nt1) * AK; }
+    };
+
+    // ---- key/value tile staging: registers, then LDS
+    uint4 kr[L::CPT], vr[L::CPT];
+    auto load_tile = [&](int t) {
+        int seg, base;
+        locate(t, seg, base);
+        const int n = seg == 0 ? p.n[0] : seg == 1 ? p.n[1] : p.n[2];
+        const void* kp = seg == 0 ? p.k[0] : seg == 1 ? p.k[1] : p.k[2];
+        const void* vp = seg == 0 ? p.v[0] : seg == 1 ? p.v[1] : p.v[2];
+        // keys past the segment's end read as zero (and are masked below)
+        const rsrc_t rk = make_rsrc(reinterpret_cast<const uint16_t*>(kp) + (size_t)bh * n * D, (unsigned)n * D * 2u);
+        const rsrc_t rv = make_rsrc(reinterpret_cast<const uint16_t*>(vp) + (size_t)bh * n * D, (unsigned)n * D * 2u);
+#pragma unroll
+        for (int it = 0; it < L::CPT; ++it) {
+            const int idx = tid + 256 * it;
+            const int r = idx / L::PPR, c = idx % L::PPR;
+            const unsigned off = (unsigned)((base + r) * D + 8 * c) * 2u;
+            kr[it] = buf_load16(rk, off);
+            vr[it] = buf_load16(rv, off);
+        }
+    };
+    auto store_tile = [&](int b) {
+#pragma unroll
+        for (int it = 0; it < L::CPT; ++it) {
+            const int idx = tid + 256 * it;
+            const int r = idx / L::PPR, c = idx % L::PPR;
+            uint2* kd = reinterpret_cast<uint2*>(&Ks[b][r * L::LDK + 8 * c]);
+            kd[0] = make_uint2(kr[it].x, kr[it].y);
+            kd[1] = make_uint2(kr[it].z, kr[it].w);
+            // bf16 -> fp16 (exact within the fp16 range), transposed
+            const uint32_t w[4] = {vr[it].x, vr[it].y, vr[it].z, vr[it].w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const _Float16 lo = (_Float16)__builtin_bit_cast(float, w[j] << 16);
+                const _Float16 hi = (_Float16)__builtin_bit_cast(float, w[j] & 0xffff0000u);
+                Vt[b][(8 * c + 2 * j) * L::LDV + r] = __builtin_bit_cast(uint16_t, lo);
+                Vt[b][(8 * c + 2 * j + 1) * L::LDV + r] = __builtin_bit_cast(uint16_t, hi);
+            }
+        }
+    };
+
+    // ---- this wave's queries as B fragments (Q^T), accumulator k order
+    u16x8 qf[2][KSD];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int ks = 0; ks < KSD; ++ks) {
+            const unsigned off = (unsigned)((q0 + 16 * qb + lc) * D + 32 * ks + 4 * lg) * 2u;
+            const uint2 lo = buf_load8(rq, off), hi = buf_load8(rq, off + 32u);
+            qf[qb][ks] = __builtin_bit_cast(u16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        }
+
+    f32x4 O[NDB][2];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) O[db][0] = O[db][1] = zero4();
+    // running max (exp2 domain) and partial sums of this lane's keys, per query
+    // block; the max starts finite so that fully masked keys give exp2(-inf) = 0
+    float m[2] = {-1e30f, -1e30f}, l[2] = {0.f, 0.f};
+    const float cs = p.scale * 1.4426950408889634f;
+
+    if (ntiles > 0) {
+        load_tile(0);
+        store_tile(0);
+    }
+    __syncthreads();
+    for (int t = 0; t < ntiles; ++t) {
+        if (t + 1 < ntiles) load_tile(t + 1);
+        const int b = t & 1;
+        int seg, base;
+        locate(t, seg, base);
+        const int kmax = min(AK, (seg == 0 ? p.n[0] : seg == 1 ? p.n[1] : p.n[2]) - base);
+
+        // S^T = K Q^T: rows = keys 16 kb + 4 g + i, column = query c
+        f32x4 S[4][2];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) S[kb][0] = S[kb][1] = zero4();
+#pragma unroll
+        for (int ks = 0; ks < KSD; ++ks)
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                const u16x8 a = frag_rows(Ks[b], L::LDK, 16 * kb, 32 * ks, lane);
+                S[kb][0] = Op::mma(a, qf[0][ks], S[kb][0]);
+                S[kb][1] = Op::mma(a, qf[1][ks], S[kb][1]);
+            }
+
+        // online softmax over the keys, per query (the four lanes of a column)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float s = (16 * kb + 4 * lg + i < kmax) ? S[kb][qb][i] * cs : -INFINITY;
+                    S[kb][qb][i] = s;
+                    mx = fmaxf(mx, s);
+                }
+            mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            const float mn = fmaxf(m[qb], mx);
+            const float corr = __builtin_amdgcn_exp2f(m[qb] - mn);
+            m[qb] = mn;
+            float ls = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float e = __builtin_amdgcn_exp2f(S[kb][qb][i] - mn);
+                    S[kb][qb][i] = e;
+                    ls += e;
+                }
+            l[qb] = l[qb] * corr + ls;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) O[db][qb] *= corr;
+        }
+
+        // O^T += V^T P^T: P^T as B fragments straight from the accumulators
+        u16x8 pf[2][2];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+            for (int k2 = 0; k2 < 2; ++k2) pf[qb][k2] = pack8_f16(S[2 * k2][qb], S[2 * k2 + 1][qb]);
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                const u16x8 a = frag_rows(Vt[b], L::LDV, 16 * db, 32 * k2, lane);
+                O[db][0] = OpF16::mma(a, pf[0][k2], O[db][0]);
+                O[db][1] = OpF16::mma(a, pf[1][k2], O[db][1]);
+            }
+
+        if (t + 1 < ntiles) store_tile(b ^ 1);   // copy b ^ 1 was last read before the previous barrier
+        __syncthreads();
+    }
+
+    // ---- O = (O^T)^T / l: lane (g, c) holds columns 16 db + 4 g + i of query c
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        float ls = l[qb];
+        ls += __shfl_xor(ls, 16, 64);
+        ls += __shfl_xor(ls, 32, 64);
+        const float inv = 1.f / ls;
+        const int row = q0 + 16 * qb + lc;                 // rows past Nq are dropped
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            const f32x4 o = O[db][qb] * inv;
+            const unsigned e = (unsigned)(row * D + 16 * db + 4 * lg);
+            if (p.out_bf16) {
+                const u16x8 w = pack8_bf16(o, o);
+                const uint4 u = __builtin_bit_cast(uint4, w);
+                buf_store8(ro, e * 2u, make_uint2(u.x, u.y));
+            } else {
+                buf_store16(ro, e * 4u, __builtin_bit_cast(uint4, o));
+            }
+        }
+    }
+}
+
+}  // namespace
+
+bool attn_supported(int d) { return d == 64 || d == 128; }
+
+hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
+    const int nqb = (a.Nq + AQ - 1) / AQ;
+    const dim3 grid((unsigned)(a.B * a.H * nqb)), block(256);
+    if (a.d == 64)
+        hipLaunchKernelGGL(gdn_attn_kernel<64>, grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL(gdn_attn_kernel<128>, grid, block, 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace gdn

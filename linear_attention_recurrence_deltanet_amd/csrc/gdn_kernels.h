@@ -64,4 +64,20 @@ hipError_t launch_pipe(const WalkArgs& a, int chunk, hipStream_t s);
 hipError_t launch_fwd_single(const FwdArgs& a, int chunk, int bv, hipStream_t s);
 int single_max_bv(int in_f32, int dk, int chunk);
 
+// Softmax attention over [sink; window; current] keys (gdn_attn.hip):
+// q, out [B*H][Nq][d]; k[s], v[s] [B*H][n[s]][d] for s = sink, window,
+// current (bf16); out fp32 or bf16.
+struct AttnArgs {
+    const void* q;
+    const void* k[3];
+    const void* v[3];
+    int n[3];
+    void* out;
+    int B, H, Nq, d;
+    float scale;
+    int out_bf16;
+};
+bool attn_supported(int d);
+hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
+
 }  // namespace gdn

@@ -20,8 +20,8 @@ GDN_BF16, GDN_F32 = 0, 1
 
 # every exported entry point of include/gdn.h
 EXPORTS = ("gdn_default_opts", "gdn_fwd_chunked", "gdn_fwd_step", "gdn_fwd_bidir",
-           "gdn_workspace_bytes", "gdn_bidir_workspace_bytes", "gdn_strerror", "gdn_last_error",
-           "gdn_version")
+           "gdn_workspace_bytes", "gdn_bidir_workspace_bytes", "gdn_attn_sink_window",
+           "gdn_strerror", "gdn_last_error", "gdn_version")
 
 
 class GdnOpts(ctypes.Structure):
@@ -67,6 +67,9 @@ def load(path: str = LIB_PATH):
     lib.gdn_workspace_bytes.restype = ctypes.c_size_t
     lib.gdn_bidir_workspace_bytes.argtypes = [i, i, i, i, i, i, ctypes.POINTER(GdnOpts)]
     lib.gdn_bidir_workspace_bytes.restype = ctypes.c_size_t
+    lib.gdn_attn_sink_window.argtypes = [vp, vp, vp, i, vp, vp, i, vp, vp, i, vp, i, i, i, i,
+                                         ctypes.c_float, ctypes.POINTER(GdnOpts)]
+    lib.gdn_attn_sink_window.restype = i
     lib.gdn_default_opts.argtypes = [ctypes.POINTER(GdnOpts)]
     lib.gdn_default_opts.restype = None
     lib.gdn_strerror.argtypes = [i]
@@ -228,3 +231,30 @@ def fwd_bidir(q, k, v, alpha, beta, state_in=None, chunk: int = 0, *, out=None, 
                                 _ptr(state_in), _ptr(out), _ptr(state_out),
                                 B, H, T, dk, dv, int(chunk), ctypes.byref(opts)))
     return out, state_out
+
+
+def attn_sink_window(q, k_sink, v_sink, k_win, v_win, k_cur, v_cur, scale=None, *, out=None,
+                     out_dtype=torch.float32, stream=None):
+    """gdn_attn_sink_window: softmax(scale q K^T) V over [sink; window; current]
+    keys.  q [B,H,Nq,d], k_x/v_x [B,H,n_x,d] bf16 device tensors (n_x may be
+    0).  scale None: 1/sqrt(d).  Returns out [B,H,Nq,d]."""
+    B, H, Nq, d = q.shape
+    segs = []
+    for name, k, v in (("sink", k_sink, v_sink), ("win", k_win, v_win), ("cur", k_cur, v_cur)):
+        for t in (k, v):
+            if not t.is_cuda or not t.is_contiguous() or t.dtype != torch.bfloat16:
+                raise ValueError(f"{name} keys and values must be contiguous bf16 device tensors")
+        if k.shape != v.shape or k.shape[:2] != (B, H) or k.shape[3] != d:
+            raise ValueError(f"{name} keys and values must be [B, H, n, d]")
+        segs.append((k, v, k.shape[2]))
+    if not q.is_cuda or not q.is_contiguous() or q.dtype != torch.bfloat16:
+        raise ValueError("q must be a contiguous bf16 device tensor")
+    if out is None:
+        out = torch.empty(B, H, Nq, d, dtype=out_dtype, device=q.device)
+    opts = make_opts(q.dtype, out.dtype, stream=stream)
+    args = []
+    for k, v, n in segs:
+        args += [_ptr(k) if n else None, _ptr(v) if n else None, int(n)]
+    _check(load().gdn_attn_sink_window(_ptr(q), *args, _ptr(out), B, H, Nq, d,
+                                       float(scale) if scale else 0.0, ctypes.byref(opts)))
+    return out

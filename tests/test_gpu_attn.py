@@ -1,0 +1,66 @@
+"""GPU parity of the sink-and-window softmax attention block
+(gdn_attn_sink_window; SANA-Streaming section 2.1, "Softmax blocks for local
+window and sink refinement") against the fp64 oracle on the same bf16 bits:
+ragged tiles, empty segments, both head sizes, bf16 outputs, large scores,
+and the full streaming-chunk size on sampled heads."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import announce, assert_close
+from linear_attention_recurrence_deltanet_amd.inputs import ATTN_WORKLOADS, make_attn_call, to_numpy64
+
+pytestmark = pytest.mark.gpu
+SEGS = ("sink", "win", "cur")
+
+
+def _run(gdn, oracle, wl, *, heads=None, qmul=1.0, scale=None, out_dtype=torch.float32, what="", **sizes):
+    announce(f"attn {what} {wl.name} {sizes} heads={heads} qmul={qmul} scale={scale} out={out_dtype}")
+    d = make_attn_call(wl, 0, **sizes)
+    d["q"] = (d["q"].float() * qmul).to(torch.bfloat16)
+    g = {k: v.cuda().contiguous() for k, v in d.items()}
+    out = gdn.attn_sink_window(g["q"], g["k_sink"], g["v_sink"], g["k_win"], g["v_win"],
+                               g["k_cur"], g["v_cur"], scale, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    got = out.to("cpu", torch.float64).numpy()
+    hs = range(d["q"].shape[1]) if heads is None else heads
+    sel = lambda x: to_numpy64(x)[:, list(hs)]
+    ref = oracle.attn_sink_window(sel(d["q"]), *(sel(d[p + s]) for s in SEGS for p in ("k_", "v_")),
+                                  scale=scale)
+    r = assert_close(got[:, list(hs)], ref, False, what + " out")
+    print(f"   out maxabs {r[0]:.2e} rel {r[1]:.2e}", flush=True)
+
+
+def test_attn_small_ragged(gdn_lib, oracle_mod):
+    wl = ATTN_WORKLOADS["attn_chunk_h16_d64"]
+    _run(gdn_lib, oracle_mod, wl, H=2, Nq=100, n_sink=70, n_win=0, n_cur=100, what="ragged")
+    _run(gdn_lib, oracle_mod, wl, H=3, Nq=257, n_sink=64, n_win=129, n_cur=257, what="three-segments")
+
+
+def test_attn_d128_bf16_out(gdn_lib, oracle_mod):
+    wl = ATTN_WORKLOADS["attn_chunk_h8_d128"]
+    _run(gdn_lib, oracle_mod, wl, H=2, Nq=300, n_sink=200, n_win=130, n_cur=300, what="d128")
+    _run(gdn_lib, oracle_mod, wl, H=2, Nq=300, n_sink=200, n_win=130, n_cur=300,
+         out_dtype=torch.bfloat16, what="d128-bf16-out")
+
+
+def test_attn_only_current_and_single_key(gdn_lib, oracle_mod):
+    wl = ATTN_WORKLOADS["attn_chunk_h16_d64"]
+    _run(gdn_lib, oracle_mod, wl, H=2, Nq=130, n_sink=0, n_win=0, n_cur=130, what="self-only")
+    _run(gdn_lib, oracle_mod, wl, H=1, Nq=1, n_sink=0, n_win=0, n_cur=1, what="one-key")
+    _run(gdn_lib, oracle_mod, wl, H=1, Nq=5, n_sink=1, n_win=0, n_cur=0, what="sink-only")
+
+
+def test_attn_large_scores_and_scale(gdn_lib, oracle_mod):
+    wl = ATTN_WORKLOADS["attn_chunk_h16_d64"]
+    _run(gdn_lib, oracle_mod, wl, H=2, Nq=200, n_sink=150, n_win=64, n_cur=200, qmul=6.0,
+         what="large-scores")
+    _run(gdn_lib, oracle_mod, wl, H=2, Nq=200, n_sink=150, n_win=64, n_cur=200, scale=0.05,
+         what="scale")
+
+
+@pytest.mark.parametrize("name", ["attn_chunk_h16_d64", "attn_chunk_h8_d128"])
+def test_attn_full_size_sampled_heads(gdn_lib, oracle_mod, name):
+    # the benchmark's shape; every output of two heads against the oracle
+    wl = ATTN_WORKLOADS[name]
+    _run(gdn_lib, oracle_mod, wl, heads=[0, wl.H - 1], what="full")
