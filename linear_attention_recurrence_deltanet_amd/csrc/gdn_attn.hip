@@ -48,11 +48,32 @@ struct APlan {
     static constexpr int KSZ = AK * LDK;          // elements of one K copy
     static constexpr int VSZ = D * LDV;           // elements of one V^T copy
     static constexpr int PPR = D / 8;             // 16-byte pieces per key row
-    static constexpr int CPT = AK * PPR / 256;    // pieces per thread per tile (K, and V)
+    static constexpr int NPC = AK / 2 * PPR / 256; // (row pair, piece) items per thread per tile
 };
 
+// Over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (one query column of an
+// accumulator tile): v_permlane32_swap / v_permlane16_swap exchange halves
+// and rows of two registers on the VALU, no LDS round trip.  Written as asm
+// with both registers in and out: through the compiler builtin, a swap of
+// two equal inputs had its second result replaced by the first (checked on
+// the hardware, whose results differ), losing the exchange.
+__device__ __forceinline__ float xlane_max4(float x) {
+    float a = x, b = x;
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+    float c = fmaxf(a, b), d = c;
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(c), "+v"(d));
+    return fmaxf(c, d);
+}
+__device__ __forceinline__ float xlane_sum4(float x) {
+    float a = x, b = x;
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+    float c = a + b, d = c;
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(c), "+v"(d));
+    return c + d;
+}
+
 // Operand fragment in accumulator k order (row lane % 16; k = kb + 4 g + i
-// and kb + 16 + 4 g + i for lane group g), from bf16 rows in LDS.
+// and kb + 16 + 4 g + i for lane group g), from 16-bit rows in LDS.
 __device__ __forceinline__ u16x8 frag_rows(const uint16_t* base, int ld, int row0, int kb, int lane) {
     const uint16_t* p = base + (row0 + (lane & 15)) * ld + kb + 4 * (lane >> 4);
     const u16x4 lo = *reinterpret_cast<const u16x4*>(p);
@@ -78,7 +99,7 @@ __device__ __forceinline__ u16x8 pack8_bf16(const f32x4& a, const f32x4& b) {
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void gdn_attn_kernel(AttnArgs p) {
+__global__ __launch_bounds__(256, 2) void gdn_attn_kernel(AttnArgs p) {
     typedef APlan<D> L;
     typedef OpBF16 Op;
     constexpr int KSD = D / 32;                   // k-steps of the head dimension
@@ -116,8 +137,10 @@ __global__ __launch_bounds__(256) void gdn_attn_kernel(AttnArgs p) {
         else { seg = 2; base = (t - nt0 - nt1) * AK; }
     };
 
-    // ---- key/value tile staging: registers, then LDS
-    uint4 kr[L::CPT], vr[L::CPT];
+    // ---- key/value tile staging: registers, then LDS.  A thread moves the
+    // same 16-byte piece of two consecutive keys, so that V can be written
+    // transposed as 4-byte (key pair) words
+    uint4 kr[2 * L::NPC], vr[2 * L::NPC];
     auto load_tile = [&](int t) {
         int seg, base;
         locate(t, seg, base);
@@ -128,30 +151,39 @@ __global__ __launch_bounds__(256) void gdn_attn_kernel(AttnArgs p) {
         const rsrc_t rk = make_rsrc(reinterpret_cast<const uint16_t*>(kp) + (size_t)bh * n * D, (unsigned)n * D * 2u);
         const rsrc_t rv = make_rsrc(reinterpret_cast<const uint16_t*>(vp) + (size_t)bh * n * D, (unsigned)n * D * 2u);
 #pragma unroll
-        for (int it = 0; it < L::CPT; ++it) {
+        for (int it = 0; it < L::NPC; ++it) {
             const int idx = tid + 256 * it;
-            const int r = idx / L::PPR, c = idx % L::PPR;
+            const int r = 2 * (idx / L::PPR), c = idx % L::PPR;
             const unsigned off = (unsigned)((base + r) * D + 8 * c) * 2u;
-            kr[it] = buf_load16(rk, off);
-            vr[it] = buf_load16(rv, off);
+            kr[2 * it] = buf_load16(rk, off);
+            kr[2 * it + 1] = buf_load16(rk, off + D * 2u);
+            vr[2 * it] = buf_load16(rv, off);
+            vr[2 * it + 1] = buf_load16(rv, off + D * 2u);
         }
     };
     auto store_tile = [&](int b) {
 #pragma unroll
-        for (int it = 0; it < L::CPT; ++it) {
+        for (int it = 0; it < L::NPC; ++it) {
             const int idx = tid + 256 * it;
-            const int r = idx / L::PPR, c = idx % L::PPR;
-            uint2* kd = reinterpret_cast<uint2*>(&Ks[b][r * L::LDK + 8 * c]);
-            kd[0] = make_uint2(kr[it].x, kr[it].y);
-            kd[1] = make_uint2(kr[it].z, kr[it].w);
-            // bf16 -> fp16 (exact within the fp16 range), transposed
-            const uint32_t w[4] = {vr[it].x, vr[it].y, vr[it].z, vr[it].w};
+            const int r = 2 * (idx / L::PPR), c = idx % L::PPR;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const _Float16 lo = (_Float16)__builtin_bit_cast(float, w[j] << 16);
-                const _Float16 hi = (_Float16)__builtin_bit_cast(float, w[j] & 0xffff0000u);
-                Vt[b][(8 * c + 2 * j) * L::LDV + r] = __builtin_bit_cast(uint16_t, lo);
-                Vt[b][(8 * c + 2 * j + 1) * L::LDV + r] = __builtin_bit_cast(uint16_t, hi);
+            for (int h = 0; h < 2; ++h) {
+                uint2* kd = reinterpret_cast<uint2*>(&Ks[b][(r + h) * L::LDK + 8 * c]);
+                kd[0] = make_uint2(kr[2 * it + h].x, kr[2 * it + h].y);
+                kd[1] = make_uint2(kr[2 * it + h].z, kr[2 * it + h].w);
+            }
+            // bf16 -> fp16 (exact for |v| in [2^-14, 65504]; smaller values keep
+            // an absolute error below 2^-25), transposed: word (key r, key r + 1)
+            const uint32_t w0[4] = {vr[2 * it].x, vr[2 * it].y, vr[2 * it].z, vr[2 * it].w};
+            const uint32_t w1[4] = {vr[2 * it + 1].x, vr[2 * it + 1].y, vr[2 * it + 1].z, vr[2 * it + 1].w};
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t a = (j & 1) ? (w0[j / 2] & 0xffff0000u) : (w0[j / 2] << 16);
+                const uint32_t e = (j & 1) ? (w1[j / 2] & 0xffff0000u) : (w1[j / 2] << 16);
+                typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+                typedef float f2 __attribute__((ext_vector_type(2)));
+                const h2 v2 = __builtin_convertvector(f2{__builtin_bit_cast(float, a), __builtin_bit_cast(float, e)}, h2);
+                *reinterpret_cast<uint32_t*>(&Vt[b][(8 * c + j) * L::LDV + r]) = __builtin_bit_cast(uint32_t, v2);
             }
         }
     };
@@ -200,35 +232,42 @@ __global__ __launch_bounds__(256) void gdn_attn_kernel(AttnArgs p) {
                 S[kb][1] = Op::mma(a, qf[1][ks], S[kb][1]);
             }
 
-        // online softmax over the keys, per query (the four lanes of a column)
+        // keys past a segment's end (its last tile only) get no weight
+        if (kmax < AK) {
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (16 * kb + 4 * lg + i >= kmax) S[kb][0][i] = S[kb][1][i] = -INFINITY;
+        }
+        // online softmax over the keys, per query (the four lanes of a column);
+        // the scale enters once, in the exponent's fma (cs > 0)
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
             float mx = -INFINITY;
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float s = (16 * kb + 4 * lg + i < kmax) ? S[kb][qb][i] * cs : -INFINITY;
-                    S[kb][qb][i] = s;
-                    mx = fmaxf(mx, s);
-                }
-            mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-            const float mn = fmaxf(m[qb], mx);
+                for (int i = 0; i < 4; ++i) mx = fmaxf(mx, S[kb][qb][i]);
+            const float mn = fmaxf(m[qb], xlane_max4(mx) * cs);
             const float corr = __builtin_amdgcn_exp2f(m[qb] - mn);
-            m[qb] = mn;
             float ls = 0.f;
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float e = __builtin_amdgcn_exp2f(S[kb][qb][i] - mn);
+                    const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][qb][i], cs, -mn));
                     S[kb][qb][i] = e;
                     ls += e;
                 }
             l[qb] = l[qb] * corr + ls;
+            // the running output is rescaled only when some query's max grew
+            // (corr is exactly 1 for the others)
+            if (__builtin_amdgcn_ballot_w64(mn > m[qb]) != 0) {
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) O[db][qb] *= corr;
+                for (int db = 0; db < NDB; ++db) O[db][qb] *= corr;
+            }
+            m[qb] = mn;
         }
 
         // O^T += V^T P^T: P^T as B fragments straight from the accumulators
@@ -253,10 +292,7 @@ __global__ __launch_bounds__(256) void gdn_attn_kernel(AttnArgs p) {
     // ---- O = (O^T)^T / l: lane (g, c) holds columns 16 db + 4 g + i of query c
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-        float ls = l[qb];
-        ls += __shfl_xor(ls, 16, 64);
-        ls += __shfl_xor(ls, 32, 64);
-        const float inv = 1.f / ls;
+        const float inv = 1.f / xlane_sum4(l[qb]);
         const int row = q0 + 16 * qb + lc;                 // rows past Nq are dropped
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
