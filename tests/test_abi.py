@@ -113,6 +113,66 @@ def test_workspace_query_is_host_only(lib):
     assert lib.gdn_workspace_bytes(1, 16, 2640, 48, 64, 64, None) == 0
 
 
+def test_bidir_needs_its_workspace_before_any_launch(lib):
+    P = ctypes.c_void_p
+    args = (P(16), P(16), P(16), P(16), P(16), None, P(16), None, 1, 2, 100, 64, 64, 0)
+    # no workspace: rejected synchronously (the pointers are fake addresses)
+    assert lib.gdn_fwd_bidir(*args, None) == gdn.GDN_ERR_ARG
+    assert b"gdn_bidir_workspace_bytes" in lib.gdn_last_error()
+    # too small a workspace: same
+    o = gdn.GdnOpts()
+    lib.gdn_default_opts(ctypes.byref(o))
+    o.workspace = P(4096)
+    o.workspace_bytes = 2 * 100 * 64 * 4 - 16
+    assert lib.gdn_fwd_bidir(*args, ctypes.byref(o)) == gdn.GDN_ERR_ARG
+    # the usual argument checks come first
+    assert lib.gdn_fwd_bidir(None, *args[1:], None) == gdn.GDN_ERR_ARG
+
+
+def test_bidir_workspace_query(lib):
+    # the fp32 plane (B*H*T*dv*4 rounded to 256) plus the split-sequence data
+    plane = (1 * 16 * 2640 * 64 * 4 + 255) // 256 * 256
+    assert lib.gdn_bidir_workspace_bytes(1, 16, 2640, 64, 64, 0, None) == \
+        plane + lib.gdn_workspace_bytes(1, 16, 2640, 64, 64, 0, None)
+    many = (4 * 32 * 16384 * 128 * 4 + 255) // 256 * 256
+    assert lib.gdn_bidir_workspace_bytes(4, 32, 16384, 128, 128, 64, None) == many
+    assert lib.gdn_bidir_workspace_bytes(1, 16, 0, 64, 64, 0, None) == 0
+    assert lib.gdn_bidir_workspace_bytes(1, 16, 2640, 48, 64, 0, None) == 0
+
+
+def _attn(lib, q=16, ks=16, vs=16, ns=8, kw=16, vw=16, nw=8, kc=16, vc=16, nc=8, out=16,
+          B=1, H=1, Nq=8, d=64, scale=0.0, opts=None):
+    P = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.gdn_attn_sink_window(P(q), P(ks), P(vs), ns, P(kw), P(vw), nw, P(kc), P(vc), nc,
+                                    P(out), B, H, Nq, d, scale, opts)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), gdn.GDN_ERR_ARG),
+    (dict(out=None), gdn.GDN_ERR_ARG),
+    (dict(ns=-1), gdn.GDN_ERR_ARG),
+    (dict(Nq=-1), gdn.GDN_ERR_ARG),
+    (dict(d=96), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(ns=0, nw=0, nc=0), gdn.GDN_ERR_ARG),          # no key at all
+    (dict(kc=None), gdn.GDN_ERR_ARG),                    # non-empty segment without keys
+    (dict(vs=24), gdn.GDN_ERR_ARG),                      # misaligned
+    (dict(q=8), gdn.GDN_ERR_ARG),
+])
+def test_attn_argument_errors_are_synchronous(lib, kw, status):
+    assert _attn(lib, **kw) == status
+    assert len(lib.gdn_last_error()) > 0
+
+
+def test_attn_empty_segments_and_dtype(lib):
+    # an empty segment may pass NULL pointers; a zero-size call launches nothing
+    assert _attn(lib, Nq=0, ks=None, vs=None, ns=0) == gdn.GDN_OK
+    o = gdn.GdnOpts()
+    lib.gdn_default_opts(ctypes.byref(o))
+    o.in_dtype = gdn.GDN_F32
+    assert _attn(lib, opts=ctypes.byref(o)) == gdn.GDN_ERR_UNSUPPORTED
+
+
+# last: it reloads the binding module (the fixture's library keeps the old types)
 def test_binding_fails_loudly_without_library(tmp_path):
     import importlib
     mod = importlib.reload(gdn)
