@@ -138,7 +138,9 @@ def bench_attention(args):
     sets = [{k: v.to(dev).contiguous() for k, v in make_attn_call(wl, i).items()} for i in range(nsets)]
     out = torch.empty(wl.B, wl.H, wl.Nq, wl.d, dtype=out_dt, device=dev)
     stream = torch.cuda.current_stream()
-    opts = gdn.make_opts(torch.bfloat16, out_dt, stream=stream)
+    ws_bytes = int(lib.gdn_attn_workspace_bytes(wl.B, wl.H, wl.Nq, wl.n_sink, wl.n_win, wl.n_cur, wl.d, None))
+    workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    opts = gdn.make_opts(torch.bfloat16, out_dt, stream=stream, workspace=workspace)
     P = lambda t: ctypes.c_void_p(t.data_ptr())
     calls = [(P(g["q"]), P(g["k_sink"]), P(g["v_sink"]), wl.n_sink, P(g["k_win"]), P(g["v_win"]), wl.n_win,
               P(g["k_cur"]), P(g["v_cur"]), wl.n_cur, P(out), wl.B, wl.H, wl.Nq, wl.d, 0.0) for g in sets]
@@ -177,7 +179,7 @@ def bench_attention(args):
         "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "Nq": wl.Nq, "n_sink": wl.n_sink,
                    "n_win": wl.n_win, "n_cur": wl.n_cur, "d": wl.d, "entry": "gdn_attn_sink_window",
-                   "out_dtype": args.out_dtype, "input_sets": nsets},
+                   "out_dtype": args.out_dtype, "input_sets": nsets, "workspace_bytes": ws_bytes},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None},
         "kernel": {"avg_ms": kern_ms, "p50_ms": statistics.median(per),

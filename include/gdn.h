@@ -177,13 +177,22 @@ size_t gdn_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk,
  * Precision: q K^T from the bf16 inputs with fp32 accumulation; the softmax
  * in fp32; P V with fp16 operands (values must lie within the fp16 range,
  * |v| < 65504) and fp32 accumulation.
- * Asynchronous on opts->stream like the other entry points; no workspace.
+ * Asynchronous on opts->stream like the other entry points.  With few
+ * heads the key range is split over several workgroups whose partial
+ * results are merged by a second launch; that needs the workspace of
+ * gdn_attn_workspace_bytes() (opts->workspace); without it the call runs
+ * unsplit (same results to rounding).
  */
 int gdn_attn_sink_window(const void* q, const void* k_sink, const void* v_sink, int n_sink,
                          const void* k_win, const void* v_win, int n_win,
                          const void* k_cur, const void* v_cur, int n_cur,
                          void* out, int B, int H, int Nq, int d, float scale,
                          const gdn_opts* opts);
+
+/* Workspace (bytes) that lets gdn_attn_sink_window split the key range for
+ * this shape; 0 when it would not split or for invalid shapes. */
+size_t gdn_attn_workspace_bytes(int B, int H, int Nq, int n_sink, int n_win, int n_cur, int d,
+                                const gdn_opts* opts);
 
 /* Static description of a status code. */
 const char* gdn_strerror(int status);

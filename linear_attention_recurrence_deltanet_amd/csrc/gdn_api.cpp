@@ -365,9 +365,27 @@ int gdn_attn_sink_window(const void* q, const void* k_sink, const void* v_sink, 
     a.B = B; a.H = H; a.Nq = Nq; a.d = d;
     a.scale = scale > 0.f ? scale : 1.f / sqrtf((float)d);
     a.out_bf16 = o.out_dtype == GDN_BF16;
+    // key ranges split over workgroups when the caller's workspace holds them
+    a.nsplit = gdn::attn_splits(B, H, Nq, ns);
+    a.part_o = nullptr;
+    a.part_ml = nullptr;
+    const size_t need = gdn::attn_workspace(B, H, Nq, d, a.nsplit);
+    if (a.nsplit > 1 && (!o.workspace || o.workspace_bytes < need || !aligned16(o.workspace))) a.nsplit = 1;
+    if (a.nsplit > 1) {
+        a.part_o = reinterpret_cast<float*>(o.workspace);
+        a.part_ml = a.part_o + (size_t)a.nsplit * B * H * Nq * d;
+    }
     hipError_t e = gdn::launch_attn(a, reinterpret_cast<hipStream_t>(o.stream));
     if (e != hipSuccess) return fail(GDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return GDN_OK;
+}
+
+size_t gdn_attn_workspace_bytes(int B, int H, int Nq, int n_sink, int n_win, int n_cur, int d,
+                                const gdn_opts* opts) {
+    (void)opts;
+    if (B <= 0 || H <= 0 || Nq <= 0 || n_sink < 0 || n_win < 0 || n_cur < 0 || !gdn::attn_supported(d)) return 0;
+    const int ns[3] = {n_sink, n_win, n_cur};
+    return gdn::attn_workspace(B, H, Nq, d, gdn::attn_splits(B, H, Nq, ns));
 }
 
 size_t gdn_bidir_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, const gdn_opts* opts) {

@@ -25,6 +25,11 @@
 //                        exactly while it is transposed into LDS
 // The output is O = (O^T)^T / l: lane (g, c) writes four consecutive columns
 // of query c, one 16-byte store in fp32.
+// Few heads leave compute units idle and a lone wave per SIMD waiting on its
+// own latencies; the key tiles are then split into up to four ranges, one
+// workgroup each, which store their unnormalised output with the running max
+// and sum of every query, and gdn_attn_combine_kernel merges the ranges with
+// the weights exp2(m_s - max_s m_s) (the log-sum-exp identity).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -113,14 +118,16 @@ __global__ __launch_bounds__(256, 2) void gdn_attn_kernel(AttnArgs p) {
     const int lc = lane & 15, lg = lane >> 4;
     const int Nq = p.Nq;
     const int nqb = (Nq + AQ - 1) / AQ;
+    const int nsplit = p.nsplit;
     int wg = blockIdx.x;
     {
         // the query blocks of one head read the same keys: keep them on one XCD
         const int w8 = (int)gridDim.x / 8 * 8;
         if (wg < w8) wg = (wg % 8) * (w8 / 8) + wg / 8;
     }
-    const int qblk = uniform(wg % nqb);
-    const int bh = uniform(wg / nqb);
+    const int sp = uniform(wg % nsplit);               // key range of this workgroup
+    const int qblk = uniform((wg / nsplit) % nqb);
+    const int bh = uniform(wg / nsplit / nqb);
     const int q0 = qblk * AQ + 32 * wave;          // this wave's first query
 
     const rsrc_t rq = make_rsrc(reinterpret_cast<const uint16_t*>(p.q) + (size_t)bh * Nq * D,
@@ -131,6 +138,7 @@ __global__ __launch_bounds__(256, 2) void gdn_attn_kernel(AttnArgs p) {
     // tiles of each segment; tile t of the walk lies in segment seg at key base
     const int nt0 = (p.n[0] + AK - 1) / AK, nt1 = (p.n[1] + AK - 1) / AK, nt2 = (p.n[2] + AK - 1) / AK;
     const int ntiles = nt0 + nt1 + nt2;
+    const int t_lo = ntiles * sp / nsplit, t_hi = ntiles * (sp + 1) / nsplit;
     auto locate = [&](int t, int& seg, int& base) {
         if (t < nt0) { seg = 0; base = t * AK; }
         else if (t < nt0 + nt1) { seg = 1; base = (t - nt0) * AK; }
@@ -207,14 +215,14 @@ __global__ __launch_bounds__(256, 2) void gdn_attn_kernel(AttnArgs p) {
     float m[2] = {-1e30f, -1e30f}, l[2] = {0.f, 0.f};
     const float cs = p.scale * 1.4426950408889634f;
 
-    if (ntiles > 0) {
-        load_tile(0);
+    if (t_lo < t_hi) {
+        load_tile(t_lo);
         store_tile(0);
     }
     __syncthreads();
-    for (int t = 0; t < ntiles; ++t) {
-        if (t + 1 < ntiles) load_tile(t + 1);
-        const int b = t & 1;
+    for (int t = t_lo; t < t_hi; ++t) {
+        if (t + 1 < t_hi) load_tile(t + 1);
+        const int b = (t - t_lo) & 1;
         int seg, base;
         locate(t, seg, base);
         const int kmax = min(AK, (seg == 0 ? p.n[0] : seg == 1 ? p.n[1] : p.n[2]) - base);
@@ -285,10 +293,28 @@ __global__ __launch_bounds__(256, 2) void gdn_attn_kernel(AttnArgs p) {
                 O[db][1] = OpF16::mma(a, pf[1][k2], O[db][1]);
             }
 
-        if (t + 1 < ntiles) store_tile(b ^ 1);   // copy b ^ 1 was last read before the previous barrier
+        if (t + 1 < t_hi) store_tile(b ^ 1);     // copy b ^ 1 was last read before the previous barrier
         __syncthreads();
     }
 
+    if (nsplit > 1) {
+        // ---- one key range: unnormalised O and (m, l) per query, for the combine
+        const size_t prow = ((size_t)sp * p.B * p.H + bh) * Nq;          // first row of this head's part
+        const rsrc_t rpo = make_rsrc(p.part_o + prow * D, (unsigned)Nq * D * 4u);
+        const rsrc_t rpm = make_rsrc(p.part_ml + prow * 2, (unsigned)Nq * 8u);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            const float ls = xlane_sum4(l[qb]);
+            const int row = q0 + 16 * qb + lc;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+                buf_store16(rpo, (unsigned)(row * D + 16 * db + 4 * lg) * 4u, __builtin_bit_cast(uint4, O[db][qb]));
+            if (lg == 0)
+                buf_store8(rpm, (unsigned)row * 8u, make_uint2(__builtin_bit_cast(uint32_t, m[qb]),
+                                                               __builtin_bit_cast(uint32_t, ls)));
+        }
+        return;
+    }
     // ---- O = (O^T)^T / l: lane (g, c) holds columns 16 db + 4 g + i of query c
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
@@ -309,17 +335,72 @@ __global__ __launch_bounds__(256, 2) void gdn_attn_kernel(AttnArgs p) {
     }
 }
 
+// Merge of the key ranges: thread = (row, four columns).  With m_s the
+// running max (exp2 domain) and l_s the sum of range s,
+//   O = sum_s 2^(m_s - m) O_s / sum_s 2^(m_s - m) l_s,   m = max_s m_s.
+template <int D>
+__global__ __launch_bounds__(256) void gdn_attn_combine_kernel(AttnArgs p) {
+    const long long rows = (long long)p.B * p.H * p.Nq;
+    const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= rows * (D / 4)) return;
+    const long long row = idx / (D / 4);
+    const int c = (int)(idx % (D / 4)) * 4;
+    float mx = -INFINITY;
+    for (int s = 0; s < p.nsplit; ++s) mx = fmaxf(mx, p.part_ml[((size_t)s * rows + row) * 2]);
+    f32x4 acc = zero4();
+    float L = 0.f;
+    for (int s = 0; s < p.nsplit; ++s) {
+        const float* ml = p.part_ml + ((size_t)s * rows + row) * 2;
+        const float w = __builtin_amdgcn_exp2f(ml[0] - mx);
+        L += w * ml[1];
+        acc += w * *reinterpret_cast<const f32x4*>(p.part_o + ((size_t)s * rows + row) * D + c);
+    }
+    const f32x4 o = acc * (1.f / L);
+    if (p.out_bf16) {
+        const u16x8 w = pack8_bf16(o, o);
+        const uint4 u = __builtin_bit_cast(uint4, w);
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + row * D + c) = make_uint2(u.x, u.y);
+    } else {
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + row * D + c) = o;
+    }
+}
+
 }  // namespace
 
 bool attn_supported(int d) { return d == 64 || d == 128; }
 
+int attn_splits(int B, int H, int Nq, const int n[3]) {
+    const long long wgs = (long long)B * H * ((Nq + 127) / 128);
+    const int ntiles = (n[0] + AK - 1) / AK + (n[1] + AK - 1) / AK + (n[2] + AK - 1) / AK;
+    // about two resident workgroups per compute unit (512 in all), rounded to
+    // the nearest count: measured best at 2 ranges for 336 query blocks and 3
+    // for 168 (4 ranges there run 2.6 workgroups per unit, in uneven rounds)
+    int ns = wgs > 0 ? (int)((512 + wgs / 2) / wgs) : 1;
+    ns = ns > 4 ? 4 : ns;
+    const int cap = ntiles / 8;                                  // at least 8 tiles per range
+    if (ns > cap) ns = cap;
+    return ns < 1 ? 1 : ns;
+}
+
+size_t attn_workspace(int B, int H, int Nq, int d, int nsplit) {
+    return nsplit > 1 ? (size_t)nsplit * B * H * Nq * (d + 2) * 4 : 0;
+}
+
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
-    const int nqb = (a.Nq + AQ - 1) / AQ;
-    const dim3 grid((unsigned)(a.B * a.H * nqb)), block(256);
+    const int nqb = (a.Nq + 127) / 128;
+    const dim3 grid((unsigned)(a.B * a.H * nqb * a.nsplit)), block(256);
     if (a.d == 64)
         hipLaunchKernelGGL(gdn_attn_kernel<64>, grid, block, 0, s, a);
     else
         hipLaunchKernelGGL(gdn_attn_kernel<128>, grid, block, 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.nsplit <= 1) return e;
+    const long long threads = (long long)a.B * a.H * a.Nq * (a.d / 4);
+    const dim3 cgrid((unsigned)((threads + 255) / 256));
+    if (a.d == 64)
+        hipLaunchKernelGGL(gdn_attn_combine_kernel<64>, cgrid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL(gdn_attn_combine_kernel<128>, cgrid, block, 0, s, a);
     return hipGetLastError();
 }
 

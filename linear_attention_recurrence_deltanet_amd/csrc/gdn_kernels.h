@@ -76,8 +76,15 @@ struct AttnArgs {
     int B, H, Nq, d;
     float scale;
     int out_bf16;
+    int nsplit;              // key ranges (1: no split)
+    float* part_o;           // nsplit > 1: [nsplit][B*H*Nq][d] unnormalised outputs
+    float* part_ml;          // nsplit > 1: [nsplit][B*H*Nq][2] running max (exp2 domain), sum
 };
 bool attn_supported(int d);
+// Key ranges the launch splits into (1 when the workgroups already fill the
+// chip), and the workspace they need.
+int attn_splits(int B, int H, int Nq, const int n[3]);
+size_t attn_workspace(int B, int H, int Nq, int d, int nsplit);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
 
 }  // namespace gdn

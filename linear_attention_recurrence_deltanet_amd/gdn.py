@@ -21,6 +21,7 @@ GDN_BF16, GDN_F32 = 0, 1
 # every exported entry point of include/gdn.h
 EXPORTS = ("gdn_default_opts", "gdn_fwd_chunked", "gdn_fwd_step", "gdn_fwd_bidir",
            "gdn_workspace_bytes", "gdn_bidir_workspace_bytes", "gdn_attn_sink_window",
+           "gdn_attn_workspace_bytes",
            "gdn_strerror", "gdn_last_error", "gdn_version")
 
 
@@ -70,6 +71,8 @@ def load(path: str = LIB_PATH):
     lib.gdn_attn_sink_window.argtypes = [vp, vp, vp, i, vp, vp, i, vp, vp, i, vp, i, i, i, i,
                                          ctypes.c_float, ctypes.POINTER(GdnOpts)]
     lib.gdn_attn_sink_window.restype = i
+    lib.gdn_attn_workspace_bytes.argtypes = [i, i, i, i, i, i, i, ctypes.POINTER(GdnOpts)]
+    lib.gdn_attn_workspace_bytes.restype = ctypes.c_size_t
     lib.gdn_default_opts.argtypes = [ctypes.POINTER(GdnOpts)]
     lib.gdn_default_opts.restype = None
     lib.gdn_strerror.argtypes = [i]
@@ -234,10 +237,12 @@ def fwd_bidir(q, k, v, alpha, beta, state_in=None, chunk: int = 0, *, out=None, 
 
 
 def attn_sink_window(q, k_sink, v_sink, k_win, v_win, k_cur, v_cur, scale=None, *, out=None,
-                     out_dtype=torch.float32, stream=None):
+                     out_dtype=torch.float32, stream=None, workspace=None):
     """gdn_attn_sink_window: softmax(scale q K^T) V over [sink; window; current]
     keys.  q [B,H,Nq,d], k_x/v_x [B,H,n_x,d] bf16 device tensors (n_x may be
-    0).  scale None: 1/sqrt(d).  Returns out [B,H,Nq,d]."""
+    0).  scale None: 1/sqrt(d).  workspace: None allocates what the split of
+    the key range needs, False passes none (unsplit), or a uint8 device
+    tensor.  Returns out [B,H,Nq,d]."""
     B, H, Nq, d = q.shape
     segs = []
     for name, k, v in (("sink", k_sink, v_sink), ("win", k_win, v_win), ("cur", k_cur, v_cur)):
@@ -251,7 +256,13 @@ def attn_sink_window(q, k_sink, v_sink, k_win, v_win, k_cur, v_cur, scale=None, 
         raise ValueError("q must be a contiguous bf16 device tensor")
     if out is None:
         out = torch.empty(B, H, Nq, d, dtype=out_dtype, device=q.device)
-    opts = make_opts(q.dtype, out.dtype, stream=stream)
+    if workspace is None:
+        n = int(load().gdn_attn_workspace_bytes(B, H, Nq, k_sink.shape[2], k_win.shape[2],
+                                                k_cur.shape[2], d, None))
+        workspace = torch.empty(n, dtype=torch.uint8, device=q.device) if n > 0 else None
+    elif workspace is False:
+        workspace = None
+    opts = make_opts(q.dtype, out.dtype, stream=stream, workspace=workspace)
     args = []
     for k, v, n in segs:
         args += [_ptr(k) if n else None, _ptr(v) if n else None, int(n)]

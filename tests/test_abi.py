@@ -172,6 +172,16 @@ def test_attn_empty_segments_and_dtype(lib):
     assert _attn(lib, opts=ctypes.byref(o)) == gdn.GDN_ERR_UNSUPPORTED
 
 
+def test_attn_workspace_query(lib):
+    # few query blocks: the key range splits (2 ranges for 16 heads of 64, 3 for 8 of 128)
+    assert lib.gdn_attn_workspace_bytes(1, 16, 2640, 2640, 2640, 2640, 64, None) == 2 * 16 * 2640 * 66 * 4
+    assert lib.gdn_attn_workspace_bytes(1, 8, 2640, 2640, 2640, 2640, 128, None) == 3 * 8 * 2640 * 130 * 4
+    # enough query blocks, or too few key tiles: no split, no workspace
+    assert lib.gdn_attn_workspace_bytes(8, 32, 4096, 2640, 2640, 2640, 64, None) == 0
+    assert lib.gdn_attn_workspace_bytes(1, 1, 64, 64, 0, 64, 64, None) == 0
+    assert lib.gdn_attn_workspace_bytes(1, 16, 2640, 2640, 2640, 2640, 96, None) == 0
+
+
 # last: it reloads the binding module (the fixture's library keeps the old types)
 def test_binding_fails_loudly_without_library(tmp_path):
     import importlib
