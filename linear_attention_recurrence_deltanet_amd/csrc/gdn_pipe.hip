@@ -951,7 +951,13 @@ __global__ __launch_bounds__(1024) void gdn_pipe_fix_kernel(WalkArgs p) {
     constexpr int PPG = RG * 16 * DK * 2 / 16;          // 16-byte pieces of Phi per correction group
     constexpr int D = DK == 64 ? 4 : 3;                 // maps in flight
     static_assert(NDB % RG == 0 && RG % NB == 0 && PPG <= 1024 && APC % 512 == 0, "fix layout");
-    __shared__ uint4 Ast[2][APC];
+    // d_k = 128: A_s of the map being folded (two copies); d_k = 64: rings of
+    // FR maps (A_s and the tile's B_s) staged for the four column owners
+    constexpr int FR = 2;                               // maps per staging group (d_k = 64)
+    constexpr int BPC = DK * 64 / 4;                    // 16-byte pieces of a map's B_s for 64 columns
+    __shared__ uint4 Ast[2][DK == 64 ? 1 : APC];
+    __shared__ uint4 As2[2][DK == 64 ? FR * APC : 1];
+    __shared__ uint4 Bs2[2][DK == 64 ? FR * BPC : 1];
     __shared__ uint4 Mf[2][KS_D][4][64];                // M as fp16 B fragments [k-step][column group][lane]
     __shared__ uint4 Phs[2][PPG];
 
@@ -1035,6 +1041,95 @@ __global__ __launch_bounds__(1024) void gdn_pipe_fix_kernel(WalkArgs p) {
     cload(ph[0], ov[0], gv2[0], av2[0], 0);
     cload(ph[1], ov[1], gv2[1], av2[1], 1);
 
+    F mI[KS_D];
+    if constexpr (DK == 64) {
+    // ---- fold by column owners: waves 0..3 (column group cg = wave) keep all
+    // d_k rows of their 16 columns in fp32, so the state needs no exchange
+    // between waves (its operand fragments come from the owner's own
+    // accumulators); all 16 waves stage the maps -- A_s and this tile's B_s --
+    // into LDS, FR maps per barrier.  The last segment's own map is staged as
+    // one more map and applied after M_in is published.
+    const bool owner = wave < 4;
+    const int nst = seg + (last ? 1 : 0);
+    const int ngrp = (nst + FR - 1) / FR;
+    constexpr int SA = FR * APC / 1024, SB = FR * BPC / 1024;   // pieces per thread per group
+    static_assert(FR * APC % 1024 == 0 && FR * BPC % 1024 == 0, "staging split");
+    f32x4 Mw[NDB];
+#pragma unroll
+    for (int ib = 0; ib < NDB; ++ib) Mw[ib] = zero4();
+    if (owner && has_in) {
+        const float* sp = p.snap + (size_t)bh * DK * dv + col;
+#pragma unroll
+        for (int ib = 0; ib < NDB; ++ib)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Mw[ib][i] = sp[(16 * ib + 4 * lg + i) * dv];
+    }
+    uint4 sa[SA], sb[SB];
+    auto sload = [&](int g) {
+#pragma unroll
+        for (int j = 0; j < SA; ++j) {
+            const int e = tid + 1024 * j, i = g * FR + e / APC;
+            sa[j] = buf_load16(rA, (g < ngrp && i < nst) ? (unsigned)((i * APC + e % APC) * 16) : kOffNone);
+        }
+#pragma unroll
+        for (int j = 0; j < SB; ++j) {
+            const int e = tid + 1024 * j, i = g * FR + e / BPC;
+            sb[j] = buf_load16(rB, (g < ngrp && i < nst)
+                                       ? (unsigned)(i * DK * dv * 4 + (vt * 4 * NDB * 64 + e % BPC) * 16) : kOffNone);
+        }
+    };
+    auto sstore = [&](int slot) {
+#pragma unroll
+        for (int j = 0; j < SA; ++j) As2[slot][tid + 1024 * j] = sa[j];
+#pragma unroll
+        for (int j = 0; j < SB; ++j) Bs2[slot][tid + 1024 * j] = sb[j];
+    };
+    // M <- A M + B on an owner: operand fragments of the old M first
+    auto oapply = [&](int slot, int r) {
+        F mB[KS_D];
+#pragma unroll
+        for (int ks = 0; ks < KS_D; ++ks) mB[ks] = Op::b_acc(Mw, ks);
+#pragma unroll
+        for (int ib = 0; ib < NDB; ++ib) {
+            f32x4 acc = __builtin_bit_cast(f32x4, Bs2[slot][r * BPC + (cg * NDB + ib) * 64 + lane]);
+#pragma unroll
+            for (int ks = 0; ks < KS_D; ++ks)
+                acc = Op::mma(__builtin_bit_cast(F, As2[slot][r * APC + (ib * KS_D + ks) * 64 + lane]), mB[ks], acc);
+            Mw[ib] = acc;
+        }
+    };
+    sload(0);
+    sstore(0);
+    sload(1);
+    __syncthreads();
+    for (int g = 0; g < ngrp; ++g) {
+        if (owner) {
+#pragma unroll
+            for (int r = 0; r < FR; ++r)
+                if (g * FR + r < seg) oapply(g & 1, r);
+        }
+        // copy (g + 1) & 1 was last read in group g - 1, before the previous barrier
+        if (g + 1 < ngrp) sstore((g + 1) & 1);
+        sload(g + 2);
+        __syncthreads();
+    }
+    if (owner) {
+#pragma unroll
+        for (int ks = 0; ks < KS_D; ++ks) Mf[0][ks][cg][lane] = __builtin_bit_cast(uint4, Op::b_acc(Mw, ks));
+        if (last) {
+            // the own map sits in the last group's copy, which no later group overwrote
+            oapply((ngrp - 1) & 1, seg % FR);
+            float* sp = p.state_out + (size_t)bh * DK * dv + col;
+#pragma unroll
+            for (int ib = 0; ib < NDB; ++ib)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sp[(16 * ib + 4 * lg + i) * dv] = Mw[ib][i];
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < KS_D; ++ks) mI[ks] = __builtin_bit_cast(F, Mf[0][ks][cg][lane]);
+    } else {
     // ---- fold: maps 0 .. seg-1, D in flight; the last segment's own map
     // (state_out) is loaded from the start
     const int nfold = seg;
@@ -1109,7 +1204,6 @@ __global__ __launch_bounds__(1024) void gdn_pipe_fix_kernel(WalkArgs p) {
     put_m(nfold & 1);
     if (last) put_a(ral, nfold & 1);
     __syncthreads();
-    F mI[KS_D];
     get_m(mI, nfold & 1);
     if (last) {
         apply(mI, nfold & 1, rbl);
@@ -1118,6 +1212,7 @@ __global__ __launch_bounds__(1024) void gdn_pipe_fix_kernel(WalkArgs p) {
         for (int r = 0; r < RB; ++r)
 #pragma unroll
             for (int i = 0; i < 4; ++i) sp[(16 * (rg * RB + r) + 4 * lg + i) * dv] = Macc[r][i];
+    }
     }
 
     // ---- outputs of the segment: O += Phi M_in, formed transposed
