@@ -226,8 +226,8 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build runs on exactly one GPU; a multi-GPU figure is not "
-              "part of it (heads and value columns shard with no communication).",
+        print("bench.py measures one GPU only; a multi-GPU figure is not part of it "
+              "(heads and value columns shard with no communication).",
               file=sys.stderr)
         sys.exit(2)
 
