@@ -85,3 +85,10 @@ def test_attn_split_key_ranges_match_unsplit(gdn_lib, oracle_mod):
     # each range rounds P to fp16 against its own running max, so the two
     # differ at that rounding level (both meet the bar against the oracle)
     assert rel < 5e-4
+
+
+def test_attn_batch_of_two(gdn_lib, oracle_mod):
+    # B = 2: heads of both batch entries, split and unsplit
+    wl = ATTN_WORKLOADS["attn_chunk_h16_d64"]
+    _run(gdn_lib, oracle_mod, wl, B=2, H=2, Nq=200, n_sink=600, n_win=0, n_cur=200, what="batch2")
+    _run(gdn_lib, oracle_mod, wl, B=2, H=3, Nq=129, n_sink=64, n_win=64, n_cur=129, what="batch2-small")

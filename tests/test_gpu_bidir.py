@@ -129,3 +129,18 @@ def test_bidir_empty_sequence(gdn_lib):
     torch.cuda.synchronize()
     assert out.shape == (1, 2, 0, 64)
     assert torch.equal(st, s0)
+
+
+@pytest.mark.parametrize("chunk", [32, 64])
+def test_bidir_gates_fp32_walker(gdn_lib, oracle_mod, chunk):
+    # fp32 inputs: the reverse walk, the accumulating store and both gates on the fp32 walker
+    _run(gdn_lib, oracle_mod, WORKLOADS["tiny_f32"], 2, T=200, chunk=chunk, gates=True,
+         what="fp32-gates")
+
+
+def test_bidir_gates_single_pass(gdn_lib, oracle_mod):
+    # 128-token chunks: the single-pass kernel, reversed and accumulating, with both gates
+    _run(gdn_lib, oracle_mod, WORKLOADS["stream_chunk_h16_d64"], 1, H=3, T=777, chunk=128, gates=True,
+         what="single-gates")
+    _run(gdn_lib, oracle_mod, WORKLOADS["stream_chunk_h16_d64"], 1, H=3, T=777, chunk=128, gates=True,
+         out_dtype=torch.bfloat16, what="single-gates-bf16")
