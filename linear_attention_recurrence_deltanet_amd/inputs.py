@@ -170,3 +170,78 @@ def make_attn_call(wl: AttnWorkload, call: int = 0, *, B: Optional[int] = None, 
         d["v_" + name] = r(n)
     return d
 
+
+
+# ---------------------------------------------------------------------------
+# Frame-wise Gated DeltaNet with a normalised readout (SANA-Streaming section
+# 2.1, "Frame-wise Gated DeltaNet"): a call holds F latent frames of N tokens;
+# one decay per frame, one write strength per token, an output gate per
+# element.  The readout divides by z . q, so the features must keep that
+# denominator away from zero: q and k are drawn non-negative (absolute values
+# of standard normal draws, then unit rows in fp32), as feature maps of
+# normalised linear attention are; with sign-symmetric draws z . q takes
+# either sign.
+#
+#   q, k = unit rows of |N(0, 1)|;  v ~ N(0, 1)
+#   alpha [F]   = exp(-softplus(N(mu_a, sigma_a)))
+#   beta  [F*N] = sigmoid(N(mu_b, sigma_b))
+#   out_gate    = sigmoid(N(0, 1))
+#   zero numerator and denominator states before the first call.
+
+@dataclasses.dataclass(frozen=True)
+class FrameWorkload:
+    name: str
+    B: int
+    H: int
+    F: int              # frames per call
+    N: int              # tokens per frame
+    dk: int
+    dv: int
+    chunk: int
+    calls: int          # successive calls with both states carried
+    alpha_mu: float
+    alpha_sigma: float
+    beta_mu: float
+    beta_sigma: float
+    seed: int
+
+    @property
+    def T(self) -> int:
+        return self.F * self.N
+
+    def replace(self, **kw) -> "FrameWorkload":
+        return dataclasses.replace(self, **kw)
+
+
+FRAME_WORKLOADS = {
+    # one streaming chunk of 3 latent frames x 880 tokens, 16 heads of 64
+    "frame_stream_h16_d64": FrameWorkload("frame_stream_h16_d64", 1, 16, 3, 880, 64, 64, 64, 1,
+                                          0.0, 1.0, 0.0, 1.0, 3001),
+    # 20 successive streaming chunks, 16 heads of 128, both states carried
+    "frame_rollout_h16_d128": FrameWorkload("frame_rollout_h16_d128", 1, 16, 3, 880, 128, 128, 64, 20,
+                                            0.0, 1.0, 0.0, 1.0, 3002),
+}
+
+
+def make_frame_call(wl: FrameWorkload, call: int = 0, *, B: Optional[int] = None,
+                    H: Optional[int] = None, F: Optional[int] = None, N: Optional[int] = None):
+    """Inputs of call number `call` (bf16 CPU tensors): q, k [B,H,F*N,dk],
+    v and out_gate [B,H,F*N,dv], alpha [B,H,F], beta [B,H,F*N]; sizes may be
+    overridden."""
+    B = wl.B if B is None else B
+    H = wl.H if H is None else H
+    F = wl.F if F is None else F
+    N = wl.N if N is None else N
+    T = F * N
+    g = torch.Generator(device="cpu")
+    g.manual_seed(wl.seed * 100003 + call)
+    f32, bf = torch.float32, torch.bfloat16
+    q = _unit_rows(torch.randn(B, H, T, wl.dk, generator=g, dtype=f32).abs())
+    k = _unit_rows(torch.randn(B, H, T, wl.dk, generator=g, dtype=f32).abs())
+    v = torch.randn(B, H, T, wl.dv, generator=g, dtype=f32)
+    za = torch.randn(B, H, F, generator=g, dtype=f32) * wl.alpha_sigma + wl.alpha_mu
+    zb = torch.randn(B, H, T, generator=g, dtype=f32) * wl.beta_sigma + wl.beta_mu
+    og = torch.sigmoid(torch.randn(B, H, T, wl.dv, generator=g, dtype=f32))
+    return dict(q=q.to(bf), k=k.to(bf), v=v.to(bf),
+                alpha=torch.exp(-torch.nn.functional.softplus(za)).to(bf),
+                beta=torch.sigmoid(zb).to(bf), out_gate=og.to(bf))

@@ -11,7 +11,9 @@ only compiles it with gcc and marshals numpy arrays through ctypes.
 Parity pins: ``tests/test_oracle_pins.py`` and ``tests/golden/``.
 
 ``attn_sink_window`` (from ``attention.py``) is the oracle of the softmax
-attention block with a sink chunk and a recent window.
+attention block with a sink chunk and a recent window; ``gdn_framewise``
+(from ``framewise.py``) that of frame-wise Gated DeltaNet with a normalised
+readout.
 """
 from __future__ import annotations
 
@@ -22,6 +24,7 @@ import subprocess
 import numpy as np
 
 from .attention import attn_sink_window  # noqa: F401
+from .framewise import gdn_framewise  # noqa: F401
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "gdn_oracle.c")

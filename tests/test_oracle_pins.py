@@ -485,3 +485,120 @@ def test_attn_matches_library_attention(oracle_mod):
     V = torch.cat([t(vs), t(vw), t(vc)], dim=2)
     ref = torch.nn.functional.scaled_dot_product_attention(t(q), K, V).numpy()
     np.testing.assert_allclose(out, ref, rtol=1e-10, atol=1e-12)
+
+
+# ---- frame-wise GDN with a normalised readout (SANA-Streaming section 2.1,
+# "Frame-wise Gated DeltaNet"; appendix G.3-G.5): one decay per frame, applied
+# once before the frame's first write; a denominator state driven by a value
+# of constant 1; output = numerator / denominator, then the output gate
+
+def _frame_case(rng, B=1, H=2, F=3, N=5, dk=6, dv=4, state=True):
+    T = F * N
+    q = np.abs(rng.standard_normal((B, H, T, dk)))     # non-negative features
+    k = np.abs(rng.standard_normal((B, H, T, dk)))
+    v = rng.standard_normal((B, H, T, dv))
+    a = np.exp(-np.log1p(np.exp(rng.standard_normal((B, H, F)))))
+    b = 1.0 / (1.0 + np.exp(-rng.standard_normal((B, H, T))))
+    s = rng.standard_normal((B, H, dk, dv)) * 0.3 if state else None
+    z = np.abs(rng.standard_normal((B, H, dk))) * 0.5 + 0.2 if state else None
+    return q, k, v, a, b, s, z
+
+
+def test_framewise_equals_tokenwise_scans(oracle_mod):
+    """Against the C token-wise oracle, an independent loop: the numerator is
+    the token-wise scan with decay alpha_f on each frame's first token and 1
+    elsewhere; the denominator is the same scan over a single value column of
+    ones started from z_in; out = numerator / denominator * gate."""
+    rng = np.random.default_rng(51)
+    q, k, v, a, b, s, z = _frame_case(rng)
+    F, N = a.shape[-1], q.shape[2] // a.shape[-1]
+    g = 1.0 / (1.0 + np.exp(-rng.standard_normal(v.shape)))
+    out, s_out, z_out = oracle_mod.gdn_framewise(q, k, v, a, b, N, s, z, out_gate=g)
+    a_tok = np.ones(b.shape)
+    a_tok[:, :, ::N] = a
+    num, s_ref = oracle_mod.gdn_fwd(q, k, v, a_tok, b, s)
+    den, z_ref = oracle_mod.gdn_fwd(q, k, np.ones(v.shape[:-1] + (1,)), a_tok, b, z[..., None])
+    np.testing.assert_allclose(out, num / den * g, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(s_out, s_ref, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(z_out, z_ref[..., 0], rtol=1e-12, atol=1e-13)
+
+
+def test_framewise_beta_zero_readout_is_decay_free(oracle_mod):
+    """beta = 0: nothing is written, both states only decay by the product of
+    the frames' alphas, and the decay cancels in the ratio: every output is
+    (M_in^T q^) / (z_in . q^)."""
+    rng = np.random.default_rng(52)
+    q, k, v, a, b, s, z = _frame_case(rng)
+    out, s_out, z_out = oracle_mod.gdn_framewise(q, k, v, a, np.zeros_like(b), q.shape[2] // a.shape[-1], s, z)
+    qh = unit(q)
+    ref = np.einsum("bhij,bhti->bhtj", s, qh) / np.einsum("bhi,bhti->bht", z, qh)[..., None]
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-13)
+    pa = a.prod(axis=-1)
+    np.testing.assert_allclose(s_out, pa[..., None, None] * s, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(z_out, pa[..., None] * z, rtol=1e-13, atol=1e-15)
+
+
+def test_framewise_constant_values_read_back(oracle_mod):
+    """From zero states, a value that is the same vector c at every token
+    drives every numerator column as c_j times the denominator: out = c."""
+    rng = np.random.default_rng(53)
+    q, k, v, a, b, _, _ = _frame_case(rng, state=False)
+    c = rng.standard_normal(v.shape[-1])
+    out, _, _ = oracle_mod.gdn_framewise(q, k, np.broadcast_to(c, v.shape), a, b, q.shape[2] // a.shape[-1])
+    np.testing.assert_allclose(out, np.broadcast_to(c, out.shape), rtol=1e-11, atol=1e-12)
+
+
+def test_framewise_shift_equivariance(oracle_mod):
+    """Adding c to every value, and z_in c^T to the numerator state, adds c to
+    every output (the normalised readout is an affine average of values)."""
+    rng = np.random.default_rng(54)
+    q, k, v, a, b, s, z = _frame_case(rng)
+    N = q.shape[2] // a.shape[-1]
+    c = rng.standard_normal(v.shape[-1])
+    o1, s1, z1 = oracle_mod.gdn_framewise(q, k, v, a, b, N, s, z)
+    o2, s2, z2 = oracle_mod.gdn_framewise(q, k, v + c, a, b, N, s + z[..., None] * c, z)
+    np.testing.assert_allclose(o2, o1 + c, rtol=1e-10, atol=1e-11)
+    np.testing.assert_allclose(s2, s1 + z1[..., None] * c, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(z2, z1, rtol=0, atol=0)
+
+
+def test_framewise_orthonormal_keys_normalised_linear_attention(oracle_mod):
+    """Orthonormal keys, zero states: nothing is corrected, so each output is
+    the normalised linear attention sum_s w_s beta_s (k_s . q_t) v_s divided by
+    sum_s w_s beta_s (k_s . q_t), with w_s the product of the decays of the
+    frames after s's frame up to t's frame."""
+    rng = np.random.default_rng(55)
+    F, N, dk, dv = 3, 4, 12, 3
+    T = F * N
+    Qo, _ = np.linalg.qr(rng.standard_normal((dk, dk)))
+    k = Qo[:T][None, None]
+    q = np.abs(rng.standard_normal((1, 1, T, dk)))
+    v = rng.standard_normal((1, 1, T, dv))
+    a = rng.uniform(0.3, 0.9, (1, 1, F))
+    b = rng.uniform(0.2, 1.0, (1, 1, T))
+    out, _, _ = oracle_mod.gdn_framewise(q, k, v, a, b, N)
+    qh = unit(q)[0, 0]
+    ref = np.empty((T, dv))
+    for t in range(T):
+        ft = t // N
+        w = np.array([np.prod(a[0, 0, s // N + 1:ft + 1]) for s in range(t + 1)])
+        c = w * b[0, 0, :t + 1] * (k[0, 0, :t + 1] @ qh[t])
+        ref[t] = c @ v[0, 0, :t + 1] / c.sum()
+    np.testing.assert_allclose(out[0, 0], ref, rtol=1e-11, atol=1e-12)
+
+
+def test_framewise_split_across_calls(oracle_mod):
+    """Frames F1 then F - F1 in two calls with both states carried equal one
+    call over all F frames."""
+    rng = np.random.default_rng(56)
+    q, k, v, a, b, s, z = _frame_case(rng, F=4, N=3)
+    N, F1 = 3, 1
+    cut = F1 * N
+    o, s_out, z_out = oracle_mod.gdn_framewise(q, k, v, a, b, N, s, z)
+    o1, s1, z1 = oracle_mod.gdn_framewise(q[:, :, :cut], k[:, :, :cut], v[:, :, :cut], a[:, :, :F1],
+                                          b[:, :, :cut], N, s, z)
+    o2, s2, z2 = oracle_mod.gdn_framewise(q[:, :, cut:], k[:, :, cut:], v[:, :, cut:], a[:, :, F1:],
+                                          b[:, :, cut:], N, s1, z1)
+    np.testing.assert_allclose(np.concatenate([o1, o2], axis=2), o, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(s2, s_out, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(z2, z_out, rtol=1e-13, atol=1e-14)
