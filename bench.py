@@ -206,6 +206,110 @@ def bench_attention(args):
     print(json.dumps(res), flush=True)
 
 
+def bench_framewise(args):
+    """Frame-wise GDN with a normalised readout (gdn_fwd_framewise): one step
+    is one call over the workload's frames with both states carried in place.
+    The call is four launches (prologue, segment walk, correction, readout);
+    the roofline figure is the call's algorithmic bytes over its duration."""
+    import torch
+    import oracle
+    from linear_attention_recurrence_deltanet_amd import gdn
+    from linear_attention_recurrence_deltanet_amd.inputs import FRAME_WORKLOADS, make_frame_call, to_numpy64
+
+    wl = FRAME_WORKLOADS[args.workload]
+    chunk = args.chunk or wl.chunk
+    lib = gdn.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    out_dt = torch.float32 if args.out_dtype == "f32" else torch.bfloat16
+    out_bytes = 4 if args.out_dtype == "f32" else 2
+    bh, T = wl.B * wl.H, wl.T
+    # q, k, v, beta, output gate read once, out written once, alpha per frame,
+    # both fp32 states read and written once
+    alg_bytes = (bh * T * (2 * wl.dk * 2 + wl.dv * 2 + 2 + wl.dv * 2 + wl.dv * out_bytes)
+                 + bh * wl.F * 2 + 2 * bh * (wl.dk * wl.dv + wl.dk) * 4)
+    per_set = bh * T * (2 * wl.dk + 2 * wl.dv + 2) * 2
+    nsets = max(2, min(64, (2 * LLC_BYTES) // per_set + 1))
+    sets = [{k: v.to(dev).contiguous() for k, v in make_frame_call(wl, i).items()} for i in range(nsets)]
+    state = torch.zeros(wl.B, wl.H, wl.dk, wl.dv, device=dev)
+    z = torch.zeros(wl.B, wl.H, wl.dk, device=dev)
+    outs = [torch.empty(wl.B, wl.H, T, wl.dv, dtype=out_dt, device=dev) for _ in range(2)]
+    ws_bytes = int(lib.gdn_framewise_workspace_bytes(wl.B, wl.H, wl.F, wl.N, wl.dk, wl.dv, chunk, None))
+    workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    calls = []
+    for i, g in enumerate(sets):
+        o = gdn.make_opts(torch.bfloat16, out_dt, True, 1.0, 1e-6, stream, workspace, out_gate=g["out_gate"])
+        calls.append(((P(g["q"]), P(g["k"]), P(g["v"]), P(g["alpha"]), P(g["beta"]), P(state), P(z),
+                       P(outs[i % 2]), P(state), P(z), wl.B, wl.H, wl.F, wl.N, wl.dk, wl.dv, chunk),
+                      ctypes.pointer(o)))
+    fn = lambda c: lib.gdn_fwd_framewise(*c[0], c[1])
+    for i in range(args.warmup):
+        if fn(calls[i % nsets]) != 0:
+            raise RuntimeError(lib.gdn_last_error().decode())
+    torch.cuda.synchronize()
+    K = args.steps
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for i in range(K):
+        fn(calls[i % nsets])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = max(t0.elapsed_time(t1), wall * 1e3) / K
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for i in range(K):
+        ev[i][0].record(stream)
+        fn(calls[i % nsets])
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    per = [a.elapsed_time(b) for a, b in ev]
+    call_ms = statistics.mean(per)
+    achieved = alg_bytes / (call_ms * 1e-3) / 1e9
+    res = {
+        "metric": "frame-wise GDN (normalised readout) tokens/sec (bf16, 1 GPU) + % of HBM roofline vs oracle",
+        "value": wl.B * T / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "F": wl.F, "N": wl.N, "T": T,
+                   "dk": wl.dk, "dv": wl.dv, "chunk": chunk, "entry": "gdn_fwd_framewise",
+                   "out_dtype": args.out_dtype, "state": "fp32 numerator and denominator carried",
+                   "input_sets": nsets, "workspace_bytes": ws_bytes},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+        "kernel": {"avg_ms": call_ms, "p50_ms": statistics.median(per),
+                   "p99_ms": sorted(per)[min(len(per) - 1, int(0.99 * len(per)))],
+                   "algorithmic_bytes": alg_bytes, "launches_per_call": 4},
+    }
+    if not args.no_cpu:
+        names = ("q", "k", "v", "alpha", "beta", "out_gate")
+        cpu_sets = [[to_numpy64(make_frame_call(wl, i)[n]) for n in names] for i in range(2)]
+        n = 0
+        c0 = time.perf_counter()
+        ms = mz = None
+        while True:
+            q, k, v, a, b, og = cpu_sets[n % 2]
+            _, ms, mz = oracle.gdn_framewise(q, k, v, a, b, wl.N, ms, mz, out_gate=og)
+            n += 1
+            el = time.perf_counter() - c0
+            if el >= args.cpu_seconds:
+                break
+        res["cpu_baseline"] = {"value": n * wl.B * T / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                               "sample": f"{n} full calls of the same workload in {el:.1f} s, fp64 token "
+                                         f"loop vectorised over heads (numpy, one thread)"}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -231,9 +335,11 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    from linear_attention_recurrence_deltanet_amd.inputs import ATTN_WORKLOADS
+    from linear_attention_recurrence_deltanet_amd.inputs import ATTN_WORKLOADS, FRAME_WORKLOADS
     if args.workload in ATTN_WORKLOADS:
         return bench_attention(args)
+    if args.workload in FRAME_WORKLOADS:
+        return bench_framewise(args)
 
     import torch
     from linear_attention_recurrence_deltanet_amd import gdn

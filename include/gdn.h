@@ -33,7 +33,8 @@
  *    sequence across workgroups need a caller-owned workspace of
  *    gdn_workspace_bytes() bytes (opts->workspace); without one the
  *    single-pass path runs instead (same results to rounding).
- *    gdn_fwd_bidir needs the workspace of gdn_bidir_workspace_bytes().
+ *    gdn_fwd_bidir needs the workspace of gdn_bidir_workspace_bytes(),
+ *    gdn_fwd_framewise that of gdn_framewise_workspace_bytes().
  *  - Aliasing: only state_in and state_out may alias (in-place state update).
  *    Other buffers must not overlap.
  *  - Errors: argument errors return synchronously before any HIP call
@@ -52,7 +53,7 @@
 extern "C" {
 #endif
 
-#define GDN_VERSION 2
+#define GDN_VERSION 3
 
 typedef enum {
     GDN_OK = 0,
@@ -157,6 +158,54 @@ size_t gdn_bidir_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk,
  */
 size_t gdn_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk,
                            const gdn_opts* opts);
+
+/*
+ * gdn_fwd_framewise: frame-wise Gated DeltaNet with a normalised readout
+ * (SANA-Streaming, section 2.1 "Frame-wise Gated DeltaNet for Global
+ * Accumulated Memory": per head, F frames of N tokens, a decay gate alpha in
+ * R^F, a write gate beta in R^{F x N} and an output gate; a numerator state
+ * S^kv and a denominator state S^z updated frame by frame with the delta-rule
+ * correction and carried across chunks; appendix G.4 "Frame-wise delta-rule
+ * update" and G.5 "Normalized readout" survive as headings only).  This
+ * library reads them as follows, per (b, h), with unit-normalised q_t, k_t
+ * and t = f*N + n:
+ *
+ *   at n == 0:  S <- alpha_f * S,  z <- alpha_f * z    (once per frame)
+ *   S <- S (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+ *   z <- (I - beta_t k_t k_t^T) z + beta_t k_t          (a value of constant 1)
+ *   out_t = (S q_t) / (z . q_t)                          (then * out_gate)
+ *
+ * Layouts (row-major, device memory owned by the caller, bf16 inputs):
+ *   q, k        [B][H][F*N][dk]
+ *   v           [B][H][F*N][dv]
+ *   alpha       [B][H][F]        decay per frame (logits if opts->gate_logits)
+ *   beta        [B][H][F*N]      write strength (logits if opts->gate_logits)
+ *   state_in    [B][H][dk][dv]   fp32 (M = S^T, as in gdn_fwd_chunked), or NULL
+ *   z_in        [B][H][dk]       fp32 denominator state, or NULL (zero)
+ *   out         [B][H][F*N][dv]  opts->out_dtype; opts->out_gate [B][H][F*N][dv]
+ *   state_out   [B][H][dk][dv]   fp32, or NULL;  z_out [B][H][dk] fp32, or NULL
+ * dk and dv are 64 or 128; chunk 32 or 64 (0: 64); B*H*F*N*(dv+64) < 2^31.
+ * state_out may alias state_in and z_out z_in.  The denominator has no sign
+ * guarantee: the readout divides by it as it is (features that keep z . q
+ * positive, such as non-negative ones, are the caller's part); a zero
+ * denominator gives Inf/NaN like any division.
+ * Precision: the numerator and denominator are one token-wise scan (as in
+ * gdn_fwd_chunked) on values [v | 1] in fp32 outputs; the division and the
+ * gate are fp32 with one rounding to out_dtype.
+ * Needs a workspace (16-byte aligned) of gdn_framewise_workspace_bytes()
+ * bytes; returns GDN_ERR_ARG without it.  F == 0 copies the states.
+ */
+int gdn_fwd_framewise(const void* q, const void* k, const void* v,
+                      const void* alpha, const void* beta,
+                      const float* state_in, const float* z_in, void* out,
+                      float* state_out, float* z_out,
+                      int B, int H, int F, int N, int dk, int dv, int chunk,
+                      const gdn_opts* opts);
+
+/* Workspace (bytes) of gdn_fwd_framewise for this shape and chunk (0: 64);
+ * 0 for unsupported shapes. */
+size_t gdn_framewise_workspace_bytes(int B, int H, int F, int N, int dk, int dv, int chunk,
+                                     const gdn_opts* opts);
 
 /*
  * gdn_attn_sink_window: the softmax attention block of the hybrid model

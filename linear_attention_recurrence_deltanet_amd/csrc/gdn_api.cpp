@@ -300,6 +300,90 @@ size_t bidir_workspace(int B, int H, int T, int dk, int dv, int chunk, const gdn
     return T == 0 ? 0 : plane_bytes(B, H, T, dv) + pl.ws_bytes;
 }
 
+// Frame-wise scan with a normalised readout.  Workspace, each part 256-byte
+// aligned: decay per token [B*H][T] bf16, values [v | 1 0 ...] [B*H][T][dv+64]
+// bf16, state [M | z 0 ...] [B*H][dk][dv+64] fp32, scan outputs
+// [B*H][T][dv+64] fp32, then the scan's own split-sequence data.
+struct FrameLayout {
+    size_t alpha, vaug, state, oaug, seg, total;
+};
+
+size_t r256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+bool frame_shape_ok(int B, int H, int F, int N, int dk, int dv, int chunk) {
+    return B > 0 && H > 0 && F >= 0 && N > 0 && (dk == 64 || dk == 128) && (dv == 64 || dv == 128) &&
+           (chunk == 32 || chunk == 64) &&
+           (long long)B * H * F * N * (dv + 64) < 0x7fffffffLL;
+}
+
+FrameLayout frame_layout(int B, int H, int F, int N, int dk, int dv, int chunk) {
+    FrameLayout L{};
+    const size_t bh = (size_t)B * H, T = (size_t)F * N, dvp = (size_t)dv + 64;
+    L.alpha = 0;
+    L.vaug = L.alpha + r256(bh * T * 2);
+    L.state = L.vaug + r256(bh * T * dvp * 2);
+    L.oaug = L.state + r256(bh * dk * dvp * 4);
+    L.seg = L.oaug + r256(bh * T * dvp * 4);
+    L.total = L.seg + make_plan(0, B, H, (int)T, dk, (int)dvp, chunk).ws_bytes;
+    return L;
+}
+
+int run_framewise(const void* q, const void* k, const void* v, const void* alpha, const void* beta,
+                  const float* state_in, const float* z_in, void* out, float* state_out, float* z_out,
+                  int B, int H, int F, int N, int dk, int dv, int chunk, const gdn_opts* opts) {
+    g_last_error[0] = '\0';
+    gdn_opts o;
+    if (opts) o = *opts; else defaults(&o);
+    if (B <= 0 || H <= 0 || F < 0 || N <= 0) return fail(GDN_ERR_ARG, "B, H and N must be positive, F non-negative");
+    if (o.in_dtype != GDN_BF16) return fail(GDN_ERR_UNSUPPORTED, "frame-wise inputs must be bf16");
+    if (o.out_dtype != GDN_BF16 && o.out_dtype != GDN_F32) return fail(GDN_ERR_ARG, "bad out_dtype");
+    if (!frame_shape_ok(B, H, F, N, dk, dv, chunk))
+        return fail(GDN_ERR_UNSUPPORTED, "frame-wise scan: dk and dv 64 or 128, chunk 32 or 64, "
+                    "B*H*F*N*(dv+64) below 2^31");
+    const int T = F * N;
+    // the scan's own checks (pointers, alignment) on the caller's buffers
+    int st = validate(q, k, v, alpha, beta, state_in, out, state_out, B, H, T, dk, dv, chunk, o);
+    if (st != GDN_OK) return st;
+    if ((z_in && !aligned16(z_in)) || (z_out && !aligned16(z_out)))
+        return fail(GDN_ERR_ARG, "z_in and z_out must be 16-byte aligned");
+    const FrameLayout L = frame_layout(B, H, F, N, dk, dv, chunk);
+    if (!o.workspace || o.workspace_bytes < L.total || !aligned16(o.workspace)) {
+        char n[32];
+        snprintf(n, sizeof(n), "%zu", L.total);
+        return fail(GDN_ERR_ARG, "gdn_fwd_framewise needs a 16-byte aligned workspace of "
+                    "gdn_framewise_workspace_bytes() = %s bytes", n);
+    }
+    char* w = reinterpret_cast<char*>(o.workspace);
+    gdn::FrameArgs a;
+    a.v = v; a.alpha = alpha; a.state_in = state_in; a.z_in = z_in;
+    a.B = B; a.H = H; a.F = F; a.N = N; a.dk = dk; a.dv = dv;
+    a.gate_logits = o.gate_logits ? 1 : 0;
+    a.alpha_tok = w + L.alpha;
+    a.v_aug = w + L.vaug;
+    a.state_aug = reinterpret_cast<float*>(w + L.state);
+    a.out_aug = reinterpret_cast<const float*>(w + L.oaug);
+    a.out_gate = o.out_gate;
+    a.out = out;
+    a.out_bf16 = o.out_dtype == GDN_BF16;
+    a.state_out = state_out;
+    a.z_out = z_out;
+    hipStream_t stream = reinterpret_cast<hipStream_t>(o.stream);
+    hipError_t e = gdn::launch_frame_prep(a, stream);
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    gdn_opts os = o;
+    os.out_dtype = GDN_F32;
+    os.out_gate = nullptr;
+    os.workspace = w + L.seg;
+    os.workspace_bytes = o.workspace_bytes - L.seg;
+    const bool has_in = state_in || z_in, want = state_out || z_out;
+    st = scan(q, k, a.v_aug, a.alpha_tok, beta, has_in ? a.state_aug : nullptr, w + L.oaug,
+              want ? a.state_aug : nullptr, B, H, T, dk, dv + 64, chunk, os, 0, 0);
+    if (st != GDN_OK) return st;
+    e = gdn::launch_frame_readout(a, stream);
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return GDN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -396,6 +480,21 @@ size_t gdn_bidir_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk,
 
 size_t gdn_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, const gdn_opts* opts) {
     return workspace_for(B, H, T, dk, dv, chunk > 0 ? chunk : STEP_CHUNK, opts);
+}
+
+int gdn_fwd_framewise(const void* q, const void* k, const void* v, const void* alpha, const void* beta,
+                      const float* state_in, const float* z_in, void* out, float* state_out, float* z_out,
+                      int B, int H, int F, int N, int dk, int dv, int chunk, const gdn_opts* opts) {
+    return run_framewise(q, k, v, alpha, beta, state_in, z_in, out, state_out, z_out, B, H, F, N, dk, dv,
+                         chunk > 0 ? chunk : STEP_CHUNK, opts);
+}
+
+size_t gdn_framewise_workspace_bytes(int B, int H, int F, int N, int dk, int dv, int chunk,
+                                     const gdn_opts* opts) {
+    (void)opts;
+    if (chunk <= 0) chunk = STEP_CHUNK;
+    if (!frame_shape_ok(B, H, F, N, dk, dv, chunk)) return 0;
+    return frame_layout(B, H, F, N, dk, dv, chunk).total;
 }
 
 const char* gdn_strerror(int status) {

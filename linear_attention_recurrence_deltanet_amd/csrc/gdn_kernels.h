@@ -87,4 +87,29 @@ int attn_splits(int B, int H, int Nq, const int n[3]);
 size_t attn_workspace(int B, int H, int Nq, int d, int nsplit);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
 
+// Frame-wise scan with a normalised readout (gdn_frame.hip): the token-wise
+// scan runs on values [v | 1 0 ... 0] and state [M | z 0 ... 0] (dv + 64
+// columns) with the frame's decay on its first token; the prologue builds
+// these in the workspace, the epilogue divides by the denominator column,
+// applies the output gate and unpacks the state.  bf16 inputs.
+struct FrameArgs {
+    const void* v;           // [B*H][T][dv], T = F * N
+    const void* alpha;       // [B*H][F] decay per frame (logits if gate_logits)
+    const float* state_in;   // [B*H][dk][dv] or null
+    const float* z_in;       // [B*H][dk] or null
+    int B, H, F, N, dk, dv;
+    int gate_logits;
+    void* alpha_tok;         // workspace: [B*H][T] decay per token
+    void* v_aug;             // workspace: [B*H][T][dv + 64]
+    float* state_aug;        // workspace: [B*H][dk][dv + 64]
+    const float* out_aug;    // workspace: [B*H][T][dv + 64] outputs of the scan
+    const void* out_gate;    // [B*H][T][dv] or null
+    void* out;               // [B*H][T][dv] fp32 or bf16
+    int out_bf16;
+    float* state_out;        // [B*H][dk][dv] or null
+    float* z_out;            // [B*H][dk] or null
+};
+hipError_t launch_frame_prep(const FrameArgs& a, hipStream_t s);
+hipError_t launch_frame_readout(const FrameArgs& a, hipStream_t s);
+
 }  // namespace gdn

@@ -21,7 +21,7 @@ GDN_BF16, GDN_F32 = 0, 1
 # every exported entry point of include/gdn.h
 EXPORTS = ("gdn_default_opts", "gdn_fwd_chunked", "gdn_fwd_step", "gdn_fwd_bidir",
            "gdn_workspace_bytes", "gdn_bidir_workspace_bytes", "gdn_attn_sink_window",
-           "gdn_attn_workspace_bytes",
+           "gdn_attn_workspace_bytes", "gdn_fwd_framewise", "gdn_framewise_workspace_bytes",
            "gdn_strerror", "gdn_last_error", "gdn_version")
 
 
@@ -73,6 +73,10 @@ def load(path: str = LIB_PATH):
     lib.gdn_attn_sink_window.restype = i
     lib.gdn_attn_workspace_bytes.argtypes = [i, i, i, i, i, i, i, ctypes.POINTER(GdnOpts)]
     lib.gdn_attn_workspace_bytes.restype = ctypes.c_size_t
+    lib.gdn_fwd_framewise.argtypes = [vp] * 10 + [i] * 7 + [ctypes.POINTER(GdnOpts)]
+    lib.gdn_fwd_framewise.restype = i
+    lib.gdn_framewise_workspace_bytes.argtypes = [i] * 7 + [ctypes.POINTER(GdnOpts)]
+    lib.gdn_framewise_workspace_bytes.restype = ctypes.c_size_t
     lib.gdn_default_opts.argtypes = [ctypes.POINTER(GdnOpts)]
     lib.gdn_default_opts.restype = None
     lib.gdn_strerror.argtypes = [i]
@@ -269,3 +273,50 @@ def attn_sink_window(q, k_sink, v_sink, k_win, v_win, k_cur, v_cur, scale=None, 
     _check(load().gdn_attn_sink_window(_ptr(q), *args, _ptr(out), B, H, Nq, d,
                                        float(scale) if scale else 0.0, ctypes.byref(opts)))
     return out
+
+
+def framewise_workspace_bytes(B, H, F, N, dk, dv, chunk=0) -> int:
+    return int(load().gdn_framewise_workspace_bytes(B, H, F, N, dk, dv, chunk, None))
+
+
+def fwd_framewise(q, k, v, alpha, beta, frame_len: int, state_in=None, z_in=None, chunk: int = 0, *,
+                  out=None, state_out=None, z_out=None, out_dtype=torch.float32, qk_l2norm=True,
+                  eps=1e-6, stream=None, workspace=None, gate_logits: bool = False, out_gate=None):
+    """gdn_fwd_framewise: frame-wise gated delta rule with a normalised
+    readout over F = T / frame_len frames.  q, k [B,H,T,dk], v [B,H,T,dv],
+    beta [B,H,T] and alpha [B,H,F] bf16 device tensors; state_in [B,H,dk,dv]
+    and z_in [B,H,dk] fp32 or None.  workspace: None allocates
+    gdn_framewise_workspace_bytes, or a uint8 device tensor.
+    Returns (out, state_out, z_out); state_out may be state_in and z_out
+    z_in (in place)."""
+    for name, t in (("q", q), ("k", k), ("v", v), ("alpha", alpha), ("beta", beta)):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be a contiguous bf16 device tensor")
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    N = int(frame_len)
+    if N <= 0 or T % N:
+        raise ValueError("T must be a whole number of frames")
+    F = T // N
+    if k.shape != q.shape or v.shape[:3] != (B, H, T) or beta.shape != (B, H, T):
+        raise ValueError("shape mismatch between q, k, v, beta")
+    if alpha.shape != (B, H, F):
+        raise ValueError("alpha must be [B, H, F]")
+    for name, t, shp in (("state_in", state_in, (B, H, dk, dv)), ("z_in", z_in, (B, H, dk))):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != shp):
+            raise ValueError(f"{name} must be contiguous fp32 {list(shp)}")
+    _check_gate(out_gate, q, B, H, T, dv)
+    if out is None:
+        out = torch.empty(B, H, T, dv, dtype=out_dtype, device=q.device)
+    if state_out is None:
+        state_out = torch.empty(B, H, dk, dv, dtype=torch.float32, device=q.device)
+    if z_out is None:
+        z_out = torch.empty(B, H, dk, dtype=torch.float32, device=q.device)
+    if workspace is None:
+        n = framewise_workspace_bytes(B, H, F, N, dk, dv, chunk)
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    opts = make_opts(q.dtype, out.dtype, qk_l2norm, 1.0, eps, stream, workspace, gate_logits, out_gate)
+    _check(load().gdn_fwd_framewise(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                    _ptr(state_in), _ptr(z_in), _ptr(out), _ptr(state_out), _ptr(z_out),
+                                    B, H, F, N, dk, dv, int(chunk), ctypes.byref(opts)))
+    return out, state_out, z_out

@@ -226,8 +226,9 @@ FRAME_WORKLOADS = {
 def make_frame_call(wl: FrameWorkload, call: int = 0, *, B: Optional[int] = None,
                     H: Optional[int] = None, F: Optional[int] = None, N: Optional[int] = None):
     """Inputs of call number `call` (bf16 CPU tensors): q, k [B,H,F*N,dk],
-    v and out_gate [B,H,F*N,dv], alpha [B,H,F], beta [B,H,F*N]; sizes may be
-    overridden."""
+    v and out_gate [B,H,F*N,dv], alpha [B,H,F], beta [B,H,F*N], and
+    'alpha_logit', 'beta_logit': the normal draws alpha and beta are mapped
+    from.  Sizes may be overridden."""
     B = wl.B if B is None else B
     H = wl.H if H is None else H
     F = wl.F if F is None else F
@@ -244,4 +245,5 @@ def make_frame_call(wl: FrameWorkload, call: int = 0, *, B: Optional[int] = None
     og = torch.sigmoid(torch.randn(B, H, T, wl.dv, generator=g, dtype=f32))
     return dict(q=q.to(bf), k=k.to(bf), v=v.to(bf),
                 alpha=torch.exp(-torch.nn.functional.softplus(za)).to(bf),
-                beta=torch.sigmoid(zb).to(bf), out_gate=og.to(bf))
+                beta=torch.sigmoid(zb).to(bf), out_gate=og.to(bf),
+                alpha_logit=za.to(bf), beta_logit=zb.to(bf))

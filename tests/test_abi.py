@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.gdn_version() == 2
+    assert lib.gdn_version() == 3
     assert lib.gdn_strerror(0) == b"ok"
     assert lib.gdn_strerror(-1) == b"invalid argument"
     assert lib.gdn_strerror(-2) == b"unsupported shape or option"
@@ -180,6 +180,48 @@ def test_attn_workspace_query(lib):
     assert lib.gdn_attn_workspace_bytes(8, 32, 4096, 2640, 2640, 2640, 64, None) == 0
     assert lib.gdn_attn_workspace_bytes(1, 1, 64, 64, 0, 64, 64, None) == 0
     assert lib.gdn_attn_workspace_bytes(1, 16, 2640, 2640, 2640, 2640, 96, None) == 0
+
+
+def _frame(lib, q=16, k=16, v=16, a=16, b=16, sin=None, zin=None, out=16, sout=None, zout=None,
+           B=1, H=2, F=3, N=100, dk=64, dv=64, chunk=0, ws=None, ws_bytes=0):
+    P = lambda x: None if x is None else ctypes.c_void_p(x)
+    o = gdn.GdnOpts()
+    lib.gdn_default_opts(ctypes.byref(o))
+    o.workspace = P(ws)
+    o.workspace_bytes = ws_bytes
+    return lib.gdn_fwd_framewise(P(q), P(k), P(v), P(a), P(b), P(sin), P(zin), P(out), P(sout), P(zout),
+                                 B, H, F, N, dk, dv, chunk, ctypes.byref(o))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), gdn.GDN_ERR_ARG),                       # no workspace
+    (dict(N=0), gdn.GDN_ERR_ARG),
+    (dict(F=-1), gdn.GDN_ERR_ARG),
+    (dict(dk=32), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(dv=32), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(chunk=128), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(q=None, ws=4096, ws_bytes=1 << 40), gdn.GDN_ERR_ARG),
+    (dict(zin=8, ws=4096, ws_bytes=1 << 40), gdn.GDN_ERR_ARG),    # misaligned z_in
+    (dict(ws=4096, ws_bytes=1000), gdn.GDN_ERR_ARG),               # workspace too small
+])
+def test_framewise_argument_errors_are_synchronous(lib, kw, status):
+    assert _frame(lib, **kw) == status
+    assert len(lib.gdn_last_error()) > 0
+
+
+def test_framewise_workspace_query(lib):
+    # per-token decay, values [v | 1 0 ...], state [M | z 0 ...], fp32 scan outputs, segment data
+    r = lambda n: (n + 255) // 256 * 256
+    B, H, F, N, dk, dv = 1, 16, 3, 880, 64, 64
+    T, dvp = F * N, dv + 64
+    parts = r(B * H * T * 2) + r(B * H * T * dvp * 2) + r(B * H * dk * dvp * 4) + r(B * H * T * dvp * 4)
+    seg = lib.gdn_workspace_bytes(B, H, T, dk, dvp, 64, None) if dvp <= 128 else None
+    n = lib.gdn_framewise_workspace_bytes(B, H, F, N, dk, dv, 0, None)
+    assert n == parts + seg
+    assert lib.gdn_framewise_workspace_bytes(B, H, F, N, dk, dv, 64, None) == n
+    assert lib.gdn_framewise_workspace_bytes(B, H, F, N, 32, dv, 0, None) == 0
+    assert lib.gdn_framewise_workspace_bytes(B, H, F, N, dk, dv, 128, None) == 0
+    assert lib.gdn_framewise_workspace_bytes(B, H, 0, N, dk, dv, 0, None) == r(B * H * dk * dvp * 4)
 
 
 # last: it reloads the binding module (the fixture's library keeps the old types)
