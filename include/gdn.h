@@ -184,7 +184,8 @@ size_t gdn_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk,
  *   z_in        [B][H][dk]       fp32 denominator state, or NULL (zero)
  *   out         [B][H][F*N][dv]  opts->out_dtype; opts->out_gate [B][H][F*N][dv]
  *   state_out   [B][H][dk][dv]   fp32, or NULL;  z_out [B][H][dk] fp32, or NULL
- * dk and dv are 64 or 128; chunk 32 or 64 (0: 64); B*H*F*N*(dv+64) < 2^31.
+ * dk and dv are 64 or 128; chunk 32 or 64 (0: 64); B*H*F*N*(dv+64) < 2^31 and
+ * F*N*(dv+64)*4 < 2^31 (GDN_ERR_UNSUPPORTED otherwise).
  * state_out may alias state_in and z_out z_in.  The denominator has no sign
  * guarantee: the readout divides by it as it is (features that keep z . q
  * positive, such as non-negative ones, are the caller's part); a zero

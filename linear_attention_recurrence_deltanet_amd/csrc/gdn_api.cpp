@@ -310,10 +310,13 @@ struct FrameLayout {
 
 size_t r256(size_t n) { return (n + 255) & ~(size_t)255; }
 
+// Limits: element indices of the prologue and epilogue over all heads, and
+// the scan's per-head byte offsets of its fp32 outputs, stay below 2^31.
 bool frame_shape_ok(int B, int H, int F, int N, int dk, int dv, int chunk) {
     return B > 0 && H > 0 && F >= 0 && N > 0 && (dk == 64 || dk == 128) && (dv == 64 || dv == 128) &&
            (chunk == 32 || chunk == 64) &&
-           (long long)B * H * F * N * (dv + 64) < 0x7fffffffLL;
+           (long long)B * H * F * N * (dv + 64) < 0x7fffffffLL &&
+           (long long)F * N * (dv + 64) * 4 < 0x7fffffffLL;
 }
 
 FrameLayout frame_layout(int B, int H, int F, int N, int dk, int dv, int chunk) {

@@ -200,6 +200,7 @@ def _frame(lib, q=16, k=16, v=16, a=16, b=16, sin=None, zin=None, out=16, sout=N
     (dict(dk=32), gdn.GDN_ERR_UNSUPPORTED),
     (dict(dv=32), gdn.GDN_ERR_UNSUPPORTED),
     (dict(chunk=128), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(H=1, F=1, N=(1 << 31) // (128 * 4)), gdn.GDN_ERR_UNSUPPORTED),   # per-head fp32 outputs above 2 GiB
     (dict(q=None, ws=4096, ws_bytes=1 << 40), gdn.GDN_ERR_ARG),
     (dict(zin=8, ws=4096, ws_bytes=1 << 40), gdn.GDN_ERR_ARG),    # misaligned z_in
     (dict(ws=4096, ws_bytes=1000), gdn.GDN_ERR_ARG),               # workspace too small
