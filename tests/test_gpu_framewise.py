@@ -78,6 +78,13 @@ def test_framewise_gate_logits(gdn_lib, oracle_mod):
     _run(gdn_lib, oracle_mod, wl, 2, H=4, F=2, N=300, gate=False, what="no-gate")
 
 
+def test_framewise_d128_chunk32_and_logits(gdn_lib, oracle_mod):
+    # d_k = d_v = 128: the scan runs on 192 value columns (three 64-column tiles)
+    wl = FRAME_WORKLOADS["frame_rollout_h16_d128"]
+    _run(gdn_lib, oracle_mod, wl, 2, H=3, F=2, N=400, chunk=32, what="d128-chunk32")
+    _run(gdn_lib, oracle_mod, wl, 1, H=4, F=3, N=250, logits=True, what="d128-logits")
+
+
 def test_framewise_bf16_out_is_fp32_out_rounded_once(gdn_lib, oracle_mod):
     """bf16 outputs are the fp32 outputs rounded once (bit for bit); against
     the oracle they hold the max-abs bound.  Their rel-L2 is the fp32 error
