@@ -18,8 +18,10 @@
 // c of each block):
 //   S^T = K Q^T          keys x queries (K from LDS, Q^T kept in registers),
 //                        bf16 operands as given
-//   online softmax over the keys: running max m and sum l per query, exp2
+//   online softmax over the keys: running max m per query, exp2
 //   O^T += V^T P^T       P^T taken as it stands from the S^T accumulators;
+//                        one more block of V^T, a row of ones, gives the
+//                        softmax denominators on the matrix cores;
 //                        fp16 operands (11-bit significand: P in bf16 alone
 //                        costs ~1e-3 relative on the output), V converted
 //                        exactly while it is transposed into LDS
@@ -56,8 +58,8 @@ struct APlan {
     static constexpr int NPC = AK / 2 * PPR / 256; // (row pair, piece) items per thread per tile
 };
 
-// Over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (one query column of an
-// accumulator tile): v_permlane32_swap / v_permlane16_swap exchange halves
+// Maximum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (one query column of
+// an accumulator tile): v_permlane32_swap / v_permlane16_swap exchange halves
 // and rows of two registers on the VALU, no LDS round trip.  Written as asm
 // with both registers in and out: through the compiler builtin, a swap of
 // two equal inputs had its second result replaced by the first (checked on
@@ -68,13 +70,6 @@ __device__ __forceinline__ float xlane_max4(float x) {
     float c = fmaxf(a, b), d = c;
     asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(c), "+v"(d));
     return fmaxf(c, d);
-}
-__device__ __forceinline__ float xlane_sum4(float x) {
-    float a = x, b = x;
-    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
-    float c = a + b, d = c;
-    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(c), "+v"(d));
-    return c + d;
 }
 
 // Operand fragment in accumulator k order (row lane % 16; k = kb + 4 g + i
@@ -210,9 +205,15 @@ __global__ __launch_bounds__(256, 2) void gdn_attn_kernel(AttnArgs p) {
     f32x4 O[NDB][2];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) O[db][0] = O[db][1] = zero4();
-    // running max (exp2 domain) and partial sums of this lane's keys, per query
-    // block; the max starts finite so that fully masked keys give exp2(-inf) = 0
-    float m[2] = {-1e30f, -1e30f}, l[2] = {0.f, 0.f};
+    // the softmax denominators ride along with the output: one more 16-row
+    // block of V^T whose first row is all ones (fp16 1.0 on lanes of row 0),
+    // so that row 0 of Lacc accumulates sum_k P[k][query] on the matrix cores
+    const uint32_t one2 = lc == 0 ? 0x3C003C00u : 0u;
+    const u16x8 ones = __builtin_bit_cast(u16x8, make_uint4(one2, one2, one2, one2));
+    f32x4 Lacc[2] = {zero4(), zero4()};
+    // running max (exp2 domain) per query block; it starts finite so that
+    // fully masked keys give exp2(-inf) = 0
+    float m[2] = {-1e30f, -1e30f};
     const float cs = p.scale * 1.4426950408889634f;
 
     if (t_lo < t_hi) {
@@ -259,21 +260,17 @@ __global__ __launch_bounds__(256, 2) void gdn_attn_kernel(AttnArgs p) {
                 for (int i = 0; i < 4; ++i) mx = fmaxf(mx, S[kb][qb][i]);
             const float mn = fmaxf(m[qb], xlane_max4(mx) * cs);
             const float corr = __builtin_amdgcn_exp2f(m[qb] - mn);
-            float ls = 0.f;
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][qb][i], cs, -mn));
-                    S[kb][qb][i] = e;
-                    ls += e;
-                }
-            l[qb] = l[qb] * corr + ls;
-            // the running output is rescaled only when some query's max grew
-            // (corr is exactly 1 for the others)
+                for (int i = 0; i < 4; ++i)
+                    S[kb][qb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][qb][i], cs, -mn));
+            // the running output and denominators are rescaled only when some
+            // query's max grew (corr is exactly 1 for the others)
             if (__builtin_amdgcn_ballot_w64(mn > m[qb]) != 0) {
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) O[db][qb] *= corr;
+                Lacc[qb] *= corr;
             }
             m[qb] = mn;
         }
@@ -285,13 +282,16 @@ __global__ __launch_bounds__(256, 2) void gdn_attn_kernel(AttnArgs p) {
 #pragma unroll
             for (int k2 = 0; k2 < 2; ++k2) pf[qb][k2] = pack8_f16(S[2 * k2][qb], S[2 * k2 + 1][qb]);
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2)
+        for (int k2 = 0; k2 < 2; ++k2) {
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
                 const u16x8 a = frag_rows(Vt[b], L::LDV, 16 * db, 32 * k2, lane);
                 O[db][0] = OpF16::mma(a, pf[0][k2], O[db][0]);
                 O[db][1] = OpF16::mma(a, pf[1][k2], O[db][1]);
             }
+            Lacc[0] = OpF16::mma(ones, pf[0][k2], Lacc[0]);
+            Lacc[1] = OpF16::mma(ones, pf[1][k2], Lacc[1]);
+        }
 
         if (t + 1 < t_hi) store_tile(b ^ 1);     // copy b ^ 1 was last read before the previous barrier
         __syncthreads();
@@ -304,7 +304,7 @@ __global__ __launch_bounds__(256, 2) void gdn_attn_kernel(AttnArgs p) {
         const rsrc_t rpm = make_rsrc(p.part_ml + prow * 2, (unsigned)Nq * 8u);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
-            const float ls = xlane_sum4(l[qb]);
+            const float ls = __shfl(Lacc[qb][0], lc);       // row 0 sits on lanes 0..15
             const int row = q0 + 16 * qb + lc;
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
@@ -318,7 +318,7 @@ __global__ __launch_bounds__(256, 2) void gdn_attn_kernel(AttnArgs p) {
     // ---- O = (O^T)^T / l: lane (g, c) holds columns 16 db + 4 g + i of query c
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-        const float inv = 1.f / xlane_sum4(l[qb]);
+        const float inv = 1.f / __shfl(Lacc[qb][0], lc);   // row 0 sits on lanes 0..15
         const int row = q0 + 16 * qb + lc;                 // rows past Nq are dropped
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
