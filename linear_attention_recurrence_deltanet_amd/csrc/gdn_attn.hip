@@ -45,6 +45,7 @@ namespace {
 
 constexpr int AQ = 128;   // queries per workgroup (4 waves x 32)
 constexpr int AK = 64;    // keys per tile
+constexpr float kLazy = 8.f;   // headroom of the softmax reference max (log2 units)
 
 template <int D>
 struct APlan {
@@ -258,7 +259,13 @@ __global__ __launch_bounds__(256, 2) void gdn_attn_kernel(AttnArgs p) {
             for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) mx = fmaxf(mx, S[kb][qb][i]);
-            const float mn = fmaxf(m[qb], xlane_max4(mx) * cs);
+            // the reference max of a query moves only when the tile's max
+            // exceeds it by more than kLazy (exp2 domain): the weights stay
+            // below 2^kLazy (exact in fp16) and most tiles skip the rescale;
+            // the result does not depend on it (numerator and denominator
+            // share the reference)
+            const float cand = xlane_max4(mx) * cs;
+            const float mn = cand > m[qb] + kLazy ? cand : m[qb];
             const float corr = __builtin_amdgcn_exp2f(m[qb] - mn);
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
