@@ -430,6 +430,23 @@ def main():
     p99 = sorted(per)[min(len(per) - 1, int(0.99 * len(per)))]
     tokens_per_step = wl.B * wl.T
 
+    # host latency of one call including dispatch (call, then wait for it),
+    # and a warm figure: the same input set every call, so it stays cached
+    host = []
+    for i in range(K):
+        h0 = time.perf_counter()
+        fn(calls[i % nsets])
+        torch.cuda.synchronize()
+        host.append((time.perf_counter() - h0) * 1e3)
+    host.sort()
+    w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0.record(stream)
+    for i in range(K):
+        fn(calls[0])
+    w1.record(stream)
+    torch.cuda.synchronize()
+    warm_ms = w0.elapsed_time(w1) / K
+
     if args.copy_calibration:
         x = torch.empty(64 << 20, dtype=torch.float32, device=dev)
         y = torch.empty_like(x)
@@ -462,6 +479,8 @@ def main():
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": None if (args.gates or args.bidir) else read_traffic(khash, wl.name)},
         "kernel": {"avg_ms": kern_ms, "p50_ms": p50, "p99_ms": p99,
+                   "host_p50_ms": host[len(host) // 2], "host_p99_ms": host[min(len(host) - 1, int(0.99 * len(host)))],
+                   "warm_ms_per_call": warm_ms,
                    "algorithmic_bytes": alg_bytes, "algorithmic_flops": algorithmic_flops(wl),
                    "mfma_frac_of_bf16_peak": algorithmic_flops(wl) / (kern_ms * 1e-3) / 1e12
                    / MFMA_BF16_PEAK_TFLOPS,
