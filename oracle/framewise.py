@@ -21,6 +21,12 @@ equations are readings:
     elementwise by the output gate.
 
 Plain token loop, vectorised over (batch, head) only; no chunking.
+
+Pins (tests/test_oracle_pins.py): equality with the C token-wise oracle run
+with the frame decays placed on each frame's first token (numerator) and on a
+value column of ones (denominator); closed forms for beta = 0, constant
+values, shifted values, orthonormal keys; split invariance across calls.  The
+readings above have no printed values on the pages to pin them against.
 """
 from __future__ import annotations
 
