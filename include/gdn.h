@@ -91,7 +91,9 @@ void gdn_default_opts(gdn_opts* opts);
  * gdn_fwd_chunked: the chunked forward over a whole sequence of T tokens per
  * head, starting from state_in and producing every o_t and the final state.
  * `chunk` is the kernel's token tile (32, 64 or 128); results do not depend
- * on it beyond rounding.  dk in {32, 64, 128}; dv in {32, 64, 128}.
+ * on it beyond rounding.  dk in {32, 64, 128}; dv in {32, 64, 128}.  With
+ * fp32 inputs the chunk is 32 or 64: 128 fp32 rows of a chunk do not fit on
+ * chip, and chunk 128 returns GDN_ERR_UNSUPPORTED.
  * opts may be NULL (defaults).  Pointers must be 16-byte aligned.
  */
 int gdn_fwd_chunked(const void* q, const void* k, const void* v,

@@ -87,11 +87,13 @@ def test_bad_dtype_in_opts(lib):
     assert _call(lib, opts=ctypes.byref(o)) == gdn.GDN_ERR_ARG
 
 
-def test_fp32_chunk_that_does_not_fit_is_rejected(lib):
+@pytest.mark.parametrize("dk", [32, 64, 128])
+def test_fp32_chunk_that_does_not_fit_is_rejected(lib, dk):
+    # 128 fp32 rows of a chunk do not fit on chip at any head size
     o = gdn.GdnOpts()
     lib.gdn_default_opts(ctypes.byref(o))
     o.in_dtype = gdn.GDN_F32
-    assert _call(lib, dk=128, chunk=128, opts=ctypes.byref(o)) == gdn.GDN_ERR_UNSUPPORTED
+    assert _call(lib, dk=dk, chunk=128, opts=ctypes.byref(o)) == gdn.GDN_ERR_UNSUPPORTED
 
 
 def test_step_validates_too(lib):
