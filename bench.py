@@ -35,6 +35,7 @@ LLC_BYTES = 256 << 20           # Infinity Cache
 KERNEL_SOURCES = ("linear_attention_recurrence_deltanet_amd/csrc/gdn_pipe.hip",
                   "linear_attention_recurrence_deltanet_amd/csrc/gdn_fwd.hip",
                   "linear_attention_recurrence_deltanet_amd/csrc/gdn_fwd_single.hip",
+                  "linear_attention_recurrence_deltanet_amd/csrc/gdn_frame.hip",
                   "linear_attention_recurrence_deltanet_amd/csrc/gdn_common.h",
                   "linear_attention_recurrence_deltanet_amd/csrc/gdn_api.cpp")
 
@@ -57,6 +58,15 @@ def algorithmic_bytes(wl, out_bytes=4, state_in=True, out_gate=False) -> int:
                     + (wl.dv * s_in if out_gate else 0))
     st = wl.B * wl.H * wl.dk * wl.dv * 4
     return b + st + (st if state_in else 0)
+
+
+def framewise_algorithmic_bytes(wl, out_bytes=4) -> int:
+    """Frame-wise call: q, k, v, beta and the output gate read once (bf16),
+    out written once, alpha once per frame, the fp32 numerator and
+    denominator states read and written once."""
+    bh, T = wl.B * wl.H, wl.T
+    return (bh * T * (2 * wl.dk * 2 + wl.dv * 2 + 2 + wl.dv * 2 + wl.dv * out_bytes)
+            + bh * wl.F * 2 + 2 * bh * (wl.dk * wl.dv + wl.dk) * 4)
 
 
 def algorithmic_flops(wl) -> int:
@@ -224,10 +234,7 @@ def bench_framewise(args):
     out_dt = torch.float32 if args.out_dtype == "f32" else torch.bfloat16
     out_bytes = 4 if args.out_dtype == "f32" else 2
     bh, T = wl.B * wl.H, wl.T
-    # q, k, v, beta, output gate read once, out written once, alpha per frame,
-    # both fp32 states read and written once
-    alg_bytes = (bh * T * (2 * wl.dk * 2 + wl.dv * 2 + 2 + wl.dv * 2 + wl.dv * out_bytes)
-                 + bh * wl.F * 2 + 2 * bh * (wl.dk * wl.dv + wl.dk) * 4)
+    alg_bytes = framewise_algorithmic_bytes(wl, out_bytes)
     per_set = bh * T * (2 * wl.dk + 2 * wl.dv + 2) * 2
     nsets = max(2, min(64, (2 * LLC_BYTES) // per_set + 1))
     sets = [{k: v.to(dev).contiguous() for k, v in make_frame_call(wl, i).items()} for i in range(nsets)]
@@ -268,6 +275,12 @@ def bench_framewise(args):
     per = [a.elapsed_time(b) for a, b in ev]
     call_ms = statistics.mean(per)
     achieved = alg_bytes / (call_ms * 1e-3) / 1e9
+    if args.copy_calibration:
+        x = torch.empty(64 << 20, dtype=torch.float32, device=dev)
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
     res = {
         "metric": "frame-wise GDN (normalised readout) tokens/sec (bf16, 1 GPU) + % of HBM roofline vs oracle",
         "value": wl.B * T / (ms_per_step * 1e-3),
@@ -286,7 +299,8 @@ def bench_framewise(args):
                    "out_dtype": args.out_dtype, "state": "fp32 numerator and denominator carried",
                    "input_sets": nsets, "workspace_bytes": ws_bytes},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": read_traffic(kernel_source_hash(), wl.name) if args.out_dtype == "f32" else None},
         "kernel": {"avg_ms": call_ms, "p50_ms": statistics.median(per),
                    "p99_ms": sorted(per)[min(len(per) - 1, int(0.99 * len(per)))],
                    "algorithmic_bytes": alg_bytes, "launches_per_call": 4},
