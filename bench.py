@@ -491,7 +491,8 @@ def main():
                    "scan": "bidirectional" if args.bidir else "forward"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": None if (args.gates or args.bidir) else read_traffic(khash, wl.name)},
+                     "traffic": None if (args.gates and args.bidir) or args.out_dtype != "f32" or args.chunk
+                     else read_traffic(khash, wl.name + ("_gates" if args.gates else "_bidir" if args.bidir else ""))},
         "kernel": {"avg_ms": kern_ms, "p50_ms": p50, "p99_ms": p99,
                    "host_p50_ms": host[len(host) // 2], "host_p99_ms": host[min(len(host) - 1, int(0.99 * len(host)))],
                    "warm_ms_per_call": warm_ms,
