@@ -186,7 +186,8 @@ size_t gdn_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk,
  *   z_in        [B][H][dk]       fp32 denominator state, or NULL (zero)
  *   out         [B][H][F*N][dv]  opts->out_dtype; opts->out_gate [B][H][F*N][dv]
  *   state_out   [B][H][dk][dv]   fp32, or NULL;  z_out [B][H][dk] fp32, or NULL
- * dk and dv are 64 or 128; chunk 32 or 64 (0: 64); B*H*F*N*(dv+64) < 2^31 and
+ * dk and dv are 64 or 128; chunk 32 or 64 (0: 32, the more accurate here:
+ * inside a frame nothing decays); B*H*F*N*(dv+64) < 2^31 and
  * F*N*(dv+64)*4 < 2^31 (GDN_ERR_UNSUPPORTED otherwise).
  * state_out may alias state_in and z_out z_in.  The denominator has no sign
  * guarantee: the readout divides by it as it is (features that keep z . q
@@ -205,7 +206,7 @@ int gdn_fwd_framewise(const void* q, const void* k, const void* v,
                       int B, int H, int F, int N, int dk, int dv, int chunk,
                       const gdn_opts* opts);
 
-/* Workspace (bytes) of gdn_fwd_framewise for this shape and chunk (0: 64);
+/* Workspace (bytes) of gdn_fwd_framewise for this shape and chunk (0: 32);
  * 0 for unsupported shapes. */
 size_t gdn_framewise_workspace_bytes(int B, int H, int F, int N, int dk, int dv, int chunk,
                                      const gdn_opts* opts);

@@ -215,10 +215,10 @@ class FrameWorkload:
 
 FRAME_WORKLOADS = {
     # one streaming chunk of 3 latent frames x 880 tokens, 16 heads of 64
-    "frame_stream_h16_d64": FrameWorkload("frame_stream_h16_d64", 1, 16, 3, 880, 64, 64, 64, 1,
+    "frame_stream_h16_d64": FrameWorkload("frame_stream_h16_d64", 1, 16, 3, 880, 64, 64, 32, 1,
                                           0.0, 1.0, 0.0, 1.0, 3001),
     # 20 successive streaming chunks, 16 heads of 128, both states carried
-    "frame_rollout_h16_d128": FrameWorkload("frame_rollout_h16_d128", 1, 16, 3, 880, 128, 128, 64, 20,
+    "frame_rollout_h16_d128": FrameWorkload("frame_rollout_h16_d128", 1, 16, 3, 880, 128, 128, 32, 20,
                                             0.0, 1.0, 0.0, 1.0, 3002),
 }
 

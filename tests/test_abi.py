@@ -218,10 +218,12 @@ def test_framewise_workspace_query(lib):
     B, H, F, N, dk, dv = 1, 16, 3, 880, 64, 64
     T, dvp = F * N, dv + 64
     parts = r(B * H * T * 2) + r(B * H * T * dvp * 2) + r(B * H * dk * dvp * 4) + r(B * H * T * dvp * 4)
-    seg = lib.gdn_workspace_bytes(B, H, T, dk, dvp, 64, None) if dvp <= 128 else None
-    n = lib.gdn_framewise_workspace_bytes(B, H, F, N, dk, dv, 0, None)
+    seg = lib.gdn_workspace_bytes(B, H, T, dk, dvp, 32, None)
+    n = lib.gdn_framewise_workspace_bytes(B, H, F, N, dk, dv, 0, None)       # default chunk 32
     assert n == parts + seg
-    assert lib.gdn_framewise_workspace_bytes(B, H, F, N, dk, dv, 64, None) == n
+    assert lib.gdn_framewise_workspace_bytes(B, H, F, N, dk, dv, 32, None) == n
+    assert lib.gdn_framewise_workspace_bytes(B, H, F, N, dk, dv, 64, None) == \
+        parts + lib.gdn_workspace_bytes(B, H, T, dk, dvp, 64, None)
     assert lib.gdn_framewise_workspace_bytes(B, H, F, N, 32, dv, 0, None) == 0
     assert lib.gdn_framewise_workspace_bytes(B, H, F, N, dk, dv, 128, None) == 0
     assert lib.gdn_framewise_workspace_bytes(B, H, 0, N, dk, dv, 0, None) == r(B * H * dk * dvp * 4)

@@ -86,9 +86,9 @@ def test_framewise_d128_chunk32_and_logits(gdn_lib, oracle_mod):
 
 
 def test_framewise_bf16_out_is_fp32_out_rounded_once(gdn_lib, oracle_mod):
-    """bf16 outputs are the fp32 outputs rounded once (bit for bit); against
-    the oracle they hold the max-abs bound.  Their rel-L2 is the fp32 error
-    plus the bf16 rounding of the output itself (about 1.7e-3 of it)."""
+    """bf16 outputs are the fp32 outputs rounded once (bit for bit) and meet
+    the bf16 bar against the oracle (their rel-L2 is the fp32 error plus the
+    bf16 rounding of the output itself, about 1.7e-3 of it)."""
     wl = FRAME_WORKLOADS["frame_stream_h16_d64"]
     announce(f"framewise bf16-out {wl.name}")
     d = make_frame_call(wl, 0)
@@ -103,7 +103,7 @@ def test_framewise_bf16_out_is_fp32_out_rounded_once(gdn_lib, oracle_mod):
                                          out_gate=to_numpy64(d["out_gate"]))
     maxabs, rel = errors(o16.to("cpu", torch.float64).numpy(), ref)
     print(f"   bf16 out maxabs {maxabs:.2e} rel {rel:.2e}", flush=True)
-    assert maxabs <= TOL_BF16["maxabs"]
+    assert maxabs <= TOL_BF16["maxabs"] and rel <= TOL_BF16["rel"]
 
 
 def test_framewise_no_frames_copies_states(gdn_lib):
