@@ -602,3 +602,18 @@ def test_framewise_split_across_calls(oracle_mod):
     np.testing.assert_allclose(np.concatenate([o1, o2], axis=2), o, rtol=1e-13, atol=1e-14)
     np.testing.assert_allclose(s2, s_out, rtol=1e-13, atol=1e-14)
     np.testing.assert_allclose(z2, z_out, rtol=1e-13, atol=1e-14)
+
+
+def test_attn_score_shift_invariance_and_value_shift(oracle_mod):
+    """Adding the same vector u to every key moves all scores of a query by
+    scale * (q . u), which the softmax ignores; adding c to every value adds
+    c to every output (the weights sum to one)."""
+    rng = np.random.default_rng(46)
+    q, ks, vs, kw, vw, kc, vc = _attn_case(rng, d=8)
+    out = oracle_mod.attn_sink_window(q, ks, vs, kw, vw, kc, vc)
+    u = 3.0 * rng.standard_normal(8)
+    out_k = oracle_mod.attn_sink_window(q, ks + u, vs, kw + u, vw, kc + u, vc)
+    np.testing.assert_allclose(out_k, out, rtol=1e-11, atol=1e-12)
+    c = rng.standard_normal(8)
+    out_v = oracle_mod.attn_sink_window(q, ks, vs + c, kw, vw + c, kc, vc + c)
+    np.testing.assert_allclose(out_v, out + c, rtol=1e-11, atol=1e-12)
