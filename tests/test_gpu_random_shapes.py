@@ -50,3 +50,60 @@ def test_random_shape(gdn_lib, oracle_mod, c):
     r1 = assert_close(out.to("cpu", torch.float64).numpy(), ref, c["f32"], "out")
     r2 = assert_close(st.to("cpu", torch.float64).numpy(), rs, c["f32"], "state")
     print(f"   out maxabs {r1[0]:.2e} rel {r1[1]:.2e} | state rel {r2[1]:.2e}", flush=True)
+
+
+def _side_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    return [dict(H=int(rng.integers(1, 5)), dk=int(rng.choice([64, 128])), dv=int(rng.choice([64, 128])),
+                 chunk=int(rng.choice([32, 64])), gates=bool(rng.random() < 0.5), state=bool(rng.random() < 0.5),
+                 T=int(rng.integers(1, 600)), F=int(rng.integers(1, 4)), N=int(rng.integers(1, 300)),
+                 seed=int(rng.integers(0, 1 << 20))) for _ in range(n)]
+
+
+BIDIR = _side_cases(6, 7)
+FRAME = _side_cases(6, 11)
+
+
+@pytest.mark.parametrize("c", BIDIR, ids=[f"H{c['H']}T{c['T']}k{c['dk']}v{c['dv']}C{c['chunk']}"
+                                          f"{'-gates' if c['gates'] else ''}{'-state' if c['state'] else ''}"
+                                          for c in BIDIR])
+def test_random_shape_bidir(gdn_lib, oracle_mod, c):
+    wl = WORKLOADS["stream_chunk_h16_d64"].replace(dk=c["dk"], dv=c["dv"], seed=c["seed"],
+                                                     state_sigma=0.3 if c["state"] else None)
+    announce(f"random bidir {c}")
+    d = make_call(wl, 0, H=c["H"], T=c["T"], gates=c["gates"])
+    g = to_dev(d)
+    a_key, b_key = ("alpha_logit", "beta_logit") if c["gates"] else ("alpha", "beta")
+    out, st = gdn_lib.fwd_bidir(g["q"], g["k"], g["v"], g[a_key], g[b_key], g["state_in"], c["chunk"],
+                                gate_logits=c["gates"], out_gate=g["out_gate"] if c["gates"] else None)
+    torch.cuda.synchronize()
+    ref, rs = oracle_mod.gdn_bidir(*(to_numpy64(d[n]) for n in ("q", "k", "v", a_key, b_key)),
+                                   None if d["state_in"] is None else to_numpy64(d["state_in"]),
+                                   gate_logits=c["gates"],
+                                   out_gate=to_numpy64(d["out_gate"]) if c["gates"] else None)
+    r1 = assert_close(out.to("cpu", torch.float64).numpy(), ref, False, "out")
+    r2 = assert_close(st.to("cpu", torch.float64).numpy(), rs, False, "state")
+    print(f"   out maxabs {r1[0]:.2e} rel {r1[1]:.2e} | state rel {r2[1]:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("c", FRAME, ids=[f"H{c['H']}F{c['F']}N{c['N']}k{c['dk']}v{c['dv']}C{c['chunk']}"
+                                          f"{'-logits' if c['gates'] else ''}" for c in FRAME])
+def test_random_shape_framewise(gdn_lib, oracle_mod, c):
+    from linear_attention_recurrence_deltanet_amd.inputs import FRAME_WORKLOADS, make_frame_call
+    wl = FRAME_WORKLOADS["frame_stream_h16_d64"].replace(dk=c["dk"], dv=c["dv"], seed=c["seed"])
+    announce(f"random framewise {c}")
+    d = make_frame_call(wl, 0, H=c["H"], F=c["F"], N=c["N"])
+    g = to_dev(d)
+    a_key, b_key = ("alpha_logit", "beta_logit") if c["gates"] else ("alpha", "beta")
+    out, st, z = gdn_lib.fwd_framewise(g["q"], g["k"], g["v"], g[a_key], g[b_key], c["N"], chunk=c["chunk"],
+                                       gate_logits=c["gates"], out_gate=g["out_gate"])
+    torch.cuda.synchronize()
+    q, k, v, a, b = (to_numpy64(d[n]) for n in ("q", "k", "v", a_key, b_key))
+    if c["gates"]:
+        a, _ = oracle_mod.gates(a, np.zeros_like(a))
+        _, b = oracle_mod.gates(np.zeros_like(b), b)
+    ref, rs, rz = oracle_mod.gdn_framewise(q, k, v, a, b, c["N"], out_gate=to_numpy64(d["out_gate"]))
+    r1 = assert_close(out.to("cpu", torch.float64).numpy(), ref, False, "out")
+    r2 = assert_close(st.to("cpu", torch.float64).numpy(), rs, False, "state")
+    r3 = assert_close(z.to("cpu", torch.float64).numpy(), rz, False, "z")
+    print(f"   out maxabs {r1[0]:.2e} rel {r1[1]:.2e} | state rel {r2[1]:.2e} | z rel {r3[1]:.2e}", flush=True)
