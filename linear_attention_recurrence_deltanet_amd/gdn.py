@@ -133,6 +133,7 @@ def _workspace(workspace, B, H, T, dk, dv, chunk, in_dtype, out_dtype, device, b
     if workspace is False:
         return None
     if workspace is not None:
+        _check_workspace(workspace, device)
         return workspace
     o = GdnOpts()
     load().gdn_default_opts(ctypes.byref(o))
@@ -141,6 +142,27 @@ def _workspace(workspace, B, H, T, dk, dv, chunk, in_dtype, out_dtype, device, b
     query = load().gdn_bidir_workspace_bytes if bidir else load().gdn_workspace_bytes
     n = int(query(B, H, T, dk, dv, chunk, ctypes.byref(o)))
     return torch.empty(n, dtype=torch.uint8, device=device) if n > 0 else None
+
+
+def _check_workspace(ws, device):
+    if not isinstance(ws, torch.Tensor) or not ws.is_cuda or ws.device != device or not ws.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous device tensor on {device}")
+
+
+def _on_stream(stream, *tensors):
+    """Tensors this call allocated on the current stream but the kernels use on
+    `stream`: tell the caching allocator, so their memory is not handed out
+    again before the work on `stream` has finished."""
+    if stream is None:
+        return
+    cur = torch.cuda.current_stream()
+    sid = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    if sid == cur.cuda_stream:
+        return
+    ext = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(sid)
+    for t in tensors:
+        if isinstance(t, torch.Tensor):
+            t.record_stream(ext)
 
 
 def _check(status: int):
@@ -156,27 +178,48 @@ def _prep(q, k, v, alpha, beta, state_in, out, state_out, out_dtype):
             raise ValueError(f"{name} must be contiguous")
         if t.dtype != q.dtype:
             raise ValueError(f"{name} dtype {t.dtype} differs from q dtype {q.dtype}")
+        if t.device != q.device:
+            raise ValueError(f"{name} is on {t.device}, q on {q.device}")
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, T, dk]")
     B, H, T, dk = q.shape
     dv = v.shape[-1]
     if k.shape != q.shape or v.shape[:3] != (B, H, T):
         raise ValueError("shape mismatch between q, k, v")
     if alpha.shape != (B, H, T) or beta.shape != (B, H, T):
         raise ValueError("alpha and beta must be [B, H, T]")
-    if state_in is not None and (state_in.dtype != torch.float32 or not state_in.is_contiguous()
-                                 or state_in.shape != (B, H, dk, dv)):
-        raise ValueError("state_in must be contiguous fp32 [B, H, dk, dv]")
+    _check_buf("state_in", state_in, (B, H, dk, dv), (torch.float32,), q.device)
     if out is None:
         out = torch.empty(B, H, T, dv, dtype=out_dtype, device=q.device)
+    else:
+        _check_buf("out", out, (B, H, T, dv), (torch.float32, torch.bfloat16), q.device)
     if state_out is None:
         state_out = torch.empty(B, H, dk, dv, dtype=torch.float32, device=q.device)
+    else:
+        _check_buf("state_out", state_out, (B, H, dk, dv), (torch.float32,), q.device)
     return B, H, T, dk, dv, out, state_out
+
+
+def _check_buf(name, t, shape, dtypes, device):
+    """A caller-supplied input or output buffer: the kernels see only its
+    address, so its shape, dtype, device and layout are checked here."""
+    if t is None:
+        return
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} dtype {t.dtype} not in {dtypes}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} shape {tuple(t.shape)} != {tuple(shape)}")
 
 
 def _check_gate(out_gate, q, B, H, T, dv):
     if out_gate is None:
         return
-    if (not out_gate.is_cuda or not out_gate.is_contiguous() or out_gate.dtype != q.dtype
-            or tuple(out_gate.shape) != (B, H, T, dv)):
+    if (not out_gate.is_cuda or out_gate.device != q.device or not out_gate.is_contiguous()
+            or out_gate.dtype != q.dtype or tuple(out_gate.shape) != (B, H, T, dv)):
         raise ValueError("out_gate must be a contiguous device tensor [B, H, T, dv] of q's dtype")
 
 
@@ -201,6 +244,7 @@ def fwd_chunked(q, k, v, alpha, beta, state_in=None, chunk: int = 64, *, out=Non
     _check(load().gdn_fwd_chunked(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
                                   _ptr(state_in), _ptr(out), _ptr(state_out),
                                   B, H, T, dk, dv, int(chunk), ctypes.byref(opts)))
+    _on_stream(stream, workspace, out, state_out)
     return out, state_out
 
 
@@ -217,6 +261,7 @@ def fwd_step(q, k, v, alpha, beta, state_in=None, *, out=None, state_out=None,
     _check(load().gdn_fwd_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
                                _ptr(state_in), _ptr(out), _ptr(state_out),
                                B, H, T, dk, dv, ctypes.byref(opts)))
+    _on_stream(stream, workspace, out, state_out)
     return out, state_out
 
 
@@ -237,6 +282,7 @@ def fwd_bidir(q, k, v, alpha, beta, state_in=None, chunk: int = 0, *, out=None, 
     _check(load().gdn_fwd_bidir(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
                                 _ptr(state_in), _ptr(out), _ptr(state_out),
                                 B, H, T, dk, dv, int(chunk), ctypes.byref(opts)))
+    _on_stream(stream, workspace, out, state_out)
     return out, state_out
 
 
@@ -258,8 +304,15 @@ def attn_sink_window(q, k_sink, v_sink, k_win, v_win, k_cur, v_cur, scale=None, 
         segs.append((k, v, k.shape[2]))
     if not q.is_cuda or not q.is_contiguous() or q.dtype != torch.bfloat16:
         raise ValueError("q must be a contiguous bf16 device tensor")
+    for name, k, v in (("sink", k_sink, v_sink), ("win", k_win, v_win), ("cur", k_cur, v_cur)):
+        if k.device != q.device or v.device != q.device:
+            raise ValueError(f"{name} keys and values must be on {q.device}")
     if out is None:
         out = torch.empty(B, H, Nq, d, dtype=out_dtype, device=q.device)
+    else:
+        _check_buf("out", out, (B, H, Nq, d), (torch.float32, torch.bfloat16), q.device)
+    if workspace is not None and workspace is not False:
+        _check_workspace(workspace, q.device)
     if workspace is None:
         n = int(load().gdn_attn_workspace_bytes(B, H, Nq, k_sink.shape[2], k_win.shape[2],
                                                 k_cur.shape[2], d, None))
@@ -272,6 +325,7 @@ def attn_sink_window(q, k_sink, v_sink, k_win, v_win, k_cur, v_cur, scale=None, 
         args += [_ptr(k) if n else None, _ptr(v) if n else None, int(n)]
     _check(load().gdn_attn_sink_window(_ptr(q), *args, _ptr(out), B, H, Nq, d,
                                        float(scale) if scale else 0.0, ctypes.byref(opts)))
+    _on_stream(stream, workspace, out)
     return out
 
 

@@ -5,28 +5,41 @@ and the ``cpu_baseline`` leg of ``bench.py``; never by the GPU library).
 Source: SANA-Streaming (paperpeel page), section 2.1 "Frame-wise Gated
 DeltaNet for Global Accumulated Memory": per head, latents of F frames of N
 tokens give q, k, v, a decay gate alpha in R^F (one per frame), a write gate
-beta in R^{F x N} (one per token) and an output gate g in R^{F x N x C}; a
-numerator state S^kv and a denominator (normaliser) state S^z are updated
-with the delta-rule correction and carried across chunks.  Appendix G.3 names
-the same three gates; G.4 ("Frame-wise delta-rule update") and G.5
-("Normalized readout") survive as headings only, so the update and readout
+beta in R^{F x N} (one per token) and an output gate g in R^{F x N x C}; the
+state is updated frame by frame rather than token by token, with the
+delta-rule correction, as a numerator state S^kv and a denominator
+(normaliser) state S^z carried across chunks.  Section 2.3 "Efficient GDN
+Kernel" computes it in three phases: frame summaries by reductions over the
+spatial tokens, a short recurrent scan over frames, and the frame's queries
+read against the frame's state.  Appendix G.4 ("Frame-wise delta-rule
+update") and G.5 ("Normalized readout") survive as headings only, so the
 equations are readings:
 
-  * within a frame the tokens are written one after another by the
-    token-wise delta rule, and the frame's decay alpha_f multiplies both
-    states once, before the frame's first token is written;
-  * the denominator state z (a d_k vector) follows the same recurrence as
-    every column of the numerator state, with a value of constant 1;
-  * the output of token t is (S_t q_t) / (z_t . q_t), then multiplied
-    elementwise by the output gate.
+  * one update per frame, from the frame's mean over its N tokens (the
+    delta rule is one gradient step on ||S k - v||^2 / 2 with step beta; the
+    frame-wise update is one step on the frame's mean loss
+    (1/N) sum_n beta_n ||S k_n - v_n||^2 / 2, taken from the decayed state):
+        G_f = (1/N) sum_n beta_{f,n} k_n k_n^T
+        S_f = alpha_f S_{f-1} (I - G_f) + (1/N) sum_n beta_{f,n} v_n k_n^T
+    With beta in [0, 1] and unit keys, I - G_f has eigenvalues in [0, 1], so
+    the state stays bounded however many tokens a frame holds; at N = 1 it is
+    the token-wise gated delta rule;
+  * the denominator z (a d_k row vector) follows the same update with a
+    value of constant 1: z_f = alpha_f z_{f-1} (I - G_f) + (1/N) sum_n beta k_n^T;
+  * every token of frame f reads the frame's updated state:
+        out_{f,n} = (S_f q_n) / (z_f . q_n), then times the output gate.
 
-Plain token loop, vectorised over (batch, head) only; no chunking.
+Plain loop over frames, vectorised over (batch, head); sums over the frame's
+tokens written out with einsum.  The state is stored transposed, M = S^T
+[d_k][d_v], as in the token-wise oracle.
 
-Pins (tests/test_oracle_pins.py): equality with the C token-wise oracle run
-with the frame decays placed on each frame's first token (numerator) and on a
-value column of ones (denominator); closed forms for beta = 0, constant
-values, shifted values, orthonormal keys; split invariance across calls.  The
-readings above have no printed values on the pages to pin them against.
+Pins (tests/test_oracle_pins.py): N = 1 equals the C token-wise oracle;
+keys orthonormal within each frame equal the token-wise scan with beta / N at
+frame ends; beta = 0 decays only; one autograd gradient step on the frame's
+mean loss; permutation of a frame's tokens; N equal tokens equal one token;
+constant values read back; shifted values; split invariance across calls.
+The readings themselves have no printed values on the pages to pin them
+against.
 """
 from __future__ import annotations
 
@@ -65,20 +78,20 @@ def gdn_framewise(q, k, v, alpha, beta, frame_len, state_in=None, z_in=None, *, 
         k = k / np.sqrt((k * k).sum(-1, keepdims=True) + eps)
     out = np.empty((B, H, T, dv))
     for f in range(F):
+        sl = slice(f * N, (f + 1) * N)
+        kf, vf, qf, bf = k[:, :, sl], v[:, :, sl], q[:, :, sl], beta[:, :, sl]
         a = alpha[:, :, f]
-        M *= a[:, :, None, None]          # the frame's decay, once
-        z *= a[:, :, None]
-        for n in range(N):
-            t = f * N + n
-            kt, qt, b = k[:, :, t], q[:, :, t], beta[:, :, t]
-            # delta-rule correction: the write replaces beta of what the state
-            # recalls for k_t by beta of the new value (1 for the normaliser)
-            recall = np.einsum("bhi,bhij->bhj", kt, M)
-            M += np.einsum("bhi,bhj->bhij", kt, b[:, :, None] * (v[:, :, t] - recall))
-            z += kt * (b * (1.0 - np.einsum("bhi,bhi->bh", kt, z)))[:, :, None]
-            num = np.einsum("bhij,bhi->bhj", M, qt)
-            den = np.einsum("bhi,bhi->bh", z, qt)
-            out[:, :, t] = num / den[:, :, None]
+        # frame summaries: the means over the frame's tokens
+        G = np.einsum("bhn,bhni,bhnj->bhij", bf, kf, kf) / N
+        Wv = np.einsum("bhn,bhni,bhnj->bhij", bf, kf, vf) / N
+        Wz = np.einsum("bhn,bhni->bhi", bf, kf) / N
+        # one decayed delta-rule step per frame: M <- alpha (I - G) M + Wv
+        M = a[:, :, None, None] * (M - np.einsum("bhik,bhkj->bhij", G, M)) + Wv
+        z = a[:, :, None] * (z - np.einsum("bhik,bhk->bhi", G, z)) + Wz
+        # every token of the frame reads the frame's updated state
+        num = np.einsum("bhij,bhni->bhnj", M, qf)
+        den = np.einsum("bhi,bhni->bhn", z, qf)
+        out[:, :, sl] = num / den[..., None]
     if out_gate is not None:
         g = _f64(out_gate)
         assert g.shape == out.shape

@@ -31,7 +31,7 @@ def _bench(*args):
 
 def test_bench_default_line():
     d = _bench("--cpu-seconds", "1")
-    assert d["config"]["workload"] == "stream_chunk_h16_d64" and d["roofline"]["bound"] == "hbm"
+    assert d["config"]["workload"] == "rollout_h16_d128" and d["roofline"]["bound"] == "hbm"
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1 and cb["unit"] == "tokens/s"
 

@@ -488,9 +488,11 @@ def test_attn_matches_library_attention(oracle_mod):
 
 
 # ---- frame-wise GDN with a normalised readout (SANA-Streaming section 2.1,
-# "Frame-wise Gated DeltaNet"; appendix G.3-G.5): one decay per frame, applied
-# once before the frame's first write; a denominator state driven by a value
-# of constant 1; output = numerator / denominator, then the output gate
+# "Frame-wise Gated DeltaNet": one state update per frame rather than per
+# token; section 2.3: frame summaries, a scan over frames, the frame's queries
+# read against its state; appendix G.3-G.5): the frame's mean of the delta
+# rule's writes and erasures, one decay per frame, a denominator state driven
+# by a value of constant 1, output = numerator / denominator, then the gate
 
 def _frame_case(rng, B=1, H=2, F=3, N=5, dk=6, dv=4, state=True):
     T = F * N
@@ -504,23 +506,80 @@ def _frame_case(rng, B=1, H=2, F=3, N=5, dk=6, dv=4, state=True):
     return q, k, v, a, b, s, z
 
 
-def test_framewise_equals_tokenwise_scans(oracle_mod):
-    """Against the C token-wise oracle, an independent loop: the numerator is
-    the token-wise scan with decay alpha_f on each frame's first token and 1
-    elsewhere; the denominator is the same scan over a single value column of
-    ones started from z_in; out = numerator / denominator * gate."""
+def test_framewise_one_token_frames_are_the_tokenwise_rule(oracle_mod):
+    """N = 1: every frame is one token, and the frame-wise update is the
+    token-wise gated delta rule of the C oracle (an independent token loop):
+    numerator = its scan over v, denominator = its scan over a value column of
+    ones from z_in, out = numerator / denominator * gate."""
     rng = np.random.default_rng(51)
-    q, k, v, a, b, s, z = _frame_case(rng)
-    F, N = a.shape[-1], q.shape[2] // a.shape[-1]
+    q, k, v, a, b, s, z = _frame_case(rng, F=7, N=1)
     g = 1.0 / (1.0 + np.exp(-rng.standard_normal(v.shape)))
-    out, s_out, z_out = oracle_mod.gdn_framewise(q, k, v, a, b, N, s, z, out_gate=g)
-    a_tok = np.ones(b.shape)
-    a_tok[:, :, ::N] = a
-    num, s_ref = oracle_mod.gdn_fwd(q, k, v, a_tok, b, s)
-    den, z_ref = oracle_mod.gdn_fwd(q, k, np.ones(v.shape[:-1] + (1,)), a_tok, b, z[..., None])
+    out, s_out, z_out = oracle_mod.gdn_framewise(q, k, v, a, b, 1, s, z, out_gate=g)
+    num, s_ref = oracle_mod.gdn_fwd(q, k, v, a, b, s)
+    den, z_ref = oracle_mod.gdn_fwd(q, k, np.ones(v.shape[:-1] + (1,)), a, b, z[..., None])
     np.testing.assert_allclose(out, num / den * g, rtol=1e-11, atol=1e-12)
     np.testing.assert_allclose(s_out, s_ref, rtol=1e-12, atol=1e-13)
     np.testing.assert_allclose(z_out, z_ref[..., 0], rtol=1e-12, atol=1e-13)
+
+
+def test_framewise_orthonormal_frame_keys_equal_sequential_writes(oracle_mod):
+    """Keys orthonormal within each frame: the frame's token writes commute
+    and do not interfere, so one frame update with beta equals the token-wise
+    scan (C oracle) over the frame's tokens with beta / N and the frame decay
+    on its first token.  The states agree at every frame end, and so does the
+    output of each frame's last token, which reads the state after the whole
+    frame in both."""
+    rng = np.random.default_rng(57)
+    F, N, dk, dv = 4, 5, 8, 3
+    k = np.empty((1, 2, F * N, dk))
+    for h in range(2):
+        for f in range(F):
+            Qo, _ = np.linalg.qr(rng.standard_normal((dk, dk)))
+            k[0, h, f * N:(f + 1) * N] = Qo[:N]
+    q = np.abs(rng.standard_normal((1, 2, F * N, dk)))
+    v = rng.standard_normal((1, 2, F * N, dv))
+    a = rng.uniform(0.3, 1.0, (1, 2, F))
+    b = rng.uniform(0.0, 1.0, (1, 2, F * N))
+    s = rng.standard_normal((1, 2, dk, dv)) * 0.4
+    z = np.abs(rng.standard_normal((1, 2, dk))) + 0.3
+    out, s_out, z_out = oracle_mod.gdn_framewise(q, k, v, a, b, N, s, z)
+    a_tok = np.ones(b.shape)
+    a_tok[:, :, ::N] = a
+    num, s_ref = oracle_mod.gdn_fwd(q, k, v, a_tok, b / N, s)
+    den, z_ref = oracle_mod.gdn_fwd(q, k, np.ones(v.shape[:-1] + (1,)), a_tok, b / N, z[..., None])
+    last = np.arange(N - 1, F * N, N)
+    np.testing.assert_allclose(out[:, :, last], (num / den)[:, :, last], rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(s_out, s_ref, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(z_out, z_ref[..., 0], rtol=1e-12, atol=1e-13)
+
+
+def test_framewise_is_one_gradient_step_on_the_frame_loss(oracle_mod):
+    """The reading as its definition: S_f is one gradient step, of unit size,
+    on L(S) = (1/N) sum_n beta_n ||S k_n - v_n||^2 / 2 taken from the decayed
+    state alpha_f S_{f-1}; the gradient comes from torch autograd in fp64, an
+    independent route to the same update (likewise z with values 1)."""
+    import torch
+    rng = np.random.default_rng(58)
+    q, k, v, a, b, s, z = _frame_case(rng, B=1, H=1, F=3, N=6, dk=5, dv=3)
+    N, F = 6, 3
+    kh = k / np.sqrt((k * k).sum(-1, keepdims=True) + 1e-6)      # the oracle's eps (pinned above)
+    S = torch.tensor(s[0, 0].T.copy(), dtype=torch.float64)       # S = M^T  [dv][dk]
+    Z = torch.tensor(z[0, 0].copy(), dtype=torch.float64)          # [dk]
+    for f in range(F):
+        K = torch.tensor(kh[0, 0, f * N:(f + 1) * N])
+        V = torch.tensor(v[0, 0, f * N:(f + 1) * N])
+        be = torch.tensor(b[0, 0, f * N:(f + 1) * N])
+        S0 = (a[0, 0, f] * S).clone().requires_grad_(True)
+        loss = 0.5 * (be[:, None] * (K @ S0.T - V) ** 2).sum() / N
+        loss.backward()
+        S = (S0 - S0.grad).detach()
+        Z0 = (a[0, 0, f] * Z).clone().requires_grad_(True)
+        lz = 0.5 * (be * (K @ Z0 - 1.0) ** 2).sum() / N
+        lz.backward()
+        Z = (Z0 - Z0.grad).detach()
+    _, s_out, z_out = oracle_mod.gdn_framewise(q, k, v, a, b, N, s, z)
+    np.testing.assert_allclose(s_out[0, 0], S.numpy().T, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(z_out[0, 0], Z.numpy(), rtol=1e-12, atol=1e-13)
 
 
 def test_framewise_beta_zero_readout_is_decay_free(oracle_mod):
@@ -536,6 +595,61 @@ def test_framewise_beta_zero_readout_is_decay_free(oracle_mod):
     pa = a.prod(axis=-1)
     np.testing.assert_allclose(s_out, pa[..., None, None] * s, rtol=1e-13, atol=1e-15)
     np.testing.assert_allclose(z_out, pa[..., None] * z, rtol=1e-13, atol=1e-15)
+
+
+def test_framewise_token_order_inside_a_frame_does_not_matter(oracle_mod):
+    """A frame is updated at once: permuting the tokens inside each frame
+    permutes their outputs the same way and leaves both states unchanged
+    (the token-sequential reading fails this)."""
+    rng = np.random.default_rng(59)
+    q, k, v, a, b, s, z = _frame_case(rng, F=3, N=6)
+    N, F = 6, 3
+    perm = np.concatenate([f * N + rng.permutation(N) for f in range(F)])
+    o1, s1, z1 = oracle_mod.gdn_framewise(q, k, v, a, b, N, s, z)
+    o2, s2, z2 = oracle_mod.gdn_framewise(q[:, :, perm], k[:, :, perm], v[:, :, perm], a, b[:, :, perm],
+                                          N, s, z)
+    np.testing.assert_allclose(o2, o1[:, :, perm], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(s2, s1, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(z2, z1, rtol=1e-12, atol=1e-13)
+
+
+def test_framewise_repeated_token_equals_one_token(oracle_mod):
+    """A frame of N copies of one token (same k, v, beta) has the mean of N
+    equal terms: it equals a one-token frame of that token."""
+    rng = np.random.default_rng(60)
+    q1, k1, v1, a, b1, s, z = _frame_case(rng, F=3, N=1)
+    N = 4
+    rep = lambda x: np.repeat(x, N, axis=2)
+    qN = np.abs(rng.standard_normal(rep(q1).shape))
+    o1, s1, z1 = oracle_mod.gdn_framewise(q1, k1, v1, a, b1, 1, s, z)
+    oN, sN, zN = oracle_mod.gdn_framewise(qN, rep(k1), rep(v1), a, rep(b1), N, s, z)
+    np.testing.assert_allclose(sN, s1, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(zN, z1, rtol=1e-12, atol=1e-13)
+    qh = unit(qN)
+    ref = np.einsum("bhfij,bhfni->bhfnj", np.stack([oracle_mod.gdn_framewise(
+        q1[:, :, :f + 1], k1[:, :, :f + 1], v1[:, :, :f + 1], a[:, :, :f + 1], b1[:, :, :f + 1], 1, s, z)[1]
+        for f in range(3)], axis=2), qh.reshape(1, 2, 3, N, -1))
+    den = np.einsum("bhfi,bhfni->bhfn", np.stack([oracle_mod.gdn_framewise(
+        q1[:, :, :f + 1], k1[:, :, :f + 1], v1[:, :, :f + 1], a[:, :, :f + 1], b1[:, :, :f + 1], 1, s, z)[2]
+        for f in range(3)], axis=2), qh.reshape(1, 2, 3, N, -1))
+    np.testing.assert_allclose(oN, (ref / den[..., None]).reshape(oN.shape), rtol=1e-11, atol=1e-12)
+
+
+def test_framewise_contraction_bound(oracle_mod):
+    """beta in [0, 1] and unit keys: I - G_f has eigenvalues in [0, 1], so
+    ||M_f||_2 <= alpha_f ||M_{f-1}||_2 + max_n ||v_n|| for frames of 880
+    tokens (a frame-sized write would blow up with the plain sum)."""
+    rng = np.random.default_rng(61)
+    q, k, v, a, b, s, z = _frame_case(rng, B=1, H=1, F=1, N=880, dk=16, dv=8)
+    norm2 = lambda m: np.linalg.norm(m, 2)
+    M = s[0, 0]
+    for f in range(5):
+        qf, kf, vf = (rng.standard_normal(x.shape) for x in (q, k, v))
+        bf = rng.uniform(0, 1, b.shape)
+        _, s_out, _ = oracle_mod.gdn_framewise(np.abs(qf), kf, vf, a, bf, 880, M[None, None], z)
+        bound = a[0, 0, 0] * norm2(M) + np.linalg.norm(vf[0, 0], axis=-1).max()
+        assert norm2(s_out[0, 0]) <= bound * (1 + 1e-12)
+        M = s_out[0, 0]
 
 
 def test_framewise_constant_values_read_back(oracle_mod):
@@ -560,31 +674,6 @@ def test_framewise_shift_equivariance(oracle_mod):
     np.testing.assert_allclose(o2, o1 + c, rtol=1e-10, atol=1e-11)
     np.testing.assert_allclose(s2, s1 + z1[..., None] * c, rtol=1e-11, atol=1e-12)
     np.testing.assert_allclose(z2, z1, rtol=0, atol=0)
-
-
-def test_framewise_orthonormal_keys_normalised_linear_attention(oracle_mod):
-    """Orthonormal keys, zero states: nothing is corrected, so each output is
-    the normalised linear attention sum_s w_s beta_s (k_s . q_t) v_s divided by
-    sum_s w_s beta_s (k_s . q_t), with w_s the product of the decays of the
-    frames after s's frame up to t's frame."""
-    rng = np.random.default_rng(55)
-    F, N, dk, dv = 3, 4, 12, 3
-    T = F * N
-    Qo, _ = np.linalg.qr(rng.standard_normal((dk, dk)))
-    k = Qo[:T][None, None]
-    q = np.abs(rng.standard_normal((1, 1, T, dk)))
-    v = rng.standard_normal((1, 1, T, dv))
-    a = rng.uniform(0.3, 0.9, (1, 1, F))
-    b = rng.uniform(0.2, 1.0, (1, 1, T))
-    out, _, _ = oracle_mod.gdn_framewise(q, k, v, a, b, N)
-    qh = unit(q)[0, 0]
-    ref = np.empty((T, dv))
-    for t in range(T):
-        ft = t // N
-        w = np.array([np.prod(a[0, 0, s // N + 1:ft + 1]) for s in range(t + 1)])
-        c = w * b[0, 0, :t + 1] * (k[0, 0, :t + 1] @ qh[t])
-        ref[t] = c @ v[0, 0, :t + 1] / c.sum()
-    np.testing.assert_allclose(out[0, 0], ref, rtol=1e-11, atol=1e-12)
 
 
 def test_framewise_split_across_calls(oracle_mod):
