@@ -220,7 +220,7 @@ def bench_attention(args):
 def bench_framewise(args):
     """Frame-wise GDN with a normalised readout (gdn_fwd_framewise): one step
     is one call over the workload's frames with both states carried in place.
-    The call is four launches (prologue, segment walk, correction, readout);
+    The call is three launches (frame summaries, scan over frames, readout);
     the roofline figure is the call's algorithmic bytes over its duration."""
     import torch
     import oracle
@@ -228,7 +228,6 @@ def bench_framewise(args):
     from linear_attention_recurrence_deltanet_amd.inputs import FRAME_WORKLOADS, make_frame_call, to_numpy64
 
     wl = FRAME_WORKLOADS[args.workload]
-    chunk = args.chunk or wl.chunk
     lib = gdn.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -242,7 +241,7 @@ def bench_framewise(args):
     state = torch.zeros(wl.B, wl.H, wl.dk, wl.dv, device=dev)
     z = torch.zeros(wl.B, wl.H, wl.dk, device=dev)
     outs = [torch.empty(wl.B, wl.H, T, wl.dv, dtype=out_dt, device=dev) for _ in range(2)]
-    ws_bytes = int(lib.gdn_framewise_workspace_bytes(wl.B, wl.H, wl.F, wl.N, wl.dk, wl.dv, chunk, None))
+    ws_bytes = int(lib.gdn_framewise_workspace_bytes(wl.B, wl.H, wl.F, wl.N, wl.dk, wl.dv, 0, None))
     workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     P = lambda t: ctypes.c_void_p(t.data_ptr())
@@ -250,7 +249,7 @@ def bench_framewise(args):
     for i, g in enumerate(sets):
         o = gdn.make_opts(torch.bfloat16, out_dt, True, 1.0, 1e-6, stream, workspace, out_gate=g["out_gate"])
         calls.append(((P(g["q"]), P(g["k"]), P(g["v"]), P(g["alpha"]), P(g["beta"]), P(state), P(z),
-                       P(outs[i % 2]), P(state), P(z), wl.B, wl.H, wl.F, wl.N, wl.dk, wl.dv, chunk),
+                       P(outs[i % 2]), P(state), P(z), wl.B, wl.H, wl.F, wl.N, wl.dk, wl.dv, 0),
                       ctypes.pointer(o)))
     fn = lambda c: lib.gdn_fwd_framewise(*c[0], c[1])
     for i in range(args.warmup):
@@ -296,7 +295,7 @@ def bench_framewise(args):
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "F": wl.F, "N": wl.N, "T": T,
-                   "dk": wl.dk, "dv": wl.dv, "chunk": chunk, "entry": "gdn_fwd_framewise",
+                   "dk": wl.dk, "dv": wl.dv, "entry": "gdn_fwd_framewise",
                    "out_dtype": args.out_dtype, "state": "fp32 numerator and denominator carried",
                    "input_sets": nsets, "workspace_bytes": ws_bytes},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -304,7 +303,7 @@ def bench_framewise(args):
                      "traffic": read_traffic(kernel_source_hash(), wl.name) if args.out_dtype == "f32" else None},
         "kernel": {"avg_ms": call_ms, "p50_ms": statistics.median(per),
                    "p99_ms": sorted(per)[min(len(per) - 1, int(0.99 * len(per)))],
-                   "algorithmic_bytes": alg_bytes, "launches_per_call": 4},
+                   "algorithmic_bytes": alg_bytes, "launches_per_call": 3},
     }
     if not args.no_cpu:
         names = ("q", "k", "v", "alpha", "beta", "out_gate")
@@ -320,8 +319,8 @@ def bench_framewise(args):
             if el >= args.cpu_seconds:
                 break
         res["cpu_baseline"] = {"value": n * wl.B * T / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-                               "sample": f"{n} full calls of the same workload in {el:.1f} s, fp64 token "
-                                         f"loop vectorised over heads (numpy, one thread)"}
+                               "sample": f"{n} full calls of the same workload in {el:.1f} s, fp64 loop "
+                                         f"over frames vectorised over heads (numpy)"}
     print(json.dumps(res), flush=True)
 
 

@@ -13,9 +13,6 @@
 namespace {
 
 constexpr int STEP_CHUNK = 64;   // token tile of gdn_fwd_step
-// default token tile of gdn_fwd_framewise: with frames that barely decay inside, 32-token chunks
-// keep the denominator's error lower (rel-L2 1.0e-3 against 1.3e-3 with 64)
-constexpr int FRAME_CHUNK = 32;
 
 thread_local char g_last_error[512] = "";
 
@@ -303,89 +300,64 @@ size_t bidir_workspace(int B, int H, int T, int dk, int dv, int chunk, const gdn
     return T == 0 ? 0 : plane_bytes(B, H, T, dv) + pl.ws_bytes;
 }
 
-// Frame-wise scan with a normalised readout.  Workspace, each part 256-byte
-// aligned: decay per token [B*H][T] bf16, values [v | 1 0 ...] [B*H][T][dv+64]
-// bf16, state [M | z 0 ...] [B*H][dk][dv+64] fp32, scan outputs
-// [B*H][T][dv+64] fp32, then the scan's own split-sequence data.
-struct FrameLayout {
-    size_t alpha, vaug, state, oaug, seg, total;
-};
-
-size_t r256(size_t n) { return (n + 255) & ~(size_t)255; }
-
-// Limits: element indices of the prologue and epilogue over all heads, and
-// the scan's per-head byte offsets of its fp32 outputs, stay below 2^31.
-bool frame_shape_ok(int B, int H, int F, int N, int dk, int dv, int chunk) {
+// Frame-wise Gated DeltaNet with a normalised readout: frame summaries, a
+// scan over frames, the readout (gdn_frame.hip).  The workspace holds the
+// summaries of every (head, frame, token split), each frame's state in the
+// form the readout reads, and z_f.
+bool frame_shape_ok(int B, int H, int F, int N, int dk, int dv) {
     return B > 0 && H > 0 && F >= 0 && N > 0 && (dk == 64 || dk == 128) && (dv == 64 || dv == 128) &&
-           (chunk == 32 || chunk == 64) &&
-           (long long)B * H * F * N * (dv + 64) < 0x7fffffffLL &&
-           (long long)F * N * (dv + 64) * 4 < 0x7fffffffLL;
-}
-
-FrameLayout frame_layout(int B, int H, int F, int N, int dk, int dv, int chunk) {
-    FrameLayout L{};
-    const size_t bh = (size_t)B * H, T = (size_t)F * N, dvp = (size_t)dv + 64;
-    L.alpha = 0;
-    L.vaug = L.alpha + r256(bh * T * 2);
-    L.state = L.vaug + r256(bh * T * dvp * 2);
-    L.oaug = L.state + r256(bh * dk * dvp * 4);
-    L.seg = L.oaug + r256(bh * T * dvp * 4);
-    L.total = L.seg + make_plan(0, B, H, (int)T, dk, (int)dvp, chunk).ws_bytes;
-    return L;
+           (long long)B * H <= 65535 && F <= 65535;
 }
 
 int run_framewise(const void* q, const void* k, const void* v, const void* alpha, const void* beta,
                   const float* state_in, const float* z_in, void* out, float* state_out, float* z_out,
-                  int B, int H, int F, int N, int dk, int dv, int chunk, const gdn_opts* opts) {
+                  int B, int H, int F, int N, int dk, int dv, const gdn_opts* opts) {
     g_last_error[0] = '\0';
     gdn_opts o;
     if (opts) o = *opts; else defaults(&o);
     if (B <= 0 || H <= 0 || F < 0 || N <= 0) return fail(GDN_ERR_ARG, "B, H and N must be positive, F non-negative");
     if (o.in_dtype != GDN_BF16) return fail(GDN_ERR_UNSUPPORTED, "frame-wise inputs must be bf16");
     if (o.out_dtype != GDN_BF16 && o.out_dtype != GDN_F32) return fail(GDN_ERR_ARG, "bad out_dtype");
-    if (!frame_shape_ok(B, H, F, N, dk, dv, chunk))
-        return fail(GDN_ERR_UNSUPPORTED, "frame-wise scan: dk and dv 64 or 128, chunk 32 or 64, "
-                    "B*H*F*N*(dv+64) and F*N*(dv+64)*4 below 2^31");
-    const int T = F * N;
-    // the scan's own checks (pointers, alignment) on the caller's buffers
-    int st = validate(q, k, v, alpha, beta, state_in, out, state_out, B, H, T, dk, dv, chunk, o);
-    if (st != GDN_OK) return st;
-    if ((z_in && !aligned16(z_in)) || (z_out && !aligned16(z_out)))
-        return fail(GDN_ERR_ARG, "z_in and z_out must be 16-byte aligned");
-    const FrameLayout L = frame_layout(B, H, F, N, dk, dv, chunk);
-    if (!o.workspace || o.workspace_bytes < L.total || !aligned16(o.workspace)) {
+    if (!frame_shape_ok(B, H, F, N, dk, dv))
+        return fail(GDN_ERR_UNSUPPORTED, "frame-wise: dk and dv 64 or 128, B*H and F at most 65535");
+    if ((long long)F * N > 0x7fffffffLL) return fail(GDN_ERR_ARG, "F*N too large");
+    if (F > 0) {
+        if (!q || !k || !v || !alpha || !beta || !out)
+            return fail(GDN_ERR_ARG, "q, k, v, alpha, beta and out must be non-null when F > 0");
+        if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+            return fail(GDN_ERR_ARG, "q, k, v and out must be 16-byte aligned");
+        if (o.out_gate && !aligned16(o.out_gate)) return fail(GDN_ERR_ARG, "out_gate must be 16-byte aligned");
+        if ((reinterpret_cast<uintptr_t>(alpha) & 1u) || (reinterpret_cast<uintptr_t>(beta) & 1u))
+            return fail(GDN_ERR_ARG, "alpha and beta must be aligned to their element size");
+    }
+    if ((state_in && !aligned16(state_in)) || (state_out && !aligned16(state_out)) ||
+        (z_in && !aligned16(z_in)) || (z_out && !aligned16(z_out)))
+        return fail(GDN_ERR_ARG, "states must be 16-byte aligned");
+    size_t off_mt = 0, off_zf = 0;
+    const size_t need = F > 0 ? gdn::frame_workspace(B, H, F, N, dk, dv, &off_mt, &off_zf) : 0;
+    if (need > 0 && (!o.workspace || o.workspace_bytes < need || !aligned16(o.workspace))) {
         char n[32];
-        snprintf(n, sizeof(n), "%zu", L.total);
+        snprintf(n, sizeof(n), "%zu", need);
         return fail(GDN_ERR_ARG, "gdn_fwd_framewise needs a 16-byte aligned workspace of "
                     "gdn_framewise_workspace_bytes() = %s bytes", n);
     }
-    char* w = reinterpret_cast<char*>(o.workspace);
+    if (F == 0 && !state_out && !z_out) return GDN_OK;
     gdn::FrameArgs a;
-    a.v = v; a.alpha = alpha; a.state_in = state_in; a.z_in = z_in;
+    a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta;
+    a.state_in = state_in; a.z_in = z_in; a.out = out; a.state_out = state_out; a.z_out = z_out;
+    a.out_gate = o.out_gate;
     a.B = B; a.H = H; a.F = F; a.N = N; a.dk = dk; a.dv = dv;
     a.gate_logits = o.gate_logits ? 1 : 0;
-    a.alpha_tok = w + L.alpha;
-    a.v_aug = w + L.vaug;
-    a.state_aug = reinterpret_cast<float*>(w + L.state);
-    a.out_aug = reinterpret_cast<const float*>(w + L.oaug);
-    a.out_gate = o.out_gate;
-    a.out = out;
+    a.qk_l2norm = o.qk_l2norm ? 1 : 0;
     a.out_bf16 = o.out_dtype == GDN_BF16;
-    a.state_out = state_out;
-    a.z_out = z_out;
-    hipStream_t stream = reinterpret_cast<hipStream_t>(o.stream);
-    hipError_t e = gdn::launch_frame_prep(a, stream);
-    if (e != hipSuccess) return fail(GDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
-    gdn_opts os = o;
-    os.out_dtype = GDN_F32;
-    os.out_gate = nullptr;
-    os.workspace = w + L.seg;
-    os.workspace_bytes = o.workspace_bytes - L.seg;
-    const bool has_in = state_in || z_in, want = state_out || z_out;
-    st = scan(q, k, a.v_aug, a.alpha_tok, beta, has_in ? a.state_aug : nullptr, w + L.oaug,
-              want ? a.state_aug : nullptr, B, H, T, dk, dv + 64, chunk, os, 0, 0);
-    if (st != GDN_OK) return st;
-    e = gdn::launch_frame_readout(a, stream);
+    a.eps = o.eps;
+    gdn::frame_plan(B, H, F, N, dk, dv, &a.nsp, &a.nts);
+    char* w = reinterpret_cast<char*>(o.workspace);
+    a.sums = reinterpret_cast<float*>(w);
+    a.mt_hi = reinterpret_cast<uint16_t*>(w + off_mt);
+    a.mt_lo = reinterpret_cast<uint16_t*>(w + off_mt + (off_zf - off_mt) / 2);
+    a.zf = reinterpret_cast<float*>(w + off_zf);
+    hipError_t e = gdn::launch_framewise(a, reinterpret_cast<hipStream_t>(o.stream));
     if (e != hipSuccess) return fail(GDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return GDN_OK;
 }
@@ -491,16 +463,16 @@ size_t gdn_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, const
 int gdn_fwd_framewise(const void* q, const void* k, const void* v, const void* alpha, const void* beta,
                       const float* state_in, const float* z_in, void* out, float* state_out, float* z_out,
                       int B, int H, int F, int N, int dk, int dv, int chunk, const gdn_opts* opts) {
-    return run_framewise(q, k, v, alpha, beta, state_in, z_in, out, state_out, z_out, B, H, F, N, dk, dv,
-                         chunk > 0 ? chunk : FRAME_CHUNK, opts);
+    (void)chunk;
+    return run_framewise(q, k, v, alpha, beta, state_in, z_in, out, state_out, z_out, B, H, F, N, dk, dv, opts);
 }
 
 size_t gdn_framewise_workspace_bytes(int B, int H, int F, int N, int dk, int dv, int chunk,
                                      const gdn_opts* opts) {
     (void)opts;
-    if (chunk <= 0) chunk = FRAME_CHUNK;
-    if (!frame_shape_ok(B, H, F, N, dk, dv, chunk)) return 0;
-    return frame_layout(B, H, F, N, dk, dv, chunk).total;
+    (void)chunk;
+    if (!frame_shape_ok(B, H, F, N, dk, dv) || F == 0) return 0;
+    return gdn::frame_workspace(B, H, F, N, dk, dv, nullptr, nullptr);
 }
 
 const char* gdn_strerror(int status) {

@@ -87,29 +87,34 @@ int attn_splits(int B, int H, int Nq, const int n[3]);
 size_t attn_workspace(int B, int H, int Nq, int d, int nsplit);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
 
-// Frame-wise scan with a normalised readout (gdn_frame.hip): the token-wise
-// scan runs on values [v | 1 0 ... 0] and state [M | z 0 ... 0] (dv + 64
-// columns) with the frame's decay on its first token; the prologue builds
-// these in the workspace, the epilogue divides by the denominator column,
-// applies the output gate and unpacks the state.  bf16 inputs.
+// Frame-wise Gated DeltaNet with a normalised readout (gdn_frame.hip): frame
+// summaries, a scan over frames, the readout; bf16 inputs.
 struct FrameArgs {
-    const void* v;           // [B*H][T][dv], T = F * N
+    const void* q;           // [B*H][T][dk], T = F * N
+    const void* k;           // [B*H][T][dk]
+    const void* v;           // [B*H][T][dv]
     const void* alpha;       // [B*H][F] decay per frame (logits if gate_logits)
+    const void* beta;        // [B*H][T] write strength (logits if gate_logits)
     const float* state_in;   // [B*H][dk][dv] or null
     const float* z_in;       // [B*H][dk] or null
-    int B, H, F, N, dk, dv;
-    int gate_logits;
-    void* alpha_tok;         // workspace: [B*H][T] decay per token
-    void* v_aug;             // workspace: [B*H][T][dv + 64]
-    float* state_aug;        // workspace: [B*H][dk][dv + 64]
-    const float* out_aug;    // workspace: [B*H][T][dv + 64] outputs of the scan
-    const void* out_gate;    // [B*H][T][dv] or null
     void* out;               // [B*H][T][dv] fp32 or bf16
-    int out_bf16;
     float* state_out;        // [B*H][dk][dv] or null
     float* z_out;            // [B*H][dk] or null
+    const void* out_gate;    // [B*H][T][dv] or null
+    int B, H, F, N, dk, dv;
+    int gate_logits, qk_l2norm, out_bf16;
+    float eps;
+    int nsp;                 // token splits of a frame's summaries
+    int nts;                 // token splits of the readout
+    float* sums;             // workspace: [B*H][F][nsp][dk][dk + dv + 16] partial summaries
+    uint16_t* mt_hi;         // workspace: [B*H][F][dv][dk] M_f^T, bf16 hi part
+    uint16_t* mt_lo;         // workspace: [B*H][F][dv][dk] bf16 lo part
+    float* zf;               // workspace: [B*H][F][dk] z_f
 };
-hipError_t launch_frame_prep(const FrameArgs& a, hipStream_t s);
-hipError_t launch_frame_readout(const FrameArgs& a, hipStream_t s);
+// Token splits of the launch plan, and the workspace (bytes) with the
+// offsets of mt_hi and zf (mt_lo follows mt_hi at the same distance).
+void frame_plan(int B, int H, int F, int N, int dk, int dv, int* nsp, int* nts);
+size_t frame_workspace(int B, int H, int F, int N, int dk, int dv, size_t* off_mt, size_t* off_zf);
+hipError_t launch_framewise(const FrameArgs& a, hipStream_t s);
 
 }  // namespace gdn

@@ -201,8 +201,7 @@ def _frame(lib, q=16, k=16, v=16, a=16, b=16, sin=None, zin=None, out=16, sout=N
     (dict(F=-1), gdn.GDN_ERR_ARG),
     (dict(dk=32), gdn.GDN_ERR_UNSUPPORTED),
     (dict(dv=32), gdn.GDN_ERR_UNSUPPORTED),
-    (dict(chunk=128), gdn.GDN_ERR_UNSUPPORTED),
-    (dict(H=1, F=1, N=(1 << 31) // (128 * 4)), gdn.GDN_ERR_UNSUPPORTED),   # per-head fp32 outputs above 2 GiB
+    (dict(B=2, H=40000), gdn.GDN_ERR_UNSUPPORTED),   # B*H above the grid's 65535
     (dict(q=None, ws=4096, ws_bytes=1 << 40), gdn.GDN_ERR_ARG),
     (dict(zin=8, ws=4096, ws_bytes=1 << 40), gdn.GDN_ERR_ARG),    # misaligned z_in
     (dict(ws=4096, ws_bytes=1000), gdn.GDN_ERR_ARG),               # workspace too small
@@ -213,20 +212,16 @@ def test_framewise_argument_errors_are_synchronous(lib, kw, status):
 
 
 def test_framewise_workspace_query(lib):
-    # per-token decay, values [v | 1 0 ...], state [M | z 0 ...], fp32 scan outputs, segment data
+    # partial frame summaries [B*H][F][nsp][dk][dk + dv + 16] fp32, each frame's
+    # M^T as bf16 hi and lo [B*H][F][dv][dk], z_f [B*H][F][dk] fp32
     r = lambda n: (n + 255) // 256 * 256
-    B, H, F, N, dk, dv = 1, 16, 3, 880, 64, 64
-    T, dvp = F * N, dv + 64
-    parts = r(B * H * T * 2) + r(B * H * T * dvp * 2) + r(B * H * dk * dvp * 4) + r(B * H * T * dvp * 4)
-    seg = lib.gdn_workspace_bytes(B, H, T, dk, dvp, 32, None)
-    n = lib.gdn_framewise_workspace_bytes(B, H, F, N, dk, dv, 0, None)       # default chunk 32
-    assert n == parts + seg
-    assert lib.gdn_framewise_workspace_bytes(B, H, F, N, dk, dv, 32, None) == n
-    assert lib.gdn_framewise_workspace_bytes(B, H, F, N, dk, dv, 64, None) == \
-        parts + lib.gdn_workspace_bytes(B, H, T, dk, dvp, 64, None)
-    assert lib.gdn_framewise_workspace_bytes(B, H, F, N, 32, dv, 0, None) == 0
-    assert lib.gdn_framewise_workspace_bytes(B, H, F, N, dk, dv, 128, None) == 0
-    assert lib.gdn_framewise_workspace_bytes(B, H, 0, N, dk, dv, 0, None) == r(B * H * dk * dvp * 4)
+    for (B, H, F, N, dk, dv, nsp) in ((1, 16, 3, 880, 64, 64, 4), (1, 16, 3, 880, 128, 128, 2),
+                                      (2, 24, 1, 880, 128, 128, 2), (1, 1, 2, 100, 64, 128, 1)):
+        bhf = B * H * F
+        want = r(bhf * nsp * dk * (dk + dv + 16) * 4) + 2 * r(bhf * dv * dk * 2) + r(bhf * dk * 4)
+        assert lib.gdn_framewise_workspace_bytes(B, H, F, N, dk, dv, 0, None) == want
+    assert lib.gdn_framewise_workspace_bytes(1, 16, 3, 880, 32, 64, 0, None) == 0
+    assert lib.gdn_framewise_workspace_bytes(1, 16, 0, 880, 64, 64, 0, None) == 0
 
 
 # last: it reloads the binding module (the fixture's library keeps the old types)

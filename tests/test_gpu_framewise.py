@@ -2,10 +2,11 @@
 (gdn_fwd_framewise; SANA-Streaming section 2.1, "Frame-wise Gated DeltaNet":
 one decay per frame, a write strength per token, a numerator and a
 denominator state carried across chunks, an output gate) against the fp64
-oracle (oracle.gdn_framewise) on the same bits: segmented and unsegmented
-scans, d_k = d_v = 64 and 128, frames that do not fill whole chunks, both
-states carried over calls and updated in place, gate logits, bf16 outputs,
-a call without frames."""
+oracle (oracle.gdn_framewise) on the same bits: the streaming shapes
+(summaries split over tokens), many heads, every (d_k, d_v) pair, ragged
+frame lengths down to one token, both states carried over calls and updated
+in place, gate logits, no output gate, bf16 outputs, a call without
+frames."""
 import numpy as np
 import pytest
 import torch
@@ -16,11 +17,11 @@ from linear_attention_recurrence_deltanet_amd.inputs import FRAME_WORKLOADS, mak
 pytestmark = pytest.mark.gpu
 
 
-def _run(gdn, oracle, wl, calls, *, B=None, H=None, F=None, N=None, chunk=0, gate=True, logits=False,
+def _run(gdn, oracle, wl, calls, *, B=None, H=None, F=None, N=None, gate=True, logits=False,
          out_dtype=torch.float32, in_place=False, what=""):
     N = wl.N if N is None else N
     announce(f"framewise {what} {wl.name} calls={calls} B={B or wl.B} H={H or wl.H} F={F or wl.F} N={N} "
-             f"chunk={chunk} gate={gate} logits={logits} out={out_dtype} in_place={in_place}")
+             f"gate={gate} logits={logits} out={out_dtype} in_place={in_place}")
     g_outs, o_outs = [], []
     gs = gz = os_ = oz = None
     for c in range(calls):
@@ -30,7 +31,7 @@ def _run(gdn, oracle, wl, calls, *, B=None, H=None, F=None, N=None, chunk=0, gat
         kw = dict(out_dtype=out_dtype, gate_logits=logits, out_gate=g["out_gate"] if gate else None)
         if in_place and gs is not None:
             kw.update(state_out=gs, z_out=gz)
-        o, gs, gz = gdn.fwd_framewise(g["q"], g["k"], g["v"], g[a_key], g[b_key], N, gs, gz, chunk, **kw)
+        o, gs, gz = gdn.fwd_framewise(g["q"], g["k"], g["v"], g[a_key], g[b_key], N, gs, gz, **kw)
         g_outs.append(o.to("cpu", torch.float64).numpy())
         q, k, v, a, b = (to_numpy64(d[n]) for n in ("q", "k", "v", a_key, b_key))
         if logits:
@@ -48,27 +49,34 @@ def _run(gdn, oracle, wl, calls, *, B=None, H=None, F=None, N=None, chunk=0, gat
 
 
 def test_framewise_stream_d64(gdn_lib, oracle_mod):
-    # 16 heads, 3 frames of 880 tokens: segment walk plus correction
+    # 16 heads, 3 frames of 880 tokens: summaries split four ways per frame
     _run(gdn_lib, oracle_mod, FRAME_WORKLOADS["frame_stream_h16_d64"], 1, what="stream")
 
 
 def test_framewise_rollout_d128_carried_in_place(gdn_lib, oracle_mod):
-    # both states carried over three calls, updated in place (d = 128)
-    _run(gdn_lib, oracle_mod, FRAME_WORKLOADS["frame_rollout_h16_d128"], 3, H=3, in_place=True,
+    # all 16 heads, both states carried over three calls, updated in place (d = 128)
+    _run(gdn_lib, oracle_mod, FRAME_WORKLOADS["frame_rollout_h16_d128"], 3, in_place=True,
          what="rollout")
 
 
-def test_framewise_many_heads_unsegmented(gdn_lib, oracle_mod):
-    # 48 heads of 128, one frame: unsegmented walks
+def test_framewise_many_heads(gdn_lib, oracle_mod):
+    # 48 heads of 128, one frame per call
     _run(gdn_lib, oracle_mod, FRAME_WORKLOADS["frame_rollout_h16_d128"], 2, B=2, H=24, F=1,
-         what="unsegmented")
+         what="many-heads")
 
 
-@pytest.mark.parametrize("N,chunk", [(100, 64), (100, 32), (1, 64), (37, 32)])
-def test_framewise_ragged_frames(gdn_lib, oracle_mod, N, chunk):
-    # frame starts inside chunks, and one-token frames (a decay on every token)
-    F = max(2, 300 // N) if N > 1 else 150
-    _run(gdn_lib, oracle_mod, FRAME_WORKLOADS["frame_stream_h16_d64"], 2, H=2, F=F, N=N, chunk=chunk,
+@pytest.mark.parametrize("dk,dv", [(64, 128), (128, 64)])
+def test_framewise_mixed_head_sizes(gdn_lib, oracle_mod, dk, dv):
+    wl = FRAME_WORKLOADS["frame_stream_h16_d64"].replace(dk=dk, dv=dv)
+    _run(gdn_lib, oracle_mod, wl, 2, H=3, F=2, N=300, what=f"dk{dk}-dv{dv}")
+
+
+@pytest.mark.parametrize("N", [1, 7, 37, 100, 129])
+def test_framewise_ragged_frames(gdn_lib, oracle_mod, N):
+    # frames that end inside a 32-token step or a 16-token readout block,
+    # and one-token frames (the token-wise rule)
+    F = max(2, 300 // N) if N > 1 else 64
+    _run(gdn_lib, oracle_mod, FRAME_WORKLOADS["frame_stream_h16_d64"], 2, H=2, F=F, N=N,
          what=f"ragged N={N}")
 
 
@@ -78,10 +86,8 @@ def test_framewise_gate_logits(gdn_lib, oracle_mod):
     _run(gdn_lib, oracle_mod, wl, 2, H=4, F=2, N=300, gate=False, what="no-gate")
 
 
-def test_framewise_d128_chunk32_and_logits(gdn_lib, oracle_mod):
-    # d_k = d_v = 128: the scan runs on 192 value columns (three 64-column tiles)
+def test_framewise_d128_logits(gdn_lib, oracle_mod):
     wl = FRAME_WORKLOADS["frame_rollout_h16_d128"]
-    _run(gdn_lib, oracle_mod, wl, 2, H=3, F=2, N=400, chunk=32, what="d128-chunk32")
     _run(gdn_lib, oracle_mod, wl, 1, H=4, F=3, N=250, logits=True, what="d128-logits")
 
 

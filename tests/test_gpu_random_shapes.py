@@ -86,7 +86,7 @@ def test_random_shape_bidir(gdn_lib, oracle_mod, c):
     print(f"   out maxabs {r1[0]:.2e} rel {r1[1]:.2e} | state rel {r2[1]:.2e}", flush=True)
 
 
-@pytest.mark.parametrize("c", FRAME, ids=[f"H{c['H']}F{c['F']}N{c['N']}k{c['dk']}v{c['dv']}C{c['chunk']}"
+@pytest.mark.parametrize("c", FRAME, ids=[f"H{c['H']}F{c['F']}N{c['N']}k{c['dk']}v{c['dv']}"
                                           f"{'-logits' if c['gates'] else ''}" for c in FRAME])
 def test_random_shape_framewise(gdn_lib, oracle_mod, c):
     from linear_attention_recurrence_deltanet_amd.inputs import FRAME_WORKLOADS, make_frame_call
@@ -95,7 +95,7 @@ def test_random_shape_framewise(gdn_lib, oracle_mod, c):
     d = make_frame_call(wl, 0, H=c["H"], F=c["F"], N=c["N"])
     g = to_dev(d)
     a_key, b_key = ("alpha_logit", "beta_logit") if c["gates"] else ("alpha", "beta")
-    out, st, z = gdn_lib.fwd_framewise(g["q"], g["k"], g["v"], g[a_key], g[b_key], c["N"], chunk=c["chunk"],
+    out, st, z = gdn_lib.fwd_framewise(g["q"], g["k"], g["v"], g[a_key], g[b_key], c["N"],
                                        gate_logits=c["gates"], out_gate=g["out_gate"])
     torch.cuda.synchronize()
     q, k, v, a, b = (to_numpy64(d[n]) for n in ("q", "k", "v", a_key, b_key))
