@@ -115,6 +115,27 @@ int gdn_fwd_step(const void* q, const void* k, const void* v,
                  int B, int H, int T, int dk, int dv,
                  const gdn_opts* opts);
 
+/* Size of the static device array behind gdn_fwd_step_noalloc (64 MiB). */
+#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * gdn_fwd_step_noalloc: gdn_fwd_step for callers that cannot allocate
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments and results as gdn_fwd_step; opts->workspace is
+ * ignored: the scratch memory of the few-head launch plan lives in a static
+ * device array of GDN_NOALLOC_SCRATCH_BYTES, one per device, resolved at the
+ * first call on the current device.  Shapes whose plan needs more scratch than
+ * that return GDN_ERR_UNSUPPORTED.  The call allocates nothing.  Every call on
+ * a device shares that device's array: calls that overlap on one device
+ * (several streams or host threads) race, so serialise them.  Nothing in the
+ * array needs to start at zero.
+ */
+int gdn_fwd_step_noalloc(const void* q, const void* k, const void* v,
+                         const void* alpha, const void* beta,
+                         const float* state_in, void* out, float* state_out,
+                         int B, int H, int T, int dk, int dv,
+                         const gdn_opts* opts);
+
 /*
  * gdn_fwd_bidir: bidirectional Gated DeltaNet over one streaming chunk
  * (SANA-Streaming, section 4.1: the streaming model runs a forward scan from

@@ -364,6 +364,8 @@ int run_framewise(const void* q, const void* k, const void* v, const void* alpha
 
 }  // namespace
 
+int gdn::api_fail(int status, const char* msg) { return fail(status, "%s", msg); }
+
 extern "C" {
 
 void gdn_default_opts(gdn_opts* opts) {

@@ -5,6 +5,10 @@
 
 namespace gdn {
 
+// Record a message for gdn_last_error() on this thread and return status
+// (for entry points outside gdn_api.cpp).
+int api_fail(int status, const char* msg);
+
 // Arguments common to every forward launch.
 struct FwdArgs {
     const void* q;

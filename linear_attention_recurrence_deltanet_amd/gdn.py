@@ -19,7 +19,7 @@ GDN_OK, GDN_ERR_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_HIP = 0, -1, -2, -3
 GDN_BF16, GDN_F32 = 0, 1
 
 # every exported entry point of include/gdn.h
-EXPORTS = ("gdn_default_opts", "gdn_fwd_chunked", "gdn_fwd_step", "gdn_fwd_bidir",
+EXPORTS = ("gdn_default_opts", "gdn_fwd_chunked", "gdn_fwd_step", "gdn_fwd_step_noalloc", "gdn_fwd_bidir",
            "gdn_workspace_bytes", "gdn_bidir_workspace_bytes", "gdn_attn_sink_window",
            "gdn_attn_workspace_bytes", "gdn_fwd_framewise", "gdn_framewise_workspace_bytes",
            "gdn_strerror", "gdn_last_error", "gdn_version")
@@ -62,6 +62,8 @@ def load(path: str = LIB_PATH):
     lib.gdn_fwd_chunked.restype = i
     lib.gdn_fwd_step.argtypes = fwd_args + [ctypes.POINTER(GdnOpts)]
     lib.gdn_fwd_step.restype = i
+    lib.gdn_fwd_step_noalloc.argtypes = fwd_args + [ctypes.POINTER(GdnOpts)]
+    lib.gdn_fwd_step_noalloc.restype = i
     lib.gdn_fwd_bidir.argtypes = fwd_args + [i, ctypes.POINTER(GdnOpts)]
     lib.gdn_fwd_bidir.restype = i
     lib.gdn_workspace_bytes.argtypes = [i, i, i, i, i, i, ctypes.POINTER(GdnOpts)]
@@ -262,6 +264,23 @@ def fwd_step(q, k, v, alpha, beta, state_in=None, *, out=None, state_out=None,
                                _ptr(state_in), _ptr(out), _ptr(state_out),
                                B, H, T, dk, dv, ctypes.byref(opts)))
     _on_stream(stream, workspace, out, state_out)
+    return out, state_out
+
+
+def fwd_step_noalloc(q, k, v, alpha, beta, state_in=None, *, out=None, state_out=None,
+                     out_dtype=torch.float32, qk_l2norm=True, scale=1.0, eps=1e-6, stream=None,
+                     gate_logits: bool = False, out_gate=None):
+    """gdn_fwd_step_noalloc: gdn_fwd_step with its scratch in the library's
+    static device array (the call allocates nothing on the device; outputs
+    not given are allocated here, by torch, before the call)."""
+    B, H, T, dk, dv, out, state_out = _prep(q, k, v, alpha, beta, state_in, out, state_out,
+                                            out_dtype)
+    _check_gate(out_gate, q, B, H, T, dv)
+    opts = make_opts(q.dtype, out.dtype, qk_l2norm, scale, eps, stream, None, gate_logits, out_gate)
+    _check(load().gdn_fwd_step_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                       _ptr(state_in), _ptr(out), _ptr(state_out),
+                                       B, H, T, dk, dv, ctypes.byref(opts)))
+    _on_stream(stream, out, state_out)
     return out, state_out
 
 
