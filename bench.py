@@ -37,7 +37,10 @@ KERNEL_SOURCES = ("linear_attention_recurrence_deltanet_amd/csrc/gdn_pipe.hip",
                   "linear_attention_recurrence_deltanet_amd/csrc/gdn_fwd.hip",
                   "linear_attention_recurrence_deltanet_amd/csrc/gdn_fwd_single.hip",
                   "linear_attention_recurrence_deltanet_amd/csrc/gdn_frame.hip",
+                  "linear_attention_recurrence_deltanet_amd/csrc/gdn_attn.hip",
+                  "linear_attention_recurrence_deltanet_amd/csrc/gdn_noalloc.hip",
                   "linear_attention_recurrence_deltanet_amd/csrc/gdn_common.h",
+                  "linear_attention_recurrence_deltanet_amd/csrc/gdn_kernels.h",
                   "linear_attention_recurrence_deltanet_amd/csrc/gdn_api.cpp")
 
 

@@ -91,7 +91,10 @@ void gdn_default_opts(gdn_opts* opts);
  * gdn_fwd_chunked: the chunked forward over a whole sequence of T tokens per
  * head, starting from state_in and producing every o_t and the final state.
  * `chunk` is the kernel's token tile (32, 64 or 128); results do not depend
- * on it beyond rounding.  dk in {32, 64, 128}; dv in {32, 64, 128}.  With
+ * on it beyond rounding.  16 returns GDN_ERR_UNSUPPORTED: the products that
+ * contract over a chunk's tokens would fill half of a 32-deep fp16/bf16
+ * matrix-core step (half of each such product is zero padding), and it
+ * doubles the serial chunk steps of 32-token chunks for the same result.  dk in {32, 64, 128}; dv in {32, 64, 128}.  With
  * fp32 inputs the chunk is 32 or 64: 128 fp32 rows of a chunk do not fit on
  * chip, and chunk 128 returns GDN_ERR_UNSUPPORTED.
  * opts may be NULL (defaults).  Pointers must be 16-byte aligned.
@@ -187,16 +190,23 @@ size_t gdn_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk,
  * (SANA-Streaming, section 2.1 "Frame-wise Gated DeltaNet for Global
  * Accumulated Memory": per head, F frames of N tokens, a decay gate alpha in
  * R^F, a write gate beta in R^{F x N} and an output gate; a numerator state
- * S^kv and a denominator state S^z updated frame by frame with the delta-rule
- * correction and carried across chunks; appendix G.4 "Frame-wise delta-rule
- * update" and G.5 "Normalized readout" survive as headings only).  This
- * library reads them as follows, per (b, h), with unit-normalised q_t, k_t
- * and t = f*N + n:
+ * S^kv and a denominator state S^z updated frame by frame, not token by
+ * token, with the delta-rule correction, and carried across chunks; section
+ * 2.3 "Efficient GDN Kernel": frame summaries by reductions over the spatial
+ * tokens, a short scan over frames, the frame's queries read against the
+ * frame's state; appendix G.4 "Frame-wise delta-rule update" and G.5
+ * "Normalized readout" survive as headings only).  This library reads the
+ * update as one delta-rule step per frame on the frame's mean loss, per
+ * (b, h), with unit-normalised q_t, k_t and t = f*N + n:
  *
- *   at n == 0:  S <- alpha_f * S,  z <- alpha_f * z    (once per frame)
- *   S <- S (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
- *   z <- (I - beta_t k_t k_t^T) z + beta_t k_t          (a value of constant 1)
- *   out_t = (S q_t) / (z . q_t)                          (then * out_gate)
+ *   G_f = (1/N) sum_n beta_t k_t k_t^T
+ *   S_f = alpha_f * S_{f-1} (I - G_f) + (1/N) sum_n beta_t v_t k_t^T
+ *   z_f = alpha_f * z_{f-1} (I - G_f) + (1/N) sum_n beta_t k_t^T    (a d_k row)
+ *   out_t = (S_f q_t) / (z_f . q_t)        for every token t of frame f,
+ *                                          then times out_gate
+ *
+ * With beta in [0, 1] and unit keys, I - G_f has its eigenvalues in [0, 1]
+ * however many tokens a frame holds; at N = 1 this is the token-wise rule.
  *
  * Layouts (row-major, device memory owned by the caller, bf16 inputs):
  *   q, k        [B][H][F*N][dk]
@@ -207,16 +217,18 @@ size_t gdn_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk,
  *   z_in        [B][H][dk]       fp32 denominator state, or NULL (zero)
  *   out         [B][H][F*N][dv]  opts->out_dtype; opts->out_gate [B][H][F*N][dv]
  *   state_out   [B][H][dk][dv]   fp32, or NULL;  z_out [B][H][dk] fp32, or NULL
- * dk and dv are 64 or 128; chunk 32 or 64 (0: 32, the more accurate here:
- * inside a frame nothing decays); B*H*F*N*(dv+64) < 2^31 and
- * F*N*(dv+64)*4 < 2^31 (GDN_ERR_UNSUPPORTED otherwise).
- * state_out may alias state_in and z_out z_in.  The denominator has no sign
- * guarantee: the readout divides by it as it is (features that keep z . q
- * positive, such as non-negative ones, are the caller's part); a zero
- * denominator gives Inf/NaN like any division.
- * Precision: the numerator and denominator are one token-wise scan (as in
- * gdn_fwd_chunked) on values [v | 1] in fp32 outputs; the division and the
- * gate are fp32 with one rounding to out_dtype.
+ * dk and dv are 64 or 128; B*H and F at most 65535, F*N below 2^31
+ * (GDN_ERR_UNSUPPORTED / GDN_ERR_ARG otherwise).  `chunk` is not used (the
+ * frame is the unit of the scan); pass 0.  state_out may alias state_in and
+ * z_out z_in.  The denominator has no sign guarantee: the readout divides by
+ * it as it is (features that keep z . q positive, such as non-negative ones,
+ * are the caller's part); a zero denominator gives Inf/NaN like any division.
+ * Precision: the frame summaries are sums over the frame's tokens with fp32
+ * accumulation (bf16 inputs exact, normalised keys as bf16 hi + lo pairs);
+ * the scan over frames keeps S and z in fp32 and forms G_f S^T with both as
+ * bf16 hi + lo (three products); the readout forms S_f q_t with S_f as bf16
+ * hi + lo against the raw queries and z_f . q_t in fp32, divides in fp32 and
+ * rounds once to out_dtype.
  * Needs a workspace (16-byte aligned) of gdn_framewise_workspace_bytes()
  * bytes; returns GDN_ERR_ARG without it.  F == 0 copies the states.
  */
@@ -227,8 +239,8 @@ int gdn_fwd_framewise(const void* q, const void* k, const void* v,
                       int B, int H, int F, int N, int dk, int dv, int chunk,
                       const gdn_opts* opts);
 
-/* Workspace (bytes) of gdn_fwd_framewise for this shape and chunk (0: 32);
- * 0 for unsupported shapes. */
+/* Workspace (bytes) of gdn_fwd_framewise for this shape (chunk is not
+ * used); 0 for unsupported shapes and F == 0. */
 size_t gdn_framewise_workspace_bytes(int B, int H, int F, int N, int dk, int dv, int chunk,
                                      const gdn_opts* opts);
 

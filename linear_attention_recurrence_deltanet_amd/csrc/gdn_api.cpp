@@ -41,6 +41,12 @@ void defaults(gdn_opts* o) {
     o->out_gate = nullptr;
 }
 
+// Sizes the calls accept: the limits validate() enforces on B, H and T.
+bool sizes_ok(int B, int H, int T, int dk, int dv) {
+    return B > 0 && H > 0 && T >= 0 && (long long)B * H * 8 <= 0x7fffffffLL &&
+           (long long)T * (dk > dv ? dk : dv) * 4 <= 0x7fffffffLL;
+}
+
 int validate(const void* q, const void* k, const void* v, const void* alpha, const void* beta,
              const float* state_in, const void* out, const float* state_out,
              int B, int H, int T, int dk, int dv, int chunk, const gdn_opts& o) {
@@ -118,7 +124,7 @@ size_t seg_workspace(int in_f32, int B, int H, int dk, int dv, int nseg) {
 Plan pipe_plan(int B, int H, int T, int dk, int dv, int chunk) {
     Plan pl{};
     pl.pipe = true;
-    const int nchunks = (T + chunk - 1) / chunk;
+    const int nchunks = (int)(((long long)T + chunk - 1) / chunk);
     const long long bh = (long long)B * H;
     const long long base = bh * (dv / 64);                                  // workgroups, unsegmented
     const int cts = gdn::pipe_seg_tiles(dk, dv);
@@ -159,7 +165,7 @@ Plan make_plan(int in_f32, int B, int H, int T, int dk, int dv, int chunk) {
         return pl;
     }
     pl.waves = w;
-    const int nchunks = (T + chunk - 1) / chunk;
+    const int nchunks = (int)(((long long)T + chunk - 1) / chunk);
     const long long base = (long long)B * H * (w ? dv / (16 * w) : 1);
     int nseg = 1;
     if (nchunks >= 4 && base < 256) {
@@ -205,7 +211,7 @@ int scan(const void* q, const void* k, const void* v, const void* alpha, const v
     } else {
         if (pl.nseg > 1 && (!o.workspace || o.workspace_bytes < pl.ws_bytes)) {
             pl.nseg = 1;                       // no workspace: unsplit walk
-            pl.seg_chunks = (T + chunk - 1) / chunk;
+            pl.seg_chunks = (int)(((long long)T + chunk - 1) / chunk);
         }
         if (pl.seg_chunks < 1) pl.seg_chunks = 1;
         a.nseg = pl.nseg;
@@ -287,14 +293,14 @@ int run_bidir(const void* q, const void* k, const void* v, const void* alpha, co
 size_t workspace_for(int B, int H, int T, int dk, int dv, int chunk, const gdn_opts* opts) {
     gdn_opts o;
     if (opts) o = *opts; else defaults(&o);
-    if (B <= 0 || H <= 0 || T < 0 || !head_ok(dk) || !head_ok(dv)) return 0;
+    if (!sizes_ok(B, H, T, dk, dv) || !head_ok(dk) || !head_ok(dv)) return 0;
     if (chunk != 32 && chunk != 64 && chunk != 128) return 0;
     Plan pl = make_plan(o.in_dtype == GDN_F32, B, H, T, dk, dv, chunk);
     return pl.ws_bytes;
 }
 
 size_t bidir_workspace(int B, int H, int T, int dk, int dv, int chunk, const gdn_opts& o) {
-    if (B <= 0 || H <= 0 || T < 0 || !head_ok(dk) || !head_ok(dv)) return 0;
+    if (!sizes_ok(B, H, T, dk, dv) || !head_ok(dk) || !head_ok(dv)) return 0;
     if (chunk != 32 && chunk != 64 && chunk != 128) return 0;
     const Plan pl = make_plan(o.in_dtype == GDN_F32, B, H, T, dk, dv, chunk);
     return T == 0 ? 0 : plane_bytes(B, H, T, dv) + pl.ws_bytes;
