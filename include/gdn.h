@@ -98,6 +98,16 @@ void gdn_default_opts(gdn_opts* opts);
  * fp32 inputs the chunk is 32 or 64: 128 fp32 rows of a chunk do not fit on
  * chip, and chunk 128 returns GDN_ERR_UNSUPPORTED.
  * opts may be NULL (defaults).  Pointers must be 16-byte aligned.
+ * Magnitudes: the rule is linear in (v, S).  With bf16 inputs the kernels
+ * run each group of 16 value columns on v / s and S / s, s the power of two
+ * of the largest |state_in| of those columns or the largest |v| of the
+ * sequence's first chunk in them, and multiply the outputs and the final
+ * state by s (exact), so the fp16 operands formed from v, S and the chunk
+ * values stay near magnitude 1 and the accuracy holds at any common scale of
+ * v and state_in (tested from 2^-16 to 2^12).  Later values more than about
+ * 2^12 times that first maximum can overflow those operands.  Exception:
+ * bf16 calls with dk or dv = 32 use unscaled fp16 operands, accurate for
+ * |v| and |state| of about 2^-10 to 2^12.
  */
 int gdn_fwd_chunked(const void* q, const void* k, const void* v,
                     const void* alpha, const void* beta,

@@ -217,6 +217,7 @@ int scan(const void* q, const void* k, const void* v, const void* alpha, const v
         a.nseg = pl.nseg;
         a.seg_chunks = pl.seg_chunks;
         a.summA = nullptr; a.summB = nullptr; a.snap = nullptr; a.phi = nullptr; a.ostage = nullptr;
+        a.sscale = nullptr;
         if (pl.nseg > 1) {
             const size_t bh = (size_t)B * H;
             // maps of segments 0 .. nseg-2 (segmented walker) or of all nseg (pipelined)
@@ -229,6 +230,8 @@ int scan(const void* q, const void* k, const void* v, const void* alpha, const v
                 char* ph = reinterpret_cast<char*>(a.snap + bh * dk * dv);
                 a.phi = ph;
                 a.ostage = ph + bh * pl.nseg * (size_t)pl.seg_chunks * chunk * dk * 2;
+                a.sscale = reinterpret_cast<float*>(reinterpret_cast<char*>(a.ostage) +
+                                                    bh * pl.nseg * (size_t)pl.seg_chunks * chunk * dv * 2);
             }
         }
         if (pl.nseg > 1 && (reinterpret_cast<uintptr_t>(o.workspace) & 15u))

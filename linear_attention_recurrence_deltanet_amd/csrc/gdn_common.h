@@ -134,6 +134,16 @@ __device__ __forceinline__ typename Op::frag frag_at(const typename Op::elem* ba
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// Workgroup barrier for exchanges through LDS only.  __syncthreads() also
+// orders global memory, which on this target waits for every load and store
+// the wave has in flight (vmcnt(0)); loads issued ahead of their use would
+// then complete at the barrier.  This one waits for the wave's LDS operations
+// only; the memory clobber keeps the compiler from moving memory accesses
+// across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // ---------------------------------------------------------------------------
 // Raw buffer access: a 128-bit resource (base, byte size) in scalar registers
 // and a 32-bit per-lane byte offset.  Loads past `bytes` return zero and
@@ -143,6 +153,9 @@ typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr int kRsrcWord3 = 0x00020000;   // 32-bit data format, raw (untyped) access
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ float uniform(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
+}
 template <class T>
 __device__ __forceinline__ T* uniform(T* p) {
     const uint64_t v = reinterpret_cast<uint64_t>(p);
@@ -261,6 +274,41 @@ __device__ __forceinline__ float group_sum(float v) {
     if constexpr (W >= 32) v += __shfl_xor(v, 16, 64);
     if constexpr (W >= 64) v += __shfl_xor(v, 32, 64);
     return v;
+}
+
+// Maximum over the 64 lanes of a wave; every lane gets it.  NaN inputs are
+// passed over (fmaxf returns the other operand).
+__device__ __forceinline__ float wave_max(float v) {
+    v = fmaxf(v, dpp<0xB1>(v));
+    v = fmaxf(v, dpp<0x4E>(v));
+    v = fmaxf(v, dpp<0x141>(v));
+    v = fmaxf(v, dpp<0x140>(v));
+    v = fmaxf(v, __shfl_xor(v, 16, 64));
+    return fmaxf(v, __shfl_xor(v, 32, 64));
+}
+
+// Largest magnitude among the eight bf16 values packed in a 16-byte piece.
+__device__ __forceinline__ float maxabs8_bf16(const uint4& raw) {
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    float m = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        m = fmaxf(m, fmaxf(fabsf(__uint_as_float(w[j] << 16)), fabsf(__uint_as_float(w[j] & 0xffff0000u))));
+    return m;
+}
+
+// Working scale of a walk whose values and state reach magnitude m: the power
+// of two 2^floor(log2 m), kept within [2^-100, 2^100]; 1 for m = 0, NaN or
+// Inf.  The recurrence is linear in (v, S), so a walk may run on v / s and
+// S / s and multiply its outputs and final state by s: exact in binary
+// floating point, and it keeps the fp16 operands formed from the state and
+// from v near magnitude 1 whatever the scale of the inputs.
+__device__ __forceinline__ float pow2_scale(float m) {
+    if (!(m > 0.f) || !(m <= 3.0e38f)) return 1.f;
+    int e;
+    (void)frexpf(m, &e);                 // m = f 2^e, f in [0.5, 1)
+    e = min(100, max(-100, e - 1));
+    return ldexpf(1.f, e);
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave.

@@ -148,6 +148,7 @@ void gdn_fwd_single_kernel(FwdArgs p) {
     float* v_gam = v_g2 + C;
     float* v_eg = v_gam + C;
     float* v_beta = v_eg + C;
+    __shared__ float v_red[4];                    // per-wave maxima for the working scale
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -171,20 +172,56 @@ void gdn_fwd_single_kernel(FwdArgs p) {
         if ((s >> 4) > (r >> 4)) Pm[r * L::LDT + s] = (E)0.f;
     }
 
-    // Initial state tile -> registers (fp32) and Mt (operand copy).
+    // Initial state tile -> registers (fp32).
     f32x4 Macc[SM];
 #pragma unroll
     for (int sl = 0; sl < SM; ++sl) {
         const int t = wave + 4 * sl;
         Macc[sl] = zero4();
+        if (t < NTM && p.state_in) {
+            const int i0 = (t / NCB) * 16 + 4 * (lane >> 4);
+            const int c = (t % NCB) * 16 + (lane & 15);
+            const float* sp = p.state_in + (size_t)bh * DK * dv + col0 + c;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Macc[sl][i] = sp[(size_t)(i0 + i) * dv];
+        }
+    }
+    // Working scale of the tile (bf16 inputs; the fp32 path keeps 1): a power
+    // of two from the largest |M| of the incoming state and the largest |v| of
+    // the first chunk in these columns.  The walk runs on M / ws and v / ws
+    // (exact) and multiplies outputs and the final state by ws, so the fp16
+    // operands formed from M, v and U stay near magnitude 1 whatever the scale
+    // of the inputs.
+    float ws = 1.f;
+    if constexpr (sizeof(In) == 2) {
+        float m = 0.f;
+#pragma unroll
+        for (int sl = 0; sl < SM; ++sl)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(Macc[sl][i]));
+        const int n0 = min(C, T);
+        for (int it = tid; it < C * VPRV; it += 256) {
+            const int r = it / VPRV, part = it % VPRV;
+            if (r < n0) {
+                const uint4 rv4 = *reinterpret_cast<const uint4*>(vg + (size_t)tm(r) * dv + col0 + part * EPV);
+                m = fmaxf(m, maxabs8_bf16(rv4));
+            }
+        }
+        m = wave_max(m);
+        if (lane == 0) v_red[wave] = m;
+        __syncthreads();
+        ws = pow2_scale(fmaxf(fmaxf(v_red[0], v_red[1]), fmaxf(v_red[2], v_red[3])));
+    }
+    const float wi = 1.f / ws;
+    // ... and its operand copy Mt, at the working scale
+#pragma unroll
+    for (int sl = 0; sl < SM; ++sl) {
+        const int t = wave + 4 * sl;
         if (t < NTM) {
             const int i0 = (t / NCB) * 16 + 4 * (lane >> 4);
             const int c = (t % NCB) * 16 + (lane & 15);
-            if (p.state_in) {
-                const float* sp = p.state_in + (size_t)bh * DK * dv + col0 + c;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) Macc[sl][i] = sp[(size_t)(i0 + i) * dv];
-            }
+            for (int i = 0; i < 4; ++i) Macc[sl][i] *= wi;
             st4(Mt + c * L::LDW + i0, Macc[sl][0], Macc[sl][1], Macc[sl][2], Macc[sl][3]);
         }
     }
@@ -230,7 +267,7 @@ void gdn_fwd_single_kernel(FwdArgs p) {
             const In* ve = reinterpret_cast<const In*>(&rv4);
 #pragma unroll
             for (int e = 0; e < EPV; ++e)
-                Vt[(part * EPV + e) * L::LDT + r] = Op::from_f32(InTraits<In>::to_f32(ve[e]));
+                Vt[(part * EPV + e) * L::LDT + r] = Op::from_f32(InTraits<In>::to_f32(ve[e]) * wi);
         }
         if (wave == 0) {
             constexpr int TPL = C >= 64 ? C / 64 : 1;   // tokens per lane
@@ -522,7 +559,7 @@ void gdn_fwd_single_kernel(FwdArgs p) {
                 for (int i = 0; i < 4; ++i) {
                     const int r = r0 + i;
                     oe[i] = r < n ? (unsigned)(tm(t0 + r) * dv + c) : kOffNone;
-                    ov[i] = Oacc[sl][i];
+                    ov[i] = Oacc[sl][i] * ws;
                     if (p.out_gate && r < n)
                         ov[i] *= InTraits<In>::to_f32(reinterpret_cast<const In*>(p.out_gate)[(size_t)bh * T * dv + oe[i]]);
                 }
@@ -570,7 +607,7 @@ void gdn_fwd_single_kernel(FwdArgs p) {
                 const int c = (t % NCB) * 16 + (lane & 15);
                 float* sp = p.state_out + (size_t)bh * DK * dv + col0 + c;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sp[(size_t)(i0 + i) * dv] = Macc[sl][i];
+                for (int i = 0; i < 4; ++i) sp[(size_t)(i0 + i) * dv] = Macc[sl][i] * ws;
             }
         }
     }

@@ -44,6 +44,8 @@ struct WalkArgs : FwdArgs {
     float* snap;             // [B*H][dk][dv] copy of state_in
     void* phi;               // pipelined: [B*H][nseg][seg_chunks*chunk][dk] fp16, fragment order
     void* ostage;            // pipelined: [B*H][nseg][seg_chunks*chunk][dv] fp16 partial outputs
+    float* sscale;           // pipelined: [B*H][dv/16] power-of-two working scale of each 16
+                             // value columns; staged outputs and maps are in units of it
     int nseg;                // segments per sequence (1: no split)
     int seg_chunks;          // chunks per segment
 };

@@ -210,13 +210,15 @@ __device__ __forceinline__ float sumsq8(const uint4& raw) {
 
 // 16x16 transpose of raw bf16 through the matrix core (A * I, exact): lane
 // (g, c) receives a[4g+i][c], i < 4.
-__device__ __forceinline__ f32x4 transpose16_bf16(const uint16_t* a, int lda, int lane) {
+// `unit` is the bf16 bit pattern of the diagonal: a power of two s gives the
+// transpose times s, still exactly (0x3F80 is 1).
+__device__ __forceinline__ f32x4 transpose16_bf16(const uint16_t* a, int lda, int lane, short unit = 0x3F80) {
     typedef short s4 __attribute__((ext_vector_type(4)));
     const int lc = lane & 15, lg = lane >> 4;
     const s4 fa = *reinterpret_cast<const s4*>(a + lc * lda + 4 * lg);
     s4 one;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) one[j] = (4 * lg + j == lc) ? (short)0x3F80 : (short)0;
+    for (int j = 0; j < 4; ++j) one[j] = (4 * lg + j == lc) ? unit : (short)0;
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(fa, one, zero4(), 0, 0, 0);
 }
 
@@ -373,6 +375,16 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
     f32x4 QM[CT][NB];
     F KMf[CT][KS_C];                                  // K^ M of the next chunk as B operand (fp16)
     F vB[CT][KS_C];                                   // V of the next chunk as B operand
+    // Working scale of each column tile: the walk runs on M / wsc and v / wsc
+    // (a power of two, so exact) and multiplies outputs and state by wsc
+    // again; the fp16 operands formed from M, v and U then stay near
+    // magnitude 1 whatever the scale of the inputs.  Every walk of a head's
+    // 16 value columns (each segment, and the correction pass) takes the
+    // same scale, from the same data: the largest |state_in| of the columns
+    // and the largest |v| of the sequence's first chunk in them.  Identity
+    // columns of a segment walk keep 1.
+    float wsc[CT], winv[CT];
+    short wunit[CT];                                  // bf16 bits of winv (exact: a power of two)
     // output gate of the next chunk's rows (this lane's row and 4 columns per
     // row block), loaded a step ahead of its use
     uint2 GV[EXT && !SEG ? CT : 1][EXT && !SEG ? NB : 1];
@@ -410,20 +422,6 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
             }
         }
     };
-    if constexpr (SEG) {
-        // Copy of the incoming state for the correction pass (state_in may
-        // alias state_out): segment 0's workgroups copy their value columns,
-        // rows of 16-byte pieces spread over all 512 threads.
-        if (seg == 0 && p.snap && p.state_in && vlo < BV) {
-            const int pr = (BV - vlo) / 4;                       // 16-byte pieces per row
-            const size_t base = (size_t)bh * DK * dv + vbase + vlo;
-            for (int e = tid; e < DK * pr; e += L::NT) {
-                const int r = e / pr, c4 = e % pr;
-                *reinterpret_cast<float4*>(p.snap + base + (size_t)r * dv + 4 * c4) =
-                    *reinterpret_cast<const float4*>(p.state_in + base + (size_t)r * dv + 4 * c4);
-            }
-        }
-    }
     // ---- incoming state of the walk (state waves): identity on identity
     // columns and zero on value columns of a segment walk, else state_in
     auto init_state = [&]() {
@@ -460,6 +458,62 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
     // compiler allocates registers per role (the branch is wave-uniform).
     if (is_state) {
         init_state();
+        // The scale of a value tile, from the largest |state_in| of its columns
+        // and the largest |v| of the sequence's first chunk in them (two
+        // 16-byte pieces per row; rows past the sequence read zero).  A
+        // segment walk's value columns start from zero: they read state_in
+        // into the accumulators only for its maximum, and segment 0 leaves
+        // the correction pass a copy of it at the working scale (state_in may
+        // alias state_out, which that pass writes).
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+            if constexpr (SEG) {
+                if (!ident(ct) && p.state_in) {
+                    const float* sp = p.state_in + (size_t)bh * DK * dv + vbase + col0(ct) + lc;
+#pragma unroll
+                    for (int ib = 0; ib < NDB; ++ib)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) Macc[ct][ib][i] = sp[(unsigned)((16 * ib + 4 * lg + i) * dv)];
+                }
+            }
+            float m = 0.f;
+            if (!ident(ct)) {
+#pragma unroll
+                for (int ib = 0; ib < NDB; ++ib)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(Macc[ct][ib][i]));
+            }
+#pragma unroll
+            for (int j = 0; j < C / 32; ++j) {
+                const int e = lane + 64 * j, r = e >> 1, part = e & 1;
+                const uint4 x = buf_load16(rv_, ident(ct) ? kOffNone
+                                                          : (unsigned)(tm(r) * dv + vbase + col0(ct) + 8 * part) * 2u);
+                m = fmaxf(m, maxabs8_bf16(x));
+            }
+            wsc[ct] = uniform(ident(ct) ? 1.f : pow2_scale(wave_max(m)));
+            winv[ct] = uniform(1.f / wsc[ct]);
+            wunit[ct] = (short)(__float_as_uint(winv[ct]) >> 16);
+#pragma unroll
+            for (int ib = 0; ib < NDB; ++ib)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) Macc[ct][ib][i] *= winv[ct];
+            if constexpr (SEG) {
+                if (!ident(ct)) {
+                    if (seg == 0) {
+                        if (p.state_in) {
+                            float* sn = p.snap + (size_t)bh * DK * dv + vbase + col0(ct) + lc;
+#pragma unroll
+                            for (int ib = 0; ib < NDB; ++ib)
+#pragma unroll
+                                for (int i = 0; i < 4; ++i) sn[(unsigned)((16 * ib + 4 * lg + i) * dv)] = Macc[ct][ib][i];
+                        }
+                        if (lane == 0) p.sscale[(size_t)bh * (dv / 16) + (vbase + col0(ct)) / 16] = wsc[ct];
+                    }
+#pragma unroll
+                    for (int ib = 0; ib < NDB; ++ib) Macc[ct][ib] = zero4();
+                }
+            }
+        }
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
@@ -543,6 +597,8 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
                                                uniform((lch * C * dv + (rb * (dv / 16) + vb16) * 256) * 2));
                                 }
                             } else {
+#pragma unroll
+                                for (int i = 0; i < 4; ++i) o[i] *= wsc[ct];
                                 // rows past T fall outside the buffer and are dropped
                                 const unsigned e0 = (unsigned)(tm(t0 + 16 * rb + lc) * dv +
                                                                vbase + col0(ct) + 4 * lg);
@@ -640,7 +696,7 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
                     f32x4 Vacc[NB];
 #pragma unroll
                     for (int rb = 0; rb < NB; ++rb)
-                        Vacc[rb] = transpose16_bf16(Vr + (16 * rb) * L::LDV + col0(ct), L::LDV, lane);
+                        Vacc[rb] = transpose16_bf16(Vr + (16 * rb) * L::LDV + col0(ct), L::LDV, lane, wunit[ct]);
 #pragma unroll
                     for (int ks = 0; ks < KS_C; ++ks) vB[ct][ks] = Op::b_acc(Vacc, ks);
                 }
@@ -891,6 +947,7 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
 #pragma unroll
                         for (int i = 0; i < 4; ++i) As[(16 * ib + 4 * lg + i) * L::LDAS + c] = (E)Macc[ct][ib][i];
                 } else {
+                    // B_s in units of the working scale
                     const int c16 = (vbase + col0(ct)) / 16;
                     f32x4* dst = reinterpret_cast<f32x4*>(summB_bh + (size_t)seg * DK * dv) + c16 * NDB * 64 + lane;
 #pragma unroll
@@ -921,7 +978,7 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
 #pragma unroll
                     for (int ib = 0; ib < NDB; ++ib)
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) sp[(unsigned)((16 * ib + 4 * lg + i) * dv)] = Macc[ct][ib][i];
+                        for (int i = 0; i < 4; ++i) sp[(unsigned)((16 * ib + 4 * lg + i) * dv)] = Macc[ct][ib][i] * wsc[ct];
                 }
             }
         }
@@ -1008,6 +1065,12 @@ __global__ __launch_bounds__(1024) void gdn_pipe_fix_kernel(WalkArgs p) {
     // Loads and stores below are unconditional (kOffNone where there is
     // nothing to move) so that the compiler counts the loads in flight
     // exactly and never drains them early.
+
+    // ---- working scale of these 16 value columns, the one every walk of them
+    // used: partial outputs, maps and the copy of state_in are in its units.
+    // The pass folds and corrects on those units too and multiplies outputs
+    // and state back (a uniform address: a scalar load).
+    const float s_w = p.sscale[(size_t)bh * (dv / 16) + c16];
 
     // ---- state entering segment 0: rows 16 (rg RB + r) + 4 lg + i, column col
     f32x4 Macc[RB];
@@ -1123,7 +1186,7 @@ __global__ __launch_bounds__(1024) void gdn_pipe_fix_kernel(WalkArgs p) {
 #pragma unroll
             for (int ib = 0; ib < NDB; ++ib)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sp[(16 * ib + 4 * lg + i) * dv] = Mw[ib][i];
+                for (int i = 0; i < 4; ++i) sp[(16 * ib + 4 * lg + i) * dv] = Mw[ib][i] * s_w;
         }
     }
     __syncthreads();
@@ -1211,7 +1274,7 @@ __global__ __launch_bounds__(1024) void gdn_pipe_fix_kernel(WalkArgs p) {
 #pragma unroll
         for (int r = 0; r < RB; ++r)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sp[(16 * (rg * RB + r) + 4 * lg + i) * dv] = Macc[r][i];
+            for (int i = 0; i < 4; ++i) sp[(16 * (rg * RB + r) + 4 * lg + i) * dv] = Macc[r][i] * s_w;
     }
     }
 
@@ -1228,6 +1291,8 @@ __global__ __launch_bounds__(1024) void gdn_pipe_fix_kernel(WalkArgs p) {
 #pragma unroll
         for (int ks = 0; ks < KS_D; ++ks)
             acc = Op::mma(mI[ks], __builtin_bit_cast(F, Phs[buf][(rg * KS_D + ks) * 64 + lane]), acc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] *= s_w;
         // rows past T fall outside the buffer and are dropped
         const unsigned e0 = (unsigned)(tm(c * C + 16 * rb + lc) * dv + col4);
         if (gated) {
@@ -1322,7 +1387,8 @@ size_t pipe_workspace(int B, int H, int dk, int dv, int chunk, int nseg, int seg
          + bh * ns * dk * dv * 4          // B_s
          + bh * dk * dv * 4               // copy of state_in
          + bh * ns * rows * dk * 2        // Phi (fp16)
-         + bh * ns * rows * dv * 2;       // partial outputs (fp16)
+         + bh * ns * rows * dv * 2        // partial outputs (fp16)
+         + bh * (dv / 16) * 4;            // working scale per 16 value columns
 }
 
 hipError_t launch_pipe(const WalkArgs& a, int chunk, hipStream_t s) {
