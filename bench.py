@@ -78,10 +78,11 @@ def algorithmic_flops(wl) -> int:
     return 6 * wl.B * wl.H * wl.T * wl.dk * wl.dv
 
 
-def read_traffic(kernel_hash: str, workload: str):
-    """HBM traffic per launch from the committed rocprofv3 counter summary,
-    if it was taken on the current kernel source."""
-    path = os.path.join(ROOT, "profiles", f"gdn_pipe_{workload}_traffic.md")
+def read_traffic(kernel_hash: str, workload: str, family: str = "gdn_pipe"):
+    """HBM traffic per launch from the committed rocprofv3 counter summary
+    (profiles/<family>_<workload>_traffic.md), if it was taken on the current
+    kernel source."""
+    path = os.path.join(ROOT, "profiles", f"{family}_{workload}_traffic.md")
     if not os.path.exists(path):
         return None
     txt = open(path).read()
@@ -303,7 +304,8 @@ def bench_framewise(args):
                    "input_sets": nsets, "workspace_bytes": ws_bytes},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": read_traffic(kernel_source_hash(), wl.name) if args.out_dtype == "f32" else None},
+                     "traffic": read_traffic(kernel_source_hash(), wl.name, "gdn_frame")
+                     if args.out_dtype == "f32" else None},
         "kernel": {"avg_ms": call_ms, "p50_ms": statistics.median(per),
                    "p99_ms": sorted(per)[min(len(per) - 1, int(0.99 * len(per)))],
                    "algorithmic_bytes": alg_bytes, "launches_per_call": 3},
