@@ -299,6 +299,13 @@ const char* gdn_last_error(void);
 /* GDN_VERSION of the built library. */
 int gdn_version(void);
 
+/* Debug switches the library reads from the environment at each call, as
+ * bit flags.  Bit 0: GDN_DEBUG_REVERSE_WORKGROUPS is set and not "0"; every
+ * launch's workgroups then take their work items in reverse order of
+ * dispatch, which must leave every result unchanged bit for bit (no
+ * workgroup of a launch reads what another writes or waits for another). */
+int gdn_debug_flags(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -6,6 +6,7 @@
 #include <math.h>
 #include <stdint.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "gdn_kernels.h"
@@ -39,6 +40,14 @@ void defaults(gdn_opts* o) {
     o->workspace_bytes = 0;
     o->gate_logits = 0;
     o->out_gate = nullptr;
+}
+
+// Debug switch: with GDN_DEBUG_REVERSE_WORKGROUPS set (and not "0") every
+// launch's workgroups take their work items in reverse order of dispatch;
+// results must not change (checked by the GPU tests).
+int debug_reverse_workgroups() {
+    const char* e = getenv("GDN_DEBUG_REVERSE_WORKGROUPS");
+    return (e && e[0] && !(e[0] == '0' && e[1] == '\0')) ? 1 : 0;
 }
 
 // Sizes the calls accept: the limits validate() enforces on B, H and T.
@@ -189,7 +198,8 @@ int scan(const void* q, const void* k, const void* v, const void* alpha, const v
          const float* state_in, void* out, float* state_out,
          int B, int H, int T, int dk, int dv, int chunk, const gdn_opts& o, int reverse, int accumulate,
          const float* acc_src = nullptr) {
-    gdn::WalkArgs a;
+    gdn::WalkArgs a{};
+    a.rev_wg = debug_reverse_workgroups();
     a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta;
     a.state_in = state_in; a.out = out; a.state_out = state_out;
     a.B = B; a.H = H; a.T = T; a.dk = dk; a.dv = dv;
@@ -351,7 +361,8 @@ int run_framewise(const void* q, const void* k, const void* v, const void* alpha
                     "gdn_framewise_workspace_bytes() = %s bytes", n);
     }
     if (F == 0 && !state_out && !z_out) return GDN_OK;
-    gdn::FrameArgs a;
+    gdn::FrameArgs a{};
+    a.rev_wg = debug_reverse_workgroups();
     a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta;
     a.state_in = state_in; a.z_in = z_in; a.out = out; a.state_out = state_out; a.z_out = z_out;
     a.out_gate = o.out_gate;
@@ -427,7 +438,8 @@ int gdn_attn_sink_window(const void* q, const void* k_sink, const void* v_sink, 
         if (ns[i] > 0 && (!aligned16(ks[i]) || !aligned16(vs[i]))) return fail(GDN_ERR_ARG, "keys and values must be 16-byte aligned");
     }
     if (!aligned16(q) || !aligned16(out)) return fail(GDN_ERR_ARG, "q and out must be 16-byte aligned");
-    gdn::AttnArgs a;
+    gdn::AttnArgs a{};
+    a.rev_wg = debug_reverse_workgroups();
     a.q = q;
     for (int i = 0; i < 3; ++i) {
         a.k[i] = ks[i];
@@ -499,5 +511,7 @@ const char* gdn_strerror(int status) {
 const char* gdn_last_error(void) { return g_last_error; }
 
 int gdn_version(void) { return GDN_VERSION; }
+
+int gdn_debug_flags(void) { return debug_reverse_workgroups(); }
 
 }  // extern "C"

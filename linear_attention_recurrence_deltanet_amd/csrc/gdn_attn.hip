@@ -115,7 +115,7 @@ __global__ __launch_bounds__(256, 2) void gdn_attn_kernel(AttnArgs p) {
     const int Nq = p.Nq;
     const int nqb = (Nq + AQ - 1) / AQ;
     const int nsplit = p.nsplit;
-    int wg = blockIdx.x;
+    int wg = block_x(p.rev_wg);
     {
         // the query blocks of one head read the same keys: keep them on one XCD
         const int w8 = (int)gridDim.x / 8 * 8;

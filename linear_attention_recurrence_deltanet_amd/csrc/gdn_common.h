@@ -134,6 +134,15 @@ __device__ __forceinline__ typename Op::frag frag_at(const typename Op::elem* ba
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// Block index along one grid dimension, taken in reverse order of dispatch
+// when `rev` is set: a debug switch (the environment variable
+// GDN_DEBUG_REVERSE_WORKGROUPS read by the API) under which every result must
+// stay the same bit for bit, since no workgroup of a launch reads what another
+// one writes and none waits for another.
+__device__ __forceinline__ int block_x(int rev) { return rev ? (int)(gridDim.x - 1 - blockIdx.x) : (int)blockIdx.x; }
+__device__ __forceinline__ int block_y(int rev) { return rev ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y; }
+__device__ __forceinline__ int block_z(int rev) { return rev ? (int)(gridDim.z - 1 - blockIdx.z) : (int)blockIdx.z; }
+
 // Workgroup barrier for exchanges through LDS only.  __syncthreads() also
 // orders global memory, which on this target waits for every load and store
 // the wave has in flight (vmcnt(0)); loads issued ahead of their use would

@@ -120,8 +120,8 @@ __global__ __launch_bounds__(256) void frame_sum_kernel(FrameArgs p) {
     __shared__ __attribute__((aligned(16))) uint16_t Vs[2][32 * VST];
     __shared__ float Ss[2][32];
 
-    const int j = blockIdx.x % NT, sp = blockIdx.x / NT, nsp = gridDim.x / NT;
-    const int f = blockIdx.y, bh = blockIdx.z;
+    const int j = block_x(p.rev_wg) % NT, sp = block_x(p.rev_wg) / NT, nsp = gridDim.x / NT;
+    const int f = block_y(p.rev_wg), bh = block_z(p.rev_wg);
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lg = lane >> 4, lc = lane & 15;
     const int N = p.N;
     const size_t T = (size_t)p.F * N;
@@ -291,7 +291,7 @@ __global__ __launch_bounds__(64 * (DV / 16)) void frame_scan_kernel(FrameArgs p)
     __shared__ float zs[2][DK];
 
     const int tid = threadIdx.x, ct = tid >> 6, lane = tid & 63, lg = lane >> 4, lc = lane & 15;
-    const int bh = blockIdx.x;
+    const int bh = block_x(p.rev_wg);
     const int nsp = p.nsp;
 
     f32x4 M[NRB];
@@ -457,8 +457,8 @@ __global__ __launch_bounds__(512) void frame_out_kernel(FrameArgs p) {
     constexpr int MST = DK + 8;
     __shared__ __attribute__((aligned(16))) uint16_t Mh[64 * MST];
     __shared__ __attribute__((aligned(16))) uint16_t Ml[64 * MST];
-    const int cg = blockIdx.x % NCG, ts = blockIdx.x / NCG, nts = gridDim.x / NCG;
-    const int f = blockIdx.y, bh = blockIdx.z;
+    const int cg = block_x(p.rev_wg) % NCG, ts = block_x(p.rev_wg) / NCG, nts = gridDim.x / NCG;
+    const int f = block_y(p.rev_wg), bh = block_z(p.rev_wg);
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lg = lane >> 4, lc = lane & 15;
     const int N = p.N;
     const size_t T = (size_t)p.F * N;

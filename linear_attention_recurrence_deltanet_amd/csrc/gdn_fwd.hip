@@ -188,14 +188,14 @@ void gdn_walk_kernel(WalkArgs p) {
     int bh, seg, ctile, ncol;
     if constexpr (SUMMARY) {
         ncol = (DK + dv) / BV;
-        ctile = blockIdx.x % ncol;
-        const int r = blockIdx.x / ncol;
+        ctile = block_x(p.rev_wg) % ncol;
+        const int r = block_x(p.rev_wg) / ncol;
         seg = r % nsum;
         bh = r / nsum;
     } else {
         ncol = dv / BV;
-        ctile = blockIdx.x % ncol;
-        const int r = blockIdx.x / ncol;
+        ctile = block_x(p.rev_wg) % ncol;
+        const int r = block_x(p.rev_wg) / ncol;
         seg = r % nseg;
         bh = r / nseg;
     }

@@ -154,8 +154,8 @@ void gdn_fwd_single_kernel(FwdArgs p) {
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int ntile = p.dv / BV;
-    const int tile = blockIdx.x % ntile;
-    const int bh = blockIdx.x / ntile;
+    const int tile = block_x(p.rev_wg) % ntile;
+    const int bh = block_x(p.rev_wg) / ntile;
     const int col0 = tile * BV;
     const int T = p.T, dv = p.dv;
     const TokMap tm = tok_map(T, p.reverse);   // walk position -> token

@@ -29,6 +29,7 @@ struct FwdArgs {
     int reverse;             // 1: walk the tokens backward (position t is token T-1-t)
     int accumulate;          // 1: out = (gated) outputs + acc_src, rounded once
     const float* acc_src;    // accumulate: fp32 [B*H][T][dv] to add
+    int rev_wg;              // debug: workgroups take their work items in reverse order
 };
 
 // Segmented chunk walkers (chunk 32 or 64).  With nseg > 1 the workspace
@@ -85,6 +86,7 @@ struct AttnArgs {
     int nsplit;              // key ranges (1: no split)
     float* part_o;           // nsplit > 1: [nsplit][B*H*Nq][d] unnormalised outputs
     float* part_ml;          // nsplit > 1: [nsplit][B*H*Nq][2] running max (exp2 domain), sum
+    int rev_wg;              // debug: workgroups take their work items in reverse order
 };
 bool attn_supported(int d);
 // Key ranges the launch splits into (1 when the workgroups already fill the
@@ -116,6 +118,7 @@ struct FrameArgs {
     uint16_t* mt_hi;         // workspace: [B*H][F][dv][dk] M_f^T, bf16 hi part
     uint16_t* mt_lo;         // workspace: [B*H][F][dv][dk] bf16 lo part
     float* zf;               // workspace: [B*H][F][dk] z_f
+    int rev_wg;              // debug: workgroups take their work items in reverse order
 };
 // Token splits of the launch plan, and the workspace (bytes) with the
 // offsets of mt_hi and zf (mt_lo follows mt_hi at the same distance).

@@ -299,7 +299,7 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
     // consecutive logical indices -- the column tiles and segments of one
     // head -- share an XCD and its L2: they read the same q/k rows at about
     // the same time.
-    int wg = blockIdx.x;
+    int wg = block_x(p.rev_wg);
     {
         const int w8 = (int)gridDim.x / 8 * 8;
         if (wg < w8) wg = (wg % 8) * (w8 / 8) + wg / 8;
@@ -1024,7 +1024,7 @@ __global__ __launch_bounds__(1024) void gdn_pipe_fix_kernel(WalkArgs p) {
     const int cg = wave & 3, rg = wave >> 2;
     const int lc = lane & 15, lg = lane >> 4;
     const int T = p.T, dv = p.dv, nseg = p.nseg;
-    int wg = blockIdx.x;
+    int wg = block_x(p.rev_wg);
     {
         // the segments of one head read the same maps: keep them on one XCD
         const int w8 = (int)gridDim.x / 8 * 8;

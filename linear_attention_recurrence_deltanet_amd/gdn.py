@@ -22,7 +22,7 @@ GDN_BF16, GDN_F32 = 0, 1
 EXPORTS = ("gdn_default_opts", "gdn_fwd_chunked", "gdn_fwd_step", "gdn_fwd_step_noalloc", "gdn_fwd_bidir",
            "gdn_workspace_bytes", "gdn_bidir_workspace_bytes", "gdn_attn_sink_window",
            "gdn_attn_workspace_bytes", "gdn_fwd_framewise", "gdn_framewise_workspace_bytes",
-           "gdn_strerror", "gdn_last_error", "gdn_version")
+           "gdn_strerror", "gdn_last_error", "gdn_version", "gdn_debug_flags")
 
 
 class GdnOpts(ctypes.Structure):
@@ -87,6 +87,8 @@ def load(path: str = LIB_PATH):
     lib.gdn_last_error.restype = ctypes.c_char_p
     lib.gdn_version.argtypes = []
     lib.gdn_version.restype = i
+    lib.gdn_debug_flags.argtypes = []
+    lib.gdn_debug_flags.restype = i
     _lib = lib
     return lib
 

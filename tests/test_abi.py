@@ -234,3 +234,12 @@ def test_binding_fails_loudly_without_library(tmp_path):
             mod.load(str(tmp_path / "missing.so"))
     finally:
         importlib.reload(gdn)
+
+
+def test_debug_flags_follow_the_environment(lib, monkeypatch):
+    monkeypatch.delenv("GDN_DEBUG_REVERSE_WORKGROUPS", raising=False)
+    assert lib.gdn_debug_flags() == 0
+    monkeypatch.setenv("GDN_DEBUG_REVERSE_WORKGROUPS", "1")
+    assert lib.gdn_debug_flags() & 1
+    monkeypatch.setenv("GDN_DEBUG_REVERSE_WORKGROUPS", "0")
+    assert lib.gdn_debug_flags() == 0
