@@ -372,6 +372,8 @@ int run_framewise(const void* q, const void* k, const void* v, const void* alpha
     a.out_bf16 = o.out_dtype == GDN_BF16;
     a.eps = o.eps;
     gdn::frame_plan(B, H, F, N, dk, dv, &a.nsp, &a.nts);
+    if ((long long)(dv / 64) * a.nts * F * B * H > 0x7fffffffLL)
+        return fail(GDN_ERR_UNSUPPORTED, "frame-wise: too many readout workgroups (B*H*F too large)");
     char* w = reinterpret_cast<char*>(o.workspace);
     a.sums = reinterpret_cast<float*>(w);
     a.mt_hi = reinterpret_cast<uint16_t*>(w + off_mt);

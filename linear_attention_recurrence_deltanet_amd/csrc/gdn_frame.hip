@@ -98,31 +98,34 @@ __device__ __forceinline__ float ld_bf16(const void* base, size_t i) {
 }
 
 // ---------------------------------------------------------------------------
-// Phase A: frame summaries.  Grid (NT * nsp, F, B*H); 4 waves.  Tile j of the
-// summary columns [G (dk) | W_v (dv)] is 64 wide; the last tile also forms
-// the 16-column block of w = (1/N) sum beta k^ (value 1 in its column 0).
-// Wave w owns rows [w * dk/4, (w+1) * dk/4) of the tile.  Tokens of split sp
-// of the frame are walked 32 at a time: the whole workgroup stages the raw
-// keys (all dk features, for the norms) and the tile's value columns in LDS,
-// with the per-token factor; each wave then transposes what it needs.
+// Phase A: frame summaries.  Grid (nsp, F, B*H); 4 waves per 64-column tile
+// of the summary columns [G (dk) | W_v (dv)], all tiles in one workgroup so
+// that the frame's keys and values are read from memory once; the last tile
+// also forms the 16-column block of w = (1/N) sum beta k^ (value 1 in its
+// column 0).  Wave (j, wr) owns rows [wr * dk/4, (wr+1) * dk/4) of tile j.
+// Tokens of split sp of the frame are walked 32 at a time: the workgroup
+// stages the raw keys (all dk features, for the norms), the values and the
+// per-token factors in LDS; each wave then transposes what it needs.
 // ---------------------------------------------------------------------------
 template <int DK, int DV>
-__global__ __launch_bounds__(256) void frame_sum_kernel(FrameArgs p) {
+__global__ __launch_bounds__(64 * 4 * ((DK + DV) / 64)) void frame_sum_kernel(FrameArgs p) {
     constexpr int NT = (DK + DV) / 64;
+    constexpr int NTH = 256 * NT;
     constexpr int NS = DK + DV + 16;
     constexpr int RB = DK / 64;          // 16-row blocks per wave
     constexpr int KST = DK + 8;          // LDS row stride of the keys (elements)
-    constexpr int VST = 64 + 8;
+    constexpr int VST = DV + 8;          // ... and of the values
     constexpr int KP = 32 * DK / 8;      // 16-byte pieces of a 32-token key block
-    constexpr int KPT = KP / 256;
-    static_assert(KP % 256 == 0, "whole pieces per thread");
+    constexpr int VP = 32 * DV / 8;      // ... and of a value block
+    static_assert(KP <= NTH && VP <= NTH, "one piece of each per thread at most");
     __shared__ __attribute__((aligned(16))) uint16_t Ks[2][32 * KST];
     __shared__ __attribute__((aligned(16))) uint16_t Vs[2][32 * VST];
-    __shared__ float Ss[2][32];
+    __shared__ float Ss[2][2][32];       // per-token factor: [buf][G (beta r^2 / N) | W (beta r / N)]
 
-    const int j = block_x(p.rev_wg) % NT, sp = block_x(p.rev_wg) / NT, nsp = gridDim.x / NT;
+    const int sp = block_x(p.rev_wg), nsp = gridDim.x;
     const int f = block_y(p.rev_wg), bh = block_z(p.rev_wg);
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lg = lane >> 4, lc = lane & 15;
+    const int j = w >> 2, wr = w & 3;    // tile and row group of this wave (wave-uniform)
     const int N = p.N;
     const size_t T = (size_t)p.F * N;
     const int L = (((N + nsp - 1) / nsp) + 31) & ~31;
@@ -144,47 +147,44 @@ __global__ __launch_bounds__(256) void frame_sum_kernel(FrameArgs p) {
     }
 
     // registers of the next step's staging; loads through buffer resources
-    // that cover exactly this split's tokens, so rows past it read zero
-    // without a branch (a branch around a load makes the wave wait for it)
+    // that cover exactly this split's tokens, so rows past it (and threads
+    // past the pieces) read zero without a branch (a branch around a load
+    // makes the wave wait for it)
     const unsigned ntok = (unsigned)(t1 > t0 ? t1 - t0 : 0);
     const rsrc_t rk = make_rsrc(kg + (row0 + t0) * DK, ntok * DK * 2);
     const rsrc_t rbeta = make_rsrc(reinterpret_cast<const uint16_t*>(p.beta) + row0 + t0, ntok * 2);
-    const rsrc_t rv = make_rsrc(vg + (row0 + t0) * DV + (gtile ? 0 : vcol), gtile ? 0u : ntok * DV * 2);
-    uint4 kreg[KPT], vreg;
-    float breg[KPT];
+    const rsrc_t rv = make_rsrc(vg + (row0 + t0) * DV, ntok * DV * 2);
+    const bool hask = tid < KP, hasv = tid < VP;
+    const int ktk = tid / (DK / 8), kfg = tid % (DK / 8);
+    const int vtk = tid / (DV / 8), vfg = tid % (DV / 8);
+    uint4 kreg, vreg;
+    float breg;
     auto fetch = [&](int ts) {
-#pragma unroll
-        for (int m = 0; m < KPT; ++m) {
-            const int e = tid + 256 * m;
-            const int tk = e / (DK / 8), fg = e % (DK / 8);
-            const unsigned t = (unsigned)(ts - t0 + tk);
-            kreg[m] = buf_load16(rk, t * DK * 2 + 16 * fg);
-            breg[m] = gate_beta(bf16_to_f32(buf_load2(rbeta, t * 2)), p.gate_logits != 0);
-        }
-        const unsigned t = (unsigned)(ts - t0 + (tid >> 3));
-        vreg = buf_load16(rv, t * DV * 2 + 16 * (tid & 7));
+        const unsigned tk = (unsigned)(ts - t0 + ktk);
+        kreg = buf_load16(rk, hask ? tk * DK * 2 + 16 * kfg : kOffNone);
+        breg = gate_beta(bf16_to_f32(buf_load2(rbeta, hask ? tk * 2 : kOffNone)), p.gate_logits != 0);
+        const unsigned tv = (unsigned)(ts - t0 + vtk);
+        vreg = buf_load16(rv, hasv ? tv * DV * 2 + 16 * vfg : kOffNone);
     };
     auto stage = [&](int buf) {
+        float ss = 0.f;
+        const uint32_t wv[4] = {kreg.x, kreg.y, kreg.z, kreg.w};
 #pragma unroll
-        for (int m = 0; m < KPT; ++m) {
-            const int e = tid + 256 * m;
-            const int tk = e / (DK / 8), fg = e % (DK / 8);
-            float ss = 0.f;
-            const uint32_t wv[4] = {kreg[m].x, kreg[m].y, kreg[m].z, kreg[m].w};
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float a = bf16_to_f32((uint16_t)(wv[q] & 0xffffu));
-                const float b = bf16_to_f32((uint16_t)(wv[q] >> 16));
-                ss += a * a + b * b;
-            }
-            ss = group_sum<DK / 8>(ss);
-            *reinterpret_cast<uint4*>(&Ks[buf][tk * KST + 8 * fg]) = kreg[m];
-            if (fg == 0) {
+        for (int q = 0; q < 4; ++q) {
+            const float a = bf16_to_f32((uint16_t)(wv[q] & 0xffffu));
+            const float b = bf16_to_f32((uint16_t)(wv[q] >> 16));
+            ss += a * a + b * b;
+        }
+        ss = group_sum<DK / 8>(ss);
+        if (hask) {
+            *reinterpret_cast<uint4*>(&Ks[buf][ktk * KST + 8 * kfg]) = kreg;
+            if (kfg == 0) {
                 const float r = p.qk_l2norm ? 1.f / sqrtf(ss + p.eps) : 1.f;
-                Ss[buf][tk] = breg[m] * (gtile ? r * r : r) * invN;
+                Ss[buf][0][ktk] = breg * r * r * invN;
+                Ss[buf][1][ktk] = breg * r * invN;
             }
         }
-        if (!gtile) *reinterpret_cast<uint4*>(&Vs[buf][(tid >> 3) * VST + 8 * (tid & 7)]) = vreg;
+        if (hasv) *reinterpret_cast<uint4*>(&Vs[buf][vtk * VST + 8 * vfg]) = vreg;
     };
 
     const int nsteps = t1 > t0 ? (t1 - t0 + 31) / 32 : 0;
@@ -202,11 +202,11 @@ __global__ __launch_bounds__(256) void frame_sum_kernel(FrameArgs p) {
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sc[h][i] = Ss[buf][16 * h + 4 * lg + i];
+            for (int i = 0; i < 4; ++i) sc[h][i] = Ss[buf][gtile ? 0 : 1][16 * h + 4 * lg + i];
         u16x8 ahi[RB], alo[RB];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
-            const int fb = w * RB + rb;
+            const int fb = wr * RB + rb;
             float x[8];
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
@@ -223,7 +223,7 @@ __global__ __launch_bounds__(256) void frame_sum_kernel(FrameArgs p) {
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const f32x4 t = gtile ? tr16(&Ks[buf][16 * h * KST + 64 * j + 16 * cb], KST, lane)
-                                      : tr16(&Vs[buf][16 * h * VST + 16 * cb], VST, lane);
+                                      : tr16(&Vs[buf][16 * h * VST + vcol + 16 * cb], VST, lane);
                 bw[2 * h] = pk_hi16(t[0], t[1]);        // exact: raw bf16 values
                 bw[2 * h + 1] = pk_hi16(t[2], t[3]);
             }
@@ -252,7 +252,7 @@ __global__ __launch_bounds__(256) void frame_sum_kernel(FrameArgs p) {
     float* dst = p.sums + (((size_t)bh * p.F + f) * nsp + sp) * DK * NS;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-        const int r0 = 16 * (w * RB + rb) + 4 * lg;
+        const int r0 = 16 * (wr * RB + rb) + 4 * lg;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -441,7 +441,8 @@ __global__ __launch_bounds__(64 * (DV / 16)) void frame_scan_kernel(FrameArgs p)
 }
 
 // ---------------------------------------------------------------------------
-// Phase C: the readout.  Grid (DV/64 * nts, F, B*H), 8 waves.  The workgroup
+// Phase C: the readout.  One workgroup of 8 waves per (64 value columns,
+// token range, frame, head).  The workgroup
 // stages M_f^T hi + lo of 64 value columns in LDS; each wave keeps them as A
 // operands (k = key index) with z_f, and walks 16-token blocks of the frame,
 // the next block's queries loading while the current one is formed.  The B
@@ -457,8 +458,26 @@ __global__ __launch_bounds__(512) void frame_out_kernel(FrameArgs p) {
     constexpr int MST = DK + 8;
     __shared__ __attribute__((aligned(16))) uint16_t Mh[64 * MST];
     __shared__ __attribute__((aligned(16))) uint16_t Ml[64 * MST];
-    const int cg = block_x(p.rev_wg) % NCG, ts = block_x(p.rev_wg) / NCG, nts = gridDim.x / NCG;
-    const int f = block_y(p.rev_wg), bh = block_z(p.rev_wg);
+    // One-dimensional grid of NCG x (nts x F x B*H) work items.  Workgroups
+    // are dealt to the 8 XCDs round-robin; the NCG column groups of one
+    // (token range, frame, head) read the same queries, so they are placed 8
+    // apart and share an XCD and its L2 (the items past the last whole
+    // multiple of 8 keep the plain order).
+    const int nts = p.nts;
+    int cg, rest;
+    {
+        const int n = (int)gridDim.x, lin = block_x(p.rev_wg);
+        const int n8 = (n / NCG) / 8 * 8 * NCG;
+        if (lin < n8) {
+            const int a = lin & 7, bq = lin >> 3;
+            cg = bq % NCG;
+            rest = a + 8 * (bq / NCG);
+        } else {
+            cg = lin % NCG;
+            rest = lin / NCG;
+        }
+    }
+    const int ts = rest % nts, f = (rest / nts) % p.F, bh = rest / (nts * p.F);
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lg = lane >> 4, lc = lane & 15;
     const int N = p.N;
     const size_t T = (size_t)p.F * N;
@@ -563,11 +582,11 @@ template <int DK, int DV>
 hipError_t launch3(const FrameArgs& a, hipStream_t s) {
     const unsigned bh = (unsigned)a.B * a.H;
     if (a.F > 0) {
-        hipLaunchKernelGGL((frame_sum_kernel<DK, DV>), dim3((DK + DV) / 64 * a.nsp, a.F, bh), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((frame_sum_kernel<DK, DV>), dim3(a.nsp, a.F, bh), dim3(256 * ((DK + DV) / 64)), 0, s, a);
     }
     hipLaunchKernelGGL((frame_scan_kernel<DK, DV>), dim3(bh), dim3(64 * (DV / 16)), 0, s, a);
     if (a.F > 0) {
-        hipLaunchKernelGGL((frame_out_kernel<DK, DV>), dim3(DV / 64 * a.nts, a.F, bh), dim3(512), 0, s, a);
+        hipLaunchKernelGGL((frame_out_kernel<DK, DV>), dim3((unsigned)(DV / 64) * a.nts * a.F * bh), dim3(512), 0, s, a);
     }
     return hipGetLastError();
 }
