@@ -105,9 +105,8 @@ void gdn_default_opts(gdn_opts* opts);
  * state by s (exact), so the fp16 operands formed from v, S and the chunk
  * values stay near magnitude 1 and the accuracy holds at any common scale of
  * v and state_in (tested from 2^-16 to 2^12).  Later values more than about
- * 2^12 times that first maximum can overflow those operands.  Exception:
- * bf16 calls with dk or dv = 32 use unscaled fp16 operands, accurate for
- * |v| and |state| of about 2^-10 to 2^12.
+ * 2^12 times that first maximum can overflow those operands.  (The walker
+ * of dk or dv = 32 takes one s per 16 * waves columns, the same way.)
  */
 int gdn_fwd_chunked(const void* q, const void* k, const void* v,
                     const void* alpha, const void* beta,

@@ -246,6 +246,39 @@ void gdn_walk_kernel(WalkArgs p) {
         }
     }
 
+    // ---------------- working scale of the tile (bf16 inputs) --------------
+    // The rule is linear in (v, S): the walk runs on v / ws and S / ws and
+    // multiplies outputs and the final state by ws (a power of two, exact),
+    // so that the fp16 operands formed from v, S and U stay near magnitude 1
+    // whatever the scale of the inputs.  Both passes of a segmented call take
+    // the same ws from the same data: the largest |state_in| of the tile's
+    // columns and the largest |v| of the sequence's first chunk in them
+    // (identity columns keep 1; fp32 inputs, on fp32 products, keep 1).
+    float ws = 1.f;
+    if constexpr (sizeof(In) == 2) {
+        __shared__ float wred[NW];
+        float m = 0.f;
+        if (!ident) {
+            const float* src = SUMMARY ? p.state_in : (nseg > 1 ? (p.state_in ? p.snap : nullptr) : p.state_in);
+            if (src) {
+                const float* sp = src + (size_t)bh * DK * dv + vcol0 + mycol;
+                for (int i = lg; i < DK; i += 4) m = fmaxf(m, fabsf(sp[(unsigned)(i * dv)]));
+            }
+            for (int e = tid; e < C * BV / 8; e += NT) {
+                const int r = e / (BV / 8), part = e % (BV / 8);
+                m = fmaxf(m, maxabs8_bf16(buf_load16(rv_, (unsigned)(tm(r) * dv + vcol0 + 8 * part) * 2u)));
+            }
+        }
+        m = wave_max(m);
+        if (lane == 0) wred[wave] = m;
+        __syncthreads();
+        float mm = 0.f;
+#pragma unroll
+        for (int w2 = 0; w2 < NW; ++w2) mm = fmaxf(mm, wred[w2]);
+        ws = uniform(ident ? 1.f : pow2_scale(mm));
+    }
+    const float wi = uniform(1.f / ws);
+
     // ---------------- incoming state: fp32 accumulator tiles --------------
     // Macc[ib] lane (lg, lc): rows 16 ib + 4 lg + i, column mycol
     f32x4 Macc[NDB];
@@ -271,9 +304,9 @@ void gdn_walk_kernel(WalkArgs p) {
 #pragma unroll
             for (int ib = 0; ib < NDB; ++ib)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) Macc[ib][i] = sp[(unsigned)((16 * ib + 4 * lg + i) * dv + mycol)];
+                for (int i = 0; i < 4; ++i) Macc[ib][i] = sp[(unsigned)((16 * ib + 4 * lg + i) * dv + mycol)] * wi;
         }
-        // fold the maps of the preceding segments: M <- A_s M + B_s.  The next
+        // fold the maps of the preceding segments (in units of ws): M <- A_s M + B_s.  The next
         // map is loaded into registers while the current one is applied.
         constexpr int AV = DK * DK * (int)sizeof(E) / 16;      // 16-byte pieces of A_s
         constexpr int APT = (AV + NT - 1) / NT;
@@ -393,7 +426,7 @@ void gdn_walk_kernel(WalkArgs p) {
                 const int idx = tid + NT * it;
                 if (idx < VV) {
                     const int r = idx / VPRV, part = idx % VPRV;
-                    put16<In>(Vr + r * L::LDV + part * EPV, pv[it], 1.0f);
+                    put16<In>(Vr + r * L::LDV + part * EPV, pv[it], wi);
                 }
             }
         }
@@ -643,6 +676,8 @@ void gdn_walk_kernel(WalkArgs p) {
             for (int rb = 0; rb < NB; ++rb) {
 #pragma unroll
                 for (int ks = 0; ks < KS_C; ++ks) Oacc[rb] = Op::mma(fp[rb][ks], uB[ks], Oacc[rb]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) Oacc[rb][i] *= ws;
                 // rows past T fall outside the buffer and are dropped
                 unsigned oe[4];
 #pragma unroll
@@ -721,7 +756,7 @@ void gdn_walk_kernel(WalkArgs p) {
 #pragma unroll
             for (int ib = 0; ib < NDB; ++ib)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sp[(unsigned)((16 * ib + 4 * lg + i) * dv + mycol)] = Macc[ib][i];
+                for (int i = 0; i < 4; ++i) sp[(unsigned)((16 * ib + 4 * lg + i) * dv + mycol)] = Macc[ib][i] * ws;
         }
     }
 }

@@ -6,8 +6,8 @@ and the fp64 oracle is exactly homogeneous.  Powers of two keep the scaled
 bf16 v and fp32 state exact, so the HIP path must meet the same bar at every
 scale: rel-L2 2e-3, and max-abs 2e-2 times the scale.  Each kernel family that
 serves bf16 inputs is covered: the segmented walk with its correction pass
-(16 heads, 42 chunks), the unsegmented walk (48 heads), and the single-pass
-kernel of 128-token chunks.
+(16 heads, 42 chunks), the unsegmented walk (48 heads), the single-pass
+kernel of 128-token chunks, and the walker of d_k = 32 heads.
 """
 import numpy as np
 import pytest
@@ -20,11 +20,13 @@ pytestmark = pytest.mark.gpu
 
 SCALES = [2.0 ** -16, 2.0 ** -8, 2.0 ** 8, 2.0 ** 12]
 
-# (label, workload, overrides of make_call, api, chunk)
+# (label, workload, overrides of make_call, api, chunk); "walker32" runs the
+# walker of d_k = 32 heads (gdn_fwd.hip: a summary pass and a main pass)
 PATHS = [
     ("segmented", "stream_chunk_h16_d64", {}, "step", None),
     ("unsegmented", "frame_step_b2_h24_d128", {}, "step", None),
     ("chunk128", "stream_chunk_h16_d64", {"H": 4}, "chunked", 128),
+    ("walker32", "stream_chunk_h16_d64", {"H": 4, "dk": 32}, "chunked", 64),
 ]
 
 
@@ -49,6 +51,9 @@ def _bar(got, ref, s, what):
 @pytest.mark.parametrize("label,wname,over,api,chunk", PATHS, ids=[p[0] for p in PATHS])
 def test_homogeneous_in_v_and_state(gdn_lib, oracle_mod, label, wname, over, api, chunk, scale):
     wl = WORKLOADS[wname]
+    over = dict(over)
+    if "dk" in over:
+        wl = wl.replace(dk=over.pop("dk"))
     d = make_call(wl, 0, **over)
     if d["state_in"] is None:
         d["state_in"] = torch.randn(d["v"].shape[0], d["v"].shape[1], wl.dk, wl.dv,
