@@ -107,3 +107,51 @@ def test_random_shape_framewise(gdn_lib, oracle_mod, c):
     r2 = assert_close(st.to("cpu", torch.float64).numpy(), rs, False, "state")
     r3 = assert_close(z.to("cpu", torch.float64).numpy(), rz, False, "z")
     print(f"   out maxabs {r1[0]:.2e} rel {r1[1]:.2e} | state rel {r2[1]:.2e} | z rel {r3[1]:.2e}", flush=True)
+
+
+def _plan_cases(n=24, seed=31337):
+    # the launch plans: few and many heads (segmented and unsegmented walks,
+    # one or two 64-column tiles), long and short sequences, the step entry
+    # and every chunk, bf16 outputs, and v / state_in at random binary scales
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        out.append(dict(B=int(rng.integers(1, 3)), H=int(rng.choice([1, 2, 3, 8, 16, 24, 40])),
+                        T=int(rng.choice([int(rng.integers(1, 200)), int(rng.integers(200, 3000)),
+                                          int(rng.integers(3000, 6000))])),
+                        dk=int(rng.choice([64, 128])), dv=int(rng.choice([64, 128])),
+                        chunk=int(rng.choice([0, 32, 64, 128])), bf16_out=bool(rng.random() < 0.25),
+                        scale_exp=int(rng.integers(-12, 11)), state=bool(rng.random() < 0.7),
+                        seed=int(rng.integers(0, 1 << 20))))
+    return out
+
+
+PLANS = _plan_cases()
+
+
+@pytest.mark.parametrize("c", PLANS, ids=[
+    f"B{c['B']}H{c['H']}T{c['T']}k{c['dk']}v{c['dv']}C{c['chunk']}s{c['scale_exp']}"
+    f"{'-bf16out' if c['bf16_out'] else ''}{'-state' if c['state'] else ''}" for c in PLANS])
+def test_random_plan(gdn_lib, oracle_mod, c):
+    wl = WORKLOADS["stream_chunk_h16_d64"].replace(dk=c["dk"], dv=c["dv"], seed=c["seed"],
+                                                     state_sigma=0.1 if c["state"] else None)
+    announce(f"random plan {c}")
+    d = make_call(wl, 0, B=c["B"], H=c["H"], T=c["T"])
+    s = 2.0 ** c["scale_exp"]
+    d["v"] = (d["v"].float() * s).to(d["v"].dtype)
+    if d["state_in"] is not None:
+        d["state_in"] = d["state_in"] * s
+    g = to_dev(d)
+    odt = torch.bfloat16 if c["bf16_out"] else torch.float32
+    if c["chunk"] == 0:
+        out, st = gdn_lib.fwd_step(g["q"], g["k"], g["v"], g["alpha"], g["beta"], g["state_in"], out_dtype=odt)
+    else:
+        out, st = gdn_lib.fwd_chunked(g["q"], g["k"], g["v"], g["alpha"], g["beta"], g["state_in"], c["chunk"],
+                                      out_dtype=odt)
+    torch.cuda.synchronize()
+    ref, rs = oracle_mod.gdn_fwd(*(to_numpy64(d[n]) for n in ("q", "k", "v", "alpha", "beta")),
+                                 None if d["state_in"] is None else to_numpy64(d["state_in"]))
+    o = out.to("cpu", torch.float64).numpy() / s
+    r1 = assert_close(o, ref / s, False, "out")
+    r2 = assert_close(st.to("cpu", torch.float64).numpy() / s, rs / s, False, "state")
+    print(f"   out maxabs/s {r1[0]:.2e} rel {r1[1]:.2e} | state rel {r2[1]:.2e}", flush=True)
