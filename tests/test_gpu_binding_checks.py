@@ -18,23 +18,27 @@ def step_inputs():
     return to_dev(make_call(WORKLOADS["stream_chunk_h16_d64"], 0, H=2, T=300))
 
 
-def _bad_buffers(B, H, T, dk, dv):
-    dev = "cuda"
-    return {
-        "out wrong shape": dict(out=torch.empty(B, H, T + 1, dv, device=dev)),
-        "out wrong dtype": dict(out=torch.empty(B, H, T, dv, dtype=torch.float16, device=dev)),
-        "out not contiguous": dict(out=torch.empty(B, H, dv, T, device=dev).transpose(2, 3)),
-        "out on the host": dict(out=torch.empty(B, H, T, dv)),
-        "state_out wrong dtype": dict(state_out=torch.empty(B, H, dk, dv, dtype=torch.bfloat16, device=dev)),
-        "state_out wrong shape": dict(state_out=torch.empty(B, H, dv, dk + 1, device=dev)),
-    }
+# built lazily, inside the test: collection runs on machines without a GPU
+BAD_BUFFERS = {
+    "out wrong shape": lambda B, H, T, dk, dv, dev: dict(out=torch.empty(B, H, T + 1, dv, device=dev)),
+    "out wrong dtype": lambda B, H, T, dk, dv, dev: dict(out=torch.empty(B, H, T, dv, dtype=torch.float16,
+                                                                         device=dev)),
+    "out not contiguous": lambda B, H, T, dk, dv, dev: dict(out=torch.empty(B, H, dv, T,
+                                                                            device=dev).transpose(2, 3)),
+    "out on the host": lambda B, H, T, dk, dv, dev: dict(out=torch.empty(B, H, T, dv)),
+    "state_out wrong dtype": lambda B, H, T, dk, dv, dev: dict(state_out=torch.empty(B, H, dk, dv,
+                                                                                     dtype=torch.bfloat16,
+                                                                                     device=dev)),
+    "state_out wrong shape": lambda B, H, T, dk, dv, dev: dict(state_out=torch.empty(B, H, dv, dk + 1,
+                                                                                     device=dev)),
+}
 
 
-@pytest.mark.parametrize("case", list(_bad_buffers(1, 2, 300, 64, 64)))
+@pytest.mark.parametrize("case", list(BAD_BUFFERS))
 @pytest.mark.parametrize("entry", ["fwd_step", "fwd_chunked", "fwd_bidir"])
 def test_forward_entries_refuse_bad_output_buffers(gdn_lib, step_inputs, entry, case):
     g = step_inputs
-    kw = _bad_buffers(1, 2, 300, 64, 64)[case]
+    kw = BAD_BUFFERS[case](1, 2, 300, 64, 64, "cuda")
     fn = getattr(gdn_lib, entry)
     args = (g["q"], g["k"], g["v"], g["alpha"], g["beta"], g["state_in"])
     announce(f"binding check {entry} {case}")
