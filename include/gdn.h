@@ -163,13 +163,22 @@ int gdn_fwd_step_noalloc(const void* q, const void* k, const void* v,
  * (both scans include token t itself).  state_out receives the final forward
  * state S^f_{T-1}; the backward state is not kept.  Same arguments, layouts
  * and conventions as gdn_fwd_chunked; chunk 0 picks the gdn_fwd_step tile.
- * The backward scan writes its outputs, in fp32, to a plane at the start of
- * the workspace; the forward scan adds them to its own before their one
- * rounding to out_dtype.  The call therefore needs a workspace (16-byte
- * aligned) of at least that plane, B*H*T*dv*4 bytes rounded up to 256, and
- * returns GDN_ERR_ARG without one; gdn_bidir_workspace_bytes() adds the
- * split-sequence data (without them both scans run unsplit).  out must not
- * alias any input.  The output gate, if given, multiplies the sum.
+ * Two ways to run, one result to rounding:
+ *  - fused (bf16 inputs, d_k 64 or 128, d_v a multiple of 64, chunk 32 or
+ *    64, few enough heads that the sequence is split into segments, and a
+ *    workspace of gdn_bidir_workspace_bytes()): one launch walks the
+ *    segments of both directions, the backward one's mirrored so that both
+ *    directions' segment s holds the same tokens, and one correction pass
+ *    forms every output as the sum of both directions' outputs, rounded
+ *    once -- the page's single output pass;
+ *  - otherwise the backward scan writes its outputs, in fp32, to a plane at
+ *    the start of the workspace and the forward scan adds them to its own
+ *    before their one rounding to out_dtype.
+ * The call needs a workspace (16-byte aligned) of at least that plane,
+ * B*H*T*dv*4 bytes rounded up to 256, and returns GDN_ERR_ARG without one;
+ * between the plane and gdn_bidir_workspace_bytes() the second way runs
+ * (both scans unsplit with the plane alone).  out must not alias any input.
+ * The output gate, if given, multiplies the sum.
  */
 int gdn_fwd_bidir(const void* q, const void* k, const void* v,
                   const void* alpha, const void* beta,
@@ -179,7 +188,10 @@ int gdn_fwd_bidir(const void* q, const void* k, const void* v,
 
 /*
  * Workspace size (bytes) for gdn_fwd_bidir with this shape and chunk (0: the
- * gdn_fwd_step tile): the fp32 plane of B*H*T*dv values rounded up to 256
+ * gdn_fwd_step tile) and opts (the input dtype picks the path).  Where the
+ * fused call applies: two sets of split-sequence data (one per direction,
+ * each rounded up to 256 bytes), planned for both directions' walks in one
+ * launch.  Otherwise: the fp32 plane of B*H*T*dv values rounded up to 256
  * bytes, then the split-sequence data of gdn_workspace_bytes().  Returns 0
  * for T == 0 and for invalid shapes.
  */

@@ -129,15 +129,16 @@ size_t seg_workspace(int in_f32, int B, int H, int dk, int dv, int nseg) {
 // the correction pass pays a launch and its first memory round trips, one
 // folded map per preceding segment and the rewrite of the segment's outputs.
 // A launch of more workgroups than compute units runs in rounds.  Constants
-// measured on MI355X.
-Plan pipe_plan(int B, int H, int T, int dk, int dv, int chunk) {
+// measured on MI355X.  walks = 2: a fused bidirectional call, whose launches
+// walk and correct both directions at once.
+Plan pipe_plan(int B, int H, int T, int dk, int dv, int chunk, int walks = 1) {
     Plan pl{};
     pl.pipe = true;
     const int nchunks = (int)(((long long)T + chunk - 1) / chunk);
     const long long bh = (long long)B * H;
     const long long base = bh * (dv / 64);                                  // workgroups, unsegmented
     const int cts = gdn::pipe_seg_tiles(dk, dv);
-    const long long sb = bh * ((dk + dv) / (64 * cts));                     // per segment
+    const long long sb = walks * bh * ((dk + dv) / (64 * cts));             // per segment
     const double step_us = (dk == 64 ? 2.7 : 4.0) * (chunk == 64 ? 1.0 : 0.6);
     const double wstep = dk == 64 ? 1.45 : 1.33;         // segment-walk step / unsegmented step
     const double fix = 9.0 / step_us;                     // correction pass: launch, first loads
@@ -150,7 +151,7 @@ Plan pipe_plan(int B, int H, int T, int dk, int dv, int chunk) {
         const int L = (nchunks + n - 1) / n;
         const int ns = (nchunks + L - 1) / L;
         if (ns < 2 || ns != n) continue;
-        const double cost = rounds(sb * ns) * (L + 1) * wstep + fix + fold * (ns - 1) + corr * L;
+        const double cost = rounds(sb * ns) * (L + 1) * wstep + fix + fold * (ns - 1) + corr * walks * L;
         if (best_n == 0 || cost < best) { best = cost; best_n = ns; }
     }
     // segments only for a clear gain over the unsegmented walk
@@ -189,6 +190,21 @@ Plan make_plan(int in_f32, int B, int H, int T, int dk, int dv, int chunk) {
     pl.nseg = nchunks > 0 ? (nchunks + pl.seg_chunks - 1) / pl.seg_chunks : 1;
     pl.ws_bytes = seg_workspace(in_f32, B, H, dk, dv, pl.nseg);
     return pl;
+}
+
+// Segment data of the pipelined walker at w (gdn::pipe_workspace bytes): the
+// maps of all nseg segments, the copy of state_in, Phi, the partial outputs
+// and the working scales.
+void carve_pipe(char* w, size_t bh, int nseg, int seg_chunks, int chunk, int dk, int dv, void** summA,
+                float** summB, float** snap, void** phi, void** ostage, float** sscale) {
+    const size_t ns = (size_t)nseg, rows = (size_t)seg_chunks * chunk;
+    *summA = w;
+    *summB = reinterpret_cast<float*>(w + bh * ns * dk * dk * 2);
+    *snap = *summB + bh * ns * dk * dv;
+    char* ph = reinterpret_cast<char*>(*snap + bh * dk * dv);
+    *phi = ph;
+    *ostage = ph + bh * ns * rows * dk * 2;
+    *sscale = reinterpret_cast<float*>(reinterpret_cast<char*>(*ostage) + bh * ns * rows * dv * 2);
 }
 
 // One scan over the sequence.  reverse: walk the tokens backward; accumulate:
@@ -230,18 +246,16 @@ int scan(const void* q, const void* k, const void* v, const void* alpha, const v
         a.sscale = nullptr;
         if (pl.nseg > 1) {
             const size_t bh = (size_t)B * H;
-            // maps of segments 0 .. nseg-2 (segmented walker) or of all nseg (pipelined)
-            const size_t ns = (size_t)(pl.pipe ? pl.nseg : pl.nseg - 1);
             char* w = reinterpret_cast<char*>(o.workspace);
-            a.summA = w;
-            a.summB = reinterpret_cast<float*>(w + bh * ns * dk * dk * (a.in_f32 ? 4 : 2));
-            a.snap = a.summB + bh * ns * dk * dv;
             if (pl.pipe) {
-                char* ph = reinterpret_cast<char*>(a.snap + bh * dk * dv);
-                a.phi = ph;
-                a.ostage = ph + bh * pl.nseg * (size_t)pl.seg_chunks * chunk * dk * 2;
-                a.sscale = reinterpret_cast<float*>(reinterpret_cast<char*>(a.ostage) +
-                                                    bh * pl.nseg * (size_t)pl.seg_chunks * chunk * dv * 2);
+                carve_pipe(w, bh, pl.nseg, pl.seg_chunks, chunk, dk, dv, &a.summA, &a.summB, &a.snap, &a.phi,
+                           &a.ostage, &a.sscale);
+            } else {
+                // maps of segments 0 .. nseg-2
+                const size_t ns = (size_t)(pl.nseg - 1);
+                a.summA = w;
+                a.summB = reinterpret_cast<float*>(w + bh * ns * dk * dk * (a.in_f32 ? 4 : 2));
+                a.snap = a.summB + bh * ns * dk * dv;
             }
         }
         if (pl.nseg > 1 && (reinterpret_cast<uintptr_t>(o.workspace) & 15u))
@@ -270,12 +284,55 @@ size_t plane_bytes(int B, int H, int T, int dv) {
 }
 size_t bidir_workspace(int B, int H, int T, int dk, int dv, int chunk, const gdn_opts& o);
 
-// Bidirectional: the backward scan (zero state, tokens in reverse, no state
-// kept) writes its fp32 outputs to the plane, then the forward scan from
-// state_in adds the plane to its own outputs before their one rounding and
-// writes state_out.  The output gate is applied in both (it distributes over
-// the sum).  Stream order keeps the two scans apart, so they share the
-// segment data; a workspace of the plane alone runs both scans unsplit.
+// Fused bidirectional plan: the pipelined walker with segments, both
+// directions walked by one launch and corrected by one pass that writes the
+// sum (no plane).  The segment count is planned for the doubled launch; the
+// workspace holds one set of segment data per direction.  nseg <= 1: the
+// fused path does not apply.
+Plan bidir_fused_plan(const gdn_opts& o, int B, int H, int T, int dk, int dv, int chunk) {
+    Plan pl{};
+    if (!gdn::pipe_supported(o.in_dtype == GDN_F32, dk, dv, chunk)) return pl;
+    pl = pipe_plan(B, H, T, dk, dv, chunk, 2);
+    if (pl.nseg > 1) pl.ws_bytes = 2 * ((pl.ws_bytes + 255) & ~(size_t)255);
+    return pl;
+}
+
+int scan_bidir_fused(const void* q, const void* k, const void* v, const void* alpha, const void* beta,
+                     const float* state_in, void* out, float* state_out,
+                     int B, int H, int T, int dk, int dv, int chunk, const gdn_opts& o, const Plan& pl) {
+    gdn::WalkArgs a{};
+    a.rev_wg = debug_reverse_workgroups();
+    a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta;
+    a.state_in = state_in; a.out = out; a.state_out = state_out;
+    a.B = B; a.H = H; a.T = T; a.dk = dk; a.dv = dv;
+    a.scale = o.scale; a.eps = o.eps; a.qk_l2norm = o.qk_l2norm ? 1 : 0;
+    a.out_bf16 = o.out_dtype == GDN_BF16; a.in_f32 = 0;
+    a.gate_logits = o.gate_logits ? 1 : 0;
+    a.out_gate = o.out_gate;
+    a.bidir = 1;
+    a.nseg = pl.nseg;
+    a.seg_chunks = pl.seg_chunks;
+    const size_t bh = (size_t)B * H;
+    char* w = reinterpret_cast<char*>(o.workspace);
+    carve_pipe(w, bh, pl.nseg, pl.seg_chunks, chunk, dk, dv, &a.summA, &a.summB, &a.snap, &a.phi, &a.ostage,
+               &a.sscale);
+    float* unused_snap = nullptr;
+    carve_pipe(w + pl.ws_bytes / 2, bh, pl.nseg, pl.seg_chunks, chunk, dk, dv, &a.bw.summA, &a.bw.summB,
+               &unused_snap, &a.bw.phi, &a.bw.ostage, &a.bw.sscale);
+    hipError_t e = gdn::launch_pipe(a, chunk, reinterpret_cast<hipStream_t>(o.stream));
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return GDN_OK;
+}
+
+// Bidirectional.  Fused (pipelined walker with segments, and a workspace of
+// gdn_bidir_workspace_bytes): one launch walks both directions' segments, one
+// correction pass writes the sum.  Otherwise: the backward scan (zero state,
+// tokens in reverse, no state kept) writes its fp32 outputs to the plane,
+// then the forward scan from state_in adds the plane to its own outputs
+// before their one rounding and writes state_out.  The output gate is applied
+// in both (it distributes over the sum).  Stream order keeps the two scans
+// apart, so they share the segment data; a workspace of the plane alone runs
+// both scans unsplit.
 int run_bidir(const void* q, const void* k, const void* v, const void* alpha, const void* beta,
               const float* state_in, void* out, float* state_out,
               int B, int H, int T, int dk, int dv, int chunk, const gdn_opts* opts) {
@@ -292,6 +349,9 @@ int run_bidir(const void* q, const void* k, const void* v, const void* alpha, co
         return fail(GDN_ERR_ARG, "gdn_fwd_bidir needs a 16-byte aligned workspace of at least the "
                     "fp32 plane (gdn_bidir_workspace_bytes() = %s bytes with the segment data)", n);
     }
+    const Plan fp = bidir_fused_plan(o, B, H, T, dk, dv, chunk);
+    if (fp.nseg > 1 && o.workspace_bytes >= fp.ws_bytes)
+        return scan_bidir_fused(q, k, v, alpha, beta, state_in, out, state_out, B, H, T, dk, dv, chunk, o, fp);
     float* plane = reinterpret_cast<float*>(o.workspace);
     gdn_opts os = o;                               // segment data after the plane
     os.workspace = reinterpret_cast<char*>(o.workspace) + pb;
@@ -315,8 +375,12 @@ size_t workspace_for(int B, int H, int T, int dk, int dv, int chunk, const gdn_o
 size_t bidir_workspace(int B, int H, int T, int dk, int dv, int chunk, const gdn_opts& o) {
     if (!sizes_ok(B, H, T, dk, dv) || !head_ok(dk) || !head_ok(dv)) return 0;
     if (chunk != 32 && chunk != 64 && chunk != 128) return 0;
+    if (T == 0) return 0;
+    const size_t pb = plane_bytes(B, H, T, dv);
+    const Plan fp = bidir_fused_plan(o, B, H, T, dk, dv, chunk);
+    if (fp.nseg > 1) return fp.ws_bytes > pb ? fp.ws_bytes : pb;
     const Plan pl = make_plan(o.in_dtype == GDN_F32, B, H, T, dk, dv, chunk);
-    return T == 0 ? 0 : plane_bytes(B, H, T, dv) + pl.ws_bytes;
+    return pb + pl.ws_bytes;
 }
 
 // Frame-wise Gated DeltaNet with a normalised readout: frame summaries, a

@@ -226,13 +226,18 @@ __device__ __forceinline__ void add_f32x4(V4& o, uint4 w) {
 // position t < T is token T - 1 - t.  Positions at or past T (the padding of
 // a partial last chunk) stay rows at or past T in both directions, so their
 // offsets lie past the range as usual (loads read zero, stores are dropped)
-// and no offset is ever negative.
+// and no offset is ever negative.  tok_map_padded(P) reverses the padded
+// length P (a whole number of chunks) instead: position t is row P - 1 - t,
+// so the backward walk's chunks are the forward chunks in reverse and its
+// padding rows (at or past T) come first.
 struct TokMap {
-    int T;
+    int last;    // reversed: position t < lim is row last - t
+    int lim;
     bool rev;
-    __device__ __forceinline__ int operator()(int t) const { return (rev && t < T) ? T - 1 - t : t; }
+    __device__ __forceinline__ int operator()(int t) const { return (rev && t < lim) ? last - t : t; }
 };
-__device__ __forceinline__ TokMap tok_map(int T, int reverse) { return TokMap{T, reverse != 0}; }
+__device__ __forceinline__ TokMap tok_map(int T, int reverse) { return TokMap{T - 1, T, reverse != 0}; }
+__device__ __forceinline__ TokMap tok_map_padded(int P) { return TokMap{P - 1, P, true}; }
 
 // Offset past every range a resource here covers (ranges stay below 2 GiB):
 // a load from it returns zeros and a store to it is dropped, with no memory

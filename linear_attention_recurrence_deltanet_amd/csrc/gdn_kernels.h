@@ -49,6 +49,19 @@ struct WalkArgs : FwdArgs {
                              // value columns; staged outputs and maps are in units of it
     int nseg;                // segments per sequence (1: no split)
     int seg_chunks;          // chunks per segment
+    // Both directions of a bidirectional call in one segmented launch pair
+    // (pipelined walker): the walk launch covers direction 0 (forward, the
+    // buffers above) and direction 1 (tokens in reverse from a zero state,
+    // the buffers in bw, segments mirrored so that both directions' segment
+    // s holds the same tokens); one correction pass writes the sum.
+    int bidir;
+    struct SegBufs {
+        void* summA;
+        float* summB;
+        void* phi;
+        void* ostage;
+        float* sscale;
+    } bw;
 };
 
 // Segmented walker: summary pass (if nseg > 1) then main pass.

@@ -304,17 +304,25 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
         const int w8 = (int)gridDim.x / 8 * 8;
         if (wg < w8) wg = (wg % 8) * (w8 / 8) + wg / 8;
     }
-    int bh, seg, ctile;
+    int bh, seg, ctile, dir = 0;
     {
         const int ncol = SEG ? (DK + dv) / BV : dv / BV;
         ctile = wg % ncol;
         const int r = wg / ncol;
         seg = r % nseg;
         bh = r / nseg;
+        // a fused bidirectional launch: both directions of a head adjacent
+        if constexpr (SEG && EXT) {
+            if (p.bidir) {
+                dir = bh & 1;
+                bh >>= 1;
+            }
+        }
     }
     bh = uniform(bh);
     seg = uniform(seg);
     ctile = uniform(ctile);
+    if constexpr (SEG && EXT) dir = uniform(dir);
     // tile-local columns [vlo, BV) are value columns; global v column = vbase + local
     int vlo, vbase;
     if constexpr (SEG) {
@@ -331,6 +339,13 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
     const int ch0 = seg * p.seg_chunks;
     const int ch1 = min(nchunks, ch0 + p.seg_chunks);
     const int nch = max(0, ch1 - ch0);
+    // First chunk in walk order.  Direction 1 of a fused bidirectional call
+    // walks the padded sequence backward (walk chunk w is chunk
+    // nchunks - 1 - w, rows reversed), so its segment `seg` covers the same
+    // chunks ch0 .. ch1 - 1 as the forward one, last chunk first; it stores
+    // its partial outputs and Phi in token order for the correction pass.
+    const int wc0 = dir ? nchunks - ch1 : ch0;
+    const float* state_in = dir ? nullptr : p.state_in;     // the backward scan starts at zero
 
     const uint16_t* qg = reinterpret_cast<const uint16_t*>(p.q) + (size_t)bh * T * DK;
     const uint16_t* kg = reinterpret_cast<const uint16_t*>(p.k) + (size_t)bh * T * DK;
@@ -353,16 +368,19 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
     // accumulating outputs add fp32 values from a separate plane before the store
     const rsrc_t rac_ = make_rsrc(accum ? p.acc_src + (size_t)bh * T * dv : nullptr,
                                   accum ? (unsigned)T * dv * 4u : 0u);
-    const TokMap tm = tok_map(T, EXT && p.reverse);   // walk position -> token
+    // walk position -> token
+    const TokMap tm = dir ? tok_map_padded(nchunks * C) : tok_map(T, EXT && p.reverse);
     const rsrc_t rg_ = make_rsrc(gated ? (const char*)p.out_gate + (size_t)bh * T * dv * 2 : nullptr,
                                  gated ? (unsigned)T * dv * 2u : 0u);
     // Phi of this segment: [chunk][row block][k-step of 32 columns of d_k][lane] x 8 fp16,
     // an MFMA operand fragment in accumulator k order (16-column blocks 2 ks, 2 ks + 1);
     // partial outputs: [chunk][row block][16 value columns][lane] x 4 fp16
-    const rsrc_t rphi_ = make_rsrc(SEG ? reinterpret_cast<E*>(p.phi) + ((size_t)bh * nseg + seg) * (size_t)p.seg_chunks * C * DK
+    const rsrc_t rphi_ = make_rsrc(SEG ? reinterpret_cast<E*>(dir ? p.bw.phi : p.phi) +
+                                             ((size_t)bh * nseg + seg) * (size_t)p.seg_chunks * C * DK
                                        : nullptr,
                                    SEG ? (unsigned)(p.seg_chunks * C * DK * 2) : 0u);
-    const rsrc_t rosg_ = make_rsrc(SEG ? reinterpret_cast<E*>(p.ostage) + ((size_t)bh * nseg + seg) * (size_t)p.seg_chunks * C * dv
+    const rsrc_t rosg_ = make_rsrc(SEG ? reinterpret_cast<E*>(dir ? p.bw.ostage : p.ostage) +
+                                             ((size_t)bh * nseg + seg) * (size_t)p.seg_chunks * C * dv
                                        : nullptr,
                                    SEG ? (unsigned)(p.seg_chunks * C * dv * 2) : 0u);
 
@@ -440,8 +458,8 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
                             Macc[ct][ib][i] = (16 * ib + 4 * lg + i == gcol) ? 1.f : 0.f;
                 }
             } else {
-                if (p.state_in) {
-                    const float* sp = p.state_in + (size_t)bh * DK * dv + vcol;
+                if (state_in) {
+                    const float* sp = state_in + (size_t)bh * DK * dv + vcol;
 #pragma unroll
                     for (int ib = 0; ib < NDB; ++ib)
 #pragma unroll
@@ -452,7 +470,7 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
         }
     };
 
-    if (!is_state && nch > 0) prefetch(ch0);
+    if (!is_state && nch > 0) prefetch(wc0);
 
     // The two roles run separate loops with the same barrier sequence, so the
     // compiler allocates registers per role (the branch is wave-uniform).
@@ -468,8 +486,8 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
             if constexpr (SEG) {
-                if (!ident(ct) && p.state_in) {
-                    const float* sp = p.state_in + (size_t)bh * DK * dv + vbase + col0(ct) + lc;
+                if (!ident(ct) && state_in) {
+                    const float* sp = state_in + (size_t)bh * DK * dv + vbase + col0(ct) + lc;
 #pragma unroll
                     for (int ib = 0; ib < NDB; ++ib)
 #pragma unroll
@@ -486,8 +504,11 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
 #pragma unroll
             for (int j = 0; j < C / 32; ++j) {
                 const int e = lane + 64 * j, r = e >> 1, part = e & 1;
-                const uint4 x = buf_load16(rv_, ident(ct) ? kOffNone
-                                                          : (unsigned)(tm(r) * dv + vbase + col0(ct) + 8 * part) * 2u);
+                // the first chunk walked: the last C tokens for direction 1
+                // (whose first walk chunk may be mostly padding)
+                const int tr = dir ? T - 1 - r : tm(r);
+                const uint4 x = buf_load16(rv_, (ident(ct) || tr < 0) ? kOffNone
+                                                          : (unsigned)(tr * dv + vbase + col0(ct) + 8 * part) * 2u);
                 m = fmaxf(m, maxabs8_bf16(x));
             }
             wsc[ct] = uniform(ident(ct) ? 1.f : pow2_scale(wave_max(m)));
@@ -500,14 +521,15 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
             if constexpr (SEG) {
                 if (!ident(ct)) {
                     if (seg == 0) {
-                        if (p.state_in) {
+                        if (state_in) {
                             float* sn = p.snap + (size_t)bh * DK * dv + vbase + col0(ct) + lc;
 #pragma unroll
                             for (int ib = 0; ib < NDB; ++ib)
 #pragma unroll
                                 for (int i = 0; i < 4; ++i) sn[(unsigned)((16 * ib + 4 * lg + i) * dv)] = Macc[ct][ib][i];
                         }
-                        if (lane == 0) p.sscale[(size_t)bh * (dv / 16) + (vbase + col0(ct)) / 16] = wsc[ct];
+                        if (lane == 0)
+                            (dir ? p.bw.sscale : p.sscale)[(size_t)bh * (dv / 16) + (vbase + col0(ct)) / 16] = wsc[ct];
                     }
 #pragma unroll
                     for (int ib = 0; ib < NDB; ++ib) Macc[ct][ib] = zero4();
@@ -528,7 +550,7 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
                 }
         }
         for (int s = 0; s <= nch; ++s) {
-            const int pc = ch0 + s;
+            const int pc = wc0 + s;
             const int vb = s & 1;
             if constexpr (EXT && !SEG) {
                 // the gate loaded last step arrives here on every path, so no
@@ -572,9 +594,13 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
                         // O^T = M^T Q^^T diag(gam) + U^T P^T, tiles of 16 columns x 16 rows;
                         // lane (lg, lc) holds row 16 rb + lc, columns col0 + 4 lg + i
                         const int cb = (ctile * BV + col0(ct)) / 16;      // 16-column block of the tile
-                        const int lch = pc - 1 - ch0;                     // chunk within the segment
+                        // chunk within the segment, row block and lane of row lc, in
+                        // token order (direction 1 mirrors all three)
+                        const int lch = dir ? nch - s : s - 1;
+                        const unsigned lrow = (unsigned)(lane ^ (dir ? 15 : 0));
 #pragma unroll
                         for (int rb = 0; rb < NB; ++rb) {
+                            const int rbs = dir ? NB - 1 - rb : rb;
                             const float gr = v_gam[16 * rb + lc];
                             f32x4 o;
 #pragma unroll
@@ -588,13 +614,13 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
                                 // offset goes in the scalar operand
                                 if (idt) {
                                     // identity columns: Phi, an operand fragment as stored
-                                    buf_store8<kStageStorePolicy>(rphi_, (unsigned)lane * 16u, w,
-                                               uniform((lch * C * DK + (rb * KS_D + cb / 2) * 512 + (cb & 1) * 4) * 2));
+                                    buf_store8<kStageStorePolicy>(rphi_, lrow * 16u, w,
+                                               uniform((lch * C * DK + (rbs * KS_D + cb / 2) * 512 + (cb & 1) * 4) * 2));
                                 } else {
                                     // value columns: partial output (zero incoming state)
                                     const int vb16 = cb - DK / 16;
-                                    buf_store8<kStageStorePolicy>(rosg_, (unsigned)lane * 8u, w,
-                                               uniform((lch * C * dv + (rb * (dv / 16) + vb16) * 256) * 2));
+                                    buf_store8<kStageStorePolicy>(rosg_, lrow * 8u, w,
+                                               uniform((lch * C * dv + (rbs * (dv / 16) + vb16) * 256) * 2));
                                 }
                             } else {
 #pragma unroll
@@ -738,12 +764,11 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
         }
     } else {
         for (int s = 0; s <= nch; ++s) {
-            const int pc = ch0 + s;
+            const int pc = wc0 + s;
             const int vb = s & 1;
             // ---- phase 1: normalise chunk pc, decay scan, prefetch pc + 1
             if (s == nch) break;
             // key waves: q^, k^ (normalised) and v rows of chunk pc; decay scan
-            const int n = min(C, T - pc * C);
 #pragma unroll
             for (int it = 0; it < QPT; ++it) {
                 const int idx = ktid + NPT * it;
@@ -772,8 +797,9 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
 #pragma unroll
                 for (int e = 0; e < TPL; ++e) {
                     const int r = lane * TPL + e;
-                    const bool ok = r < n;
-                    // padding rows: alpha = 1, beta = 0
+                    const bool ok = r < C && tm(pc * C + r) < T;
+                    // padding rows (past T, at either end of the walk) and lanes past
+                    // the chunk: alpha = 1, beta = 0
                     bb[e] = ok ? gate_beta(bf16_to_f32(pb[e]), logits) : 0.f;
                     run += ok ? gate_log2_alpha(bf16_to_f32(pa[e]), logits) : 0.f;
                     la[e] = run;
@@ -793,7 +819,7 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
                     }
                 }
             }
-            if (pc + 1 < ch1) prefetch(pc + 1);
+            if (s + 1 < nch) prefetch(pc + 1);
             __syncthreads();
             const float* vcur = vecs + vb * 4 * C;
             const float* v_g2 = vcur;
@@ -933,8 +959,8 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
         // MFMA A-operand fragments [ib][ks][lane] x 16 bytes (fp16), B_s in
         // accumulator order [column block of 16][ib][lane] x f32x4.  Each
         // fold operand is then one coalesced 16-byte load per lane.
-        E* summA_bh = reinterpret_cast<E*>(p.summA) + (size_t)bh * nseg * DK * DK;
-        float* summB_bh = p.summB + (size_t)bh * nseg * DK * dv;
+        E* summA_bh = reinterpret_cast<E*>(dir ? p.bw.summA : p.summA) + (size_t)bh * nseg * DK * DK;
+        float* summB_bh = (dir ? p.bw.summB : p.summB) + (size_t)bh * nseg * DK * dv;
         __syncthreads();                                  // both role loops done: LDS free
         E* As = reinterpret_cast<E*>(smem);
         if (is_state) {
@@ -996,7 +1022,11 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
 // map.  The segment's outputs then get Phi M added, row block rg of each
 // chunk on row group rg (fp32 out, or bf16); the last segment also applies
 // its own map for state_out.
-template <int DK, int C>
+// BI (fused bidirectional call): the backward direction's state entering the
+// segment is folded the same way, from zero through the maps of the segments
+// after this one, last first; each output is the sum of both directions'
+// corrected outputs, each in its own working scale, rounded once.
+template <int DK, int C, bool BI>
 __global__ __launch_bounds__(1024) void gdn_pipe_fix_kernel(WalkArgs p) {
     typedef OpF16 Op;
     typedef Op::frag F;
@@ -1006,7 +1036,9 @@ __global__ __launch_bounds__(1024) void gdn_pipe_fix_kernel(WalkArgs p) {
     constexpr int APC = DK * DK * 2 / 16;               // 16-byte pieces of one A_s
     constexpr int APT = (APC + 1023) / 1024;            // ... per thread
     constexpr int PPG = RG * 16 * DK * 2 / 16;          // 16-byte pieces of Phi per correction group
-    constexpr int D = DK == 64 ? 4 : 3;                 // maps in flight
+    // maps in flight; a bidirectional pass at d_k = 128 keeps two, as it
+    // holds the first direction's folded state in registers meanwhile
+    constexpr int D = DK == 64 ? 4 : (BI ? 2 : 3);
     static_assert(NDB % RG == 0 && RG % NB == 0 && PPG <= 1024 && APC % 512 == 0, "fix layout");
     // d_k = 128: A_s of the map being folded (two copies); d_k = 64: rings of
     // FR maps (A_s and the tile's B_s) staged for the four column owners
@@ -1017,6 +1049,10 @@ __global__ __launch_bounds__(1024) void gdn_pipe_fix_kernel(WalkArgs p) {
     __shared__ uint4 Bs2[2][DK == 64 ? FR * BPC : 1];
     __shared__ uint4 Mf[2][KS_D][4][64];                // M as fp16 B fragments [k-step][column group][lane]
     __shared__ uint4 Phs[2][PPG];
+    // the backward direction's Phi [2][PPG], staged over the fold buffers,
+    // which are free once both folds are done
+    static_assert((DK == 64 ? FR * APC : APC) >= 2 * PPG, "backward Phi staging");
+    uint4* const Phb = DK == 64 ? &As2[0][0] : &Ast[0][0];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -1042,15 +1078,30 @@ __global__ __launch_bounds__(1024) void gdn_pipe_fix_kernel(WalkArgs p) {
     const int nchunks = (T + C - 1) / C;
     const int ch0 = seg * p.seg_chunks;
     const int ch1 = min(nchunks, ch0 + p.seg_chunks);
-    const rsrc_t rA = make_rsrc(reinterpret_cast<const _Float16*>(p.summA) + (size_t)bh * nseg * DK * DK,
-                                (unsigned)(nseg * DK * DK * 2));
-    const rsrc_t rB = make_rsrc(p.summB + (size_t)bh * nseg * DK * dv, (unsigned)(nseg * DK * dv * 4));
-    const rsrc_t rP = make_rsrc(reinterpret_cast<const _Float16*>(p.phi) +
-                                    ((size_t)bh * nseg + seg) * (size_t)p.seg_chunks * C * DK,
-                                (unsigned)(p.seg_chunks * C * DK * 2));
-    const rsrc_t rO = make_rsrc(reinterpret_cast<const _Float16*>(p.ostage) +
-                                    ((size_t)bh * nseg + seg) * (size_t)p.seg_chunks * C * dv,
-                                (unsigned)(p.seg_chunks * C * dv * 2));
+    // segment data of one direction: maps of all segments, this segment's Phi
+    // and partial outputs
+    auto maps_a = [&](const void* base) {
+        return make_rsrc(reinterpret_cast<const _Float16*>(base) + (size_t)bh * nseg * DK * DK,
+                         (unsigned)(nseg * DK * DK * 2));
+    };
+    auto maps_b = [&](const float* base) {
+        return make_rsrc(base + (size_t)bh * nseg * DK * dv, (unsigned)(nseg * DK * dv * 4));
+    };
+    auto seg_phi = [&](const void* base) {
+        return make_rsrc(reinterpret_cast<const _Float16*>(base) +
+                             ((size_t)bh * nseg + seg) * (size_t)p.seg_chunks * C * DK,
+                         (unsigned)(p.seg_chunks * C * DK * 2));
+    };
+    auto seg_out = [&](const void* base) {
+        return make_rsrc(reinterpret_cast<const _Float16*>(base) +
+                             ((size_t)bh * nseg + seg) * (size_t)p.seg_chunks * C * dv,
+                         (unsigned)(p.seg_chunks * C * dv * 2));
+    };
+    const rsrc_t rA = maps_a(p.summA), rB = maps_b(p.summB), rP = seg_phi(p.phi), rO = seg_out(p.ostage);
+    const rsrc_t rAb = BI ? maps_a(p.bw.summA) : make_rsrc(nullptr, 0u);
+    const rsrc_t rBb = BI ? maps_b(p.bw.summB) : make_rsrc(nullptr, 0u);
+    const rsrc_t rPb = BI ? seg_phi(p.bw.phi) : make_rsrc(nullptr, 0u);
+    const rsrc_t rOb = BI ? seg_out(p.bw.ostage) : make_rsrc(nullptr, 0u);
     const rsrc_t rW = make_rsrc((const char*)p.out + (size_t)bh * T * dv * (p.out_bf16 ? 2 : 4),
                                 (unsigned)T * dv * (p.out_bf16 ? 2u : 4u));
     const bool gated = p.out_gate != nullptr;
@@ -1059,8 +1110,9 @@ __global__ __launch_bounds__(1024) void gdn_pipe_fix_kernel(WalkArgs p) {
     const int col4 = vt * 64 + 16 * cg + 4 * lg;        // first of this lane's four output columns
     const TokMap tm = tok_map(T, p.reverse);            // walk position -> token
     // accumulating outputs add an fp32 plane before the store (empty range otherwise)
-    const rsrc_t rAc = make_rsrc(p.accumulate ? p.acc_src + (size_t)bh * T * dv : nullptr,
-                                 p.accumulate ? (unsigned)T * dv * 4u : 0u);
+    const bool accum = !BI && p.accumulate;
+    const rsrc_t rAc = make_rsrc(accum ? p.acc_src + (size_t)bh * T * dv : nullptr,
+                                 accum ? (unsigned)T * dv * 4u : 0u);
 
     // Loads and stores below are unconditional (kOffNone where there is
     // nothing to move) so that the compiler counts the loads in flight
@@ -1069,221 +1121,255 @@ __global__ __launch_bounds__(1024) void gdn_pipe_fix_kernel(WalkArgs p) {
     // ---- working scale of these 16 value columns, the one every walk of them
     // used: partial outputs, maps and the copy of state_in are in its units.
     // The pass folds and corrects on those units too and multiplies outputs
-    // and state back (a uniform address: a scalar load).
+    // and state back (a uniform address: a scalar load).  Each direction of a
+    // bidirectional call has its own.
     const float s_w = p.sscale[(size_t)bh * (dv / 16) + c16];
-
-    // ---- state entering segment 0: rows 16 (rg RB + r) + 4 lg + i, column col
-    f32x4 Macc[RB];
-#pragma unroll
-    for (int r = 0; r < RB; ++r) Macc[r] = zero4();
-    if (has_in) {
-        const float* sp = p.snap + (size_t)bh * DK * dv + col;
-#pragma unroll
-        for (int r = 0; r < RB; ++r)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) Macc[r][i] = sp[(16 * (rg * RB + r) + 4 * lg + i) * dv];
-    }
+    const float s_b = BI ? p.bw.sscale[(size_t)bh * (dv / 16) + c16] : 0.f;
 
     // ---- correction operands of a group of CPG chunks (RG row blocks): one
     // 16-byte piece of Phi per thread, staged in LDS; the wave's own row block
-    // of the partial outputs (fp16, 4 columns per lane)
-    auto cload = [&](uint4& h, uint2& o, uint2& gt, uint4& av, int g) {
+    // of the partial outputs (fp16, 4 columns per lane); the same of the
+    // backward direction (stored in token order by its walk)
+    auto cload = [&](uint4& h, uint2& o, uint2& gt, uint4& av, uint4& hb, uint2& ob, int g) {
         const int c0 = ch0 + g * CPG;
         const int c = c0 + rg / NB, rb = rg % NB;
-        h = buf_load16(rP, (c0 < ch1 && tid < PPG) ? (unsigned)((c0 - ch0) * C * DK * 2 + tid * 16) : kOffNone);
-        o = buf_load8(rO, c < ch1 ? (unsigned)((((c - ch0) * NB + rb) * (dv / 16) + c16) * 64 + lane) * 8u
-                                  : kOffNone);
+        const unsigned hoff = (c0 < ch1 && tid < PPG) ? (unsigned)((c0 - ch0) * C * DK * 2 + tid * 16) : kOffNone;
+        const unsigned ooff = c < ch1 ? (unsigned)((((c - ch0) * NB + rb) * (dv / 16) + c16) * 64 + lane) * 8u
+                                      : kOffNone;
+        h = buf_load16(rP, hoff);
+        o = buf_load8(rO, ooff);
+        if constexpr (BI) {
+            hb = buf_load16(rPb, hoff);
+            ob = buf_load8(rOb, ooff);
+        }
         // output gate of the same four elements (the range is empty without one)
         const unsigned e = (unsigned)(tm(c * C + 16 * rb + lc) * dv + col4);
         gt = buf_load8(rG, c < ch1 ? e * 2u : kOffNone);
         // values to accumulate onto (the range is empty unless accumulating)
-        av = buf_load16(rAc, c < ch1 ? e * 4u : kOffNone);
+        if constexpr (!BI) av = buf_load16(rAc, c < ch1 ? e * 4u : kOffNone);
     };
-    uint4 ph[2], av2[2];
-    uint2 ov[2], gv2[2];
-    cload(ph[0], ov[0], gv2[0], av2[0], 0);
-    cload(ph[1], ov[1], gv2[1], av2[1], 1);
+    uint4 ph[2], av2[2], phb[2];
+    uint2 ov[2], gv2[2], ovb[2];
+    cload(ph[0], ov[0], gv2[0], av2[0], phb[0], ovb[0], 0);
+    cload(ph[1], ov[1], gv2[1], av2[1], phb[1], ovb[1], 1);
 
+    // ---- the state entering the segment, per direction, as fp16 B fragments
+    // of the whole of M for every wave.  A direction folds nfold maps, map
+    // indices base, base + step, ..., onto the copy of state_in (from_snap) or
+    // zero; own: the map after them is this segment's own, applied to M_in for
+    // state_out.
     F mI[KS_D];
+    F mIb[BI ? KS_D : 1];
     if constexpr (DK == 64) {
     // ---- fold by column owners: waves 0..3 (column group cg = wave) keep all
     // d_k rows of their 16 columns in fp32, so the state needs no exchange
     // between waves (its operand fragments come from the owner's own
     // accumulators); all 16 waves stage the maps -- A_s and this tile's B_s --
-    // into LDS, FR maps per barrier.  The last segment's own map is staged as
-    // one more map and applied after M_in is published.
+    // into LDS, FR maps per barrier.  The own map is staged as one more map
+    // and applied after M_in is published.
     const bool owner = wave < 4;
-    const int nst = seg + (last ? 1 : 0);
-    const int ngrp = (nst + FR - 1) / FR;
     constexpr int SA = FR * APC / 1024, SB = FR * BPC / 1024;   // pieces per thread per group
     static_assert(FR * APC % 1024 == 0 && FR * BPC % 1024 == 0, "staging split");
-    f32x4 Mw[NDB];
+    auto fold = [&](const rsrc_t& rA_, const rsrc_t& rB_, int nfold, bool own, int base, int step,
+                    bool from_snap, F (&mOut)[KS_D]) {
+        const int nst = nfold + (own ? 1 : 0);
+        const int ngrp = (nst + FR - 1) / FR;
+        f32x4 Mw[NDB];
 #pragma unroll
-    for (int ib = 0; ib < NDB; ++ib) Mw[ib] = zero4();
-    if (owner && has_in) {
-        const float* sp = p.snap + (size_t)bh * DK * dv + col;
-#pragma unroll
-        for (int ib = 0; ib < NDB; ++ib)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) Mw[ib][i] = sp[(16 * ib + 4 * lg + i) * dv];
-    }
-    uint4 sa[SA], sb[SB];
-    auto sload = [&](int g) {
-#pragma unroll
-        for (int j = 0; j < SA; ++j) {
-            const int e = tid + 1024 * j, i = g * FR + e / APC;
-            sa[j] = buf_load16(rA, (g < ngrp && i < nst) ? (unsigned)((i * APC + e % APC) * 16) : kOffNone);
-        }
-#pragma unroll
-        for (int j = 0; j < SB; ++j) {
-            const int e = tid + 1024 * j, i = g * FR + e / BPC;
-            sb[j] = buf_load16(rB, (g < ngrp && i < nst)
-                                       ? (unsigned)(i * DK * dv * 4 + (vt * 4 * NDB * 64 + e % BPC) * 16) : kOffNone);
-        }
-    };
-    auto sstore = [&](int slot) {
-#pragma unroll
-        for (int j = 0; j < SA; ++j) As2[slot][tid + 1024 * j] = sa[j];
-#pragma unroll
-        for (int j = 0; j < SB; ++j) Bs2[slot][tid + 1024 * j] = sb[j];
-    };
-    // M <- A M + B on an owner: operand fragments of the old M first
-    auto oapply = [&](int slot, int r) {
-        F mB[KS_D];
-#pragma unroll
-        for (int ks = 0; ks < KS_D; ++ks) mB[ks] = Op::b_acc(Mw, ks);
-#pragma unroll
-        for (int ib = 0; ib < NDB; ++ib) {
-            f32x4 acc = __builtin_bit_cast(f32x4, Bs2[slot][r * BPC + (cg * NDB + ib) * 64 + lane]);
-#pragma unroll
-            for (int ks = 0; ks < KS_D; ++ks)
-                acc = Op::mma(__builtin_bit_cast(F, As2[slot][r * APC + (ib * KS_D + ks) * 64 + lane]), mB[ks], acc);
-            Mw[ib] = acc;
-        }
-    };
-    sload(0);
-    sstore(0);
-    sload(1);
-    __syncthreads();
-    for (int g = 0; g < ngrp; ++g) {
-        if (owner) {
-#pragma unroll
-            for (int r = 0; r < FR; ++r)
-                if (g * FR + r < seg) oapply(g & 1, r);
-        }
-        // copy (g + 1) & 1 was last read in group g - 1, before the previous barrier
-        if (g + 1 < ngrp) sstore((g + 1) & 1);
-        sload(g + 2);
-        __syncthreads();
-    }
-    if (owner) {
-#pragma unroll
-        for (int ks = 0; ks < KS_D; ++ks) Mf[0][ks][cg][lane] = __builtin_bit_cast(uint4, Op::b_acc(Mw, ks));
-        if (last) {
-            // the own map sits in the last group's copy, which no later group overwrote
-            oapply((ngrp - 1) & 1, seg % FR);
-            float* sp = p.state_out + (size_t)bh * DK * dv + col;
+        for (int ib = 0; ib < NDB; ++ib) Mw[ib] = zero4();
+        if (owner && from_snap) {
+            const float* sp = p.snap + (size_t)bh * DK * dv + col;
 #pragma unroll
             for (int ib = 0; ib < NDB; ++ib)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sp[(16 * ib + 4 * lg + i) * dv] = Mw[ib][i] * s_w;
+                for (int i = 0; i < 4; ++i) Mw[ib][i] = sp[(16 * ib + 4 * lg + i) * dv];
         }
-    }
-    __syncthreads();
+        uint4 sa[SA], sb[SB];
+        auto sload = [&](int g) {
 #pragma unroll
-    for (int ks = 0; ks < KS_D; ++ks) mI[ks] = __builtin_bit_cast(F, Mf[0][ks][cg][lane]);
-    } else {
-    // ---- fold: maps 0 .. seg-1, D in flight; the last segment's own map
-    // (state_out) is loaded from the start
-    const int nfold = seg;
-    uint4 ra[D][APT], ral[APT];
-    f32x4 rb[D][RB], rbl[RB];
-    auto issue = [&](uint4 (&a)[APT], f32x4 (&b)[RB], int i, bool ok) {
-#pragma unroll
-        for (int j = 0; j < APT; ++j)
-            a[j] = buf_load16(rA, (ok && tid + 1024 * j < APC) ? (unsigned)(i * APC * 16 + (tid + 1024 * j) * 16)
-                                                               : kOffNone);
-#pragma unroll
-        for (int r = 0; r < RB; ++r)
-            b[r] = __builtin_bit_cast(f32x4, buf_load16(rB,
-                        ok ? (unsigned)(i * DK * dv * 4 + ((c16 * NDB + rg * RB + r) * 64 + lane) * 16) : kOffNone));
-    };
-    // A_s into LDS copy buf (APC pieces over the first APC threads' slots)
-    auto put_a = [&](const uint4 (&a)[APT], int buf) {
-#pragma unroll
-        for (int j = 0; j < APT; ++j)
-            if (tid + 1024 * j < APC) Ast[buf][tid + 1024 * j] = a[j];
-    };
-    // this wave's rows of M as halves of fp16 B fragments (rows 32 ks + 16 h + ...)
-    auto put_m = [&](int buf) {
-#pragma unroll
-        for (int r = 0; r < RB; ++r) {
-            const int ib = rg * RB + r;
-            reinterpret_cast<uint2*>(&Mf[buf][ib / 2][cg][lane])[ib & 1] =
-                make_uint2(Op::pk2(Macc[r][0], Macc[r][1]), Op::pk2(Macc[r][2], Macc[r][3]));
-        }
-    };
-    auto get_m = [&](F (&mF)[KS_D], int buf) {
-#pragma unroll
-        for (int ks = 0; ks < KS_D; ++ks) mF[ks] = __builtin_bit_cast(F, Mf[buf][ks][cg][lane]);
-    };
-    // this wave's rows of A M + B
-    auto apply = [&](const F (&mF)[KS_D], int buf, const f32x4 (&b)[RB]) {
-        F fa[RB][KS_D];
-#pragma unroll
-        for (int r = 0; r < RB; ++r)
-#pragma unroll
-            for (int ks = 0; ks < KS_D; ++ks)
-                fa[r][ks] = __builtin_bit_cast(F, Ast[buf][((rg * RB + r) * KS_D + ks) * 64 + lane]);
-#pragma unroll
-        for (int r = 0; r < RB; ++r) {
-            f32x4 acc = b[r];
-#pragma unroll
-            for (int ks = 0; ks < KS_D; ++ks) acc = Op::mma(fa[r][ks], mF[ks], acc);
-            Macc[r] = acc;
-        }
-    };
-    issue(ral, rbl, seg, last);
-#pragma unroll
-    for (int d = 0; d < D; ++d) issue(ra[d], rb[d], d, d < nfold);
-    for (int i0 = 0; i0 < nfold; i0 += D) {
-#pragma unroll
-        for (int d = 0; d < D; ++d) {
-            const int i = i0 + d;
-            // copies i & 1 were last read two steps ago, before the previous barrier
-            put_a(ra[d], i & 1);
-            put_m(i & 1);
-            __syncthreads();
-            if (i < nfold) {
-                F mF[KS_D];
-                get_m(mF, i & 1);
-                apply(mF, i & 1, rb[d]);
+            for (int j = 0; j < SA; ++j) {
+                const int e = tid + 1024 * j, i = g * FR + e / APC;
+                sa[j] = buf_load16(rA_, (g < ngrp && i < nst) ? (unsigned)(((base + step * i) * APC + e % APC) * 16)
+                                                              : kOffNone);
             }
-            issue(ra[d], rb[d], i + D, i + D < nfold);
+#pragma unroll
+            for (int j = 0; j < SB; ++j) {
+                const int e = tid + 1024 * j, i = g * FR + e / BPC;
+                sb[j] = buf_load16(rB_, (g < ngrp && i < nst)
+                                            ? (unsigned)((base + step * i) * DK * dv * 4 + (vt * 4 * NDB * 64 + e % BPC) * 16)
+                                            : kOffNone);
+            }
+        };
+        auto sstore = [&](int slot) {
+#pragma unroll
+            for (int j = 0; j < SA; ++j) As2[slot][tid + 1024 * j] = sa[j];
+#pragma unroll
+            for (int j = 0; j < SB; ++j) Bs2[slot][tid + 1024 * j] = sb[j];
+        };
+        // M <- A M + B on an owner: operand fragments of the old M first
+        auto oapply = [&](int slot, int r) {
+            F mB[KS_D];
+#pragma unroll
+            for (int ks = 0; ks < KS_D; ++ks) mB[ks] = Op::b_acc(Mw, ks);
+#pragma unroll
+            for (int ib = 0; ib < NDB; ++ib) {
+                f32x4 acc = __builtin_bit_cast(f32x4, Bs2[slot][r * BPC + (cg * NDB + ib) * 64 + lane]);
+#pragma unroll
+                for (int ks = 0; ks < KS_D; ++ks)
+                    acc = Op::mma(__builtin_bit_cast(F, As2[slot][r * APC + (ib * KS_D + ks) * 64 + lane]), mB[ks], acc);
+                Mw[ib] = acc;
+            }
+        };
+        sload(0);
+        sstore(0);
+        sload(1);
+        __syncthreads();
+        for (int g = 0; g < ngrp; ++g) {
+            if (owner) {
+#pragma unroll
+                for (int r = 0; r < FR; ++r)
+                    if (g * FR + r < nfold) oapply(g & 1, r);
+            }
+            // copy (g + 1) & 1 was last read in group g - 1, before the previous barrier
+            if (g + 1 < ngrp) sstore((g + 1) & 1);
+            sload(g + 2);
+            __syncthreads();
         }
+        if (owner) {
+#pragma unroll
+            for (int ks = 0; ks < KS_D; ++ks) Mf[0][ks][cg][lane] = __builtin_bit_cast(uint4, Op::b_acc(Mw, ks));
+            if (own) {
+                // the own map sits in the last group's copy, which no later group overwrote
+                oapply((ngrp - 1) & 1, nfold % FR);
+                float* sp = p.state_out + (size_t)bh * DK * dv + col;
+#pragma unroll
+                for (int ib = 0; ib < NDB; ++ib)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) sp[(16 * ib + 4 * lg + i) * dv] = Mw[ib][i] * s_w;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int ks = 0; ks < KS_D; ++ks) mOut[ks] = __builtin_bit_cast(F, Mf[0][ks][cg][lane]);
+    };
+    fold(rA, rB, seg, last, 0, 1, has_in, mI);
+    if constexpr (BI) {
+        __syncthreads();                  // every wave has read Mf and the staged maps
+        fold(rAb, rBb, nseg - 1 - seg, false, nseg - 1, -1, false, mIb);
     }
-    // M_in of this segment as B fragments for every wave; the last segment's
-    // own map alongside
-    put_m(nfold & 1);
-    if (last) put_a(ral, nfold & 1);
-    __syncthreads();
-    get_m(mI, nfold & 1);
-    if (last) {
-        apply(mI, nfold & 1, rbl);
-        float* sp = p.state_out + (size_t)bh * DK * dv + col;
+    } else {
+    // ---- fold: D maps in flight; the own map (state_out) is loaded from the start
+    auto fold = [&](const rsrc_t& rA_, const rsrc_t& rB_, int nfold, bool own, int base, int step,
+                    bool from_snap, F (&mOut)[KS_D]) {
+        // rows 16 (rg RB + r) + 4 lg + i of M, column col
+        f32x4 Macc[RB];
 #pragma unroll
-        for (int r = 0; r < RB; ++r)
+        for (int r = 0; r < RB; ++r) Macc[r] = zero4();
+        if (from_snap) {
+            const float* sp = p.snap + (size_t)bh * DK * dv + col;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sp[(16 * (rg * RB + r) + 4 * lg + i) * dv] = Macc[r][i] * s_w;
+            for (int r = 0; r < RB; ++r)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) Macc[r][i] = sp[(16 * (rg * RB + r) + 4 * lg + i) * dv];
+        }
+        uint4 ra[D][APT], ral[APT];
+        f32x4 rb[D][RB], rbl[RB];
+        // map index m (valid when ok)
+        auto issue = [&](uint4 (&a)[APT], f32x4 (&b)[RB], int m, bool ok) {
+#pragma unroll
+            for (int j = 0; j < APT; ++j)
+                a[j] = buf_load16(rA_, (ok && tid + 1024 * j < APC) ? (unsigned)(m * APC * 16 + (tid + 1024 * j) * 16)
+                                                                    : kOffNone);
+#pragma unroll
+            for (int r = 0; r < RB; ++r)
+                b[r] = __builtin_bit_cast(f32x4, buf_load16(rB_,
+                            ok ? (unsigned)(m * DK * dv * 4 + ((c16 * NDB + rg * RB + r) * 64 + lane) * 16) : kOffNone));
+        };
+        // A_s into LDS copy buf (APC pieces over the first APC threads' slots)
+        auto put_a = [&](const uint4 (&a)[APT], int buf) {
+#pragma unroll
+            for (int j = 0; j < APT; ++j)
+                if (tid + 1024 * j < APC) Ast[buf][tid + 1024 * j] = a[j];
+        };
+        // this wave's rows of M as halves of fp16 B fragments (rows 32 ks + 16 h + ...)
+        auto put_m = [&](int buf) {
+#pragma unroll
+            for (int r = 0; r < RB; ++r) {
+                const int ib = rg * RB + r;
+                reinterpret_cast<uint2*>(&Mf[buf][ib / 2][cg][lane])[ib & 1] =
+                    make_uint2(Op::pk2(Macc[r][0], Macc[r][1]), Op::pk2(Macc[r][2], Macc[r][3]));
+            }
+        };
+        auto get_m = [&](F (&mF)[KS_D], int buf) {
+#pragma unroll
+            for (int ks = 0; ks < KS_D; ++ks) mF[ks] = __builtin_bit_cast(F, Mf[buf][ks][cg][lane]);
+        };
+        // this wave's rows of A M + B
+        auto apply = [&](const F (&mF)[KS_D], int buf, const f32x4 (&b)[RB]) {
+            F fa[RB][KS_D];
+#pragma unroll
+            for (int r = 0; r < RB; ++r)
+#pragma unroll
+                for (int ks = 0; ks < KS_D; ++ks)
+                    fa[r][ks] = __builtin_bit_cast(F, Ast[buf][((rg * RB + r) * KS_D + ks) * 64 + lane]);
+#pragma unroll
+            for (int r = 0; r < RB; ++r) {
+                f32x4 acc = b[r];
+#pragma unroll
+                for (int ks = 0; ks < KS_D; ++ks) acc = Op::mma(fa[r][ks], mF[ks], acc);
+                Macc[r] = acc;
+            }
+        };
+        issue(ral, rbl, base + step * nfold, own);
+#pragma unroll
+        for (int d = 0; d < D; ++d) issue(ra[d], rb[d], base + step * d, d < nfold);
+        for (int i0 = 0; i0 < nfold; i0 += D) {
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                const int i = i0 + d;
+                // copies i & 1 were last read two steps ago, before the previous barrier
+                put_a(ra[d], i & 1);
+                put_m(i & 1);
+                __syncthreads();
+                if (i < nfold) {
+                    F mF[KS_D];
+                    get_m(mF, i & 1);
+                    apply(mF, i & 1, rb[d]);
+                }
+                issue(ra[d], rb[d], base + step * (i + D), i + D < nfold);
+            }
+        }
+        // M_in of this segment as B fragments for every wave; the own map alongside
+        put_m(nfold & 1);
+        if (own) put_a(ral, nfold & 1);
+        __syncthreads();
+        get_m(mOut, nfold & 1);
+        if (own) {
+            apply(mOut, nfold & 1, rbl);
+            float* sp = p.state_out + (size_t)bh * DK * dv + col;
+#pragma unroll
+            for (int r = 0; r < RB; ++r)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sp[(16 * (rg * RB + r) + 4 * lg + i) * dv] = Macc[r][i] * s_w;
+        }
+    };
+    fold(rA, rB, seg, last, 0, 1, has_in, mI);
+    if constexpr (BI) {
+        __syncthreads();                  // every wave has read Mf and the staged map
+        fold(rAb, rBb, nseg - 1 - seg, false, nseg - 1, -1, false, mIb);
     }
     }
 
     // ---- outputs of the segment: O += Phi M_in, formed transposed
     // (O^T = M^T Phi^T): lane (lg, lc) holds row lc of the wave's row block
     // and four consecutive columns, one 16-byte access
-    auto cfix = [&](const uint4& h, const uint2& o, const uint2& gt, const uint4& av, int g, int buf) {
+    auto cfix = [&](const uint4& h, const uint2& o, const uint2& gt, const uint4& av, const uint4& hb,
+                    const uint2& ob, int g, int buf) {
         const int c = ch0 + g * CPG + rg / NB, rb = rg % NB;
-        if (tid < PPG) Phs[buf][tid] = h;
+        if (tid < PPG) {
+            Phs[buf][tid] = h;
+            if constexpr (BI) Phb[buf * PPG + tid] = hb;
+        }
         __syncthreads();                  // copy buf reused two groups later, after another barrier
         typedef _Float16 h4 __attribute__((ext_vector_type(4)));
         const h4 ot = __builtin_bit_cast(h4, o);
@@ -1293,6 +1379,15 @@ __global__ __launch_bounds__(1024) void gdn_pipe_fix_kernel(WalkArgs p) {
             acc = Op::mma(mI[ks], __builtin_bit_cast(F, Phs[buf][(rg * KS_D + ks) * 64 + lane]), acc);
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[i] *= s_w;
+        if constexpr (BI) {
+            const h4 otb = __builtin_bit_cast(h4, ob);
+            f32x4 accb = {(float)otb[0], (float)otb[1], (float)otb[2], (float)otb[3]};
+#pragma unroll
+            for (int ks = 0; ks < KS_D; ++ks)
+                accb = Op::mma(mIb[ks], __builtin_bit_cast(F, Phb[buf * PPG + (rg * KS_D + ks) * 64 + lane]), accb);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] += accb[i] * s_b;
+        }
         // rows past T fall outside the buffer and are dropped
         const unsigned e0 = (unsigned)(tm(c * C + 16 * rb + lc) * dv + col4);
         if (gated) {
@@ -1301,7 +1396,7 @@ __global__ __launch_bounds__(1024) void gdn_pipe_fix_kernel(WalkArgs p) {
             acc[2] *= __builtin_bit_cast(float, gt.y << 16);
             acc[3] *= __builtin_bit_cast(float, gt.y & 0xffff0000u);
         }
-        add_f32x4(acc, av);                // accumulating: one rounding of the sum
+        if constexpr (!BI) add_f32x4(acc, av);   // accumulating: one rounding of the sum
         if (p.out_bf16) {
             const uint2 w = make_uint2(
                 (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[0]) |
@@ -1315,10 +1410,10 @@ __global__ __launch_bounds__(1024) void gdn_pipe_fix_kernel(WalkArgs p) {
     };
     const int ngroups = (ch1 - ch0 + CPG - 1) / CPG;
     for (int g = 0; g < ngroups; g += 2) {
-        cfix(ph[0], ov[0], gv2[0], av2[0], g, 0);
-        cload(ph[0], ov[0], gv2[0], av2[0], g + 2);
-        cfix(ph[1], ov[1], gv2[1], av2[1], g + 1, 1);
-        cload(ph[1], ov[1], gv2[1], av2[1], g + 3);
+        cfix(ph[0], ov[0], gv2[0], av2[0], phb[0], ovb[0], g, 0);
+        cload(ph[0], ov[0], gv2[0], av2[0], phb[0], ovb[0], g + 2);
+        cfix(ph[1], ov[1], gv2[1], av2[1], phb[1], ovb[1], g + 1, 1);
+        cload(ph[1], ov[1], gv2[1], av2[1], phb[1], ovb[1], g + 3);
     }
 }
 
@@ -1339,10 +1434,16 @@ hipError_t launch_pipe_g(const WalkArgs& a, hipStream_t s) {
     const int bh = a.B * a.H;
     if (a.nseg > 1) {
         const int grid = bh * a.nseg * ((DK + a.dv) / (64 * CTS));
-        hipLaunchKernelGGL((gdn_pipe_kernel<DK, C, SCT, true, SNCW, 4, EXT>), dim3(grid), dim3(64 * (SNCW + 4)), 0, s, a);
+        // a fused bidirectional call walks both directions in one launch
+        const int walks = EXT && a.bidir ? 2 : 1;
+        hipLaunchKernelGGL((gdn_pipe_kernel<DK, C, SCT, true, SNCW, 4, EXT>), dim3(grid * walks), dim3(64 * (SNCW + 4)),
+                           0, s, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((gdn_pipe_fix_kernel<DK, C>), dim3(bh * a.nseg * (a.dv / 64)), dim3(1024), 0, s, a);
+        if (walks == 2)
+            hipLaunchKernelGGL((gdn_pipe_fix_kernel<DK, C, true>), dim3(bh * a.nseg * (a.dv / 64)), dim3(1024), 0, s, a);
+        else
+            hipLaunchKernelGGL((gdn_pipe_fix_kernel<DK, C, false>), dim3(bh * a.nseg * (a.dv / 64)), dim3(1024), 0, s, a);
         return hipGetLastError();
     }
     hipLaunchKernelGGL((gdn_pipe_kernel<DK, C, 1, false, 4, UNPW, EXT>), dim3(bh * (a.dv / 64)), dim3(64 * (4 + UNPW)), 0, s, a);
@@ -1351,7 +1452,8 @@ hipError_t launch_pipe_g(const WalkArgs& a, hipStream_t s) {
 
 template <int DK, int C, int CTS>
 hipError_t launch_pipe_t(const WalkArgs& a, hipStream_t s) {
-    if (a.gate_logits || a.out_gate || a.reverse || a.accumulate) return launch_pipe_g<DK, C, CTS, true>(a, s);
+    if (a.gate_logits || a.out_gate || a.reverse || a.accumulate || a.bidir)
+        return launch_pipe_g<DK, C, CTS, true>(a, s);
     return launch_pipe_g<DK, C, CTS, false>(a, s);
 }
 

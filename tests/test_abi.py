@@ -131,11 +131,30 @@ def test_bidir_needs_its_workspace_before_any_launch(lib):
     assert lib.gdn_fwd_bidir(None, *args[1:], None) == gdn.GDN_ERR_ARG
 
 
+def _pipe_segment_data(bh, T, dk, dv, chunk, nseg):
+    # maps, copy of state_in, Phi, partial outputs, working scales
+    rows = -(-(-(-T // chunk)) // nseg) * chunk
+    return (bh * nseg * dk * dk * 2 + bh * nseg * dk * dv * 4 + bh * dk * dv * 4
+            + bh * nseg * rows * dk * 2 + bh * nseg * rows * dv * 2 + bh * (dv // 16) * 4)
+
+
 def test_bidir_workspace_query(lib):
-    # the fp32 plane (B*H*T*dv*4 rounded to 256) plus the split-sequence data
+    # few heads: the fused call, one set of segment data (256-byte aligned)
+    # per direction for the segment count planned for both directions' walks
+    got = lib.gdn_bidir_workspace_bytes(1, 16, 2640, 64, 64, 0, None)
+    fused = {2 * ((_pipe_segment_data(16, 2640, 64, 64, 64, n) + 255) // 256 * 256)
+             for n in range(2, 22) if -(-42 // -(-42 // n)) == n}
+    assert got in fused
     plane = (1 * 16 * 2640 * 64 * 4 + 255) // 256 * 256
-    assert lib.gdn_bidir_workspace_bytes(1, 16, 2640, 64, 64, 0, None) == \
-        plane + lib.gdn_workspace_bytes(1, 16, 2640, 64, 64, 0, None)
+    assert got > plane
+    # fp32 inputs (fp32 walker): the fp32 plane (B*H*T*dv*4 rounded to 256)
+    # plus the split-sequence data
+    f32 = gdn.GdnOpts()
+    lib.gdn_default_opts(ctypes.byref(f32))
+    f32.in_dtype = gdn.GDN_F32
+    assert lib.gdn_bidir_workspace_bytes(1, 16, 2640, 64, 64, 64, ctypes.byref(f32)) == \
+        plane + lib.gdn_workspace_bytes(1, 16, 2640, 64, 64, 64, ctypes.byref(f32))
+    # many heads: unsegmented, the plane alone
     many = (4 * 32 * 16384 * 128 * 4 + 255) // 256 * 256
     assert lib.gdn_bidir_workspace_bytes(4, 32, 16384, 128, 128, 64, None) == many
     assert lib.gdn_bidir_workspace_bytes(1, 16, 0, 64, 64, 0, None) == 0

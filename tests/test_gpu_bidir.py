@@ -3,8 +3,10 @@
 streaming chunk, section 2.3: the two histories combined for the output)
 against the fp64 oracle (oracle.gdn_bidir) on the same bits: every launch
 path (segment walk plus correction, unsegmented walk, fp32 walker, 128-token
-single pass), the state carried across calls, ragged lengths whose padding
-sits at the start of the backward walk, gates, bf16 outputs."""
+single pass), the fused call of few heads (both directions walked by one
+launch, one correction pass writing the sum) and the two-scan call with its
+fp32 plane, the state carried across calls, ragged lengths whose padding sits
+at the start of the backward walk, gates, bf16 outputs."""
 import numpy as np
 import pytest
 import torch
@@ -103,6 +105,46 @@ def test_bidir_needs_its_workspace(gdn_lib, out_dtype):
 def test_bidir_ragged(gdn_lib, oracle_mod, T):
     # a partial last chunk is the first chunk of the backward walk
     _run(gdn_lib, oracle_mod, WORKLOADS["stream_chunk_h16_d64"], 1, H=3, T=T, what=f"T{T}")
+
+
+def _plane(B, H, T, dv):
+    return (B * H * T * dv * 4 + 255) // 256 * 256
+
+
+def _fused(gdn, B, H, T, dk, dv, chunk=0):
+    # the workspace query names the fused call's own data, not the plane
+    lib = gdn.load()
+    return lib.gdn_bidir_workspace_bytes(B, H, T, dk, dv, chunk, None) != \
+        _plane(B, H, T, dv) + lib.gdn_workspace_bytes(B, H, T, dk, dv, chunk, None)
+
+
+@pytest.mark.parametrize("T,out_dtype", [(777, torch.float32), (1281, torch.float32), (2639, torch.float32),
+                                         (2639, torch.bfloat16)])
+def test_bidir_fused_ragged(gdn_lib, oracle_mod, T, out_dtype):
+    # few heads: both directions walked by one launch and corrected by one
+    # pass; partial last chunks (the backward walk's padding comes first) and
+    # segments of unequal length
+    assert _fused(gdn_lib, 1, 3, T, 64, 64)
+    _run(gdn_lib, oracle_mod, WORKLOADS["stream_chunk_h16_d64"], 1, H=3, T=T, out_dtype=out_dtype,
+         what=f"fused-T{T}")
+
+
+def test_bidir_fused_d128_gates_ragged(gdn_lib, oracle_mod):
+    assert _fused(gdn_lib, 1, 2, 1999, 128, 128)
+    _run(gdn_lib, oracle_mod, WORKLOADS["rollout_h16_d128"], 2, H=2, T=1999, gates=True, what="fused-d128-gates")
+
+
+def test_bidir_two_scan_path(gdn_lib, oracle_mod):
+    # a workspace below the fused call's that holds the plane and one set of
+    # segment data: the two scans in stream order, the plane between them
+    wl = WORKLOADS["stream_chunk_h16_d64"]
+    lib = gdn_lib.load()
+    assert _fused(gdn_lib, 1, 16, 2640, 64, 64)
+    n = _plane(1, 16, 2640, 64) + lib.gdn_workspace_bytes(1, 16, 2640, 64, 64, 0, None)
+    assert n < lib.gdn_bidir_workspace_bytes(1, 16, 2640, 64, 64, 0, None)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    _run(gdn_lib, oracle_mod, wl, 1, workspace=ws, what="two-scan")
+    _run(gdn_lib, oracle_mod, wl, 1, workspace=ws, gates=True, out_dtype=torch.bfloat16, what="two-scan-gates-bf16")
 
 
 @pytest.mark.parametrize("chunk", [32, 128])
