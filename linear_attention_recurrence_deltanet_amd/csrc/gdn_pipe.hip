@@ -5,7 +5,7 @@
 // streaming chunks, section 2.1 and appendix G.6).  With M = S^T [dk][dv],
 // g_r = sum_{s<=r} log alpha_s, gam = exp(g), G_rs = exp(g_r - g_s) (r >= s):
 //     A  = diag(beta) strict_tril(K^ K^T .* G),  T = (I + A)^-1 diag(beta)
-//     U  = T V - T diag(gam) (K^ M0)
+//     U  = T (V - diag(gam) (K^ M0))   (= T V + (-T diag(gam)) (K^ M0))
 //     O  = diag(gam) (Q^ M0) + tril(Q^ K^T .* G) U
 //     M  = gam_C M0 + K^T diag(exp(g_C - g)) U
 //
@@ -26,10 +26,13 @@
 // the matrix cores, the vector ALUs and LDS are kept busy by different waves.
 //
 // One step (chunk c done, chunk c+1 prepared), phases separated by barriers:
-//   1  state: U = T V + (-T diag gam)(K^ M), O, M update  | key: normalise c+1
+//   1  state: U = T Y, O, M update                        | key: normalise c+1
 //   2  state: K^ M, Q^ M of c+1                           | key: K^ K^T of c+1
-//   3  state: V tiles of c+1 as operands, K^T blocks      | key: diagonal
+//   3  state: Y = V - diag(gam) K^ M of c+1, K^T blocks   | key: diagonal
 //                                                           blocks of T
+// (the segment walk at d_k = 128 keeps V and K^ M apart and forms
+// U = T V + (-T diag gam)(K^ M) with a second triangular operand: there the
+// extra phase-3 work of Y measured slower than the saved products)
 //   4  state: P = tril(Q^ K^T .* G) of c+1               | key: off-diagonal
 //                                                           block columns of T
 // Operand precision as in the segmented walker: fp16 operands (11-bit
@@ -70,8 +73,11 @@ struct PPlan {
     static constexpr int O_KH = O_QH + pal16(C * LDD * 2);          // k^   [C][LDD]
     static constexpr int O_KT = O_KH + pal16(C * LDD * 2);          // k^T  [DK][LDC]
     static constexpr int O_PM = O_KT + pal16(DK * LDC * 2);         // P    [C][LDC]
-    static constexpr int O_T2 = O_PM + pal16(C * LDC * 2);          // -T diag(gam)
-    static constexpr int O_TM = O_T2 + pal16(C * LDC * 2);          // T    [C][LDC]
+    // one product U = T Y (YF), or T V + (-T diag(gam)) (K^ M) with the
+    // second triangular operand stored too
+    static constexpr bool YF = !(SEG && DK == 128);
+    static constexpr int O_T2 = O_PM + pal16(C * LDC * 2);          // -T diag(gam) (not YF)
+    static constexpr int O_TM = O_T2 + (YF ? 0 : pal16(C * LDC * 2));  // T    [C][LDC]
     static constexpr int O_TT = O_TM + pal16(C * LDC * 2);          // T^T  [C][LDC]
     static constexpr int O_AOFF = O_TT + pal16(C * LDC * 2);        // A off-diagonal
     static constexpr int O_AD = O_AOFF + pal16(C * LDC * 2);        // A diag^T fp32
@@ -278,6 +284,7 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
     E* Pm = reinterpret_cast<E*>(smem + L::O_PM);
     E* T2n = reinterpret_cast<E*>(smem + L::O_T2);
     E* Tm = reinterpret_cast<E*>(smem + L::O_TM);
+    constexpr bool YF = L::YF;
     E* Tt = reinterpret_cast<E*>(smem + L::O_TT);
     E* Aoff = reinterpret_cast<E*>(smem + L::O_AOFF);
     float* Adt = reinterpret_cast<float*>(smem + L::O_AD);
@@ -391,8 +398,12 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
     // (Q^ M)^T = M^T Q^^T of the next chunk: lane (lg, lc) holds row 16 rb + lc,
     // columns col0 + 4 lg + i
     f32x4 QM[CT][NB];
-    F KMf[CT][KS_C];                                  // K^ M of the next chunk as B operand (fp16)
-    F vB[CT][KS_C];                                   // V of the next chunk as B operand
+    // Y = V - diag(gam) K^ M of the next chunk as B operand (fp16): one
+    // product U = T Y instead of T V + (-T diag(gam)) (K^ M).  Phase 2 leaves
+    // K^ M here (fp16), phase 3 replaces it by Y, formed in fp32 (YF), or
+    // puts V beside it
+    F yB[CT][KS_C];
+    F vB[YF ? 1 : CT][KS_C];
     // Working scale of each column tile: the walk runs on M / wsc and v / wsc
     // (a power of two, so exact) and multiplies outputs and state by wsc
     // again; the fp16 operands formed from M, v and U then stay near
@@ -573,7 +584,6 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct) {
                     const bool idt = ident(ct);
-                    const F* kmB = KMf[ct];
                     f32x4 U[NB];
 #pragma unroll
                     for (int rb = 0; rb < NB; ++rb) {
@@ -581,8 +591,12 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
                         // T and P are lower triangular: k-steps past row block rb are zero
 #pragma unroll
                         for (int ks = 0; ks <= rb / 2; ++ks) {
-                            if (!idt) acc = Op::mma(a_lower<L::LDC>(Tm, rb, ks, lane), vB[ct][ks], acc);
-                            acc = Op::mma(a_lower<L::LDC>(T2n, rb, ks, lane), kmB[ks], acc);
+                            if constexpr (YF) {
+                                acc = Op::mma(a_lower<L::LDC>(Tm, rb, ks, lane), yB[ct][ks], acc);
+                            } else {
+                                if (!idt) acc = Op::mma(a_lower<L::LDC>(Tm, rb, ks, lane), vB[ct][ks], acc);
+                                acc = Op::mma(a_lower<L::LDC>(T2n, rb, ks, lane), yB[ct][ks], acc);
+                            }
                         }
                         U[rb] = acc;
                     }
@@ -695,12 +709,12 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
                     f32x4 km = zero4();
 #pragma unroll
                     for (int ks = 0; ks < KS_D; ++ks) km = Op::mma(fk[ks], mB[ct][ks], km);
-                    // kept as the B operand of phase 1 (row blocks 2j, 2j+1 -> k-step j)
+                    // fp16, in the B operand order of phase 1 (row blocks 2j, 2j+1 -> k-step j)
                     if (rb % 2 == 0)
                         KMlo[ct] = km;
                     else
-                        KMf[ct][rb / 2] = Op::pack8(KMlo[ct][0], KMlo[ct][1], KMlo[ct][2], KMlo[ct][3],
-                                                    km[0], km[1], km[2], km[3]);
+                        yB[ct][rb / 2] = Op::pack8(KMlo[ct][0], KMlo[ct][1], KMlo[ct][2], KMlo[ct][3],
+                                                   km[0], km[1], km[2], km[3]);
                     f32x4 qm = zero4();
 #pragma unroll
                     for (int ks = 0; ks < KS_D; ++ks) qm = Op::mma(mB[ct][ks], fq[ks], qm);
@@ -715,25 +729,54 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
                 }
             }
             __syncthreads();
-            // ---- phase 3: V tiles of chunk pc as B operands
+            // ---- phase 3: Y = V - diag(gam) K^ M of chunk pc (V tiles transposed on
+            // the matrix cores; identity columns have no V): lane (lg, lc) holds
+            // rows 16 rb + 4 lg + i of column lc in each
+            if constexpr (!YF) {
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct) {
-                if (!ident(ct)) {
-                    f32x4 Vacc[NB];
+                for (int ct = 0; ct < CT; ++ct) {
+                    if (!ident(ct)) {
+                        f32x4 Vacc[NB];
 #pragma unroll
-                    for (int rb = 0; rb < NB; ++rb)
-                        Vacc[rb] = transpose16_bf16(Vr + (16 * rb) * L::LDV + col0(ct), L::LDV, lane, wunit[ct]);
+                        for (int rb = 0; rb < NB; ++rb)
+                            Vacc[rb] = transpose16_bf16(Vr + (16 * rb) * L::LDV + col0(ct), L::LDV, lane, wunit[ct]);
 #pragma unroll
-                    for (int ks = 0; ks < KS_C; ++ks) vB[ct][ks] = Op::b_acc(Vacc, ks);
+                        for (int ks = 0; ks < KS_C; ++ks) vB[ct][ks] = Op::b_acc(Vacc, ks);
+                    }
+                }
+            } else {
+                const float* v_gam_c = vecs + vb * 4 * C + C;
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+                    f32x4 Y[NB];
+#pragma unroll
+                    for (int rb = 0; rb < NB; ++rb) {
+                        const f32x4 vt = ident(ct) ? zero4()
+                                                   : transpose16_bf16(Vr + (16 * rb) * L::LDV + col0(ct), L::LDV,
+                                                                      lane, wunit[ct]);
+                        const f32x4 gr = *reinterpret_cast<const f32x4*>(v_gam_c + 16 * rb + 4 * lg);
+                        const f16x8 km = __builtin_bit_cast(f16x8, yB[ct][rb / 2]);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) Y[rb][i] = vt[i] - gr[i] * (float)km[4 * (rb & 1) + i];
+                    }
+#pragma unroll
+                    for (int ks = 0; ks < KS_C; ++ks) yB[ct][ks] = Op::b_acc(Y, ks);
                 }
             }
+            // The LDS addresses of the K^T blocks and of P derive from the lane
+            // index read afresh here (volatile, so not hoisted): formed every
+            // step instead of kept across the loop, where at d_k = 128 they
+            // would be spilled, and every reload of a spill waits for all
+            // outstanding memory operations, the output stores included.
+            int lq;
+            asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lq));
             // K^T blocks: Kt[16 ib + c][16 sb + 4 lg + i] = k^[16 sb + 4 lg + i][16 ib + c]
 #pragma unroll
             for (int u = 0; u < NTW / NCW; ++u) {
                 const int t = wave + NCW * u;
                 const int ib = t / NB, sb = t % NB;
-                const f32x4 x = transpose16<Op>(Kh + (16 * sb) * L::LDD + 16 * ib, L::LDD, lane);
-                st4h(Kt + (16 * ib + lc) * L::LDC + 16 * sb + 4 * lg, x[0], x[1], x[2], x[3]);
+                const f32x4 x = transpose16<Op>(Kh + (16 * sb) * L::LDD + 16 * ib, L::LDD, lq);
+                st4h(Kt + (16 * ib + (lq & 15)) * L::LDC + 16 * sb + 4 * (lq >> 4), x[0], x[1], x[2], x[3]);
             }
             __syncthreads();
             // ---- phase 4: P = tril(Q^ K^T .* G) of chunk pc, needed from the
@@ -743,7 +786,7 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
                 const float* v_g2 = vecs + vb * 4 * C;
 #pragma unroll
                 for (int u = 0; u < (NTS + NCW - 1) / NCW; ++u)
-                    if (wave + NCW * u < NTS) p_tile<L>(Kh, Qh, Pm, v_g2, wave + NCW * u, lane);
+                    if (wave + NCW * u < NTS) p_tile<L>(Kh, Qh, Pm, v_g2, wave + NCW * u, lq);
             }
             if constexpr (EXT && !SEG) {
                 // output gate and values to accumulate onto of chunk pc, used
@@ -856,7 +899,7 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
                     const int r = 16 * b + 4 * q + i;
                     const float t = x[i] * bc;
                     Tm[r * L::LDC + c] = (E)t;
-                    T2n[r * L::LDC + c] = (E)(-t * gc);
+                    if constexpr (!YF) T2n[r * L::LDC + c] = (E)(-t * gc);
                     Xd[r * L::LDX + j] = (E)x[i];
                 }
                 st4h(Tt + c * L::LDC + 16 * b + 4 * q, x[0] * bc, x[1] * bc, x[2] * bc, x[3] * bc);
@@ -904,7 +947,7 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
                         for (int ii = 0; ii < 4; ++ii) {
                             const int r = 16 * i + 4 * lg + ii;
                             Tm[r * L::LDC + c] = (E)tn[ii];
-                            T2n[r * L::LDC + c] = (E)(t[ii] * gc);
+                            if constexpr (!YF) T2n[r * L::LDC + c] = (E)(t[ii] * gc);
                         }
                         st4h(Tt + c * L::LDC + 16 * i + 4 * lg, tn[0], tn[1], tn[2], tn[3]);
                     }
@@ -939,7 +982,7 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
                                 Tc[i][ii] = -t[ii];
                                 const int r = 16 * i + 4 * lg + ii;
                                 Tm[r * L::LDC + c] = (E)(-t[ii]);
-                                T2n[r * L::LDC + c] = (E)(t[ii] * gc);
+                                if constexpr (!YF) T2n[r * L::LDC + c] = (E)(t[ii] * gc);
                             }
                             st4h(Tt + c * L::LDC + 16 * i + 4 * lg, -t[0], -t[1], -t[2], -t[3]);
                         }
