@@ -343,20 +343,34 @@ __global__ __launch_bounds__(64 * (DV / 16)) void frame_scan_kernel(FrameArgs p)
             *reinterpret_cast<uint2*>(&Gl[row * GST + 4 * c4]) = make_uint2(l0, l1);
         }
         __syncthreads();
-        if (f + 1 < p.F) load_g(f + 1);     // in flight during this frame's products
         const rsrc_t rs = sums_rsrc(f);
         const float a = exp2f(gate_log2_alpha(ld_bf16(p.alpha, (size_t)bh * p.F + f), p.gate_logits != 0));
-        float wv[NRB][4];
+        // w_f and W_f of every split, issued first (in the order they are
+        // used: the wait for w_f leaves W_f in flight) and summed where they
+        // are needed, so that their memory latency overlaps the denominator
+        // update; the next frame's G is loaded after them
+        uint32_t wzr[ZIT][MS];
 #pragma unroll
-        for (int rb = 0; rb < NRB; ++rb)
+        for (int zi = 0; zi < ZIT; ++zi) {
+            const int row = (tid + NTH * zi) >> 2;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int o = (16 * rb + 4 * lg + i) * NS + DK + 16 * ct + lc;
-                float x = 0.f;
+            for (int s = 0; s < MS; ++s)
+                wzr[zi][s] = buf_load4(rs, (tid + NTH * zi < 4 * DK) ? (unsigned)(((s * DK + row) * NS + DK + DV) * 4)
+                                                                     : kOffNone);
+        }
+        // one lane offset per split (the split in it, so that an absent split
+        // falls past the range and reads zero); the row, uniform, as the
+        // scalar offset
+        uint32_t wr[MS][NRB][4];
 #pragma unroll
-                for (int s = 0; s < MS; ++s) x += __uint_as_float(buf_load4(rs, (unsigned)((s * DK * NS + o) * 4)));
-                wv[rb][i] = x;
-            }
+        for (int s = 0; s < MS; ++s) {
+            const unsigned wlane = (unsigned)(((s * DK + 4 * lg) * NS + DK + 16 * ct + lc) * 4);
+#pragma unroll
+            for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    wr[s][rb][i] = __builtin_amdgcn_raw_buffer_load_b32(rs, wlane, (unsigned)((16 * rb + i) * NS * 4), 0);
+        }
         // denominator: z <- alpha (z - G z) + w, four threads per row
 #pragma unroll
         for (int zi = 0; zi < ZIT; ++zi) {
@@ -375,14 +389,25 @@ __global__ __launch_bounds__(64 * (DV / 16)) void frame_scan_kernel(FrameArgs p)
             y += __shfl_xor(y, 2, 64);
             float wz = 0.f;
 #pragma unroll
-            for (int s = 0; s < MS; ++s)
-                wz += __uint_as_float(buf_load4(rs, (unsigned)(((s * DK + row) * NS + DK + DV) * 4)));
+            for (int s = 0; s < MS; ++s) wz += __uint_as_float(wzr[zi][s]);
             if (part == 0) {
                 const float zn = a * (zs[zb][row] - y) + wz;
                 zs[zb ^ 1][row] = zn;
                 p.zf[((size_t)bh * p.F + f) * DK + row] = zn;
             }
         }
+        // W_f, summed over the splits once the denominator update has covered
+        // its latency
+        float wv[NRB][4];
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float w = 0.f;
+#pragma unroll
+                for (int s = 0; s < MS; ++s) w += __uint_as_float(wr[s][rb][i]);
+                wv[rb][i] = w;
+            }
         // B operand: the state, hi + lo, k in accumulator order
         u16x8 bhi[NKS], blo[NKS];
 #pragma unroll
@@ -415,6 +440,7 @@ __global__ __launch_bounds__(64 * (DV / 16)) void frame_scan_kernel(FrameArgs p)
 #pragma unroll
             for (int i = 0; i < 4; ++i) M[rb][i] = a * (M[rb][i] - y[i]) + wv[rb][i];
         }
+        if (f + 1 < p.F) load_g(f + 1);     // staged at the start of the next frame
         // the frame's state for the readout: M^T as bf16 hi + lo
         const size_t base = (((size_t)bh * p.F + f) * DV + 16 * ct + lc) * DK;
 #pragma unroll
