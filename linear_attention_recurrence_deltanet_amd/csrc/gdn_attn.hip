@@ -46,6 +46,9 @@ namespace {
 constexpr int AQ = 128;   // queries per workgroup (4 waves x 32)
 constexpr int AK = 64;    // keys per tile
 constexpr float kLazy = 8.f;   // headroom of the softmax reference max (log2 units)
+// outputs (and the parts of a split call) written through as produced (sc0
+// sc1): measured 0.7-1.4% faster per call than the default policy
+constexpr int kOutPolicy = 1 | 16;
 
 template <int D>
 struct APlan {
@@ -315,9 +318,9 @@ __global__ __launch_bounds__(256, 2) void gdn_attn_kernel(AttnArgs p) {
             const int row = q0 + 16 * qb + lc;
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
-                buf_store16(rpo, (unsigned)(row * D + 16 * db + 4 * lg) * 4u, __builtin_bit_cast(uint4, O[db][qb]));
+                buf_store16<kOutPolicy>(rpo, (unsigned)(row * D + 16 * db + 4 * lg) * 4u, __builtin_bit_cast(uint4, O[db][qb]));
             if (lg == 0)
-                buf_store8(rpm, (unsigned)row * 8u, make_uint2(__builtin_bit_cast(uint32_t, m[qb]),
+                buf_store8<kOutPolicy>(rpm, (unsigned)row * 8u, make_uint2(__builtin_bit_cast(uint32_t, m[qb]),
                                                                __builtin_bit_cast(uint32_t, ls)));
         }
         return;
@@ -334,9 +337,9 @@ __global__ __launch_bounds__(256, 2) void gdn_attn_kernel(AttnArgs p) {
             if (p.out_bf16) {
                 const u16x8 w = pack8_bf16(o, o);
                 const uint4 u = __builtin_bit_cast(uint4, w);
-                buf_store8(ro, e * 2u, make_uint2(u.x, u.y));
+                buf_store8<kOutPolicy>(ro, e * 2u, make_uint2(u.x, u.y));
             } else {
-                buf_store16(ro, e * 4u, __builtin_bit_cast(uint4, o));
+                buf_store16<kOutPolicy>(ro, e * 4u, __builtin_bit_cast(uint4, o));
             }
         }
     }

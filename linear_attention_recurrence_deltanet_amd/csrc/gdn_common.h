@@ -193,8 +193,9 @@ __device__ __forceinline__ uint16_t buf_load2(rsrc_t r, unsigned off) {
 __device__ __forceinline__ uint32_t buf_load4(rsrc_t r, unsigned off) {
     return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }
+template <int AUX = 0>
 __device__ __forceinline__ void buf_store4(rsrc_t r, unsigned off, float v) {
-    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, AUX);
 }
 __device__ __forceinline__ void buf_store2(rsrc_t r, unsigned off, uint16_t v) {
     __builtin_amdgcn_raw_buffer_store_b16(v, r, off, 0, 0);
@@ -207,9 +208,10 @@ __device__ __forceinline__ void buf_store8(rsrc_t r, unsigned off, uint2 v, unsi
     typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
     __builtin_amdgcn_raw_buffer_store_b64(u32x2{v.x, v.y}, r, off, (int)soff, AUX);
 }
+template <int AUX = 0>
 __device__ __forceinline__ void buf_store16(rsrc_t r, unsigned off, uint4 v) {
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-    __builtin_amdgcn_raw_buffer_store_b128(u32x4{v.x, v.y, v.z, v.w}, r, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4{v.x, v.y, v.z, v.w}, r, off, 0, AUX);
 }
 // Accumulating outputs (the second scan of a bidirectional call) add fp32
 // values from a separate plane before their one rounding: four of them, as

@@ -186,3 +186,35 @@ def test_bidir_gates_single_pass(gdn_lib, oracle_mod):
          what="single-gates")
     _run(gdn_lib, oracle_mod, WORKLOADS["stream_chunk_h16_d64"], 1, H=3, T=777, chunk=128, gates=True,
          out_dtype=torch.bfloat16, what="single-gates-bf16")
+
+
+def test_bidir_fused_batch_in_place(gdn_lib, oracle_mod):
+    # B = 2 in one fused call, state updated in place (state_out aliases
+    # state_in), two carried calls; the working scale of each direction is
+    # per head
+    wl = WORKLOADS["stream_chunk_h16_d64"]
+    B, H, T = 2, 3, 1500
+    assert _fused(gdn_lib, B, H, T, 64, 64)
+    announce(f"bidir fused batch in place B={B} H={H} T={T}")
+    state = None
+    o_state = None
+    g_outs, o_outs = [], []
+    for c in range(2):
+        d = make_call(wl, c, B=B, H=H, T=T)
+        g = to_dev(d)
+        if state is None:
+            if d["state_in"] is None:
+                state = torch.zeros(B, H, 64, 64, device="cuda")
+                o_state = np.zeros((B, H, 64, 64))
+            else:
+                state = g["state_in"].clone()
+                o_state = to_numpy64(d["state_in"])
+        o, s = gdn_lib.fwd_bidir(g["q"], g["k"], g["v"], g["alpha"], g["beta"], state, state_out=state)
+        assert s.data_ptr() == state.data_ptr()
+        g_outs.append(o.to("cpu", torch.float64).numpy())
+        q, k, v, a, b = (to_numpy64(d[n]) for n in ("q", "k", "v", "alpha", "beta"))
+        oo, o_state = oracle_mod.gdn_bidir(q, k, v, a, b, o_state)
+        o_outs.append(oo)
+    torch.cuda.synchronize()
+    assert_close(np.concatenate(g_outs, 2), np.concatenate(o_outs, 2), False, "batch in place out")
+    assert_close(state.to("cpu", torch.float64).numpy(), o_state, False, "batch in place state")
