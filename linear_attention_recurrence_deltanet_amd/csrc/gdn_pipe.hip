@@ -60,6 +60,9 @@ constexpr int kStageStorePolicy = 1 | 16;
 // and the single-frame step.
 constexpr int kOutPolicy = 1 | 16;
 
+// Instantiations of the walker by the features a call uses (EXT).
+constexpr int kExtGates = 1, kExtAll = 3;
+
 // Compile-time LDS plan (bytes).
 template <int DK, int C, int CT, bool SEG, int NCW_ = 4, int NPW_ = 4>
 struct PPlan {
@@ -249,12 +252,15 @@ __device__ __forceinline__ f32x4 transpose16_bf16(const uint16_t* a, int lda, in
 // NCW: state waves (4, or 8 with one column tile each: three waves per SIMD
 //      instead of two when one state wave would otherwise carry two tiles).
 // NPW: key waves (4 or 8).
-// EXT: gate logits, the output gate, the backward walk and accumulating
-//      outputs are honoured (a separate instantiation, so that calls without
-//      them run none of that code).
-template <int DK, int C, int CT, bool SEG, int NCW = 4, int NPW = 4, bool EXT = false>
+// EXT: 0 plain; kExtGates: gate logits and the output gate are honoured;
+//      kExtAll: also the backward walk, accumulating outputs and the fused
+//      bidirectional launch (separate instantiations, so that calls without
+//      them run none of that code: the full variant costs 3-8% even unused).
+template <int DK, int C, int CT, bool SEG, int NCW = 4, int NPW = 4, int EXT = 0>
 __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) {
     typedef PPlan<DK, C, CT, SEG, NCW, NPW> L;
+    constexpr bool XG = EXT != 0;                    // gates
+    constexpr bool XR = EXT == kExtAll;              // reverse, accumulate, fused bidirectional
     typedef OpF16 Op;
     typedef _Float16 E;
     typedef Op::frag F;
@@ -325,7 +331,7 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
         seg = r % nseg;
         bh = r / nseg;
         // a fused bidirectional launch: both directions of a head adjacent
-        if constexpr (SEG && EXT) {
+        if constexpr (SEG && XR) {
             if (p.bidir) {
                 dir = bh & 1;
                 bh >>= 1;
@@ -335,7 +341,7 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
     bh = uniform(bh);
     seg = uniform(seg);
     ctile = uniform(ctile);
-    if constexpr (SEG && EXT) dir = uniform(dir);
+    if constexpr (SEG && XR) dir = uniform(dir);
     // tile-local columns [vlo, BV) are value columns; global v column = vbase + local
     int vlo, vbase;
     if constexpr (SEG) {
@@ -375,14 +381,14 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
     const unsigned osz = p.out_bf16 ? 2u : 4u;
     const rsrc_t ro_ = make_rsrc(SEG ? nullptr : (const char*)p.out + (size_t)bh * T * dv * osz,
                                  SEG ? 0u : (unsigned)T * dv * osz);
-    const bool gated = EXT && !SEG && p.out_gate != nullptr;   // a segment walk leaves it to the correction
-    const bool logits = EXT && p.gate_logits;
-    const bool accum = EXT && !SEG && p.accumulate;
+    const bool gated = XG && !SEG && p.out_gate != nullptr;    // a segment walk leaves it to the correction
+    const bool logits = XG && p.gate_logits;
+    const bool accum = XR && !SEG && p.accumulate;
     // accumulating outputs add fp32 values from a separate plane before the store
     const rsrc_t rac_ = make_rsrc(accum ? p.acc_src + (size_t)bh * T * dv : nullptr,
                                   accum ? (unsigned)T * dv * 4u : 0u);
     // walk position -> token
-    const TokMap tm = dir ? tok_map_padded(nchunks * C) : tok_map(T, EXT && p.reverse);
+    const TokMap tm = dir ? tok_map_padded(nchunks * C) : tok_map(T, XR && p.reverse);
     const rsrc_t rg_ = make_rsrc(gated ? (const char*)p.out_gate + (size_t)bh * T * dv * 2 : nullptr,
                                  gated ? (unsigned)T * dv * 2u : 0u);
     // Phi of this segment: [chunk][row block][k-step of 32 columns of d_k][lane] x 8 fp16,
@@ -422,8 +428,8 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
     short wunit[CT];                                  // bf16 bits of winv (exact: a power of two)
     // output gate of the next chunk's rows (this lane's row and 4 columns per
     // row block), loaded a step ahead of its use
-    uint2 GV[EXT && !SEG ? CT : 1][EXT && !SEG ? NB : 1];
-    uint4 AV[EXT && !SEG ? CT : 1][EXT && !SEG ? NB : 1];     // values to accumulate onto, likewise
+    uint2 GV[XG && !SEG ? CT : 1][XG && !SEG ? NB : 1];
+    uint4 AV[XR && !SEG ? CT : 1][XR && !SEG ? NB : 1];       // values to accumulate onto, likewise
     auto col0 = [&](int ct) { return 16 * (ct * NCW + wave); };
     auto ident = [&](int ct) { return SEG && col0(ct) < vlo; };
 
@@ -557,27 +563,29 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
         for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
             for (int ks = 0; ks < KS_D; ++ks) mB[ct][ks] = Op::b_acc(Macc[ct], ks);
-        if constexpr (EXT && !SEG) {
+        if constexpr (XG && !SEG) {
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
                 for (int rb = 0; rb < NB; ++rb) {
                     GV[ct][rb] = make_uint2(0u, 0u);
-                    AV[ct][rb] = make_uint4(0u, 0u, 0u, 0u);
+                    if constexpr (XR) AV[ct][rb] = make_uint4(0u, 0u, 0u, 0u);
                 }
         }
         for (int s = 0; s <= nch; ++s) {
             const int pc = wc0 + s;
             const int vb = s & 1;
-            if constexpr (EXT && !SEG) {
+            if constexpr (XG && !SEG) {
                 // the gate loaded last step arrives here on every path, so no
                 // later reuse of its registers waits for the output stores
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-                    for (int rb = 0; rb < NB; ++rb)
-                        asm volatile("" ::"v"(GV[ct][rb].x), "v"(GV[ct][rb].y), "v"(AV[ct][rb].x),
-                                     "v"(AV[ct][rb].y), "v"(AV[ct][rb].z), "v"(AV[ct][rb].w));
+                    for (int rb = 0; rb < NB; ++rb) {
+                        asm volatile("" ::"v"(GV[ct][rb].x), "v"(GV[ct][rb].y));
+                        if constexpr (XR)
+                            asm volatile("" ::"v"(AV[ct][rb].x), "v"(AV[ct][rb].y), "v"(AV[ct][rb].z), "v"(AV[ct][rb].w));
+                    }
             }
             // ---- phase 1: finish chunk pc - 1
             if (s > 0) {
@@ -648,7 +656,7 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
                                 // rows past T fall outside the buffer and are dropped
                                 const unsigned e0 = (unsigned)(tm(t0 + 16 * rb + lc) * dv +
                                                                vbase + col0(ct) + 4 * lg);
-                                if constexpr (EXT && !SEG) {
+                                if constexpr (XG && !SEG) {
                                     // consumed on every path (1 without a gate): a use under a
                                     // branch leaves the load pending on the other path, and the
                                     // next write of these registers then waits for every
@@ -659,7 +667,7 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
                                     o[2] *= gated ? __builtin_bit_cast(float, w.y << 16) : 1.f;
                                     o[3] *= gated ? __builtin_bit_cast(float, w.y & 0xffff0000u) : 1.f;
                                     // accumulating: the plane is added (zeros otherwise), one rounding
-                                    add_f32x4(o, AV[ct][rb]);
+                                    if constexpr (XR) add_f32x4(o, AV[ct][rb]);
                                 }
                                 if (p.out_bf16) {
                                     const uint2 w = make_uint2(
@@ -700,6 +708,23 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
             if (s == nch) break;
             __syncthreads();
             // ---- phase 2: K^ M, Q^ M of chunk pc
+            if constexpr (XG && !SEG) {
+                // output gate and values to accumulate onto of chunk pc, used
+                // when it is finished next step (issued three phases ahead of
+                // that, so the wait at the top of the step finds them loaded).
+                // Issued whether or not a gate is given (the resource is empty
+                // then), so that the wait before its use counts exactly and
+                // does not drain the output stores issued in between
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                    for (int rb = 0; rb < NB; ++rb) {
+                        const unsigned e = (unsigned)(tm(pc * C + 16 * rb + lc) * dv + vbase + col0(ct) + 4 * lg);
+                        GV[ct][rb] = buf_load8(rg_, e * 2u);
+                        if constexpr (XR) AV[ct][rb] = buf_load16(rac_, e * 4u);
+                    }
+            }
+
             // K^ M and Q^ M of chunk pc with the state after chunk pc - 1
             f32x4 KMlo[CT];
 #pragma unroll
@@ -793,21 +818,6 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
 #pragma unroll
                 for (int u = 0; u < (NTS + NCW - 1) / NCW; ++u)
                     if (wave + NCW * u < NTS) p_tile<L>(Kh, Qh, Pm, v_g2, wave + NCW * u, lq);
-            }
-            if constexpr (EXT && !SEG) {
-                // output gate and values to accumulate onto of chunk pc, used
-                // when it is finished next step.
-                // Issued whether or not a gate is given (the resource is empty
-                // then), so that the wait before its use counts exactly and
-                // does not drain the output stores issued in between
-#pragma unroll
-                for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-                    for (int rb = 0; rb < NB; ++rb) {
-                        const unsigned e = (unsigned)(tm(pc * C + 16 * rb + lc) * dv + vbase + col0(ct) + 4 * lg);
-                        GV[ct][rb] = buf_load8(rg_, e * 2u);
-                        AV[ct][rb] = buf_load16(rac_, e * 4u);
-                    }
             }
             __syncthreads();
         }
@@ -1475,7 +1485,7 @@ __global__ __launch_bounds__(1024) void gdn_pipe_fix_kernel(WalkArgs p) {
 // ---------------------------------------------------------------------------
 namespace {
 
-template <int DK, int C, int CTS, bool EXT>
+template <int DK, int C, int CTS, int EXT>
 hipError_t launch_pipe_g(const WalkArgs& a, hipStream_t s) {
     // a segment tile of 128 columns: eight state waves of one tile each
     // (three waves per SIMD; measured faster than four state waves of two
@@ -1488,7 +1498,7 @@ hipError_t launch_pipe_g(const WalkArgs& a, hipStream_t s) {
     if (a.nseg > 1) {
         const int grid = bh * a.nseg * ((DK + a.dv) / (64 * CTS));
         // a fused bidirectional call walks both directions in one launch
-        const int walks = EXT && a.bidir ? 2 : 1;
+        const int walks = EXT == kExtAll && a.bidir ? 2 : 1;
         hipLaunchKernelGGL((gdn_pipe_kernel<DK, C, SCT, true, SNCW, 4, EXT>), dim3(grid * walks), dim3(64 * (SNCW + 4)),
                            0, s, a);
         hipError_t e = hipGetLastError();
@@ -1505,9 +1515,9 @@ hipError_t launch_pipe_g(const WalkArgs& a, hipStream_t s) {
 
 template <int DK, int C, int CTS>
 hipError_t launch_pipe_t(const WalkArgs& a, hipStream_t s) {
-    if (a.gate_logits || a.out_gate || a.reverse || a.accumulate || a.bidir)
-        return launch_pipe_g<DK, C, CTS, true>(a, s);
-    return launch_pipe_g<DK, C, CTS, false>(a, s);
+    if (a.reverse || a.accumulate || a.bidir) return launch_pipe_g<DK, C, CTS, kExtAll>(a, s);
+    if (a.gate_logits || a.out_gate) return launch_pipe_g<DK, C, CTS, kExtGates>(a, s);
+    return launch_pipe_g<DK, C, CTS, 0>(a, s);
 }
 
 template <int DK, int C>
