@@ -511,11 +511,19 @@ __global__ __launch_bounds__(512) void frame_out_kernel(FrameArgs p) {
     const uint16_t* qg = reinterpret_cast<const uint16_t*>(p.q);
     const uint16_t* gg = reinterpret_cast<const uint16_t*>(p.out_gate);
 
+    // Prologue: every load it needs -- this column group's M_f^T (hi + lo), z_f
+    // and the first block's queries and gate -- is issued before any is
+    // used, so the workgroup pays one memory round trip before its first
+    // products, not one per kind of operand
     const size_t mb = ((size_t)bh * p.F + f) * DV * DK + (size_t)64 * cg * DK;
-    for (int e = tid; e < 64 * DK / 8; e += 512) {
-        const int r = e / (DK / 8), c8 = e % (DK / 8);
-        *reinterpret_cast<uint4*>(&Mh[r * MST + 8 * c8]) = *reinterpret_cast<const uint4*>(p.mt_hi + mb + (size_t)r * DK + 8 * c8);
-        *reinterpret_cast<uint4*>(&Ml[r * MST + 8 * c8]) = *reinterpret_cast<const uint4*>(p.mt_lo + mb + (size_t)r * DK + 8 * c8);
+    constexpr int MIT = 64 * DK / 8 / 512;          // 16-byte pieces per thread of each of hi, lo
+    static_assert(MIT * 512 * 8 == 64 * DK, "whole pieces");
+    uint4 mh[MIT], ml[MIT];
+#pragma unroll
+    for (int j = 0; j < MIT; ++j) {
+        const int e = tid + 512 * j, r = e / (DK / 8), c8 = e % (DK / 8);
+        mh[j] = *reinterpret_cast<const uint4*>(p.mt_hi + mb + (size_t)r * DK + 8 * c8);
+        ml[j] = *reinterpret_cast<const uint4*>(p.mt_lo + mb + (size_t)r * DK + 8 * c8);
     }
     float zq[NKS][8];
     const float* zf = p.zf + ((size_t)bh * p.F + f) * DK;
@@ -523,15 +531,6 @@ __global__ __launch_bounds__(512) void frame_out_kernel(FrameArgs p) {
     for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
         for (int q = 0; q < 8; ++q) zq[ks][q] = zf[32 * ks + 8 * lg + q];
-    __syncthreads();
-    u16x8 ah[4][NKS], al[4][NKS];
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            ah[ct][ks] = *reinterpret_cast<const u16x8*>(&Mh[(16 * ct + lc) * MST + 32 * ks + 8 * lg]);
-            al[ct][ks] = *reinterpret_cast<const u16x8*>(&Ml[(16 * ct + lc) * MST + 32 * ks + 8 * lg]);
-        }
 
     // queries and gate of the frame through buffer resources: rows past the
     // frame read zero without a branch
@@ -553,6 +552,21 @@ __global__ __launch_bounds__(512) void frame_out_kernel(FrameArgs p) {
         for (int ct = 0; ct < 4; ++ct) gn[ct] = buf_load8(rg, (t * DV + 64 * cg + 16 * ct + 4 * lg) * 2);
     };
     load_q(b);
+#pragma unroll
+    for (int j = 0; j < MIT; ++j) {
+        const int e = tid + 512 * j, r = e / (DK / 8), c8 = e % (DK / 8);
+        *reinterpret_cast<uint4*>(&Mh[r * MST + 8 * c8]) = mh[j];
+        *reinterpret_cast<uint4*>(&Ml[r * MST + 8 * c8]) = ml[j];
+    }
+    __syncthreads();
+    u16x8 ah[4][NKS], al[4][NKS];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            ah[ct][ks] = *reinterpret_cast<const u16x8*>(&Mh[(16 * ct + lc) * MST + 32 * ks + 8 * lg]);
+            al[ct][ks] = *reinterpret_cast<const u16x8*>(&Ml[(16 * ct + lc) * MST + 32 * ks + 8 * lg]);
+        }
     for (; b < nb; b += stride) {
         u16x8 qf[NKS];
         uint2 gf[4];
@@ -628,9 +642,13 @@ void frame_plan(int B, int H, int F, int N, int dk, int dv, int* nsp, int* nts) 
     const long long ms = dk == 128 ? 2 : 4;     // max_splits<DK>() of the scan
     if (smax > ms) smax = ms;
     *nsp = (int)(s < 1 ? 1 : (s > smax ? smax : s));
-    // readout: about 256 workgroups of 8 waves, each wave at least one 16-token block
+    // readout: about 1024 workgroups of 8 waves, each wave at least one 16-token
+    // block: a workgroup's time is mostly its first memory round trips, so more
+    // and shorter token ranges finish sooner (measured against 256 and 512
+    // targets: 42.0 and 40.0 -> 40.0 us at d = 64, 92.0 and 91.2 -> 88.8 us at
+    // d = 128 per frame-wise call)
     const long long ncg = dv / 64;
-    long long r = (256 + ncg * bhf - 1) / (ncg * bhf);
+    long long r = (1024 + ncg * bhf - 1) / (ncg * bhf);
     long long rmax = (N + 127) / 128;
     *nts = (int)(r < 1 ? 1 : (r > rmax ? rmax : r));
 }
