@@ -49,6 +49,15 @@ struct WalkArgs : FwdArgs {
                              // value columns; staged outputs and maps are in units of it
     int nseg;                // segments per sequence (1: no split)
     int seg_chunks;          // chunks per segment
+    // pipelined, plain calls: segment 0 walks its value columns from
+    // state_in and writes its outputs directly (its tiles of identity columns
+    // only are not launched) and leaves its final state, at the working
+    // scale, in snap; the correction pass then covers segments 1 .. nseg-1,
+    // folding from snap through the maps of segments 1 .. s-1
+    int seg0_direct;
+    // pipelined: the last fix_split segments are corrected by two workgroups
+    // each, one per half of the segment's chunks
+    int fix_split;
     // Both directions of a bidirectional call in one segmented launch pair
     // (pipelined walker): the walk launch covers direction 0 (forward, the
     // buffers above) and direction 1 (tokens in reverse from a zero state,

@@ -323,13 +323,25 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
         const int w8 = (int)gridDim.x / 8 * 8;
         if (wg < w8) wg = (wg % 8) * (w8 / 8) + wg / 8;
     }
+    // Segment 0 of a plain call walks its value columns from state_in (the
+    // true incoming state), so its tiles of identity columns only are not
+    // launched: per head, segment 0 has ncol - skip tiles, the others ncol.
+    const bool direct = SEG && EXT == 0 && p.seg0_direct;
     int bh, seg, ctile, dir = 0;
     {
         const int ncol = SEG ? (DK + dv) / BV : dv / BV;
-        ctile = wg % ncol;
-        const int r = wg / ncol;
-        seg = r % nseg;
-        bh = r / nseg;
+        const int skip = direct && DK != dv ? DK / BV : 0;
+        const int per = ncol * nseg - skip;
+        int i = wg % per;
+        bh = wg / per;
+        if (i < ncol - skip) {
+            seg = 0;
+            ctile = skip + i;
+        } else {
+            i -= ncol - skip;
+            seg = 1 + i / ncol;
+            ctile = i % ncol;
+        }
         // a fused bidirectional launch: both directions of a head adjacent
         if constexpr (SEG && XR) {
             if (p.bidir) {
@@ -341,18 +353,35 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
     bh = uniform(bh);
     seg = uniform(seg);
     ctile = uniform(ctile);
+    // this walk is segment 0 of a plain call: outputs and final state direct
+    const bool direct0 = direct && seg == 0;
     if constexpr (SEG && XR) dir = uniform(dir);
-    // tile-local columns [vlo, BV) are value columns; global v column = vbase + local
-    int vlo, vbase;
+    // Tile-local columns [vlo, BV) are value columns, global v column =
+    // vbase + local; local columns [0, vlo) are identity columns ibase + local.
+    // A segment walk with d_k = d_v gives every tile half identity and half
+    // value columns (tile t: identity and value columns t BV/2 .. t BV/2 +
+    // BV/2 - 1), so that each SIMD pairs an identity wave with a value wave
+    // and the tiles of a segment take the same time (pure tiles of 128
+    // columns at d = 128 left the value tiles 1.3 us behind, measured on
+    // MI355X); other shapes lay [identity | value] out in order.
+    int vlo, vbase, ibase = 0;
     if constexpr (SEG) {
-        const int gc0 = ctile * BV;
-        vlo = min(BV, max(0, DK - gc0));
-        vbase = gc0 - DK;
+        if (DK == dv) {
+            vlo = BV / 2;
+            ibase = ctile * (BV / 2);
+            vbase = ibase - BV / 2;
+        } else {
+            const int gc0 = ctile * BV;
+            vlo = min(BV, max(0, DK - gc0));
+            vbase = gc0 - DK;
+            ibase = gc0;
+        }
     } else {
         vlo = 0;
         vbase = ctile * BV;
     }
     vlo = uniform(vlo);
+    ibase = uniform(ibase);
 
     const int nchunks = (T + C - 1) / C;
     const int ch0 = seg * p.seg_chunks;
@@ -379,8 +408,9 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
     // outputs of the unsegmented walk; a segment walk stages fp16 partial
     // outputs that the correction pass completes
     const unsigned osz = p.out_bf16 ? 2u : 4u;
-    const rsrc_t ro_ = make_rsrc(SEG ? nullptr : (const char*)p.out + (size_t)bh * T * dv * osz,
-                                 SEG ? 0u : (unsigned)T * dv * osz);
+    const bool final_out = !SEG || direct0;
+    const rsrc_t ro_ = make_rsrc(final_out ? (const char*)p.out + (size_t)bh * T * dv * osz : nullptr,
+                                 final_out ? (unsigned)T * dv * osz : 0u);
     const bool gated = XG && !SEG && p.out_gate != nullptr;    // a segment walk leaves it to the correction
     const bool logits = XG && p.gate_logits;
     const bool accum = XR && !SEG && p.accumulate;
@@ -468,7 +498,7 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
     auto init_state = [&]() {
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
-            const int gcol = ctile * BV + col0(ct) + lc;      // segment tile: [ident | value]
+            const int gcol = ibase + col0(ct) + lc;           // identity column of a segment tile
             const int vcol = vbase + col0(ct) + lc;
 #pragma unroll
             for (int ib = 0; ib < NDB; ++ib) Macc[ct][ib] = zero4();
@@ -544,7 +574,7 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
             if constexpr (SEG) {
                 if (!ident(ct)) {
                     if (seg == 0) {
-                        if (state_in) {
+                        if (state_in && !direct0) {
                             float* sn = p.snap + (size_t)bh * DK * dv + vbase + col0(ct) + lc;
 #pragma unroll
                             for (int ib = 0; ib < NDB; ++ib)
@@ -554,8 +584,11 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
                         if (lane == 0)
                             (dir ? p.bw.sscale : p.sscale)[(size_t)bh * (dv / 16) + (vbase + col0(ct)) / 16] = wsc[ct];
                     }
+                    // a direct segment 0 keeps state_in (at the working scale)
+                    if (!direct0) {
 #pragma unroll
-                    for (int ib = 0; ib < NDB; ++ib) Macc[ct][ib] = zero4();
+                        for (int ib = 0; ib < NDB; ++ib) Macc[ct][ib] = zero4();
+                    }
                 }
             }
         }
@@ -621,7 +654,8 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
                         for (int ks = 0; ks < KS_C; ++ks) uB[ks] = Op::b_acc(U, ks);
                         // O^T = M^T Q^^T diag(gam) + U^T P^T, tiles of 16 columns x 16 rows;
                         // lane (lg, lc) holds row 16 rb + lc, columns col0 + 4 lg + i
-                        const int cb = (ctile * BV + col0(ct)) / 16;      // 16-column block of the tile
+                        // 16-column block: of d_k for identity columns, of d_v for value columns
+                        const int cb = ((idt ? ibase : vbase) + col0(ct)) / 16;
                         // chunk within the segment, row block and lane of row lc, in
                         // token order (direction 1 mirrors all three)
                         const int lch = dir ? nch - s : s - 1;
@@ -637,6 +671,27 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
                             for (int ks = 0; ks <= rb / 2; ++ks)
                                 o = Op::mma(uB[ks], a_lower<L::LDC>(Pm, rb, ks, lane), o);
                             if constexpr (SEG) {
+                              if (direct0) {
+                                // segment 0 walked from state_in: the value columns'
+                                // outputs are final (identity columns of a mixed tile
+                                // store nothing); rows past T are dropped
+                                if (!idt) {
+#pragma unroll
+                                    for (int i = 0; i < 4; ++i) o[i] *= wsc[ct];
+                                    const unsigned e0 = (unsigned)(tm(t0 + 16 * rb + lc) * dv +
+                                                                   vbase + col0(ct) + 4 * lg);
+                                    if (p.out_bf16) {
+                                        const uint2 w = make_uint2(
+                                            (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)o[0]) |
+                                                ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)o[1]) << 16),
+                                            (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)o[2]) |
+                                                ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)o[3]) << 16));
+                                        buf_store8<kOutPolicy>(ro_, e0 * 2u, w);
+                                    } else {
+                                        buf_store16<kOutPolicy>(ro_, e0 * 4u, __builtin_bit_cast(uint4, o));
+                                    }
+                                }
+                              } else {
                                 const uint2 w = make_uint2(Op::pk2(o[0], o[1]), Op::pk2(o[2], o[3]));
                                 // in range by construction: the wave-uniform part of the
                                 // offset goes in the scalar operand
@@ -646,10 +701,10 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
                                                uniform((lch * C * DK + (rbs * KS_D + cb / 2) * 512 + (cb & 1) * 4) * 2));
                                 } else {
                                     // value columns: partial output (zero incoming state)
-                                    const int vb16 = cb - DK / 16;
                                     buf_store8<kStageStorePolicy>(rosg_, lrow * 8u, w,
-                                               uniform((lch * C * dv + (rbs * (dv / 16) + vb16) * 256) * 2));
+                                               uniform((lch * C * dv + (rbs * (dv / 16) + cb) * 256) * 2));
                                 }
+                              }
                             } else {
 #pragma unroll
                                 for (int i = 0; i < 4; ++i) o[i] *= wsc[ct];
@@ -1025,8 +1080,19 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
         if (is_state) {
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct) {
-                if (ident(ct)) {
-                    const int c = ctile * BV + col0(ct) + lc;     // identity column = k index
+                if (direct0) {
+                    // segment 0 walked from state_in: its final state (at the
+                    // working scale) is the state entering segment 1, from which
+                    // the correction pass folds; it writes no map
+                    if (!ident(ct)) {
+                        float* sn = p.snap + (size_t)bh * DK * dv + vbase + col0(ct) + lc;
+#pragma unroll
+                        for (int ib = 0; ib < NDB; ++ib)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) sn[(unsigned)((16 * ib + 4 * lg + i) * dv)] = Macc[ct][ib][i];
+                    }
+                } else if (ident(ct)) {
+                    const int c = ibase + col0(ct) + lc;          // identity column = k index
 #pragma unroll
                     for (int ib = 0; ib < NDB; ++ib)
 #pragma unroll
@@ -1043,9 +1109,9 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
             }
         }
         __syncthreads();
-        const int k0 = ctile * BV;                        // first identity column of the tile
-        if (k0 < DK) {
-            const int ks0 = k0 / 32, nks = (min(DK, k0 + BV) - k0) / 32;
+        const int k0 = ibase;                             // first identity column of the tile
+        if (vlo > 0 && !direct0) {
+            const int ks0 = k0 / 32, nks = vlo / 32;
             const rsrc_t ra_ = make_rsrc(summA_bh + (size_t)seg * DK * DK, (unsigned)(DK * DK * 2));
             for (int f = wave; f < NDB * nks; f += NW) {
                 const int ib = f / nks, ks = ks0 + f % nks;
@@ -1088,7 +1154,14 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void gdn_pipe_kernel(WalkArgs p) 
 // segment is folded the same way, from zero through the maps of the segments
 // after this one, last first; each output is the sum of both directions'
 // corrected outputs, each in its own working scale, rounded once.
-template <int DK, int C, bool BI>
+// PL: a plain call (no output gate, no accumulation), whose corrections load
+// only Phi and the partial outputs: measured on MI355X (per-workgroup clock
+// stamps, same box) the pass ends 1.3 us earlier on the 16-head d = 128
+// rollout and 1.2 us on the d = 64 streaming chunk than with the gate and
+// accumulation loads issued on empty ranges.  Two correction groups stay in
+// flight: four, six and eight were each slower (their loads, issued before
+// the fold, delay the map loads the fold waits on).
+template <int DK, int C, bool BI, bool PL = false>
 __global__ __launch_bounds__(1024) void gdn_pipe_fix_kernel(WalkArgs p) {
     typedef OpF16 Op;
     typedef Op::frag F;
@@ -1129,18 +1202,49 @@ __global__ __launch_bounds__(1024) void gdn_pipe_fix_kernel(WalkArgs p) {
         const int w8 = (int)gridDim.x / 8 * 8;
         if (wg < w8) wg = (wg % 8) * (w8 / 8) + wg / 8;
     }
+    // Segments s0 .. nseg - 1 are corrected (s0 = 1 when segment 0 walked
+    // from state_in and wrote its outputs itself); the last nsp of them, whose
+    // folds are the longest, by two workgroups each, one per half of their
+    // chunks, so that the deepest fold is not followed by a whole segment of
+    // corrections.
     const int ntile = dv / 64;
     const int vt = uniform(wg % ntile);
-    const int seg = uniform((wg / ntile) % nseg);
-    const int bh = uniform(wg / ntile / nseg);
-    const bool last = seg == nseg - 1 && p.state_out != nullptr;
-    const bool has_in = p.state_in != nullptr;
+    const int s0 = BI ? 0 : p.seg0_direct;
+    const int nsp = BI ? 0 : p.fix_split;
+    const int n1 = nseg - s0 - nsp;                     // segments of one workgroup
+    const int per = n1 + 2 * nsp;
+    int seg, part, nparts;
+    {
+        int i = (wg / ntile) % per;
+        if (i < n1) {
+            seg = s0 + i;
+            part = 0;
+            nparts = 1;
+        } else {
+            i -= n1;
+            seg = s0 + n1 + i / 2;
+            part = i % 2;
+            nparts = 2;
+        }
+    }
+    seg = uniform(seg);
+    part = uniform(part);
+    nparts = uniform(nparts);
+    const int bh = uniform(wg / ntile / per);
+    const bool last = seg == nseg - 1 && part == 0 && p.state_out != nullptr;
+    // the state the fold starts from: segment 1's incoming state (written by a
+    // direct segment 0), else the copy of state_in (zero without one)
+    const bool from_snap = s0 > 0 || p.state_in != nullptr;
 
     const int col = vt * 64 + 16 * cg + lc;             // value column of this lane
     const int c16 = vt * 4 + cg;                        // its 16-column block
     const int nchunks = (T + C - 1) / C;
     const int ch0 = seg * p.seg_chunks;
     const int ch1 = min(nchunks, ch0 + p.seg_chunks);
+    // the chunks this workgroup corrects: [cb, ce) of the segment's [ch0, ch1)
+    const int half = (ch1 - ch0 + 1) / 2;
+    const int cb = uniform(nparts == 2 && part == 1 ? ch0 + half : ch0);
+    const int ce = uniform(nparts == 2 && part == 0 ? min(ch1, ch0 + half) : ch1);
     // segment data of one direction: maps of all segments, this segment's Phi
     // and partial outputs
     auto maps_a = [&](const void* base) {
@@ -1194,27 +1298,32 @@ __global__ __launch_bounds__(1024) void gdn_pipe_fix_kernel(WalkArgs p) {
     // of the partial outputs (fp16, 4 columns per lane); the same of the
     // backward direction (stored in token order by its walk)
     auto cload = [&](uint4& h, uint2& o, uint2& gt, uint4& av, uint4& hb, uint2& ob, int g) {
-        const int c0 = ch0 + g * CPG;
+        const int c0 = cb + g * CPG;
         const int c = c0 + rg / NB, rb = rg % NB;
-        const unsigned hoff = (c0 < ch1 && tid < PPG) ? (unsigned)((c0 - ch0) * C * DK * 2 + tid * 16) : kOffNone;
-        const unsigned ooff = c < ch1 ? (unsigned)((((c - ch0) * NB + rb) * (dv / 16) + c16) * 64 + lane) * 8u
-                                      : kOffNone;
+        const unsigned hoff = (c0 < ce && tid < PPG) ? (unsigned)((c0 - ch0) * C * DK * 2 + tid * 16) : kOffNone;
+        const unsigned ooff = c < ce ? (unsigned)((((c - ch0) * NB + rb) * (dv / 16) + c16) * 64 + lane) * 8u
+                                     : kOffNone;
         h = buf_load16(rP, hoff);
         o = buf_load8(rO, ooff);
         if constexpr (BI) {
             hb = buf_load16(rPb, hoff);
             ob = buf_load8(rOb, ooff);
         }
-        // output gate of the same four elements (the range is empty without one)
-        const unsigned e = (unsigned)(tm(c * C + 16 * rb + lc) * dv + col4);
-        gt = buf_load8(rG, c < ch1 ? e * 2u : kOffNone);
-        // values to accumulate onto (the range is empty unless accumulating)
-        if constexpr (!BI) av = buf_load16(rAc, c < ch1 ? e * 4u : kOffNone);
+        if constexpr (!PL) {
+            // output gate of the same four elements (the range is empty without one)
+            const unsigned e = (unsigned)(tm(c * C + 16 * rb + lc) * dv + col4);
+            gt = buf_load8(rG, c < ce ? e * 2u : kOffNone);
+            // values to accumulate onto (the range is empty unless accumulating)
+            if constexpr (!BI) av = buf_load16(rAc, c < ce ? e * 4u : kOffNone);
+        }
     };
-    uint4 ph[2], av2[2], phb[2];
-    uint2 ov[2], gv2[2], ovb[2];
-    cload(ph[0], ov[0], gv2[0], av2[0], phb[0], ovb[0], 0);
-    cload(ph[1], ov[1], gv2[1], av2[1], phb[1], ovb[1], 1);
+    // a ring of NPF correction groups in flight, the first issued before the fold
+    constexpr int NPF = 2;
+    static_assert(NPF % 2 == 0, "the staging copies alternate");
+    uint4 ph[NPF], av2[NPF], phb[NPF];
+    uint2 ov[NPF], gv2[NPF], ovb[NPF];
+#pragma unroll
+    for (int j = 0; j < NPF; ++j) cload(ph[j], ov[j], gv2[j], av2[j], phb[j], ovb[j], j);
 
     // ---- the state entering the segment, per direction, as fp16 B fragments
     // of the whole of M for every wave.  A direction folds nfold maps, map
@@ -1315,7 +1424,7 @@ __global__ __launch_bounds__(1024) void gdn_pipe_fix_kernel(WalkArgs p) {
 #pragma unroll
         for (int ks = 0; ks < KS_D; ++ks) mOut[ks] = __builtin_bit_cast(F, Mf[0][ks][cg][lane]);
     };
-    fold(rA, rB, seg, last, 0, 1, has_in, mI);
+    fold(rA, rB, seg - s0, last, s0, 1, from_snap, mI);
     if constexpr (BI) {
         __syncthreads();                  // every wave has read Mf and the staged maps
         fold(rAb, rBb, nseg - 1 - seg, false, nseg - 1, -1, false, mIb);
@@ -1416,7 +1525,7 @@ __global__ __launch_bounds__(1024) void gdn_pipe_fix_kernel(WalkArgs p) {
                 for (int i = 0; i < 4; ++i) sp[(16 * (rg * RB + r) + 4 * lg + i) * dv] = Macc[r][i] * s_w;
         }
     };
-    fold(rA, rB, seg, last, 0, 1, has_in, mI);
+    fold(rA, rB, seg - s0, last, s0, 1, from_snap, mI);
     if constexpr (BI) {
         __syncthreads();                  // every wave has read Mf and the staged map
         fold(rAb, rBb, nseg - 1 - seg, false, nseg - 1, -1, false, mIb);
@@ -1428,7 +1537,7 @@ __global__ __launch_bounds__(1024) void gdn_pipe_fix_kernel(WalkArgs p) {
     // and four consecutive columns, one 16-byte access
     auto cfix = [&](const uint4& h, const uint2& o, const uint2& gt, const uint4& av, const uint4& hb,
                     const uint2& ob, int g, int buf) {
-        const int c = ch0 + g * CPG + rg / NB, rb = rg % NB;
+        const int c = cb + g * CPG + rg / NB, rb = rg % NB;
         if (tid < PPG) {
             Phs[buf][tid] = h;
             if constexpr (BI) Phb[buf * PPG + tid] = hb;
@@ -1453,30 +1562,31 @@ __global__ __launch_bounds__(1024) void gdn_pipe_fix_kernel(WalkArgs p) {
         }
         // rows past T fall outside the buffer and are dropped
         const unsigned e0 = (unsigned)(tm(c * C + 16 * rb + lc) * dv + col4);
-        if (gated) {
+        if (!PL && gated) {
             acc[0] *= __builtin_bit_cast(float, gt.x << 16);
             acc[1] *= __builtin_bit_cast(float, gt.x & 0xffff0000u);
             acc[2] *= __builtin_bit_cast(float, gt.y << 16);
             acc[3] *= __builtin_bit_cast(float, gt.y & 0xffff0000u);
         }
-        if constexpr (!BI) add_f32x4(acc, av);   // accumulating: one rounding of the sum
+        if constexpr (!BI && !PL) add_f32x4(acc, av);   // accumulating: one rounding of the sum
         if (p.out_bf16) {
             const uint2 w = make_uint2(
                 (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[0]) |
                     ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[1]) << 16),
                 (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[2]) |
                     ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[3]) << 16));
-            buf_store8<kOutPolicy>(rW, c < ch1 ? e0 * 2u : kOffNone, w);
+            buf_store8<kOutPolicy>(rW, c < ce ? e0 * 2u : kOffNone, w);
         } else {
-            buf_store16<kOutPolicy>(rW, c < ch1 ? e0 * 4u : kOffNone, __builtin_bit_cast(uint4, acc));
+            buf_store16<kOutPolicy>(rW, c < ce ? e0 * 4u : kOffNone, __builtin_bit_cast(uint4, acc));
         }
     };
-    const int ngroups = (ch1 - ch0 + CPG - 1) / CPG;
-    for (int g = 0; g < ngroups; g += 2) {
-        cfix(ph[0], ov[0], gv2[0], av2[0], phb[0], ovb[0], g, 0);
-        cload(ph[0], ov[0], gv2[0], av2[0], phb[0], ovb[0], g + 2);
-        cfix(ph[1], ov[1], gv2[1], av2[1], phb[1], ovb[1], g + 1, 1);
-        cload(ph[1], ov[1], gv2[1], av2[1], phb[1], ovb[1], g + 3);
+    const int ngroups = (ce - cb + CPG - 1) / CPG;
+    for (int g = 0; g < ngroups; g += NPF) {
+#pragma unroll
+        for (int j = 0; j < NPF; ++j) {
+            cfix(ph[j], ov[j], gv2[j], av2[j], phb[j], ovb[j], g + j, j & 1);
+            cload(ph[j], ov[j], gv2[j], av2[j], phb[j], ovb[j], g + j + NPF);
+        }
     }
 }
 
@@ -1496,17 +1606,37 @@ hipError_t launch_pipe_g(const WalkArgs& a, hipStream_t s) {
     static_assert(pipe_fits<DK, C, 1, false, 4, UNPW>() && pipe_fits<DK, C, SCT, true, SNCW>(), "LDS plan exceeds 160 KiB");
     const int bh = a.B * a.H;
     if (a.nseg > 1) {
-        const int grid = bh * a.nseg * ((DK + a.dv) / (64 * CTS));
+        WalkArgs b = a;
+        const int ncol = (DK + a.dv) / (64 * CTS);
+        // plain calls: segment 0 walks from state_in and writes its outputs
+        // itself, so its tiles of identity columns only are not launched
+        b.seg0_direct = EXT == 0 ? 1 : 0;
+        const int skip = b.seg0_direct && DK != a.dv ? DK / (64 * CTS) : 0;
+        const int grid = bh * (a.nseg * ncol - skip);
         // a fused bidirectional call walks both directions in one launch
         const int walks = EXT == kExtAll && a.bidir ? 2 : 1;
+        b.fix_split = 0;
         hipLaunchKernelGGL((gdn_pipe_kernel<DK, C, SCT, true, SNCW, 4, EXT>), dim3(grid * walks), dim3(64 * (SNCW + 4)),
-                           0, s, a);
+                           0, s, b);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        if (walks == 2)
-            hipLaunchKernelGGL((gdn_pipe_fix_kernel<DK, C, true>), dim3(bh * a.nseg * (a.dv / 64)), dim3(1024), 0, s, a);
-        else
-            hipLaunchKernelGGL((gdn_pipe_fix_kernel<DK, C, false>), dim3(bh * a.nseg * (a.dv / 64)), dim3(1024), 0, s, a);
+        // correction: one workgroup per (head, corrected segment, 64 value
+        // columns); the deepest segments take a second one while the launch
+        // still fits one round on the 256 compute units
+        const long long unit = (long long)bh * (a.dv / 64);
+        if (walks == 2) {
+            hipLaunchKernelGGL((gdn_pipe_fix_kernel<DK, C, true>), dim3(unit * a.nseg), dim3(1024), 0, s, b);
+        } else {
+            const int nfix = a.nseg - b.seg0_direct;
+            const long long room = 256 / unit - nfix;
+            b.fix_split = (int)(room <= 0 ? 0 : (room < nfix ? room : nfix));
+            if (!a.out_gate && !a.accumulate)
+                hipLaunchKernelGGL((gdn_pipe_fix_kernel<DK, C, false, true>), dim3(unit * (nfix + b.fix_split)),
+                                   dim3(1024), 0, s, b);
+            else
+                hipLaunchKernelGGL((gdn_pipe_fix_kernel<DK, C, false>), dim3(unit * (nfix + b.fix_split)), dim3(1024),
+                                   0, s, b);
+        }
         return hipGetLastError();
     }
     hipLaunchKernelGGL((gdn_pipe_kernel<DK, C, 1, false, 4, UNPW, EXT>), dim3(bh * (a.dv / 64)), dim3(64 * (4 + UNPW)), 0, s, a);
