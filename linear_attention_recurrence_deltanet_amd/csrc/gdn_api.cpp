@@ -130,8 +130,12 @@ size_t seg_workspace(int in_f32, int B, int H, int dk, int dv, int nseg) {
 // folded map per preceding segment and the rewrite of the segment's outputs.
 // A launch of more workgroups than compute units runs in rounds.  Constants
 // measured on MI355X.  walks = 2: a fused bidirectional call, whose launches
-// walk and correct both directions at once.
-Plan pipe_plan(int B, int H, int T, int dk, int dv, int chunk, int walks = 1) {
+// walk and correct both directions at once.  plain: no gates, not reversed,
+// not accumulating; segment 0 then walks from state_in and needs no
+// correction (one folded map fewer), and the pass starts sooner and rewrites
+// a chunk faster, since it loads no gate or accumulation operands (refitted
+// to the 16-head rollout, streaming chunk and 48-head single-frame step).
+Plan pipe_plan(int B, int H, int T, int dk, int dv, int chunk, int walks = 1, bool plain = false) {
     Plan pl{};
     pl.pipe = true;
     const int nchunks = (int)(((long long)T + chunk - 1) / chunk);
@@ -141,9 +145,9 @@ Plan pipe_plan(int B, int H, int T, int dk, int dv, int chunk, int walks = 1) {
     const long long sb = walks * bh * ((dk + dv) / (64 * cts));             // per segment
     const double step_us = (dk == 64 ? 2.7 : 4.0) * (chunk == 64 ? 1.0 : 0.6);
     const double wstep = dk == 64 ? 1.45 : 1.33;         // segment-walk step / unsegmented step
-    const double fix = 9.0 / step_us;                     // correction pass: launch, first loads
+    const double fix = (plain ? 5.0 : 9.0) / step_us;    // correction pass: launch, first loads
     const double fold = 0.15;                             // one folded map
-    const double corr = 0.3 * chunk / 64;                 // outputs of one chunk rewritten
+    const double corr = (plain ? 0.2 : 0.3) * chunk / 64; // outputs of one chunk rewritten
     auto rounds = [](long long wgs) { return (double)((wgs + 255) / 256); };
     int best_n = 0;
     double best = 0;
@@ -151,7 +155,13 @@ Plan pipe_plan(int B, int H, int T, int dk, int dv, int chunk, int walks = 1) {
         const int L = (nchunks + n - 1) / n;
         const int ns = (nchunks + L - 1) / L;
         if (ns < 2 || ns != n) continue;
-        const double cost = rounds(sb * ns) * (L + 1) * wstep + fix + fold * (ns - 1) + corr * walks * L;
+        const int nfold = plain ? ns - 2 : ns - 1;       // maps folded by the last segment
+        // the correction pass runs in rounds too (one workgroup per head, 64
+        // value columns and corrected segment): five segments of the 48-head
+        // single-frame step, two rounds of each launch, measured 61 us per
+        // call against 51 us for two segments in one round
+        const long long fixw = bh * (dv / 64) * (plain ? ns - 1 : ns);
+        const double cost = rounds(sb * ns) * (L + 1) * wstep + rounds(fixw) * (fix + fold * nfold + corr * walks * L);
         if (best_n == 0 || cost < best) { best = cost; best_n = ns; }
     }
     // segments only for a clear gain over the unsegmented walk
@@ -162,8 +172,8 @@ Plan pipe_plan(int B, int H, int T, int dk, int dv, int chunk, int walks = 1) {
     return pl;
 }
 
-Plan make_plan(int in_f32, int B, int H, int T, int dk, int dv, int chunk) {
-    if (gdn::pipe_supported(in_f32, dk, dv, chunk)) return pipe_plan(B, H, T, dk, dv, chunk);
+Plan make_plan(int in_f32, int B, int H, int T, int dk, int dv, int chunk, bool plain) {
+    if (gdn::pipe_supported(in_f32, dk, dv, chunk)) return pipe_plan(B, H, T, dk, dv, chunk, 1, plain);
     Plan pl{};
     int w = chunk == 128 ? 0 : gdn::walk_max_waves(in_f32, dk, chunk);
     while (w > 0 && (16 * w > dk || 16 * w > dv)) w >>= 1;
@@ -227,7 +237,10 @@ int scan(const void* q, const void* k, const void* v, const void* alpha, const v
     a.accumulate = accumulate;
     a.acc_src = acc_src;
     if (T == 0 && !state_out) return GDN_OK;
-    Plan pl = make_plan(a.in_f32, B, H, T, dk, dv, chunk);
+    // the same test as the launch's choice of the plain walker (no gates, not
+    // reversed, not accumulating)
+    const bool plain = !a.gate_logits && !a.out_gate && !reverse && !accumulate;
+    Plan pl = make_plan(a.in_f32, B, H, T, dk, dv, chunk, plain);
     hipStream_t stream = reinterpret_cast<hipStream_t>(o.stream);
     hipError_t e;
     if (pl.single) {
@@ -292,7 +305,7 @@ size_t bidir_workspace(int B, int H, int T, int dk, int dv, int chunk, const gdn
 Plan bidir_fused_plan(const gdn_opts& o, int B, int H, int T, int dk, int dv, int chunk) {
     Plan pl{};
     if (!gdn::pipe_supported(o.in_dtype == GDN_F32, dk, dv, chunk)) return pl;
-    pl = pipe_plan(B, H, T, dk, dv, chunk, 2);
+    pl = pipe_plan(B, H, T, dk, dv, chunk, 2, false);
     if (pl.nseg > 1) pl.ws_bytes = 2 * ((pl.ws_bytes + 255) & ~(size_t)255);
     return pl;
 }
@@ -368,7 +381,8 @@ size_t workspace_for(int B, int H, int T, int dk, int dv, int chunk, const gdn_o
     if (opts) o = *opts; else defaults(&o);
     if (!sizes_ok(B, H, T, dk, dv) || !head_ok(dk) || !head_ok(dv)) return 0;
     if (chunk != 32 && chunk != 64 && chunk != 128) return 0;
-    Plan pl = make_plan(o.in_dtype == GDN_F32, B, H, T, dk, dv, chunk);
+    // a forward call's plan (plain without gates), as the call itself makes it
+    Plan pl = make_plan(o.in_dtype == GDN_F32, B, H, T, dk, dv, chunk, !o.gate_logits && !o.out_gate);
     return pl.ws_bytes;
 }
 
@@ -379,7 +393,8 @@ size_t bidir_workspace(int B, int H, int T, int dk, int dv, int chunk, const gdn
     const size_t pb = plane_bytes(B, H, T, dv);
     const Plan fp = bidir_fused_plan(o, B, H, T, dk, dv, chunk);
     if (fp.nseg > 1) return fp.ws_bytes > pb ? fp.ws_bytes : pb;
-    const Plan pl = make_plan(o.in_dtype == GDN_F32, B, H, T, dk, dv, chunk);
+    // the two scans reverse or accumulate: not plain
+    const Plan pl = make_plan(o.in_dtype == GDN_F32, B, H, T, dk, dv, chunk, false);
     return pb + pl.ws_bytes;
 }
 

@@ -1231,7 +1231,8 @@ __global__ __launch_bounds__(1024) void gdn_pipe_fix_kernel(WalkArgs p) {
     part = uniform(part);
     nparts = uniform(nparts);
     const int bh = uniform(wg / ntile / per);
-    const bool last = seg == nseg - 1 && part == 0 && p.state_out != nullptr;
+    // state_out: applied by the last segment's workgroup with fewer chunks
+    const bool last = seg == nseg - 1 && part == nparts - 1 && p.state_out != nullptr;
     // the state the fold starts from: segment 1's incoming state (written by a
     // direct segment 0), else the copy of state_in (zero without one)
     const bool from_snap = s0 > 0 || p.state_in != nullptr;
