@@ -116,3 +116,45 @@ def test_direct_segment_zero_is_deterministic_and_resumable(gdn_lib):
     torch.cuda.synchronize()
     assert torch.equal(o1, o1b) and torch.equal(s1, s1b)
     assert torch.equal(o2, o2r) and torch.equal(s2, s2r)
+
+
+def _gated(gdn, oracle, wl, calls, *, H, T, chunk=None, out_dtype=torch.float32, what=""):
+    announce(f"segments gated {what}: {wl.name} dk={wl.dk} dv={wl.dv} H={H} T={T} calls={calls} "
+             f"chunk={chunk} out={out_dtype}")
+    g_outs, o_outs = [], []
+    g_state = o_state = None
+    for c in range(calls):
+        d = make_call(wl, c, H=H, T=T, gates=True)
+        g = to_dev(d)
+        s_in = g["state_in"] if c == 0 else g_state
+        kw = dict(out_dtype=out_dtype, gate_logits=True, out_gate=g["out_gate"])
+        if chunk is None:
+            o, s = gdn.fwd_step(g["q"], g["k"], g["v"], g["alpha_logit"], g["beta_logit"], s_in, **kw)
+        else:
+            o, s = gdn.fwd_chunked(g["q"], g["k"], g["v"], g["alpha_logit"], g["beta_logit"], s_in,
+                                   chunk, **kw)
+        g_outs.append(o.to("cpu", torch.float64).numpy())
+        g_state = s
+        q, k, v, a, b = (to_numpy64(d[n]) for n in ("q", "k", "v", "alpha_logit", "beta_logit"))
+        os_in = to_numpy64(d["state_in"]) if (c == 0 and d["state_in"] is not None) else o_state
+        oo, o_state = oracle.gdn_fwd(q, k, v, a, b, os_in, gate_logits=True,
+                                     out_gate=to_numpy64(d["out_gate"]))
+        o_outs.append(oo)
+    torch.cuda.synchronize()
+    r1 = assert_close(np.concatenate(g_outs, 2), np.concatenate(o_outs, 2), False, what + " out")
+    r2 = assert_close(g_state.to("cpu", torch.float64).numpy(), o_state, False, what + " state")
+    print(f"   out maxabs {r1[0]:.2e} rel {r1[1]:.2e} | state maxabs {r2[0]:.2e} rel {r2[1]:.2e}",
+          flush=True)
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_gated_d64_last_segment_of_one_chunk(gdn_lib, oracle_mod, out_dtype):
+    # gated call (logits and an output gate), 40 chunks in 14 segments: gated
+    # calls keep the general form (segment 0 from zero, corrected like the
+    # others, the gate applied by the correction pass), split halves included
+    _gated(gdn_lib, oracle_mod, D64, 2, H=16, T=40 * 64, out_dtype=out_dtype, what="d64")
+
+
+@pytest.mark.parametrize("chunk", [32, 64])
+def test_gated_d128_segments(gdn_lib, oracle_mod, chunk):
+    _gated(gdn_lib, oracle_mod, D128, 2, H=16, T=2640, chunk=chunk, what=f"d128 chunk {chunk}")
