@@ -20,6 +20,8 @@ pytestmark = pytest.mark.gpu
 @pytest.mark.parametrize("wl_name,first,second", [
     ("rollout_h16_d128", dict(H=16, T=2640), dict(H=5, T=700)),       # segmented plan, then a smaller one
     ("stream_chunk_h16_d64", dict(H=16, T=2640), dict(H=3, T=333)),
+    # 48 heads of one frame: two segments, the largest scratch of the workloads
+    ("frame_step_b2_h24_d128", dict(B=2, H=24, T=880), dict(B=1, H=20, T=640)),
 ])
 def test_noalloc_equals_step_on_two_calls(gdn_lib, oracle_mod, wl_name, first, second):
     wl = WORKLOADS[wl_name]
