@@ -262,3 +262,30 @@ def test_debug_flags_follow_the_environment(lib, monkeypatch):
     assert lib.gdn_debug_flags() & 1
     monkeypatch.setenv("GDN_DEBUG_REVERSE_WORKGROUPS", "0")
     assert lib.gdn_debug_flags() == 0
+
+
+def _seg_bytes(B, H, dk, dv, chunk, nseg, seg_chunks):
+    """Workspace of a segmented pipelined call: maps (A_s fp16, B_s fp32) of
+    every segment, a copy of the state, Phi and the partial outputs (fp16)
+    of seg_chunks chunks per segment, and the working scales."""
+    bh, rows = B * H, seg_chunks * chunk
+    return (bh * nseg * dk * dk * 2 + bh * nseg * dk * dv * 4 + bh * dk * dv * 4
+            + bh * nseg * rows * dk * 2 + bh * nseg * rows * dv * 2 + bh * (dv // 16) * 4)
+
+
+def test_launch_plans_of_the_workloads(lib):
+    # The plan's segment counts for the five workloads, read back through the
+    # workspace query (a host-only computation): the 16-head rollout (d=128)
+    # in 7 segments of 6 chunks, the 16-head streaming chunk (d=64) in 14 of
+    # 3, the 48-head single frame in 2 of 7, the 128-head prefill unsplit.
+    assert lib.gdn_workspace_bytes(1, 16, 2640, 128, 128, 0, None) == _seg_bytes(1, 16, 128, 128, 64, 7, 6)
+    assert lib.gdn_workspace_bytes(1, 16, 2640, 64, 64, 0, None) == _seg_bytes(1, 16, 64, 64, 64, 14, 3)
+    assert lib.gdn_workspace_bytes(2, 24, 880, 128, 128, 0, None) == _seg_bytes(2, 24, 128, 128, 64, 2, 7)
+    assert lib.gdn_workspace_bytes(4, 32, 16384, 128, 128, 64, None) == 0
+    # a gated single-frame call keeps the costlier general form of the
+    # correction pass in the estimate, and stays unsplit
+    # (the options type of the loaded library: an earlier test reloads the binding)
+    o = lib.gdn_workspace_bytes.argtypes[-1]._type_()
+    lib.gdn_default_opts(ctypes.byref(o))
+    o.gate_logits = 1
+    assert lib.gdn_workspace_bytes(2, 24, 880, 128, 128, 0, ctypes.byref(o)) == 0
